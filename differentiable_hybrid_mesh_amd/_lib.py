@@ -1,0 +1,185 @@
+"""ctypes binding of libgm.so (include/gm.h): same names, argument marshalling only.
+
+Every array argument is a torch tensor on the GPU (or None); the binding passes its
+data pointer.  No computation happens here.  Importing this module does not touch
+the GPU; ``lib()`` raises if libgm.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgm.so")
+
+GM_TILE = 16
+GM_REC = 16
+GM_GRAD = 13
+GM_OK, GM_ERR_ARG, GM_ERR_CAPACITY, GM_ERR_HIP = 0, -1, -2, -3
+
+
+class GmError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"gm status {status}: {msg}")
+        self.status = status
+
+
+class GmCamera(C.Structure):
+    _fields_ = [("width", C.c_int32), ("height", C.c_int32), ("fx", C.c_float), ("fy", C.c_float),
+                ("cx", C.c_float), ("cy", C.c_float), ("R", C.c_float * 9), ("t", C.c_float * 3),
+                ("near_z", C.c_float)]
+
+
+class GmLight(C.Structure):
+    _fields_ = [("pos", C.c_float * 3), ("ambient", C.c_float * 3), ("diffuse", C.c_float * 3),
+                ("specular", C.c_float * 3), ("shininess", C.c_float)]
+
+
+class GmMesh(C.Structure):
+    _fields_ = [("V", C.c_int32), ("F", C.c_int32), ("Vt", C.c_int32), ("tex_size", C.c_int32),
+                ("verts", C.c_void_p), ("faces", C.c_void_p), ("face_mask", C.c_void_p),
+                ("vcolor", C.c_void_p), ("vnormal", C.c_void_p), ("uv", C.c_void_p),
+                ("faces_uv", C.c_void_p), ("mips", C.c_void_p)]
+
+
+EXPORTS = ["gm_bin_triangles_ws", "gm_bin_triangles", "gm_raster_zbuffer", "gm_project_gaussians",
+           "gm_sort_tile_keys_ws", "gm_sort_tile_keys", "gm_composite_hybrid_fwd",
+           "gm_composite_hybrid_bwd", "gm_mipmaps_floats", "gm_build_mipmaps", "gm_last_error",
+           "gm_version"]
+
+_lib = None
+
+
+def lib():
+    """Load libgm.so; raise a clear error when it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python __graft_entry__.py build` "
+                          "(or differentiable_hybrid_mesh_amd/build.py) first")
+    L = C.CDLL(LIB_PATH)
+    P, I32, I64, SZ, F32 = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_float
+    cam, mesh, light = C.POINTER(GmCamera), C.POINTER(GmMesh), C.POINTER(GmLight)
+    L.gm_bin_triangles_ws.argtypes = [I32, I32, I32, I32]
+    L.gm_bin_triangles_ws.restype = SZ
+    L.gm_bin_triangles.argtypes = [cam, mesh, P, P, P, I64, C.POINTER(C.c_int64), P, SZ, P]
+    L.gm_raster_zbuffer.argtypes = [cam, mesh, P, P, P, P, P, P, P]
+    L.gm_project_gaussians.argtypes = [cam, I32, P, P, P, P, P, I32, P, P]
+    L.gm_sort_tile_keys_ws.argtypes = [I32, I64, I32, I32]
+    L.gm_sort_tile_keys_ws.restype = SZ
+    L.gm_sort_tile_keys.argtypes = [cam, I32, P, P, F32, P, P, I64, C.POINTER(C.c_int64), P, SZ, P]
+    L.gm_composite_hybrid_fwd.argtypes = [cam, P, P, P, P, P, mesh, P, light, P, F32, P, P, P, P, P, P]
+    L.gm_composite_hybrid_bwd.argtypes = [cam, I32, P, P, P, P, P, mesh, P, light, P, F32, P, P, P, P,
+                                          P, P, P, P, P]
+    L.gm_mipmaps_floats.argtypes = [I32]
+    L.gm_mipmaps_floats.restype = SZ
+    L.gm_build_mipmaps.argtypes = [P, I32, P, P]
+    L.gm_last_error.argtypes = []
+    L.gm_last_error.restype = C.c_char_p
+    L.gm_version.argtypes = []
+    L.gm_version.restype = I32
+    for name in EXPORTS:
+        if not hasattr(L, name):
+            raise ImportError(f"{LIB_PATH} does not export {name}")
+    for name in ("gm_bin_triangles", "gm_raster_zbuffer", "gm_project_gaussians", "gm_sort_tile_keys",
+                 "gm_composite_hybrid_fwd", "gm_composite_hybrid_bwd", "gm_build_mipmaps"):
+        getattr(L, name).restype = C.c_int
+    _lib = L
+    return L
+
+
+def ptr(t) -> Optional[int]:
+    """Device pointer of a tensor (None passes NULL)."""
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def check(status: int):
+    if status != GM_OK:
+        raise GmError(status, lib().gm_last_error().decode(errors="replace"))
+    return status
+
+
+# ---------------------------------------------------------------------------
+# the six calls and the auxiliary ones, same names as the C ABI
+# ---------------------------------------------------------------------------
+
+def gm_bin_triangles_ws(V, F, width, height) -> int:
+    return lib().gm_bin_triangles_ws(V, F, width, height)
+
+
+def gm_bin_triangles(cam, mesh, vscreen, tile_offsets, tile_tris, cap, ws, stream):
+    """Returns (status, n_pairs); GM_ERR_CAPACITY is returned, not raised."""
+    n = C.c_int64(0)
+    st = lib().gm_bin_triangles(C.byref(cam), C.byref(mesh), ptr(vscreen), ptr(tile_offsets),
+                                ptr(tile_tris), int(cap), C.byref(n), ptr(ws),
+                                0 if ws is None else ws.numel() * ws.element_size(), stream)
+    if st not in (GM_OK, GM_ERR_CAPACITY):
+        check(st)
+    return st, n.value
+
+
+def gm_raster_zbuffer(cam, mesh, vscreen, tile_offsets, tile_tris, face_id, depth, tile_dmax, stream):
+    check(lib().gm_raster_zbuffer(C.byref(cam), C.byref(mesh), ptr(vscreen), ptr(tile_offsets),
+                                  ptr(tile_tris), ptr(face_id), ptr(depth), ptr(tile_dmax), stream))
+
+
+def gm_project_gaussians(cam, N, means, quats, scales, opacity, sh, sh_degree, rec, stream):
+    check(lib().gm_project_gaussians(C.byref(cam), int(N), ptr(means), ptr(quats), ptr(scales),
+                                     ptr(opacity), ptr(sh), int(sh_degree), ptr(rec), stream))
+
+
+def gm_sort_tile_keys_ws(N, cap, width, height) -> int:
+    return lib().gm_sort_tile_keys_ws(int(N), int(cap), width, height)
+
+
+def gm_sort_tile_keys(cam, N, rec, tile_dmax, softness, tile_ranges, sorted_ids, cap, ws, stream):
+    """Returns (status, n_keys); GM_ERR_CAPACITY is returned, not raised."""
+    n = C.c_int64(0)
+    st = lib().gm_sort_tile_keys(C.byref(cam), int(N), ptr(rec), ptr(tile_dmax), float(softness),
+                                 ptr(tile_ranges), ptr(sorted_ids), int(cap), C.byref(n), ptr(ws),
+                                 0 if ws is None else ws.numel() * ws.element_size(), stream)
+    if st not in (GM_OK, GM_ERR_CAPACITY):
+        check(st)
+    return st, n.value
+
+
+def _light_ref(light):
+    return None if light is None else C.byref(light)
+
+
+def gm_composite_hybrid_fwd(cam, rec, tile_ranges, sorted_ids, face_id, depth, mesh, vscreen, light, bg,
+                            softness, out_rgb, out_depth, out_alpha, state_T, state_last, stream):
+    bgv = (C.c_float * 3)(*[float(x) for x in bg])
+    check(lib().gm_composite_hybrid_fwd(C.byref(cam), ptr(rec), ptr(tile_ranges), ptr(sorted_ids),
+                                        ptr(face_id), ptr(depth), C.byref(mesh), ptr(vscreen),
+                                        _light_ref(light), C.cast(bgv, C.c_void_p), float(softness),
+                                        ptr(out_rgb), ptr(out_depth), ptr(out_alpha), ptr(state_T),
+                                        ptr(state_last), stream))
+
+
+def gm_composite_hybrid_bwd(cam, N, rec, tile_ranges, sorted_ids, face_id, depth, mesh, vscreen, light, bg,
+                            softness, state_T, state_last, g_rgb, g_depth, g_alpha, g_rec, g_mesh_rgb,
+                            g_mesh_depth, stream):
+    bgv = (C.c_float * 3)(*[float(x) for x in bg])
+    check(lib().gm_composite_hybrid_bwd(C.byref(cam), int(N), ptr(rec), ptr(tile_ranges), ptr(sorted_ids),
+                                        ptr(face_id), ptr(depth), C.byref(mesh), ptr(vscreen),
+                                        _light_ref(light), C.cast(bgv, C.c_void_p), float(softness),
+                                        ptr(state_T), ptr(state_last), ptr(g_rgb), ptr(g_depth),
+                                        ptr(g_alpha), ptr(g_rec), ptr(g_mesh_rgb), ptr(g_mesh_depth),
+                                        stream))
+
+
+def gm_mipmaps_floats(S) -> int:
+    return lib().gm_mipmaps_floats(int(S))
+
+
+def gm_build_mipmaps(tex, S, mips, stream):
+    check(lib().gm_build_mipmaps(ptr(tex), int(S), ptr(mips), stream))
+
+
+def gm_version() -> int:
+    return lib().gm_version()

@@ -1,0 +1,64 @@
+"""Build libgm.so (the gfx950 HIP library) in-tree with hipcc.
+
+Every source under ``csrc/`` is compiled for gfx950 only, with packed-fp32
+instructions disabled, fp32 denormals kept, hardware float atomics, and the
+translation units' own ``#pragma clang fp contract(off)`` deciding contraction.
+"""
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libgm.so")
+BUILD_DIR = os.path.join(HERE, "_build")
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CFLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-munsafe-fp-atomics", "-fno-gpu-flush-denormals-to-zero",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link libgm.so; returns its path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    procs = []
+    objs = []
+    for src in sources():
+        obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
+        objs.append(obj)
+        cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+    failed = []
+    for src, p in procs:
+        out, _ = p.communicate()
+        text = out.decode(errors="replace")
+        if p.returncode != 0:
+            failed.append((src, text))
+        elif verbose and text.strip():
+            print(text)
+    if failed:
+        for src, text in failed:
+            sys.stderr.write(f"--- {src}\n{text}\n")
+        raise RuntimeError("hipcc failed for " + ", ".join(os.path.basename(s) for s, _ in failed))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,210 @@
+// libgm: error state, device-wide scan, mip pyramid.
+#include <cstdarg>
+#include <cstring>
+
+#include "gm_internal.h"
+
+namespace gm {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+}
+
+void clear_error() { g_err[0] = 0; }
+
+gm_status check_camera(const gm_camera* cam)
+{
+    GM_ARG_CHECK(cam != nullptr, "camera is NULL");
+    GM_ARG_CHECK(cam->width > 0 && cam->height > 0, "image size %dx%d must be positive", cam->width,
+                 cam->height);
+    GM_ARG_CHECK(cam->width <= 16384 && cam->height <= 16384, "image size %dx%d above 16384",
+                 cam->width, cam->height);
+    GM_ARG_CHECK(cam->near_z > 0.0f, "near_z must be positive");
+    GM_ARG_CHECK(cam->fx != 0.0f && cam->fy != 0.0f, "focal lengths must be non-zero");
+    return GM_OK;
+}
+
+gm_status read_back_i64(const long long* dev, int64_t* host, hipStream_t stream)
+{
+    long long v = 0;
+    GM_HIP_CHECK(hipMemcpyAsync(&v, dev, sizeof(v), hipMemcpyDeviceToHost, stream));
+    GM_HIP_CHECK(hipStreamSynchronize(stream));
+    *host = (int64_t)v;
+    return GM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// exclusive scan: 256 threads x 16 items per block
+// ---------------------------------------------------------------------------
+constexpr int SCAN_THREADS = 256;
+constexpr int SCAN_ITEMS = 16;
+constexpr int SCAN_CHUNK = SCAN_THREADS * SCAN_ITEMS;
+
+// Inclusive block scan of one int64 per thread (wave64 shuffles + LDS across waves).
+__device__ inline long long block_incl_scan(long long x, long long* lds_waves, long long* total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        long long y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) lds_waves[wave] = x;
+    __syncthreads();
+    long long off = 0, all = 0;
+    const int nw = blockDim.x >> 6;
+    for (int w = 0; w < nw; ++w) {
+        long long s = lds_waves[w];
+        if (w < wave) off += s;
+        all += s;
+    }
+    __syncthreads();
+    if (total) *total = all;
+    return x + off;
+}
+
+__global__ void __launch_bounds__(SCAN_THREADS) k_scan_block_sums(const int32_t* __restrict__ in,
+                                                                  int64_t n,
+                                                                  long long* __restrict__ sums)
+{
+    __shared__ long long lds[SCAN_THREADS / 64];
+    const int64_t base = (int64_t)blockIdx.x * SCAN_CHUNK;
+    long long s = 0;
+#pragma unroll
+    for (int k = 0; k < SCAN_ITEMS; ++k) {
+        int64_t i = base + (int64_t)k * SCAN_THREADS + threadIdx.x;
+        if (i < n) s += in[i];
+    }
+    long long tot;
+    block_incl_scan(s, lds, &tot);
+    if (threadIdx.x == 0) sums[blockIdx.x] = tot;
+}
+
+// Single block: exclusive scan of the block sums in place, grand total to *total.
+__global__ void __launch_bounds__(1024) k_scan_sums(long long* __restrict__ sums, int64_t nb,
+                                                    long long* __restrict__ total)
+{
+    __shared__ long long lds[1024 / 64];
+    long long carry = 0;
+    for (int64_t b0 = 0; b0 < nb; b0 += 1024) {
+        int64_t i = b0 + threadIdx.x;
+        long long v = i < nb ? sums[i] : 0;
+        long long tot;
+        long long inc = block_incl_scan(v, lds, &tot);
+        if (i < nb) sums[i] = carry + inc - v;
+        carry += tot;
+    }
+    if (threadIdx.x == 0) *total = carry;
+}
+
+__global__ void __launch_bounds__(SCAN_THREADS) k_scan_apply(const int32_t* __restrict__ in,
+                                                             int64_t n,
+                                                             const long long* __restrict__ sums,
+                                                             const long long* __restrict__ total,
+                                                             int32_t* __restrict__ out)
+{
+    __shared__ long long lds[SCAN_THREADS / 64];
+    const int64_t base = (int64_t)blockIdx.x * SCAN_CHUNK + (int64_t)threadIdx.x * SCAN_ITEMS;
+    int32_t v[SCAN_ITEMS];
+    long long s = 0;
+#pragma unroll
+    for (int k = 0; k < SCAN_ITEMS; ++k) {
+        int64_t i = base + k;
+        v[k] = i < n ? in[i] : 0;
+        s += v[k];
+    }
+    long long inc = block_incl_scan(s, lds, nullptr);
+    long long run = sums[blockIdx.x] + inc - s;
+#pragma unroll
+    for (int k = 0; k < SCAN_ITEMS; ++k) {
+        int64_t i = base + k;
+        if (i < n) out[i] = (int32_t)run;
+        run += v[k];
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) out[n] = (int32_t)*total;
+}
+
+size_t scan_ws_bytes(int64_t n)
+{
+    int64_t nb = div_up(n > 0 ? n : 1, SCAN_CHUNK);
+    return align_up(sizeof(long long) * (size_t)(nb + 1), 256);
+}
+
+// The total is written to *total (device) even when it overflows int32; callers
+// check it before trusting out[].
+gm_status exclusive_scan(const int32_t* in, int32_t* out, int64_t n, long long* total, void* ws,
+                         hipStream_t stream)
+{
+    int64_t nb = div_up(n > 0 ? n : 1, SCAN_CHUNK);
+    long long* sums = (long long*)ws;
+    if (n > 0) {
+        k_scan_block_sums<<<(unsigned)nb, SCAN_THREADS, 0, stream>>>(in, n, sums);
+        GM_LAUNCH_CHECK();
+    } else {
+        GM_HIP_CHECK(hipMemsetAsync(sums, 0, sizeof(long long), stream));
+    }
+    k_scan_sums<<<1, 1024, 0, stream>>>(sums, nb, total);
+    GM_LAUNCH_CHECK();
+    k_scan_apply<<<(unsigned)nb, SCAN_THREADS, 0, stream>>>(in, n, sums, total, out);
+    GM_LAUNCH_CHECK();
+    return GM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// mip pyramid (box filter)
+// ---------------------------------------------------------------------------
+__global__ void k_mip_level(const float* __restrict__ src, int s, float* __restrict__ dst)
+{
+    const int h = s >> 1;
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= h * h * 3) return;
+    const int c = i % 3, x = (i / 3) % h, y = i / (3 * h);
+    const float a = src[((2 * y) * s + 2 * x) * 3 + c];
+    const float b = src[((2 * y) * s + 2 * x + 1) * 3 + c];
+    const float d = src[((2 * y + 1) * s + 2 * x) * 3 + c];
+    const float e = src[((2 * y + 1) * s + 2 * x + 1) * 3 + c];
+    dst[i] = 0.25f * ((a + b) + (d + e));
+}
+
+}  // namespace gm
+
+using namespace gm;
+
+extern "C" {
+
+const char* gm_last_error(void) { return g_err; }
+
+int32_t gm_version(void) { return 100; }
+
+size_t gm_mipmaps_floats(int32_t S)
+{
+    size_t n = 0;
+    for (int32_t s = S; s >= 1; s >>= 1) n += (size_t)s * s * 3;
+    return n;
+}
+
+gm_status gm_build_mipmaps(const float* tex, int32_t S, float* mips, hipStream_t stream)
+{
+    clear_error();
+    GM_ARG_CHECK(tex && mips, "texture or mip buffer is NULL");
+    GM_ARG_CHECK(S > 0 && (S & (S - 1)) == 0 && S <= 16384, "texture side %d is not a power of two", S);
+    GM_HIP_CHECK(hipMemcpyAsync(mips, tex, sizeof(float) * (size_t)S * S * 3, hipMemcpyDeviceToDevice,
+                                stream));
+    float* src = mips;
+    for (int s = S; s > 1; s >>= 1) {
+        float* dst = src + (size_t)s * s * 3;
+        int n = (s / 2) * (s / 2) * 3;
+        k_mip_level<<<(unsigned)div_up(n, 256), 256, 0, stream>>>(src, s, dst);
+        GM_LAUNCH_CHECK();
+        src = dst;
+    }
+    return GM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,569 @@
+// Hybrid compositing, forward and backward (gmesh README, "Design Details > Hybrid
+// rendering"), with the mesh surface resolve of "Mesh rasterizer" step 2 and the
+// v1.1 texture and lighting notes as its prologue.
+//
+// One 256-thread block per 16x16 tile, one thread per pixel.  Records of the tile's
+// list are staged in LDS in batches of 256 (64 bytes each, read by all lanes at the
+// same address: an LDS broadcast).  The forward walks front to back with a
+// tile-level early exit; the backward walks back to front from the last entry any
+// pixel of the tile used, recovering the transmittance by division, reduces the 13
+// per-Gaussian gradients over each wave with shuffles into LDS accumulators, and
+// flushes one float atomic per (tile, Gaussian, field).
+//
+// The per-pair arithmetic is one inline function shared by both kernels and built
+// without contraction, so the forward and the backward take the same skip and stop
+// decisions bit for bit.
+#pragma clang fp contract(off)
+
+#include "gm_internal.h"
+
+namespace gm {
+
+constexpr int CT = 256;     // threads per block = pixels per tile
+constexpr int CB = 256;     // records per LDS batch
+constexpr float SKIP_ALPHA = 1.0f / 255.0f;
+constexpr float STOP_T = 1e-4f;
+constexpr float ALPHA_MAX = 0.99f;
+
+struct CompParams {
+    DevCamera cam;
+    const float* rec;
+    const int32_t* ranges;
+    const int32_t* ids;
+    const int32_t* face_id;
+    const float* depth;
+    // mesh surface
+    int V, F, Vt, tex_size, nlev;
+    const float* vscreen;
+    const int32_t* faces;
+    const float* vcolor;
+    const float* vnormal;
+    const float* uv;
+    const int32_t* faces_uv;
+    const float* mips;
+    int lit;
+    float lpos[3], lamb[3], ldif[3], lspec[3], lshin;
+    float bg[3];
+    float softness;
+};
+
+// ---------------------------------------------------------------------------
+// mesh surface colour c_m at a covered pixel
+// ---------------------------------------------------------------------------
+__device__ inline void bilinear_tex(const float* __restrict__ lvl, int s, float u, float v, float* out)
+{
+    u = fminf(fmaxf(u, 0.0f), 1.0f);
+    v = fminf(fmaxf(v, 0.0f), 1.0f);
+    const float x = u * (float)s - 0.5f, y = v * (float)s - 0.5f;
+    const float x0 = floorf(x), y0 = floorf(y);
+    const float ax = x - x0, ay = y - y0;
+    int ix0 = (int)x0, iy0 = (int)y0;
+    int ix1 = min(max(ix0 + 1, 0), s - 1), iy1 = min(max(iy0 + 1, 0), s - 1);
+    ix0 = min(max(ix0, 0), s - 1);
+    iy0 = min(max(iy0, 0), s - 1);
+    const float* p00 = lvl + ((size_t)iy0 * s + ix0) * 3;
+    const float* p01 = lvl + ((size_t)iy0 * s + ix1) * 3;
+    const float* p10 = lvl + ((size_t)iy1 * s + ix0) * 3;
+    const float* p11 = lvl + ((size_t)iy1 * s + ix1) * 3;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        const float top = p00[c] + (p01[c] - p00[c]) * ax;
+        const float bot = p10[c] + (p11[c] - p10[c]) * ax;
+        out[c] = top + (bot - top) * ay;
+    }
+}
+
+__device__ void surface_color(const CompParams& P, int f, int px, int py, float* cm)
+{
+    const int V = P.V, F = P.F;
+    const float* vs = P.vscreen;
+    int vi[3];
+    double u[3], v[3], z[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        vi[k] = P.faces[k * F + f];
+        u[k] = (double)vs[vi[k]];
+        v[k] = (double)vs[V + vi[k]];
+        z[k] = (double)vs[2 * V + vi[k]];
+    }
+    const double pu = px + 0.5, pv = py + 0.5;
+    const double A = (u[1] - u[0]) * (v[2] - v[0]) - (v[1] - v[0]) * (u[2] - u[0]);
+    const double E[3] = {(u[2] - u[1]) * (pv - v[1]) - (v[2] - v[1]) * (pu - u[1]),
+                         (u[0] - u[2]) * (pv - v[2]) - (v[0] - v[2]) * (pu - u[2]),
+                         (u[1] - u[0]) * (pv - v[0]) - (v[1] - v[0]) * (pu - u[0])};
+    double lam[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) lam[k] = E[k] / A;
+    const double zz = 1.0 / ((lam[0] / z[0] + lam[1] / z[1]) + lam[2] / z[2]);
+    float b[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) b[k] = (float)(lam[k] / z[k] * zz);
+
+    float base[3] = {0.0f, 0.0f, 0.0f};
+    if (P.mips && P.uv) {
+        float uvk[3][2];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int ti = P.faces_uv[k * F + f];
+            uvk[k][0] = P.uv[ti];
+            uvk[k][1] = P.uv[P.Vt + ti];
+        }
+        const float uu = b[0] * uvk[0][0] + b[1] * uvk[1][0] + b[2] * uvk[2][0];
+        const float vv = b[0] * uvk[0][1] + b[1] * uvk[1][1] + b[2] * uvk[2][1];
+        // analytic screen derivatives of the perspective-correct uv (quotient rule)
+        const int ea[3] = {1, 2, 0}, eb[3] = {2, 0, 1};
+        double W = 0.0, dwx[3], dwy[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            W += lam[k] / z[k];
+            dwx[k] = (-(v[eb[k]] - v[ea[k]]) / A) / z[k];
+            dwy[k] = ((u[eb[k]] - u[ea[k]]) / A) / z[k];
+        }
+        float dux = 0.f, dvx = 0.f, duy = 0.f, dvy = 0.f;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const float ax = (float)(dwx[k] / W), ay = (float)(dwy[k] / W);
+            dux += ax * (uvk[k][0] - uu);
+            dvx += ax * (uvk[k][1] - vv);
+            duy += ay * (uvk[k][0] - uu);
+            dvy += ay * (uvk[k][1] - vv);
+        }
+        const float S0 = (float)P.tex_size;
+        const float lx = sqrtf((S0 * dux) * (S0 * dux) + (S0 * dvx) * (S0 * dvx));
+        const float ly = sqrtf((S0 * duy) * (S0 * duy) + (S0 * dvy) * (S0 * dvy));
+        const float rho = fmaxf(lx, ly);
+        const float lmax = (float)(P.nlev - 1);
+        float lod = rho > 0.0f ? log2f(rho) : 0.0f;
+        lod = fminf(fmaxf(lod, 0.0f), lmax);
+        const int l0 = (int)floorf(lod);
+        const int l1 = min(l0 + 1, P.nlev - 1);
+        const float tl = lod - (float)l0;
+        size_t o0 = 0, o1 = 0, o = 0;
+        for (int l = 0; l < P.nlev; ++l) {
+            if (l == l0) o0 = o;
+            if (l == l1) o1 = o;
+            const size_t s = (size_t)(P.tex_size >> l);
+            o += s * s * 3;
+        }
+        float c0[3], c1[3];
+        bilinear_tex(P.mips + o0, P.tex_size >> l0, uu, vv, c0);
+        bilinear_tex(P.mips + o1, P.tex_size >> l1, uu, vv, c1);
+#pragma unroll
+        for (int c = 0; c < 3; ++c) base[c] = c0[c] + (c1[c] - c0[c]) * tl;
+    } else if (P.vcolor) {
+#pragma unroll
+        for (int c = 0; c < 3; ++c)
+            base[c] = b[0] * P.vcolor[c * V + vi[0]] + b[1] * P.vcolor[c * V + vi[1]] + b[2] * P.vcolor[c * V + vi[2]];
+    }
+    if (P.lit && P.vnormal) {
+        const float* R = P.cam.R;
+        float nw[3];
+#pragma unroll
+        for (int c = 0; c < 3; ++c)
+            nw[c] = b[0] * P.vnormal[c * V + vi[0]] + b[1] * P.vnormal[c * V + vi[1]] + b[2] * P.vnormal[c * V + vi[2]];
+        float n[3], L[3], x[3];
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            n[r] = R[r * 3 + 0] * nw[0] + R[r * 3 + 1] * nw[1] + R[r * 3 + 2] * nw[2];
+            L[r] = R[r * 3 + 0] * P.lpos[0] + R[r * 3 + 1] * P.lpos[1] + R[r * 3 + 2] * P.lpos[2] + P.cam.t[r];
+        }
+        const float zf = (float)zz;
+        x[0] = ((float)pu - P.cam.cx) / P.cam.fx * zf;
+        x[1] = ((float)pv - P.cam.cy) / P.cam.fy * zf;
+        x[2] = zf;
+        float l[3] = {L[0] - x[0], L[1] - x[1], L[2] - x[2]};
+        float e[3] = {-x[0], -x[1], -x[2]};
+        const float in = 1.0f / sqrtf(n[0] * n[0] + n[1] * n[1] + n[2] * n[2]);
+        const float il = 1.0f / sqrtf(l[0] * l[0] + l[1] * l[1] + l[2] * l[2]);
+        const float ie = 1.0f / sqrtf(e[0] * e[0] + e[1] * e[1] + e[2] * e[2]);
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            n[r] *= in;
+            l[r] *= il;
+            e[r] *= ie;
+        }
+        const float ndl = n[0] * l[0] + n[1] * l[1] + n[2] * l[2];
+        const float rde = (2.0f * ndl * n[0] - l[0]) * e[0] + (2.0f * ndl * n[1] - l[1]) * e[1] +
+                          (2.0f * ndl * n[2] - l[2]) * e[2];
+        const float diff = fmaxf(ndl, 0.0f);
+        const float spec = (ndl > 0.0f && rde > 0.0f) ? powf(rde, P.lshin) : 0.0f;
+#pragma unroll
+        for (int c = 0; c < 3; ++c) cm[c] = base[c] * (P.lamb[c] + P.ldif[c] * diff) + P.lspec[c] * spec;
+    } else {
+#pragma unroll
+        for (int c = 0; c < 3; ++c) cm[c] = base[c];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// the per-pair evaluation shared by both walks
+// ---------------------------------------------------------------------------
+struct Staged {
+    float4 a;  // u, v, Q00, Q01
+    float4 b;  // Q11, opacity, r, g
+    float4 c;  // b, z_c, g0, g1
+    float4 d;  // sigma, kappa = 1/(sigma softness), -, -
+};
+
+__device__ __forceinline__ float normal_cdf(float s) { return 0.5f * erfcf(-s * 0.70710678118654752f); }
+
+// alpha = min(0.99, o exp(-q)); returns alpha_F = alpha f (0 when below the skip
+// threshold before f is formed); also returns the intermediates the backward needs.
+__device__ __forceinline__ float eval_pair(const Staged& g, float pxc, float pyc, bool on, float D,
+                                           float softness, float& dx, float& dy, float& G, float& alpha,
+                                           float& f, float& s)
+{
+    dx = pxc - g.a.x;
+    dy = pyc - g.a.y;
+    const float q = 0.5f * (g.a.z * dx * dx + g.b.x * dy * dy) + g.a.w * dx * dy;
+    G = __expf(-q);
+    alpha = fminf(g.b.y * G, ALPHA_MAX);
+    f = 1.0f;
+    s = 0.0f;
+    if (alpha < SKIP_ALPHA) return 0.0f;
+    if (on) {
+        const float num = (D - g.c.y) - (g.c.z * dx + g.c.w * dy);
+        if (softness > 0.0f) {
+            s = num * g.d.y;
+            f = normal_cdf(s);
+        } else {
+            f = num > 0.0f ? 1.0f : 0.0f;
+        }
+    }
+    return alpha * f;
+}
+
+__device__ __forceinline__ void stage_record(const CompParams& P, int id, Staged& st)
+{
+    const float4* r = reinterpret_cast<const float4*>(P.rec + (size_t)id * GM_REC);
+    st.a = r[0];
+    st.b = r[1];
+    st.c = r[2];
+    float4 d = r[3];
+    d.y = P.softness > 0.0f ? 1.0f / (d.x * P.softness) : 0.0f;
+    st.d = d;
+}
+
+// ---------------------------------------------------------------------------
+// forward
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(CT)
+k_composite_fwd(CompParams P, float* __restrict__ out_rgb, float* __restrict__ out_depth,
+                float* __restrict__ out_alpha, float* __restrict__ state_T, int32_t* __restrict__ state_last)
+{
+    __shared__ Staged s_g[CB];
+    const int tile = blockIdx.x;
+    const int tx = tile % P.cam.tx, ty = tile / P.cam.tx;
+    const int px = tx * GM_TILE + (threadIdx.x & 15), py = ty * GM_TILE + (threadIdx.x >> 4);
+    const bool inside = px < P.cam.width && py < P.cam.height;
+    const int pix = py * P.cam.width + px;
+    const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
+    const int start = P.ranges[2 * tile], end = P.ranges[2 * tile + 1];
+
+    const int fid = inside ? P.face_id[pix] : -1;
+    const bool on = fid >= 0;
+    const float D = on ? P.depth[pix] : INFINITY;
+
+    float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f, Z = 0.0f;
+    int last = 0;
+    bool done = !inside;
+    for (int b0 = start; b0 < end; b0 += CB) {
+        if (__syncthreads_count(done) == CT) break;
+        const int j = b0 + threadIdx.x;
+        if (j < end) stage_record(P, P.ids[j], s_g[threadIdx.x]);
+        __syncthreads();
+        const int nb = min(CB, end - b0);
+        if (!done) {
+            for (int k = 0; k < nb; ++k) {
+                const Staged& g = s_g[k];
+                float dx, dy, G, al, f, s;
+                const float aF = eval_pair(g, pxc, pyc, on, D, P.softness, dx, dy, G, al, f, s);
+                if (aF < SKIP_ALPHA) continue;
+                const float Tn = T * (1.0f - aF);
+                if (Tn < STOP_T) {
+                    done = true;
+                    break;
+                }
+                const float w = aF * T;
+                C0 += w * g.b.z;
+                C1 += w * g.b.w;
+                C2 += w * g.c.x;
+                Z += w * g.c.y;
+                T = Tn;
+                last = b0 + k - start + 1;
+            }
+        }
+    }
+    if (!inside) return;
+    float cm[3] = {0.0f, 0.0f, 0.0f};
+    if (on) surface_color(P, fid, px, py, cm);
+    const float am = on ? 1.0f : 0.0f;
+    out_rgb[3 * pix + 0] = C0 + T * (on ? cm[0] : P.bg[0]);
+    out_rgb[3 * pix + 1] = C1 + T * (on ? cm[1] : P.bg[1]);
+    out_rgb[3 * pix + 2] = C2 + T * (on ? cm[2] : P.bg[2]);
+    out_alpha[pix] = 1.0f - T * (1.0f - am);
+    out_depth[pix] = Z + (on ? T * D : 0.0f);
+    state_T[pix] = T;
+    state_last[pix] = last;
+}
+
+// ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__global__ void __launch_bounds__(CT)
+k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* __restrict__ state_last,
+                const float* __restrict__ g_rgb, const float* __restrict__ g_depth,
+                const float* __restrict__ g_alpha, float* __restrict__ g_rec, float* __restrict__ g_mesh_rgb,
+                float* __restrict__ g_mesh_depth)
+{
+    __shared__ Staged s_g[CB];
+    __shared__ int s_id[CB];
+    __shared__ float s_acc[CB][GM_GRAD];
+    __shared__ int s_max[CT / 64];
+    const int tile = blockIdx.x;
+    const int tx = tile % P.cam.tx, ty = tile / P.cam.tx;
+    const int px = tx * GM_TILE + (threadIdx.x & 15), py = ty * GM_TILE + (threadIdx.x >> 4);
+    const bool inside = px < P.cam.width && py < P.cam.height;
+    const int pix = py * P.cam.width + px;
+    const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
+    const int start = P.ranges[2 * tile];
+
+    const int fid = inside ? P.face_id[pix] : -1;
+    const bool on = fid >= 0;
+    const float D = on ? P.depth[pix] : INFINITY;
+    const float TF = inside ? state_T[pix] : 1.0f;
+    const int last = inside ? state_last[pix] : 0;
+    float GC[3] = {0.0f, 0.0f, 0.0f}, GZ = 0.0f, GA = 0.0f;
+    if (inside) {
+        GC[0] = g_rgb[3 * pix + 0];
+        GC[1] = g_rgb[3 * pix + 1];
+        GC[2] = g_rgb[3 * pix + 2];
+        if (g_depth) GZ = g_depth[pix];
+        if (g_alpha) GA = g_alpha[pix];
+    }
+    float cm[3] = {0.0f, 0.0f, 0.0f};
+    if (on) surface_color(P, fid, px, py, cm);
+    const float am = on ? 1.0f : 0.0f;
+    // B = dL/dT_F: background / mesh term of colour, depth and alpha
+    float Bt = GZ * (on ? D : 0.0f) - GA * (1.0f - am);
+#pragma unroll
+    for (int c = 0; c < 3; ++c) Bt += GC[c] * (on ? cm[c] : P.bg[c]);
+    float acc = TF * Bt;
+    float T = TF;
+    float gD = 0.0f;
+
+    // longest prefix any pixel of the tile used
+    int m = last;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o, 64));
+    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+    __syncthreads();
+    int mlast = 0;
+#pragma unroll
+    for (int w = 0; w < CT / 64; ++w) mlast = max(mlast, s_max[w]);
+
+    for (int bend = start + mlast; bend > start; bend -= CB) {
+        const int b0 = max(start, bend - CB);
+        const int nb = bend - b0;
+        __syncthreads();
+        if (threadIdx.x < nb) {
+            const int id = P.ids[b0 + threadIdx.x];
+            s_id[threadIdx.x] = id;
+            stage_record(P, id, s_g[threadIdx.x]);
+#pragma unroll
+            for (int c = 0; c < GM_GRAD; ++c) s_acc[threadIdx.x][c] = 0.0f;
+        }
+        __syncthreads();
+        for (int k = nb - 1; k >= 0; --k) {
+            const Staged& g = s_g[k];
+            const int rel = b0 + k - start;
+            float gr[GM_GRAD];
+#pragma unroll
+            for (int c = 0; c < GM_GRAD; ++c) gr[c] = 0.0f;
+            bool act = false;
+            if (rel < last) {
+                float dx, dy, G, al, f, s;
+                const float aF = eval_pair(g, pxc, pyc, on, D, P.softness, dx, dy, G, al, f, s);
+                if (aF >= SKIP_ALPHA) {
+                    act = true;
+                    const float om = 1.0f - aF;
+                    const float Ti = T / om;
+                    const float w = aF * Ti;
+                    const float Vv = GC[0] * g.b.z + GC[1] * g.b.w + GC[2] * g.c.x + GZ * g.c.y;
+                    const float daF = Ti * Vv - acc / om;
+                    acc += w * Vv;
+                    T = Ti;
+                    gr[6] = w * GC[0];
+                    gr[7] = w * GC[1];
+                    gr[8] = w * GC[2];
+                    gr[9] = w * GZ;
+                    const float da = f * daF;
+                    if (g.b.y * G <= ALPHA_MAX) {
+                        gr[5] = G * da;
+                        const float H = g.b.y * G * da;
+                        gr[2] = -0.5f * dx * dx * H;
+                        gr[3] = -dx * dy * H;
+                        gr[4] = -0.5f * dy * dy * H;
+                        gr[0] = H * (g.a.z * dx + g.a.w * dy);
+                        gr[1] = H * (g.a.w * dx + g.b.x * dy);
+                    }
+                    if (on && P.softness > 0.0f) {
+                        const float phi = 0.39894228040143268f * __expf(-0.5f * s * s);
+                        const float ds = al * phi * daF;
+                        const float kap = g.d.y;
+                        gr[9] -= kap * ds;
+                        gr[10] = -kap * ds * dx;
+                        gr[11] = -kap * ds * dy;
+                        gr[0] += kap * ds * g.c.z;
+                        gr[1] += kap * ds * g.c.w;
+                        gr[12] = -ds * s / g.d.x;
+                        gD += kap * ds;
+                    }
+                }
+            }
+            if (__ballot(act)) {
+#pragma unroll
+                for (int c = 0; c < GM_GRAD; ++c) {
+                    const float v = wave_sum(gr[c]);
+                    if ((threadIdx.x & 63) == 0 && v != 0.0f) atomicAdd(&s_acc[k][c], v);
+                }
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x < nb) {
+            float* dst = g_rec + (size_t)s_id[threadIdx.x] * GM_GRAD;
+#pragma unroll
+            for (int c = 0; c < GM_GRAD; ++c) {
+                const float v = s_acc[threadIdx.x][c];
+                if (v != 0.0f) unsafeAtomicAdd(dst + c, v);
+            }
+        }
+    }
+    if (!inside) return;
+    if (g_mesh_rgb) {
+        g_mesh_rgb[3 * pix + 0] = TF * am * GC[0];
+        g_mesh_rgb[3 * pix + 1] = TF * am * GC[1];
+        g_mesh_rgb[3 * pix + 2] = TF * am * GC[2];
+    }
+    if (g_mesh_depth) g_mesh_depth[pix] = TF * am * GZ + gD;
+}
+
+__global__ void k_zero_f32(float* __restrict__ p, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+static gm_status fill_params(CompParams& P, const gm_camera* cam, const float* rec, const int32_t* ranges,
+                             const int32_t* ids, const int32_t* face_id, const float* depth,
+                             const gm_mesh* mesh, const float* vscreen, const gm_light* light,
+                             const float* bg, float softness)
+{
+    if (gm_status s = check_camera(cam)) return s;
+    GM_ARG_CHECK(ranges && face_id && depth && bg, "tile_ranges / face_id / depth / bg is NULL");
+    GM_ARG_CHECK(softness >= 0.0f, "softness must be >= 0");
+    GM_ARG_CHECK(((uintptr_t)rec & 15) == 0, "rec must be 16-byte aligned");
+    P = CompParams{};
+    P.cam = dev_camera(*cam);
+    P.rec = rec;
+    P.ranges = ranges;
+    P.ids = ids;
+    P.face_id = face_id;
+    P.depth = depth;
+    if (mesh && mesh->F > 0) {
+        GM_ARG_CHECK(mesh->faces && vscreen, "mesh faces / vscreen is NULL");
+        P.V = mesh->V;
+        P.F = mesh->F;
+        P.Vt = mesh->Vt;
+        P.vscreen = vscreen;
+        P.faces = mesh->faces;
+        P.vcolor = mesh->vcolor;
+        P.vnormal = mesh->vnormal;
+        if (mesh->mips) {
+            GM_ARG_CHECK(mesh->uv && mesh->faces_uv, "textured mesh needs uv and faces_uv");
+            GM_ARG_CHECK(mesh->tex_size > 0 && (mesh->tex_size & (mesh->tex_size - 1)) == 0,
+                         "tex_size %d is not a power of two", mesh->tex_size);
+            P.uv = mesh->uv;
+            P.faces_uv = mesh->faces_uv;
+            P.mips = mesh->mips;
+            P.tex_size = mesh->tex_size;
+            int n = 0;
+            for (int s = mesh->tex_size; s >= 1; s >>= 1) ++n;
+            P.nlev = n;
+        }
+    }
+    if (light) {
+        P.lit = 1;
+        for (int i = 0; i < 3; ++i) {
+            P.lpos[i] = light->pos[i];
+            P.lamb[i] = light->ambient[i];
+            P.ldif[i] = light->diffuse[i];
+            P.lspec[i] = light->specular[i];
+        }
+        P.lshin = light->shininess;
+    }
+    for (int i = 0; i < 3; ++i) P.bg[i] = bg[i];
+    P.softness = softness;
+    return GM_OK;
+}
+
+}  // namespace gm
+
+using namespace gm;
+
+extern "C" {
+
+gm_status gm_composite_hybrid_fwd(const gm_camera* cam, const float* rec, const int32_t* tile_ranges,
+                                  const int32_t* sorted_ids, const int32_t* face_id, const float* depth,
+                                  const gm_mesh* mesh, const float* vscreen, const gm_light* light,
+                                  const float* bg, float softness, float* out_rgb, float* out_depth,
+                                  float* out_alpha, float* state_T, int32_t* state_last, hipStream_t stream)
+{
+    clear_error();
+    CompParams P;
+    if (gm_status s = fill_params(P, cam, rec, tile_ranges, sorted_ids, face_id, depth, mesh, vscreen, light,
+                                  bg, softness))
+        return s;
+    GM_ARG_CHECK(out_rgb && out_depth && out_alpha && state_T && state_last, "an output is NULL");
+    const int64_t T = (int64_t)P.cam.tx * P.cam.ty;
+    k_composite_fwd<<<(unsigned)T, CT, 0, stream>>>(P, out_rgb, out_depth, out_alpha, state_T, state_last);
+    GM_LAUNCH_CHECK();
+    return GM_OK;
+}
+
+gm_status gm_composite_hybrid_bwd(const gm_camera* cam, int32_t N, const float* rec, const int32_t* tile_ranges,
+                                  const int32_t* sorted_ids, const int32_t* face_id, const float* depth,
+                                  const gm_mesh* mesh, const float* vscreen, const gm_light* light,
+                                  const float* bg, float softness, const float* state_T,
+                                  const int32_t* state_last, const float* g_rgb, const float* g_depth,
+                                  const float* g_alpha, float* g_rec, float* g_mesh_rgb, float* g_mesh_depth,
+                                  hipStream_t stream)
+{
+    clear_error();
+    CompParams P;
+    if (gm_status s = fill_params(P, cam, rec, tile_ranges, sorted_ids, face_id, depth, mesh, vscreen, light,
+                                  bg, softness))
+        return s;
+    GM_ARG_CHECK(N >= 0, "N = %d is negative", N);
+    GM_ARG_CHECK(state_T && state_last && g_rgb, "state or g_rgb is NULL");
+    GM_ARG_CHECK(N == 0 || g_rec, "g_rec is NULL");
+    const int64_t T = (int64_t)P.cam.tx * P.cam.ty;
+    if (N > 0) {
+        const int64_t n = (int64_t)N * GM_GRAD;
+        k_zero_f32<<<(unsigned)div_up(n, 256), 256, 0, stream>>>(g_rec, n);
+        GM_LAUNCH_CHECK();
+    }
+    k_composite_bwd<<<(unsigned)T, CT, 0, stream>>>(P, state_T, state_last, g_rgb, g_depth, g_alpha, g_rec,
+                                                   g_mesh_rgb, g_mesh_depth);
+    GM_LAUNCH_CHECK();
+    return GM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,211 @@
+// 3D Gaussian projection with the EWA conditional depth model and SH colour
+// (gmesh README, "Design Details > Hybrid rendering": z*(p) = z_c + g.(p - mean2d),
+// g = (Sigma_uv + eps I)^-1 Sigma_uv,z, sigma^2 = Sigma_zz - Sigma_z,uv g).
+//
+// The record fields that decide tile membership and order are evaluated in fp32 in
+// a fixed order with no fused multiply-add and correctly rounded / and sqrt, so
+// that every implementation of the same order gets the same bits.
+#pragma clang fp contract(off)
+
+#include "gm_internal.h"
+
+namespace gm {
+
+constexpr float EPS2D = 0.3f;  // px^2: low-pass dilation, also the eps of the depth model
+
+// Real SH up to degree 3 (splatting sign/order convention); closed-form constants.
+__device__ inline void sh_basis_f(float x, float y, float z, float* Y)
+{
+    const float c0 = 0.28209479177387814f;   // 1/(2 sqrt(pi))
+    const float c1 = 0.48860251190291992f;   // sqrt(3/(4 pi))
+    const float c2a = 1.0925484305920792f;   // (1/2) sqrt(15/pi)
+    const float c2b = 0.31539156525252005f;  // (1/4) sqrt(5/pi)
+    const float c2c = 0.54627421529603959f;  // (1/4) sqrt(15/pi)
+    const float c3a = 0.59004358992664352f;  // (1/4) sqrt(35/(2 pi))
+    const float c3b = 2.8906114426405538f;   // (1/2) sqrt(105/pi)
+    const float c3c = 0.45704579946446572f;  // (1/4) sqrt(21/(2 pi))
+    const float c3d = 0.37317633259011546f;  // (1/4) sqrt(7/pi)
+    const float c3e = 1.4453057213202769f;   // (1/4) sqrt(105/pi)
+    const float xx = x * x, yy = y * y, zz = z * z;
+    Y[0] = c0;
+    Y[1] = -c1 * y;
+    Y[2] = c1 * z;
+    Y[3] = -c1 * x;
+    Y[4] = c2a * x * y;
+    Y[5] = -c2a * y * z;
+    Y[6] = c2b * (2.0f * zz - xx - yy);
+    Y[7] = -c2a * x * z;
+    Y[8] = c2c * (xx - yy);
+    Y[9] = -c3a * y * (3.0f * xx - yy);
+    Y[10] = c3b * x * y * z;
+    Y[11] = -c3c * y * (4.0f * zz - xx - yy);
+    Y[12] = c3d * z * (2.0f * zz - 3.0f * xx - 3.0f * yy);
+    Y[13] = -c3c * x * (4.0f * zz - xx - yy);
+    Y[14] = c3e * z * (xx - yy);
+    Y[15] = -c3a * x * (xx - 3.0f * yy);
+}
+
+__global__ void __launch_bounds__(256)
+k_project_gaussians(DevCamera cam, int N, const float* __restrict__ means,
+                    const float* __restrict__ quats, const float* __restrict__ scales,
+                    const float* __restrict__ opacity, const float* __restrict__ sh, int sh_degree,
+                    float* __restrict__ rec)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= N) return;
+    const float* W = cam.R;
+    const float mx = means[i], my = means[N + i], mz = means[2 * N + i];
+    const float xc = ((W[0] * mx + W[1] * my) + W[2] * mz) + cam.t[0];
+    const float yc = ((W[3] * mx + W[4] * my) + W[5] * mz) + cam.t[1];
+    const float zc = ((W[6] * mx + W[7] * my) + W[8] * mz) + cam.t[2];
+    bool ok = zc >= cam.near_z;
+
+    float qw = quats[i], qx = quats[N + i], qy = quats[2 * N + i], qz = quats[3 * N + i];
+    const float qq = ((qw * qw + qx * qx) + qy * qy) + qz * qz;
+    if (!(qq > 0.0f)) ok = false;
+    const float qn = sqrtf(qq);
+    qw = qw / qn;
+    qx = qx / qn;
+    qy = qy / qn;
+    qz = qz / qn;
+    float Rq[9];
+    Rq[0] = 1.0f - 2.0f * ((qy * qy) + (qz * qz));
+    Rq[1] = 2.0f * ((qx * qy) - (qw * qz));
+    Rq[2] = 2.0f * ((qx * qz) + (qw * qy));
+    Rq[3] = 2.0f * ((qx * qy) + (qw * qz));
+    Rq[4] = 1.0f - 2.0f * ((qx * qx) + (qz * qz));
+    Rq[5] = 2.0f * ((qy * qz) - (qw * qx));
+    Rq[6] = 2.0f * ((qx * qz) - (qw * qy));
+    Rq[7] = 2.0f * ((qy * qz) + (qw * qx));
+    Rq[8] = 1.0f - 2.0f * ((qx * qx) + (qy * qy));
+    const float s[3] = {scales[i], scales[N + i], scales[2 * N + i]};
+    float M[9];
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) M[r * 3 + c] = Rq[r * 3 + c] * s[c];
+    float S[9];  // Sigma = M M^T (world)
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int c = r; c < 3; ++c) {
+            const float v = (M[r * 3 + 0] * M[c * 3 + 0] + M[r * 3 + 1] * M[c * 3 + 1]) + M[r * 3 + 2] * M[c * 3 + 2];
+            S[r * 3 + c] = v;
+            S[c * 3 + r] = v;
+        }
+    float A[9], C[9];  // Sigma_c = (W Sigma) W^T
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int c = 0; c < 3; ++c)
+            A[r * 3 + c] = (W[r * 3 + 0] * S[0 * 3 + c] + W[r * 3 + 1] * S[1 * 3 + c]) + W[r * 3 + 2] * S[2 * 3 + c];
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int c = r; c < 3; ++c) {
+            const float v = (A[r * 3 + 0] * W[c * 3 + 0] + A[r * 3 + 1] * W[c * 3 + 1]) + A[r * 3 + 2] * W[c * 3 + 2];
+            C[r * 3 + c] = v;
+            C[c * 3 + r] = v;
+        }
+    // pinhole Jacobian at the mean (no frustum clamp)
+    const float z2 = zc * zc;
+    const float J00 = cam.fx / zc;
+    const float J02 = -(cam.fx * xc) / z2;
+    const float J11 = cam.fy / zc;
+    const float J12 = -(cam.fy * yc) / z2;
+    float T0[3], T1[3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        T0[c] = J00 * C[0 * 3 + c] + J02 * C[2 * 3 + c];
+        T1[c] = J11 * C[1 * 3 + c] + J12 * C[2 * 3 + c];
+    }
+    const float S00 = T0[0] * J00 + T0[2] * J02;
+    const float S01 = T0[1] * J11 + T0[2] * J12;
+    const float S11 = T1[1] * J11 + T1[2] * J12;
+    const float k0 = T0[2], k1 = T1[2], Szz = C[8];
+    const float a = S00 + EPS2D, b = S01, c = S11 + EPS2D;
+    const float det = a * c - b * b;
+    if (!(det > 0.0f)) ok = false;
+    const float Q00 = c / det, Q01 = (-b) / det, Q11 = a / det;
+    const float g0 = Q00 * k0 + Q01 * k1;
+    const float g1 = Q01 * k0 + Q11 * k1;
+    const float var = Szz - (k0 * g0 + k1 * g1);
+    const float sig = sqrtf(var > 1e-12f ? var : 1e-12f);
+    const float u = (cam.fx * xc) / zc + cam.cx;
+    const float v = (cam.fy * yc) / zc + cam.cy;
+    const float m = (a + c) * 0.5f;
+    const float disc = m * m - det;
+    const float lam = m + sqrtf(disc > 0.1f ? disc : 0.1f);
+    const float rad = ceilf(3.0f * sqrtf(lam));
+    int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+    if (ok) {
+        float fx0 = floorf((u - rad) / 16.0f), fx1 = ceilf((u + rad) / 16.0f);
+        float fy0 = floorf((v - rad) / 16.0f), fy1 = ceilf((v + rad) / 16.0f);
+        fx0 = fminf(fmaxf(fx0, 0.0f), (float)cam.tx);
+        fx1 = fminf(fmaxf(fx1, 0.0f), (float)cam.tx);
+        fy0 = fminf(fmaxf(fy0, 0.0f), (float)cam.ty);
+        fy1 = fminf(fmaxf(fy1, 0.0f), (float)cam.ty);
+        r0 = (int)fx0;
+        r1 = (int)fy0;
+        r2 = (int)fx1;
+        r3 = (int)fy1;
+        if (r0 >= r2 || r1 >= r3) r0 = r1 = r2 = r3 = 0;
+    }
+    const int ntiles = (r2 - r0) * (r3 - r1);
+
+    // colour (value arithmetic, fp32)
+    float col[3];
+    if (sh_degree < 0) {
+        col[0] = sh[i];
+        col[1] = sh[N + i];
+        col[2] = sh[2 * N + i];
+    } else {
+        float cw[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) cw[j] = -(W[j] * cam.t[0] + W[3 + j] * cam.t[1] + W[6 + j] * cam.t[2]);
+        float dx = mx - cw[0], dy = my - cw[1], dz = mz - cw[2];
+        const float nrm = sqrtf(dx * dx + dy * dy + dz * dz);
+        dx /= nrm;
+        dy /= nrm;
+        dz /= nrm;
+        float Y[16];
+        sh_basis_f(dx, dy, dz, Y);
+        const int K = (sh_degree + 1) * (sh_degree + 1);
+#pragma unroll
+        for (int ch = 0; ch < 3; ++ch) {
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k) acc += Y[k] * sh[((size_t)k * 3 + ch) * N + i];
+            acc += 0.5f;
+            col[ch] = acc > 0.0f ? acc : 0.0f;
+        }
+    }
+    float4* o = reinterpret_cast<float4*>(rec + (size_t)i * GM_REC);
+    o[0] = make_float4(u, v, Q00, Q01);
+    o[1] = make_float4(Q11, opacity[i], col[0], col[1]);
+    o[2] = make_float4(col[2], zc, g0, g1);
+    o[3] = make_float4(sig, __int_as_float(r0 | (r1 << 16)), __int_as_float(r2 | (r3 << 16)),
+                       __int_as_float(ntiles));
+}
+
+}  // namespace gm
+
+using namespace gm;
+
+extern "C" gm_status gm_project_gaussians(const gm_camera* cam, int32_t N, const float* means,
+                                          const float* quats, const float* scales,
+                                          const float* opacity, const float* sh, int32_t sh_degree,
+                                          float* rec, hipStream_t stream)
+{
+    clear_error();
+    if (gm_status s = check_camera(cam)) return s;
+    GM_ARG_CHECK(N >= 0, "N = %d is negative", N);
+    GM_ARG_CHECK(sh_degree >= -1 && sh_degree <= 3, "sh_degree %d outside -1..3", sh_degree);
+    if (N == 0) return GM_OK;
+    GM_ARG_CHECK(means && quats && scales && opacity && sh && rec, "an input or rec is NULL");
+    GM_ARG_CHECK(((uintptr_t)rec & 15) == 0, "rec must be 16-byte aligned");
+    const DevCamera dc = dev_camera(*cam);
+    k_project_gaussians<<<(unsigned)div_up(N, 256), 256, 0, stream>>>(dc, N, means, quats, scales, opacity,
+                                                                      sh, sh_degree, rec);
+    GM_LAUNCH_CHECK();
+    return GM_OK;
+}

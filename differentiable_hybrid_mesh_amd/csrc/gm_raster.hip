@@ -1,0 +1,274 @@
+// Mesh visibility: vertex projection, 16x16 tile binning and the per-pixel
+// nearest-triangle z-buffer (gmesh README, "Design Details > Mesh rasterizer",
+// step 1, and the near-plane rule).
+//
+// Decisions here must be reproducible bit for bit: vertex projection runs in fp32
+// in the written order with no contraction, edge functions and depth in fp64.
+#pragma clang fp contract(off)
+
+#include "gm_internal.h"
+
+namespace gm {
+
+constexpr int ZB_THREADS = 256;  // one thread per pixel of a 16x16 tile
+constexpr int ZB_BATCH = 128;    // triangles staged in LDS per round
+
+__global__ void k_fill_i32(int32_t* __restrict__ p, int64_t n, int32_t v)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// vscreen = (u, v, z_c) planes: x_c = ((R0 x + R1 y) + R2 z) + t0, u = (fx x_c)/z_c + cx.
+__global__ void k_project_vertices(DevCamera cam, int V, const float* __restrict__ verts,
+                                   float* __restrict__ vscreen)
+{
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= V) return;
+    const float x = verts[i], y = verts[V + i], z = verts[2 * V + i];
+    const float xc = ((cam.R[0] * x + cam.R[1] * y) + cam.R[2] * z) + cam.t[0];
+    const float yc = ((cam.R[3] * x + cam.R[4] * y) + cam.R[5] * z) + cam.t[1];
+    const float zc = ((cam.R[6] * x + cam.R[7] * y) + cam.R[8] * z) + cam.t[2];
+    vscreen[i] = (cam.fx * xc) / zc + cam.cx;
+    vscreen[V + i] = (cam.fy * yc) / zc + cam.cy;
+    vscreen[2 * V + i] = zc;
+}
+
+// Tile rectangle (inclusive) of a face's pixel-centre bounding box, or false.
+__device__ inline bool face_tile_rect(const DevCamera& cam, int V, int F, int f,
+                                      const int32_t* __restrict__ faces,
+                                      const uint8_t* __restrict__ mask,
+                                      const float* __restrict__ vs, int* r)
+{
+    if (mask && !mask[f]) return false;
+    double u[3], v[3];
+    for (int k = 0; k < 3; ++k) {
+        const int vi = faces[k * F + f];
+        u[k] = (double)vs[vi];
+        v[k] = (double)vs[V + vi];
+        if (!(vs[2 * V + vi] >= cam.near_z)) return false;  // near plane: skip
+    }
+    const double A = (u[1] - u[0]) * (v[2] - v[0]) - (v[1] - v[0]) * (u[2] - u[0]);
+    if (!(A != 0.0)) return false;
+    const double umin = fmin(fmin(u[0], u[1]), u[2]), umax = fmax(fmax(u[0], u[1]), u[2]);
+    const double vmin = fmin(fmin(v[0], v[1]), v[2]), vmax = fmax(fmax(v[0], v[1]), v[2]);
+    const double a = fmax(ceil(umin - 0.5), 0.0), b = fmin(floor(umax - 0.5), (double)(cam.width - 1));
+    const double c = fmax(ceil(vmin - 0.5), 0.0), d = fmin(floor(vmax - 0.5), (double)(cam.height - 1));
+    if (!(a <= b) || !(c <= d)) return false;
+    r[0] = (int)a / GM_TILE;
+    r[1] = (int)c / GM_TILE;
+    r[2] = (int)b / GM_TILE;
+    r[3] = (int)d / GM_TILE;
+    return true;
+}
+
+__global__ void k_bin_count(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
+                            const uint8_t* __restrict__ mask, const float* __restrict__ vs,
+                            int2* __restrict__ face_rect, int32_t* __restrict__ tile_cnt)
+{
+    const int f = blockIdx.x * blockDim.x + threadIdx.x;
+    if (f >= F) return;
+    int r[4];
+    if (!face_tile_rect(cam, V, F, f, faces, mask, vs, r)) {
+        face_rect[f] = make_int2(1, 0);  // empty: x0 > x1
+        return;
+    }
+    face_rect[f] = make_int2(r[0] | (r[1] << 16), r[2] | (r[3] << 16));
+    for (int ty = r[1]; ty <= r[3]; ++ty)
+        for (int tx = r[0]; tx <= r[2]; ++tx) atomicAdd(&tile_cnt[ty * cam.tx + tx], 1);
+}
+
+__global__ void k_bin_scatter(DevCamera cam, int F, const int2* __restrict__ face_rect,
+                              const int32_t* __restrict__ tile_off, int32_t* __restrict__ cursor,
+                              int32_t* __restrict__ tile_tris)
+{
+    const int f = blockIdx.x * blockDim.x + threadIdx.x;
+    if (f >= F) return;
+    const int2 pr = face_rect[f];
+    const int x0 = pr.x & 0xffff, y0 = pr.x >> 16, x1 = pr.y & 0xffff, y1 = pr.y >> 16;
+    if (pr.x == 1 && pr.y == 0) return;
+    for (int ty = y0; ty <= y1; ++ty)
+        for (int tx = x0; tx <= x1; ++tx) {
+            const int t = ty * cam.tx + tx;
+            const int pos = atomicAdd(&cursor[t], 1);
+            tile_tris[tile_off[t] + pos] = f;
+        }
+}
+
+// One block per tile, one thread per pixel.  Triangles of the tile's bin are set up
+// in fp64 by one thread each and staged in LDS; every pixel then tests the batch.
+__global__ void __launch_bounds__(ZB_THREADS)
+k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
+          const float* __restrict__ vs, const int32_t* __restrict__ tile_off,
+          const int32_t* __restrict__ tile_tris, int32_t* __restrict__ face_id,
+          float* __restrict__ depth, float* __restrict__ tile_dmax)
+{
+    __shared__ double s_u[3][ZB_BATCH], s_v[3][ZB_BATCH], s_z[3][ZB_BATCH];
+    __shared__ double s_du[3][ZB_BATCH], s_dv[3][ZB_BATCH], s_A[ZB_BATCH];
+    __shared__ int s_f[ZB_BATCH];
+    __shared__ float s_red[ZB_THREADS / 64];
+
+    const int tile = blockIdx.x;
+    const int tx = tile % cam.tx, ty = tile / cam.tx;
+    const int px = tx * GM_TILE + (threadIdx.x & 15), py = ty * GM_TILE + (threadIdx.x >> 4);
+    const bool inside = px < cam.width && py < cam.height;
+    const double pu = px + 0.5, pv = py + 0.5;
+    const int start = tile_off[tile], end = tile_off[tile + 1];
+
+    double best = INFINITY;
+    int bid = -1;
+    for (int b0 = start; b0 < end; b0 += ZB_BATCH) {
+        const int nb = min(ZB_BATCH, end - b0);
+        __syncthreads();
+        if (threadIdx.x < nb) {
+            const int f = tile_tris[b0 + threadIdx.x];
+            const int j = threadIdx.x;
+            double u[3], v[3];
+            for (int k = 0; k < 3; ++k) {
+                const int vi = faces[k * F + f];
+                u[k] = (double)vs[vi];
+                v[k] = (double)vs[V + vi];
+                s_u[k][j] = u[k];
+                s_v[k][j] = v[k];
+                s_z[k][j] = (double)vs[2 * V + vi];
+            }
+            // edges (v1,v2), (v2,v0), (v0,v1): a = ea[k], b = eb[k]
+            s_du[0][j] = u[2] - u[1];
+            s_dv[0][j] = v[2] - v[1];
+            s_du[1][j] = u[0] - u[2];
+            s_dv[1][j] = v[0] - v[2];
+            s_du[2][j] = u[1] - u[0];
+            s_dv[2][j] = v[1] - v[0];
+            s_A[j] = (u[1] - u[0]) * (v[2] - v[0]) - (v[1] - v[0]) * (u[2] - u[0]);
+            s_f[j] = f;
+        }
+        __syncthreads();
+        for (int j = 0; j < nb; ++j) {
+            // E_k = (b.u - a.u)(p.v - a.v) - (b.v - a.v)(p.u - a.u)
+            const double E0 = s_du[0][j] * (pv - s_v[1][j]) - s_dv[0][j] * (pu - s_u[1][j]);
+            const double E1 = s_du[1][j] * (pv - s_v[2][j]) - s_dv[1][j] * (pu - s_u[2][j]);
+            const double E2 = s_du[2][j] * (pv - s_v[0][j]) - s_dv[2][j] * (pu - s_u[0][j]);
+            const double A = s_A[j];
+            const bool cov = A > 0 ? (E0 >= 0 && E1 >= 0 && E2 >= 0) : (E0 <= 0 && E1 <= 0 && E2 <= 0);
+            if (!cov) continue;
+            const double l0 = E0 / A, l1 = E1 / A, l2 = E2 / A;
+            const double inv = (l0 / s_z[0][j] + l1 / s_z[1][j]) + l2 / s_z[2][j];
+            const double z = 1.0 / inv;
+            const int f = s_f[j];
+            if (z < best || (z == best && f < bid)) {
+                best = z;
+                bid = f;
+            }
+        }
+    }
+    const float d = bid >= 0 ? (float)best : INFINITY;
+    if (inside) {
+        face_id[py * cam.width + px] = bid;
+        depth[py * cam.width + px] = d;
+    }
+    // tile_dmax: max depth over in-image pixels, +inf when any of them is empty
+    float m = inside ? d : -INFINITY;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float r = s_red[0];
+        for (int w = 1; w < ZB_THREADS / 64; ++w) r = fmaxf(r, s_red[w]);
+        tile_dmax[tile] = r;  // an empty pixel has depth +inf, so the max is +inf
+    }
+}
+
+}  // namespace gm
+
+using namespace gm;
+
+extern "C" {
+
+size_t gm_bin_triangles_ws(int32_t V, int32_t F, int32_t width, int32_t height)
+{
+    (void)V;
+    const int64_t T = div_up(width, GM_TILE) * div_up(height, GM_TILE);
+    size_t b = 0;
+    b += align_up(sizeof(int2) * (size_t)(F > 0 ? F : 1), 256);   // face rects
+    b += align_up(sizeof(int32_t) * (size_t)T, 256);               // tile counts
+    b += align_up(sizeof(int32_t) * (size_t)T, 256);               // cursors
+    b += align_up(sizeof(long long), 256);                         // total
+    b += scan_ws_bytes(T);
+    return b;
+}
+
+gm_status gm_bin_triangles(const gm_camera* cam, const gm_mesh* mesh, float* vscreen,
+                           int32_t* tile_offsets, int32_t* tile_tris, int64_t cap, int64_t* n_pairs,
+                           void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    if (gm_status s = check_camera(cam)) return s;
+    GM_ARG_CHECK(mesh != nullptr, "mesh is NULL");
+    GM_ARG_CHECK(mesh->V >= 0 && mesh->F >= 0, "negative mesh size");
+    GM_ARG_CHECK(mesh->V == 0 || (mesh->verts && vscreen), "verts / vscreen is NULL");
+    GM_ARG_CHECK(mesh->F == 0 || mesh->faces, "faces is NULL");
+    GM_ARG_CHECK(tile_offsets && n_pairs && ws, "tile_offsets / n_pairs / ws is NULL");
+    GM_ARG_CHECK(cap >= 0 && (cap == 0 || tile_tris), "tile_tris is NULL or cap negative");
+    const size_t need = gm_bin_triangles_ws(mesh->V, mesh->F, cam->width, cam->height);
+    GM_ARG_CHECK(ws_bytes >= need, "workspace %zu bytes, %zu needed", ws_bytes, need);
+
+    const DevCamera dc = dev_camera(*cam);
+    const int64_t T = (int64_t)dc.tx * dc.ty;
+    const int V = mesh->V, F = mesh->F;
+    char* w = (char*)ws;
+    int2* face_rect = (int2*)w;
+    w += align_up(sizeof(int2) * (size_t)(F > 0 ? F : 1), 256);
+    int32_t* tile_cnt = (int32_t*)w;
+    w += align_up(sizeof(int32_t) * (size_t)T, 256);
+    int32_t* cursor = (int32_t*)w;
+    w += align_up(sizeof(int32_t) * (size_t)T, 256);
+    long long* total = (long long*)w;
+    w += align_up(sizeof(long long), 256);
+    void* scan_ws = w;
+
+    k_fill_i32<<<(unsigned)div_up(2 * T + 64, 256), 256, 0, stream>>>(tile_cnt, (cursor - tile_cnt) + T, 0);
+    GM_LAUNCH_CHECK();
+    if (V > 0) {
+        k_project_vertices<<<(unsigned)div_up(V, 256), 256, 0, stream>>>(dc, V, mesh->verts, vscreen);
+        GM_LAUNCH_CHECK();
+    }
+    if (F > 0) {
+        k_bin_count<<<(unsigned)div_up(F, 256), 256, 0, stream>>>(dc, V, F, mesh->faces, mesh->face_mask,
+                                                                 vscreen, face_rect, tile_cnt);
+        GM_LAUNCH_CHECK();
+    }
+    if (gm_status s = exclusive_scan(tile_cnt, tile_offsets, T, total, scan_ws, stream)) return s;
+    int64_t n = 0;
+    if (gm_status s = read_back_i64(total, &n, stream)) return s;
+    *n_pairs = n;
+    if (n > cap || n > INT32_MAX) {
+        set_error("tile_tris capacity %lld, %lld pairs needed", (long long)cap, (long long)n);
+        return GM_ERR_CAPACITY;
+    }
+    if (F > 0 && n > 0) {
+        k_bin_scatter<<<(unsigned)div_up(F, 256), 256, 0, stream>>>(dc, F, face_rect, tile_offsets, cursor,
+                                                                   tile_tris);
+        GM_LAUNCH_CHECK();
+    }
+    return GM_OK;
+}
+
+gm_status gm_raster_zbuffer(const gm_camera* cam, const gm_mesh* mesh, const float* vscreen,
+                            const int32_t* tile_offsets, const int32_t* tile_tris, int32_t* face_id,
+                            float* depth, float* tile_dmax, hipStream_t stream)
+{
+    clear_error();
+    if (gm_status s = check_camera(cam)) return s;
+    GM_ARG_CHECK(mesh != nullptr, "mesh is NULL");
+    GM_ARG_CHECK(face_id && depth && tile_dmax && tile_offsets, "an output or tile_offsets is NULL");
+    GM_ARG_CHECK(mesh->F == 0 || (mesh->faces && vscreen && tile_tris), "faces / vscreen / tile_tris is NULL");
+    const DevCamera dc = dev_camera(*cam);
+    const int64_t T = (int64_t)dc.tx * dc.ty;
+    k_zbuffer<<<(unsigned)T, ZB_THREADS, 0, stream>>>(dc, mesh->V, mesh->F, mesh->faces, vscreen,
+                                                     tile_offsets, tile_tris, face_id, depth, tile_dmax);
+    GM_LAUNCH_CHECK();
+    return GM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,365 @@
+// Per-tile Gaussian lists in centre-depth order with the occlusion cull
+// (gmesh README, "Design Details > Hybrid rendering": composited "in the usual
+// sorted 3DGS order"; cull_occluded drops Gaussians certainly hidden behind the
+// mesh in fully covered 16x16 tiles without changing the result).
+//
+// Strategy: stable LSD radix sort of the visible Gaussians by the bits of their
+// fp32 depth (ties keep id order), one pass that counts the surviving tiles of
+// every Gaussian in that order, a scan, one pass that emits (tile, id) pairs in
+// that order, and a stable LSD radix sort of the pairs by tile.  Stability keeps
+// every tile's list in (depth, id) order.  The radix passes rank keys inside a
+// block with wave64 ballots (8 ballots give each lane the mask of lanes holding
+// the same digit), so the scatter is stable without any sorting network.
+#include <algorithm>
+
+#include "gm_internal.h"
+
+namespace gm {
+
+constexpr int RS_THREADS = 256;
+constexpr int RS_ITEMS = 16;
+constexpr int RS_CHUNK = RS_THREADS * RS_ITEMS;  // keys per block
+constexpr int RS_RADIX = 256;
+
+__global__ void k_fill_i32s(int32_t* __restrict__ p, int64_t n, int32_t v)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+// stable LSD radix sort pass
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(RS_THREADS)
+k_radix_hist(const uint32_t* __restrict__ keys, const long long* __restrict__ d_count, int shift,
+             int nblocks, int32_t* __restrict__ hist)
+{
+    __shared__ int32_t h[RS_RADIX];
+    const long long n = *d_count;
+    h[threadIdx.x] = 0;
+    __syncthreads();
+    const long long base = (long long)blockIdx.x * RS_CHUNK;
+#pragma unroll 4
+    for (int k = 0; k < RS_ITEMS; ++k) {
+        const long long e = base + (long long)k * RS_THREADS + threadIdx.x;
+        if (e < n) atomicAdd(&h[(keys[e] >> shift) & 0xff], 1);
+    }
+    __syncthreads();
+    hist[threadIdx.x * nblocks + blockIdx.x] = h[threadIdx.x];
+}
+
+__global__ void __launch_bounds__(RS_THREADS)
+k_radix_scatter(const uint32_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
+                const long long* __restrict__ d_count, int shift, int nblocks,
+                const int32_t* __restrict__ offs, uint32_t* __restrict__ keys_out,
+                int32_t* __restrict__ vals_out)
+{
+    __shared__ int32_t s_base[RS_RADIX];            // global start of each digit for this block
+    __shared__ int32_t s_wcnt[RS_THREADS / 64][RS_RADIX];
+    const long long n = *d_count;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    s_base[threadIdx.x] = offs[threadIdx.x * nblocks + blockIdx.x];
+    const long long base = (long long)blockIdx.x * RS_CHUNK;
+    for (int k = 0; k < RS_ITEMS; ++k) {
+        const long long e = base + (long long)k * RS_THREADS + threadIdx.x;
+        const bool act = e < n;
+        uint32_t key = 0;
+        int32_t val = 0;
+        if (act) {
+            key = keys_in[e];
+            val = vals_in[e];
+        }
+        const int d = (key >> shift) & 0xff;
+        for (int w = 0; w < RS_THREADS / 64; ++w) s_wcnt[w][threadIdx.x] = 0;
+        __syncthreads();
+        // lanes holding the same digit
+        unsigned long long peers = __ballot(act);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const bool bit = (d >> b) & 1;
+            const unsigned long long bb = __ballot(bit);
+            peers &= bit ? bb : ~bb;
+        }
+        const int rank = __popcll(peers & lt);
+        if (act && rank == 0) s_wcnt[wave][d] = __popcll(peers);
+        __syncthreads();
+        if (act) {
+            int pos = s_base[d] + rank;
+            for (int w = 0; w < wave; ++w) pos += s_wcnt[w][d];
+            keys_out[pos] = key;
+            vals_out[pos] = val;
+        }
+        __syncthreads();
+        int add = 0;
+        for (int w = 0; w < RS_THREADS / 64; ++w) add += s_wcnt[w][threadIdx.x];
+        s_base[threadIdx.x] += add;
+        __syncthreads();
+    }
+}
+
+size_t radix_ws_bytes(int64_t n)
+{
+    const int64_t nb = div_up(n > 0 ? n : 1, RS_CHUNK);
+    return 2 * align_up(sizeof(int32_t) * (size_t)(RS_RADIX * nb + 1), 256) + scan_ws_bytes(RS_RADIX * nb) +
+           align_up(sizeof(long long), 256);
+}
+
+// Sorts n_max-bounded (keys, vals) by key bits [lo_bit, hi_bit) with LSD passes of 8
+// bits; the live count is *d_count (device).  Ping-pongs between (ka, va) and
+// (kb, vb); the result lands in (k_out, v_out), which must be one of the two pairs'
+// buffers chosen by the caller so that the final pass writes there.
+static gm_status radix_sort(uint32_t* ka, int32_t* va, uint32_t* kb, int32_t* vb, int npass, int lo_bit,
+                            const long long* d_count, int64_t n_max, void* ws, hipStream_t stream)
+{
+    const int nb = (int)div_up(n_max > 0 ? n_max : 1, RS_CHUNK);
+    char* w = (char*)ws;
+    int32_t* hist = (int32_t*)w;
+    w += align_up(sizeof(int32_t) * (size_t)(RS_RADIX * nb + 1), 256);
+    int32_t* offs = (int32_t*)w;
+    w += align_up(sizeof(int32_t) * (size_t)(RS_RADIX * nb + 1), 256);
+    long long* tot = (long long*)w;
+    w += align_up(sizeof(long long), 256);
+    void* scan_ws = w;
+    uint32_t* kin = ka;
+    int32_t* vin = va;
+    uint32_t* kout = kb;
+    int32_t* vout = vb;
+    for (int p = 0; p < npass; ++p) {
+        const int shift = lo_bit + 8 * p;
+        k_radix_hist<<<nb, RS_THREADS, 0, stream>>>(kin, d_count, shift, nb, hist);
+        GM_LAUNCH_CHECK();
+        if (gm_status s = exclusive_scan(hist, offs, (int64_t)RS_RADIX * nb, tot, scan_ws, stream)) return s;
+        k_radix_scatter<<<nb, RS_THREADS, 0, stream>>>(kin, vin, d_count, shift, nb, offs, kout, vout);
+        GM_LAUNCH_CHECK();
+        uint32_t* tk = kin;
+        int32_t* tv = vin;
+        kin = kout;
+        vin = vout;
+        kout = tk;
+        vout = tv;
+    }
+    return GM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// visible Gaussians, depth keys
+// ---------------------------------------------------------------------------
+__global__ void k_visible_flags(int N, const float* __restrict__ rec, int32_t* __restrict__ flag)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= N) return;
+    flag[i] = __float_as_int(rec[(size_t)i * GM_REC + 15]) > 0 ? 1 : 0;
+}
+
+__global__ void k_visible_compact(int N, const float* __restrict__ rec, const int32_t* __restrict__ flag,
+                                  const int32_t* __restrict__ pos, uint32_t* __restrict__ keys,
+                                  int32_t* __restrict__ vals)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= N || !flag[i]) return;
+    const int p = pos[i];
+    keys[p] = __float_as_uint(rec[(size_t)i * GM_REC + 9]);  // z_c > 0: bits order like values
+    vals[p] = i;
+}
+
+// ---------------------------------------------------------------------------
+// occlusion cull (fp32); identical code in the counting and the emitting pass
+// ---------------------------------------------------------------------------
+struct CullParams {
+    const float* tile_dmax;  // nullptr: no culling
+    float softness;
+};
+
+__device__ inline bool culled(const DevCamera& cam, const CullParams& cp, int tx, int ty, float u, float v,
+                              float zc, float g0, float g1, float sig, float o)
+{
+    if (!cp.tile_dmax) return false;
+    const float dmax = cp.tile_dmax[ty * cam.tx + tx];
+    if (!(dmax < INFINITY)) return false;
+    const float xa = tx * GM_TILE + 0.5f, ya = ty * GM_TILE + 0.5f;
+    const float xb = (float)min((tx + 1) * GM_TILE, cam.width) - 0.5f;
+    const float yb = (float)min((ty + 1) * GM_TILE, cam.height) - 0.5f;
+    const float ax = g0 * (xa - u), bx = g0 * (xb - u);
+    const float ay = g1 * (ya - v), by = g1 * (yb - v);
+    const float zmin = zc + (fminf(ax, bx) + fminf(ay, by));
+    const float lim = dmax + 1e-5f * fabsf(dmax);
+    const float amax = fminf(o, 0.99f);
+    float bound;
+    if (cp.softness > 0.0f) {
+        const float s = (lim - zmin) / (sig * cp.softness);
+        bound = amax * (0.5f * erfcf(-s * 0.70710678118654752f));
+    } else {
+        bound = zmin < lim ? amax : 0.0f;
+    }
+    return bound < (1.0f / 255.0f) * (1.0f - 1e-3f);
+}
+
+__global__ void __launch_bounds__(256)
+k_count_pairs(DevCamera cam, CullParams cp, const long long* __restrict__ d_nvis, int N,
+              const int32_t* __restrict__ order, const float* __restrict__ rec, int32_t* __restrict__ cnt)
+{
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= N) return;
+    if (j >= *d_nvis) {
+        cnt[j] = 0;
+        return;
+    }
+    const int i = order[j];
+    const float4* r = reinterpret_cast<const float4*>(rec + (size_t)i * GM_REC);
+    const float4 a = r[0], b = r[1], c = r[2], d = r[3];
+    const int lo = __float_as_int(d.y), hi = __float_as_int(d.z);
+    const int x0 = lo & 0xffff, y0 = lo >> 16, x1 = hi & 0xffff, y1 = hi >> 16;
+    int n = 0;
+    for (int ty = y0; ty < y1; ++ty)
+        for (int tx = x0; tx < x1; ++tx)
+            n += culled(cam, cp, tx, ty, a.x, a.y, c.y, c.z, c.w, d.x, b.y) ? 0 : 1;
+    cnt[j] = n;
+}
+
+__global__ void __launch_bounds__(256)
+k_emit_pairs(DevCamera cam, CullParams cp, const long long* __restrict__ d_nvis,
+             const int32_t* __restrict__ order, const float* __restrict__ rec,
+             const int32_t* __restrict__ off, uint32_t* __restrict__ tkeys, int32_t* __restrict__ tvals)
+{
+    const int j = blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= *d_nvis) return;
+    const int i = order[j];
+    const float4* r = reinterpret_cast<const float4*>(rec + (size_t)i * GM_REC);
+    const float4 a = r[0], b = r[1], c = r[2], d = r[3];
+    const int lo = __float_as_int(d.y), hi = __float_as_int(d.z);
+    const int x0 = lo & 0xffff, y0 = lo >> 16, x1 = hi & 0xffff, y1 = hi >> 16;
+    int p = off[j];
+    const int pend = off[j + 1];  // the counting pass took the same decisions; never write past it
+    for (int ty = y0; ty < y1; ++ty)
+        for (int tx = x0; tx < x1; ++tx) {
+            if (culled(cam, cp, tx, ty, a.x, a.y, c.y, c.z, c.w, d.x, b.y)) continue;
+            if (p >= pend) return;
+            tkeys[p] = (uint32_t)(ty * cam.tx + tx);
+            tvals[p] = i;
+            ++p;
+        }
+}
+
+__global__ void k_tile_ranges(const uint32_t* __restrict__ keys, int64_t K, int32_t* __restrict__ ranges)
+{
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= K) return;
+    const uint32_t t = keys[k];
+    if (k == 0 || keys[k - 1] != t) ranges[2 * t] = (int32_t)k;
+    if (k == K - 1 || keys[k + 1] != t) ranges[2 * t + 1] = (int32_t)(k + 1);
+}
+
+__global__ void k_store_count(long long* __restrict__ dst, int64_t v) { *dst = v; }
+
+struct SortWs {
+    int32_t *flag, *pos;
+    uint32_t *dka, *dkb;
+    int32_t *dva, *dvb;
+    uint32_t *tka, *tkb;
+    int32_t* tva;
+    long long *nvis, *npairs;
+    void* aux;  // scans and radix histograms
+};
+
+static size_t sort_layout(int64_t N, int64_t cap, int64_t T, char* base, SortWs* w)
+{
+    const int64_t n1 = N > 0 ? N : 1, c1 = cap > 0 ? cap : 1;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        char* p = base ? base + o : nullptr;
+        o += align_up(bytes, 256);
+        return p;
+    };
+    SortWs s;
+    s.flag = (int32_t*)take(4 * n1);
+    s.pos = (int32_t*)take(4 * (n1 + 1));
+    s.dka = (uint32_t*)take(4 * n1);
+    s.dkb = (uint32_t*)take(4 * n1);
+    s.dva = (int32_t*)take(4 * n1);
+    s.dvb = (int32_t*)take(4 * n1);
+    s.tka = (uint32_t*)take(4 * c1);
+    s.tkb = (uint32_t*)take(4 * c1);
+    s.tva = (int32_t*)take(4 * c1);
+    s.nvis = (long long*)take(8);
+    s.npairs = (long long*)take(8);
+    const int64_t m = std::max<int64_t>(std::max<int64_t>(n1, c1), T);
+    s.aux = take(std::max(radix_ws_bytes(m), scan_ws_bytes(m)));
+    if (w) *w = s;
+    return o;
+}
+
+}  // namespace gm
+
+using namespace gm;
+
+extern "C" {
+
+size_t gm_sort_tile_keys_ws(int32_t N, int64_t cap, int32_t width, int32_t height)
+{
+    const int64_t T = div_up(width, GM_TILE) * div_up(height, GM_TILE);
+    return sort_layout(N, cap, T, nullptr, nullptr);
+}
+
+gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec, const float* tile_dmax,
+                            float softness, int32_t* tile_ranges, int32_t* sorted_ids, int64_t cap,
+                            int64_t* n_keys, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    if (gm_status s = check_camera(cam)) return s;
+    GM_ARG_CHECK(N >= 0, "N = %d is negative", N);
+    GM_ARG_CHECK(softness >= 0.0f, "softness must be >= 0");
+    GM_ARG_CHECK(tile_ranges && n_keys && ws, "tile_ranges / n_keys / ws is NULL");
+    GM_ARG_CHECK(N == 0 || rec, "rec is NULL");
+    GM_ARG_CHECK(cap >= 0 && (cap == 0 || sorted_ids), "sorted_ids is NULL or cap negative");
+    const DevCamera dc = dev_camera(*cam);
+    const int64_t T = (int64_t)dc.tx * dc.ty;
+    const size_t need = sort_layout(N, cap, T, nullptr, nullptr);
+    GM_ARG_CHECK(ws_bytes >= need, "workspace %zu bytes, %zu needed", ws_bytes, need);
+    SortWs w;
+    sort_layout(N, cap, T, (char*)ws, &w);
+
+    k_fill_i32s<<<(unsigned)div_up(2 * T, 256), 256, 0, stream>>>(tile_ranges, 2 * T, 0);
+    GM_LAUNCH_CHECK();
+    if (N == 0) {
+        *n_keys = 0;
+        return GM_OK;
+    }
+    const unsigned gN = (unsigned)div_up(N, 256);
+    // 1. visible Gaussians in id order, then stable sort by depth bits
+    k_visible_flags<<<gN, 256, 0, stream>>>(N, rec, w.flag);
+    GM_LAUNCH_CHECK();
+    if (gm_status s = exclusive_scan(w.flag, w.pos, N, w.nvis, w.aux, stream)) return s;
+    k_visible_compact<<<gN, 256, 0, stream>>>(N, rec, w.flag, w.pos, w.dka, w.dva);
+    GM_LAUNCH_CHECK();
+    if (gm_status s = radix_sort(w.dka, w.dva, w.dkb, w.dvb, 4, 0, w.nvis, N, w.aux, stream)) return s;
+    const int32_t* order = w.dva;  // 4 passes: back in the first buffer pair
+    // 2. surviving tiles per Gaussian (depth order), scan, read back the total
+    CullParams cp{tile_dmax, softness};
+    k_count_pairs<<<gN, 256, 0, stream>>>(dc, cp, w.nvis, N, order, rec, w.flag);
+    GM_LAUNCH_CHECK();
+    if (gm_status s = exclusive_scan(w.flag, w.pos, N, w.npairs, w.aux, stream)) return s;
+    int64_t K = 0;
+    if (gm_status s = read_back_i64(w.npairs, &K, stream)) return s;
+    *n_keys = K;
+    if (K > cap || K > INT32_MAX) {
+        set_error("sorted_ids capacity %lld, %lld keys needed", (long long)cap, (long long)K);
+        return GM_ERR_CAPACITY;
+    }
+    if (K == 0) return GM_OK;
+    // 3. emit (tile, id) in depth order; 4. stable sort by tile
+    int npass = 1;
+    while (npass < 4 && (T - 1) >> (8 * npass)) ++npass;
+    uint32_t* ka = w.tka;
+    int32_t* va = (npass % 2 == 0) ? sorted_ids : w.tva;
+    int32_t* vb = (npass % 2 == 0) ? w.tva : sorted_ids;
+    k_emit_pairs<<<gN, 256, 0, stream>>>(dc, cp, w.nvis, order, rec, w.pos, ka, va);
+    GM_LAUNCH_CHECK();
+    if (gm_status s = radix_sort(ka, va, w.tkb, vb, npass, 0, w.npairs, K, w.aux, stream)) return s;
+    const uint32_t* kfin = (npass % 2 == 0) ? w.tka : w.tkb;
+    k_tile_ranges<<<(unsigned)div_up(K, 256), 256, 0, stream>>>(kfin, K, tile_ranges);
+    GM_LAUNCH_CHECK();
+    return GM_OK;
+}
+
+}  // extern "C"

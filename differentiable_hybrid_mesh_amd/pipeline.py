@@ -1,0 +1,196 @@
+"""Buffer management around the six C-ABI calls (allocation and call order only).
+
+``DeviceScene`` uploads a scene's arrays to the GPU once.  ``Renderer`` owns the
+per-view device buffers (torch tensors used as plain device memory), grows the two
+variable-length lists on GM_ERR_CAPACITY, and runs
+
+    gm_bin_triangles -> gm_raster_zbuffer -> gm_project_gaussians ->
+    gm_sort_tile_keys -> gm_composite_hybrid_fwd   (forward)
+    gm_composite_hybrid_bwd                          (backward)
+
+on the current torch stream.  Every step of the path runs in libgm's kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib as G
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_camera(width, height, fx, fy, cx, cy, R, t, near_z=0.01) -> G.GmCamera:
+    cam = G.GmCamera()
+    cam.width, cam.height = int(width), int(height)
+    cam.fx, cam.fy, cam.cx, cam.cy = float(fx), float(fy), float(cx), float(cy)
+    R = np.asarray(R, np.float32).reshape(-1)
+    t = np.asarray(t, np.float32).reshape(-1)
+    for i in range(9):
+        cam.R[i] = float(R[i])
+    for i in range(3):
+        cam.t[i] = float(t[i])
+    cam.near_z = float(near_z)
+    return cam
+
+
+def make_light(light: Optional[dict]) -> Optional[G.GmLight]:
+    if light is None:
+        return None
+    L = G.GmLight()
+    for i in range(3):
+        L.pos[i] = float(light["pos"][i])
+        L.ambient[i] = float(light["ambient"][i])
+        L.diffuse[i] = float(light["diffuse"][i])
+        L.specular[i] = float(light["specular"][i])
+    L.shininess = float(light["shininess"])
+    return L
+
+
+class DeviceScene:
+    """A scene's inputs resident in GPU memory (SoA planes, as the ABI takes them)."""
+
+    def __init__(self, scene, device: str = "cuda"):
+        self.scene = scene
+        self.device = device
+
+        def up(a):
+            return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+        self.verts, self.faces, self.face_mask = up(scene.verts), up(scene.faces), up(scene.face_mask)
+        self.vcolor, self.vnormal = up(scene.vcolor), up(scene.vnormal)
+        self.uv, self.faces_uv, self.texture = up(scene.uv), up(scene.faces_uv), up(scene.texture)
+        self.means, self.quats, self.scales = up(scene.means), up(scene.quats), up(scene.scales)
+        self.opacity, self.sh = up(scene.opacity), up(scene.sh)
+        self.mips = None
+        self.tex_size = 0
+        if self.texture is not None:
+            S = int(scene.texture.shape[0])
+            self.tex_size = S
+            self.mips = torch.empty(G.gm_mipmaps_floats(S), dtype=torch.float32, device=device)
+            G.gm_build_mipmaps(self.texture, S, self.mips, _stream())
+        m = G.GmMesh()
+        m.V, m.F = scene.V, scene.F
+        m.Vt = 0 if scene.uv is None else int(scene.uv.shape[1])
+        m.tex_size = self.tex_size
+        m.verts, m.faces, m.face_mask = G.ptr(self.verts), G.ptr(self.faces), G.ptr(self.face_mask)
+        m.vcolor, m.vnormal = G.ptr(self.vcolor), G.ptr(self.vnormal)
+        m.uv, m.faces_uv, m.mips = G.ptr(self.uv), G.ptr(self.faces_uv), G.ptr(self.mips)
+        self.mesh = m
+        self.light = make_light(scene.light)
+        self.cams = [make_camera(scene.width, scene.height, scene.fx, scene.fy, scene.cx, scene.cy,
+                                 v.R, v.t, scene.near_z) for v in scene.views]
+
+    def grads(self, view: int):
+        g = self.scene.grads[view]
+        return {k: torch.from_numpy(np.ascontiguousarray(v)).to(self.device) for k, v in g.items()}
+
+
+class Renderer:
+    """Per-view device buffers and the call sequence of one forward / backward."""
+
+    def __init__(self, ds: DeviceScene, pair_cap: Optional[int] = None, key_cap: Optional[int] = None):
+        s = ds.scene
+        self.ds = ds
+        dev = ds.device
+        self.W, self.H = s.width, s.height
+        self.T = s.tiles_x * s.tiles_y
+        self.N = s.N
+        i32, f32 = torch.int32, torch.float32
+        self.vscreen = torch.empty((3, max(s.V, 1)), dtype=f32, device=dev)
+        self.tile_offsets = torch.empty(self.T + 1, dtype=i32, device=dev)
+        self.ws_bin = torch.empty(G.gm_bin_triangles_ws(s.V, s.F, s.width, s.height), dtype=torch.uint8,
+                                  device=dev)
+        self.pair_cap = pair_cap if pair_cap is not None else 4 * s.F + 1024
+        self.tile_tris = torch.empty(max(self.pair_cap, 1), dtype=i32, device=dev)
+        self.face_id = torch.empty((self.H, self.W), dtype=i32, device=dev)
+        self.depth = torch.empty((self.H, self.W), dtype=f32, device=dev)
+        self.tile_dmax = torch.empty(self.T, dtype=f32, device=dev)
+        self.rec = torch.empty((max(self.N, 1), G.GM_REC), dtype=f32, device=dev)
+        self.tile_ranges = torch.empty((self.T, 2), dtype=i32, device=dev)
+        self.key_cap = key_cap if key_cap is not None else 8 * self.N + 1024
+        self._alloc_keys(self.key_cap)
+        self.out_rgb = torch.empty((self.H, self.W, 3), dtype=f32, device=dev)
+        self.out_depth = torch.empty((self.H, self.W), dtype=f32, device=dev)
+        self.out_alpha = torch.empty((self.H, self.W), dtype=f32, device=dev)
+        self.state_T = torch.empty((self.H, self.W), dtype=f32, device=dev)
+        self.state_last = torch.empty((self.H, self.W), dtype=i32, device=dev)
+        self.g_rec = torch.empty((max(self.N, 1), G.GM_GRAD), dtype=f32, device=dev)
+        self.g_mesh_rgb = torch.empty((self.H, self.W, 3), dtype=f32, device=dev)
+        self.g_mesh_depth = torch.empty((self.H, self.W), dtype=f32, device=dev)
+        self.n_pairs = 0
+        self.n_keys = 0
+        self.view = 0
+        self.cull = True
+
+    def _alloc_keys(self, cap):
+        s = self.ds.scene
+        self.key_cap = int(cap)
+        self.sorted_ids = torch.empty(max(self.key_cap, 1), dtype=torch.int32, device=self.ds.device)
+        self.ws_sort = torch.empty(G.gm_sort_tile_keys_ws(self.N, self.key_cap, s.width, s.height),
+                                   dtype=torch.uint8, device=self.ds.device)
+
+    # -- the six calls ---------------------------------------------------------
+    def bin_and_zbuffer(self, view: int):
+        ds, cam, st = self.ds, self.ds.cams[view], _stream()
+        while True:
+            status, n = G.gm_bin_triangles(cam, ds.mesh, self.vscreen, self.tile_offsets, self.tile_tris,
+                                           self.pair_cap, self.ws_bin, st)
+            if status == G.GM_OK:
+                break
+            self.pair_cap = int(n * 1.25) + 1024
+            self.tile_tris = torch.empty(self.pair_cap, dtype=torch.int32, device=ds.device)
+        self.n_pairs = n
+        G.gm_raster_zbuffer(cam, ds.mesh, self.vscreen, self.tile_offsets, self.tile_tris, self.face_id,
+                            self.depth, self.tile_dmax, st)
+
+    def project(self, view: int):
+        ds, s = self.ds, self.ds.scene
+        G.gm_project_gaussians(ds.cams[view], self.N, ds.means, ds.quats, ds.scales, ds.opacity, ds.sh,
+                               s.sh_degree, self.rec, _stream())
+
+    def sort(self, view: int, cull: bool = True):
+        ds, s, st = self.ds, self.ds.scene, _stream()
+        dmax = self.tile_dmax if cull else None
+        while True:
+            status, n = G.gm_sort_tile_keys(ds.cams[view], self.N, self.rec, dmax, s.softness,
+                                            self.tile_ranges, self.sorted_ids, self.key_cap, self.ws_sort, st)
+            if status == G.GM_OK:
+                break
+            self._alloc_keys(int(n * 1.25) + 1024)
+        self.n_keys = n
+
+    def composite_fwd(self, view: int):
+        ds, s = self.ds, self.ds.scene
+        G.gm_composite_hybrid_fwd(ds.cams[view], self.rec, self.tile_ranges, self.sorted_ids, self.face_id,
+                                  self.depth, ds.mesh, self.vscreen, ds.light, s.bg, s.softness, self.out_rgb,
+                                  self.out_depth, self.out_alpha, self.state_T, self.state_last, _stream())
+
+    def composite_bwd(self, view: int, g_rgb, g_depth=None, g_alpha=None):
+        ds, s = self.ds, self.ds.scene
+        G.gm_composite_hybrid_bwd(ds.cams[view], self.N, self.rec, self.tile_ranges, self.sorted_ids,
+                                  self.face_id, self.depth, ds.mesh, self.vscreen, ds.light, s.bg, s.softness,
+                                  self.state_T, self.state_last, g_rgb, g_depth, g_alpha, self.g_rec,
+                                  self.g_mesh_rgb, self.g_mesh_depth, _stream())
+
+    # -- whole passes -----------------------------------------------------------
+    def forward(self, view: int = 0, cull: bool = True):
+        self.view, self.cull = view, cull
+        self.bin_and_zbuffer(view)
+        self.project(view)
+        self.sort(view, cull)
+        self.composite_fwd(view)
+        return {"rgb": self.out_rgb, "depth": self.out_depth, "alpha": self.out_alpha}
+
+    def backward(self, g_rgb, g_depth=None, g_alpha=None):
+        self.composite_bwd(self.view, g_rgb, g_depth, g_alpha)
+        return {"rec": self.g_rec[: self.N], "mesh_rgb": self.g_mesh_rgb, "mesh_depth": self.g_mesh_depth}
+
+    def step(self, view: int, grads: dict, cull: bool = True):
+        """One forward + backward of one view (the benchmark's unit of work)."""
+        self.forward(view, cull)
+        return self.backward(grads["rgb"], grads.get("depth"), grads.get("alpha"))

@@ -1,0 +1,256 @@
+/*
+ * gm.h — C ABI of the MI355X (gfx950) hybrid mesh + 3D Gaussian tile rasterizer.
+ *
+ * The method is the one of the gmesh README ("A Lightweight and Differentiable
+ * Renderer for Joint Mesh and 3D Gaussian Splat Scenes", section "Design Details"):
+ * triangles are binned into 16x16 tiles and a z-buffer finds the nearest triangle
+ * at every pixel centre; 3D Gaussians are projected to 2D conics with an affine
+ * (EWA) model of their depth; Gaussians certainly hidden behind the mesh in fully
+ * covered tiles are culled; the rest are sorted per tile by centre depth and
+ * composited front to back, each one split at the mesh surface by
+ * f = Phi((D - z*(p)) / (sigma softness)), with the mesh colour filling the
+ * remaining transmittance; the backward pass of that composite gives gradients of
+ * every Gaussian record and of the mesh colour and depth.
+ *
+ * Conventions (the README states that meshes and Gaussians share one pinhole
+ * camera and pixel convention; its camera-axes section carries no text, so the
+ * gsplat/OpenCV reading is used):
+ *   x_c = R x_w + t, R row-major; +x right, +y down, +z forward;
+ *   u = fx x_c / z_c + cx, v = fy y_c / z_c + cy;
+ *   pixel (i, j) is column i, row j, with centre (i + 0.5, j + 0.5);
+ *   tiles are 16x16 pixels, TX = ceil(W/16), TY = ceil(H/16), T = TX*TY,
+ *   tile id = ty*TX + tx.
+ *
+ * Memory.  Every array pointer is a DEVICE pointer to caller-owned memory unless
+ * marked (host).  "[k][N]" is k contiguous planes of N values (structure of
+ * arrays).  The library never allocates, frees or keeps a pointer after a call
+ * returns.  Calls are asynchronous on `stream` except where stated: the two calls
+ * that produce a variable-length list read back its length (one small
+ * device-to-host copy and a stream synchronisation).
+ *
+ * Errors.  Every call returns a gm_status.  GM_ERR_ARG: a required pointer is
+ * NULL, a size is negative or out of range, the workspace is too small; checked on
+ * the host before anything is launched.  GM_ERR_CAPACITY: an output list does not
+ * fit; `*n_pairs` / `*n_keys` then hold the size needed and the list outputs are
+ * not written.  GM_ERR_HIP: a HIP call failed.  gm_last_error() returns a
+ * thread-local message for the last non-OK status.  Degenerate data follow rules,
+ * not errors: zero-area triangles cover nothing, Gaussians with det <= 0 or behind
+ * the near plane are not listed, N = 0 and F = 0 are legal.
+ */
+#ifndef GM_H
+#define GM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GM_TILE 16
+/* Floats per projected Gaussian record (64 bytes, see gm_project_gaussians). */
+#define GM_REC 16
+/* Floats per Gaussian gradient record (see gm_composite_hybrid_bwd). */
+#define GM_GRAD 13
+
+typedef enum {
+    GM_OK = 0,
+    GM_ERR_ARG = -1,
+    GM_ERR_CAPACITY = -2,
+    GM_ERR_HIP = -3
+} gm_status;
+
+/* Pinhole camera; passed by host pointer and read at call time. */
+typedef struct gm_camera {
+    int32_t width, height; /* pixels, > 0 */
+    float fx, fy, cx, cy;  /* pixel units */
+    float R[9];            /* world -> camera rotation, row-major */
+    float t[3];            /* world -> camera translation */
+    float near_z;          /* near plane, > 0 (0.01 in every workload) */
+} gm_camera;
+
+/* World-space point light for per-pixel Phong shading of the mesh (README v1.1:
+ * a point light shades the mesh per pixel with interpolated vertex normals and a
+ * specular highlight that follows the camera).  Host pointer; NULL = unlit. */
+typedef struct gm_light {
+    float pos[3];
+    float ambient[3], diffuse[3], specular[3];
+    float shininess;
+} gm_light;
+
+/* Mesh attributes (README "Mesh rasterizer" and v1.1: vertex colours, or a texture
+ * with per-corner texture coordinates as in OBJ files; optional vertex normals for
+ * lighting).  Host pointer to a struct of device pointers; unused ones NULL. */
+typedef struct gm_mesh {
+    int32_t V, F;             /* vertices, faces (>= 0) */
+    int32_t Vt;               /* texture coordinates (0 when untextured) */
+    int32_t tex_size;         /* S: square power-of-two texture side, 0 when untextured */
+    const float* verts;       /* [3][V] world positions */
+    const int32_t* faces;     /* [3][F] vertex ids */
+    const uint8_t* face_mask; /* [F] 0 = triangle absent (stochastic binary opacity), or NULL */
+    const float* vcolor;      /* [3][V] base colour, or NULL */
+    const float* vnormal;     /* [3][V] world normals, or NULL (then unlit) */
+    const float* uv;          /* [2][Vt], or NULL */
+    const int32_t* faces_uv;  /* [3][F] texture-coordinate ids, or NULL */
+    const float* mips;        /* pyramid written by gm_build_mipmaps, or NULL */
+} gm_mesh;
+
+/* ---------------------------------------------------------------------------
+ * 1. gm_bin_triangles — vertex projection and 16x16 tile binning.
+ * README "Mesh rasterizer", step 1 (triangles binned into 16x16 tiles) and the
+ * near-plane rule (triangles with a vertex in front of the near plane are
+ * skipped, no clipping).
+ *
+ * Writes vscreen [3][V] = (u, v, z_c) per vertex, evaluated in fp32 as
+ *   x_c = ((R0 x + R1 y) + R2 z) + t0 (likewise y_c, z_c), u = (fx x_c)/z_c + cx.
+ * A face is binned when its mask is non-zero, all three z_c >= near_z and its
+ * fp64 signed area is non-zero; it goes to every tile that holds a pixel centre of
+ * its pixel-centre bounding box.  tile_offsets [T+1] (exclusive prefix sums) and
+ * tile_tris [n_pairs] list the face ids per tile (order inside a tile unspecified).
+ * cap: capacity of tile_tris; *n_pairs (host, out): number of (tile, face) pairs.
+ * ws: device workspace of at least gm_bin_triangles_ws(...) bytes.
+ * Synchronises `stream` once (the pair count readback).
+ * ------------------------------------------------------------------------- */
+size_t gm_bin_triangles_ws(int32_t V, int32_t F, int32_t width, int32_t height);
+gm_status gm_bin_triangles(const gm_camera* cam, const gm_mesh* mesh, float* vscreen,
+                           int32_t* tile_offsets, int32_t* tile_tris, int64_t cap,
+                           int64_t* n_pairs, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * 2. gm_raster_zbuffer — nearest triangle at every pixel centre.
+ * README "Mesh rasterizer", step 1 (a kernel finds the nearest triangle at each
+ * pixel centre; this visibility decision is the only non-differentiable step).
+ *
+ * For pixel centre p the edge functions E_k(p) = (b.u-a.u)(p.v-a.v) -
+ * (b.v-a.v)(p.u-a.u) of edges (v1,v2), (v2,v0), (v0,v1) are evaluated in fp64; p is
+ * covered when E_k * sign(A) >= 0 for k = 0,1,2 (inclusive, no back-face culling).
+ * Depth z = 1 / sum_k (E_k/A)/z_k in fp64.  The smallest z wins, an exact tie goes
+ * to the smaller face id.  Outputs: face_id [H][W] (-1 = empty), depth [H][W] =
+ * fp32 rounding of z (+inf = empty), tile_dmax [T] = max depth over the tile's
+ * in-image pixels, +inf when any of them is empty (input of the occlusion cull).
+ * ------------------------------------------------------------------------- */
+gm_status gm_raster_zbuffer(const gm_camera* cam, const gm_mesh* mesh, const float* vscreen,
+                            const int32_t* tile_offsets, const int32_t* tile_tris,
+                            int32_t* face_id, float* depth, float* tile_dmax, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * 3. gm_project_gaussians — EWA projection, conditional depth model, colour.
+ * README "Hybrid rendering": z*(p) = z_c + g.(p - mean2d) with
+ * g = (Sigma_uv + eps I)^-1 Sigma_uv,z and sigma^2 = Sigma_zz - Sigma_z,uv g, from
+ * the projected 3D covariance; projection and spherical-harmonics colour as in
+ * 3D Gaussian splatting.  eps = 0.3 px^2, also the 2D splat dilation.
+ *
+ * Inputs: means [3][N] world, quats [4][N] (w, x, y, z; normalised here), scales
+ * [3][N] linear (exp of log-scales), opacity [N] in [0, 1] (sigmoid of logits),
+ * sh [(d+1)^2][3][N] coefficients for sh_degree d in 0..3, or sh [1][3][N] plain
+ * RGB when sh_degree = -1.  Colour = max(0, sum_lm Y_lm(dir) c_lm + 0.5) at
+ * dir = normalize(mean - camera centre), real SH in the splatting sign convention.
+ *
+ * Output rec [N][GM_REC] floats per Gaussian (64-byte aligned records):
+ *   0 u, 1 v (mean2d), 2 Q00, 3 Q01, 4 Q11 (conic = (Sigma_uv + eps I)^-1),
+ *   5 opacity, 6..8 rgb, 9 z_c, 10 g0, 11 g1, 12 sigma,
+ *   13 int32 tx0 | ty0 << 16, 14 int32 tx1 | ty1 << 16 (tile rect, exclusive),
+ *   15 int32 number of tiles in the rect (0 = not listed).
+ * The decision fields (0..5, 9..15) are evaluated in fp32 in a fixed order with no
+ * fused multiply-add; the rect uses radius ceil(3 sqrt(lambda_max)).  A Gaussian is
+ * not listed when z_c < near_z, det <= 0 or its rect misses the image.
+ * ------------------------------------------------------------------------- */
+gm_status gm_project_gaussians(const gm_camera* cam, int32_t N, const float* means,
+                               const float* quats, const float* scales, const float* opacity,
+                               const float* sh, int32_t sh_degree, float* rec, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * 4. gm_sort_tile_keys — occlusion cull, per-tile lists in depth order.
+ * README "Hybrid rendering": Gaussians are composited "in the usual sorted 3DGS
+ * order" (Limitations: sorted by centre depth); cull_occluded removes Gaussians
+ * certainly hidden behind the mesh in fully covered 16x16 tiles without changing
+ * the result.
+ *
+ * Lists every listed Gaussian i in every tile of its rect, ordered by (bits of
+ * fp32 z_c, i).  With tile_dmax != NULL, pair (t, i) is dropped when t is fully
+ * covered (tile_dmax[t] < inf) and
+ *   min(0.99, o_i) Phi((Dmax_t + 1e-5 |Dmax_t| - zmin_ti) / (sigma_i softness))
+ *     < (1/255)(1 - 1e-3),
+ * zmin_ti = min of z*_i over the four corner pixel centres of the tile (softness 0:
+ * dropped when zmin_ti >= Dmax_t + 1e-5 |Dmax_t|).  Such a pair falls under the
+ * 1/255 skip rule at every pixel of the tile, so outputs are unchanged.
+ * Outputs: tile_ranges [T][2] = [start, end) into sorted_ids [n_keys].
+ * cap: capacity of sorted_ids; *n_keys (host, out).  ws: at least
+ * gm_sort_tile_keys_ws(N, cap, W, H) bytes.  Synchronises `stream` once.
+ * ------------------------------------------------------------------------- */
+size_t gm_sort_tile_keys_ws(int32_t N, int64_t cap, int32_t width, int32_t height);
+gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec,
+                            const float* tile_dmax, float softness, int32_t* tile_ranges,
+                            int32_t* sorted_ids, int64_t cap, int64_t* n_keys, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * 5. gm_composite_hybrid_fwd — depth-tested front-to-back composite.
+ * README "Hybrid rendering": per pixel each Gaussian is split at the mesh surface,
+ * f = Phi((D - z*(p)) / (sigma softness)); front parts alpha f and back parts
+ * alpha (1 - f) form two layers, C = C_front + T_front (a_m c_m + (1 - a_m)(C_back +
+ * T_back bg)).  Mesh coverage a_m is binary here (no edge antialiasing), so the
+ * back layer never contributes and one front layer is evaluated:
+ *   alpha_i = min(0.99, o exp(-q)), q = (Q00 dx^2 + 2 Q01 dx dy + Q11 dy^2)/2,
+ *   alpha_F = alpha f (f = 1 off the mesh), entries with alpha_F < 1/255 skipped,
+ *   the walk stops before an entry that would bring T below 1e-4;
+ *   rgb = C_F + T_F (a_m c_m + (1 - a_m) bg), alpha = 1 - T_F (1 - a_m),
+ *   depth = sum w_i z_c,i + T_F a_m D.
+ * c_m: perspective-correct barycentrics from face_id; base colour from vertex
+ * colours or the trilinear mip texture; Phong when `light` and normals are given:
+ *   c_m = base (ka + kd max(0, n.l)) + ks [n.l > 0] max(0, r.e)^shininess.
+ * Inputs: the outputs of calls 1-4; bg (host, 3 floats); softness >= 0.
+ * Outputs: out_rgb [H][W][3], out_depth [H][W], out_alpha [H][W]; state for the
+ * backward: state_T [H][W] (final transmittance), state_last [H][W] (index in the
+ * tile list + 1 of the last included entry).  Deterministic.
+ * ------------------------------------------------------------------------- */
+gm_status gm_composite_hybrid_fwd(const gm_camera* cam, const float* rec,
+                                  const int32_t* tile_ranges, const int32_t* sorted_ids,
+                                  const int32_t* face_id, const float* depth, const gm_mesh* mesh,
+                                  const float* vscreen, const gm_light* light, const float* bg,
+                                  float softness, float* out_rgb, float* out_depth,
+                                  float* out_alpha, float* state_T, int32_t* state_last,
+                                  hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * 6. gm_composite_hybrid_bwd — reverse mode of call 5.
+ * README "Hybrid rendering": everything is differentiable, Gaussian parameters
+ * also through the split, and the mesh through its depth and interpolated colour.
+ *
+ * Inputs: every input of call 5, its state, and upstream gradients g_rgb
+ * [H][W][3], g_depth [H][W] (or NULL = 0), g_alpha [H][W] (or NULL = 0).
+ * Outputs (zero-filled by the call, then accumulated with float atomics):
+ *   g_rec [N][GM_GRAD]: d/d(u, v, Q00, Q01, Q11, opacity, r, g, b, z_c, g0, g1, sigma);
+ *   g_mesh_rgb [H][W][3] = dL/dc_m, g_mesh_depth [H][W] = dL/dD (either may be NULL).
+ * Skipped and stopped entries get no gradient; the clamp at 0.99 has zero
+ * derivative; the decisions are not differentiated.
+ * ------------------------------------------------------------------------- */
+gm_status gm_composite_hybrid_bwd(const gm_camera* cam, int32_t N, const float* rec,
+                                  const int32_t* tile_ranges, const int32_t* sorted_ids,
+                                  const int32_t* face_id, const float* depth, const gm_mesh* mesh,
+                                  const float* vscreen, const gm_light* light, const float* bg,
+                                  float softness, const float* state_T, const int32_t* state_last,
+                                  const float* g_rgb, const float* g_depth, const float* g_alpha,
+                                  float* g_rec, float* g_mesh_rgb, float* g_mesh_depth,
+                                  hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Auxiliary.
+ * gm_build_mipmaps: README v1.1 (trilinear mipmapping by default): box-filter
+ * pyramid of a square power-of-two texture tex [S][S][3] (HWC, values in [0, 1]);
+ * level l+1 texel = mean of the 2x2 block below it; levels stored back to back in
+ * mips [gm_mipmaps_floats(S)].
+ * ------------------------------------------------------------------------- */
+size_t gm_mipmaps_floats(int32_t S);
+gm_status gm_build_mipmaps(const float* tex, int32_t S, float* mips, hipStream_t stream);
+
+/* Thread-local message for the last non-OK status of this thread ("" if none). */
+const char* gm_last_error(void);
+/* ABI version (major * 100 + minor). */
+int32_t gm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GM_H */

@@ -375,7 +375,7 @@ def render_view(scene, view_index: int = 0, tiles=None, cull: bool = True, backw
     TX, TY, T = n_tiles(cam)
     tiles = np.arange(T, dtype=np.int32) if tiles is None else np.asarray(tiles, np.int32)
     if prefilter is None:
-        prefilter = scene.F * scene.width * scene.height > 5e9
+        prefilter = scene.F * scene.width * scene.height > 1e9
     res = {"cam": cam, "tiles": tiles}
     if scene.F > 0:
         vs = project_vertices(cam, scene.verts)

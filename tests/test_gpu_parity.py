@@ -1,0 +1,202 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small workloads (64x64 random soup, 512x512 icosphere, 800x800 textured soup, tiny
+edge cases) are compared on every tile.  The 1080p workloads are compared on a
+sample of tiles, with upstream gradients zero outside the sample so that the
+oracle can produce the full gradient of every Gaussian.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import scenes
+import tiny
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def _scene(name):
+    if name not in _CACHE:
+        _CACHE[name] = scenes.make_scene(name)
+    return _CACHE[name]
+
+
+def _renderer(scene):
+    from differentiable_hybrid_mesh_amd.pipeline import DeviceScene, Renderer
+    return Renderer(DeviceScene(scene))
+
+
+def _run(scene, view, tiles=None, cull=True, masked=False):
+    """Run GPU fwd+bwd and the oracle on ``tiles`` (all tiles when None)."""
+    import torch
+    T = scene.tiles_x * scene.tiles_y
+    tiles = np.arange(T, dtype=np.int32) if tiles is None else np.asarray(tiles, np.int32)
+    g = P.masked_grads(scene, view, tiles) if masked else scene.grads[view]
+    r = _renderer(scene)
+    r.forward(view, cull=cull)
+    gd = {k: torch.from_numpy(v).cuda() for k, v in g.items()}
+    r.backward(gd["rgb"], gd["depth"], gd["alpha"])
+    gpu = P.gpu_state(r, with_grads=True)
+    ora = oracle.render_view(scene, view, tiles=tiles, cull=cull, backward=True, grads=g)
+    return gpu, ora, tiles
+
+
+def _check_all(scene, view, gpu, ora, tiles, cull, label):
+    rep = {}
+    rep["vscreen_mismatch"] = P.compare_vscreen(gpu, ora) if scene.F else 0
+    zb = P.compare_zbuffer(scene, gpu, ora, tiles)
+    rep.update({k: v for k, v in zb.items() if k != "ties"})
+    rep.update(P.compare_records(gpu, ora) if scene.N else {})
+    rep.update(P.compare_lists(scene, gpu, ora, tiles, cull) if scene.N else {})
+    im = P.compare_images(scene, gpu, ora, tiles, ties=zb["ties"])
+    rep.update({k: v for k, v in im.items() if not k.endswith("_mask")})
+    gr = P.compare_grads(scene, gpu, ora, tiles, im["straddle_mask"])
+    rep.update(gr)
+    print(label, {k: v for k, v in rep.items()}, flush=True)
+    assert rep["vscreen_mismatch"] == 0
+    assert rep["face_mismatch"] == 0 and rep["depth_mismatch"] == 0 and rep["dmax_mismatch"] == 0
+    if scene.N:
+        assert rep["valid_mismatch"] == 0 and rep["rect_mismatch"] == 0 and rep["ntiles_mismatch"] == 0
+        assert rep["field_mismatch"] == 0 and rep["rgb_ok"]
+        assert rep["list_mismatch"] == 0
+    assert rep["img_bad"] == 0
+    npx = len(tiles) * 256
+    assert rep["straddle"] <= max(4, 2e-3 * npx), "too many straddle exemptions"
+    assert not rep["planes_bad"] and rep["elem_bad"] == 0
+    assert rep["mesh_rgb_bad"] == 0 and rep["mesh_depth_bad"] == 0
+    return rep
+
+
+@pytest.mark.parametrize("cull", [True, False])
+def test_c1_full(cull):
+    s = _scene("c1")
+    gpu, ora, tiles = _run(s, 0, cull=cull)
+    _check_all(s, 0, gpu, ora, tiles, cull, "c1 cull=%s" % cull)
+    assert P.compare_bins(s, 0, gpu) == 0
+
+
+def test_c2_full():
+    s = _scene("c2")
+    gpu, ora, tiles = _run(s, 0, cull=True)
+    _check_all(s, 0, gpu, ora, tiles, True, "c2")
+    assert P.compare_bins(s, 0, gpu) == 0
+
+
+@pytest.mark.parametrize("view", [0, 5, 11])
+def test_c4_views(view):
+    s = _scene("c4")
+    gpu, ora, tiles = _run(s, view, cull=True)
+    _check_all(s, view, gpu, ora, tiles, True, "c4 view %d" % view)
+    assert P.compare_bins(s, view, gpu) == 0
+
+
+def _sample_tiles(scene, n, seed=0):
+    rng = np.random.default_rng(seed)
+    T = scene.tiles_x * scene.tiles_y
+    t = set(rng.choice(T, size=n, replace=False).tolist())
+    # a band across the middle row (silhouettes, covered interior) and the ragged last row
+    mid = scene.tiles_y // 2
+    t.update(range(mid * scene.tiles_x + scene.tiles_x // 2 - 8, mid * scene.tiles_x + scene.tiles_x // 2 + 8))
+    t.update(range((scene.tiles_y - 1) * scene.tiles_x, (scene.tiles_y - 1) * scene.tiles_x + 4))
+    return np.array(sorted(t), np.int32)
+
+
+@pytest.mark.slow
+def test_c3_sampled():
+    s = _scene("c3")
+    tiles = _sample_tiles(s, 24)
+    gpu, ora, tiles = _run(s, 0, tiles=tiles, cull=True, masked=True)
+    _check_all(s, 0, gpu, ora, tiles, True, "c3 sampled")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("view", [0, 1, 2, 3])
+def test_c5_sampled(view):
+    s = _scene("c5")
+    tiles = _sample_tiles(s, 12, seed=view)
+    gpu, ora, tiles = _run(s, view, tiles=tiles, cull=True, masked=True)
+    _check_all(s, view, gpu, ora, tiles, True, "c5 view %d sampled" % view)
+
+
+# ---------------------------------------------------------------------------
+# invariants and edge cases
+# ---------------------------------------------------------------------------
+
+def test_cull_invariance_and_determinism():
+    """Culling on vs off: bitwise-equal images; forward bitwise repeatable."""
+    import torch
+    s = _scene("c2")
+    r = _renderer(s)
+    r.forward(0, cull=True)
+    a = P.gpu_state(r)
+    n_cull = r.n_keys
+    r.forward(0, cull=False)
+    b = P.gpu_state(r)
+    assert r.n_keys > n_cull
+    for k in ("rgb", "depth", "alpha", "T"):
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+    r.forward(0, cull=True)
+    c = P.gpu_state(r)
+    for k in ("rgb", "depth", "alpha", "T", "last", "ids", "ranges", "face_id"):
+        assert np.array_equal(np.asarray(a[k]).view(np.uint8), np.asarray(c[k]).view(np.uint8)), k
+    g = {k: torch.from_numpy(v).cuda() for k, v in s.grads[0].items()}
+    r.forward(0, cull=True)
+    r.backward(g["rgb"], g["depth"], g["alpha"])
+    ga = P.to_np(r.g_rec).copy()
+    r.forward(0, cull=False)
+    r.backward(g["rgb"], g["depth"], g["alpha"])
+    gb = P.to_np(r.g_rec)
+    assert np.allclose(ga, gb, rtol=1e-5, atol=1e-6 * np.abs(ga).max())
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3, 4])
+def test_tiny_random_scenes(seed):
+    s = tiny.random_tiny(seed, n_tri=8, n_gauss=16, size=32 + 7 * seed)  # ragged tiles
+    gpu, ora, tiles = _run(s, 0, cull=True)
+    _check_all(s, 0, gpu, ora, tiles, True, "tiny %d" % seed)
+
+
+def test_no_mesh_plain_splatting():
+    s = tiny.random_tiny(5, n_tri=1, n_gauss=40, size=48)
+    s.verts, s.faces, s.vcolor = None, None, None
+    gpu, ora, tiles = _run(s, 0, cull=True)
+    _check_all(s, 0, gpu, ora, tiles, True, "no mesh")
+
+
+def test_empty_gaussians_and_empty_mesh():
+    s = tiny.random_tiny(6, n_tri=5, n_gauss=1, size=40)
+    s.means = np.zeros((3, 0), np.float32)
+    s.quats = np.zeros((4, 0), np.float32)
+    s.scales = np.zeros((3, 0), np.float32)
+    s.opacity = np.zeros(0, np.float32)
+    s.sh = np.zeros((1, 3, 0), np.float32)
+    gpu, ora, tiles = _run(s, 0, cull=True)
+    _check_all(s, 0, gpu, ora, tiles, True, "N=0")
+
+
+def test_softness_zero_and_sh_degrees():
+    for deg in (0, 1, 2, 3):
+        s = tiny.random_tiny(10 + deg, n_tri=6, n_gauss=24, size=40)
+        rng = np.random.default_rng(deg)
+        K = (deg + 1) ** 2
+        s.sh = rng.normal(0, 0.3, size=(K, 3, s.N)).astype(np.float32)
+        s.sh_degree = deg
+        s.softness = 0.0 if deg == 1 else 0.5
+        gpu, ora, tiles = _run(s, 0, cull=True)
+        _check_all(s, 0, gpu, ora, tiles, True, "deg %d softness %g" % (deg, s.softness))
+
+
+def test_capacity_error_reports_needed_size():
+    import torch
+    from differentiable_hybrid_mesh_amd import _lib as G
+    from differentiable_hybrid_mesh_amd.pipeline import DeviceScene, Renderer
+    s = _scene("c1")
+    r = Renderer(DeviceScene(s), pair_cap=1, key_cap=1)
+    st, n = G.gm_bin_triangles(r.ds.cams[0], r.ds.mesh, r.vscreen, r.tile_offsets, r.tile_tris, 1, r.ws_bin,
+                               torch.cuda.current_stream().cuda_stream)
+    assert st == G.GM_ERR_CAPACITY and n > 1
+    r.forward(0)  # grows both lists and succeeds
+    assert r.n_pairs == n and r.key_cap >= r.n_keys > 1
