@@ -76,7 +76,8 @@ def compare_vscreen(gpu, ora):
 
 def compare_zbuffer(scene, gpu, ora, tiles):
     m = tile_pixel_mask(scene, tiles)
-    tie = (ora["z2"] - ora["z1"]) <= DEPTH_TIE * ora["z1"]
+    with np.errstate(invalid="ignore"):
+        tie = (ora["z2"] - ora["z1"]) <= DEPTH_TIE * ora["z1"]
     gf, of = gpu["face_id"], ora["face_id"]
     bad = m & (gf != of) & ~tie
     exempt = int(np.count_nonzero(m & (gf != of) & tie))
@@ -153,22 +154,26 @@ def compare_lists(scene, gpu, ora, tiles, cull):
 
 
 def compare_images(scene, gpu, ora, tiles, ties=None):
+    """Every pixel of the sampled tiles is checked; a pixel that misses the tolerance
+    is exempt only when the oracle marks it as a straddle (or a depth tie)."""
     c = ora["comp"]
     m = tile_pixel_mask(scene, tiles)
     strad = m & (c["margin"] < STRADDLE)
     if ties is not None:
         strad |= ties
-    ok = m & ~strad
     d_rgb = np.abs(gpu["rgb"].astype(np.float64) - c["rgb"]).max(-1)
     d_dep = np.abs(gpu["depth"].astype(np.float64) - c["depth"])
     d_alp = np.abs(gpu["alpha"].astype(np.float64) - c["alpha"])
     worst = np.maximum(np.maximum(d_rgb, d_dep), d_alp)
-    bad = ok & ~(worst <= IMG_TOL)
-    return {"img_bad": int(np.count_nonzero(bad)), "straddle": int(np.count_nonzero(strad & ~(ties if ties is not None else False))),
+    fail = m & ~(worst <= IMG_TOL)
+    used = fail & strad
+    ok = m & ~used
+    return {"img_bad": int(np.count_nonzero(fail & ~strad)), "straddle": int(np.count_nonzero(used)),
+            "straddle_candidates": int(np.count_nonzero(strad)),
             "rgb_max": float(d_rgb[ok].max()) if ok.any() else 0.0,
             "depth_max": float(d_dep[ok].max()) if ok.any() else 0.0,
             "alpha_max": float(d_alp[ok].max()) if ok.any() else 0.0,
-            "straddle_mask": strad, "bad_mask": bad}
+            "straddle_mask": strad, "fail_mask": fail}
 
 
 def exempt_gaussians(scene, ora, tiles, strad_mask):
@@ -183,25 +188,39 @@ def exempt_gaussians(scene, ora, tiles, strad_mask):
 
 
 def compare_grads(scene, gpu, ora, tiles, strad_mask):
+    """All Gaussians are checked; a Gaussian that misses the tolerance is exempt only
+    when it is listed in a tile holding a straddle pixel."""
     c = ora["comp"]
     ref = c["grad"]
     got = gpu["g_rec"].astype(np.float64)
     ex = exempt_gaussians(scene, ora, tiles, strad_mask)
-    keep = np.ones(len(ref), bool)
-    keep[ex] = False
-    res = {"grad_exempt": int(len(ex)), "planes_bad": [], "elem_bad": 0}
+    exm = np.zeros(len(ref), bool)
+    exm[ex] = True
+    res = {"grad_exempt": 0, "planes_bad": [], "elem_bad": 0}
+    used = np.zeros(len(ref), bool)
+    for k in range(13):
+        r, g = ref[:, k], got[:, k]
+        d = g - r
+        rms = np.sqrt(np.mean(r * r)) if len(r) else 0.0
+        fail = np.abs(d) > GRAD_TOL * (np.abs(r) + rms) + 1e-12
+        res["elem_bad"] += int(np.count_nonzero(fail & ~exm))
+        used |= fail & exm
+    res["grad_exempt"] = int(np.count_nonzero(used))
+    keep = ~used
     for k in range(13):
         r, g = ref[keep, k], got[keep, k]
-        d = g - r
         nr = np.linalg.norm(r)
-        if np.linalg.norm(d) > GRAD_TOL * nr + 1e-12:
-            res["planes_bad"].append((k, float(np.linalg.norm(d) / max(nr, 1e-30))))
-        rms = np.sqrt(np.mean(r * r)) if len(r) else 0.0
-        res["elem_bad"] += int(np.count_nonzero(np.abs(d) > GRAD_TOL * (np.abs(r) + rms) + 1e-12))
-    m = tile_pixel_mask(scene, tiles) & ~strad_mask
+        if np.linalg.norm(g - r) > GRAD_TOL * nr + 1e-12:
+            res["planes_bad"].append((k, float(np.linalg.norm(g - r) / max(nr, 1e-30))))
+    m = tile_pixel_mask(scene, tiles)
     for name, key in (("mesh_rgb", "g_mesh_rgb"), ("mesh_depth", "g_mesh_depth")):
         r = c[key][m]
         g = gpu[key][m].astype(np.float64)
         rms = np.sqrt(np.mean(r * r)) if r.size else 0.0
-        res[name + "_bad"] = int(np.count_nonzero(np.abs(g - r) > GRAD_TOL * (np.abs(r) + rms) + 1e-9))
+        fail = np.abs(g - r) > GRAD_TOL * (np.abs(r) + rms) + 1e-9
+        if fail.ndim > 1:
+            fail = fail.any(-1)
+        sm = strad_mask[m]
+        res[name + "_bad"] = int(np.count_nonzero(fail & ~sm))
+        res[name + "_exempt"] = int(np.count_nonzero(fail & sm))
     return res

@@ -64,7 +64,8 @@ def _check_all(scene, view, gpu, ora, tiles, cull, label):
         assert rep["list_mismatch"] == 0
     assert rep["img_bad"] == 0
     npx = len(tiles) * 256
-    assert rep["straddle"] <= max(4, 2e-3 * npx), "too many straddle exemptions"
+    assert rep["straddle"] <= max(2, 1e-4 * npx), "too many straddle exemptions used"
+    assert rep["grad_exempt"] <= max(2, 1e-4 * max(scene.N, 1)), "too many gradient exemptions used"
     assert not rep["planes_bad"] and rep["elem_bad"] == 0
     assert rep["mesh_rgb_bad"] == 0 and rep["mesh_depth_bad"] == 0
     return rep
