@@ -70,9 +70,8 @@ def lib():
     L.gm_sort_tile_keys_ws.argtypes = [I32, I64, I32, I32]
     L.gm_sort_tile_keys_ws.restype = SZ
     L.gm_sort_tile_keys.argtypes = [cam, I32, P, P, F32, P, P, I64, C.POINTER(C.c_int64), P, SZ, P]
-    L.gm_composite_hybrid_fwd.argtypes = [cam, P, P, P, P, P, mesh, P, light, P, F32, P, P, P, P, P, P]
-    L.gm_composite_hybrid_bwd.argtypes = [cam, I32, P, P, P, P, P, mesh, P, light, P, F32, P, P, P, P,
-                                          P, P, P, P, P]
+    L.gm_composite_hybrid_fwd.argtypes = [cam, P, P, P, P, P, mesh, P, light, P, F32, P, P, P, P, P, P, P]
+    L.gm_composite_hybrid_bwd.argtypes = [cam, I32, P, P, P, P, P, F32, P, P, P, P, P, P, P, P, P, P]
     L.gm_mipmaps_floats.argtypes = [I32]
     L.gm_mipmaps_floats.restype = SZ
     L.gm_build_mipmaps.argtypes = [P, I32, P, P]
@@ -152,25 +151,21 @@ def _light_ref(light):
 
 
 def gm_composite_hybrid_fwd(cam, rec, tile_ranges, sorted_ids, face_id, depth, mesh, vscreen, light, bg,
-                            softness, out_rgb, out_depth, out_alpha, state_T, state_last, stream):
+                            softness, out_rgb, out_depth, out_alpha, state_T, state_last, state_cm, stream):
     bgv = (C.c_float * 3)(*[float(x) for x in bg])
     check(lib().gm_composite_hybrid_fwd(C.byref(cam), ptr(rec), ptr(tile_ranges), ptr(sorted_ids),
                                         ptr(face_id), ptr(depth), C.byref(mesh), ptr(vscreen),
                                         _light_ref(light), C.cast(bgv, C.c_void_p), float(softness),
                                         ptr(out_rgb), ptr(out_depth), ptr(out_alpha), ptr(state_T),
-                                        ptr(state_last), stream))
+                                        ptr(state_last), ptr(state_cm), stream))
 
 
-def gm_composite_hybrid_bwd(cam, N, rec, tile_ranges, sorted_ids, face_id, depth, mesh, vscreen, light, bg,
-                            softness, state_T, state_last, g_rgb, g_depth, g_alpha, g_rec, g_mesh_rgb,
-                            g_mesh_depth, stream):
-    bgv = (C.c_float * 3)(*[float(x) for x in bg])
+def gm_composite_hybrid_bwd(cam, N, rec, tile_ranges, sorted_ids, face_id, depth, softness, state_T, state_last,
+                            state_cm, g_rgb, g_depth, g_alpha, g_rec, g_mesh_rgb, g_mesh_depth, stream):
     check(lib().gm_composite_hybrid_bwd(C.byref(cam), int(N), ptr(rec), ptr(tile_ranges), ptr(sorted_ids),
-                                        ptr(face_id), ptr(depth), C.byref(mesh), ptr(vscreen),
-                                        _light_ref(light), C.cast(bgv, C.c_void_p), float(softness),
-                                        ptr(state_T), ptr(state_last), ptr(g_rgb), ptr(g_depth),
-                                        ptr(g_alpha), ptr(g_rec), ptr(g_mesh_rgb), ptr(g_mesh_depth),
-                                        stream))
+                                        ptr(face_id), ptr(depth), float(softness), ptr(state_T),
+                                        ptr(state_last), ptr(state_cm), ptr(g_rgb), ptr(g_depth),
+                                        ptr(g_alpha), ptr(g_rec), ptr(g_mesh_rgb), ptr(g_mesh_depth), stream))
 
 
 def gm_mipmaps_floats(S) -> int:

@@ -196,19 +196,35 @@ __device__ void surface_color(const CompParams& P, int f, int px, int py, float*
 }
 
 // ---------------------------------------------------------------------------
+// surface colour prepass: state_cm = c_m on the mesh, bg elsewhere
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_shade(CompParams P, float* __restrict__ state_cm)
+{
+    const int pix = blockIdx.x * blockDim.x + threadIdx.x;
+    if (pix >= P.cam.width * P.cam.height) return;
+    const int fid = P.face_id[pix];
+    float cm[3] = {P.bg[0], P.bg[1], P.bg[2]};
+    if (fid >= 0) surface_color(P, fid, pix % P.cam.width, pix / P.cam.width, cm);
+    state_cm[3 * pix + 0] = cm[0];
+    state_cm[3 * pix + 1] = cm[1];
+    state_cm[3 * pix + 2] = cm[2];
+}
+
+// ---------------------------------------------------------------------------
 // the per-pair evaluation shared by both walks
 // ---------------------------------------------------------------------------
 struct Staged {
     float4 a;  // u, v, Q00, Q01
     float4 b;  // Q11, opacity, r, g
     float4 c;  // b, z_c, g0, g1
-    float4 d;  // sigma, kappa = 1/(sigma softness), -, -
+    float4 d;  // sigma, kappa = 1/(sigma softness), q_skip, -
 };
 
 __device__ __forceinline__ float normal_cdf(float s) { return 0.5f * erfcf(-s * 0.70710678118654752f); }
 
 // alpha = min(0.99, o exp(-q)); returns alpha_F = alpha f (0 when below the skip
-// threshold before f is formed); also returns the intermediates the backward needs.
+// threshold before f is formed) and the intermediates the backward needs.  A pair
+// with q above q_skip is below the threshold with margin and exp() is not formed.
 __device__ __forceinline__ float eval_pair(const Staged& g, float pxc, float pyc, bool on, float D,
                                            float softness, float& dx, float& dy, float& G, float& alpha,
                                            float& f, float& s)
@@ -216,10 +232,15 @@ __device__ __forceinline__ float eval_pair(const Staged& g, float pxc, float pyc
     dx = pxc - g.a.x;
     dy = pyc - g.a.y;
     const float q = 0.5f * (g.a.z * dx * dx + g.b.x * dy * dy) + g.a.w * dx * dy;
-    G = __expf(-q);
-    alpha = fminf(g.b.y * G, ALPHA_MAX);
     f = 1.0f;
     s = 0.0f;
+    if (q > g.d.z) {
+        G = 0.0f;
+        alpha = 0.0f;
+        return 0.0f;
+    }
+    G = __expf(-q);
+    alpha = fminf(g.b.y * G, ALPHA_MAX);
     if (alpha < SKIP_ALPHA) return 0.0f;
     if (on) {
         const float num = (D - g.c.y) - (g.c.z * dx + g.c.w * dy);
@@ -233,27 +254,100 @@ __device__ __forceinline__ float eval_pair(const Staged& g, float pxc, float pyc
     return alpha * f;
 }
 
-__device__ __forceinline__ void stage_record(const CompParams& P, int id, Staged& st)
+// Stage one record and decide for which of the tile's four 16x4-pixel waves it can
+// matter.  A wave bit is cleared only when every pixel of the wave would skip the
+// entry anyway (alpha_F < 1/255), so skipping it leaves every result bit-identical:
+//  * the alpha >= 1/255 region is the ellipse q <= q_skip; its bounding box, widened
+//    by a margin that covers fp32 rounding of q (scaled by the conic's
+//    conditioning), misses the wave's pixel centres; or
+//  * the wave lies entirely on the mesh (wdmax = max D over its pixels) and the
+//    conditional depth, minimal at a corner of the wave's rectangle, keeps f small
+//    enough that min(0.99, o) f < (1/255)(1 - 1e-3), with a 1e-5 |D| depth slack.
+__device__ __forceinline__ uint32_t stage_record(const CompParams& P, float4 ra, float4 rb, float4 rc,
+                                                 float4 rd, int tx, int ty, const float* wdmax, Staged& st)
 {
-    const float4* r = reinterpret_cast<const float4*>(P.rec + (size_t)id * GM_REC);
-    st.a = r[0];
-    st.b = r[1];
-    st.c = r[2];
-    float4 d = r[3];
-    d.y = P.softness > 0.0f ? 1.0f / (d.x * P.softness) : 0.0f;
-    st.d = d;
+    st.a = ra;
+    st.b = rb;
+    st.c = rc;
+    const float o = rb.y;
+    const float lq = o > 0.0f ? logf(255.0f * o) : -1.0f;
+    const float qs = o > 0.0f ? lq + 1e-4f + 1e-4f * fabsf(lq) : -1.0f;
+    const float kap = P.softness > 0.0f ? 1.0f / (rd.x * P.softness) : 0.0f;
+    st.d = make_float4(rd.x, kap, qs, 0.0f);
+    if (!(qs >= 0.0f)) return 0u;  // o exp(-q) < 1/255 everywhere
+    const float Q00 = ra.z, Q01 = ra.w, Q11 = rb.x;
+    const float detQ = Q00 * Q11 - Q01 * Q01;
+    if (!(detQ > 0.0f) || !(Q00 > 0.0f) || !(Q11 > 0.0f)) return 0xFu;
+    const float rho = fminf(fabsf(Q01) / sqrtf(Q00 * Q11), 0.999999f);
+    const float qe = qs * (1.0f + 1e-5f * (1.0f + rho) / (1.0f - rho)) + 1e-4f;
+    const float ex = sqrtf(2.0f * qe * Q11 / detQ) * 1.001f + 0.01f;
+    const float ey = sqrtf(2.0f * qe * Q00 / detQ) * 1.001f + 0.01f;
+    const float u = ra.x, v = ra.y;
+    const float xa = (float)(tx * GM_TILE) + 0.5f, xb = xa + 15.0f;
+    if (u + ex < xa || u - ex > xb) return 0u;
+    const float amax = fminf(o, ALPHA_MAX);
+    const float thr = (1.0f / 255.0f) * (1.0f - 1e-3f);
+    // f must reach thr/amax somewhere for the entry to matter
+    const float scrit = P.softness > 0.0f && amax > thr ? -1.41421356237309515f * erfcinvf(2.0f * thr / amax) - 1e-3f
+                                                         : 0.0f;
+    const float g0 = rc.z, g1 = rc.w, zc = rc.y;
+    const float gxm = fminf(g0 * (xa - u), g0 * (xb - u));
+    uint32_t m = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float ya = (float)(ty * GM_TILE + 4 * w) + 0.5f, yb = ya + 3.0f;
+        if (v + ey < ya || v - ey > yb) continue;
+        const float dm = wdmax[w];
+        if (dm < 0.0f) continue;  // no pixel of this wave is in the image
+        if (dm < INFINITY) {
+            const float zmin = zc + (gxm + fminf(g1 * (ya - v), g1 * (yb - v)));
+            const float lim = dm + 1e-5f * fabsf(dm);
+            if (P.softness > 0.0f) {
+                if (amax <= thr) continue;
+                if ((lim - zmin) * kap < scrit) continue;
+            } else if (zmin >= lim) {
+                continue;
+            }
+        }
+        m |= 1u << w;
+    }
+    return m;
+}
+
+__device__ __forceinline__ void load_record(const float* __restrict__ rec, int id, float4& ra, float4& rb,
+                                            float4& rc, float4& rd)
+{
+    const float4* r = reinterpret_cast<const float4*>(rec + (size_t)id * GM_REC);
+    ra = r[0];
+    rb = r[1];
+    rc = r[2];
+    rd = r[3];
+}
+
+// Per-wave max mesh depth: +inf when a pixel of the wave is off the mesh, -1 when no
+// pixel of the wave is in the image.
+__device__ __forceinline__ void wave_dmax(bool inside, bool on, float D, float* s_wd)
+{
+    float m = inside ? (on ? D : INFINITY) : -1.0f;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if ((threadIdx.x & 63) == 0) s_wd[threadIdx.x >> 6] = m;
 }
 
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(CT)
-k_composite_fwd(CompParams P, float* __restrict__ out_rgb, float* __restrict__ out_depth,
-                float* __restrict__ out_alpha, float* __restrict__ state_T, int32_t* __restrict__ state_last)
+k_composite_fwd(CompParams P, const float* __restrict__ state_cm, float* __restrict__ out_rgb,
+                float* __restrict__ out_depth, float* __restrict__ out_alpha, float* __restrict__ state_T,
+                int32_t* __restrict__ state_last)
 {
     __shared__ Staged s_g[CB];
+    __shared__ uint8_t s_m[CB];
+    __shared__ float s_wd[CT / 64];
     const int tile = blockIdx.x;
     const int tx = tile % P.cam.tx, ty = tile / P.cam.tx;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int px = tx * GM_TILE + (threadIdx.x & 15), py = ty * GM_TILE + (threadIdx.x >> 4);
     const bool inside = px < P.cam.width && py < P.cam.height;
     const int pix = py * P.cam.width + px;
@@ -263,45 +357,56 @@ k_composite_fwd(CompParams P, float* __restrict__ out_rgb, float* __restrict__ o
     const int fid = inside ? P.face_id[pix] : -1;
     const bool on = fid >= 0;
     const float D = on ? P.depth[pix] : INFINITY;
+    wave_dmax(inside, on, D, s_wd);
 
     float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f, Z = 0.0f;
     int last = 0;
     bool done = !inside;
+    float4 ra, rb, rc, rd;
+    if (start + (int)threadIdx.x < end) load_record(P.rec, P.ids[start + threadIdx.x], ra, rb, rc, rd);
     for (int b0 = start; b0 < end; b0 += CB) {
         if (__syncthreads_count(done) == CT) break;
-        const int j = b0 + threadIdx.x;
-        if (j < end) stage_record(P, P.ids[j], s_g[threadIdx.x]);
-        __syncthreads();
         const int nb = min(CB, end - b0);
-        if (!done) {
-            for (int k = 0; k < nb; ++k) {
-                const Staged& g = s_g[k];
-                float dx, dy, G, al, f, s;
-                const float aF = eval_pair(g, pxc, pyc, on, D, P.softness, dx, dy, G, al, f, s);
-                if (aF < SKIP_ALPHA) continue;
-                const float Tn = T * (1.0f - aF);
-                if (Tn < STOP_T) {
-                    done = true;
+        s_m[threadIdx.x] = threadIdx.x < nb ? (uint8_t)stage_record(P, ra, rb, rc, rd, tx, ty, s_wd, s_g[threadIdx.x]) : 0;
+        if (b0 + CB + (int)threadIdx.x < end) load_record(P.rec, P.ids[b0 + CB + threadIdx.x], ra, rb, rc, rd);
+        __syncthreads();
+        bool wdone = __ballot(!done) == 0;
+        for (int i = 0; i < CB / 64 && !wdone; ++i) {
+            unsigned long long m = __ballot((s_m[i * 64 + lane] >> wave) & 1);
+            while (m) {
+                const int k = i * 64 + __builtin_ctzll(m);
+                m &= m - 1;
+                if (!done) {
+                    const Staged& g = s_g[k];
+                    float dx, dy, G, al, f, s;
+                    const float aF = eval_pair(g, pxc, pyc, on, D, P.softness, dx, dy, G, al, f, s);
+                    if (aF >= SKIP_ALPHA) {
+                        const float Tn = T * (1.0f - aF);
+                        if (Tn < STOP_T) {
+                            done = true;
+                        } else {
+                            const float w = aF * T;
+                            C0 += w * g.b.z;
+                            C1 += w * g.b.w;
+                            C2 += w * g.c.x;
+                            Z += w * g.c.y;
+                            T = Tn;
+                            last = b0 + k - start + 1;
+                        }
+                    }
+                }
+                if (__ballot(!done) == 0) {
+                    wdone = true;
                     break;
                 }
-                const float w = aF * T;
-                C0 += w * g.b.z;
-                C1 += w * g.b.w;
-                C2 += w * g.c.x;
-                Z += w * g.c.y;
-                T = Tn;
-                last = b0 + k - start + 1;
             }
         }
     }
     if (!inside) return;
-    float cm[3] = {0.0f, 0.0f, 0.0f};
-    if (on) surface_color(P, fid, px, py, cm);
-    const float am = on ? 1.0f : 0.0f;
-    out_rgb[3 * pix + 0] = C0 + T * (on ? cm[0] : P.bg[0]);
-    out_rgb[3 * pix + 1] = C1 + T * (on ? cm[1] : P.bg[1]);
-    out_rgb[3 * pix + 2] = C2 + T * (on ? cm[2] : P.bg[2]);
-    out_alpha[pix] = 1.0f - T * (1.0f - am);
+    out_rgb[3 * pix + 0] = C0 + T * state_cm[3 * pix + 0];
+    out_rgb[3 * pix + 1] = C1 + T * state_cm[3 * pix + 1];
+    out_rgb[3 * pix + 2] = C2 + T * state_cm[3 * pix + 2];
+    out_alpha[pix] = on ? 1.0f : 1.0f - T;
     out_depth[pix] = Z + (on ? T * D : 0.0f);
     state_T[pix] = T;
     state_last[pix] = last;
@@ -310,25 +415,54 @@ k_composite_fwd(CompParams P, float* __restrict__ out_rgb, float* __restrict__ o
 // ---------------------------------------------------------------------------
 // backward
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_sum(float v)
+// Sum 16 per-lane values over the 64 lanes of a wave with a halving ("transpose")
+// reduction: at each butterfly step a lane keeps half of its values and sends the
+// other half to its partner, so 16 values need 8+4+2+1+1+1 = 17 shuffles instead of
+// 16*6.  On return lane l holds the wave total of value (l >> 2) when (l & 3) == 0.
+__device__ __forceinline__ float wave_sum16(const float* v, int lane)
 {
+    float a[8], b[4], c[2];
+    const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8, h2 = lane & 4;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    for (int i = 0; i < 8; ++i) {
+        const float send = h5 ? v[i] : v[8 + i];
+        const float keep = h5 ? v[8 + i] : v[i];
+        a[i] = keep + __shfl_xor(send, 32, 64);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float send = h4 ? a[i] : a[4 + i];
+        const float keep = h4 ? a[4 + i] : a[i];
+        b[i] = keep + __shfl_xor(send, 16, 64);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float send = h3 ? b[i] : b[2 + i];
+        const float keep = h3 ? b[2 + i] : b[i];
+        c[i] = keep + __shfl_xor(send, 8, 64);
+    }
+    const float send = h2 ? c[0] : c[1];
+    float d = (h2 ? c[1] : c[0]) + __shfl_xor(send, 4, 64);
+    d += __shfl_xor(d, 2, 64);
+    d += __shfl_xor(d, 1, 64);
+    return d;
 }
 
 __global__ void __launch_bounds__(CT)
 k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* __restrict__ state_last,
-                const float* __restrict__ g_rgb, const float* __restrict__ g_depth,
-                const float* __restrict__ g_alpha, float* __restrict__ g_rec, float* __restrict__ g_mesh_rgb,
-                float* __restrict__ g_mesh_depth)
+                const float* __restrict__ state_cm, const float* __restrict__ g_rgb,
+                const float* __restrict__ g_depth, const float* __restrict__ g_alpha, float* __restrict__ g_rec,
+                float* __restrict__ g_mesh_rgb, float* __restrict__ g_mesh_depth)
 {
     __shared__ Staged s_g[CB];
     __shared__ int s_id[CB];
+    __shared__ uint8_t s_m[CB];
     __shared__ float s_acc[CB][GM_GRAD];
-    __shared__ int s_max[CT / 64];
+    __shared__ float s_wd[CT / 64];
+    __shared__ int s_wl[CT / 64];
     const int tile = blockIdx.x;
     const int tx = tile % P.cam.tx, ty = tile / P.cam.tx;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int px = tx * GM_TILE + (threadIdx.x & 15), py = ty * GM_TILE + (threadIdx.x >> 4);
     const bool inside = px < P.cam.width && py < P.cam.height;
     const int pix = py * P.cam.width + px;
@@ -340,104 +474,124 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
     const float D = on ? P.depth[pix] : INFINITY;
     const float TF = inside ? state_T[pix] : 1.0f;
     const int last = inside ? state_last[pix] : 0;
-    float GC[3] = {0.0f, 0.0f, 0.0f}, GZ = 0.0f, GA = 0.0f;
+    float GC0 = 0.0f, GC1 = 0.0f, GC2 = 0.0f, GZ = 0.0f, GA = 0.0f, Bt = 0.0f;
     if (inside) {
-        GC[0] = g_rgb[3 * pix + 0];
-        GC[1] = g_rgb[3 * pix + 1];
-        GC[2] = g_rgb[3 * pix + 2];
+        GC0 = g_rgb[3 * pix + 0];
+        GC1 = g_rgb[3 * pix + 1];
+        GC2 = g_rgb[3 * pix + 2];
         if (g_depth) GZ = g_depth[pix];
         if (g_alpha) GA = g_alpha[pix];
+        // B = dL/dT_F: the colour behind the Gaussians, the mesh depth and the alpha
+        Bt = GC0 * state_cm[3 * pix + 0] + GC1 * state_cm[3 * pix + 1] + GC2 * state_cm[3 * pix + 2] +
+             (on ? GZ * D : -GA);
     }
-    float cm[3] = {0.0f, 0.0f, 0.0f};
-    if (on) surface_color(P, fid, px, py, cm);
-    const float am = on ? 1.0f : 0.0f;
-    // B = dL/dT_F: background / mesh term of colour, depth and alpha
-    float Bt = GZ * (on ? D : 0.0f) - GA * (1.0f - am);
-#pragma unroll
-    for (int c = 0; c < 3; ++c) Bt += GC[c] * (on ? cm[c] : P.bg[c]);
     float acc = TF * Bt;
     float T = TF;
     float gD = 0.0f;
 
-    // longest prefix any pixel of the tile used
+    wave_dmax(inside, on, D, s_wd);
     int m = last;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o, 64));
-    if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+    if (lane == 0) s_wl[wave] = m;
     __syncthreads();
-    int mlast = 0;
-#pragma unroll
-    for (int w = 0; w < CT / 64; ++w) mlast = max(mlast, s_max[w]);
+    const int mlast = max(max(s_wl[0], s_wl[1]), max(s_wl[2], s_wl[3]));
 
+    float4 ra, rb, rc, rd;
+    int id = 0;
+    {
+        const int bend = start + mlast;
+        const int b0 = max(start, bend - CB);
+        if (b0 + (int)threadIdx.x < bend) {
+            id = P.ids[b0 + threadIdx.x];
+            load_record(P.rec, id, ra, rb, rc, rd);
+        }
+    }
     for (int bend = start + mlast; bend > start; bend -= CB) {
         const int b0 = max(start, bend - CB);
         const int nb = bend - b0;
         __syncthreads();
-        if (threadIdx.x < nb) {
-            const int id = P.ids[b0 + threadIdx.x];
+        uint32_t msk = 0;
+        if ((int)threadIdx.x < nb) {
+            msk = stage_record(P, ra, rb, rc, rd, tx, ty, s_wd, s_g[threadIdx.x]);
+            const int rel = b0 + threadIdx.x - start;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                if (rel >= s_wl[w]) msk &= ~(1u << w);
             s_id[threadIdx.x] = id;
-            stage_record(P, id, s_g[threadIdx.x]);
 #pragma unroll
             for (int c = 0; c < GM_GRAD; ++c) s_acc[threadIdx.x][c] = 0.0f;
         }
+        s_m[threadIdx.x] = (uint8_t)msk;
+        {
+            const int nend = b0, nb0 = max(start, nend - CB);
+            if (nb0 + (int)threadIdx.x < nend) {
+                id = P.ids[nb0 + threadIdx.x];
+                load_record(P.rec, id, ra, rb, rc, rd);
+            }
+        }
         __syncthreads();
-        for (int k = nb - 1; k >= 0; --k) {
-            const Staged& g = s_g[k];
-            const int rel = b0 + k - start;
-            float gr[GM_GRAD];
+        for (int i = CB / 64 - 1; i >= 0; --i) {
+            unsigned long long mm = __ballot((s_m[i * 64 + lane] >> wave) & 1);
+            while (mm) {
+                const int kk = 63 - __builtin_clzll(mm);
+                mm &= ~(1ull << kk);
+                const int k = i * 64 + kk;
+                const Staged& g = s_g[k];
+                const int rel = b0 + k - start;
+                float gr[16];
 #pragma unroll
-            for (int c = 0; c < GM_GRAD; ++c) gr[c] = 0.0f;
-            bool act = false;
-            if (rel < last) {
-                float dx, dy, G, al, f, s;
-                const float aF = eval_pair(g, pxc, pyc, on, D, P.softness, dx, dy, G, al, f, s);
-                if (aF >= SKIP_ALPHA) {
-                    act = true;
-                    const float om = 1.0f - aF;
-                    const float Ti = T / om;
-                    const float w = aF * Ti;
-                    const float Vv = GC[0] * g.b.z + GC[1] * g.b.w + GC[2] * g.c.x + GZ * g.c.y;
-                    const float daF = Ti * Vv - acc / om;
-                    acc += w * Vv;
-                    T = Ti;
-                    gr[6] = w * GC[0];
-                    gr[7] = w * GC[1];
-                    gr[8] = w * GC[2];
-                    gr[9] = w * GZ;
-                    const float da = f * daF;
-                    if (g.b.y * G <= ALPHA_MAX) {
-                        gr[5] = G * da;
-                        const float H = g.b.y * G * da;
-                        gr[2] = -0.5f * dx * dx * H;
-                        gr[3] = -dx * dy * H;
-                        gr[4] = -0.5f * dy * dy * H;
-                        gr[0] = H * (g.a.z * dx + g.a.w * dy);
-                        gr[1] = H * (g.a.w * dx + g.b.x * dy);
-                    }
-                    if (on && P.softness > 0.0f) {
-                        const float phi = 0.39894228040143268f * __expf(-0.5f * s * s);
-                        const float ds = al * phi * daF;
-                        const float kap = g.d.y;
-                        gr[9] -= kap * ds;
-                        gr[10] = -kap * ds * dx;
-                        gr[11] = -kap * ds * dy;
-                        gr[0] += kap * ds * g.c.z;
-                        gr[1] += kap * ds * g.c.w;
-                        gr[12] = -ds * s / g.d.x;
-                        gD += kap * ds;
+                for (int c = 0; c < 16; ++c) gr[c] = 0.0f;
+                bool act = false;
+                if (rel < last) {
+                    float dx, dy, G, al, f, s;
+                    const float aF = eval_pair(g, pxc, pyc, on, D, P.softness, dx, dy, G, al, f, s);
+                    if (aF >= SKIP_ALPHA) {
+                        act = true;
+                        const float om = 1.0f - aF;
+                        const float Ti = T / om;
+                        const float w = aF * Ti;
+                        const float Vv = GC0 * g.b.z + GC1 * g.b.w + GC2 * g.c.x + GZ * g.c.y;
+                        const float daF = Ti * Vv - acc / om;
+                        acc += w * Vv;
+                        T = Ti;
+                        gr[6] = w * GC0;
+                        gr[7] = w * GC1;
+                        gr[8] = w * GC2;
+                        gr[9] = w * GZ;
+                        const float da = f * daF;
+                        if (g.b.y * G <= ALPHA_MAX) {
+                            gr[5] = G * da;
+                            const float H = g.b.y * G * da;
+                            gr[2] = -0.5f * dx * dx * H;
+                            gr[3] = -dx * dy * H;
+                            gr[4] = -0.5f * dy * dy * H;
+                            gr[0] = H * (g.a.z * dx + g.a.w * dy);
+                            gr[1] = H * (g.a.w * dx + g.b.x * dy);
+                        }
+                        if (on && P.softness > 0.0f) {
+                            const float phi = 0.39894228040143268f * __expf(-0.5f * s * s);
+                            const float ds = al * phi * daF;
+                            const float kap = g.d.y;
+                            gr[9] -= kap * ds;
+                            gr[10] = -kap * ds * dx;
+                            gr[11] = -kap * ds * dy;
+                            gr[0] += kap * ds * g.c.z;
+                            gr[1] += kap * ds * g.c.w;
+                            gr[12] = -ds * s / g.d.x;
+                            gD += kap * ds;
+                        }
                     }
                 }
-            }
-            if (__ballot(act)) {
-#pragma unroll
-                for (int c = 0; c < GM_GRAD; ++c) {
-                    const float v = wave_sum(gr[c]);
-                    if ((threadIdx.x & 63) == 0 && v != 0.0f) atomicAdd(&s_acc[k][c], v);
+                if (__ballot(act)) {
+                    const float v = wave_sum16(gr, lane);
+                    const int c = lane >> 2;
+                    if ((lane & 3) == 0 && c < GM_GRAD && v != 0.0f) atomicAdd(&s_acc[k][c], v);
                 }
             }
         }
         __syncthreads();
-        if (threadIdx.x < nb) {
+        if ((int)threadIdx.x < nb) {
             float* dst = g_rec + (size_t)s_id[threadIdx.x] * GM_GRAD;
 #pragma unroll
             for (int c = 0; c < GM_GRAD; ++c) {
@@ -447,10 +601,11 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
         }
     }
     if (!inside) return;
+    const float am = on ? 1.0f : 0.0f;
     if (g_mesh_rgb) {
-        g_mesh_rgb[3 * pix + 0] = TF * am * GC[0];
-        g_mesh_rgb[3 * pix + 1] = TF * am * GC[1];
-        g_mesh_rgb[3 * pix + 2] = TF * am * GC[2];
+        g_mesh_rgb[3 * pix + 0] = TF * am * GC0;
+        g_mesh_rgb[3 * pix + 1] = TF * am * GC1;
+        g_mesh_rgb[3 * pix + 2] = TF * am * GC2;
     }
     if (g_mesh_depth) g_mesh_depth[pix] = TF * am * GZ + gD;
 }
@@ -524,26 +679,7 @@ gm_status gm_composite_hybrid_fwd(const gm_camera* cam, const float* rec, const 
                                   const int32_t* sorted_ids, const int32_t* face_id, const float* depth,
                                   const gm_mesh* mesh, const float* vscreen, const gm_light* light,
                                   const float* bg, float softness, float* out_rgb, float* out_depth,
-                                  float* out_alpha, float* state_T, int32_t* state_last, hipStream_t stream)
-{
-    clear_error();
-    CompParams P;
-    if (gm_status s = fill_params(P, cam, rec, tile_ranges, sorted_ids, face_id, depth, mesh, vscreen, light,
-                                  bg, softness))
-        return s;
-    GM_ARG_CHECK(out_rgb && out_depth && out_alpha && state_T && state_last, "an output is NULL");
-    const int64_t T = (int64_t)P.cam.tx * P.cam.ty;
-    k_composite_fwd<<<(unsigned)T, CT, 0, stream>>>(P, out_rgb, out_depth, out_alpha, state_T, state_last);
-    GM_LAUNCH_CHECK();
-    return GM_OK;
-}
-
-gm_status gm_composite_hybrid_bwd(const gm_camera* cam, int32_t N, const float* rec, const int32_t* tile_ranges,
-                                  const int32_t* sorted_ids, const int32_t* face_id, const float* depth,
-                                  const gm_mesh* mesh, const float* vscreen, const gm_light* light,
-                                  const float* bg, float softness, const float* state_T,
-                                  const int32_t* state_last, const float* g_rgb, const float* g_depth,
-                                  const float* g_alpha, float* g_rec, float* g_mesh_rgb, float* g_mesh_depth,
+                                  float* out_alpha, float* state_T, int32_t* state_last, float* state_cm,
                                   hipStream_t stream)
 {
     clear_error();
@@ -551,8 +687,32 @@ gm_status gm_composite_hybrid_bwd(const gm_camera* cam, int32_t N, const float* 
     if (gm_status s = fill_params(P, cam, rec, tile_ranges, sorted_ids, face_id, depth, mesh, vscreen, light,
                                   bg, softness))
         return s;
+    GM_ARG_CHECK(out_rgb && out_depth && out_alpha && state_T && state_last && state_cm, "an output is NULL");
+    const int64_t T = (int64_t)P.cam.tx * P.cam.ty;
+    const int64_t HW = (int64_t)P.cam.width * P.cam.height;
+    k_shade<<<(unsigned)div_up(HW, 256), 256, 0, stream>>>(P, state_cm);
+    GM_LAUNCH_CHECK();
+    k_composite_fwd<<<(unsigned)T, CT, 0, stream>>>(P, state_cm, out_rgb, out_depth, out_alpha, state_T,
+                                                   state_last);
+    GM_LAUNCH_CHECK();
+    return GM_OK;
+}
+
+gm_status gm_composite_hybrid_bwd(const gm_camera* cam, int32_t N, const float* rec, const int32_t* tile_ranges,
+                                  const int32_t* sorted_ids, const int32_t* face_id, const float* depth,
+                                  float softness, const float* state_T, const int32_t* state_last,
+                                  const float* state_cm, const float* g_rgb, const float* g_depth,
+                                  const float* g_alpha, float* g_rec, float* g_mesh_rgb, float* g_mesh_depth,
+                                  hipStream_t stream)
+{
+    clear_error();
+    CompParams P;
+    const float zero3[3] = {0.0f, 0.0f, 0.0f};
+    if (gm_status s = fill_params(P, cam, rec, tile_ranges, sorted_ids, face_id, depth, nullptr, nullptr, nullptr,
+                                  zero3, softness))
+        return s;
     GM_ARG_CHECK(N >= 0, "N = %d is negative", N);
-    GM_ARG_CHECK(state_T && state_last && g_rgb, "state or g_rgb is NULL");
+    GM_ARG_CHECK(state_T && state_last && state_cm && g_rgb, "state or g_rgb is NULL");
     GM_ARG_CHECK(N == 0 || g_rec, "g_rec is NULL");
     const int64_t T = (int64_t)P.cam.tx * P.cam.ty;
     if (N > 0) {
@@ -560,8 +720,8 @@ gm_status gm_composite_hybrid_bwd(const gm_camera* cam, int32_t N, const float* 
         k_zero_f32<<<(unsigned)div_up(n, 256), 256, 0, stream>>>(g_rec, n);
         GM_LAUNCH_CHECK();
     }
-    k_composite_bwd<<<(unsigned)T, CT, 0, stream>>>(P, state_T, state_last, g_rgb, g_depth, g_alpha, g_rec,
-                                                   g_mesh_rgb, g_mesh_depth);
+    k_composite_bwd<<<(unsigned)T, CT, 0, stream>>>(P, state_T, state_last, state_cm, g_rgb, g_depth, g_alpha,
+                                                   g_rec, g_mesh_rgb, g_mesh_depth);
     GM_LAUNCH_CHECK();
     return GM_OK;
 }

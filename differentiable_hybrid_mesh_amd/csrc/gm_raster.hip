@@ -106,6 +106,7 @@ k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
     __shared__ double s_u[3][ZB_BATCH], s_v[3][ZB_BATCH], s_z[3][ZB_BATCH];
     __shared__ double s_du[3][ZB_BATCH], s_dv[3][ZB_BATCH], s_A[ZB_BATCH];
     __shared__ int s_f[ZB_BATCH];
+    __shared__ int4 s_box[ZB_BATCH];  // pixel box widened by one pixel: x0, x1, y0, y1
     __shared__ float s_red[ZB_THREADS / 64];
 
     const int tile = blockIdx.x;
@@ -141,9 +142,18 @@ k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
             s_dv[2][j] = v[1] - v[0];
             s_A[j] = (u[1] - u[0]) * (v[2] - v[0]) - (v[1] - v[0]) * (u[2] - u[0]);
             s_f[j] = f;
+            // a pixel centre covered by the triangle lies in its bounding box; the box
+            // is widened by a pixel so that this integer reject never overrides the
+            // fp64 edge test
+            const double umin = fmin(fmin(u[0], u[1]), u[2]), umax = fmax(fmax(u[0], u[1]), u[2]);
+            const double vmin = fmin(fmin(v[0], v[1]), v[2]), vmax = fmax(fmax(v[0], v[1]), v[2]);
+            s_box[j] = make_int4((int)fmax(floor(umin) - 1.0, -2.0), (int)fmin(ceil(umax) + 1.0, 32768.0),
+                                 (int)fmax(floor(vmin) - 1.0, -2.0), (int)fmin(ceil(vmax) + 1.0, 32768.0));
         }
         __syncthreads();
         for (int j = 0; j < nb; ++j) {
+            const int4 bx = s_box[j];
+            if (px < bx.x || px > bx.y || py < bx.z || py > bx.w) continue;
             // E_k = (b.u - a.u)(p.v - a.v) - (b.v - a.v)(p.u - a.u)
             const double E0 = s_du[0][j] * (pv - s_v[1][j]) - s_dv[0][j] * (pu - s_u[1][j]);
             const double E1 = s_du[1][j] * (pv - s_v[2][j]) - s_dv[1][j] * (pu - s_u[2][j]);

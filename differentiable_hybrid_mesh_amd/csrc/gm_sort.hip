@@ -195,50 +195,54 @@ __device__ inline bool culled(const DevCamera& cam, const CullParams& cp, int tx
     return bound < (1.0f / 255.0f) * (1.0f - 1e-3f);
 }
 
-__global__ void __launch_bounds__(256)
-k_count_pairs(DevCamera cam, CullParams cp, const long long* __restrict__ d_nvis, int N,
-              const int32_t* __restrict__ order, const float* __restrict__ rec, int32_t* __restrict__ cnt)
-{
-    const int j = blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= N) return;
-    if (j >= *d_nvis) {
-        cnt[j] = 0;
-        return;
-    }
-    const int i = order[j];
-    const float4* r = reinterpret_cast<const float4*>(rec + (size_t)i * GM_REC);
-    const float4 a = r[0], b = r[1], c = r[2], d = r[3];
-    const int lo = __float_as_int(d.y), hi = __float_as_int(d.z);
-    const int x0 = lo & 0xffff, y0 = lo >> 16, x1 = hi & 0xffff, y1 = hi >> 16;
-    int n = 0;
-    for (int ty = y0; ty < y1; ++ty)
-        for (int tx = x0; tx < x1; ++tx)
-            n += culled(cam, cp, tx, ty, a.x, a.y, c.y, c.z, c.w, d.x, b.y) ? 0 : 1;
-    cnt[j] = n;
-}
+// One wave per Gaussian (in depth order): lane l tests tile l of the rect, a ballot
+// gives every surviving tile its rank, so counts and emitted pairs need no per-lane
+// loops and the pair writes of a wave are contiguous.  Rect tiles are visited in
+// row-major order.
+constexpr int PW_WAVES = 4;  // waves per 256-thread block
 
-__global__ void __launch_bounds__(256)
-k_emit_pairs(DevCamera cam, CullParams cp, const long long* __restrict__ d_nvis,
-             const int32_t* __restrict__ order, const float* __restrict__ rec,
-             const int32_t* __restrict__ off, uint32_t* __restrict__ tkeys, int32_t* __restrict__ tvals)
+template <bool EMIT>
+__global__ void __launch_bounds__(64 * PW_WAVES)
+k_pairs(DevCamera cam, CullParams cp, const long long* __restrict__ d_nvis, int N,
+        const int32_t* __restrict__ order, const float* __restrict__ rec, int32_t* __restrict__ cnt,
+        const int32_t* __restrict__ off, uint32_t* __restrict__ tkeys, int32_t* __restrict__ tvals)
 {
-    const int j = blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= *d_nvis) return;
-    const int i = order[j];
-    const float4* r = reinterpret_cast<const float4*>(rec + (size_t)i * GM_REC);
-    const float4 a = r[0], b = r[1], c = r[2], d = r[3];
-    const int lo = __float_as_int(d.y), hi = __float_as_int(d.z);
-    const int x0 = lo & 0xffff, y0 = lo >> 16, x1 = hi & 0xffff, y1 = hi >> 16;
-    int p = off[j];
-    const int pend = off[j + 1];  // the counting pass took the same decisions; never write past it
-    for (int ty = y0; ty < y1; ++ty)
-        for (int tx = x0; tx < x1; ++tx) {
-            if (culled(cam, cp, tx, ty, a.x, a.y, c.y, c.z, c.w, d.x, b.y)) continue;
-            if (p >= pend) return;
-            tkeys[p] = (uint32_t)(ty * cam.tx + tx);
-            tvals[p] = i;
-            ++p;
+    const int lane = threadIdx.x & 63;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    const long long nvis = *d_nvis;
+    const int nwaves = gridDim.x * PW_WAVES;
+    for (int j = blockIdx.x * PW_WAVES + (threadIdx.x >> 6); j < N; j += nwaves) {
+        if (j >= nvis) {
+            if (!EMIT && lane == 0) cnt[j] = 0;
+            continue;
         }
+        const int i = order[j];
+        const float4* r = reinterpret_cast<const float4*>(rec + (size_t)i * GM_REC);
+        const float4 a = r[0], b = r[1], c = r[2], d = r[3];
+        const int lo = __float_as_int(d.y), hi = __float_as_int(d.z);
+        const int x0 = lo & 0xffff, y0 = lo >> 16, x1 = hi & 0xffff, y1 = hi >> 16;
+        const int w = x1 - x0, nt = w * (y1 - y0);
+        int p = EMIT ? off[j] : 0;
+        const int pend = EMIT ? off[j + 1] : 0;  // the counting pass took the same decisions
+        for (int c0 = 0; c0 < nt; c0 += 64) {
+            const int t = c0 + lane;
+            bool keep = false;
+            int tx = 0, ty = 0;
+            if (t < nt) {
+                ty = y0 + t / w;
+                tx = x0 + t % w;
+                keep = !culled(cam, cp, tx, ty, a.x, a.y, c.y, c.z, c.w, d.x, b.y);
+            }
+            const unsigned long long m = __ballot(keep);
+            if (EMIT && keep && p + __popcll(m & lt) < pend) {
+                const int q = p + __popcll(m & lt);
+                tkeys[q] = (uint32_t)(ty * cam.tx + tx);
+                tvals[q] = i;
+            }
+            p += __popcll(m);
+        }
+        if (!EMIT && lane == 0) cnt[j] = p;
+    }
 }
 
 __global__ void k_tile_ranges(const uint32_t* __restrict__ keys, int64_t K, int32_t* __restrict__ ranges)
@@ -336,7 +340,9 @@ gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec, c
     const int32_t* order = w.dva;  // 4 passes: back in the first buffer pair
     // 2. surviving tiles per Gaussian (depth order), scan, read back the total
     CullParams cp{tile_dmax, softness};
-    k_count_pairs<<<gN, 256, 0, stream>>>(dc, cp, w.nvis, N, order, rec, w.flag);
+    const unsigned gW = (unsigned)std::min<int64_t>(div_up(N, PW_WAVES), 16384);
+    k_pairs<false><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, w.nvis, N, order, rec, w.flag, nullptr, nullptr,
+                                                    nullptr);
     GM_LAUNCH_CHECK();
     if (gm_status s = exclusive_scan(w.flag, w.pos, N, w.npairs, w.aux, stream)) return s;
     int64_t K = 0;
@@ -353,7 +359,7 @@ gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec, c
     uint32_t* ka = w.tka;
     int32_t* va = (npass % 2 == 0) ? sorted_ids : w.tva;
     int32_t* vb = (npass % 2 == 0) ? w.tva : sorted_ids;
-    k_emit_pairs<<<gN, 256, 0, stream>>>(dc, cp, w.nvis, order, rec, w.pos, ka, va);
+    k_pairs<true><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, w.nvis, N, order, rec, nullptr, w.pos, ka, va);
     GM_LAUNCH_CHECK();
     if (gm_status s = radix_sort(ka, va, w.tkb, vb, npass, 0, w.npairs, K, w.aux, stream)) return s;
     const uint32_t* kfin = (npass % 2 == 0) ? w.tka : w.tkb;

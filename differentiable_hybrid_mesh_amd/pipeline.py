@@ -119,6 +119,7 @@ class Renderer:
         self.out_alpha = torch.empty((self.H, self.W), dtype=f32, device=dev)
         self.state_T = torch.empty((self.H, self.W), dtype=f32, device=dev)
         self.state_last = torch.empty((self.H, self.W), dtype=i32, device=dev)
+        self.state_cm = torch.empty((self.H, self.W, 3), dtype=f32, device=dev)
         self.g_rec = torch.empty((max(self.N, 1), G.GM_GRAD), dtype=f32, device=dev)
         self.g_mesh_rgb = torch.empty((self.H, self.W, 3), dtype=f32, device=dev)
         self.g_mesh_depth = torch.empty((self.H, self.W), dtype=f32, device=dev)
@@ -168,14 +169,15 @@ class Renderer:
         ds, s = self.ds, self.ds.scene
         G.gm_composite_hybrid_fwd(ds.cams[view], self.rec, self.tile_ranges, self.sorted_ids, self.face_id,
                                   self.depth, ds.mesh, self.vscreen, ds.light, s.bg, s.softness, self.out_rgb,
-                                  self.out_depth, self.out_alpha, self.state_T, self.state_last, _stream())
+                                  self.out_depth, self.out_alpha, self.state_T, self.state_last, self.state_cm,
+                                  _stream())
 
     def composite_bwd(self, view: int, g_rgb, g_depth=None, g_alpha=None):
         ds, s = self.ds, self.ds.scene
         G.gm_composite_hybrid_bwd(ds.cams[view], self.N, self.rec, self.tile_ranges, self.sorted_ids,
-                                  self.face_id, self.depth, ds.mesh, self.vscreen, ds.light, s.bg, s.softness,
-                                  self.state_T, self.state_last, g_rgb, g_depth, g_alpha, self.g_rec,
-                                  self.g_mesh_rgb, self.g_mesh_depth, _stream())
+                                  self.face_id, self.depth, s.softness, self.state_T, self.state_last,
+                                  self.state_cm, g_rgb, g_depth, g_alpha, self.g_rec, self.g_mesh_rgb,
+                                  self.g_mesh_depth, _stream())
 
     # -- whole passes -----------------------------------------------------------
     def forward(self, view: int = 0, cull: bool = True):

@@ -203,7 +203,8 @@ gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec,
  * Inputs: the outputs of calls 1-4; bg (host, 3 floats); softness >= 0.
  * Outputs: out_rgb [H][W][3], out_depth [H][W], out_alpha [H][W]; state for the
  * backward: state_T [H][W] (final transmittance), state_last [H][W] (index in the
- * tile list + 1 of the last included entry).  Deterministic.
+ * tile list + 1 of the last included entry), state_cm [H][W][3] (the colour behind
+ * the Gaussians: c_m on the mesh, bg elsewhere).  Deterministic.
  * ------------------------------------------------------------------------- */
 gm_status gm_composite_hybrid_fwd(const gm_camera* cam, const float* rec,
                                   const int32_t* tile_ranges, const int32_t* sorted_ids,
@@ -211,29 +212,30 @@ gm_status gm_composite_hybrid_fwd(const gm_camera* cam, const float* rec,
                                   const float* vscreen, const gm_light* light, const float* bg,
                                   float softness, float* out_rgb, float* out_depth,
                                   float* out_alpha, float* state_T, int32_t* state_last,
-                                  hipStream_t stream);
+                                  float* state_cm, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * 6. gm_composite_hybrid_bwd — reverse mode of call 5.
  * README "Hybrid rendering": everything is differentiable, Gaussian parameters
  * also through the split, and the mesh through its depth and interpolated colour.
  *
- * Inputs: every input of call 5, its state, and upstream gradients g_rgb
- * [H][W][3], g_depth [H][W] (or NULL = 0), g_alpha [H][W] (or NULL = 0).
+ * Inputs: the camera, records, lists, z-buffer and softness given to call 5, its
+ * three state buffers, and upstream gradients g_rgb [H][W][3], g_depth [H][W] (or
+ * NULL = 0), g_alpha [H][W] (or NULL = 0).
  * Outputs (zero-filled by the call, then accumulated with float atomics):
  *   g_rec [N][GM_GRAD]: d/d(u, v, Q00, Q01, Q11, opacity, r, g, b, z_c, g0, g1, sigma);
  *   g_mesh_rgb [H][W][3] = dL/dc_m, g_mesh_depth [H][W] = dL/dD (either may be NULL).
  * Skipped and stopped entries get no gradient; the clamp at 0.99 has zero
- * derivative; the decisions are not differentiated.
+ * derivative; the decisions are not differentiated.  The transmittance before each
+ * entry is recovered from the final one by division (1 - alpha_F >= 0.01).
  * ------------------------------------------------------------------------- */
 gm_status gm_composite_hybrid_bwd(const gm_camera* cam, int32_t N, const float* rec,
                                   const int32_t* tile_ranges, const int32_t* sorted_ids,
-                                  const int32_t* face_id, const float* depth, const gm_mesh* mesh,
-                                  const float* vscreen, const gm_light* light, const float* bg,
-                                  float softness, const float* state_T, const int32_t* state_last,
-                                  const float* g_rgb, const float* g_depth, const float* g_alpha,
-                                  float* g_rec, float* g_mesh_rgb, float* g_mesh_depth,
-                                  hipStream_t stream);
+                                  const int32_t* face_id, const float* depth, float softness,
+                                  const float* state_T, const int32_t* state_last,
+                                  const float* state_cm, const float* g_rgb, const float* g_depth,
+                                  const float* g_alpha, float* g_rec, float* g_mesh_rgb,
+                                  float* g_mesh_depth, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Auxiliary.
