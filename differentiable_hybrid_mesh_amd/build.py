@@ -13,6 +13,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libgm.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
@@ -21,7 +22,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-munsafe-fp-atomics", "-fno-gpu-flush-denormals-to-zero",
+    "-munsafe-fp-atomics", "-fno-gpu-flush-denormals-to-zero", f"-I{INCLUDE}",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
 

@@ -217,23 +217,38 @@ struct Staged {
     float4 a;  // u, v, Q00, Q01
     float4 b;  // Q11, opacity, r, g
     float4 c;  // b, z_c, g0, g1
-    float4 d;  // sigma, kappa = 1/(sigma softness), q_skip, -
+    float4 d;  // sigma, kappa = 1/(sigma softness), q_skip, 1/sigma
 };
 
-__device__ __forceinline__ float normal_cdf(float s) { return 0.5f * erfcf(-s * 0.70710678118654752f); }
+// Standard normal CDF Phi(s) and density phi(s) from one exponential.
+// erfc(z) for z >= 0 follows Abramowitz & Stegun, Handbook of Mathematical
+// Functions, formula 7.1.26 (|error| <= 1.5e-7): erfc(z) = t P(t) exp(-z^2),
+// t = 1 / (1 + p z).  With z = |s| / sqrt(2), exp(-z^2) = exp(-s^2 / 2), which is
+// also what phi needs, so the backward gets both for the price of one exp.
+__device__ __forceinline__ float normal_cdf_pdf(float s, float& pdf)
+{
+    const float e = __expf(-0.5f * s * s);
+    pdf = 0.39894228040143268f * e;
+    const float z = fabsf(s) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * z);
+    const float poly = t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+    const float half_tail = 0.5f * poly * e;  // Phi(-|s|)
+    return s <= 0.0f ? half_tail : 1.0f - half_tail;
+}
 
 // alpha = min(0.99, o exp(-q)); returns alpha_F = alpha f (0 when below the skip
 // threshold before f is formed) and the intermediates the backward needs.  A pair
 // with q above q_skip is below the threshold with margin and exp() is not formed.
 __device__ __forceinline__ float eval_pair(const Staged& g, float pxc, float pyc, bool on, float D,
                                            float softness, float& dx, float& dy, float& G, float& alpha,
-                                           float& f, float& s)
+                                           float& f, float& s, float& pdf)
 {
     dx = pxc - g.a.x;
     dy = pyc - g.a.y;
     const float q = 0.5f * (g.a.z * dx * dx + g.b.x * dy * dy) + g.a.w * dx * dy;
     f = 1.0f;
     s = 0.0f;
+    pdf = 0.0f;
     if (q > g.d.z) {
         G = 0.0f;
         alpha = 0.0f;
@@ -246,7 +261,7 @@ __device__ __forceinline__ float eval_pair(const Staged& g, float pxc, float pyc
         const float num = (D - g.c.y) - (g.c.z * dx + g.c.w * dy);
         if (softness > 0.0f) {
             s = num * g.d.y;
-            f = normal_cdf(s);
+            f = normal_cdf_pdf(s, pdf);
         } else {
             f = num > 0.0f ? 1.0f : 0.0f;
         }
@@ -273,7 +288,7 @@ __device__ __forceinline__ uint32_t stage_record(const CompParams& P, float4 ra,
     const float lq = o > 0.0f ? logf(255.0f * o) : -1.0f;
     const float qs = o > 0.0f ? lq + 1e-4f + 1e-4f * fabsf(lq) : -1.0f;
     const float kap = P.softness > 0.0f ? 1.0f / (rd.x * P.softness) : 0.0f;
-    st.d = make_float4(rd.x, kap, qs, 0.0f);
+    st.d = make_float4(rd.x, kap, qs, 1.0f / rd.x);
     if (!(qs >= 0.0f)) return 0u;  // o exp(-q) < 1/255 everywhere
     const float Q00 = ra.z, Q01 = ra.w, Q11 = rb.x;
     const float detQ = Q00 * Q11 - Q01 * Q01;
@@ -378,8 +393,8 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, float* __restr
                 m &= m - 1;
                 if (!done) {
                     const Staged& g = s_g[k];
-                    float dx, dy, G, al, f, s;
-                    const float aF = eval_pair(g, pxc, pyc, on, D, P.softness, dx, dy, G, al, f, s);
+                    float dx, dy, G, al, f, s, pdf;
+                    const float aF = eval_pair(g, pxc, pyc, on, D, P.softness, dx, dy, G, al, f, s, pdf);
                     if (aF >= SKIP_ALPHA) {
                         const float Tn = T * (1.0f - aF);
                         if (Tn < STOP_T) {
@@ -416,35 +431,45 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, float* __restr
 // backward
 // ---------------------------------------------------------------------------
 // Sum 16 per-lane values over the 64 lanes of a wave with a halving ("transpose")
-// reduction: at each butterfly step a lane keeps half of its values and sends the
-// other half to its partner, so 16 values need 8+4+2+1+1+1 = 17 shuffles instead of
-// 16*6.  On return lane l holds the wave total of value (l >> 2) when (l & 3) == 0.
+// reduction: at each butterfly step a lane keeps half of its values and receives its
+// partner's copy of them, so 16 values need 8+4+2+1 exchanges plus two full steps
+// instead of 16*6.  The exchanges use gfx950's cross-half lane swaps (lanes 32-63
+// with 0-31, odd 16-lane rows with even ones) and DPP row/quad moves, all VALU.
+// On return lane l holds the wave total of value (l >> 2) when (l & 3) == 0.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
 __device__ __forceinline__ float wave_sum16(const float* v, int lane)
 {
     float a[8], b[4], c[2];
-    const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8, h2 = lane & 4;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float send = h5 ? v[i] : v[8 + i];
-        const float keep = h5 ? v[8 + i] : v[i];
-        a[i] = keep + __shfl_xor(send, 32, 64);
+    for (int i = 0; i < 8; ++i) {  // lanes 0-31 keep v[i], lanes 32-63 keep v[8+i]
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[8 + i]), false,
+                                                        false);
+        a[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float send = h4 ? a[i] : a[4 + i];
-        const float keep = h4 ? a[4 + i] : a[i];
-        b[i] = keep + __shfl_xor(send, 16, 64);
+    for (int i = 0; i < 4; ++i) {  // even 16-lane rows keep a[i], odd rows a[4+i]
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[i]), __float_as_uint(a[4 + i]), false,
+                                                        false);
+        b[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
+    const bool h3 = lane & 8, h2 = lane & 4;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 2; ++i) {  // partner: lane ^ 8 (rotate a 16-lane row by 8)
         const float send = h3 ? b[i] : b[2 + i];
         const float keep = h3 ? b[2 + i] : b[i];
-        c[i] = keep + __shfl_xor(send, 8, 64);
+        c[i] = keep + dpp<0x128>(send);
     }
+    // partner: the mirrored lane in the 8-lane half row (bit 2 flipped); the two
+    // quad steps below sum the four lanes of each half, so the pairing is exact
     const float send = h2 ? c[0] : c[1];
-    float d = (h2 ? c[1] : c[0]) + __shfl_xor(send, 4, 64);
-    d += __shfl_xor(d, 2, 64);
-    d += __shfl_xor(d, 1, 64);
+    float d = (h2 ? c[1] : c[0]) + dpp<0x141>(send);
+    d += dpp<0x4E>(d);  // quad_perm [2,3,0,1]
+    d += dpp<0xB1>(d);  // quad_perm [1,0,3,2]
     return d;
 }
 
@@ -544,15 +569,17 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
                 for (int c = 0; c < 16; ++c) gr[c] = 0.0f;
                 bool act = false;
                 if (rel < last) {
-                    float dx, dy, G, al, f, s;
-                    const float aF = eval_pair(g, pxc, pyc, on, D, P.softness, dx, dy, G, al, f, s);
+                    float dx, dy, G, al, f, s, pdf;
+                    const float aF = eval_pair(g, pxc, pyc, on, D, P.softness, dx, dy, G, al, f, s, pdf);
                     if (aF >= SKIP_ALPHA) {
                         act = true;
-                        const float om = 1.0f - aF;
-                        const float Ti = T / om;
+                        // 1 - alpha_F >= 0.01: a hardware reciprocal (1 ulp) keeps the
+                        // recovered transmittance far inside the gradient tolerance
+                        const float iom = __builtin_amdgcn_rcpf(1.0f - aF);
+                        const float Ti = T * iom;
                         const float w = aF * Ti;
                         const float Vv = GC0 * g.b.z + GC1 * g.b.w + GC2 * g.c.x + GZ * g.c.y;
-                        const float daF = Ti * Vv - acc / om;
+                        const float daF = Ti * Vv - acc * iom;
                         acc += w * Vv;
                         T = Ti;
                         gr[6] = w * GC0;
@@ -570,15 +597,14 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
                             gr[1] = H * (g.a.w * dx + g.b.x * dy);
                         }
                         if (on && P.softness > 0.0f) {
-                            const float phi = 0.39894228040143268f * __expf(-0.5f * s * s);
-                            const float ds = al * phi * daF;
+                            const float ds = al * pdf * daF;
                             const float kap = g.d.y;
                             gr[9] -= kap * ds;
                             gr[10] = -kap * ds * dx;
                             gr[11] = -kap * ds * dy;
                             gr[0] += kap * ds * g.c.z;
                             gr[1] += kap * ds * g.c.w;
-                            gr[12] = -ds * s / g.d.x;
+                            gr[12] = -ds * s * g.d.w;
                             gD += kap * ds;
                         }
                     }

@@ -7,7 +7,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/gm.h"
+#include "gm.h"
 
 namespace gm {
 

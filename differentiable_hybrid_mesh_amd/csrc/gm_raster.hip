@@ -95,22 +95,34 @@ __global__ void k_bin_scatter(DevCamera cam, int F, const int2* __restrict__ fac
         }
 }
 
+// Triangle setup as staged in LDS: one 128-byte record, read by a whole wave at
+// the same address (broadcast).
+struct TriSetup {
+    double u[3], v[3];   // screen vertices
+    double du[3], dv[3]; // edge deltas b - a of edges (v1,v2), (v2,v0), (v0,v1)
+    double z[3];         // camera depths
+    double A;            // twice the signed area
+};
+
 // One block per tile, one thread per pixel.  Triangles of the tile's bin are set up
-// in fp64 by one thread each and staged in LDS; every pixel then tests the batch.
+// in fp64 by one thread each and staged in LDS together with their pixel box and a
+// 4-bit mask of the 16x4-pixel waves the box reaches; each wave then walks only the
+// triangles of its mask, and each pixel only those whose box holds it.
 __global__ void __launch_bounds__(ZB_THREADS)
 k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
           const float* __restrict__ vs, const int32_t* __restrict__ tile_off,
           const int32_t* __restrict__ tile_tris, int32_t* __restrict__ face_id,
           float* __restrict__ depth, float* __restrict__ tile_dmax)
 {
-    __shared__ double s_u[3][ZB_BATCH], s_v[3][ZB_BATCH], s_z[3][ZB_BATCH];
-    __shared__ double s_du[3][ZB_BATCH], s_dv[3][ZB_BATCH], s_A[ZB_BATCH];
+    __shared__ TriSetup s_t[ZB_BATCH];
     __shared__ int s_f[ZB_BATCH];
     __shared__ int4 s_box[ZB_BATCH];  // pixel box widened by one pixel: x0, x1, y0, y1
+    __shared__ uint8_t s_m[ZB_BATCH];
     __shared__ float s_red[ZB_THREADS / 64];
 
     const int tile = blockIdx.x;
     const int tx = tile % cam.tx, ty = tile / cam.tx;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int px = tx * GM_TILE + (threadIdx.x & 15), py = ty * GM_TILE + (threadIdx.x >> 4);
     const bool inside = px < cam.width && py < cam.height;
     const double pu = px + 0.5, pv = py + 0.5;
@@ -121,53 +133,65 @@ k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
     for (int b0 = start; b0 < end; b0 += ZB_BATCH) {
         const int nb = min(ZB_BATCH, end - b0);
         __syncthreads();
-        if (threadIdx.x < nb) {
-            const int f = tile_tris[b0 + threadIdx.x];
+        if (threadIdx.x < ZB_BATCH) {
             const int j = threadIdx.x;
-            double u[3], v[3];
-            for (int k = 0; k < 3; ++k) {
-                const int vi = faces[k * F + f];
-                u[k] = (double)vs[vi];
-                v[k] = (double)vs[V + vi];
-                s_u[k][j] = u[k];
-                s_v[k][j] = v[k];
-                s_z[k][j] = (double)vs[2 * V + vi];
+            uint8_t m = 0;
+            if (j < nb) {
+                const int f = tile_tris[b0 + j];
+                TriSetup t;
+                for (int k = 0; k < 3; ++k) {
+                    const int vi = faces[k * F + f];
+                    t.u[k] = (double)vs[vi];
+                    t.v[k] = (double)vs[V + vi];
+                    t.z[k] = (double)vs[2 * V + vi];
+                }
+                t.du[0] = t.u[2] - t.u[1];
+                t.dv[0] = t.v[2] - t.v[1];
+                t.du[1] = t.u[0] - t.u[2];
+                t.dv[1] = t.v[0] - t.v[2];
+                t.du[2] = t.u[1] - t.u[0];
+                t.dv[2] = t.v[1] - t.v[0];
+                t.A = (t.u[1] - t.u[0]) * (t.v[2] - t.v[0]) - (t.v[1] - t.v[0]) * (t.u[2] - t.u[0]);
+                s_t[j] = t;
+                s_f[j] = f;
+                // a pixel centre covered by the triangle lies in its bounding box; the
+                // box is widened by a pixel so that this integer reject never overrides
+                // the fp64 edge test
+                const double umin = fmin(fmin(t.u[0], t.u[1]), t.u[2]), umax = fmax(fmax(t.u[0], t.u[1]), t.u[2]);
+                const double vmin = fmin(fmin(t.v[0], t.v[1]), t.v[2]), vmax = fmax(fmax(t.v[0], t.v[1]), t.v[2]);
+                const int4 bx = make_int4((int)fmax(floor(umin) - 1.0, -2.0), (int)fmin(ceil(umax) + 1.0, 32768.0),
+                                          (int)fmax(floor(vmin) - 1.0, -2.0), (int)fmin(ceil(vmax) + 1.0, 32768.0));
+                s_box[j] = bx;
+                if (bx.x <= tx * GM_TILE + 15 && bx.y >= tx * GM_TILE)
+                    for (int w = 0; w < 4; ++w)
+                        if (bx.z <= ty * GM_TILE + 4 * w + 3 && bx.w >= ty * GM_TILE + 4 * w) m |= 1u << w;
             }
-            // edges (v1,v2), (v2,v0), (v0,v1): a = ea[k], b = eb[k]
-            s_du[0][j] = u[2] - u[1];
-            s_dv[0][j] = v[2] - v[1];
-            s_du[1][j] = u[0] - u[2];
-            s_dv[1][j] = v[0] - v[2];
-            s_du[2][j] = u[1] - u[0];
-            s_dv[2][j] = v[1] - v[0];
-            s_A[j] = (u[1] - u[0]) * (v[2] - v[0]) - (v[1] - v[0]) * (u[2] - u[0]);
-            s_f[j] = f;
-            // a pixel centre covered by the triangle lies in its bounding box; the box
-            // is widened by a pixel so that this integer reject never overrides the
-            // fp64 edge test
-            const double umin = fmin(fmin(u[0], u[1]), u[2]), umax = fmax(fmax(u[0], u[1]), u[2]);
-            const double vmin = fmin(fmin(v[0], v[1]), v[2]), vmax = fmax(fmax(v[0], v[1]), v[2]);
-            s_box[j] = make_int4((int)fmax(floor(umin) - 1.0, -2.0), (int)fmin(ceil(umax) + 1.0, 32768.0),
-                                 (int)fmax(floor(vmin) - 1.0, -2.0), (int)fmin(ceil(vmax) + 1.0, 32768.0));
+            s_m[j] = m;
         }
         __syncthreads();
-        for (int j = 0; j < nb; ++j) {
-            const int4 bx = s_box[j];
-            if (px < bx.x || px > bx.y || py < bx.z || py > bx.w) continue;
-            // E_k = (b.u - a.u)(p.v - a.v) - (b.v - a.v)(p.u - a.u)
-            const double E0 = s_du[0][j] * (pv - s_v[1][j]) - s_dv[0][j] * (pu - s_u[1][j]);
-            const double E1 = s_du[1][j] * (pv - s_v[2][j]) - s_dv[1][j] * (pu - s_u[2][j]);
-            const double E2 = s_du[2][j] * (pv - s_v[0][j]) - s_dv[2][j] * (pu - s_u[0][j]);
-            const double A = s_A[j];
-            const bool cov = A > 0 ? (E0 >= 0 && E1 >= 0 && E2 >= 0) : (E0 <= 0 && E1 <= 0 && E2 <= 0);
-            if (!cov) continue;
-            const double l0 = E0 / A, l1 = E1 / A, l2 = E2 / A;
-            const double inv = (l0 / s_z[0][j] + l1 / s_z[1][j]) + l2 / s_z[2][j];
-            const double z = 1.0 / inv;
-            const int f = s_f[j];
-            if (z < best || (z == best && f < bid)) {
-                best = z;
-                bid = f;
+        for (int i = 0; i < ZB_BATCH / 64; ++i) {
+            unsigned long long mm = __ballot((s_m[i * 64 + lane] >> wave) & 1);
+            while (mm) {
+                const int j = i * 64 + __builtin_ctzll(mm);
+                mm &= mm - 1;
+                const int4 bx = s_box[j];
+                if (px < bx.x || px > bx.y || py < bx.z || py > bx.w) continue;
+                const TriSetup& t = s_t[j];
+                // E_k = (b.u - a.u)(p.v - a.v) - (b.v - a.v)(p.u - a.u)
+                const double E0 = t.du[0] * (pv - t.v[1]) - t.dv[0] * (pu - t.u[1]);
+                const double E1 = t.du[1] * (pv - t.v[2]) - t.dv[1] * (pu - t.u[2]);
+                const double E2 = t.du[2] * (pv - t.v[0]) - t.dv[2] * (pu - t.u[0]);
+                const double A = t.A;
+                const bool cov = A > 0 ? (E0 >= 0 && E1 >= 0 && E2 >= 0) : (E0 <= 0 && E1 <= 0 && E2 <= 0);
+                if (!cov) continue;
+                const double l0 = E0 / A, l1 = E1 / A, l2 = E2 / A;
+                const double inv = (l0 / t.z[0] + l1 / t.z[1]) + l2 / t.z[2];
+                const double z = 1.0 / inv;
+                const int f = s_f[j];
+                if (z < best || (z == best && f < bid)) {
+                    best = z;
+                    bid = f;
+                }
             }
         }
     }
@@ -177,10 +201,10 @@ k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
         depth[py * cam.width + px] = d;
     }
     // tile_dmax: max depth over in-image pixels, +inf when any of them is empty
-    float m = inside ? d : -INFINITY;
+    float mx = inside ? d : -INFINITY;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = m;
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) s_red[wave] = mx;
     __syncthreads();
     if (threadIdx.x == 0) {
         float r = s_red[0];

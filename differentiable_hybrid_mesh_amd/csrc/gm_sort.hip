@@ -48,21 +48,43 @@ k_radix_hist(const uint32_t* __restrict__ keys, const long long* __restrict__ d_
     hist[threadIdx.x * nblocks + blockIdx.x] = h[threadIdx.x];
 }
 
+// Stable scatter of one LSD pass.  Every key gets its rank inside the block in 16
+// rounds of 256 (wave ballots give the rank among lanes holding the same digit,
+// per-wave digit counts in LDS the rank across waves, a running count per digit the
+// rank across rounds); keys are first placed in LDS in digit order and then written
+// out in that order, so each digit's run leaves the block as contiguous stores.
 __global__ void __launch_bounds__(RS_THREADS)
 k_radix_scatter(const uint32_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
-                const long long* __restrict__ d_count, int shift, int nblocks,
-                const int32_t* __restrict__ offs, uint32_t* __restrict__ keys_out,
-                int32_t* __restrict__ vals_out)
+                const long long* __restrict__ d_count, int shift, int nblocks, const int32_t* __restrict__ hist,
+                const int32_t* __restrict__ offs, uint32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out)
 {
-    __shared__ int32_t s_base[RS_RADIX];            // global start of each digit for this block
+    __shared__ uint32_t s_k[RS_CHUNK];
+    __shared__ int32_t s_v[RS_CHUNK];
+    __shared__ int32_t s_lstart[RS_RADIX], s_goff[RS_RADIX], s_run[RS_RADIX];
     __shared__ int32_t s_wcnt[RS_THREADS / 64][RS_RADIX];
+    __shared__ int32_t s_wsum[RS_THREADS / 64];
     const long long n = *d_count;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const unsigned long long lt = (1ull << lane) - 1ull;
-    s_base[threadIdx.x] = offs[threadIdx.x * nblocks + blockIdx.x];
     const long long base = (long long)blockIdx.x * RS_CHUNK;
+    if (base >= n) return;
+    // block-local start of every digit: exclusive scan of this block's histogram
+    const int c = hist[t * nblocks + blockIdx.x];
+    int x = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) s_wsum[wave] = x;
+    s_goff[t] = offs[t * nblocks + blockIdx.x];
+    s_run[t] = 0;
+    __syncthreads();
+    int wo = 0;
+    for (int w = 0; w < wave; ++w) wo += s_wsum[w];
+    s_lstart[t] = wo + x - c;
     for (int k = 0; k < RS_ITEMS; ++k) {
-        const long long e = base + (long long)k * RS_THREADS + threadIdx.x;
+        const long long e = base + (long long)k * RS_THREADS + t;
         const bool act = e < n;
         uint32_t key = 0;
         int32_t val = 0;
@@ -71,9 +93,8 @@ k_radix_scatter(const uint32_t* __restrict__ keys_in, const int32_t* __restrict_
             val = vals_in[e];
         }
         const int d = (key >> shift) & 0xff;
-        for (int w = 0; w < RS_THREADS / 64; ++w) s_wcnt[w][threadIdx.x] = 0;
+        for (int w = 0; w < RS_THREADS / 64; ++w) s_wcnt[w][t] = 0;
         __syncthreads();
-        // lanes holding the same digit
         unsigned long long peers = __ballot(act);
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
@@ -85,16 +106,24 @@ k_radix_scatter(const uint32_t* __restrict__ keys_in, const int32_t* __restrict_
         if (act && rank == 0) s_wcnt[wave][d] = __popcll(peers);
         __syncthreads();
         if (act) {
-            int pos = s_base[d] + rank;
+            int pos = s_lstart[d] + s_run[d] + rank;
             for (int w = 0; w < wave; ++w) pos += s_wcnt[w][d];
-            keys_out[pos] = key;
-            vals_out[pos] = val;
+            s_k[pos] = key;
+            s_v[pos] = val;
         }
         __syncthreads();
         int add = 0;
-        for (int w = 0; w < RS_THREADS / 64; ++w) add += s_wcnt[w][threadIdx.x];
-        s_base[threadIdx.x] += add;
-        __syncthreads();
+        for (int w = 0; w < RS_THREADS / 64; ++w) add += s_wcnt[w][t];
+        s_run[t] += add;
+    }
+    __syncthreads();
+    const int nvalid = (int)min((long long)RS_CHUNK, n - base);
+    for (int p = t; p < nvalid; p += RS_THREADS) {
+        const uint32_t key = s_k[p];
+        const int d = (key >> shift) & 0xff;
+        const int g = s_goff[d] + (p - s_lstart[d]);
+        keys_out[g] = key;
+        vals_out[g] = s_v[p];
     }
 }
 
@@ -130,7 +159,7 @@ static gm_status radix_sort(uint32_t* ka, int32_t* va, uint32_t* kb, int32_t* vb
         k_radix_hist<<<nb, RS_THREADS, 0, stream>>>(kin, d_count, shift, nb, hist);
         GM_LAUNCH_CHECK();
         if (gm_status s = exclusive_scan(hist, offs, (int64_t)RS_RADIX * nb, tot, scan_ws, stream)) return s;
-        k_radix_scatter<<<nb, RS_THREADS, 0, stream>>>(kin, vin, d_count, shift, nb, offs, kout, vout);
+        k_radix_scatter<<<nb, RS_THREADS, 0, stream>>>(kin, vin, d_count, shift, nb, hist, offs, kout, vout);
         GM_LAUNCH_CHECK();
         uint32_t* tk = kin;
         int32_t* tv = vin;
@@ -171,8 +200,23 @@ struct CullParams {
     float softness;
 };
 
+// f must reach (1/255)(1 - 1e-3) / min(0.99, o) for the pair to matter anywhere;
+// the matching split value is s_crit = Phi^-1(that) = -sqrt(2) erfcinv(2 that), once
+// per Gaussian (+inf when even f = 1 cannot reach it).
+__device__ inline float cull_scrit(float o)
+{
+    const float amax = fminf(o, 0.99f);
+    const float y = (1.0f / 255.0f) * (1.0f - 1e-3f) / amax;
+    if (!(y < 1.0f)) return INFINITY;
+    return -1.41421356237309515f * erfcinvf(2.0f * y);
+}
+
+// Pair (tile, Gaussian) is dropped when the tile is fully covered and
+// min(0.99, o) Phi((Dmax + 1e-5 |Dmax| - zmin) / (sigma softness)) < (1/255)(1 - 1e-3),
+// evaluated as s < s_crit.  zmin is the conditional depth's minimum over the four
+// corner pixel centres of the tile.
 __device__ inline bool culled(const DevCamera& cam, const CullParams& cp, int tx, int ty, float u, float v,
-                              float zc, float g0, float g1, float sig, float o)
+                              float zc, float g0, float g1, float sig, float scrit)
 {
     if (!cp.tile_dmax) return false;
     const float dmax = cp.tile_dmax[ty * cam.tx + tx];
@@ -184,64 +228,98 @@ __device__ inline bool culled(const DevCamera& cam, const CullParams& cp, int tx
     const float ay = g1 * (ya - v), by = g1 * (yb - v);
     const float zmin = zc + (fminf(ax, bx) + fminf(ay, by));
     const float lim = dmax + 1e-5f * fabsf(dmax);
-    const float amax = fminf(o, 0.99f);
-    float bound;
-    if (cp.softness > 0.0f) {
-        const float s = (lim - zmin) / (sig * cp.softness);
-        bound = amax * (0.5f * erfcf(-s * 0.70710678118654752f));
-    } else {
-        bound = zmin < lim ? amax : 0.0f;
-    }
-    return bound < (1.0f / 255.0f) * (1.0f - 1e-3f);
+    if (cp.softness > 0.0f) return (lim - zmin) / (sig * cp.softness) < scrit;
+    return !(zmin < lim) || scrit == INFINITY;
 }
 
-// One wave per Gaussian (in depth order): lane l tests tile l of the rect, a ballot
-// gives every surviving tile its rank, so counts and emitted pairs need no per-lane
-// loops and the pair writes of a wave are contiguous.  Rect tiles are visited in
-// row-major order.
+// Pairs of the visible Gaussians in depth order.  A wave takes a chunk of 64
+// consecutive Gaussians, prefix-sums the tile counts of their rects and treats the
+// chunk's (Gaussian, tile) pairs as one flat sequence, 64 per step: lane l finds the
+// Gaussian of flat index f by binary search over the prefix sums in LDS, tests tile
+// f - start(Gaussian) of its rect (row-major), and a ballot ranks the surviving
+// pairs.  The counting pass produces one total per chunk; the emitting pass writes
+// each chunk's pairs as one contiguous run in (depth, id, tile) order.
 constexpr int PW_WAVES = 4;  // waves per 256-thread block
 
 template <bool EMIT>
 __global__ void __launch_bounds__(64 * PW_WAVES)
-k_pairs(DevCamera cam, CullParams cp, const long long* __restrict__ d_nvis, int N,
-        const int32_t* __restrict__ order, const float* __restrict__ rec, int32_t* __restrict__ cnt,
-        const int32_t* __restrict__ off, uint32_t* __restrict__ tkeys, int32_t* __restrict__ tvals)
+k_pairs(DevCamera cam, CullParams cp, const long long* __restrict__ d_nvis, int nchunks,
+        const int32_t* __restrict__ order, const float* __restrict__ rec, int32_t* __restrict__ chunk_cnt,
+        const int32_t* __restrict__ chunk_off, uint32_t* __restrict__ tkeys, int32_t* __restrict__ tvals)
 {
-    const int lane = threadIdx.x & 63;
+    __shared__ float s_f[PW_WAVES][8][64];  // u, v, opacity, z_c, g0, g1, sigma, s_crit
+    __shared__ int s_i[PW_WAVES][4][64];    // rect lo, rect hi, id, inclusive prefix of tile counts
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const unsigned long long lt = (1ull << lane) - 1ull;
-    const long long nvis = *d_nvis;
-    const int nwaves = gridDim.x * PW_WAVES;
-    for (int j = blockIdx.x * PW_WAVES + (threadIdx.x >> 6); j < N; j += nwaves) {
-        if (j >= nvis) {
-            if (!EMIT && lane == 0) cnt[j] = 0;
-            continue;
+    const int nvis = (int)*d_nvis;
+    for (int chunk = blockIdx.x * PW_WAVES + wave; chunk < nchunks; chunk += gridDim.x * PW_WAVES) {
+        const int jl = chunk * 64 + lane;
+        int nt = 0;
+        if (jl < nvis) {
+            const int id = order[jl];
+            const float4* r = reinterpret_cast<const float4*>(rec + (size_t)id * GM_REC);
+            const float4 a = r[0], b = r[1], c = r[2], d = r[3];
+            const int lo = __float_as_int(d.y), hi = __float_as_int(d.z);
+            nt = ((hi & 0xffff) - (lo & 0xffff)) * ((hi >> 16) - (lo >> 16));
+            s_f[wave][0][lane] = a.x;
+            s_f[wave][1][lane] = a.y;
+            s_f[wave][2][lane] = b.y;
+            s_f[wave][3][lane] = c.y;
+            s_f[wave][4][lane] = c.z;
+            s_f[wave][5][lane] = c.w;
+            s_f[wave][6][lane] = d.x;
+            s_f[wave][7][lane] = cull_scrit(b.y);
+            s_i[wave][0][lane] = lo;
+            s_i[wave][1][lane] = hi;
+            s_i[wave][2][lane] = id;
         }
-        const int i = order[j];
-        const float4* r = reinterpret_cast<const float4*>(rec + (size_t)i * GM_REC);
-        const float4 a = r[0], b = r[1], c = r[2], d = r[3];
-        const int lo = __float_as_int(d.y), hi = __float_as_int(d.z);
-        const int x0 = lo & 0xffff, y0 = lo >> 16, x1 = hi & 0xffff, y1 = hi >> 16;
-        const int w = x1 - x0, nt = w * (y1 - y0);
-        int p = EMIT ? off[j] : 0;
-        const int pend = EMIT ? off[j + 1] : 0;  // the counting pass took the same decisions
-        for (int c0 = 0; c0 < nt; c0 += 64) {
-            const int t = c0 + lane;
+        int P = nt;
+#pragma unroll
+        for (int k = 1; k < 64; k <<= 1) {
+            const int y = __shfl_up(P, k, 64);
+            if (lane >= k) P += y;
+        }
+        s_i[wave][3][lane] = P;
+        const int total = __shfl(P, 63, 64);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        int p = EMIT ? chunk_off[chunk] : 0;
+        const int pend = EMIT ? chunk_off[chunk + 1] : 0;  // the counting pass took the same decisions
+        for (int f0 = 0; f0 < total; f0 += 64) {
+            const int f = f0 + lane;
             bool keep = false;
-            int tx = 0, ty = 0;
-            if (t < nt) {
-                ty = y0 + t / w;
-                tx = x0 + t % w;
-                keep = !culled(cam, cp, tx, ty, a.x, a.y, c.y, c.z, c.w, d.x, b.y);
+            int tile = 0, id = 0;
+            if (f < total) {
+                int lo = 0, hi = 63;
+                while (lo < hi) {  // first g with prefix[g] > f
+                    const int mid = (lo + hi) >> 1;
+                    if (s_i[wave][3][mid] > f) hi = mid;
+                    else lo = mid + 1;
+                }
+                const int g = lo;
+                const int t = f - (g > 0 ? s_i[wave][3][g - 1] : 0);
+                const int rlo = s_i[wave][0][g], rhi = s_i[wave][1][g];
+                const int x0 = rlo & 0xffff, y0 = rlo >> 16, w = (rhi & 0xffff) - x0;
+                const int ty = y0 + t / w, tx = x0 + t % w;
+                tile = ty * cam.tx + tx;
+                id = s_i[wave][2][g];
+                keep = !culled(cam, cp, tx, ty, s_f[wave][0][g], s_f[wave][1][g], s_f[wave][3][g], s_f[wave][4][g],
+                               s_f[wave][5][g], s_f[wave][6][g], s_f[wave][7][g]);
             }
             const unsigned long long m = __ballot(keep);
-            if (EMIT && keep && p + __popcll(m & lt) < pend) {
+            if (EMIT && keep) {
                 const int q = p + __popcll(m & lt);
-                tkeys[q] = (uint32_t)(ty * cam.tx + tx);
-                tvals[q] = i;
+                if (q < pend) {
+                    tkeys[q] = (uint32_t)tile;
+                    tvals[q] = id;
+                }
             }
             p += __popcll(m);
         }
-        if (!EMIT && lane == 0) cnt[j] = p;
+        if (!EMIT && lane == 0) chunk_cnt[chunk] = p;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -338,13 +416,15 @@ gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec, c
     GM_LAUNCH_CHECK();
     if (gm_status s = radix_sort(w.dka, w.dva, w.dkb, w.dvb, 4, 0, w.nvis, N, w.aux, stream)) return s;
     const int32_t* order = w.dva;  // 4 passes: back in the first buffer pair
-    // 2. surviving tiles per Gaussian (depth order), scan, read back the total
+    // 2. surviving (Gaussian, tile) pairs per chunk of 64 Gaussians in depth order,
+    //    scan, read back the total
     CullParams cp{tile_dmax, softness};
-    const unsigned gW = (unsigned)std::min<int64_t>(div_up(N, PW_WAVES), 16384);
-    k_pairs<false><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, w.nvis, N, order, rec, w.flag, nullptr, nullptr,
-                                                    nullptr);
+    const int nchunks = (int)div_up(N, 64);
+    const unsigned gW = (unsigned)std::min<int64_t>(div_up(nchunks, PW_WAVES), 2048);
+    k_pairs<false><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, w.nvis, nchunks, order, rec, w.flag, nullptr,
+                                                    nullptr, nullptr);
     GM_LAUNCH_CHECK();
-    if (gm_status s = exclusive_scan(w.flag, w.pos, N, w.npairs, w.aux, stream)) return s;
+    if (gm_status s = exclusive_scan(w.flag, w.pos, nchunks, w.npairs, w.aux, stream)) return s;
     int64_t K = 0;
     if (gm_status s = read_back_i64(w.npairs, &K, stream)) return s;
     *n_keys = K;
@@ -359,7 +439,7 @@ gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec, c
     uint32_t* ka = w.tka;
     int32_t* va = (npass % 2 == 0) ? sorted_ids : w.tva;
     int32_t* vb = (npass % 2 == 0) ? w.tva : sorted_ids;
-    k_pairs<true><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, w.nvis, N, order, rec, nullptr, w.pos, ka, va);
+    k_pairs<true><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, w.nvis, nchunks, order, rec, nullptr, w.pos, ka, va);
     GM_LAUNCH_CHECK();
     if (gm_status s = radix_sort(ka, va, w.tkb, vb, npass, 0, w.npairs, K, w.aux, stream)) return s;
     const uint32_t* kfin = (npass % 2 == 0) ? w.tka : w.tkb;
