@@ -24,6 +24,7 @@ constexpr int CB = 256;     // records per LDS batch
 constexpr float SKIP_ALPHA = 1.0f / 255.0f;
 constexpr float STOP_T = 1e-4f;
 constexpr float ALPHA_MAX = 0.99f;
+constexpr int NBASIS = 14;  // per-entry basis sums accumulated by the backward
 
 struct CompParams {
     DevCamera cam;
@@ -214,11 +215,17 @@ __global__ void __launch_bounds__(256) k_shade(CompParams P, float* __restrict__
 // the per-pair evaluation shared by both walks
 // ---------------------------------------------------------------------------
 struct Staged {
-    float4 a;  // u, v, Q00, Q01
-    float4 b;  // Q11, opacity, r, g
+    float4 a;  // u, v, Q00/2, Q01
+    float4 b;  // Q11/2, opacity, r, g
     float4 c;  // b, z_c, g0, g1
     float4 d;  // sigma, kappa = 1/(sigma softness), q_skip, 1/sigma
 };
+
+// q = (Q00 dx^2 + 2 Q01 dx dy + Q11 dy^2) / 2 from the half-conic (hq00, q01, hq11).
+__device__ __forceinline__ float quad_form(float hq00, float q01, float hq11, float dx, float dy)
+{
+    return __builtin_fmaf(dx, __builtin_fmaf(hq00, dx, q01 * dy), (hq11 * dy) * dy);
+}
 
 // Standard normal CDF Phi(s) and density phi(s) from one exponential.
 // erfc(z) for z >= 0 follows Abramowitz & Stegun, Handbook of Mathematical
@@ -245,7 +252,7 @@ __device__ __forceinline__ float eval_pair(const Staged& g, float pxc, float pyc
 {
     dx = pxc - g.a.x;
     dy = pyc - g.a.y;
-    const float q = 0.5f * (g.a.z * dx * dx + g.b.x * dy * dy) + g.a.w * dx * dy;
+    const float q = quad_form(g.a.z, g.a.w, g.b.x, dx, dy);
     f = 1.0f;
     s = 0.0f;
     pdf = 0.0f;
@@ -258,7 +265,7 @@ __device__ __forceinline__ float eval_pair(const Staged& g, float pxc, float pyc
     alpha = fminf(g.b.y * G, ALPHA_MAX);
     if (alpha < SKIP_ALPHA) return 0.0f;
     if (on) {
-        const float num = (D - g.c.y) - (g.c.z * dx + g.c.w * dy);
+        const float num = (D - g.c.y) - __builtin_fmaf(g.c.z, dx, g.c.w * dy);
         if (softness > 0.0f) {
             s = num * g.d.y;
             f = normal_cdf_pdf(s, pdf);
@@ -269,20 +276,41 @@ __device__ __forceinline__ float eval_pair(const Staged& g, float pxc, float pyc
     return alpha * f;
 }
 
+// Minimum of q over the rectangle [xa, xb] x [ya, yb] of offsets (dx, dy): zero
+// when the rectangle holds the centre, else the least of the four edge minima (q
+// is convex; on an edge it is a 1D quadratic minimised at a clamped stationary point).
+__device__ __forceinline__ float quad_min_rect(float hq00, float q01, float hq11, float xa, float xb, float ya,
+                                               float yb)
+{
+    if (xa <= 0.0f && xb >= 0.0f && ya <= 0.0f && yb >= 0.0f) return 0.0f;
+    float m = INFINITY;
+    const float ix = -q01 / (2.0f * hq11), iy = -q01 / (2.0f * hq00);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const float X = e ? xb : xa;
+        const float Y = fminf(fmaxf(ix * X, ya), yb);
+        m = fminf(m, quad_form(hq00, q01, hq11, X, Y));
+        const float Y2 = e ? yb : ya;
+        const float X2 = fminf(fmaxf(iy * Y2, xa), xb);
+        m = fminf(m, quad_form(hq00, q01, hq11, X2, Y2));
+    }
+    return m;
+}
+
 // Stage one record and decide for which of the tile's four 16x4-pixel waves it can
 // matter.  A wave bit is cleared only when every pixel of the wave would skip the
 // entry anyway (alpha_F < 1/255), so skipping it leaves every result bit-identical:
-//  * the alpha >= 1/255 region is the ellipse q <= q_skip; its bounding box, widened
-//    by a margin that covers fp32 rounding of q (scaled by the conic's
-//    conditioning), misses the wave's pixel centres; or
+//  * q exceeds q_skip on the whole rectangle of the wave's pixel centres, with a
+//    margin that covers fp32 rounding of q scaled by the conic's conditioning; or
 //  * the wave lies entirely on the mesh (wdmax = max D over its pixels) and the
 //    conditional depth, minimal at a corner of the wave's rectangle, keeps f small
 //    enough that min(0.99, o) f < (1/255)(1 - 1e-3), with a 1e-5 |D| depth slack.
 __device__ __forceinline__ uint32_t stage_record(const CompParams& P, float4 ra, float4 rb, float4 rc,
                                                  float4 rd, int tx, int ty, const float* wdmax, Staged& st)
 {
-    st.a = ra;
-    st.b = rb;
+    const float Q00 = ra.z, Q01 = ra.w, Q11 = rb.x;
+    st.a = make_float4(ra.x, ra.y, 0.5f * Q00, Q01);
+    st.b = make_float4(0.5f * Q11, rb.y, rb.z, rb.w);
     st.c = rc;
     const float o = rb.y;
     const float lq = o > 0.0f ? logf(255.0f * o) : -1.0f;
@@ -290,32 +318,28 @@ __device__ __forceinline__ uint32_t stage_record(const CompParams& P, float4 ra,
     const float kap = P.softness > 0.0f ? 1.0f / (rd.x * P.softness) : 0.0f;
     st.d = make_float4(rd.x, kap, qs, 1.0f / rd.x);
     if (!(qs >= 0.0f)) return 0u;  // o exp(-q) < 1/255 everywhere
-    const float Q00 = ra.z, Q01 = ra.w, Q11 = rb.x;
     const float detQ = Q00 * Q11 - Q01 * Q01;
     if (!(detQ > 0.0f) || !(Q00 > 0.0f) || !(Q11 > 0.0f)) return 0xFu;
     const float rho = fminf(fabsf(Q01) / sqrtf(Q00 * Q11), 0.999999f);
     const float qe = qs * (1.0f + 1e-5f * (1.0f + rho) / (1.0f - rho)) + 1e-4f;
-    const float ex = sqrtf(2.0f * qe * Q11 / detQ) * 1.001f + 0.01f;
-    const float ey = sqrtf(2.0f * qe * Q00 / detQ) * 1.001f + 0.01f;
     const float u = ra.x, v = ra.y;
-    const float xa = (float)(tx * GM_TILE) + 0.5f, xb = xa + 15.0f;
-    if (u + ex < xa || u - ex > xb) return 0u;
+    const float xa = (float)(tx * GM_TILE) + 0.5f - u, xb = xa + 15.0f;
     const float amax = fminf(o, ALPHA_MAX);
     const float thr = (1.0f / 255.0f) * (1.0f - 1e-3f);
     // f must reach thr/amax somewhere for the entry to matter
     const float scrit = P.softness > 0.0f && amax > thr ? -1.41421356237309515f * erfcinvf(2.0f * thr / amax) - 1e-3f
                                                          : 0.0f;
     const float g0 = rc.z, g1 = rc.w, zc = rc.y;
-    const float gxm = fminf(g0 * (xa - u), g0 * (xb - u));
+    const float gxm = fminf(g0 * xa, g0 * xb);
     uint32_t m = 0;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        const float ya = (float)(ty * GM_TILE + 4 * w) + 0.5f, yb = ya + 3.0f;
-        if (v + ey < ya || v - ey > yb) continue;
+        const float ya = (float)(ty * GM_TILE + 4 * w) + 0.5f - v, yb = ya + 3.0f;
         const float dm = wdmax[w];
         if (dm < 0.0f) continue;  // no pixel of this wave is in the image
+        if (quad_min_rect(st.a.z, Q01, st.b.x, xa, xb, ya, yb) * (1.0f - 1e-5f) > qe) continue;
         if (dm < INFINITY) {
-            const float zmin = zc + (gxm + fminf(g1 * (ya - v), g1 * (yb - v)));
+            const float zmin = zc + (gxm + fminf(g1 * ya, g1 * yb));
             const float lim = dm + 1e-5f * fabsf(dm);
             if (P.softness > 0.0f) {
                 if (amax <= thr) continue;
@@ -401,10 +425,10 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, float* __restr
                             done = true;
                         } else {
                             const float w = aF * T;
-                            C0 += w * g.b.z;
-                            C1 += w * g.b.w;
-                            C2 += w * g.c.x;
-                            Z += w * g.c.y;
+                            C0 = __builtin_fmaf(w, g.b.z, C0);
+                            C1 = __builtin_fmaf(w, g.b.w, C1);
+                            C2 = __builtin_fmaf(w, g.c.x, C2);
+                            Z = __builtin_fmaf(w, g.c.y, Z);
                             T = Tn;
                             last = b0 + k - start + 1;
                         }
@@ -482,7 +506,7 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
     __shared__ Staged s_g[CB];
     __shared__ int s_id[CB];
     __shared__ uint8_t s_m[CB];
-    __shared__ float s_acc[CB][GM_GRAD];
+    __shared__ float s_acc[CB][NBASIS];
     __shared__ float s_wd[CT / 64];
     __shared__ int s_wl[CT / 64];
     const int tile = blockIdx.x;
@@ -545,7 +569,7 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
                 if (rel >= s_wl[w]) msk &= ~(1u << w);
             s_id[threadIdx.x] = id;
 #pragma unroll
-            for (int c = 0; c < GM_GRAD; ++c) s_acc[threadIdx.x][c] = 0.0f;
+            for (int c = 0; c < NBASIS; ++c) s_acc[threadIdx.x][c] = 0.0f;
         }
         s_m[threadIdx.x] = (uint8_t)msk;
         {
@@ -564,6 +588,10 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
                 const int k = i * 64 + kk;
                 const Staged& g = s_g[k];
                 const int rel = b0 + k - start;
+                // per-pixel basis sums; the 13 record gradients are linear in them
+                // (formed once per entry at the flush):
+                //  0-2 w GC, 3 w GZ, 4 H, 5 H dx, 6 H dy, 7 H dx^2, 8 H dx dy, 9 H dy^2,
+                //  10 ds, 11 ds dx, 12 ds dy, 13 ds s   (H = dL/dq-weighted alpha, ds = dL/ds)
                 float gr[16];
 #pragma unroll
                 for (int c = 0; c < 16; ++c) gr[c] = 0.0f;
@@ -578,52 +606,66 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
                         const float iom = __builtin_amdgcn_rcpf(1.0f - aF);
                         const float Ti = T * iom;
                         const float w = aF * Ti;
-                        const float Vv = GC0 * g.b.z + GC1 * g.b.w + GC2 * g.c.x + GZ * g.c.y;
-                        const float daF = Ti * Vv - acc * iom;
-                        acc += w * Vv;
+                        const float Vv = __builtin_fmaf(GC0, g.b.z, __builtin_fmaf(GC1, g.b.w, __builtin_fmaf(GC2, g.c.x, GZ * g.c.y)));
+                        const float daF = __builtin_fmaf(Ti, Vv, -acc * iom);
+                        acc = __builtin_fmaf(w, Vv, acc);
                         T = Ti;
-                        gr[6] = w * GC0;
-                        gr[7] = w * GC1;
-                        gr[8] = w * GC2;
-                        gr[9] = w * GZ;
-                        const float da = f * daF;
-                        if (g.b.y * G <= ALPHA_MAX) {
-                            gr[5] = G * da;
-                            const float H = g.b.y * G * da;
-                            gr[2] = -0.5f * dx * dx * H;
-                            gr[3] = -dx * dy * H;
-                            gr[4] = -0.5f * dy * dy * H;
-                            gr[0] = H * (g.a.z * dx + g.a.w * dy);
-                            gr[1] = H * (g.a.w * dx + g.b.x * dy);
+                        gr[0] = w * GC0;
+                        gr[1] = w * GC1;
+                        gr[2] = w * GC2;
+                        gr[3] = w * GZ;
+                        const float oG = g.b.y * G;
+                        if (oG <= ALPHA_MAX) {
+                            const float H = oG * (f * daF);
+                            const float Hx = H * dx, Hy = H * dy;
+                            gr[4] = H;
+                            gr[5] = Hx;
+                            gr[6] = Hy;
+                            gr[7] = Hx * dx;
+                            gr[8] = Hx * dy;
+                            gr[9] = Hy * dy;
                         }
                         if (on && P.softness > 0.0f) {
-                            const float ds = al * pdf * daF;
-                            const float kap = g.d.y;
-                            gr[9] -= kap * ds;
-                            gr[10] = -kap * ds * dx;
-                            gr[11] = -kap * ds * dy;
-                            gr[0] += kap * ds * g.c.z;
-                            gr[1] += kap * ds * g.c.w;
-                            gr[12] = -ds * s * g.d.w;
-                            gD += kap * ds;
+                            const float ds = (al * pdf) * daF;
+                            gr[10] = ds;
+                            gr[11] = ds * dx;
+                            gr[12] = ds * dy;
+                            gr[13] = ds * s;
+                            gD = __builtin_fmaf(g.d.y, ds, gD);
                         }
                     }
                 }
                 if (__ballot(act)) {
                     const float v = wave_sum16(gr, lane);
                     const int c = lane >> 2;
-                    if ((lane & 3) == 0 && c < GM_GRAD && v != 0.0f) atomicAdd(&s_acc[k][c], v);
+                    if ((lane & 3) == 0 && c < NBASIS && v != 0.0f) atomicAdd(&s_acc[k][c], v);
                 }
             }
         }
         __syncthreads();
         if ((int)threadIdx.x < nb) {
+            const float* S = s_acc[threadIdx.x];
+            const Staged& g = s_g[threadIdx.x];
+            const float kap = g.d.y;
+            const float q00 = 2.0f * g.a.z, q01 = g.a.w, q11 = 2.0f * g.b.x;
+            float gv[GM_GRAD];
+            gv[0] = __builtin_fmaf(q00, S[5], __builtin_fmaf(q01, S[6], kap * g.c.z * S[10]));
+            gv[1] = __builtin_fmaf(q01, S[5], __builtin_fmaf(q11, S[6], kap * g.c.w * S[10]));
+            gv[2] = -0.5f * S[7];
+            gv[3] = -S[8];
+            gv[4] = -0.5f * S[9];
+            gv[5] = S[4] != 0.0f ? S[4] / g.b.y : 0.0f;  // dL/do = sum G f dL/dalpha_F = (sum H) / o
+            gv[6] = S[0];
+            gv[7] = S[1];
+            gv[8] = S[2];
+            gv[9] = S[3] - kap * S[10];
+            gv[10] = -kap * S[11];
+            gv[11] = -kap * S[12];
+            gv[12] = -S[13] * g.d.w;
             float* dst = g_rec + (size_t)s_id[threadIdx.x] * GM_GRAD;
 #pragma unroll
-            for (int c = 0; c < GM_GRAD; ++c) {
-                const float v = s_acc[threadIdx.x][c];
-                if (v != 0.0f) unsafeAtomicAdd(dst + c, v);
-            }
+            for (int c = 0; c < GM_GRAD; ++c)
+                if (gv[c] != 0.0f) unsafeAtomicAdd(dst + c, gv[c]);
         }
     }
     if (!inside) return;
