@@ -238,7 +238,11 @@ __device__ __forceinline__ float normal_cdf_pdf(float s, float& pdf)
     pdf = 0.39894228040143268f * e;
     const float z = fabsf(s) * 0.70710678118654752f;
     const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * z);
-    const float poly = t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+    float poly = __builtin_fmaf(t, 1.061405429f, -1.453152027f);
+    poly = __builtin_fmaf(t, poly, 1.421413741f);
+    poly = __builtin_fmaf(t, poly, -0.284496736f);
+    poly = __builtin_fmaf(t, poly, 0.254829592f);
+    poly *= t;
     const float half_tail = 0.5f * poly * e;  // Phi(-|s|)
     return s <= 0.0f ? half_tail : 1.0f - half_tail;
 }
@@ -539,6 +543,7 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
     float gD = 0.0f;
 
     wave_dmax(inside, on, D, s_wd);
+    const bool wave_on = __ballot(on) != 0;
     int m = last;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o, 64));
@@ -588,53 +593,65 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
                 const int k = i * 64 + kk;
                 const Staged& g = s_g[k];
                 const int rel = b0 + k - start;
+                // Straight-line evaluation (nearly every walked entry is active for some
+                // lane of the wave): inactive lanes carry zeros through the same
+                // arithmetic.  The expressions and their order are those of eval_pair,
+                // so the skip decisions are the forward's bit for bit.
+                const float dx = pxc - g.a.x, dy = pyc - g.a.y;
+                const float q = quad_form(g.a.z, g.a.w, g.b.x, dx, dy);
+                const float G = __expf(-q);
+                const float oG = g.b.y * G;
+                const float al = fminf(oG, ALPHA_MAX);
+                float f = 1.0f, pdf = 0.0f, sv = 0.0f;
+                if (wave_on) {
+                    const float num = (D - g.c.y) - __builtin_fmaf(g.c.z, dx, g.c.w * dy);
+                    if (P.softness > 0.0f) {
+                        sv = on ? num * g.d.y : 0.0f;  // off the mesh D = +inf: keep s finite
+                        float pd;
+                        const float fo = normal_cdf_pdf(sv, pd);
+                        f = on ? fo : 1.0f;
+                        pdf = on ? pd : 0.0f;
+                    } else {
+                        f = (on && !(num > 0.0f)) ? 0.0f : 1.0f;
+                    }
+                }
+                const float aF = al * f;
+                const bool act = rel < last && !(q > g.d.z) && al >= SKIP_ALPHA && aF >= SKIP_ALPHA;
                 // per-pixel basis sums; the 13 record gradients are linear in them
                 // (formed once per entry at the flush):
                 //  0-2 w GC, 3 w GZ, 4 H, 5 H dx, 6 H dy, 7 H dx^2, 8 H dx dy, 9 H dy^2,
-                //  10 ds, 11 ds dx, 12 ds dy, 13 ds s   (H = dL/dq-weighted alpha, ds = dL/ds)
+                //  10 ds, 11 ds dx, 12 ds dy, 13 ds s   (H = o G dL/dalpha, ds = dL/ds)
+                const float aFe = act ? aF : 0.0f;
+                // 1 - alpha_F >= 0.01: a hardware reciprocal (1 ulp) keeps the
+                // recovered transmittance far inside the gradient tolerance
+                const float iom = __builtin_amdgcn_rcpf(1.0f - aFe);
+                const float Ti = T * iom;
+                const float w = aFe * Ti;
+                const float Vv = __builtin_fmaf(GC0, g.b.z, __builtin_fmaf(GC1, g.b.w, __builtin_fmaf(GC2, g.c.x, GZ * g.c.y)));
+                const float daF = act ? __builtin_fmaf(Ti, Vv, -acc * iom) : 0.0f;
+                acc = __builtin_fmaf(w, Vv, acc);
+                T = Ti;
                 float gr[16];
-#pragma unroll
-                for (int c = 0; c < 16; ++c) gr[c] = 0.0f;
-                bool act = false;
-                if (rel < last) {
-                    float dx, dy, G, al, f, s, pdf;
-                    const float aF = eval_pair(g, pxc, pyc, on, D, P.softness, dx, dy, G, al, f, s, pdf);
-                    if (aF >= SKIP_ALPHA) {
-                        act = true;
-                        // 1 - alpha_F >= 0.01: a hardware reciprocal (1 ulp) keeps the
-                        // recovered transmittance far inside the gradient tolerance
-                        const float iom = __builtin_amdgcn_rcpf(1.0f - aF);
-                        const float Ti = T * iom;
-                        const float w = aF * Ti;
-                        const float Vv = __builtin_fmaf(GC0, g.b.z, __builtin_fmaf(GC1, g.b.w, __builtin_fmaf(GC2, g.c.x, GZ * g.c.y)));
-                        const float daF = __builtin_fmaf(Ti, Vv, -acc * iom);
-                        acc = __builtin_fmaf(w, Vv, acc);
-                        T = Ti;
-                        gr[0] = w * GC0;
-                        gr[1] = w * GC1;
-                        gr[2] = w * GC2;
-                        gr[3] = w * GZ;
-                        const float oG = g.b.y * G;
-                        if (oG <= ALPHA_MAX) {
-                            const float H = oG * (f * daF);
-                            const float Hx = H * dx, Hy = H * dy;
-                            gr[4] = H;
-                            gr[5] = Hx;
-                            gr[6] = Hy;
-                            gr[7] = Hx * dx;
-                            gr[8] = Hx * dy;
-                            gr[9] = Hy * dy;
-                        }
-                        if (on && P.softness > 0.0f) {
-                            const float ds = (al * pdf) * daF;
-                            gr[10] = ds;
-                            gr[11] = ds * dx;
-                            gr[12] = ds * dy;
-                            gr[13] = ds * s;
-                            gD = __builtin_fmaf(g.d.y, ds, gD);
-                        }
-                    }
-                }
+                gr[0] = w * GC0;
+                gr[1] = w * GC1;
+                gr[2] = w * GC2;
+                gr[3] = w * GZ;
+                const float H = oG <= ALPHA_MAX ? oG * (f * daF) : 0.0f;
+                const float Hx = H * dx, Hy = H * dy;
+                gr[4] = H;
+                gr[5] = Hx;
+                gr[6] = Hy;
+                gr[7] = Hx * dx;
+                gr[8] = Hx * dy;
+                gr[9] = Hy * dy;
+                const float ds = (al * pdf) * daF;
+                gr[10] = ds;
+                gr[11] = ds * dx;
+                gr[12] = ds * dy;
+                gr[13] = ds * sv;
+                gr[14] = 0.0f;
+                gr[15] = 0.0f;
+                gD = __builtin_fmaf(g.d.y, ds, gD);
                 if (__ballot(act)) {
                     const float v = wave_sum16(gr, lane);
                     const int c = lane >> 2;

@@ -118,7 +118,7 @@ def compare_records(gpu, ora, rgb_tol=1e-5):
     res["field_mismatch"] = int(np.count_nonzero(fb))
     res["rgb_maxdiff"] = float(np.abs(g[valid][:, 6:9].astype(np.float64) - ora["rgb64"][valid]).max()) \
         if valid.any() else 0.0
-    res["rgb_ok"] = res["rgb_maxdiff"] <= rgb_tol
+    res["rgb_ok"] = bool(res["rgb_maxdiff"] <= rgb_tol) and bool(np.isfinite(g[valid][:, :13]).all())
     return res
 
 
@@ -202,7 +202,7 @@ def compare_grads(scene, gpu, ora, tiles, strad_mask):
         r, g = ref[:, k], got[:, k]
         d = g - r
         rms = np.sqrt(np.mean(r * r)) if len(r) else 0.0
-        fail = np.abs(d) > GRAD_TOL * (np.abs(r) + rms) + 1e-12
+        fail = ~(np.abs(d) <= GRAD_TOL * (np.abs(r) + rms) + 1e-12)  # NaN fails
         res["elem_bad"] += int(np.count_nonzero(fail & ~exm))
         used |= fail & exm
     res["grad_exempt"] = int(np.count_nonzero(used))
@@ -210,14 +210,14 @@ def compare_grads(scene, gpu, ora, tiles, strad_mask):
     for k in range(13):
         r, g = ref[keep, k], got[keep, k]
         nr = np.linalg.norm(r)
-        if np.linalg.norm(g - r) > GRAD_TOL * nr + 1e-12:
+        if not np.linalg.norm(g - r) <= GRAD_TOL * nr + 1e-12:  # NaN fails
             res["planes_bad"].append((k, float(np.linalg.norm(g - r) / max(nr, 1e-30))))
     m = tile_pixel_mask(scene, tiles)
     for name, key in (("mesh_rgb", "g_mesh_rgb"), ("mesh_depth", "g_mesh_depth")):
         r = c[key][m]
         g = gpu[key][m].astype(np.float64)
         rms = np.sqrt(np.mean(r * r)) if r.size else 0.0
-        fail = np.abs(g - r) > GRAD_TOL * (np.abs(r) + rms) + 1e-9
+        fail = ~(np.abs(g - r) <= GRAD_TOL * (np.abs(r) + rms) + 1e-9)  # NaN fails
         if fail.ndim > 1:
             fail = fail.any(-1)
         sm = strad_mask[m]

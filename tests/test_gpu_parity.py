@@ -56,6 +56,8 @@ def _check_all(scene, view, gpu, ora, tiles, cull, label):
     gr = P.compare_grads(scene, gpu, ora, tiles, im["straddle_mask"])
     rep.update(gr)
     print(label, {k: v for k, v in rep.items()}, flush=True)
+    for key in ("rgb", "depth", "alpha", "T", "g_rec", "g_mesh_rgb", "g_mesh_depth"):
+        assert np.isfinite(gpu[key]).all(), key
     assert rep["vscreen_mismatch"] == 0
     assert rep["face_mismatch"] == 0 and rep["depth_mismatch"] == 0 and rep["dmax_mismatch"] == 0
     if scene.N:
@@ -150,6 +152,7 @@ def test_cull_invariance_and_determinism():
     r.forward(0, cull=False)
     r.backward(g["rgb"], g["depth"], g["alpha"])
     gb = P.to_np(r.g_rec)
+    assert np.isfinite(ga).all() and np.isfinite(gb).all()
     assert np.allclose(ga, gb, rtol=1e-5, atol=1e-6 * np.abs(ga).max())
 
 
