@@ -1,16 +1,22 @@
 """Benchmark: hybrid render fwd+bwd throughput at 1080p on one MI355X.
 
-One step = the whole hot path over one view of the workload:
-gm_bin_triangles -> gm_raster_zbuffer -> gm_project_gaussians -> gm_sort_tile_keys
--> gm_composite_hybrid_fwd -> gm_composite_hybrid_bwd, inputs resident in HBM.
+One step = the whole hot path over one view of the workload, inputs resident in
+HBM: gm_bin_triangles -> gm_raster_zbuffer -> gm_project_gaussians ->
+gm_sort_tile_keys -> gm_composite_hybrid_fwd -> gm_composite_hybrid_bwd.
 
-Prints one JSON line (rank 0): the metric, per-stage times, a roofline entry for
-the dominant kernel (timed live with HIP events on the library's stream) and the
-CPU oracle's throughput on a bounded sample of the same workload.
+Prints one JSON line with the metric, per-stage times (HIP events on the library's
+stream, recorded inside the timed region), a roofline entry for the dominant
+kernel and the CPU oracle's throughput on a bounded sample of the same workload.
+
+``--copy-calibration`` instead runs a plain device copy of known size; profiled
+with ``rocprofv3 --pmc FETCH_SIZE`` / ``WRITE_SIZE`` it gives the factors that turn
+those counters into bytes.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -19,8 +25,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (256 CU x 4 SIMD x 16 lanes... x 2 x 2.4 GHz)
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector (counts packed FMA)
+STAGES = ["bin", "zbuffer", "project", "sort", "fwd", "bwd"]
 
 WORKLOADS = {
     "c3": "1920x1080, 200k-face displaced sphere (vertex colour + Phong), 1M Gaussians SH3",
@@ -28,6 +35,16 @@ WORKLOADS = {
     "c2": "512x512, 5120-face icosphere, 100k Gaussians",
     "c4": "800x800 textured 4096-triangle soup, no Gaussians, one of 16 views",
 }
+
+# Algorithmic flops of the composite per (pixel, list entry) pair, counted on the
+# definition (transcendentals count 1): evaluating a pair (offset, quadratic form,
+# exp, opacity clamp, split numerator, Phi, alpha_F) is 26; the reverse-mode
+# gradient of an included pair (transmittance recovery, colour/depth terms, conic,
+# mean, opacity, split terms) is 62 more; the forward's accumulation of an included
+# pair is 10 more.
+FLOPS_EVAL = 26
+FLOPS_GRAD = 62
+FLOPS_ACCUM = 10
 
 
 def parse():
@@ -38,27 +55,40 @@ def parse():
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS))
     ap.add_argument("--view", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tiles", type=int, default=640, help="tiles in the oracle's timed sample")
+    ap.add_argument("--cpu-tiles", type=int, default=0,
+                    help="tiles in the oracle's timed sample (0: every tile of the view)")
+    ap.add_argument("--copy-calibration", action="store_true")
     return ap.parse_args()
 
 
-def algorithmic_bytes(r, scene):
-    """Compulsory HBM bytes of one view per stage (each input read once, each output
-    written once), from the run's own counts."""
+def copy_calibration():
     import torch
-    N, V, F, HW, T = scene.N, scene.V, scene.F, scene.width * scene.height, r.T
-    K, P = r.n_keys, r.n_pairs
-    nvis = int((r.rec[:N, 15].view(torch.int32) > 0).sum().item()) if N else 0
-    d = scene.sh_degree
-    shb = 12 * (d + 1) ** 2 if d >= 0 else 12
-    return {
-        "bin": 12 * V + 12 * V + 12 * F + 8 * P + 4 * T,
-        "zbuffer": 4 * P + 12 * F + 12 * V + 8 * HW + 4 * T,
-        "project": N * (12 + 16 + 12 + 4 + shb + 64),
-        "sort": 64 * N + 28 * K + 8 * T,
-        "fwd": 4 * K + 64 * nvis + 8 * HW + 20 * HW + 8 * HW,
-        "bwd": 4 * K + 64 * nvis + 8 * HW + 8 * HW + 20 * HW + 52 * nvis + 16 * HW,
-    }, nvis
+    n = 1 << 28  # 1 GiB of fp32
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
+
+
+def source_digest(kernel_file):
+    with open(os.path.join(ROOT, "differentiable_hybrid_mesh_amd", "csrc", kernel_file), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, kernel_file, config):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary of this
+    kernel, or None when the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{config}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.e+]+)", text)
+    if not m or not b or m.group(1) != source_digest(kernel_file):
+        return None
+    return float(b.group(1))
 
 
 def main():
@@ -67,8 +97,12 @@ def main():
         print("bench.py: this build measures one GPU only (the renderer has no multi-GPU path); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     import scenes
+    from differentiable_hybrid_mesh_amd import _lib as G
     from differentiable_hybrid_mesh_amd.pipeline import DeviceScene, Renderer
 
     torch.cuda.set_device(0)
@@ -77,87 +111,110 @@ def main():
     ds = DeviceScene(scene)
     r = Renderer(ds)
     g = ds.grads(view)
+    cam = ds.cams[view]
     torch.cuda.synchronize()
 
-    stages = ["bin", "zbuffer", "project", "sort", "fwd", "bwd"]
-
     def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        r.bin_and_zbuffer(view) if ev is None else _bin_z(ev)
-        if ev is not None:
-            ev[2].record()
-        r.project(view)
-        if ev is not None:
-            ev[3].record()
-        r.sort(view, True)
-        if ev is not None:
-            ev[4].record()
-        r.composite_fwd(view)
-        if ev is not None:
-            ev[5].record()
-        r.composite_bwd(view, g["rgb"], g["depth"], g["alpha"])
-        if ev is not None:
-            ev[6].record()
+        st = torch.cuda.current_stream().cuda_stream
 
-    def _bin_z(ev):
-        ds_, cam, st = r.ds, r.ds.cams[view], torch.cuda.current_stream().cuda_stream
-        from differentiable_hybrid_mesh_amd import _lib as G
-        status, n = G.gm_bin_triangles(cam, ds_.mesh, r.vscreen, r.tile_offsets, r.tile_tris, r.pair_cap,
-                                       r.ws_bin, st)
-        assert status == G.GM_OK
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        while True:
+            status, n = G.gm_bin_triangles(cam, ds.mesh, r.vscreen, r.tile_offsets, r.tile_tris, r.pair_cap,
+                                           r.ws_bin, st)
+            if status == G.GM_OK:
+                break
+            r.pair_cap = int(n * 1.25) + 1024
+            r.tile_tris = torch.empty(r.pair_cap, dtype=torch.int32, device="cuda")
         r.n_pairs = n
-        ev[1].record()
-        G.gm_raster_zbuffer(cam, ds_.mesh, r.vscreen, r.tile_offsets, r.tile_tris, r.face_id, r.depth,
+        mark(1)
+        G.gm_raster_zbuffer(cam, ds.mesh, r.vscreen, r.tile_offsets, r.tile_tris, r.face_id, r.depth,
                             r.tile_dmax, st)
+        mark(2)
+        r.project(view)
+        mark(3)
+        r.sort(view, True)
+        mark(4)
+        r.composite_fwd(view)
+        mark(5)
+        r.composite_bwd(view, g["rgb"], g["depth"], g["alpha"])
+        mark(6)
 
     for _ in range(max(args.warmup, 1)):
         step()  # the first step also grows the list capacities
     torch.cuda.synchronize()
 
-    # timed region: K whole steps, no per-stage events
+    # timed region: K whole steps; stage events on the library's (current) stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
-    for _ in range(args.steps):
-        step()
+    for k in range(args.steps):
+        step(evs[k])
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = t0.elapsed_time(t1) / args.steps
-
-    # per-stage split (separate pass, same work, HIP events on the library's stream)
-    per = {k: [] for k in stages}
-    for _ in range(max(3, min(args.steps, 10))):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
-        step(ev)
-        torch.cuda.synchronize()
-        for i, k in enumerate(stages):
-            per[k].append(ev[i].elapsed_time(ev[i + 1]))
-    stage_ms = {k: float(np.median(v)) for k, v in per.items()}
+    stage_ms = {s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, s in enumerate(STAGES)}
 
     px = scene.width * scene.height
     value = px / (ms * 1e-3) / 1e6
-    alg, nvis = algorithmic_bytes(r, scene)
-    dom = max(stage_ms, key=stage_ms.get)
-    dom_s = stage_ms[dom] * 1e-3
-    roof = {"kernel": {"bwd": "k_composite_bwd", "fwd": "k_composite_fwd", "sort": "gm_sort_tile_keys",
-                       "project": "k_project_gaussians", "zbuffer": "k_zbuffer", "bin": "gm_bin_triangles"}[dom],
-            "bound": "hbm", "achieved": alg[dom] / dom_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "traffic": None}
-    roof["frac"] = roof["achieved"] / roof["peak"]
+    N = scene.N
+    nvis = int((r.rec[:N, 15].view(torch.int32) > 0).sum().item()) if N else 0
+    walked = int(r.state_last.sum().item())  # pairs up to each pixel's last included entry
+    incl_frac = included_fraction(scene, view) if N else 0.0
 
-    total_alg = sum(alg.values())
+    # compulsory HBM bytes per stage (each input read once, each output written once)
+    V, F, HW, T, K, Pp = scene.V, scene.F, px, r.T, r.n_keys, r.n_pairs
+    d = scene.sh_degree
+    shb = 12 * (d + 1) ** 2 if d >= 0 else 12
+    alg_bytes = {
+        "bin": 12 * V + 12 * V + 12 * F + 8 * Pp + 4 * T,
+        "zbuffer": 4 * Pp + 12 * F + 12 * V + 8 * HW + 4 * T,
+        "project": N * (12 + 16 + 12 + 4 + shb + 64),
+        "sort": 64 * N + 28 * K + 8 * T,
+        "fwd": 4 * K + 64 * nvis + 8 * HW + 12 * HW + 20 * HW + 20 * HW,
+        "bwd": 4 * K + 64 * nvis + 8 * HW + 8 * HW + 12 * HW + 20 * HW + 52 * nvis + 16 * HW,
+    }
+    alg_flops = {
+        "fwd": walked * FLOPS_EVAL + walked * incl_frac * FLOPS_ACCUM,
+        "bwd": walked * FLOPS_EVAL + walked * incl_frac * FLOPS_GRAD,
+    }
+    # dominant single kernel: bin and sort are chains of many small kernels, the other
+    # stages are one main kernel each (the composite stages add a zero-fill or a
+    # shading prepass of a few percent)
+    dom = max(["zbuffer", "project", "fwd", "bwd"], key=stage_ms.get)
+    kname = {"bwd": "k_composite_bwd", "fwd": "k_composite_fwd", "sort": "gm_sort_tile_keys",
+             "project": "k_project_gaussians", "zbuffer": "k_zbuffer", "bin": "gm_bin_triangles"}[dom]
+    kfile = {"bwd": "gm_composite.hip", "fwd": "gm_composite.hip", "sort": "gm_sort.hip",
+             "project": "gm_project.hip", "zbuffer": "gm_raster.hip", "bin": "gm_raster.hip"}[dom]
+    dom_s = stage_ms[dom] * 1e-3
+    if dom in alg_flops:
+        ach = alg_flops[dom] / dom_s / 1e12
+        roof = {"kernel": kname, "bound": "alu", "achieved": round(ach, 3), "peak": FP32_VALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / FP32_VALU_PEAK_TFLOPS, 4)}
+    else:
+        ach = alg_bytes[dom] / dom_s / 1e9
+        roof = {"kernel": kname, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = measured_traffic(kname, kfile, args.config)
+    roof["units"] = {"walked_pairs": walked, "included_fraction": round(incl_frac, 4)} if dom in alg_flops \
+        else {"algorithmic_bytes": alg_bytes[dom]}
+    roof["launch_ms"] = round(stage_ms[dom], 4)
+
+    total_alg = sum(alg_bytes.values())
     out = {
         "metric": "hybrid render Mpixels/s fwd+bwd at 1080p",
         "value": round(value, 3), "unit": "Mpixels/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded PCG64 scene generators)",
         "config": {"workload": f"{args.config}: {WORKLOADS[args.config]}", "view": view,
-                   "width": scene.width, "height": scene.height, "faces": scene.F, "gaussians": scene.N,
-                   "pairs": r.n_pairs, "keys": r.n_keys, "visible": nvis, "parallelism": "single GPU"},
+                   "width": scene.width, "height": scene.height, "faces": scene.F, "gaussians": N,
+                   "tri_tile_pairs": r.n_pairs, "keys": r.n_keys, "visible": nvis, "parallelism": "single GPU"},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "hbm_algorithmic_GBps": round(total_alg / (ms * 1e-3) / 1e9, 1),
         "hbm_algorithmic_frac": round(total_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -169,20 +226,34 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def included_fraction(scene, view, ntiles=48):
+    """Included / walked pairs of the reverse pass, counted by the oracle on a fixed
+    sample of tiles of the same view (used to weight the per-pair flop figures)."""
+    import oracle
+    T = scene.tiles_x * scene.tiles_y
+    rng = np.random.default_rng(5)
+    tiles = np.sort(rng.choice(T, size=min(ntiles, T), replace=False)).astype(np.int32)
+    res = oracle.render_view(scene, view, tiles=tiles, cull=True, backward=False)
+    c = res["comp"]
+    m = c["n_last"] >= 0
+    w = int(c["n_last"][m].sum())
+    return float(c["n_incl"][m].sum()) / w if w else 0.0
+
+
 def cpu_baseline(scene, view, ntiles):
     """The oracle (fwd+bwd, OpenMP on the host cores) on a bounded sample of tiles."""
     import oracle
     T = scene.tiles_x * scene.tiles_y
     rng = np.random.default_rng(123)
-    tiles = np.sort(rng.choice(T, size=min(ntiles, T), replace=False)).astype(np.int32)
+    n = T if ntiles <= 0 else min(ntiles, T)
+    tiles = np.sort(rng.choice(T, size=n, replace=False)).astype(np.int32)
     t = time.perf_counter()
     oracle.render_view(scene, view, tiles=tiles, cull=True, backward=True)
     dt = time.perf_counter() - t
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     px = len(tiles) * 256
-    return {"value": round(px / dt / 1e6, 6), "unit": "Mpixels/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(tiles)} random 16x16 tiles of view {view} ({px} px), fwd+bwd incl. projection of "
-                      f"all Gaussians and z-buffer of the sampled tiles; {dt:.1f} s"}
+    return {"value": round(px / dt / 1e6, 6), "unit": "Mpixels/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{len(tiles)} of {T} 16x16 tiles of view {view} ({px} px): projection and depth order of "
+                      f"all Gaussians, z-buffer, lists, composite and reverse mode of those tiles; {dt:.1f} s"}
 
 
 if __name__ == "__main__":

@@ -92,6 +92,8 @@ def lib():
         _lib.oc_Phi.argtypes = [D]
         _lib.oc_Phi.restype = D
         _lib.oc_sh_basis.argtypes = [D, D, D, P]
+        _lib.oc_num_threads.argtypes = []
+        _lib.oc_num_threads.restype = I
     return _lib
 
 
@@ -341,6 +343,10 @@ def composite(cam: Camera, meshref: Optional[MeshRef], rec64, tiles, offsets, id
     lib().oc_composite(C.byref(a))
     out["pairs"] = int(out["pairs"][0])
     return out
+
+
+def num_threads() -> int:
+    return int(lib().oc_num_threads())
 
 
 def Phi(s: float) -> float:

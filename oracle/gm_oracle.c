@@ -961,5 +961,18 @@ void oc_composite(oc_comp* a)
     if (a->pairs_evaluated) *a->pairs_evaluated = pairs_total;
 }
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+/* Threads the OpenMP loops of this library use. */
+int oc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
 /* Erf-based normal CDF, exported so that tests can pin it against closed values. */
 double oc_Phi(double s) { return Phi(s); }
