@@ -420,7 +420,7 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, float* __restr
                 const int k = i * 64 + __builtin_ctzll(m);
                 m &= m - 1;
                 if (!done) {
-                    const Staged& g = s_g[k];
+                    const Staged g = s_g[k];  // one 64-byte LDS broadcast read
                     float dx, dy, G, al, f, s, pdf;
                     const float aF = eval_pair(g, pxc, pyc, on, D, P.softness, dx, dy, G, al, f, s, pdf);
                     if (aF >= SKIP_ALPHA) {
@@ -591,7 +591,7 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
                 const int kk = 63 - __builtin_clzll(mm);
                 mm &= ~(1ull << kk);
                 const int k = i * 64 + kk;
-                const Staged& g = s_g[k];
+                const Staged g = s_g[k];  // one 64-byte LDS broadcast read
                 const int rel = b0 + k - start;
                 // Straight-line evaluation (nearly every walked entry is active for some
                 // lane of the wave): inactive lanes carry zeros through the same
@@ -616,7 +616,7 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
                     }
                 }
                 const float aF = al * f;
-                const bool act = rel < last && !(q > g.d.z) && al >= SKIP_ALPHA && aF >= SKIP_ALPHA;
+                const bool act = (rel < last) & !(q > g.d.z) & (al >= SKIP_ALPHA) & (aF >= SKIP_ALPHA);
                 // per-pixel basis sums; the 13 record gradients are linear in them
                 // (formed once per entry at the flush):
                 //  0-2 w GC, 3 w GZ, 4 H, 5 H dx, 6 H dy, 7 H dx^2, 8 H dx dy, 9 H dy^2,

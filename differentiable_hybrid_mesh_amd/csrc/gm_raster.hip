@@ -95,8 +95,7 @@ __global__ void k_bin_scatter(DevCamera cam, int F, const int2* __restrict__ fac
         }
 }
 
-// Triangle setup as staged in LDS: one 128-byte record, read by a whole wave at
-// the same address (broadcast).
+// Triangle setup as staged in LDS: one 128-byte record.
 struct TriSetup {
     double u[3], v[3];   // screen vertices
     double du[3], dv[3]; // edge deltas b - a of edges (v1,v2), (v2,v0), (v0,v1)
@@ -104,10 +103,17 @@ struct TriSetup {
     double A;            // twice the signed area
 };
 
-// One block per tile, one thread per pixel.  Triangles of the tile's bin are set up
-// in fp64 by one thread each and staged in LDS together with their pixel box and a
-// 4-bit mask of the 16x4-pixel waves the box reaches; each wave then walks only the
-// triangles of its mask, and each pixel only those whose box holds it.
+constexpr int ZB_CHUNK = 1024;  // candidates per round (bounds the covered list)
+constexpr unsigned long long ZB_INF = 0x7FF0000000000000ull;  // +inf as fp64 bits
+
+// One block per tile.  Each staged triangle contributes the pixels of its box
+// (widened by a pixel, clipped to the tile and the image) as candidates; the
+// candidates of a batch form one flat sequence that all 256 threads walk, so lanes
+// stay busy whatever the triangle size.  A covered candidate lowers its pixel's
+// nearest depth with an LDS min on the fp64 bit pattern (positive doubles order like
+// their bits) and joins a list; a second phase over that list gives every pixel the
+// smallest face id among the candidates at exactly its nearest depth.  Decision rule
+// and arithmetic are those of the per-pixel definition, bit for bit.
 __global__ void __launch_bounds__(ZB_THREADS)
 k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
           const float* __restrict__ vs, const int32_t* __restrict__ tile_off,
@@ -116,8 +122,16 @@ k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
 {
     __shared__ TriSetup s_t[ZB_BATCH];
     __shared__ int s_f[ZB_BATCH];
-    __shared__ int4 s_box[ZB_BATCH];  // pixel box widened by one pixel: x0, x1, y0, y1
-    __shared__ uint8_t s_m[ZB_BATCH];
+    __shared__ int4 s_box[ZB_BATCH];       // clipped box in tile-local pixels: x0, w, y0, -
+    __shared__ int s_coff[ZB_BATCH + 1];   // candidate prefix sums
+    __shared__ unsigned long long s_minz[ZB_THREADS];
+    __shared__ int s_id[ZB_THREADS];
+    __shared__ unsigned long long s_cz[ZB_CHUNK];
+    __shared__ int s_cid[ZB_CHUNK];
+    __shared__ short s_cpx[ZB_CHUNK];
+    __shared__ uint8_t s_map[ZB_CHUNK];   // candidate -> staged triangle, per round
+    __shared__ int s_ncov;
+    __shared__ int s_wsum[ZB_THREADS / 64];
     __shared__ float s_red[ZB_THREADS / 64];
 
     const int tile = blockIdx.x;
@@ -125,57 +139,78 @@ k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int px = tx * GM_TILE + (threadIdx.x & 15), py = ty * GM_TILE + (threadIdx.x >> 4);
     const bool inside = px < cam.width && py < cam.height;
-    const double pu = px + 0.5, pv = py + 0.5;
+    const int xlim = min(GM_TILE, cam.width - tx * GM_TILE), ylim = min(GM_TILE, cam.height - ty * GM_TILE);
     const int start = tile_off[tile], end = tile_off[tile + 1];
 
-    double best = INFINITY;
-    int bid = -1;
+    s_minz[threadIdx.x] = ZB_INF;
+    s_id[threadIdx.x] = 0x7fffffff;
     for (int b0 = start; b0 < end; b0 += ZB_BATCH) {
         const int nb = min(ZB_BATCH, end - b0);
         __syncthreads();
-        if (threadIdx.x < ZB_BATCH) {
+        int cnt = 0;
+        if (threadIdx.x < nb) {
             const int j = threadIdx.x;
-            uint8_t m = 0;
-            if (j < nb) {
-                const int f = tile_tris[b0 + j];
-                TriSetup t;
-                for (int k = 0; k < 3; ++k) {
-                    const int vi = faces[k * F + f];
-                    t.u[k] = (double)vs[vi];
-                    t.v[k] = (double)vs[V + vi];
-                    t.z[k] = (double)vs[2 * V + vi];
-                }
-                t.du[0] = t.u[2] - t.u[1];
-                t.dv[0] = t.v[2] - t.v[1];
-                t.du[1] = t.u[0] - t.u[2];
-                t.dv[1] = t.v[0] - t.v[2];
-                t.du[2] = t.u[1] - t.u[0];
-                t.dv[2] = t.v[1] - t.v[0];
-                t.A = (t.u[1] - t.u[0]) * (t.v[2] - t.v[0]) - (t.v[1] - t.v[0]) * (t.u[2] - t.u[0]);
-                s_t[j] = t;
-                s_f[j] = f;
-                // a pixel centre covered by the triangle lies in its bounding box; the
-                // box is widened by a pixel so that this integer reject never overrides
-                // the fp64 edge test
-                const double umin = fmin(fmin(t.u[0], t.u[1]), t.u[2]), umax = fmax(fmax(t.u[0], t.u[1]), t.u[2]);
-                const double vmin = fmin(fmin(t.v[0], t.v[1]), t.v[2]), vmax = fmax(fmax(t.v[0], t.v[1]), t.v[2]);
-                const int4 bx = make_int4((int)fmax(floor(umin) - 1.0, -2.0), (int)fmin(ceil(umax) + 1.0, 32768.0),
-                                          (int)fmax(floor(vmin) - 1.0, -2.0), (int)fmin(ceil(vmax) + 1.0, 32768.0));
-                s_box[j] = bx;
-                if (bx.x <= tx * GM_TILE + 15 && bx.y >= tx * GM_TILE)
-                    for (int w = 0; w < 4; ++w)
-                        if (bx.z <= ty * GM_TILE + 4 * w + 3 && bx.w >= ty * GM_TILE + 4 * w) m |= 1u << w;
+            const int f = tile_tris[b0 + j];
+            TriSetup t;
+            for (int k = 0; k < 3; ++k) {
+                const int vi = faces[k * F + f];
+                t.u[k] = (double)vs[vi];
+                t.v[k] = (double)vs[V + vi];
+                t.z[k] = (double)vs[2 * V + vi];
             }
-            s_m[j] = m;
+            t.du[0] = t.u[2] - t.u[1];
+            t.dv[0] = t.v[2] - t.v[1];
+            t.du[1] = t.u[0] - t.u[2];
+            t.dv[1] = t.v[0] - t.v[2];
+            t.du[2] = t.u[1] - t.u[0];
+            t.dv[2] = t.v[1] - t.v[0];
+            t.A = (t.u[1] - t.u[0]) * (t.v[2] - t.v[0]) - (t.v[1] - t.v[0]) * (t.u[2] - t.u[0]);
+            s_t[j] = t;
+            s_f[j] = f;
+            // a pixel centre covered by the triangle lies in its bounding box; the box
+            // is widened by a pixel so that it never excludes a pixel the fp64 edge
+            // test would accept
+            const double umin = fmin(fmin(t.u[0], t.u[1]), t.u[2]), umax = fmax(fmax(t.u[0], t.u[1]), t.u[2]);
+            const double vmin = fmin(fmin(t.v[0], t.v[1]), t.v[2]), vmax = fmax(fmax(t.v[0], t.v[1]), t.v[2]);
+            const double ox = tx * GM_TILE, oy = ty * GM_TILE;
+            // pixel-centre range [ceil(min - 1/2), floor(max - 1/2)], widened by one pixel
+            const int x0 = (int)fmax(ceil(umin - 0.5) - 1.0 - ox, 0.0);
+            const int x1 = (int)fmin(floor(umax - 0.5) + 1.0 - ox, xlim - 1.0);
+            const int y0 = (int)fmax(ceil(vmin - 0.5) - 1.0 - oy, 0.0);
+            const int y1 = (int)fmin(floor(vmax - 0.5) + 1.0 - oy, ylim - 1.0);
+            if (x0 <= x1 && y0 <= y1) cnt = (x1 - x0 + 1) * (y1 - y0 + 1);
+            s_box[j] = make_int4(x0, x1 - x0 + 1, y0, 0);
         }
+        // exclusive scan of the candidate counts (threads >= nb contribute 0)
+        int x = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(x, d, 64);
+            if (lane >= d) x += y;
+        }
+        if (lane == 63) s_wsum[wave] = x;
         __syncthreads();
-        for (int i = 0; i < ZB_BATCH / 64; ++i) {
-            unsigned long long mm = __ballot((s_m[i * 64 + lane] >> wave) & 1);
-            while (mm) {
-                const int j = i * 64 + __builtin_ctzll(mm);
-                mm &= mm - 1;
+        int wo = 0;
+        for (int w = 0; w < wave; ++w) wo += s_wsum[w];
+        if (threadIdx.x < ZB_BATCH) s_coff[threadIdx.x] = wo + x - cnt;
+        const int total = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+        if (threadIdx.x == 0) s_coff[ZB_BATCH] = total;
+        __syncthreads();
+        for (int c0 = 0; c0 < total; c0 += ZB_CHUNK) {
+            const unsigned long long prev = s_minz[threadIdx.x];
+            if (threadIdx.x == 0) s_ncov = 0;
+            const int cend = min(c0 + ZB_CHUNK, total);
+            if ((int)threadIdx.x < nb) {  // each staged triangle labels its candidates in this round
+                const int a = max(s_coff[threadIdx.x], c0), b = min(s_coff[threadIdx.x + 1], cend);
+                for (int c = a; c < b; ++c) s_map[c - c0] = (uint8_t)threadIdx.x;
+            }
+            __syncthreads();
+            for (int c = c0 + threadIdx.x; c < cend; c += ZB_THREADS) {
+                const int j = s_map[c - c0];
                 const int4 bx = s_box[j];
-                if (px < bx.x || px > bx.y || py < bx.z || py > bx.w) continue;
+                const int loc = c - s_coff[j];
+                const int ly = bx.z + loc / bx.y, lx = bx.x + loc % bx.y;
+                const double pu = tx * GM_TILE + lx + 0.5, pv = ty * GM_TILE + ly + 0.5;
                 const TriSetup& t = s_t[j];
                 // E_k = (b.u - a.u)(p.v - a.v) - (b.v - a.v)(p.u - a.u)
                 const double E0 = t.du[0] * (pv - t.v[1]) - t.dv[0] * (pu - t.u[1]);
@@ -187,15 +222,29 @@ k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
                 const double l0 = E0 / A, l1 = E1 / A, l2 = E2 / A;
                 const double inv = (l0 / t.z[0] + l1 / t.z[1]) + l2 / t.z[2];
                 const double z = 1.0 / inv;
-                const int f = s_f[j];
-                if (z < best || (z == best && f < bid)) {
-                    best = z;
-                    bid = f;
-                }
+                const unsigned long long zb = (unsigned long long)__double_as_longlong(z);
+                const int p = ly * GM_TILE + lx;
+                atomicMin(&s_minz[p], zb);
+                const int slot = atomicAdd(&s_ncov, 1);
+                s_cz[slot] = zb;
+                s_cid[slot] = s_f[j];
+                s_cpx[slot] = (short)p;
             }
+            __syncthreads();
+            if (s_minz[threadIdx.x] < prev) s_id[threadIdx.x] = 0x7fffffff;  // a nearer surface: forget older ties
+            __syncthreads();
+            const int ncov = s_ncov;
+            for (int q = threadIdx.x; q < ncov; q += ZB_THREADS) {
+                const int p = s_cpx[q];
+                if (s_cz[q] == s_minz[p]) atomicMin(&s_id[p], s_cid[q]);
+            }
+            __syncthreads();
         }
     }
-    const float d = bid >= 0 ? (float)best : INFINITY;
+    __syncthreads();
+    const unsigned long long mz = s_minz[threadIdx.x];
+    const int bid = mz == ZB_INF ? -1 : s_id[threadIdx.x];
+    const float d = bid >= 0 ? (float)__longlong_as_double((long long)mz) : INFINITY;
     if (inside) {
         face_id[py * cam.width + px] = bid;
         depth[py * cam.width + px] = d;
