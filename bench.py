@@ -121,14 +121,8 @@ def main():
             if ev is not None:
                 ev[i].record()
         mark(0)
-        while True:
-            status, n = G.gm_bin_triangles(cam, ds.mesh, r.vscreen, r.tile_offsets, r.tile_tris, r.pair_cap,
-                                           r.ws_bin, st)
-            if status == G.GM_OK:
-                break
-            r.pair_cap = int(n * 1.25) + 1024
-            r.tile_tris = torch.empty(r.pair_cap, dtype=torch.int32, device="cuda")
-        r.n_pairs = n
+        G.gm_bin_triangles(cam, ds.mesh, r.vscreen, r.tile_offsets, r.tile_tris, r.pair_cap, r.counts[0:1],
+                           r.ws_bin, st)
         mark(1)
         G.gm_raster_zbuffer(cam, ds.mesh, r.vscreen, r.tile_offsets, r.tile_tris, r.face_id, r.depth,
                             r.tile_dmax, st)
@@ -141,10 +135,16 @@ def main():
         mark(5)
         r.composite_bwd(view, g["rgb"], g["depth"], g["alpha"])
         mark(6)
+        r.fetch_counts()  # list lengths to pinned host memory, checked after the run
 
+    # warm-up; the list capacities grow until both lists fit (no step synchronises:
+    # the lengths are read back once the stream has finished)
     for _ in range(max(args.warmup, 1)):
-        step()  # the first step also grows the list capacities
+        step()
     torch.cuda.synchronize()
+    while not r.read_counts():
+        step()
+        torch.cuda.synchronize()
 
     # timed region: K whole steps; stage events on the library's (current) stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
@@ -158,6 +158,8 @@ def main():
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    if not r.read_counts():  # every timed step used the same capacities as the warm-up
+        raise RuntimeError("a list outgrew its capacity inside the timed region")
     ms = t0.elapsed_time(t1) / args.steps
     stage_ms = {s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, s in enumerate(STAGES)}
 

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libgm.so")
 GM_TILE = 16
 GM_REC = 16
 GM_GRAD = 13
-GM_OK, GM_ERR_ARG, GM_ERR_CAPACITY, GM_ERR_HIP = 0, -1, -2, -3
+GM_OK, GM_ERR_ARG, GM_ERR_HIP = 0, -1, -3
 
 
 class GmError(RuntimeError):
@@ -64,12 +64,12 @@ def lib():
     cam, mesh, light = C.POINTER(GmCamera), C.POINTER(GmMesh), C.POINTER(GmLight)
     L.gm_bin_triangles_ws.argtypes = [I32, I32, I32, I32]
     L.gm_bin_triangles_ws.restype = SZ
-    L.gm_bin_triangles.argtypes = [cam, mesh, P, P, P, I64, C.POINTER(C.c_int64), P, SZ, P]
+    L.gm_bin_triangles.argtypes = [cam, mesh, P, P, P, I64, P, P, SZ, P]
     L.gm_raster_zbuffer.argtypes = [cam, mesh, P, P, P, P, P, P, P]
     L.gm_project_gaussians.argtypes = [cam, I32, P, P, P, P, P, I32, P, P]
     L.gm_sort_tile_keys_ws.argtypes = [I32, I64, I32, I32]
     L.gm_sort_tile_keys_ws.restype = SZ
-    L.gm_sort_tile_keys.argtypes = [cam, I32, P, P, F32, P, P, I64, C.POINTER(C.c_int64), P, SZ, P]
+    L.gm_sort_tile_keys.argtypes = [cam, I32, P, P, F32, P, P, I64, P, P, SZ, P]
     L.gm_composite_hybrid_fwd.argtypes = [cam, P, P, P, P, P, mesh, P, light, P, F32, P, P, P, P, P, P, P]
     L.gm_composite_hybrid_bwd.argtypes = [cam, I32, P, P, P, P, P, F32, P, P, P, P, P, P, P, P, P, P]
     L.gm_mipmaps_floats.argtypes = [I32]
@@ -110,15 +110,11 @@ def gm_bin_triangles_ws(V, F, width, height) -> int:
     return lib().gm_bin_triangles_ws(V, F, width, height)
 
 
-def gm_bin_triangles(cam, mesh, vscreen, tile_offsets, tile_tris, cap, ws, stream):
-    """Returns (status, n_pairs); GM_ERR_CAPACITY is returned, not raised."""
-    n = C.c_int64(0)
-    st = lib().gm_bin_triangles(C.byref(cam), C.byref(mesh), ptr(vscreen), ptr(tile_offsets),
-                                ptr(tile_tris), int(cap), C.byref(n), ptr(ws),
-                                0 if ws is None else ws.numel() * ws.element_size(), stream)
-    if st not in (GM_OK, GM_ERR_CAPACITY):
-        check(st)
-    return st, n.value
+def gm_bin_triangles(cam, mesh, vscreen, tile_offsets, tile_tris, cap, n_pairs, ws, stream):
+    """n_pairs: device int64 tensor that receives the pair count (asynchronously)."""
+    check(lib().gm_bin_triangles(C.byref(cam), C.byref(mesh), ptr(vscreen), ptr(tile_offsets),
+                                 ptr(tile_tris), int(cap), ptr(n_pairs), ptr(ws),
+                                 0 if ws is None else ws.numel() * ws.element_size(), stream))
 
 
 def gm_raster_zbuffer(cam, mesh, vscreen, tile_offsets, tile_tris, face_id, depth, tile_dmax, stream):
@@ -135,15 +131,11 @@ def gm_sort_tile_keys_ws(N, cap, width, height) -> int:
     return lib().gm_sort_tile_keys_ws(int(N), int(cap), width, height)
 
 
-def gm_sort_tile_keys(cam, N, rec, tile_dmax, softness, tile_ranges, sorted_ids, cap, ws, stream):
-    """Returns (status, n_keys); GM_ERR_CAPACITY is returned, not raised."""
-    n = C.c_int64(0)
-    st = lib().gm_sort_tile_keys(C.byref(cam), int(N), ptr(rec), ptr(tile_dmax), float(softness),
-                                 ptr(tile_ranges), ptr(sorted_ids), int(cap), C.byref(n), ptr(ws),
-                                 0 if ws is None else ws.numel() * ws.element_size(), stream)
-    if st not in (GM_OK, GM_ERR_CAPACITY):
-        check(st)
-    return st, n.value
+def gm_sort_tile_keys(cam, N, rec, tile_dmax, softness, tile_ranges, sorted_ids, cap, n_keys, ws, stream):
+    """n_keys: device int64 tensor that receives the key count (asynchronously)."""
+    check(lib().gm_sort_tile_keys(C.byref(cam), int(N), ptr(rec), ptr(tile_dmax), float(softness),
+                                  ptr(tile_ranges), ptr(sorted_ids), int(cap), ptr(n_keys), ptr(ws),
+                                  0 if ws is None else ws.numel() * ws.element_size(), stream))
 
 
 def _light_ref(light):

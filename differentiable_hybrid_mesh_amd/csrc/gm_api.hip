@@ -130,6 +130,62 @@ __global__ void __launch_bounds__(SCAN_THREADS) k_scan_apply(const int32_t* __re
     if (blockIdx.x == 0 && threadIdx.x == 0) out[n] = (int32_t)*total;
 }
 
+// Single block of 1024 threads: the whole scan for short inputs (one launch).
+// Thread t owns items [16 t, 16 t + 16), read as four 16-byte loads when both
+// arrays are 16-byte aligned.
+constexpr int SCAN1_THREADS = 1024;
+constexpr int SCAN1_ITEMS = 16;
+constexpr int64_t SCAN1_MAX = (int64_t)SCAN1_THREADS * SCAN1_ITEMS;
+
+__global__ void __launch_bounds__(SCAN1_THREADS) k_scan_single(const int32_t* __restrict__ in, int64_t n,
+                                                               int32_t* __restrict__ out,
+                                                               long long* __restrict__ total)
+{
+    __shared__ long long lds[SCAN1_THREADS / 64];
+    const int64_t base = (int64_t)threadIdx.x * SCAN1_ITEMS;
+    const bool vec = ((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(out)) & 15) == 0 &&
+                     base + SCAN1_ITEMS <= n;
+    int32_t v[SCAN1_ITEMS];
+    if (vec) {
+#pragma unroll
+        for (int k = 0; k < SCAN1_ITEMS / 4; ++k) {
+            const int4 q = reinterpret_cast<const int4*>(in + base)[k];
+            v[4 * k] = q.x;
+            v[4 * k + 1] = q.y;
+            v[4 * k + 2] = q.z;
+            v[4 * k + 3] = q.w;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < SCAN1_ITEMS; ++k) v[k] = base + k < n ? in[base + k] : 0;
+    }
+    long long s = 0;
+#pragma unroll
+    for (int k = 0; k < SCAN1_ITEMS; ++k) s += v[k];
+    long long tot;
+    const long long inc = block_incl_scan(s, lds, &tot);
+    long long run = inc - s;
+    int32_t o[SCAN1_ITEMS];
+#pragma unroll
+    for (int k = 0; k < SCAN1_ITEMS; ++k) {
+        o[k] = (int32_t)run;
+        run += v[k];
+    }
+    if (vec) {
+#pragma unroll
+        for (int k = 0; k < SCAN1_ITEMS / 4; ++k)
+            reinterpret_cast<int4*>(out + base)[k] = make_int4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < SCAN1_ITEMS; ++k)
+            if (base + k < n) out[base + k] = o[k];
+    }
+    if (threadIdx.x == 0) {
+        out[n] = (int32_t)tot;
+        *total = tot;
+    }
+}
+
 size_t scan_ws_bytes(int64_t n)
 {
     int64_t nb = div_up(n > 0 ? n : 1, SCAN_CHUNK);
@@ -141,14 +197,15 @@ size_t scan_ws_bytes(int64_t n)
 gm_status exclusive_scan(const int32_t* in, int32_t* out, int64_t n, long long* total, void* ws,
                          hipStream_t stream)
 {
-    int64_t nb = div_up(n > 0 ? n : 1, SCAN_CHUNK);
-    long long* sums = (long long*)ws;
-    if (n > 0) {
-        k_scan_block_sums<<<(unsigned)nb, SCAN_THREADS, 0, stream>>>(in, n, sums);
+    if (n <= SCAN1_MAX) {
+        k_scan_single<<<1, SCAN1_THREADS, 0, stream>>>(in, n, out, total);
         GM_LAUNCH_CHECK();
-    } else {
-        GM_HIP_CHECK(hipMemsetAsync(sums, 0, sizeof(long long), stream));
+        return GM_OK;
     }
+    int64_t nb = div_up(n, SCAN_CHUNK);
+    long long* sums = (long long*)ws;
+    k_scan_block_sums<<<(unsigned)nb, SCAN_THREADS, 0, stream>>>(in, n, sums);
+    GM_LAUNCH_CHECK();
     k_scan_sums<<<1, 1024, 0, stream>>>(sums, nb, total);
     GM_LAUNCH_CHECK();
     k_scan_apply<<<(unsigned)nb, SCAN_THREADS, 0, stream>>>(in, n, sums, total, out);

@@ -6,6 +6,8 @@
 // in the written order with no contraction, edge functions and depth in fp64.
 #pragma clang fp contract(off)
 
+#include <algorithm>
+
 #include "gm_internal.h"
 
 namespace gm {
@@ -78,20 +80,27 @@ __global__ void k_bin_count(DevCamera cam, int V, int F, const int32_t* __restri
         for (int tx = r[0]; tx <= r[2]; ++tx) atomicAdd(&tile_cnt[ty * cam.tx + tx], 1);
 }
 
-__global__ void k_bin_scatter(DevCamera cam, int F, const int2* __restrict__ face_rect,
-                              const int32_t* __restrict__ tile_off, int32_t* __restrict__ cursor,
-                              int32_t* __restrict__ tile_tris)
+// Threads [0, F) scatter face ids.  When the pair total exceeds cap nothing is
+// scattered and threads [0, T] instead clear tile_offsets, so the bins read as
+// empty downstream (the caller enlarges tile_tris and bins again).
+__global__ void k_bin_scatter(DevCamera cam, int F, int T, const int2* __restrict__ face_rect,
+                              int32_t* __restrict__ tile_off, const long long* __restrict__ total,
+                              int64_t cap, int32_t* __restrict__ cursor, int32_t* __restrict__ tile_tris)
 {
-    const int f = blockIdx.x * blockDim.x + threadIdx.x;
-    if (f >= F) return;
-    const int2 pr = face_rect[f];
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (*total > cap) {
+        if (i <= T) tile_off[i] = 0;
+        return;
+    }
+    if (i >= F) return;
+    const int2 pr = face_rect[i];
     const int x0 = pr.x & 0xffff, y0 = pr.x >> 16, x1 = pr.y & 0xffff, y1 = pr.y >> 16;
     if (pr.x == 1 && pr.y == 0) return;
     for (int ty = y0; ty <= y1; ++ty)
         for (int tx = x0; tx <= x1; ++tx) {
             const int t = ty * cam.tx + tx;
             const int pos = atomicAdd(&cursor[t], 1);
-            tile_tris[tile_off[t] + pos] = f;
+            tile_tris[tile_off[t] + pos] = i;
         }
 }
 
@@ -104,16 +113,19 @@ struct TriSetup {
 };
 
 constexpr int ZB_CHUNK = 1024;  // candidates per round (bounds the covered list)
+constexpr int ZB_PER_THREAD = ZB_CHUNK / ZB_THREADS;
 constexpr unsigned long long ZB_INF = 0x7FF0000000000000ull;  // +inf as fp64 bits
 
 // One block per tile.  Each staged triangle contributes the pixels of its box
 // (widened by a pixel, clipped to the tile and the image) as candidates; the
-// candidates of a batch form one flat sequence that all 256 threads walk, so lanes
-// stay busy whatever the triangle size.  A covered candidate lowers its pixel's
-// nearest depth with an LDS min on the fp64 bit pattern (positive doubles order like
-// their bits) and joins a list; a second phase over that list gives every pixel the
-// smallest face id among the candidates at exactly its nearest depth.  Decision rule
-// and arithmetic are those of the per-pixel definition, bit for bit.
+// candidates of a batch form one flat sequence, walked in rounds of ZB_CHUNK with
+// four consecutive candidates per thread, so lanes stay busy whatever the triangle
+// size.  A round runs in three phases: the fp64 edge test appends covered
+// candidates to a compact list; the perspective-correct depth of every listed
+// candidate lowers its pixel's nearest depth with an LDS min on the fp64 bit
+// pattern (positive doubles order like their bits); then every pixel takes the
+// smallest face id among the candidates at exactly its nearest depth.  Decision
+// rule and arithmetic are those of the per-pixel definition, bit for bit.
 __global__ void __launch_bounds__(ZB_THREADS)
 k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
           const float* __restrict__ vs, const int32_t* __restrict__ tile_off,
@@ -122,28 +134,30 @@ k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
 {
     __shared__ TriSetup s_t[ZB_BATCH];
     __shared__ int s_f[ZB_BATCH];
-    __shared__ int4 s_box[ZB_BATCH];       // clipped box in tile-local pixels: x0, w, y0, -
+    __shared__ int4 s_box[ZB_BATCH];       // clipped box in tile-local pixels: x0, w, y0, bits of 1/w
     __shared__ int s_coff[ZB_BATCH + 1];   // candidate prefix sums
     __shared__ unsigned long long s_minz[ZB_THREADS];
     __shared__ int s_id[ZB_THREADS];
     __shared__ unsigned long long s_cz[ZB_CHUNK];
-    __shared__ int s_cid[ZB_CHUNK];
-    __shared__ short s_cpx[ZB_CHUNK];
-    __shared__ uint8_t s_map[ZB_CHUNK];   // candidate -> staged triangle, per round
-    __shared__ int s_ncov;
+    __shared__ int s_cov[ZB_CHUNK];        // covered candidates: local pixel | staged index << 8
+    __shared__ int s_ncov[2];              // list lengths, alternating between rounds
     __shared__ int s_wsum[ZB_THREADS / 64];
     __shared__ float s_red[ZB_THREADS / 64];
 
     const int tile = blockIdx.x;
     const int tx = tile % cam.tx, ty = tile / cam.tx;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const unsigned long long lt = (1ull << lane) - 1ull;
     const int px = tx * GM_TILE + (threadIdx.x & 15), py = ty * GM_TILE + (threadIdx.x >> 4);
     const bool inside = px < cam.width && py < cam.height;
     const int xlim = min(GM_TILE, cam.width - tx * GM_TILE), ylim = min(GM_TILE, cam.height - ty * GM_TILE);
     const int start = tile_off[tile], end = tile_off[tile + 1];
+    const double ox = tx * GM_TILE, oy = ty * GM_TILE;
 
     s_minz[threadIdx.x] = ZB_INF;
     s_id[threadIdx.x] = 0x7fffffff;
+    if (threadIdx.x == 0) s_ncov[0] = 0;
+    int round = 0;
     for (int b0 = start; b0 < end; b0 += ZB_BATCH) {
         const int nb = min(ZB_BATCH, end - b0);
         __syncthreads();
@@ -172,14 +186,14 @@ k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
             // test would accept
             const double umin = fmin(fmin(t.u[0], t.u[1]), t.u[2]), umax = fmax(fmax(t.u[0], t.u[1]), t.u[2]);
             const double vmin = fmin(fmin(t.v[0], t.v[1]), t.v[2]), vmax = fmax(fmax(t.v[0], t.v[1]), t.v[2]);
-            const double ox = tx * GM_TILE, oy = ty * GM_TILE;
             // pixel-centre range [ceil(min - 1/2), floor(max - 1/2)], widened by one pixel
             const int x0 = (int)fmax(ceil(umin - 0.5) - 1.0 - ox, 0.0);
             const int x1 = (int)fmin(floor(umax - 0.5) + 1.0 - ox, xlim - 1.0);
             const int y0 = (int)fmax(ceil(vmin - 0.5) - 1.0 - oy, 0.0);
             const int y1 = (int)fmin(floor(vmax - 0.5) + 1.0 - oy, ylim - 1.0);
-            if (x0 <= x1 && y0 <= y1) cnt = (x1 - x0 + 1) * (y1 - y0 + 1);
-            s_box[j] = make_int4(x0, x1 - x0 + 1, y0, 0);
+            const int w = max(x1 - x0 + 1, 1);
+            if (x0 <= x1 && y0 <= y1) cnt = w * (y1 - y0 + 1);
+            s_box[j] = make_int4(x0, w, y0, __float_as_int(1.0f / (float)w));
         }
         // exclusive scan of the candidate counts (threads >= nb contribute 0)
         int x = cnt;
@@ -196,47 +210,79 @@ k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
         const int total = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
         if (threadIdx.x == 0) s_coff[ZB_BATCH] = total;
         __syncthreads();
-        for (int c0 = 0; c0 < total; c0 += ZB_CHUNK) {
+        for (int c0 = 0; c0 < total; c0 += ZB_CHUNK, ++round) {
+            const int par = round & 1;
             const unsigned long long prev = s_minz[threadIdx.x];
-            if (threadIdx.x == 0) s_ncov = 0;
             const int cend = min(c0 + ZB_CHUNK, total);
-            if ((int)threadIdx.x < nb) {  // each staged triangle labels its candidates in this round
-                const int a = max(s_coff[threadIdx.x], c0), b = min(s_coff[threadIdx.x + 1], cend);
-                for (int c = a; c < b; ++c) s_map[c - c0] = (uint8_t)threadIdx.x;
+            // phase 1: edge test of four consecutive candidates per thread
+            const int cf = c0 + ZB_PER_THREAD * threadIdx.x;
+            int j = 0;
+            if (cf < cend) {  // last staged triangle whose candidates start at or before cf
+                int lo = 0, hi = nb - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (s_coff[mid] <= cf) lo = mid;
+                    else hi = mid - 1;
+                }
+                j = lo;
+            }
+#pragma unroll
+            for (int k = 0; k < ZB_PER_THREAD; ++k) {
+                const int c = cf + k;
+                bool cov = false;
+                int p = 0;
+                if (c < cend) {
+                    while (s_coff[j + 1] <= c) ++j;
+                    const int4 bx = s_box[j];
+                    const int loc = c - s_coff[j];
+                    const int qy = (int)(((float)loc + 0.5f) * __int_as_float(bx.w));
+                    const int ly = bx.z + qy, lx = bx.x + (loc - qy * bx.y);
+                    const double pu = ox + lx + 0.5, pv = oy + ly + 0.5;
+                    const TriSetup& t = s_t[j];
+                    // E_k = (b.u - a.u)(p.v - a.v) - (b.v - a.v)(p.u - a.u)
+                    const double E0 = t.du[0] * (pv - t.v[1]) - t.dv[0] * (pu - t.u[1]);
+                    const double E1 = t.du[1] * (pv - t.v[2]) - t.dv[1] * (pu - t.u[2]);
+                    const double E2 = t.du[2] * (pv - t.v[0]) - t.dv[2] * (pu - t.u[0]);
+                    cov = t.A > 0 ? (E0 >= 0 && E1 >= 0 && E2 >= 0) : (E0 <= 0 && E1 <= 0 && E2 <= 0);
+                    p = ly * GM_TILE + lx;
+                }
+                const unsigned long long m = __ballot(cov);
+                if (m) {
+                    const int leader = __ffsll((long long)m) - 1;
+                    int slot = 0;
+                    if (lane == leader) slot = atomicAdd(&s_ncov[par], __popcll(m));
+                    slot = __builtin_amdgcn_readlane(slot, leader);
+                    if (cov) s_cov[slot + __popcll(m & lt)] = p | (j << 8);
+                }
             }
             __syncthreads();
-            for (int c = c0 + threadIdx.x; c < cend; c += ZB_THREADS) {
-                const int j = s_map[c - c0];
-                const int4 bx = s_box[j];
-                const int loc = c - s_coff[j];
-                const int ly = bx.z + loc / bx.y, lx = bx.x + loc % bx.y;
-                const double pu = tx * GM_TILE + lx + 0.5, pv = ty * GM_TILE + ly + 0.5;
-                const TriSetup& t = s_t[j];
-                // E_k = (b.u - a.u)(p.v - a.v) - (b.v - a.v)(p.u - a.u)
+            // phase 2: depth of the covered candidates, nearest depth per pixel
+            const int ncov = s_ncov[par];
+            if (threadIdx.x == 0) s_ncov[par ^ 1] = 0;
+            for (int q = threadIdx.x; q < ncov; q += ZB_THREADS) {
+                const int e = s_cov[q];
+                const int p = e & 0xff, jj = e >> 8;
+                const double pu = ox + (p & 15) + 0.5, pv = oy + (p >> 4) + 0.5;
+                const TriSetup& t = s_t[jj];
                 const double E0 = t.du[0] * (pv - t.v[1]) - t.dv[0] * (pu - t.u[1]);
                 const double E1 = t.du[1] * (pv - t.v[2]) - t.dv[1] * (pu - t.u[2]);
                 const double E2 = t.du[2] * (pv - t.v[0]) - t.dv[2] * (pu - t.u[0]);
                 const double A = t.A;
-                const bool cov = A > 0 ? (E0 >= 0 && E1 >= 0 && E2 >= 0) : (E0 <= 0 && E1 <= 0 && E2 <= 0);
-                if (!cov) continue;
                 const double l0 = E0 / A, l1 = E1 / A, l2 = E2 / A;
                 const double inv = (l0 / t.z[0] + l1 / t.z[1]) + l2 / t.z[2];
                 const double z = 1.0 / inv;
                 const unsigned long long zb = (unsigned long long)__double_as_longlong(z);
-                const int p = ly * GM_TILE + lx;
                 atomicMin(&s_minz[p], zb);
-                const int slot = atomicAdd(&s_ncov, 1);
-                s_cz[slot] = zb;
-                s_cid[slot] = s_f[j];
-                s_cpx[slot] = (short)p;
+                s_cz[q] = zb;
             }
             __syncthreads();
             if (s_minz[threadIdx.x] < prev) s_id[threadIdx.x] = 0x7fffffff;  // a nearer surface: forget older ties
             __syncthreads();
-            const int ncov = s_ncov;
+            // phase 3: smallest face id at exactly the nearest depth
             for (int q = threadIdx.x; q < ncov; q += ZB_THREADS) {
-                const int p = s_cpx[q];
-                if (s_cz[q] == s_minz[p]) atomicMin(&s_id[p], s_cid[q]);
+                const int e = s_cov[q];
+                const int p = e & 0xff;
+                if (s_cz[q] == s_minz[p]) atomicMin(&s_id[p], s_f[e >> 8]);
             }
             __syncthreads();
         }
@@ -276,7 +322,6 @@ size_t gm_bin_triangles_ws(int32_t V, int32_t F, int32_t width, int32_t height)
     b += align_up(sizeof(int2) * (size_t)(F > 0 ? F : 1), 256);   // face rects
     b += align_up(sizeof(int32_t) * (size_t)T, 256);               // tile counts
     b += align_up(sizeof(int32_t) * (size_t)T, 256);               // cursors
-    b += align_up(sizeof(long long), 256);                         // total
     b += scan_ws_bytes(T);
     return b;
 }
@@ -306,9 +351,8 @@ gm_status gm_bin_triangles(const gm_camera* cam, const gm_mesh* mesh, float* vsc
     w += align_up(sizeof(int32_t) * (size_t)T, 256);
     int32_t* cursor = (int32_t*)w;
     w += align_up(sizeof(int32_t) * (size_t)T, 256);
-    long long* total = (long long*)w;
-    w += align_up(sizeof(long long), 256);
     void* scan_ws = w;
+    long long* total = reinterpret_cast<long long*>(n_pairs);
 
     k_fill_i32<<<(unsigned)div_up(2 * T + 64, 256), 256, 0, stream>>>(tile_cnt, (cursor - tile_cnt) + T, 0);
     GM_LAUNCH_CHECK();
@@ -322,18 +366,12 @@ gm_status gm_bin_triangles(const gm_camera* cam, const gm_mesh* mesh, float* vsc
         GM_LAUNCH_CHECK();
     }
     if (gm_status s = exclusive_scan(tile_cnt, tile_offsets, T, total, scan_ws, stream)) return s;
-    int64_t n = 0;
-    if (gm_status s = read_back_i64(total, &n, stream)) return s;
-    *n_pairs = n;
-    if (n > cap || n > INT32_MAX) {
-        set_error("tile_tris capacity %lld, %lld pairs needed", (long long)cap, (long long)n);
-        return GM_ERR_CAPACITY;
-    }
-    if (F > 0 && n > 0) {
-        k_bin_scatter<<<(unsigned)div_up(F, 256), 256, 0, stream>>>(dc, F, face_rect, tile_offsets, cursor,
-                                                                   tile_tris);
-        GM_LAUNCH_CHECK();
-    }
+    // the scatter compares the total with cap on the device
+    const int64_t nthr = std::max<int64_t>(F, T + 1);
+    k_bin_scatter<<<(unsigned)div_up(nthr, 256), 256, 0, stream>>>(dc, F, (int)T, face_rect, tile_offsets, total,
+                                                                  std::min<int64_t>(cap, INT32_MAX), cursor,
+                                                                  tile_tris);
+    GM_LAUNCH_CHECK();
     return GM_OK;
 }
 

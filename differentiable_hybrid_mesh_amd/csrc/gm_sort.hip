@@ -17,84 +17,97 @@
 namespace gm {
 
 constexpr int RS_THREADS = 256;
+constexpr int RS_WAVES = RS_THREADS / 64;
 constexpr int RS_ITEMS = 16;
 constexpr int RS_CHUNK = RS_THREADS * RS_ITEMS;  // keys per block
 constexpr int RS_RADIX = 256;
 
-__global__ void k_fill_i32s(int32_t* __restrict__ p, int64_t n, int32_t v)
+__global__ void k_sort_init(int32_t* __restrict__ ranges, int64_t n2, long long* __restrict__ n_keys,
+                            long long* __restrict__ d_n, long long n)
 {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = v;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n2) ranges[i] = 0;
+    if (i == 0) {
+        *n_keys = 0;
+        *d_n = n;
+    }
+}
+
+// Live key count of a pass.  A count above the buffers' capacity means the
+// emitting pass wrote nothing, so there is nothing to sort.
+__device__ inline long long live_count(const long long* __restrict__ d_count, long long n_max)
+{
+    const long long c = *d_count;
+    return c > n_max ? 0 : c;
 }
 
 // ---------------------------------------------------------------------------
 // stable LSD radix sort pass
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(RS_THREADS)
-k_radix_hist(const uint32_t* __restrict__ keys, const long long* __restrict__ d_count, int shift,
-             int nblocks, int32_t* __restrict__ hist)
+k_radix_hist(const uint32_t* __restrict__ keys, const long long* __restrict__ d_count, long long n_max,
+             int shift, int nblocks, int32_t* __restrict__ hist)
 {
-    __shared__ int32_t h[RS_RADIX];
-    const long long n = *d_count;
-    h[threadIdx.x] = 0;
+    __shared__ int32_t h[RS_WAVES][RS_RADIX];  // one histogram per wave: fewer colliding LDS atomics
+    const long long n = live_count(d_count, n_max);
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int w = 0; w < RS_WAVES; ++w) h[w][threadIdx.x] = 0;
     __syncthreads();
     const long long base = (long long)blockIdx.x * RS_CHUNK;
 #pragma unroll 4
     for (int k = 0; k < RS_ITEMS; ++k) {
         const long long e = base + (long long)k * RS_THREADS + threadIdx.x;
-        if (e < n) atomicAdd(&h[(keys[e] >> shift) & 0xff], 1);
+        if (e < n) atomicAdd(&h[wave][(keys[e] >> shift) & 0xff], 1);
     }
     __syncthreads();
-    hist[threadIdx.x * nblocks + blockIdx.x] = h[threadIdx.x];
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < RS_WAVES; ++w) c += h[w][threadIdx.x];
+    hist[threadIdx.x * nblocks + blockIdx.x] = c;
 }
 
-// Stable scatter of one LSD pass.  Every key gets its rank inside the block in 16
-// rounds of 256 (wave ballots give the rank among lanes holding the same digit,
-// per-wave digit counts in LDS the rank across waves, a running count per digit the
-// rank across rounds); keys are first placed in LDS in digit order and then written
-// out in that order, so each digit's run leaves the block as contiguous stores.
+// Stable scatter of one LSD pass over a block of RS_CHUNK keys.  Wave w ranks its
+// own 1024 consecutive keys in 16 rounds of 64 without block barriers: 8 ballots
+// give each lane the lanes holding the same digit, and a per-wave running count per
+// digit in LDS carries the rank across rounds (a wave's LDS operations complete in
+// program order).  One block scan then turns the per-wave counts into bases, keys
+// are placed in LDS in digit order, and each digit's run leaves the block as
+// contiguous stores.
 __global__ void __launch_bounds__(RS_THREADS)
 k_radix_scatter(const uint32_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
-                const long long* __restrict__ d_count, int shift, int nblocks, const int32_t* __restrict__ hist,
+                const long long* __restrict__ d_count, long long n_max, int shift, int nblocks,
                 const int32_t* __restrict__ offs, uint32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out)
 {
     __shared__ uint32_t s_k[RS_CHUNK];
     __shared__ int32_t s_v[RS_CHUNK];
-    __shared__ int32_t s_lstart[RS_RADIX], s_goff[RS_RADIX], s_run[RS_RADIX];
-    __shared__ int32_t s_wcnt[RS_THREADS / 64][RS_RADIX];
-    __shared__ int32_t s_wsum[RS_THREADS / 64];
-    const long long n = *d_count;
+    __shared__ int32_t s_wc[RS_WAVES][RS_RADIX];  // running counts per wave, then per-wave bases
+    __shared__ int32_t s_lstart[RS_RADIX], s_goff[RS_RADIX];
+    __shared__ int32_t s_wsum[RS_WAVES];
+    const long long n = live_count(d_count, n_max);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const unsigned long long lt = (1ull << lane) - 1ull;
     const long long base = (long long)blockIdx.x * RS_CHUNK;
     if (base >= n) return;
-    // block-local start of every digit: exclusive scan of this block's histogram
-    const int c = hist[t * nblocks + blockIdx.x];
-    int x = c;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(x, d, 64);
-        if (lane >= d) x += y;
-    }
-    if (lane == 63) s_wsum[wave] = x;
+    for (int w = 0; w < RS_WAVES; ++w) s_wc[w][t] = 0;
     s_goff[t] = offs[t * nblocks + blockIdx.x];
-    s_run[t] = 0;
     __syncthreads();
-    int wo = 0;
-    for (int w = 0; w < wave; ++w) wo += s_wsum[w];
-    s_lstart[t] = wo + x - c;
-    for (int k = 0; k < RS_ITEMS; ++k) {
-        const long long e = base + (long long)k * RS_THREADS + t;
+    uint32_t key[RS_ITEMS];
+    int32_t val[RS_ITEMS];
+    int rank[RS_ITEMS];
+    const long long wbase = base + (long long)wave * (RS_CHUNK / RS_WAVES);
+#pragma unroll
+    for (int r = 0; r < RS_ITEMS; ++r) {
+        const long long e = wbase + r * 64 + lane;
         const bool act = e < n;
-        uint32_t key = 0;
-        int32_t val = 0;
-        if (act) {
-            key = keys_in[e];
-            val = vals_in[e];
-        }
-        const int d = (key >> shift) & 0xff;
-        for (int w = 0; w < RS_THREADS / 64; ++w) s_wcnt[w][t] = 0;
-        __syncthreads();
+        key[r] = act ? keys_in[e] : 0u;
+        val[r] = act ? vals_in[e] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < RS_ITEMS; ++r) {
+        const bool act = wbase + r * 64 + lane < n;
+        const int d = (key[r] >> shift) & 0xff;
         unsigned long long peers = __ballot(act);
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
@@ -102,27 +115,53 @@ k_radix_scatter(const uint32_t* __restrict__ keys_in, const int32_t* __restrict_
             const unsigned long long bb = __ballot(bit);
             peers &= bit ? bb : ~bb;
         }
-        const int rank = __popcll(peers & lt);
-        if (act && rank == 0) s_wcnt[wave][d] = __popcll(peers);
-        __syncthreads();
-        if (act) {
-            int pos = s_lstart[d] + s_run[d] + rank;
-            for (int w = 0; w < wave; ++w) pos += s_wcnt[w][d];
-            s_k[pos] = key;
-            s_v[pos] = val;
+        const int before = s_wc[wave][d];
+        rank[r] = before + __popcll(peers & lt);
+        if (act && (peers >> lane) == 1ull) s_wc[wave][d] = before + __popcll(peers);  // last lane of the group
+    }
+    __syncthreads();
+    // digit t: per-wave counts -> block-local start of the digit and per-wave bases
+    int cw[RS_WAVES];
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < RS_WAVES; ++w) {
+        cw[w] = s_wc[w][t];
+        c += cw[w];
+    }
+    int x = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) s_wsum[wave] = x;
+    __syncthreads();
+    int wo = 0;
+    for (int w = 0; w < wave; ++w) wo += s_wsum[w];
+    const int lstart = wo + x - c;
+    s_lstart[t] = lstart;
+    int run = lstart;
+#pragma unroll
+    for (int w = 0; w < RS_WAVES; ++w) {
+        s_wc[w][t] = run;
+        run += cw[w];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RS_ITEMS; ++r) {
+        if (wbase + r * 64 + lane < n) {
+            const int pos = s_wc[wave][(key[r] >> shift) & 0xff] + rank[r];
+            s_k[pos] = key[r];
+            s_v[pos] = val[r];
         }
-        __syncthreads();
-        int add = 0;
-        for (int w = 0; w < RS_THREADS / 64; ++w) add += s_wcnt[w][t];
-        s_run[t] += add;
     }
     __syncthreads();
     const int nvalid = (int)min((long long)RS_CHUNK, n - base);
     for (int p = t; p < nvalid; p += RS_THREADS) {
-        const uint32_t key = s_k[p];
-        const int d = (key >> shift) & 0xff;
+        const uint32_t k = s_k[p];
+        const int d = (k >> shift) & 0xff;
         const int g = s_goff[d] + (p - s_lstart[d]);
-        keys_out[g] = key;
+        keys_out[g] = k;
         vals_out[g] = s_v[p];
     }
 }
@@ -134,12 +173,13 @@ size_t radix_ws_bytes(int64_t n)
            align_up(sizeof(long long), 256);
 }
 
-// Sorts n_max-bounded (keys, vals) by key bits [lo_bit, hi_bit) with LSD passes of 8
-// bits; the live count is *d_count (device).  Ping-pongs between (ka, va) and
+// Sorts n_max-bounded (keys, vals) by key bits [lo_bit, lo_bit + 8 npass) with LSD
+// passes of 8 bits; the live count is *d_count (device), zero when above n_max.  Ping-pongs between (ka, va) and
 // (kb, vb); the result lands in (k_out, v_out), which must be one of the two pairs'
 // buffers chosen by the caller so that the final pass writes there.
 static gm_status radix_sort(uint32_t* ka, int32_t* va, uint32_t* kb, int32_t* vb, int npass, int lo_bit,
-                            const long long* d_count, int64_t n_max, void* ws, hipStream_t stream)
+                            const long long* d_count, int64_t n_max, void* ws, hipStream_t stream,
+                            const int32_t** last_offs = nullptr)
 {
     const int nb = (int)div_up(n_max > 0 ? n_max : 1, RS_CHUNK);
     char* w = (char*)ws;
@@ -156,10 +196,10 @@ static gm_status radix_sort(uint32_t* ka, int32_t* va, uint32_t* kb, int32_t* vb
     int32_t* vout = vb;
     for (int p = 0; p < npass; ++p) {
         const int shift = lo_bit + 8 * p;
-        k_radix_hist<<<nb, RS_THREADS, 0, stream>>>(kin, d_count, shift, nb, hist);
+        k_radix_hist<<<nb, RS_THREADS, 0, stream>>>(kin, d_count, n_max, shift, nb, hist);
         GM_LAUNCH_CHECK();
         if (gm_status s = exclusive_scan(hist, offs, (int64_t)RS_RADIX * nb, tot, scan_ws, stream)) return s;
-        k_radix_scatter<<<nb, RS_THREADS, 0, stream>>>(kin, vin, d_count, shift, nb, hist, offs, kout, vout);
+        k_radix_scatter<<<nb, RS_THREADS, 0, stream>>>(kin, vin, d_count, n_max, shift, nb, offs, kout, vout);
         GM_LAUNCH_CHECK();
         uint32_t* tk = kin;
         int32_t* tv = vin;
@@ -168,28 +208,25 @@ static gm_status radix_sort(uint32_t* ka, int32_t* va, uint32_t* kb, int32_t* vb
         kout = tk;
         vout = tv;
     }
+    if (last_offs) *last_offs = offs;  // [digit][block] exclusive offsets of the last pass
     return GM_OK;
 }
 
 // ---------------------------------------------------------------------------
-// visible Gaussians, depth keys
+// depth keys
 // ---------------------------------------------------------------------------
-__global__ void k_visible_flags(int N, const float* __restrict__ rec, int32_t* __restrict__ flag)
+// Key of Gaussian i: the bits of its fp32 z_c when it is listed (z_c > 0, so the bits
+// order like the values and the top byte is below 0x80), all ones otherwise; the
+// stable sort then puts the listed Gaussians first in (z_c, id) order, and the last
+// pass's offset of top byte 0xff is their number.
+__global__ void k_depth_keys(int N, const float* __restrict__ rec, uint32_t* __restrict__ keys,
+                             int32_t* __restrict__ vals)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= N) return;
-    flag[i] = __float_as_int(rec[(size_t)i * GM_REC + 15]) > 0 ? 1 : 0;
-}
-
-__global__ void k_visible_compact(int N, const float* __restrict__ rec, const int32_t* __restrict__ flag,
-                                  const int32_t* __restrict__ pos, uint32_t* __restrict__ keys,
-                                  int32_t* __restrict__ vals)
-{
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= N || !flag[i]) return;
-    const int p = pos[i];
-    keys[p] = __float_as_uint(rec[(size_t)i * GM_REC + 9]);  // z_c > 0: bits order like values
-    vals[p] = i;
+    const bool vis = __float_as_int(rec[(size_t)i * GM_REC + 15]) > 0;
+    keys[i] = vis ? __float_as_uint(rec[(size_t)i * GM_REC + 9]) : 0xffffffffu;
+    vals[i] = i;
 }
 
 // ---------------------------------------------------------------------------
@@ -243,15 +280,17 @@ constexpr int PW_WAVES = 4;  // waves per 256-thread block
 
 template <bool EMIT>
 __global__ void __launch_bounds__(64 * PW_WAVES)
-k_pairs(DevCamera cam, CullParams cp, const long long* __restrict__ d_nvis, int nchunks,
+k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nchunks,
         const int32_t* __restrict__ order, const float* __restrict__ rec, int32_t* __restrict__ chunk_cnt,
-        const int32_t* __restrict__ chunk_off, uint32_t* __restrict__ tkeys, int32_t* __restrict__ tvals)
+        const int32_t* __restrict__ chunk_off, const long long* __restrict__ d_total, long long cap,
+        uint32_t* __restrict__ tkeys, int32_t* __restrict__ tvals)
 {
     __shared__ float s_f[PW_WAVES][8][64];  // u, v, opacity, z_c, g0, g1, sigma, s_crit
     __shared__ int s_i[PW_WAVES][4][64];    // rect lo, rect hi, id, inclusive prefix of tile counts
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const unsigned long long lt = (1ull << lane) - 1ull;
-    const int nvis = (int)*d_nvis;
+    const int nvis = *d_nvis;
+    if (EMIT && *d_total > cap) return;  // over capacity: nothing is written
     for (int chunk = blockIdx.x * PW_WAVES + wave; chunk < nchunks; chunk += gridDim.x * PW_WAVES) {
         const int jl = chunk * 64 + lane;
         int nt = 0;
@@ -323,16 +362,35 @@ k_pairs(DevCamera cam, CullParams cp, const long long* __restrict__ d_nvis, int 
     }
 }
 
-__global__ void k_tile_ranges(const uint32_t* __restrict__ keys, int64_t K, int32_t* __restrict__ ranges)
+// Tile ranges from the tile-sorted keys, four keys per thread.
+__global__ void k_tile_ranges(const uint32_t* __restrict__ keys, const long long* __restrict__ d_count,
+                              long long n_max, int32_t* __restrict__ ranges)
 {
-    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= K) return;
-    const uint32_t t = keys[k];
-    if (k == 0 || keys[k - 1] != t) ranges[2 * t] = (int32_t)k;
-    if (k == K - 1 || keys[k + 1] != t) ranges[2 * t + 1] = (int32_t)(k + 1);
+    const long long K = live_count(d_count, n_max);
+    const long long k0 = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (k0 >= K) return;
+    uint32_t v[6];  // keys k0 - 1 .. k0 + 4, all ones outside [0, K)
+    v[0] = k0 > 0 ? keys[k0 - 1] : 0xffffffffu;
+    if (k0 + 4 <= K) {
+        const uint4 q = *reinterpret_cast<const uint4*>(keys + k0);  // k0 % 4 == 0, buffer 16-B aligned
+        v[1] = q.x;
+        v[2] = q.y;
+        v[3] = q.z;
+        v[4] = q.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[1 + i] = k0 + i < K ? keys[k0 + i] : 0xffffffffu;
+    }
+    v[5] = k0 + 4 < K ? keys[k0 + 4] : 0xffffffffu;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const long long k = k0 + i;
+        if (k >= K) break;
+        const uint32_t t = v[1 + i];
+        if (v[i] != t) ranges[2 * t] = (int32_t)k;
+        if (v[2 + i] != t) ranges[2 * t + 1] = (int32_t)(k + 1);
+    }
 }
-
-__global__ void k_store_count(long long* __restrict__ dst, int64_t v) { *dst = v; }
 
 struct SortWs {
     int32_t *flag, *pos;
@@ -340,8 +398,9 @@ struct SortWs {
     int32_t *dva, *dvb;
     uint32_t *tka, *tkb;
     int32_t* tva;
-    long long *nvis, *npairs;
-    void* aux;  // scans and radix histograms
+    long long* n;
+    void* scan;  // scan of the chunk counts
+    void* aux;   // radix histograms and their scans
 };
 
 static size_t sort_layout(int64_t N, int64_t cap, int64_t T, char* base, SortWs* w)
@@ -363,10 +422,10 @@ static size_t sort_layout(int64_t N, int64_t cap, int64_t T, char* base, SortWs*
     s.tka = (uint32_t*)take(4 * c1);
     s.tkb = (uint32_t*)take(4 * c1);
     s.tva = (int32_t*)take(4 * c1);
-    s.nvis = (long long*)take(8);
-    s.npairs = (long long*)take(8);
+    s.n = (long long*)take(8);
     const int64_t m = std::max<int64_t>(std::max<int64_t>(n1, c1), T);
-    s.aux = take(std::max(radix_ws_bytes(m), scan_ws_bytes(m)));
+    s.scan = take(scan_ws_bytes(div_up(n1, 64)));
+    s.aux = take(radix_ws_bytes(m));
     if (w) *w = s;
     return o;
 }
@@ -401,49 +460,44 @@ gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec, c
     SortWs w;
     sort_layout(N, cap, T, (char*)ws, &w);
 
-    k_fill_i32s<<<(unsigned)div_up(2 * T, 256), 256, 0, stream>>>(tile_ranges, 2 * T, 0);
+    long long* total = reinterpret_cast<long long*>(n_keys);
+    k_sort_init<<<(unsigned)div_up(2 * T, 256), 256, 0, stream>>>(tile_ranges, 2 * T, total, w.n, N);
     GM_LAUNCH_CHECK();
-    if (N == 0) {
-        *n_keys = 0;
-        return GM_OK;
-    }
+    if (N == 0) return GM_OK;
     const unsigned gN = (unsigned)div_up(N, 256);
-    // 1. visible Gaussians in id order, then stable sort by depth bits
-    k_visible_flags<<<gN, 256, 0, stream>>>(N, rec, w.flag);
+    // 1. stable sort of all Gaussians by depth key; the listed ones come first
+    k_depth_keys<<<gN, 256, 0, stream>>>(N, rec, w.dka, w.dva);
     GM_LAUNCH_CHECK();
-    if (gm_status s = exclusive_scan(w.flag, w.pos, N, w.nvis, w.aux, stream)) return s;
-    k_visible_compact<<<gN, 256, 0, stream>>>(N, rec, w.flag, w.pos, w.dka, w.dva);
-    GM_LAUNCH_CHECK();
-    if (gm_status s = radix_sort(w.dka, w.dva, w.dkb, w.dvb, 4, 0, w.nvis, N, w.aux, stream)) return s;
+    const int32_t* offs = nullptr;
+    if (gm_status s = radix_sort(w.dka, w.dva, w.dkb, w.dvb, 4, 0, w.n, N, w.aux, stream, &offs)) return s;
     const int32_t* order = w.dva;  // 4 passes: back in the first buffer pair
-    // 2. surviving (Gaussian, tile) pairs per chunk of 64 Gaussians in depth order,
-    //    scan, read back the total
+    // number of listed Gaussians = offset of top byte 0xff in the last pass, block 0;
+    // it stays valid until the tile sort below reuses the histogram buffers
+    const int32_t* d_nvis = offs + (size_t)(RS_RADIX - 1) * div_up(N, RS_CHUNK);
+    // 2. surviving (Gaussian, tile) pairs per chunk of 64 Gaussians in depth order, scan
     CullParams cp{tile_dmax, softness};
     const int nchunks = (int)div_up(N, 64);
     const unsigned gW = (unsigned)std::min<int64_t>(div_up(nchunks, PW_WAVES), 2048);
-    k_pairs<false><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, w.nvis, nchunks, order, rec, w.flag, nullptr,
-                                                    nullptr, nullptr);
+    k_pairs<false><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, d_nvis, nchunks, order, rec, w.flag, nullptr,
+                                                    nullptr, 0, nullptr, nullptr);
     GM_LAUNCH_CHECK();
-    if (gm_status s = exclusive_scan(w.flag, w.pos, nchunks, w.npairs, w.aux, stream)) return s;
-    int64_t K = 0;
-    if (gm_status s = read_back_i64(w.npairs, &K, stream)) return s;
-    *n_keys = K;
-    if (K > cap || K > INT32_MAX) {
-        set_error("sorted_ids capacity %lld, %lld keys needed", (long long)cap, (long long)K);
-        return GM_ERR_CAPACITY;
-    }
-    if (K == 0) return GM_OK;
-    // 3. emit (tile, id) in depth order; 4. stable sort by tile
+    if (gm_status s = exclusive_scan(w.flag, w.pos, nchunks, total, w.scan, stream)) return s;
+    // 3. emit (tile, id) in depth order; 4. stable sort by tile; 5. tile ranges.
+    //    Every kernel from here on compares the total with cap on the device and
+    //    writes nothing above it.
+    const int64_t kcap = std::min<int64_t>(cap, INT32_MAX);
+    if (kcap == 0) return GM_OK;
     int npass = 1;
     while (npass < 4 && (T - 1) >> (8 * npass)) ++npass;
     uint32_t* ka = w.tka;
     int32_t* va = (npass % 2 == 0) ? sorted_ids : w.tva;
     int32_t* vb = (npass % 2 == 0) ? w.tva : sorted_ids;
-    k_pairs<true><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, w.nvis, nchunks, order, rec, nullptr, w.pos, ka, va);
+    k_pairs<true><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, d_nvis, nchunks, order, rec, nullptr, w.pos, total,
+                                                   kcap, ka, va);
     GM_LAUNCH_CHECK();
-    if (gm_status s = radix_sort(ka, va, w.tkb, vb, npass, 0, w.npairs, K, w.aux, stream)) return s;
+    if (gm_status s = radix_sort(ka, va, w.tkb, vb, npass, 0, total, kcap, w.aux, stream)) return s;
     const uint32_t* kfin = (npass % 2 == 0) ? w.tka : w.tkb;
-    k_tile_ranges<<<(unsigned)div_up(K, 256), 256, 0, stream>>>(kfin, K, tile_ranges);
+    k_tile_ranges<<<(unsigned)div_up(div_up(kcap, 4), 256), 256, 0, stream>>>(kfin, total, kcap, tile_ranges);
     GM_LAUNCH_CHECK();
     return GM_OK;
 }

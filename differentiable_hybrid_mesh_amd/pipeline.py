@@ -1,8 +1,9 @@
 """Buffer management around the six C-ABI calls (allocation and call order only).
 
 ``DeviceScene`` uploads a scene's arrays to the GPU once.  ``Renderer`` owns the
-per-view device buffers (torch tensors used as plain device memory), grows the two
-variable-length lists on GM_ERR_CAPACITY, and runs
+per-view device buffers (torch tensors used as plain device memory), reads the two
+list lengths back once per forward pass (the calls themselves never synchronise),
+grows a list that overflowed and runs the pass again, and runs
 
     gm_bin_triangles -> gm_raster_zbuffer -> gm_project_gaussians ->
     gm_sort_tile_keys -> gm_composite_hybrid_fwd   (forward)
@@ -125,6 +126,8 @@ class Renderer:
         self.g_mesh_depth = torch.empty((self.H, self.W), dtype=f32, device=dev)
         self.n_pairs = 0
         self.n_keys = 0
+        self.counts = torch.zeros(2, dtype=torch.int64, device=dev)  # device: n_pairs, n_keys
+        self.counts_host = torch.zeros(2, dtype=torch.int64, pin_memory=True)
         self.view = 0
         self.cull = True
 
@@ -138,14 +141,8 @@ class Renderer:
     # -- the six calls ---------------------------------------------------------
     def bin_and_zbuffer(self, view: int):
         ds, cam, st = self.ds, self.ds.cams[view], _stream()
-        while True:
-            status, n = G.gm_bin_triangles(cam, ds.mesh, self.vscreen, self.tile_offsets, self.tile_tris,
-                                           self.pair_cap, self.ws_bin, st)
-            if status == G.GM_OK:
-                break
-            self.pair_cap = int(n * 1.25) + 1024
-            self.tile_tris = torch.empty(self.pair_cap, dtype=torch.int32, device=ds.device)
-        self.n_pairs = n
+        G.gm_bin_triangles(cam, ds.mesh, self.vscreen, self.tile_offsets, self.tile_tris, self.pair_cap,
+                           self.counts[0:1], self.ws_bin, st)
         G.gm_raster_zbuffer(cam, ds.mesh, self.vscreen, self.tile_offsets, self.tile_tris, self.face_id,
                             self.depth, self.tile_dmax, st)
 
@@ -155,15 +152,29 @@ class Renderer:
                                s.sh_degree, self.rec, _stream())
 
     def sort(self, view: int, cull: bool = True):
-        ds, s, st = self.ds, self.ds.scene, _stream()
+        ds, s = self.ds, self.ds.scene
         dmax = self.tile_dmax if cull else None
-        while True:
-            status, n = G.gm_sort_tile_keys(ds.cams[view], self.N, self.rec, dmax, s.softness,
-                                            self.tile_ranges, self.sorted_ids, self.key_cap, self.ws_sort, st)
-            if status == G.GM_OK:
-                break
-            self._alloc_keys(int(n * 1.25) + 1024)
-        self.n_keys = n
+        G.gm_sort_tile_keys(ds.cams[view], self.N, self.rec, dmax, s.softness, self.tile_ranges, self.sorted_ids,
+                            self.key_cap, self.counts[1:2], self.ws_sort, _stream())
+
+    def fetch_counts(self):
+        """Queue a copy of the two list lengths to pinned host memory (no wait)."""
+        self.counts_host.copy_(self.counts, non_blocking=True)
+
+    def read_counts(self) -> bool:
+        """After the stream has passed fetch_counts(): store the lengths, grow any list
+        that overflowed; True when both fitted."""
+        n_pairs, n_keys = (int(x) for x in self.counts_host.tolist())
+        self.n_pairs, self.n_keys = n_pairs, n_keys
+        ok = True
+        if n_pairs > self.pair_cap:
+            self.pair_cap = int(n_pairs * 1.25) + 1024
+            self.tile_tris = torch.empty(self.pair_cap, dtype=torch.int32, device=self.ds.device)
+            ok = False
+        if n_keys > self.key_cap:
+            self._alloc_keys(int(n_keys * 1.25) + 1024)
+            ok = False
+        return ok
 
     def composite_fwd(self, view: int):
         ds, s = self.ds, self.ds.scene
@@ -180,12 +191,22 @@ class Renderer:
                                   self.g_mesh_depth, _stream())
 
     # -- whole passes -----------------------------------------------------------
-    def forward(self, view: int = 0, cull: bool = True):
+    def forward_async(self, view: int = 0, cull: bool = True):
+        """Queue one forward pass and the copy of the list lengths; no synchronisation.
+        The outputs are valid once read_counts() returns True for this pass."""
         self.view, self.cull = view, cull
         self.bin_and_zbuffer(view)
         self.project(view)
         self.sort(view, cull)
         self.composite_fwd(view)
+        self.fetch_counts()
+
+    def forward(self, view: int = 0, cull: bool = True):
+        while True:
+            self.forward_async(view, cull)
+            torch.cuda.current_stream().synchronize()
+            if self.read_counts():
+                break
         return {"rgb": self.out_rgb, "depth": self.out_depth, "alpha": self.out_alpha}
 
     def backward(self, g_rgb, g_depth=None, g_alpha=None):
@@ -196,3 +217,9 @@ class Renderer:
         """One forward + backward of one view (the benchmark's unit of work)."""
         self.forward(view, cull)
         return self.backward(grads["rgb"], grads.get("depth"), grads.get("alpha"))
+
+    def step_async(self, view: int, grads: dict, cull: bool = True):
+        """step() without synchronisation: the lengths are checked by the caller with
+        read_counts() after the stream has run (the lists must already be large enough)."""
+        self.forward_async(view, cull)
+        self.composite_bwd(view, grads["rgb"], grads.get("depth"), grads.get("alpha"))

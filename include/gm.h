@@ -24,15 +24,18 @@
  * Memory.  Every array pointer is a DEVICE pointer to caller-owned memory unless
  * marked (host).  "[k][N]" is k contiguous planes of N values (structure of
  * arrays).  The library never allocates, frees or keeps a pointer after a call
- * returns.  Calls are asynchronous on `stream` except where stated: the two calls
- * that produce a variable-length list read back its length (one small
- * device-to-host copy and a stream synchronisation).
+ * returns.  Every call is asynchronous on `stream` and never synchronises it.
+ *
+ * Variable-length lists.  The two calls that produce one (gm_bin_triangles,
+ * gm_sort_tile_keys) write its length to a device int64 (`n_pairs`, `n_keys`) and
+ * take the list's capacity `cap`.  When the length exceeds cap the list is not
+ * written and the call's other outputs describe an empty list (every tile range
+ * empty), so later calls stay in bounds; the caller reads the length once the
+ * stream has reached it, and on overflow enlarges the list and calls again.
  *
  * Errors.  Every call returns a gm_status.  GM_ERR_ARG: a required pointer is
  * NULL, a size is negative or out of range, the workspace is too small; checked on
- * the host before anything is launched.  GM_ERR_CAPACITY: an output list does not
- * fit; `*n_pairs` / `*n_keys` then hold the size needed and the list outputs are
- * not written.  GM_ERR_HIP: a HIP call failed.  gm_last_error() returns a
+ * the host before anything is launched.  GM_ERR_HIP: a HIP call failed.  gm_last_error() returns a
  * thread-local message for the last non-OK status.  Degenerate data follow rules,
  * not errors: zero-area triangles cover nothing, Gaussians with det <= 0 or behind
  * the near plane are not listed, N = 0 and F = 0 are legal.
@@ -57,7 +60,6 @@ extern "C" {
 typedef enum {
     GM_OK = 0,
     GM_ERR_ARG = -1,
-    GM_ERR_CAPACITY = -2,
     GM_ERR_HIP = -3
 } gm_status;
 
@@ -108,9 +110,9 @@ typedef struct gm_mesh {
  * fp64 signed area is non-zero; it goes to every tile that holds a pixel centre of
  * its pixel-centre bounding box.  tile_offsets [T+1] (exclusive prefix sums) and
  * tile_tris [n_pairs] list the face ids per tile (order inside a tile unspecified).
- * cap: capacity of tile_tris; *n_pairs (host, out): number of (tile, face) pairs.
+ * cap: capacity of tile_tris; n_pairs (device int64, out): number of (tile, face)
+ * pairs; above cap, tile_tris is not written and tile_offsets is all zeros.
  * ws: device workspace of at least gm_bin_triangles_ws(...) bytes.
- * Synchronises `stream` once (the pair count readback).
  * ------------------------------------------------------------------------- */
 size_t gm_bin_triangles_ws(int32_t V, int32_t F, int32_t width, int32_t height);
 gm_status gm_bin_triangles(const gm_camera* cam, const gm_mesh* mesh, float* vscreen,
@@ -176,8 +178,9 @@ gm_status gm_project_gaussians(const gm_camera* cam, int32_t N, const float* mea
  * dropped when zmin_ti >= Dmax_t + 1e-5 |Dmax_t|).  Such a pair falls under the
  * 1/255 skip rule at every pixel of the tile, so outputs are unchanged.
  * Outputs: tile_ranges [T][2] = [start, end) into sorted_ids [n_keys].
- * cap: capacity of sorted_ids; *n_keys (host, out).  ws: at least
- * gm_sort_tile_keys_ws(N, cap, W, H) bytes.  Synchronises `stream` once.
+ * cap: capacity of sorted_ids; n_keys (device int64, out): number of listed pairs;
+ * above cap, sorted_ids is not written and every tile range is [0, 0).  ws: at
+ * least gm_sort_tile_keys_ws(N, cap, W, H) bytes.
  * ------------------------------------------------------------------------- */
 size_t gm_sort_tile_keys_ws(int32_t N, int64_t cap, int32_t width, int32_t height);
 gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec,

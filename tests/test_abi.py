@@ -69,11 +69,12 @@ def test_argument_errors_before_any_launch(G):
     assert L.gm_raster_zbuffer(C.byref(bad), None, None, None, None, None, None, None, None) == G.GM_ERR_ARG
     # workspace too small
     m = G.GmMesh()
-    n = C.c_int64(0)
-    assert L.gm_bin_triangles(C.byref(cam), C.byref(m), 16, 16, 16, 0, C.byref(n), 16, 1, None) == G.GM_ERR_ARG
+    assert L.gm_bin_triangles(C.byref(cam), C.byref(m), 16, 16, 16, 0, 16, 16, 1, None) == G.GM_ERR_ARG
     assert b"workspace" in L.gm_last_error()
+    # missing count pointer
+    assert L.gm_bin_triangles(C.byref(cam), C.byref(m), 16, 16, 16, 0, None, 16, 1 << 20, None) == G.GM_ERR_ARG
     # negative softness
-    assert L.gm_sort_tile_keys(C.byref(cam), 0, None, None, C.c_float(-1.0), 16, None, 0, C.byref(n), 16,
+    assert L.gm_sort_tile_keys(C.byref(cam), 0, None, None, C.c_float(-1.0), 16, None, 0, 16, 16,
                                1 << 20, None) == G.GM_ERR_ARG
     # texture side not a power of two
     assert L.gm_build_mipmaps(16, 100, 16, None) == G.GM_ERR_ARG

@@ -193,14 +193,29 @@ def test_softness_zero_and_sh_degrees():
         _check_all(s, 0, gpu, ora, tiles, True, "deg %d softness %g" % (deg, s.softness))
 
 
-def test_capacity_error_reports_needed_size():
+def test_list_overflow_reports_needed_size():
+    """A list above its capacity is not written, reads as empty downstream, and its
+    length is reported on the device; the renderer then grows it and succeeds."""
     import torch
     from differentiable_hybrid_mesh_amd import _lib as G
     from differentiable_hybrid_mesh_amd.pipeline import DeviceScene, Renderer
     s = _scene("c1")
     r = Renderer(DeviceScene(s), pair_cap=1, key_cap=1)
-    st, n = G.gm_bin_triangles(r.ds.cams[0], r.ds.mesh, r.vscreen, r.tile_offsets, r.tile_tris, 1, r.ws_bin,
-                               torch.cuda.current_stream().cuda_stream)
-    assert st == G.GM_ERR_CAPACITY and n > 1
+    st = torch.cuda.current_stream().cuda_stream
+    r.tile_tris.fill_(-7)
+    G.gm_bin_triangles(r.ds.cams[0], r.ds.mesh, r.vscreen, r.tile_offsets, r.tile_tris, 1, r.counts[0:1],
+                       r.ws_bin, st)
+    torch.cuda.synchronize()
+    n = int(r.counts[0].item())
+    assert n > 1
+    assert int(r.tile_tris[0].item()) == -7 and int(r.tile_offsets.abs().sum().item()) == 0
     r.forward(0)  # grows both lists and succeeds
     assert r.n_pairs == n and r.key_cap >= r.n_keys > 1
+    k = r.n_keys
+    # the sort with one slot: sorted_ids untouched, every range empty, length reported
+    r.sorted_ids.fill_(-7)
+    G.gm_sort_tile_keys(r.ds.cams[0], r.N, r.rec, r.tile_dmax, s.softness, r.tile_ranges, r.sorted_ids, 1,
+                        r.counts[1:2], r.ws_sort, st)
+    torch.cuda.synchronize()
+    assert int(r.counts[1].item()) == k
+    assert int((r.sorted_ids != -7).sum().item()) == 0 and int(r.tile_ranges.abs().sum().item()) == 0
