@@ -64,44 +64,77 @@ __device__ inline bool face_tile_rect(const DevCamera& cam, int V, int F, int f,
     return true;
 }
 
+// Faces of one wave are neighbours in the mesh and share tiles, so the wave walks
+// the tiles of its faces' rects in lockstep (the k-th tile of every face at step k)
+// and at each step groups lanes by tile with ballots: one atomic per distinct tile.
+__device__ __forceinline__ void next_tile(int& cx, int& cy, int x0, int x1)
+{
+    if (++cx > x1) {
+        cx = x0;
+        ++cy;
+    }
+}
+
 __global__ void k_bin_count(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
                             const uint8_t* __restrict__ mask, const float* __restrict__ vs,
                             int2* __restrict__ face_rect, int32_t* __restrict__ tile_cnt)
 {
     const int f = blockIdx.x * blockDim.x + threadIdx.x;
-    if (f >= F) return;
-    int r[4];
-    if (!face_tile_rect(cam, V, F, f, faces, mask, vs, r)) {
-        face_rect[f] = make_int2(1, 0);  // empty: x0 > x1
-        return;
+    const int lane = threadIdx.x & 63;
+    int r[4] = {0, 0, 0, 0};
+    const bool ok = f < F && face_tile_rect(cam, V, F, f, faces, mask, vs, r);
+    if (f < F) face_rect[f] = ok ? make_int2(r[0] | (r[1] << 16), r[2] | (r[3] << 16)) : make_int2(1, 0);
+    const int nt = ok ? (r[2] - r[0] + 1) * (r[3] - r[1] + 1) : 0;
+    int cx = r[0], cy = r[1];
+    for (int k = 0; __ballot(k < nt); ++k) {
+        const int tk = k < nt ? cy * cam.tx + cx : -1;
+        unsigned long long pend = __ballot(tk >= 0);
+        while (pend) {
+            const int leader = __builtin_ctzll(pend);
+            const int tl = __builtin_amdgcn_readlane(tk, leader);
+            const unsigned long long grp = __ballot(tk == tl);
+            if (lane == leader) atomicAdd(&tile_cnt[tl], __popcll(grp));
+            pend &= ~grp;
+        }
+        next_tile(cx, cy, r[0], r[2]);
     }
-    face_rect[f] = make_int2(r[0] | (r[1] << 16), r[2] | (r[3] << 16));
-    for (int ty = r[1]; ty <= r[3]; ++ty)
-        for (int tx = r[0]; tx <= r[2]; ++tx) atomicAdd(&tile_cnt[ty * cam.tx + tx], 1);
 }
 
-// Threads [0, F) scatter face ids.  When the pair total exceeds cap nothing is
-// scattered and threads [0, T] instead clear tile_offsets, so the bins read as
-// empty downstream (the caller enlarges tile_tris and bins again).
+// Threads [0, F) scatter face ids, grouped as in the count.  When the pair total
+// exceeds cap nothing is scattered and threads [0, T] instead clear tile_offsets,
+// so the bins read as empty downstream (the caller enlarges tile_tris and bins
+// again).
 __global__ void k_bin_scatter(DevCamera cam, int F, int T, const int2* __restrict__ face_rect,
                               int32_t* __restrict__ tile_off, const long long* __restrict__ total,
                               int64_t cap, int32_t* __restrict__ cursor, int32_t* __restrict__ tile_tris)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (*total > cap) {
+    if (*total > cap) {  // uniform
         if (i <= T) tile_off[i] = 0;
         return;
     }
-    if (i >= F) return;
-    const int2 pr = face_rect[i];
+    const int lane = threadIdx.x & 63;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    const int2 pr = i < F ? face_rect[i] : make_int2(1, 0);
+    const bool ok = !(pr.x == 1 && pr.y == 0);
     const int x0 = pr.x & 0xffff, y0 = pr.x >> 16, x1 = pr.y & 0xffff, y1 = pr.y >> 16;
-    if (pr.x == 1 && pr.y == 0) return;
-    for (int ty = y0; ty <= y1; ++ty)
-        for (int tx = x0; tx <= x1; ++tx) {
-            const int t = ty * cam.tx + tx;
-            const int pos = atomicAdd(&cursor[t], 1);
-            tile_tris[tile_off[t] + pos] = i;
+    const int nt = ok ? (x1 - x0 + 1) * (y1 - y0 + 1) : 0;
+    int cx = x0, cy = y0;
+    for (int k = 0; __ballot(k < nt); ++k) {
+        const int tk = k < nt ? cy * cam.tx + cx : -1;
+        unsigned long long pend = __ballot(tk >= 0);
+        while (pend) {
+            const int leader = __builtin_ctzll(pend);
+            const int tl = __builtin_amdgcn_readlane(tk, leader);
+            const unsigned long long grp = __ballot(tk == tl);
+            int base = 0;
+            if (lane == leader) base = atomicAdd(&cursor[tl], __popcll(grp));
+            base = __builtin_amdgcn_readlane(base, leader);
+            if (tk == tl) tile_tris[tile_off[tl] + base + __popcll(grp & lt)] = i;
+            pend &= ~grp;
         }
+        next_tile(cx, cy, x0, x1);
+    }
 }
 
 // Triangle setup as staged in LDS: one 128-byte record.

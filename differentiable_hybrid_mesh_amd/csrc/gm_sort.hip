@@ -42,12 +42,14 @@ __device__ inline long long live_count(const long long* __restrict__ d_count, lo
 }
 
 // ---------------------------------------------------------------------------
-// stable LSD radix sort pass
+// stable LSD radix sort pass over a digit of BITS <= 8 bits
 // ---------------------------------------------------------------------------
+template <int BITS>
 __global__ void __launch_bounds__(RS_THREADS)
 k_radix_hist(const uint32_t* __restrict__ keys, const long long* __restrict__ d_count, long long n_max,
              int shift, int nblocks, int32_t* __restrict__ hist)
 {
+    constexpr int R = 1 << BITS;
     __shared__ int32_t h[RS_WAVES][RS_RADIX];  // one histogram per wave: fewer colliding LDS atomics
     const long long n = live_count(d_count, n_max);
     const int wave = threadIdx.x >> 6;
@@ -58,13 +60,15 @@ k_radix_hist(const uint32_t* __restrict__ keys, const long long* __restrict__ d_
 #pragma unroll 4
     for (int k = 0; k < RS_ITEMS; ++k) {
         const long long e = base + (long long)k * RS_THREADS + threadIdx.x;
-        if (e < n) atomicAdd(&h[wave][(keys[e] >> shift) & 0xff], 1);
+        if (e < n) atomicAdd(&h[wave][(keys[e] >> shift) & (R - 1)], 1);
     }
     __syncthreads();
-    int c = 0;
+    if (threadIdx.x < R) {
+        int c = 0;
 #pragma unroll
-    for (int w = 0; w < RS_WAVES; ++w) c += h[w][threadIdx.x];
-    hist[threadIdx.x * nblocks + blockIdx.x] = c;
+        for (int w = 0; w < RS_WAVES; ++w) c += h[w][threadIdx.x];
+        hist[threadIdx.x * nblocks + blockIdx.x] = c;
+    }
 }
 
 // Stable scatter of one LSD pass over a block of RS_CHUNK keys.  Wave w ranks its
@@ -74,6 +78,7 @@ k_radix_hist(const uint32_t* __restrict__ keys, const long long* __restrict__ d_
 // program order).  One block scan then turns the per-wave counts into bases, keys
 // are placed in LDS in digit order, and each digit's run leaves the block as
 // contiguous stores.
+template <int BITS>
 __global__ void __launch_bounds__(RS_THREADS)
 k_radix_scatter(const uint32_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
                 const long long* __restrict__ d_count, long long n_max, int shift, int nblocks,
@@ -84,6 +89,7 @@ k_radix_scatter(const uint32_t* __restrict__ keys_in, const int32_t* __restrict_
     __shared__ int32_t s_wc[RS_WAVES][RS_RADIX];  // running counts per wave, then per-wave bases
     __shared__ int32_t s_lstart[RS_RADIX], s_goff[RS_RADIX];
     __shared__ int32_t s_wsum[RS_WAVES];
+    constexpr int R = 1 << BITS;
     const long long n = live_count(d_count, n_max);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const unsigned long long lt = (1ull << lane) - 1ull;
@@ -91,7 +97,7 @@ k_radix_scatter(const uint32_t* __restrict__ keys_in, const int32_t* __restrict_
     if (base >= n) return;
 #pragma unroll
     for (int w = 0; w < RS_WAVES; ++w) s_wc[w][t] = 0;
-    s_goff[t] = offs[t * nblocks + blockIdx.x];
+    if (t < R) s_goff[t] = offs[t * nblocks + blockIdx.x];
     __syncthreads();
     uint32_t key[RS_ITEMS];
     int32_t val[RS_ITEMS];
@@ -107,10 +113,10 @@ k_radix_scatter(const uint32_t* __restrict__ keys_in, const int32_t* __restrict_
 #pragma unroll
     for (int r = 0; r < RS_ITEMS; ++r) {
         const bool act = wbase + r * 64 + lane < n;
-        const int d = (key[r] >> shift) & 0xff;
+        const int d = (key[r] >> shift) & (R - 1);
         unsigned long long peers = __ballot(act);
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
+        for (int b = 0; b < BITS; ++b) {
             const bool bit = (d >> b) & 1;
             const unsigned long long bb = __ballot(bit);
             peers &= bit ? bb : ~bb;
@@ -150,7 +156,7 @@ k_radix_scatter(const uint32_t* __restrict__ keys_in, const int32_t* __restrict_
 #pragma unroll
     for (int r = 0; r < RS_ITEMS; ++r) {
         if (wbase + r * 64 + lane < n) {
-            const int pos = s_wc[wave][(key[r] >> shift) & 0xff] + rank[r];
+            const int pos = s_wc[wave][(key[r] >> shift) & (R - 1)] + rank[r];
             s_k[pos] = key[r];
             s_v[pos] = val[r];
         }
@@ -159,12 +165,14 @@ k_radix_scatter(const uint32_t* __restrict__ keys_in, const int32_t* __restrict_
     const int nvalid = (int)min((long long)RS_CHUNK, n - base);
     for (int p = t; p < nvalid; p += RS_THREADS) {
         const uint32_t k = s_k[p];
-        const int d = (k >> shift) & 0xff;
+        const int d = (k >> shift) & (R - 1);
         const int g = s_goff[d] + (p - s_lstart[d]);
         keys_out[g] = k;
         vals_out[g] = s_v[p];
     }
 }
+
+static int radix_passes(int nbits) { return nbits <= 0 ? 1 : (nbits + 7) / 8; }
 
 size_t radix_ws_bytes(int64_t n)
 {
@@ -173,11 +181,26 @@ size_t radix_ws_bytes(int64_t n)
            align_up(sizeof(long long), 256);
 }
 
-// Sorts n_max-bounded (keys, vals) by key bits [lo_bit, lo_bit + 8 npass) with LSD
-// passes of 8 bits; the live count is *d_count (device), zero when above n_max.  Ping-pongs between (ka, va) and
-// (kb, vb); the result lands in (k_out, v_out), which must be one of the two pairs'
-// buffers chosen by the caller so that the final pass writes there.
-static gm_status radix_sort(uint32_t* ka, int32_t* va, uint32_t* kb, int32_t* vb, int npass, int lo_bit,
+template <int BITS>
+static gm_status radix_pass(const uint32_t* kin, const int32_t* vin, uint32_t* kout, int32_t* vout, int shift,
+                            const long long* d_count, int64_t n_max, int nb, int32_t* hist, int32_t* offs,
+                            long long* tot, void* scan_ws, hipStream_t stream)
+{
+    k_radix_hist<BITS><<<nb, RS_THREADS, 0, stream>>>(kin, d_count, n_max, shift, nb, hist);
+    GM_LAUNCH_CHECK();
+    if (gm_status s = exclusive_scan(hist, offs, (int64_t)(1 << BITS) * nb, tot, scan_ws, stream)) return s;
+    k_radix_scatter<BITS><<<nb, RS_THREADS, 0, stream>>>(kin, vin, d_count, n_max, shift, nb, offs, kout, vout);
+    GM_LAUNCH_CHECK();
+    return GM_OK;
+}
+
+// Sorts n_max-bounded (keys, vals) by key bits [0, nbits) with LSD passes of at most 8
+// bits, split as evenly as possible (fewer digit values per pass than 256 give longer
+// runs of equal digits and so longer contiguous stores); the live count is *d_count
+// (device), zero when above n_max.  Ping-pongs between (ka, va) and (kb, vb): an even
+// number of passes ends in (ka, va), an odd one in (kb, vb).  *last_offs receives the
+// [digit][block] exclusive offsets of the last pass.
+static gm_status radix_sort(uint32_t* ka, int32_t* va, uint32_t* kb, int32_t* vb, int nbits,
                             const long long* d_count, int64_t n_max, void* ws, hipStream_t stream,
                             const int32_t** last_offs = nullptr)
 {
@@ -194,13 +217,23 @@ static gm_status radix_sort(uint32_t* ka, int32_t* va, uint32_t* kb, int32_t* vb
     int32_t* vin = va;
     uint32_t* kout = kb;
     int32_t* vout = vb;
+    const int npass = radix_passes(nbits);
+    int shift = 0;
     for (int p = 0; p < npass; ++p) {
-        const int shift = lo_bit + 8 * p;
-        k_radix_hist<<<nb, RS_THREADS, 0, stream>>>(kin, d_count, n_max, shift, nb, hist);
-        GM_LAUNCH_CHECK();
-        if (gm_status s = exclusive_scan(hist, offs, (int64_t)RS_RADIX * nb, tot, scan_ws, stream)) return s;
-        k_radix_scatter<<<nb, RS_THREADS, 0, stream>>>(kin, vin, d_count, n_max, shift, nb, offs, kout, vout);
-        GM_LAUNCH_CHECK();
+        const int bits = (nbits - shift + (npass - p) - 1) / (npass - p);  // ceil(remaining / passes left)
+        gm_status s = GM_OK;
+        switch (bits) {
+        case 1: s = radix_pass<1>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 2: s = radix_pass<2>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 3: s = radix_pass<3>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 4: s = radix_pass<4>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 5: s = radix_pass<5>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 6: s = radix_pass<6>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 7: s = radix_pass<7>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        default: s = radix_pass<8>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        }
+        if (s) return s;
+        shift += bits;
         uint32_t* tk = kin;
         int32_t* tv = vin;
         kin = kout;
@@ -208,7 +241,7 @@ static gm_status radix_sort(uint32_t* ka, int32_t* va, uint32_t* kb, int32_t* vb
         kout = tk;
         vout = tv;
     }
-    if (last_offs) *last_offs = offs;  // [digit][block] exclusive offsets of the last pass
+    if (last_offs) *last_offs = offs;
     return GM_OK;
 }
 
@@ -235,6 +268,7 @@ __global__ void k_depth_keys(int N, const float* __restrict__ rec, uint32_t* __r
 struct CullParams {
     const float* tile_dmax;  // nullptr: no culling
     float softness;
+    int lds;                 // 1: tile_dmax is staged in dynamic LDS (T floats)
 };
 
 // f must reach (1/255)(1 - 1e-3) / min(0.99, o) for the pair to matter anywhere;
@@ -250,13 +284,12 @@ __device__ inline float cull_scrit(float o)
 
 // Pair (tile, Gaussian) is dropped when the tile is fully covered and
 // min(0.99, o) Phi((Dmax + 1e-5 |Dmax| - zmin) / (sigma softness)) < (1/255)(1 - 1e-3),
-// evaluated as s < s_crit.  zmin is the conditional depth's minimum over the four
-// corner pixel centres of the tile.
-__device__ inline bool culled(const DevCamera& cam, const CullParams& cp, int tx, int ty, float u, float v,
-                              float zc, float g0, float g1, float sig, float scrit)
+// evaluated as Dmax + 1e-5 |Dmax| - zmin < s_crit sigma softness (sigma softness > 0;
+// rounding only moves decisions inside the threshold's 1e-3 margin).  zmin is the
+// conditional depth's minimum over the four corner pixel centres of the tile.
+__device__ inline bool culled(const DevCamera& cam, float softness, float dmax, int tx, int ty, float u, float v,
+                              float zc, float g0, float g1, float sig_soft, float scrit)
 {
-    if (!cp.tile_dmax) return false;
-    const float dmax = cp.tile_dmax[ty * cam.tx + tx];
     if (!(dmax < INFINITY)) return false;
     const float xa = tx * GM_TILE + 0.5f, ya = ty * GM_TILE + 0.5f;
     const float xb = (float)min((tx + 1) * GM_TILE, cam.width) - 0.5f;
@@ -265,18 +298,23 @@ __device__ inline bool culled(const DevCamera& cam, const CullParams& cp, int tx
     const float ay = g1 * (ya - v), by = g1 * (yb - v);
     const float zmin = zc + (fminf(ax, bx) + fminf(ay, by));
     const float lim = dmax + 1e-5f * fabsf(dmax);
-    if (cp.softness > 0.0f) return (lim - zmin) / (sig * cp.softness) < scrit;
+    if (softness > 0.0f) return lim - zmin < scrit * sig_soft;
     return !(zmin < lim) || scrit == INFINITY;
 }
 
 // Pairs of the visible Gaussians in depth order.  A wave takes a chunk of 64
-// consecutive Gaussians, prefix-sums the tile counts of their rects and treats the
-// chunk's (Gaussian, tile) pairs as one flat sequence, 64 per step: lane l finds the
-// Gaussian of flat index f by binary search over the prefix sums in LDS, tests tile
-// f - start(Gaussian) of its rect (row-major), and a ballot ranks the surviving
-// pairs.  The counting pass produces one total per chunk; the emitting pass writes
-// each chunk's pairs as one contiguous run in (depth, id, tile) order.
-constexpr int PW_WAVES = 4;  // waves per 256-thread block
+// consecutive Gaussians (one per lane), prefix-sums the tile counts of their rects
+// and treats the chunk's (Gaussian, tile) pairs as one flat sequence, 64 per step.
+// Lane l of a step owns flat index f = f0 + l; its Gaussian is the last one whose
+// range starts at or before f: the one carried over from the previous step, unless
+// one of the few Gaussians starting inside the step (a ballot) starts at or before
+// f (a binary search over the starts in LDS when many start there).  The tile is
+// f - start of the rect (row-major, the row from a reciprocal multiply), the cull
+// reads tile_dmax from LDS, and a ballot ranks the surviving pairs.  The counting
+// pass produces one total per chunk; the emitting pass writes each chunk's pairs as
+// one contiguous run in (depth, id, tile) order.
+constexpr int PW_WAVES = 8;  // waves per 512-thread block
+constexpr int PW_LDS_MAX_TILES = 10240;  // tile_dmax staged in LDS up to this many tiles
 
 template <bool EMIT>
 __global__ void __launch_bounds__(64 * PW_WAVES)
@@ -285,12 +323,18 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
         const int32_t* __restrict__ chunk_off, const long long* __restrict__ d_total, long long cap,
         uint32_t* __restrict__ tkeys, int32_t* __restrict__ tvals)
 {
-    __shared__ float s_f[PW_WAVES][8][64];  // u, v, opacity, z_c, g0, g1, sigma, s_crit
-    __shared__ int s_i[PW_WAVES][4][64];    // rect lo, rect hi, id, inclusive prefix of tile counts
+    extern __shared__ float s_dmax[];       // tile_dmax when cp.lds
+    __shared__ float s_f[PW_WAVES][7][64];  // u, v, z_c, g0, g1, sigma softness, s_crit
+    __shared__ int s_i[PW_WAVES][4][64];    // rect lo, rect hi, id, first flat index
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const unsigned long long lt = (1ull << lane) - 1ull;
     const int nvis = *d_nvis;
-    if (EMIT && *d_total > cap) return;  // over capacity: nothing is written
+    if (EMIT && *d_total > cap) return;  // over capacity: nothing is written (uniform)
+    const int T = cam.tx * cam.ty;
+    if (cp.tile_dmax && cp.lds) {
+        for (int i = threadIdx.x; i < T; i += blockDim.x) s_dmax[i] = cp.tile_dmax[i];
+        __syncthreads();
+    }
     for (int chunk = blockIdx.x * PW_WAVES + wave; chunk < nchunks; chunk += gridDim.x * PW_WAVES) {
         const int jl = chunk * 64 + lane;
         int nt = 0;
@@ -302,12 +346,11 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
             nt = ((hi & 0xffff) - (lo & 0xffff)) * ((hi >> 16) - (lo >> 16));
             s_f[wave][0][lane] = a.x;
             s_f[wave][1][lane] = a.y;
-            s_f[wave][2][lane] = b.y;
-            s_f[wave][3][lane] = c.y;
-            s_f[wave][4][lane] = c.z;
-            s_f[wave][5][lane] = c.w;
-            s_f[wave][6][lane] = d.x;
-            s_f[wave][7][lane] = cull_scrit(b.y);
+            s_f[wave][2][lane] = c.y;
+            s_f[wave][3][lane] = c.z;
+            s_f[wave][4][lane] = c.w;
+            s_f[wave][5][lane] = d.x * cp.softness;
+            s_f[wave][6][lane] = cull_scrit(b.y);
             s_i[wave][0][lane] = lo;
             s_i[wave][1][lane] = hi;
             s_i[wave][2][lane] = id;
@@ -318,43 +361,64 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
             const int y = __shfl_up(P, k, 64);
             if (lane >= k) P += y;
         }
-        s_i[wave][3][lane] = P;
-        const int total = __shfl(P, 63, 64);
+        const int start = P - nt;  // first flat index of this lane's Gaussian
+        s_i[wave][3][lane] = start;
+        const int total = __builtin_amdgcn_readlane(P, 63);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         int p = EMIT ? chunk_off[chunk] : 0;
         const int pend = EMIT ? chunk_off[chunk + 1] : 0;  // the counting pass took the same decisions
+        int carry = 0;  // Gaussian of flat index f0 - 1
         for (int f0 = 0; f0 < total; f0 += 64) {
             const int f = f0 + lane;
+            unsigned long long m = __ballot(nt > 0 && start >= f0 && start < f0 + 64);
+            int g = carry;
+            if (__popcll(m) <= 6) {
+                while (m) {
+                    const int h = __builtin_ctzll(m);
+                    m &= m - 1;
+                    if (f >= __builtin_amdgcn_readlane(start, h)) g = h;
+                }
+            } else {
+                int lo = 0, hi = 63;
+                while (lo < hi) {  // last g with start[g] <= f
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (s_i[wave][3][mid] <= f) lo = mid;
+                    else hi = mid - 1;
+                }
+                g = lo;
+            }
+            carry = __builtin_amdgcn_readlane(g, 63);
             bool keep = false;
             int tile = 0, id = 0;
             if (f < total) {
-                int lo = 0, hi = 63;
-                while (lo < hi) {  // first g with prefix[g] > f
-                    const int mid = (lo + hi) >> 1;
-                    if (s_i[wave][3][mid] > f) hi = mid;
-                    else lo = mid + 1;
-                }
-                const int g = lo;
-                const int t = f - (g > 0 ? s_i[wave][3][g - 1] : 0);
+                const int t = f - s_i[wave][3][g];
                 const int rlo = s_i[wave][0][g], rhi = s_i[wave][1][g];
                 const int x0 = rlo & 0xffff, y0 = rlo >> 16, w = (rhi & 0xffff) - x0;
-                const int ty = y0 + t / w, tx = x0 + t % w;
+                // row = floor(t / w): the quotient's fraction is at least 1/(2w) away from
+                // an integer and t < 2^20, so one reciprocal multiply is exact enough
+                const int q = (int)(((float)t + 0.5f) * __builtin_amdgcn_rcpf((float)w));
+                const int ty = y0 + q, tx = x0 + (t - q * w);
                 tile = ty * cam.tx + tx;
                 id = s_i[wave][2][g];
-                keep = !culled(cam, cp, tx, ty, s_f[wave][0][g], s_f[wave][1][g], s_f[wave][3][g], s_f[wave][4][g],
-                               s_f[wave][5][g], s_f[wave][6][g], s_f[wave][7][g]);
+                keep = true;
+                if (cp.tile_dmax) {
+                    const float dmax = cp.lds ? s_dmax[tile] : cp.tile_dmax[tile];
+                    keep = !culled(cam, cp.softness, dmax, tx, ty, s_f[wave][0][g], s_f[wave][1][g],
+                                   s_f[wave][2][g], s_f[wave][3][g], s_f[wave][4][g], s_f[wave][5][g],
+                                   s_f[wave][6][g]);
+                }
             }
-            const unsigned long long m = __ballot(keep);
+            const unsigned long long km = __ballot(keep);
             if (EMIT && keep) {
-                const int q = p + __popcll(m & lt);
+                const int q = p + __popcll(km & lt);
                 if (q < pend) {
                     tkeys[q] = (uint32_t)tile;
                     tvals[q] = id;
                 }
             }
-            p += __popcll(m);
+            p += __popcll(km);
         }
         if (!EMIT && lane == 0) chunk_cnt[chunk] = p;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -469,17 +533,19 @@ gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec, c
     k_depth_keys<<<gN, 256, 0, stream>>>(N, rec, w.dka, w.dva);
     GM_LAUNCH_CHECK();
     const int32_t* offs = nullptr;
-    if (gm_status s = radix_sort(w.dka, w.dva, w.dkb, w.dvb, 4, 0, w.n, N, w.aux, stream, &offs)) return s;
+    if (gm_status s = radix_sort(w.dka, w.dva, w.dkb, w.dvb, 32, w.n, N, w.aux, stream, &offs)) return s;
     const int32_t* order = w.dva;  // 4 passes: back in the first buffer pair
     // number of listed Gaussians = offset of top byte 0xff in the last pass, block 0;
     // it stays valid until the tile sort below reuses the histogram buffers
     const int32_t* d_nvis = offs + (size_t)(RS_RADIX - 1) * div_up(N, RS_CHUNK);
     // 2. surviving (Gaussian, tile) pairs per chunk of 64 Gaussians in depth order, scan
-    CullParams cp{tile_dmax, softness};
+    const bool lds = tile_dmax && T <= PW_LDS_MAX_TILES;
+    CullParams cp{tile_dmax, softness, lds ? 1 : 0};
+    const size_t shm = lds ? sizeof(float) * (size_t)T : 0;
     const int nchunks = (int)div_up(N, 64);
-    const unsigned gW = (unsigned)std::min<int64_t>(div_up(nchunks, PW_WAVES), 2048);
-    k_pairs<false><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, d_nvis, nchunks, order, rec, w.flag, nullptr,
-                                                    nullptr, 0, nullptr, nullptr);
+    const unsigned gW = (unsigned)std::min<int64_t>(div_up(nchunks, PW_WAVES), 512);
+    k_pairs<false><<<gW, 64 * PW_WAVES, shm, stream>>>(dc, cp, d_nvis, nchunks, order, rec, w.flag, nullptr,
+                                                      nullptr, 0, nullptr, nullptr);
     GM_LAUNCH_CHECK();
     if (gm_status s = exclusive_scan(w.flag, w.pos, nchunks, total, w.scan, stream)) return s;
     // 3. emit (tile, id) in depth order; 4. stable sort by tile; 5. tile ranges.
@@ -487,15 +553,16 @@ gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec, c
     //    writes nothing above it.
     const int64_t kcap = std::min<int64_t>(cap, INT32_MAX);
     if (kcap == 0) return GM_OK;
-    int npass = 1;
-    while (npass < 4 && (T - 1) >> (8 * npass)) ++npass;
+    int tbits = 0;
+    while (tbits < 31 && ((T - 1) >> tbits)) ++tbits;
+    const int npass = radix_passes(tbits);
     uint32_t* ka = w.tka;
     int32_t* va = (npass % 2 == 0) ? sorted_ids : w.tva;
     int32_t* vb = (npass % 2 == 0) ? w.tva : sorted_ids;
-    k_pairs<true><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, d_nvis, nchunks, order, rec, nullptr, w.pos, total,
-                                                   kcap, ka, va);
+    k_pairs<true><<<gW, 64 * PW_WAVES, shm, stream>>>(dc, cp, d_nvis, nchunks, order, rec, nullptr, w.pos, total,
+                                                     kcap, ka, va);
     GM_LAUNCH_CHECK();
-    if (gm_status s = radix_sort(ka, va, w.tkb, vb, npass, 0, total, kcap, w.aux, stream)) return s;
+    if (gm_status s = radix_sort(ka, va, w.tkb, vb, tbits, total, kcap, w.aux, stream)) return s;
     const uint32_t* kfin = (npass % 2 == 0) ? w.tka : w.tkb;
     k_tile_ranges<<<(unsigned)div_up(div_up(kcap, 4), 256), 256, 0, stream>>>(kfin, total, kcap, tile_ranges);
     GM_LAUNCH_CHECK();
