@@ -122,17 +122,25 @@ __global__ void k_bin_scatter(DevCamera cam, int F, int T, const int2* __restric
     int cx = x0, cy = y0;
     for (int k = 0; __ballot(k < nt); ++k) {
         const int tk = k < nt ? cy * cam.tx + cx : -1;
+        // group membership first, then every group's leader reserves its slots with
+        // one atomic, all groups in the same instruction
+        int leader = lane, rank = 0, cnt = 0;
         unsigned long long pend = __ballot(tk >= 0);
         while (pend) {
-            const int leader = __builtin_ctzll(pend);
-            const int tl = __builtin_amdgcn_readlane(tk, leader);
+            const int l = __builtin_ctzll(pend);
+            const int tl = __builtin_amdgcn_readlane(tk, l);
             const unsigned long long grp = __ballot(tk == tl);
-            int base = 0;
-            if (lane == leader) base = atomicAdd(&cursor[tl], __popcll(grp));
-            base = __builtin_amdgcn_readlane(base, leader);
-            if (tk == tl) tile_tris[tile_off[tl] + base + __popcll(grp & lt)] = i;
+            if (tk == tl) {
+                leader = l;
+                rank = __popcll(grp & lt);
+            }
+            if (lane == l) cnt = __popcll(grp);
             pend &= ~grp;
         }
+        int base = 0;
+        if (cnt > 0) base = atomicAdd(&cursor[tk], cnt);
+        base = __shfl(base, leader, 64);
+        if (tk >= 0) tile_tris[tile_off[tk] + base + rank] = i;
         next_tile(cx, cy, x0, x1);
     }
 }
