@@ -2,8 +2,9 @@
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  It loads ``liboracle.so`` built from
-``gm_oracle.c`` with gcc (``-O2 -fopenmp -ffp-contract=off``) and shares no code with
-the HIP library; the two meet only at the seeded inputs of ``scenes``.
+``gm_oracle.c`` and ``project_bwd.c`` with gcc (``-O2 -fopenmp -ffp-contract=off``)
+and shares no code with the HIP library; the two meet only at the seeded inputs of
+``scenes``.
 
 The functions below marshal numpy arrays into the C oracle and return plain numpy
 arrays.  ``render_view`` runs the whole definition for one view on a set of tiles
@@ -19,7 +20,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "gm_oracle.c")
+_SRCS = [os.path.join(_HERE, "gm_oracle.c"), os.path.join(_HERE, "project_bwd.c")]
 _LIB = os.path.join(_HERE, "liboracle.so")
 NREC = 13
 
@@ -29,9 +30,9 @@ GCC_FLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11
 
 def build(force: bool = False) -> str:
     """Compile the oracle with gcc (no -ffast-math, no contraction)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    if force or not os.path.exists(_LIB) or any(os.path.getmtime(_LIB) < os.path.getmtime(f) for f in _SRCS):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"])
+        subprocess.check_call(["gcc", *GCC_FLAGS, *_SRCS, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -94,6 +95,8 @@ def lib():
         _lib.oc_sh_basis.argtypes = [D, D, D, P]
         _lib.oc_num_threads.argtypes = []
         _lib.oc_num_threads.restype = I
+        _lib.oc_project_f64.argtypes = [cam, I, P, P, P, P, P, I, P]
+        _lib.oc_project_bwd.argtypes = [cam, I, P, P, P, P, I, P, P, P, P, P, P, P]
     return _lib
 
 
@@ -420,3 +423,39 @@ def render_view(scene, view_index: int = 0, tiles=None, cull: bool = True, backw
                      bg=scene.bg, softness=scene.softness, grads=g)
     res["comp"] = comp
     return res
+
+
+# ---------------------------------------------------------------------------
+# projection backward (project_bwd.c)
+# ---------------------------------------------------------------------------
+
+def _sh_planes(sh_degree: int) -> int:
+    return 1 if sh_degree < 0 else (sh_degree + 1) ** 2
+
+
+def project_f64(cam: Camera, means, quats, scales, opacity, sh, sh_degree) -> np.ndarray:
+    """fp64 records [N][13] from fp64 inputs (same formulas as project_gaussians)."""
+    means, quats, scales = _c(means, np.float64), _c(quats, np.float64), _c(scales, np.float64)
+    opacity, sh = _c(opacity, np.float64), _c(sh, np.float64)
+    N = means.shape[1]
+    out = np.zeros((N, NREC), np.float64)
+    lib().oc_project_f64(C.byref(cam), N, _p(means), _p(quats), _p(scales), _p(opacity), _p(sh),
+                         int(sh_degree), _p(out))
+    return out
+
+
+def project_bwd(cam: Camera, means, quats, scales, sh, sh_degree, listed, g_rec) -> dict:
+    """Gradients of sum(g_rec * records) with respect to the projection inputs (fp64).
+    Returns means [3][N], quats [4][N], scales [3][N], opacity [N], sh [K][3][N]."""
+    means, quats, scales = _c(means, np.float64), _c(quats, np.float64), _c(scales, np.float64)
+    sh = _c(sh, np.float64)
+    listed = _c(listed, np.int32)
+    g_rec = _c(g_rec, np.float64)
+    N = means.shape[1]
+    K = _sh_planes(sh_degree)
+    out = {"means": np.zeros((3, N)), "quats": np.zeros((4, N)), "scales": np.zeros((3, N)),
+           "opacity": np.zeros(N), "sh": np.zeros((K, 3, N))}
+    lib().oc_project_bwd(C.byref(cam), N, _p(means), _p(quats), _p(scales), _p(sh), int(sh_degree), _p(listed),
+                         _p(g_rec), _p(out["means"]), _p(out["quats"]), _p(out["scales"]), _p(out["opacity"]),
+                         _p(out["sh"]))
+    return out
