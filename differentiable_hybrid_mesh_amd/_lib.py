@@ -45,8 +45,8 @@ class GmMesh(C.Structure):
 
 EXPORTS = ["gm_bin_triangles_ws", "gm_bin_triangles", "gm_raster_zbuffer", "gm_project_gaussians",
            "gm_sort_tile_keys_ws", "gm_sort_tile_keys", "gm_composite_hybrid_fwd",
-           "gm_composite_hybrid_bwd", "gm_mipmaps_floats", "gm_build_mipmaps", "gm_last_error",
-           "gm_version"]
+           "gm_composite_hybrid_bwd", "gm_project_gaussians_bwd", "gm_mipmaps_floats", "gm_build_mipmaps",
+           "gm_last_error", "gm_version"]
 
 _lib = None
 
@@ -72,6 +72,7 @@ def lib():
     L.gm_sort_tile_keys.argtypes = [cam, I32, P, P, F32, P, P, I64, P, P, SZ, P]
     L.gm_composite_hybrid_fwd.argtypes = [cam, P, P, P, P, P, mesh, P, light, P, F32, P, P, P, P, P, P, P]
     L.gm_composite_hybrid_bwd.argtypes = [cam, I32, P, P, P, P, P, F32, P, P, P, P, P, P, P, P, P, P]
+    L.gm_project_gaussians_bwd.argtypes = [cam, I32, P, P, P, P, P, I32, P, P, P, P, P, P, P, P, P, P]
     L.gm_mipmaps_floats.argtypes = [I32]
     L.gm_mipmaps_floats.restype = SZ
     L.gm_build_mipmaps.argtypes = [P, I32, P, P]
@@ -83,7 +84,8 @@ def lib():
         if not hasattr(L, name):
             raise ImportError(f"{LIB_PATH} does not export {name}")
     for name in ("gm_bin_triangles", "gm_raster_zbuffer", "gm_project_gaussians", "gm_sort_tile_keys",
-                 "gm_composite_hybrid_fwd", "gm_composite_hybrid_bwd", "gm_build_mipmaps"):
+                 "gm_composite_hybrid_fwd", "gm_composite_hybrid_bwd", "gm_project_gaussians_bwd",
+                 "gm_build_mipmaps"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -158,6 +160,14 @@ def gm_composite_hybrid_bwd(cam, N, rec, tile_ranges, sorted_ids, face_id, depth
                                         ptr(face_id), ptr(depth), float(softness), ptr(state_T),
                                         ptr(state_last), ptr(state_cm), ptr(g_rgb), ptr(g_depth),
                                         ptr(g_alpha), ptr(g_rec), ptr(g_mesh_rgb), ptr(g_mesh_depth), stream))
+
+
+def gm_project_gaussians_bwd(cam, N, means, quats, scales, opacity, sh, sh_degree, rec, g_rec, g_means, g_quats,
+                             g_scales, g_opacity, g_sh, g_log_scales, g_logit_opacity, stream):
+    check(lib().gm_project_gaussians_bwd(C.byref(cam), int(N), ptr(means), ptr(quats), ptr(scales), ptr(opacity),
+                                         ptr(sh), int(sh_degree), ptr(rec), ptr(g_rec), ptr(g_means), ptr(g_quats),
+                                         ptr(g_scales), ptr(g_opacity), ptr(g_sh), ptr(g_log_scales),
+                                         ptr(g_logit_opacity), stream))
 
 
 def gm_mipmaps_floats(S) -> int:

@@ -8,42 +8,11 @@
 #pragma clang fp contract(off)
 
 #include "gm_internal.h"
+#include "gm_sh.h"
 
 namespace gm {
 
 constexpr float EPS2D = 0.3f;  // px^2: low-pass dilation, also the eps of the depth model
-
-// Real SH up to degree 3 (splatting sign/order convention); closed-form constants.
-__device__ inline void sh_basis_f(float x, float y, float z, float* Y)
-{
-    const float c0 = 0.28209479177387814f;   // 1/(2 sqrt(pi))
-    const float c1 = 0.48860251190291992f;   // sqrt(3/(4 pi))
-    const float c2a = 1.0925484305920792f;   // (1/2) sqrt(15/pi)
-    const float c2b = 0.31539156525252005f;  // (1/4) sqrt(5/pi)
-    const float c2c = 0.54627421529603959f;  // (1/4) sqrt(15/pi)
-    const float c3a = 0.59004358992664352f;  // (1/4) sqrt(35/(2 pi))
-    const float c3b = 2.8906114426405538f;   // (1/2) sqrt(105/pi)
-    const float c3c = 0.45704579946446572f;  // (1/4) sqrt(21/(2 pi))
-    const float c3d = 0.37317633259011546f;  // (1/4) sqrt(7/pi)
-    const float c3e = 1.4453057213202769f;   // (1/4) sqrt(105/pi)
-    const float xx = x * x, yy = y * y, zz = z * z;
-    Y[0] = c0;
-    Y[1] = -c1 * y;
-    Y[2] = c1 * z;
-    Y[3] = -c1 * x;
-    Y[4] = c2a * x * y;
-    Y[5] = -c2a * y * z;
-    Y[6] = c2b * (2.0f * zz - xx - yy);
-    Y[7] = -c2a * x * z;
-    Y[8] = c2c * (xx - yy);
-    Y[9] = -c3a * y * (3.0f * xx - yy);
-    Y[10] = c3b * x * y * z;
-    Y[11] = -c3c * y * (4.0f * zz - xx - yy);
-    Y[12] = c3d * z * (2.0f * zz - 3.0f * xx - 3.0f * yy);
-    Y[13] = -c3c * x * (4.0f * zz - xx - yy);
-    Y[14] = c3e * z * (xx - yy);
-    Y[15] = -c3a * x * (xx - 3.0f * yy);
-}
 
 __global__ void __launch_bounds__(256)
 k_project_gaussians(DevCamera cam, int N, const float* __restrict__ means,

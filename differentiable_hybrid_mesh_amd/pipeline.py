@@ -190,6 +190,29 @@ class Renderer:
                                   self.state_cm, g_rgb, g_depth, g_alpha, self.g_rec, self.g_mesh_rgb,
                                   self.g_mesh_depth, _stream())
 
+    def project_bwd(self, view: int, g_rec=None, log_params: bool = False):
+        """Gradients of the Gaussian parameters from record gradients (default: the
+        last composite backward's).  Buffers are allocated on first use."""
+        ds, s = self.ds, self.ds.scene
+        N = self.N
+        if not hasattr(self, "g_means"):
+            dev, f32 = ds.device, torch.float32
+            K = 1 if s.sh_degree < 0 else (s.sh_degree + 1) ** 2
+            self.g_means = torch.empty((3, max(N, 1)), dtype=f32, device=dev)
+            self.g_quats = torch.empty((4, max(N, 1)), dtype=f32, device=dev)
+            self.g_scales = torch.empty((3, max(N, 1)), dtype=f32, device=dev)
+            self.g_opacity = torch.empty(max(N, 1), dtype=f32, device=dev)
+            self.g_sh = torch.empty((K, 3, max(N, 1)), dtype=f32, device=dev)
+            self.g_log_scales = torch.empty((3, max(N, 1)), dtype=f32, device=dev)
+            self.g_logit = torch.empty(max(N, 1), dtype=f32, device=dev)
+        G.gm_project_gaussians_bwd(ds.cams[view], N, ds.means, ds.quats, ds.scales, ds.opacity, ds.sh, s.sh_degree,
+                                   self.rec, self.g_rec if g_rec is None else g_rec, self.g_means, self.g_quats,
+                                   self.g_scales, self.g_opacity, self.g_sh,
+                                   self.g_log_scales if log_params else None, self.g_logit if log_params else None,
+                                   _stream())
+        return {"means": self.g_means[:, :N], "quats": self.g_quats[:, :N], "scales": self.g_scales[:, :N],
+                "opacity": self.g_opacity[:N], "sh": self.g_sh[..., :N]}
+
     # -- whole passes -----------------------------------------------------------
     def forward_async(self, view: int = 0, cull: bool = True):
         """Queue one forward pass and the copy of the list lengths; no synchronisation.

@@ -241,6 +241,30 @@ gm_status gm_composite_hybrid_bwd(const gm_camera* cam, int32_t N, const float* 
                                   float* g_mesh_depth, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * 7. gm_project_gaussians_bwd — gradients of the Gaussians' own parameters.
+ * README "Hybrid rendering": the renderer is differentiable end to end, through the
+ * depth split as well, so means, rotations, scales, opacities and colour
+ * coefficients get gradients through their projected records.
+ *
+ * Reverse mode of call 3 for every Gaussian: given g_rec [N][GM_GRAD] (the record
+ * gradients of call 6: u, v, Q00, Q01, Q11, opacity, r, g, b, z_c, g0, g1, sigma),
+ * writes g_means [3][N], g_quats [4][N] (raw quaternion, before normalisation),
+ * g_scales [3][N] (linear scales), g_opacity [N] and g_sh [(d+1)^2][3][N] (or
+ * [1][3][N] for sh_degree = -1).  Optional outputs (NULL to skip): g_log_scales
+ * [3][N] = g_scales * scales and g_logit_opacity [N] = g_opacity * o (1 - o), the
+ * gradients with respect to log-scales and opacity logits (opacity is then
+ * required).  Inputs are those of call 3 plus its output rec; Gaussians that rec
+ * does not list (word 15 = 0) get zeros.  A colour channel clamped at zero in the
+ * forward passes no gradient.  Every output element is written (no accumulation).
+ * ------------------------------------------------------------------------- */
+gm_status gm_project_gaussians_bwd(const gm_camera* cam, int32_t N, const float* means,
+                                   const float* quats, const float* scales, const float* opacity,
+                                   const float* sh, int32_t sh_degree, const float* rec,
+                                   const float* g_rec, float* g_means, float* g_quats,
+                                   float* g_scales, float* g_opacity, float* g_sh,
+                                   float* g_log_scales, float* g_logit_opacity, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Auxiliary.
  * gm_build_mipmaps: README v1.1 (trilinear mipmapping by default): box-filter
  * pyramid of a square power-of-two texture tex [S][S][3] (HWC, values in [0, 1]);

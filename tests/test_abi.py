@@ -80,3 +80,12 @@ def test_argument_errors_before_any_launch(G):
     assert L.gm_build_mipmaps(16, 100, 16, None) == G.GM_ERR_ARG
     # rec misaligned
     assert L.gm_project_gaussians(C.byref(cam), 1, 16, 16, 16, 16, 16, 0, 17, None) == G.GM_ERR_ARG
+    # projection backward: degree out of range, a NULL output, logit chain without opacity
+    bw = [16] * 5
+    assert L.gm_project_gaussians_bwd(C.byref(cam), 1, 16, 16, 16, 16, 16, 5, 16, 16, *bw, None, None,
+                                      None) == G.GM_ERR_ARG
+    assert L.gm_project_gaussians_bwd(C.byref(cam), 1, 16, 16, 16, 16, 16, 0, 16, 16, 16, None, 16, 16, 16,
+                                      None, None, None) == G.GM_ERR_ARG
+    assert L.gm_project_gaussians_bwd(C.byref(cam), 1, 16, 16, 16, None, 16, 0, 16, 16, *bw, None, 16,
+                                      None) == G.GM_ERR_ARG
+    assert b"opacity" in L.gm_last_error()
