@@ -208,6 +208,8 @@ def main():
         else {"algorithmic_bytes": alg_bytes[dom]}
     roof["launch_ms"] = round(stage_ms[dom], 4)
 
+    next_stages = {"project_bwd": time_project_bwd(r, scene, view, args.steps)} if N else {}
+
     total_alg = sum(alg_bytes.values())
     out = {
         "metric": "hybrid render Mpixels/s fwd+bwd at 1080p",
@@ -221,11 +223,42 @@ def main():
         "hbm_algorithmic_GBps": round(total_alg / (ms * 1e-3) / 1e9, 1),
         "hbm_algorithmic_frac": round(total_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roof,
+        "next_stages": next_stages,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(scene, view, args.cpu_tiles)
     print(json.dumps(out), flush=True)
+
+
+def time_project_bwd(r, scene, view, steps):
+    """The projection backward (gradients of the Gaussian parameters from the record
+    gradients of the composite backward), timed on its own: it follows the composite
+    backward in a training step but is not part of the rendering step measured above.
+    HBM-bound; algorithmic bytes per listed Gaussian = inputs read (means, quaternion,
+    scales, SH coefficients, the record's colour and list words, 13 record gradients)
+    plus outputs written (3 + 4 + 3 + 1 + 3K gradients); an unlisted one reads its list
+    word and writes zeros."""
+    import torch
+    N = scene.N
+    K = 1 if scene.sh_degree < 0 else (scene.sh_degree + 1) ** 2
+    nl = int((r.rec[:N, 15].view(torch.int32) > 0).sum().item())
+    per_listed = 4 * (3 + 4 + 3 + 3 * K + 4 + 13) + 4 * (3 + 4 + 3 + 1 + 3 * K)
+    per_unlisted = 4 + 4 * (3 + 4 + 3 + 1 + 3 * K)
+    nbytes = nl * per_listed + (N - nl) * per_unlisted
+    r.project_bwd(view)  # allocates the gradient buffers
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        r.project_bwd(view)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": "k_project_bwd", "ms": round(ms, 4), "bound": "hbm", "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": nbytes, "listed": nl}
 
 
 def included_fraction(scene, view, ntiles=48):
