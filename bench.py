@@ -137,8 +137,9 @@ def main():
         mark(6)
         r.fetch_counts()  # list lengths to pinned host memory, checked after the run
 
-    # warm-up; the list capacities grow until both lists fit (no step synchronises:
-    # the lengths are read back once the stream has finished)
+    # list capacities first (binning, projection and sorting only), then the warm-up;
+    # no step synchronises: the lengths are read back once the stream has finished
+    r.fit_lists(view, True)
     for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()

@@ -224,6 +224,17 @@ class Renderer:
         self.composite_fwd(view)
         self.fetch_counts()
 
+    def fit_lists(self, view: int = 0, cull: bool = True):
+        """Run the list-producing calls (no compositing) until both lists fit."""
+        while True:
+            self.bin_and_zbuffer(view)
+            self.project(view)
+            self.sort(view, cull)
+            self.fetch_counts()
+            torch.cuda.current_stream().synchronize()
+            if self.read_counts():
+                return
+
     def forward(self, view: int = 0, cull: bool = True):
         while True:
             self.forward_async(view, cull)
