@@ -301,7 +301,7 @@ __device__ __forceinline__ float quad_min_rect(float hq00, float q01, float hq11
     return m;
 }
 
-// Stage one record and decide for which of the tile's four 16x4-pixel waves it can
+// Stage one record and decide for which of the tile's four 8x8-pixel waves it can
 // matter.  A wave bit is cleared only when every pixel of the wave would skip the
 // entry anyway (alpha_F < 1/255), so skipping it leaves every result bit-identical:
 //  * q exceeds q_skip on the whole rectangle of the wave's pixel centres, with a
@@ -327,18 +327,19 @@ __device__ __forceinline__ uint32_t stage_record(const CompParams& P, float4 ra,
     const float rho = fminf(fabsf(Q01) / sqrtf(Q00 * Q11), 0.999999f);
     const float qe = qs * (1.0f + 1e-5f * (1.0f + rho) / (1.0f - rho)) + 1e-4f;
     const float u = ra.x, v = ra.y;
-    const float xa = (float)(tx * GM_TILE) + 0.5f - u, xb = xa + 15.0f;
     const float amax = fminf(o, ALPHA_MAX);
     const float thr = (1.0f / 255.0f) * (1.0f - 1e-3f);
     // f must reach thr/amax somewhere for the entry to matter
     const float scrit = P.softness > 0.0f && amax > thr ? -1.41421356237309515f * erfcinvf(2.0f * thr / amax) - 1e-3f
                                                          : 0.0f;
     const float g0 = rc.z, g1 = rc.w, zc = rc.y;
-    const float gxm = fminf(g0 * xa, g0 * xb);
     uint32_t m = 0;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        const float ya = (float)(ty * GM_TILE + 4 * w) + 0.5f - v, yb = ya + 3.0f;
+        // wave w covers the 8x8 pixel quadrant (w & 1, w >> 1) of the tile
+        const float xa = (float)(tx * GM_TILE + 8 * (w & 1)) + 0.5f - u, xb = xa + 7.0f;
+        const float ya = (float)(ty * GM_TILE + 8 * (w >> 1)) + 0.5f - v, yb = ya + 7.0f;
+        const float gxm = fminf(g0 * xa, g0 * xb);
         const float dm = wdmax[w];
         if (dm < 0.0f) continue;  // no pixel of this wave is in the image
         if (quad_min_rect(st.a.z, Q01, st.b.x, xa, xb, ya, yb) * (1.0f - 1e-5f) > qe) continue;
@@ -391,7 +392,7 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, float* __restr
     const int tile = blockIdx.x;
     const int tx = tile % P.cam.tx, ty = tile / P.cam.tx;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int px = tx * GM_TILE + (threadIdx.x & 15), py = ty * GM_TILE + (threadIdx.x >> 4);
+    const int px = tx * GM_TILE + 8 * (wave & 1) + (lane & 7), py = ty * GM_TILE + 8 * (wave >> 1) + (lane >> 3);
     const bool inside = px < P.cam.width && py < P.cam.height;
     const int pix = py * P.cam.width + px;
     const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
@@ -516,7 +517,7 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
     const int tile = blockIdx.x;
     const int tx = tile % P.cam.tx, ty = tile / P.cam.tx;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int px = tx * GM_TILE + (threadIdx.x & 15), py = ty * GM_TILE + (threadIdx.x >> 4);
+    const int px = tx * GM_TILE + 8 * (wave & 1) + (lane & 7), py = ty * GM_TILE + 8 * (wave >> 1) + (lane >> 3);
     const bool inside = px < P.cam.width && py < P.cam.height;
     const int pix = py * P.cam.width + px;
     const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
@@ -679,10 +680,20 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
             gv[10] = -kap * S[11];
             gv[11] = -kap * S[12];
             gv[12] = -S[13] * g.d.w;
-            float* dst = g_rec + (size_t)s_id[threadIdx.x] * GM_GRAD;
+            float* dst = s_acc[threadIdx.x];
 #pragma unroll
-            for (int c = 0; c < GM_GRAD; ++c)
-                if (gv[c] != 0.0f) unsafeAtomicAdd(dst + c, gv[c]);
+            for (int c = 0; c < GM_GRAD; ++c) dst[c] = gv[c];
+        }
+        __syncthreads();
+        // flush with 16 lanes per entry (one lane per field): each atomic instruction
+        // then touches the 52-byte gradient records of only four Gaussians instead of
+        // 64, so the memory-side atomics arrive grouped by cache line
+        for (int e0 = 0; e0 < nb; e0 += CT / 16) {
+            const int e = e0 + (int)(threadIdx.x >> 4), c = threadIdx.x & 15;
+            if (e < nb && c < GM_GRAD) {
+                const float v = s_acc[e][c];
+                if (v != 0.0f) unsafeAtomicAdd(g_rec + (size_t)s_id[e] * GM_GRAD + c, v);
+            }
         }
     }
     if (!inside) return;
