@@ -2,7 +2,8 @@
 // rendering"), with the mesh surface resolve of "Mesh rasterizer" step 2 and the
 // v1.1 texture and lighting notes as its prologue.
 //
-// One 256-thread block per 16x16 tile, one thread per pixel.  Records of the tile's
+// One 256-thread block per 16x16 tile, one thread per pixel, each wave an 8x8
+// quadrant (the most compact 64-pixel footprint).  Records of the tile's
 // list are staged in LDS in batches of 256 (64 bytes each, read by all lanes at the
 // same address: an LDS broadcast).  The forward walks front to back with a
 // tile-level early exit; the backward walks back to front from the last entry any
@@ -247,37 +248,45 @@ __device__ __forceinline__ float normal_cdf_pdf(float s, float& pdf)
     return s <= 0.0f ? half_tail : 1.0f - half_tail;
 }
 
-// alpha = min(0.99, o exp(-q)); returns alpha_F = alpha f (0 when below the skip
-// threshold before f is formed) and the intermediates the backward needs.  A pair
-// with q above q_skip is below the threshold with margin and exp() is not formed.
-__device__ __forceinline__ float eval_pair(const Staged& g, float pxc, float pyc, bool on, float D,
-                                           float softness, float& dx, float& dy, float& G, float& alpha,
-                                           float& f, float& s, float& pdf)
+// One (pixel, entry) pair, straight-line (an entry that passed its wave's mask is
+// live for most lanes, so branching would only serialise both paths):
+// alpha = min(0.99, o exp(-q)), split f = Phi((D - z*) / (sigma softness)) on the
+// mesh (1 off it), alpha_F = alpha f.  The pair is included when q <= q_skip (a
+// pair above it is below the 1/255 threshold with margin), alpha >= 1/255 and
+// alpha_F >= 1/255.  Both walks call this one function, so the forward and the
+// backward take the same decisions bit for bit.
+struct Pair {
+    float dx, dy, q, oG, al, f, pdf, s, aF;
+    bool ok;  // passes the skip rules
+};
+
+__device__ __forceinline__ Pair eval_pair(const Staged& g, float pxc, float pyc, bool on, bool wave_on, float D,
+                                          float softness)
 {
-    dx = pxc - g.a.x;
-    dy = pyc - g.a.y;
-    const float q = quad_form(g.a.z, g.a.w, g.b.x, dx, dy);
-    f = 1.0f;
-    s = 0.0f;
-    pdf = 0.0f;
-    if (q > g.d.z) {
-        G = 0.0f;
-        alpha = 0.0f;
-        return 0.0f;
-    }
-    G = __expf(-q);
-    alpha = fminf(g.b.y * G, ALPHA_MAX);
-    if (alpha < SKIP_ALPHA) return 0.0f;
-    if (on) {
-        const float num = (D - g.c.y) - __builtin_fmaf(g.c.z, dx, g.c.w * dy);
+    Pair p;
+    p.dx = pxc - g.a.x;
+    p.dy = pyc - g.a.y;
+    p.q = quad_form(g.a.z, g.a.w, g.b.x, p.dx, p.dy);
+    p.oG = g.b.y * __expf(-p.q);
+    p.al = fminf(p.oG, ALPHA_MAX);
+    p.f = 1.0f;
+    p.pdf = 0.0f;
+    p.s = 0.0f;
+    if (wave_on) {  // uniform: some pixel of the wave is on the mesh
+        const float num = (D - g.c.y) - __builtin_fmaf(g.c.z, p.dx, g.c.w * p.dy);
         if (softness > 0.0f) {
-            s = num * g.d.y;
-            f = normal_cdf_pdf(s, pdf);
+            p.s = on ? num * g.d.y : 0.0f;  // off the mesh D = +inf: keep s finite
+            float pd;
+            const float fo = normal_cdf_pdf(p.s, pd);
+            p.f = on ? fo : 1.0f;
+            p.pdf = on ? pd : 0.0f;
         } else {
-            f = num > 0.0f ? 1.0f : 0.0f;
+            p.f = (on && !(num > 0.0f)) ? 0.0f : 1.0f;
         }
     }
-    return alpha * f;
+    p.aF = p.al * p.f;
+    p.ok = !(p.q > g.d.z) & (p.al >= SKIP_ALPHA) & (p.aF >= SKIP_ALPHA);
+    return p;
 }
 
 // Minimum of q over the rectangle [xa, xb] x [ya, yb] of offsets (dx, dy): zero
@@ -402,6 +411,7 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, float* __restr
     const bool on = fid >= 0;
     const float D = on ? P.depth[pix] : INFINITY;
     wave_dmax(inside, on, D, s_wd);
+    const bool wave_on = __ballot(on) != 0;
 
     float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f, Z = 0.0f;
     int last = 0;
@@ -420,25 +430,21 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, float* __restr
             while (m) {
                 const int k = i * 64 + __builtin_ctzll(m);
                 m &= m - 1;
-                if (!done) {
-                    const Staged g = s_g[k];  // one 64-byte LDS broadcast read
-                    float dx, dy, G, al, f, s, pdf;
-                    const float aF = eval_pair(g, pxc, pyc, on, D, P.softness, dx, dy, G, al, f, s, pdf);
-                    if (aF >= SKIP_ALPHA) {
-                        const float Tn = T * (1.0f - aF);
-                        if (Tn < STOP_T) {
-                            done = true;
-                        } else {
-                            const float w = aF * T;
-                            C0 = __builtin_fmaf(w, g.b.z, C0);
-                            C1 = __builtin_fmaf(w, g.b.w, C1);
-                            C2 = __builtin_fmaf(w, g.c.x, C2);
-                            Z = __builtin_fmaf(w, g.c.y, Z);
-                            T = Tn;
-                            last = b0 + k - start + 1;
-                        }
-                    }
-                }
+                const Staged g = s_g[k];  // one 64-byte LDS broadcast read
+                const Pair pr = eval_pair(g, pxc, pyc, on, wave_on, D, P.softness);
+                const float aF = pr.aF;
+                const bool live = !done & pr.ok;
+                const float Tn = T * (1.0f - aF);
+                const bool stop = live & (Tn < STOP_T);
+                const bool inc = live & !stop;
+                const float w = inc ? aF * T : 0.0f;
+                C0 = __builtin_fmaf(w, g.b.z, C0);
+                C1 = __builtin_fmaf(w, g.b.w, C1);
+                C2 = __builtin_fmaf(w, g.c.x, C2);
+                Z = __builtin_fmaf(w, g.c.y, Z);
+                T = inc ? Tn : T;
+                last = inc ? b0 + k - start + 1 : last;
+                done = done | stop;
                 if (__ballot(!done) == 0) {
                     wdone = true;
                     break;
@@ -594,30 +600,11 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
                 const int k = i * 64 + kk;
                 const Staged g = s_g[k];  // one 64-byte LDS broadcast read
                 const int rel = b0 + k - start;
-                // Straight-line evaluation (nearly every walked entry is active for some
-                // lane of the wave): inactive lanes carry zeros through the same
-                // arithmetic.  The expressions and their order are those of eval_pair,
-                // so the skip decisions are the forward's bit for bit.
-                const float dx = pxc - g.a.x, dy = pyc - g.a.y;
-                const float q = quad_form(g.a.z, g.a.w, g.b.x, dx, dy);
-                const float G = __expf(-q);
-                const float oG = g.b.y * G;
-                const float al = fminf(oG, ALPHA_MAX);
-                float f = 1.0f, pdf = 0.0f, sv = 0.0f;
-                if (wave_on) {
-                    const float num = (D - g.c.y) - __builtin_fmaf(g.c.z, dx, g.c.w * dy);
-                    if (P.softness > 0.0f) {
-                        sv = on ? num * g.d.y : 0.0f;  // off the mesh D = +inf: keep s finite
-                        float pd;
-                        const float fo = normal_cdf_pdf(sv, pd);
-                        f = on ? fo : 1.0f;
-                        pdf = on ? pd : 0.0f;
-                    } else {
-                        f = (on && !(num > 0.0f)) ? 0.0f : 1.0f;
-                    }
-                }
-                const float aF = al * f;
-                const bool act = (rel < last) & !(q > g.d.z) & (al >= SKIP_ALPHA) & (aF >= SKIP_ALPHA);
+                // inactive lanes carry zeros through the same arithmetic
+                const Pair pr = eval_pair(g, pxc, pyc, on, wave_on, D, P.softness);
+                const float dx = pr.dx, dy = pr.dy, oG = pr.oG, al = pr.al, f = pr.f, pdf = pr.pdf, sv = pr.s;
+                const float aF = pr.aF;
+                const bool act = (rel < last) & pr.ok;
                 // per-pixel basis sums; the 13 record gradients are linear in them
                 // (formed once per entry at the flush):
                 //  0-2 w GC, 3 w GZ, 4 H, 5 H dx, 6 H dy, 7 H dx^2, 8 H dx dy, 9 H dy^2,
