@@ -302,53 +302,123 @@ __device__ inline bool culled(const DevCamera& cam, float softness, float dmax, 
     return !(zmin < lim) || scrit == INFINITY;
 }
 
-// Pairs of the visible Gaussians in depth order.  A wave takes a chunk of 64
-// consecutive Gaussians (one per lane), prefix-sums the tile counts of their rects
-// and treats the chunk's (Gaussian, tile) pairs as one flat sequence, 64 per step.
-// Lane l of a step owns flat index f = f0 + l; its Gaussian is the last one whose
-// range starts at or before f: the one carried over from the previous step, unless
-// one of the few Gaussians starting inside the step (a ballot) starts at or before
-// f (a binary search over the starts in LDS when many start there).  The tile is
-// f - start of the rect (row-major, the row from a reciprocal multiply), the cull
-// reads tile_dmax from LDS, and a ballot ranks the surviving pairs.  The counting
-// pass produces one total per chunk; the emitting pass writes each chunk's pairs as
-// one contiguous run in (depth, id, tile) order.
-constexpr int PW_WAVES = 8;  // waves per 512-thread block
+// Pairs of the visible Gaussians in depth order: a counting pass, a scan of the
+// per-chunk counts, an emitting pass.
+//
+// A wave takes a chunk of 64 consecutive Gaussians (one per lane), prefix-sums the
+// tile counts of their rects and treats the chunk's (Gaussian, tile) pairs as one
+// flat sequence, 64 per step.  Lane l of a step owns flat index f = f0 + l; its
+// Gaussian is the last one whose range starts at or before f: the one carried over
+// from the previous step, unless one of the few Gaussians starting inside the step
+// (a ballot) starts at or before f (a binary search over the starts in LDS when
+// many start there).  The tile is f - start of the rect (row-major, the row from a
+// reciprocal multiply) and the cull reads tile_dmax from LDS.
+//
+// The counting pass takes every cull decision, stores each step's ballot of
+// surviving pairs (the first PW_WORDS steps of a chunk) and the chunk's count.  The
+// emitting pass skips steps whose ballot is empty, reuses the stored decisions for
+// the others (recomputing them only past PW_WORDS steps) and writes each chunk's
+// pairs as one contiguous run in (depth, id, tile) order.
+constexpr int PW_WAVES = 8;              // waves per 512-thread block
 constexpr int PW_LDS_MAX_TILES = 10240;  // tile_dmax staged in LDS up to this many tiles
+constexpr int PW_WORDS = 64;             // stored step ballots per chunk (4096 pairs)
+
+struct ChunkCtx {
+    int wave, lane, total, start, nt;
+    unsigned long long lt;
+};
+
+// Owner Gaussian (lane index in the chunk) of flat index f = f0 + lane, given the
+// owner of f0 - 1 (carry); returns the owner of f0 + 63 in carry.
+__device__ __forceinline__ int step_owner(const int (*s_start)[64], const ChunkCtx& c, int f0, int& carry)
+{
+    const int f = f0 + c.lane;
+    unsigned long long m = __ballot(c.nt > 0 && c.start >= f0 && c.start < f0 + 64);
+    int g = carry;
+    if (__popcll(m) <= 6) {
+        while (m) {
+            const int h = __builtin_ctzll(m);
+            m &= m - 1;
+            if (f >= __builtin_amdgcn_readlane(c.start, h)) g = h;
+        }
+    } else {
+        int lo = 0, hi = 63;
+        while (lo < hi) {  // last g with start[g] <= f
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_start[c.wave][mid] <= f) lo = mid;
+            else hi = mid - 1;
+        }
+        g = lo;
+    }
+    carry = __builtin_amdgcn_readlane(g, 63);
+    return g;
+}
+
+// Owner of f0 + 63 when the step itself is skipped: the last Gaussian starting in
+// the step, else the carried one.
+__device__ __forceinline__ void skip_owner(const ChunkCtx& c, int f0, int& carry)
+{
+    const unsigned long long m = __ballot(c.nt > 0 && c.start >= f0 && c.start < f0 + 64);
+    if (m) carry = 63 - __builtin_clzll(m);
+}
 
 template <bool EMIT>
 __global__ void __launch_bounds__(64 * PW_WAVES)
 k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nchunks,
         const int32_t* __restrict__ order, const float* __restrict__ rec, int32_t* __restrict__ chunk_cnt,
-        const int32_t* __restrict__ chunk_off, const long long* __restrict__ d_total, long long cap,
-        uint32_t* __restrict__ tkeys, int32_t* __restrict__ tvals)
+        const int32_t* __restrict__ chunk_off, unsigned long long* __restrict__ bits,
+        const long long* __restrict__ d_total, long long cap, uint32_t* __restrict__ tkeys,
+        int32_t* __restrict__ tvals)
 {
     extern __shared__ float s_dmax[];       // tile_dmax when cp.lds
     __shared__ float s_f[PW_WAVES][7][64];  // u, v, z_c, g0, g1, sigma softness, s_crit
-    __shared__ int s_i[PW_WAVES][4][64];    // rect lo, rect hi, id, first flat index
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const unsigned long long lt = (1ull << lane) - 1ull;
+    __shared__ int s_i[PW_WAVES][3][64];    // rect lo, rect hi, id
+    __shared__ int s_start[PW_WAVES][64];   // first flat index of each Gaussian of the chunk
+    ChunkCtx c;
+    c.lane = threadIdx.x & 63;
+    c.wave = threadIdx.x >> 6;
+    c.lt = (1ull << c.lane) - 1ull;
+    const int lane = c.lane, wave = c.wave;
     const int nvis = *d_nvis;
     if (EMIT && *d_total > cap) return;  // over capacity: nothing is written (uniform)
     const int T = cam.tx * cam.ty;
-    if (cp.tile_dmax && cp.lds) {
+    if (cp.tile_dmax && cp.lds && !EMIT) {
         for (int i = threadIdx.x; i < T; i += blockDim.x) s_dmax[i] = cp.tile_dmax[i];
         __syncthreads();
     }
+    // tile and id of the pair at flat index f0 + lane (owner g), and its keep
+    // decision when `decide` (otherwise it is already known)
+    auto keep_of = [&](int f0, int g, int& tile, int& id, bool decide) -> bool {
+        const int f = f0 + lane;
+        if (f >= c.total) return false;
+        const int t = f - s_start[wave][g];
+        const int rlo = s_i[wave][0][g], rhi = s_i[wave][1][g];
+        const int x0 = rlo & 0xffff, y0 = rlo >> 16, w = (rhi & 0xffff) - x0;
+        // row = floor(t / w): the quotient's fraction is at least 1/(2w) away from an
+        // integer and t < 2^20, so one reciprocal multiply is exact enough
+        const int q = (int)(((float)t + 0.5f) * __builtin_amdgcn_rcpf((float)w));
+        const int ty = y0 + q, tx = x0 + (t - q * w);
+        tile = ty * cam.tx + tx;
+        id = s_i[wave][2][g];
+        if (!decide || !cp.tile_dmax) return true;
+        const float dmax = (cp.lds && !EMIT) ? s_dmax[tile] : cp.tile_dmax[tile];
+        return !culled(cam, cp.softness, dmax, tx, ty, s_f[wave][0][g], s_f[wave][1][g], s_f[wave][2][g],
+                       s_f[wave][3][g], s_f[wave][4][g], s_f[wave][5][g], s_f[wave][6][g]);
+    };
     for (int chunk = blockIdx.x * PW_WAVES + wave; chunk < nchunks; chunk += gridDim.x * PW_WAVES) {
         const int jl = chunk * 64 + lane;
         int nt = 0;
         if (jl < nvis) {
             const int id = order[jl];
             const float4* r = reinterpret_cast<const float4*>(rec + (size_t)id * GM_REC);
-            const float4 a = r[0], b = r[1], c = r[2], d = r[3];
+            const float4 a = r[0], b = r[1], cc = r[2], d = r[3];
             const int lo = __float_as_int(d.y), hi = __float_as_int(d.z);
             nt = ((hi & 0xffff) - (lo & 0xffff)) * ((hi >> 16) - (lo >> 16));
             s_f[wave][0][lane] = a.x;
             s_f[wave][1][lane] = a.y;
-            s_f[wave][2][lane] = c.y;
-            s_f[wave][3][lane] = c.z;
-            s_f[wave][4][lane] = c.w;
+            s_f[wave][2][lane] = cc.y;
+            s_f[wave][3][lane] = cc.z;
+            s_f[wave][4][lane] = cc.w;
             s_f[wave][5][lane] = d.x * cp.softness;
             s_f[wave][6][lane] = cull_scrit(b.y);
             s_i[wave][0][lane] = lo;
@@ -361,66 +431,55 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
             const int y = __shfl_up(P, k, 64);
             if (lane >= k) P += y;
         }
-        const int start = P - nt;  // first flat index of this lane's Gaussian
-        s_i[wave][3][lane] = start;
-        const int total = __builtin_amdgcn_readlane(P, 63);
+        c.nt = nt;
+        c.start = P - nt;
+        s_start[wave][lane] = c.start;
+        c.total = __builtin_amdgcn_readlane(P, 63);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        int p = EMIT ? chunk_off[chunk] : 0;
-        const int pend = EMIT ? chunk_off[chunk + 1] : 0;  // the counting pass took the same decisions
-        int carry = 0;  // Gaussian of flat index f0 - 1
-        for (int f0 = 0; f0 < total; f0 += 64) {
-            const int f = f0 + lane;
-            unsigned long long m = __ballot(nt > 0 && start >= f0 && start < f0 + 64);
-            int g = carry;
-            if (__popcll(m) <= 6) {
-                while (m) {
-                    const int h = __builtin_ctzll(m);
-                    m &= m - 1;
-                    if (f >= __builtin_amdgcn_readlane(start, h)) g = h;
-                }
-            } else {
-                int lo = 0, hi = 63;
-                while (lo < hi) {  // last g with start[g] <= f
-                    const int mid = (lo + hi + 1) >> 1;
-                    if (s_i[wave][3][mid] <= f) lo = mid;
-                    else hi = mid - 1;
-                }
-                g = lo;
+        unsigned long long* cbits = bits + (size_t)chunk * PW_WORDS;
+        int carry = 0;
+        if (!EMIT) {
+            int cnt = 0;
+            for (int f0 = 0, st = 0; f0 < c.total; f0 += 64, ++st) {
+                const int g = step_owner(s_start, c, f0, carry);
+                int tile, id;
+                const unsigned long long km = __ballot(keep_of(f0, g, tile, id, true));
+                if (st < PW_WORDS && lane == 0) cbits[st] = km;
+                cnt += __popcll(km);
             }
-            carry = __builtin_amdgcn_readlane(g, 63);
-            bool keep = false;
-            int tile = 0, id = 0;
-            if (f < total) {
-                const int t = f - s_i[wave][3][g];
-                const int rlo = s_i[wave][0][g], rhi = s_i[wave][1][g];
-                const int x0 = rlo & 0xffff, y0 = rlo >> 16, w = (rhi & 0xffff) - x0;
-                // row = floor(t / w): the quotient's fraction is at least 1/(2w) away from
-                // an integer and t < 2^20, so one reciprocal multiply is exact enough
-                const int q = (int)(((float)t + 0.5f) * __builtin_amdgcn_rcpf((float)w));
-                const int ty = y0 + q, tx = x0 + (t - q * w);
-                tile = ty * cam.tx + tx;
-                id = s_i[wave][2][g];
-                keep = true;
-                if (cp.tile_dmax) {
-                    const float dmax = cp.lds ? s_dmax[tile] : cp.tile_dmax[tile];
-                    keep = !culled(cam, cp.softness, dmax, tx, ty, s_f[wave][0][g], s_f[wave][1][g],
-                                   s_f[wave][2][g], s_f[wave][3][g], s_f[wave][4][g], s_f[wave][5][g],
-                                   s_f[wave][6][g]);
+            if (lane == 0) chunk_cnt[chunk] = cnt;
+        } else {
+            int p = chunk_off[chunk];
+            // the counting pass's decisions, one step per lane, read once per chunk
+            const int nsteps = (c.total + 63) >> 6;
+            const unsigned long long myword = lane < min(nsteps, PW_WORDS) ? cbits[lane] : 0ull;
+            for (int f0 = 0, st = 0; f0 < c.total; f0 += 64, ++st) {
+                unsigned long long km;
+                int g, tile = 0, id = 0;
+                if (st < PW_WORDS) {
+                    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)myword, st);
+                    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(myword >> 32), st);
+                    km = (unsigned long long)lo | ((unsigned long long)hi << 32);
+                    if (km == 0ull) {
+                        skip_owner(c, f0, carry);
+                        continue;
+                    }
+                    g = step_owner(s_start, c, f0, carry);
+                    if ((km >> lane) & 1ull) keep_of(f0, g, tile, id, false);
+                } else {
+                    g = step_owner(s_start, c, f0, carry);
+                    km = __ballot(keep_of(f0, g, tile, id, true));
                 }
-            }
-            const unsigned long long km = __ballot(keep);
-            if (EMIT && keep) {
-                const int q = p + __popcll(km & lt);
-                if (q < pend) {
+                if ((km >> lane) & 1ull) {
+                    const int q = p + __popcll(km & c.lt);
                     tkeys[q] = (uint32_t)tile;
                     tvals[q] = id;
                 }
+                p += __popcll(km);
             }
-            p += __popcll(km);
         }
-        if (!EMIT && lane == 0) chunk_cnt[chunk] = p;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
     }
@@ -457,7 +516,8 @@ __global__ void k_tile_ranges(const uint32_t* __restrict__ keys, const long long
 }
 
 struct SortWs {
-    int32_t *flag, *pos;
+    int32_t *cnt, *off;            // per-chunk pair counts and their exclusive prefix
+    unsigned long long* bits;      // per-chunk step ballots of the counting pass
     uint32_t *dka, *dkb;
     int32_t *dva, *dvb;
     uint32_t *tka, *tkb;
@@ -477,8 +537,10 @@ static size_t sort_layout(int64_t N, int64_t cap, int64_t T, char* base, SortWs*
         return p;
     };
     SortWs s;
-    s.flag = (int32_t*)take(4 * n1);
-    s.pos = (int32_t*)take(4 * (n1 + 1));
+    const int64_t nch = div_up(n1, 64);
+    s.cnt = (int32_t*)take(4 * nch);
+    s.off = (int32_t*)take(4 * (nch + 1));
+    s.bits = (unsigned long long*)take(8 * (size_t)nch * PW_WORDS);
     s.dka = (uint32_t*)take(4 * n1);
     s.dkb = (uint32_t*)take(4 * n1);
     s.dva = (int32_t*)take(4 * n1);
@@ -488,7 +550,7 @@ static size_t sort_layout(int64_t N, int64_t cap, int64_t T, char* base, SortWs*
     s.tva = (int32_t*)take(4 * c1);
     s.n = (long long*)take(8);
     const int64_t m = std::max<int64_t>(std::max<int64_t>(n1, c1), T);
-    s.scan = take(scan_ws_bytes(div_up(n1, 64)));
+    s.scan = take(scan_ws_bytes(nch));
     s.aux = take(radix_ws_bytes(m));
     if (w) *w = s;
     return o;
@@ -544,10 +606,10 @@ gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec, c
     const size_t shm = lds ? sizeof(float) * (size_t)T : 0;
     const int nchunks = (int)div_up(N, 64);
     const unsigned gW = (unsigned)std::min<int64_t>(div_up(nchunks, PW_WAVES), 512);
-    k_pairs<false><<<gW, 64 * PW_WAVES, shm, stream>>>(dc, cp, d_nvis, nchunks, order, rec, w.flag, nullptr,
+    k_pairs<false><<<gW, 64 * PW_WAVES, shm, stream>>>(dc, cp, d_nvis, nchunks, order, rec, w.cnt, nullptr, w.bits,
                                                       nullptr, 0, nullptr, nullptr);
     GM_LAUNCH_CHECK();
-    if (gm_status s = exclusive_scan(w.flag, w.pos, nchunks, total, w.scan, stream)) return s;
+    if (gm_status s = exclusive_scan(w.cnt, w.off, nchunks, total, w.scan, stream)) return s;
     // 3. emit (tile, id) in depth order; 4. stable sort by tile; 5. tile ranges.
     //    Every kernel from here on compares the total with cap on the device and
     //    writes nothing above it.
@@ -559,8 +621,8 @@ gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec, c
     uint32_t* ka = w.tka;
     int32_t* va = (npass % 2 == 0) ? sorted_ids : w.tva;
     int32_t* vb = (npass % 2 == 0) ? w.tva : sorted_ids;
-    k_pairs<true><<<gW, 64 * PW_WAVES, shm, stream>>>(dc, cp, d_nvis, nchunks, order, rec, nullptr, w.pos, total,
-                                                     kcap, ka, va);
+    k_pairs<true><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, d_nvis, nchunks, order, rec, nullptr, w.off, w.bits,
+                                                   total, kcap, ka, va);
     GM_LAUNCH_CHECK();
     if (gm_status s = radix_sort(ka, va, w.tkb, vb, tbits, total, kcap, w.aux, stream)) return s;
     const uint32_t* kfin = (npass % 2 == 0) ? w.tka : w.tkb;

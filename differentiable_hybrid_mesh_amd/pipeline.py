@@ -165,6 +165,8 @@ class Renderer:
         """After the stream has passed fetch_counts(): store the lengths, grow any list
         that overflowed; True when both fitted."""
         n_pairs, n_keys = (int(x) for x in self.counts_host.tolist())
+        if n_pairs < 0 or n_keys < 0:
+            raise RuntimeError("list construction reported a failure (negative length)")
         self.n_pairs, self.n_keys = n_pairs, n_keys
         ok = True
         if n_pairs > self.pair_cap:

@@ -28,10 +28,11 @@
  *
  * Variable-length lists.  The two calls that produce one (gm_bin_triangles,
  * gm_sort_tile_keys) write its length to a device int64 (`n_pairs`, `n_keys`) and
- * take the list's capacity `cap`.  When the length exceeds cap the list is not
- * written and the call's other outputs describe an empty list (every tile range
- * empty), so later calls stay in bounds; the caller reads the length once the
- * stream has reached it, and on overflow enlarges the list and calls again.
+ * take the list's capacity `cap`.  Nothing is written beyond cap, and when the
+ * length exceeds cap the call's other outputs describe an empty list (empty bins,
+ * every tile range empty), so later calls stay in bounds; the caller reads the
+ * length once the stream has reached it, and on overflow enlarges the list and
+ * calls again.
  *
  * Errors.  Every call returns a gm_status.  GM_ERR_ARG: a required pointer is
  * NULL, a size is negative or out of range, the workspace is too small; checked on
@@ -178,9 +179,10 @@ gm_status gm_project_gaussians(const gm_camera* cam, int32_t N, const float* mea
  * dropped when zmin_ti >= Dmax_t + 1e-5 |Dmax_t|).  Such a pair falls under the
  * 1/255 skip rule at every pixel of the tile, so outputs are unchanged.
  * Outputs: tile_ranges [T][2] = [start, end) into sorted_ids [n_keys].
- * cap: capacity of sorted_ids; n_keys (device int64, out): number of listed pairs;
- * above cap, sorted_ids is not written and every tile range is [0, 0).  ws: at
- * least gm_sort_tile_keys_ws(N, cap, W, H) bytes.
+ * cap: capacity of sorted_ids; n_keys (device int64, out): number of listed pairs
+ * (negative if list construction failed, which does not happen in correct use);
+ * above cap, every tile range is [0, 0) and the contents of sorted_ids are
+ * unspecified.  ws: at least gm_sort_tile_keys_ws(N, cap, W, H) bytes.
  * ------------------------------------------------------------------------- */
 size_t gm_sort_tile_keys_ws(int32_t N, int64_t cap, int32_t width, int32_t height);
 gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec,
