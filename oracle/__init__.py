@@ -2,9 +2,9 @@
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  It loads ``liboracle.so`` built from
-``gm_oracle.c`` and ``project_bwd.c`` with gcc (``-O2 -fopenmp -ffp-contract=off``)
-and shares no code with the HIP library; the two meet only at the seeded inputs of
-``scenes``.
+``gm_oracle.c``, ``project_bwd.c`` and ``mesh_bwd.c`` with gcc (``-O2 -fopenmp
+-ffp-contract=off``) and shares no code with the HIP library; the two meet only at
+the seeded inputs of ``scenes``.
 
 The functions below marshal numpy arrays into the C oracle and return plain numpy
 arrays.  ``render_view`` runs the whole definition for one view on a set of tiles
@@ -20,7 +20,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRCS = [os.path.join(_HERE, "gm_oracle.c"), os.path.join(_HERE, "project_bwd.c")]
+_SRCS = [os.path.join(_HERE, "gm_oracle.c"), os.path.join(_HERE, "project_bwd.c"),
+         os.path.join(_HERE, "mesh_bwd.c")]
 _LIB = os.path.join(_HERE, "liboracle.so")
 NREC = 13
 
@@ -73,6 +74,14 @@ class Comp(C.Structure):
 _lib = None
 
 
+class MeshB(C.Structure):
+    """mb_mesh of mesh_bwd.c: fp64 mesh attributes for the mesh-side backward."""
+    _fields_ = [("V", C.c_int), ("F", C.c_int), ("Vt", C.c_int), ("S", C.c_int),
+                ("verts", C.c_void_p), ("faces", C.c_void_p), ("vcolor", C.c_void_p),
+                ("vnormal", C.c_void_p), ("uv", C.c_void_p), ("faces_uv", C.c_void_p),
+                ("tex", C.c_void_p), ("light", C.c_void_p)]
+
+
 def lib():
     global _lib
     if _lib is None:
@@ -97,6 +106,8 @@ def lib():
         _lib.oc_num_threads.restype = I
         _lib.oc_project_f64.argtypes = [cam, I, P, P, P, P, P, I, P]
         _lib.oc_project_bwd.argtypes = [cam, I, P, P, P, P, I, P, P, P, P, P, P, P]
+        _lib.oc_mesh_fwd64.argtypes = [cam, C.POINTER(MeshB), I, P, P, P, P]
+        _lib.oc_mesh_bwd.argtypes = [cam, C.POINTER(MeshB), I, P, P, P, P, P, P, P, P, P, P]
     return _lib
 
 
@@ -458,4 +469,65 @@ def project_bwd(cam: Camera, means, quats, scales, sh, sh_degree, listed, g_rec)
     lib().oc_project_bwd(C.byref(cam), N, _p(means), _p(quats), _p(scales), _p(sh), int(sh_degree), _p(listed),
                          _p(g_rec), _p(out["means"]), _p(out["quats"]), _p(out["scales"]), _p(out["opacity"]),
                          _p(out["sh"]))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# mesh-side backward (mesh_bwd.c)
+# ---------------------------------------------------------------------------
+
+def light_vector(light) -> Optional[np.ndarray]:
+    """pos, ambient, diffuse, specular, shininess as 13 fp64 values (None: unlit)."""
+    if light is None:
+        return None
+    return np.concatenate([np.asarray(light[k], np.float64).reshape(-1)
+                           for k in ("pos", "ambient", "diffuse", "specular", "shininess")])
+
+
+class MeshB64:
+    """fp64 copies of a mesh's arrays (overridable for finite differences)."""
+
+    def __init__(self, scene, verts=None, vcolor=None, vnormal=None, uv=None, tex=None, light=None):
+        def f64(a):
+            return None if a is None else np.ascontiguousarray(a, np.float64)
+        self.verts = f64(scene.verts if verts is None else verts)
+        self.faces = np.ascontiguousarray(scene.faces, np.int32)
+        self.vcolor = f64(scene.vcolor if vcolor is None else vcolor)
+        self.vnormal = f64(scene.vnormal if vnormal is None else vnormal)
+        self.uv = f64(scene.uv if uv is None else uv)
+        self.faces_uv = None if scene.faces_uv is None else np.ascontiguousarray(scene.faces_uv, np.int32)
+        self.tex = f64(scene.texture if tex is None else tex)
+        self.light = light_vector(scene.light) if light is None else f64(light)
+        if self.vnormal is None:
+            self.light = None
+        m = MeshB()
+        m.V, m.F = self.verts.shape[1], self.faces.shape[1]
+        m.Vt = 0 if self.uv is None else self.uv.shape[1]
+        m.S = 0 if self.tex is None else self.tex.shape[0]
+        m.verts, m.faces = _p(self.verts), _p(self.faces)
+        m.vcolor, m.vnormal, m.uv = _p(self.vcolor), _p(self.vnormal), _p(self.uv)
+        m.faces_uv, m.tex, m.light = _p(self.faces_uv), _p(self.tex), _p(self.light)
+        self.struct = m
+
+
+def mesh_fwd64(cam: Camera, mesh: MeshB64, pix, face):
+    """c_m [n][3] and D [n] at the given pixels, each covered by the given face."""
+    pix, face = _c(pix, np.int32), _c(face, np.int32)
+    n = len(pix)
+    cm, D = np.zeros((n, 3)), np.zeros(n)
+    lib().oc_mesh_fwd64(C.byref(cam), C.byref(mesh.struct), n, _p(pix), _p(face), _p(cm), _p(D))
+    return cm, D
+
+
+def mesh_bwd(cam: Camera, mesh: MeshB64, pix, face, g_cm=None, g_D=None) -> dict:
+    """Gradients of sum(g_cm * c_m) + sum(g_D * D) with respect to the mesh inputs."""
+    pix, face = _c(pix, np.int32), _c(face, np.int32)
+    n = len(pix)
+    m = mesh.struct
+    out = {"verts": np.zeros((3, m.V)), "vcolor": np.zeros((3, m.V)), "vnormal": np.zeros((3, m.V)),
+           "uv": np.zeros((2, max(m.Vt, 1))), "tex": np.zeros((max(m.S, 1), max(m.S, 1), 3)),
+           "light": np.zeros(13)}
+    lib().oc_mesh_bwd(C.byref(cam), C.byref(m), n, _p(pix), _p(face), _p(_c(g_cm, np.float64)),
+                      _p(_c(g_D, np.float64)), _p(out["verts"]), _p(out["vcolor"]), _p(out["vnormal"]),
+                      _p(out["uv"]), _p(out["tex"]), _p(out["light"]))
     return out
