@@ -45,8 +45,8 @@ class GmMesh(C.Structure):
 
 EXPORTS = ["gm_bin_triangles_ws", "gm_bin_triangles", "gm_raster_zbuffer", "gm_project_gaussians",
            "gm_sort_tile_keys_ws", "gm_sort_tile_keys", "gm_composite_hybrid_fwd",
-           "gm_composite_hybrid_bwd", "gm_project_gaussians_bwd", "gm_mipmaps_floats", "gm_build_mipmaps",
-           "gm_last_error", "gm_version"]
+           "gm_composite_hybrid_bwd", "gm_project_gaussians_bwd", "gm_mesh_bwd", "gm_mipmaps_floats",
+           "gm_build_mipmaps", "gm_last_error", "gm_version"]
 
 _lib = None
 
@@ -73,6 +73,7 @@ def lib():
     L.gm_composite_hybrid_fwd.argtypes = [cam, P, P, P, P, P, mesh, P, light, P, F32, P, P, P, P, P, P, P]
     L.gm_composite_hybrid_bwd.argtypes = [cam, I32, P, P, P, P, P, F32, P, P, P, P, P, P, P, P, P, P]
     L.gm_project_gaussians_bwd.argtypes = [cam, I32, P, P, P, P, P, I32, P, P, P, P, P, P, P, P, P, P]
+    L.gm_mesh_bwd.argtypes = [cam, mesh, light, P, P, P, P, P, P, P, P, P, P]
     L.gm_mipmaps_floats.argtypes = [I32]
     L.gm_mipmaps_floats.restype = SZ
     L.gm_build_mipmaps.argtypes = [P, I32, P, P]
@@ -85,7 +86,7 @@ def lib():
             raise ImportError(f"{LIB_PATH} does not export {name}")
     for name in ("gm_bin_triangles", "gm_raster_zbuffer", "gm_project_gaussians", "gm_sort_tile_keys",
                  "gm_composite_hybrid_fwd", "gm_composite_hybrid_bwd", "gm_project_gaussians_bwd",
-                 "gm_build_mipmaps"):
+                 "gm_mesh_bwd", "gm_build_mipmaps"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -168,6 +169,13 @@ def gm_project_gaussians_bwd(cam, N, means, quats, scales, opacity, sh, sh_degre
                                          ptr(sh), int(sh_degree), ptr(rec), ptr(g_rec), ptr(g_means), ptr(g_quats),
                                          ptr(g_scales), ptr(g_opacity), ptr(g_sh), ptr(g_log_scales),
                                          ptr(g_logit_opacity), stream))
+
+
+def gm_mesh_bwd(cam, mesh, light, face_id, g_mesh_rgb, g_mesh_depth, g_verts, g_vcolor, g_vnormal, g_uv, g_mips,
+                g_light, stream):
+    check(lib().gm_mesh_bwd(C.byref(cam), C.byref(mesh), _light_ref(light), ptr(face_id), ptr(g_mesh_rgb),
+                            ptr(g_mesh_depth), ptr(g_verts), ptr(g_vcolor), ptr(g_vnormal), ptr(g_uv), ptr(g_mips),
+                            ptr(g_light), stream))
 
 
 def gm_mipmaps_floats(S) -> int:

@@ -1,0 +1,487 @@
+// Mesh side of the backward: from dL/dc_m and dL/dD per pixel to the gradients of
+// the vertex positions, vertex colours, vertex normals, texture coordinates, texels
+// and the point light (gmesh README, "Design Details": the surface colour comes from
+// perspective-correct barycentrics of the nearest triangle, vertex colours or a
+// trilinear mip-mapped texture, per-pixel Phong shading of interpolated normals;
+// the mesh depth D enters the hybrid composite through the split; the renderer is
+// differentiable with respect to the mesh as well).
+//
+// One thread per pixel; a covered pixel re-evaluates its surface in fp64 (the
+// barycentric chain divides by the triangle's area and by depths, and the level of
+// detail must select the same pyramid levels as the forward's definition) and runs
+// the reverse mode, adding into the per-vertex and per-texel gradients with float
+// atomics; the light's 13 gradients are summed per block first.  Texel gradients
+// land on the two pyramid levels each lookup used, and a level-by-level pass then
+// hands every coarse texel's gradient down to its 2x2 children (the adjoint of the
+// box-filter pyramid), so level 0 ends up holding dL/dtexture.  Visibility and the
+// level of detail are taken as given (no gradient), as in the reverse mode's
+// definition.  Value arithmetic only, so contraction is on.
+#include "gm_internal.h"
+
+namespace gm {
+
+constexpr int MB_THREADS = 256;
+
+struct MeshBwdParams {
+    DevCamera cam;
+    int V, F, Vt, S, nlev;
+    const float* verts;
+    const int32_t* faces;
+    const float* vcolor;
+    const float* vnormal;
+    const float* uv;
+    const int32_t* faces_uv;
+    const float* mips;
+    int lit;
+    double lpos[3], lamb[3], ldif[3], lspec[3], lshin;
+};
+
+__host__ __device__ inline size_t level_offset(int S, int l)
+{
+    size_t o = 0;
+    for (int k = 0; k < l; ++k) o += (size_t)(S >> k) * (S >> k) * 3;
+    return o;
+}
+
+// Bilinear lookup (clamp to edge) with its texel indices, weights and d/d(u, v).
+struct Bilin {
+    int idx[4];
+    double wgt[4];
+    double col[3], du[3], dv[3];
+};
+
+__device__ inline void bilin(const float* __restrict__ lvl, int s, double u, double v, Bilin& b)
+{
+    const double cu = fmin(fmax(u, 0.0), 1.0), cv = fmin(fmax(v, 0.0), 1.0);
+    const double su = (u > 0.0 && u < 1.0) ? 1.0 : 0.0, sv = (v > 0.0 && v < 1.0) ? 1.0 : 0.0;
+    const double x = cu * s - 0.5, y = cv * s - 0.5;
+    const double x0 = floor(x), y0 = floor(y);
+    const double ax = x - x0, ay = y - y0;
+    int ix0 = (int)x0, iy0 = (int)y0;
+    const int ix1 = min(max(ix0 + 1, 0), s - 1), iy1 = min(max(iy0 + 1, 0), s - 1);
+    ix0 = min(max(ix0, 0), s - 1);
+    iy0 = min(max(iy0, 0), s - 1);
+    b.idx[0] = (iy0 * s + ix0) * 3;
+    b.idx[1] = (iy0 * s + ix1) * 3;
+    b.idx[2] = (iy1 * s + ix0) * 3;
+    b.idx[3] = (iy1 * s + ix1) * 3;
+    b.wgt[0] = (1.0 - ax) * (1.0 - ay);
+    b.wgt[1] = ax * (1.0 - ay);
+    b.wgt[2] = (1.0 - ax) * ay;
+    b.wgt[3] = ax * ay;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        const double t00 = lvl[b.idx[0] + c], t01 = lvl[b.idx[1] + c];
+        const double t10 = lvl[b.idx[2] + c], t11 = lvl[b.idx[3] + c];
+        const double top = t00 + (t01 - t00) * ax, bot = t10 + (t11 - t10) * ax;
+        b.col[c] = top + (bot - top) * ay;
+        b.du[c] = ((t01 - t00) * (1.0 - ay) + (t11 - t10) * ay) * s * su;
+        b.dv[c] = (bot - top) * s * sv;
+    }
+}
+
+__device__ __forceinline__ void addf(float* p, double v)
+{
+    if (v != 0.0) unsafeAtomicAdd(p, (float)v);
+}
+
+__global__ void __launch_bounds__(MB_THREADS)
+k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __restrict__ g_rgb,
+           const float* __restrict__ g_depth, float* __restrict__ g_verts, float* __restrict__ g_vcolor,
+           float* __restrict__ g_vnormal, float* __restrict__ g_uv, float* __restrict__ g_mips,
+           float* __restrict__ g_light)
+{
+    __shared__ float s_light[13][MB_THREADS / 64];
+    const int pix = blockIdx.x * blockDim.x + threadIdx.x;
+    const int W = P.cam.width, H = P.cam.height;
+    double gl[13];
+#pragma unroll
+    for (int i = 0; i < 13; ++i) gl[i] = 0.0;
+    const int f = pix < W * H ? face_id[pix] : -1;
+    if (f >= 0) {
+        const int px = pix % W, py = pix / W;
+        const double pu = px + 0.5, pv = py + 0.5;
+        double R[9], t[3];
+#pragma unroll
+        for (int i = 0; i < 9; ++i) R[i] = P.cam.R[i];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) t[i] = P.cam.t[i];
+        const double fx = P.cam.fx, fy = P.cam.fy, cx = P.cam.cx, cy = P.cam.cy;
+        // ---- forward ---------------------------------------------------------------
+        int vi[3];
+        double xc[3][3], u[3], v[3], z[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            vi[k] = P.faces[k * P.F + f];
+            const double X0 = P.verts[vi[k]], X1 = P.verts[P.V + vi[k]], X2 = P.verts[2 * P.V + vi[k]];
+#pragma unroll
+            for (int r = 0; r < 3; ++r) xc[k][r] = R[3 * r] * X0 + R[3 * r + 1] * X1 + R[3 * r + 2] * X2 + t[r];
+            u[k] = fx * xc[k][0] / xc[k][2] + cx;
+            v[k] = fy * xc[k][1] / xc[k][2] + cy;
+            z[k] = xc[k][2];
+        }
+        const int ea[3] = {1, 2, 0}, eb[3] = {2, 0, 1};  // edge opposite corner k
+        double lam[3], w[3], Wsum = 0.0;
+        const double A = (u[1] - u[0]) * (v[2] - v[0]) - (v[1] - v[0]) * (u[2] - u[0]);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int a = ea[k], b = eb[k];
+            const double E = (u[b] - u[a]) * (pv - v[a]) - (v[b] - v[a]) * (pu - u[a]);
+            lam[k] = E / A;
+            w[k] = lam[k] / z[k];
+            Wsum += w[k];
+        }
+        const double zz = 1.0 / Wsum;
+        double bb[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) bb[k] = w[k] * zz;
+
+        double gc[3], gz = g_depth ? (double)g_depth[pix] : 0.0;
+#pragma unroll
+        for (int c = 0; c < 3; ++c) gc[c] = g_rgb ? (double)g_rgb[3 * pix + c] : 0.0;
+        double gb[3] = {0.0, 0.0, 0.0}, gbase[3];
+
+        // base colour (forward values needed by the lighting's backward)
+        double base[3] = {0.0, 0.0, 0.0};
+        const bool textured = P.mips != nullptr;
+        Bilin B0, B1;
+        int l0 = 0, l1 = 0, ti[3] = {0, 0, 0};
+        double tl = 0.0, uvk[3][2], uu = 0.0, vv = 0.0;
+        if (textured) {
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                ti[k] = P.faces_uv[k * P.F + f];
+                uvk[k][0] = P.uv[ti[k]];
+                uvk[k][1] = P.uv[P.Vt + ti[k]];
+                uu += bb[k] * uvk[k][0];
+                vv += bb[k] * uvk[k][1];
+            }
+            double dux = 0.0, dvx = 0.0, duy = 0.0, dvy = 0.0;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                const double dwx = (-(v[eb[k]] - v[ea[k]]) / A) / z[k];
+                const double dwy = ((u[eb[k]] - u[ea[k]]) / A) / z[k];
+                dux += dwx * (uvk[k][0] - uu) / Wsum;
+                dvx += dwx * (uvk[k][1] - vv) / Wsum;
+                duy += dwy * (uvk[k][0] - uu) / Wsum;
+                dvy += dwy * (uvk[k][1] - vv) / Wsum;
+            }
+            const double S0 = P.S;
+            const double lx = sqrt(S0 * dux * S0 * dux + S0 * dvx * S0 * dvx);
+            const double ly = sqrt(S0 * duy * S0 * duy + S0 * dvy * S0 * dvy);
+            const double rho = fmax(lx, ly);
+            const double lmax = P.nlev - 1;
+            double lod = rho > 0.0 ? log2(rho) : 0.0;
+            lod = fmin(fmax(lod, 0.0), lmax);
+            l0 = (int)floor(lod);
+            l1 = min(l0 + 1, P.nlev - 1);
+            tl = lod - l0;
+            bilin(P.mips + level_offset(P.S, l0), P.S >> l0, uu, vv, B0);
+            bilin(P.mips + level_offset(P.S, l1), P.S >> l1, uu, vv, B1);
+#pragma unroll
+            for (int c = 0; c < 3; ++c) base[c] = B0.col[c] + (B1.col[c] - B0.col[c]) * tl;
+        } else if (P.vcolor) {
+#pragma unroll
+            for (int c = 0; c < 3; ++c)
+#pragma unroll
+                for (int k = 0; k < 3; ++k) base[c] += bb[k] * P.vcolor[c * P.V + vi[k]];
+        }
+
+        // ---- lighting: forward values, then reverse -------------------------------------
+        if (P.lit && P.vnormal) {
+            double nw[3], nt[3], L[3], x[3], lt[3], et[3];
+#pragma unroll
+            for (int c = 0; c < 3; ++c) {
+                nw[c] = 0.0;
+#pragma unroll
+                for (int k = 0; k < 3; ++k) nw[c] += bb[k] * P.vnormal[c * P.V + vi[k]];
+            }
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                nt[r] = R[3 * r] * nw[0] + R[3 * r + 1] * nw[1] + R[3 * r + 2] * nw[2];
+                L[r] = R[3 * r] * P.lpos[0] + R[3 * r + 1] * P.lpos[1] + R[3 * r + 2] * P.lpos[2] + t[r];
+            }
+            x[0] = (pu - cx) / fx * zz;
+            x[1] = (pv - cy) / fy * zz;
+            x[2] = zz;
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                lt[r] = L[r] - x[r];
+                et[r] = -x[r];
+            }
+            const double nn = sqrt(nt[0] * nt[0] + nt[1] * nt[1] + nt[2] * nt[2]);
+            const double ln = sqrt(lt[0] * lt[0] + lt[1] * lt[1] + lt[2] * lt[2]);
+            const double en = sqrt(et[0] * et[0] + et[1] * et[1] + et[2] * et[2]);
+            double n[3], l[3], e[3], rv[3];
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                n[r] = nt[r] / nn;
+                l[r] = lt[r] / ln;
+                e[r] = et[r] / en;
+            }
+            const double ndl = n[0] * l[0] + n[1] * l[1] + n[2] * l[2];
+#pragma unroll
+            for (int r = 0; r < 3; ++r) rv[r] = 2.0 * ndl * n[r] - l[r];
+            const double rde = rv[0] * e[0] + rv[1] * e[1] + rv[2] * e[2];
+            const double diff = ndl > 0.0 ? ndl : 0.0;
+            const bool spec_on = ndl > 0.0 && rde > 0.0;
+            const double spec = spec_on ? pow(rde, P.lshin) : 0.0;
+            double gdiff = 0.0, gspec = 0.0;
+#pragma unroll
+            for (int c = 0; c < 3; ++c) {
+                gbase[c] = gc[c] * (P.lamb[c] + P.ldif[c] * diff);
+                gl[3 + c] = gc[c] * base[c];
+                gl[6 + c] = gc[c] * base[c] * diff;
+                gl[9 + c] = gc[c] * spec;
+                gdiff += gc[c] * base[c] * P.ldif[c];
+                gspec += gc[c] * P.lspec[c];
+            }
+            double gndl = ndl > 0.0 ? gdiff : 0.0, grde = 0.0;
+            if (spec_on) {
+                grde = gspec * P.lshin * pow(rde, P.lshin - 1.0);
+                gl[12] = gspec * spec * log(rde);
+            }
+            double gn[3], glv[3], ge[3], rn = 0.0;
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {  // rde = r . e, r = 2 ndl n - l
+                const double grr = grde * e[r];
+                ge[r] = grde * rv[r];
+                rn += grr * n[r];
+                gn[r] = 2.0 * ndl * grr;
+                glv[r] = -grr;
+            }
+            gndl += 2.0 * rn;
+            double dn = 0.0, dl = 0.0, de = 0.0;
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {  // ndl = n . l
+                gn[r] += gndl * l[r];
+                glv[r] += gndl * n[r];
+                dn += n[r] * gn[r];
+                dl += l[r] * glv[r];
+                de += e[r] * ge[r];
+            }
+            double gnt[3], glt[3], get[3];
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {  // normalisations
+                gnt[r] = (gn[r] - n[r] * dn) / nn;
+                glt[r] = (glv[r] - l[r] * dl) / ln;
+                get[r] = (ge[r] - e[r] * de) / en;
+            }
+            double gnw[3];
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {  // nt = R nw, L = R pos + t
+                gnw[j] = R[j] * gnt[0] + R[3 + j] * gnt[1] + R[6 + j] * gnt[2];
+                gl[j] = R[j] * glt[0] + R[3 + j] * glt[1] + R[6 + j] * glt[2];
+            }
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {  // nw = sum b_k normal_k
+                double acc = 0.0;
+#pragma unroll
+                for (int c = 0; c < 3; ++c) {
+                    acc += P.vnormal[c * P.V + vi[k]] * gnw[c];
+                    if (g_vnormal) addf(&g_vnormal[c * P.V + vi[k]], bb[k] * gnw[c]);
+                }
+                gb[k] += acc;
+            }
+            // x = ((pu - cx)/fx z, (pv - cy)/fy z, z); lt = L - x, et = -x
+            const double gx0 = -glt[0] - get[0], gx1 = -glt[1] - get[1], gx2 = -glt[2] - get[2];
+            gz += gx0 * (pu - cx) / fx + gx1 * (pv - cy) / fy + gx2;
+        } else {
+#pragma unroll
+            for (int c = 0; c < 3; ++c) gbase[c] = gc[c];
+        }
+
+        // ---- base colour ---------------------------------------------------------------
+        if (textured) {
+            double guu = 0.0, gvv = 0.0;
+            float* m0 = g_mips ? g_mips + level_offset(P.S, l0) : nullptr;
+            float* m1 = g_mips ? g_mips + level_offset(P.S, l1) : nullptr;
+#pragma unroll
+            for (int c = 0; c < 3; ++c) {
+                const double a0 = gbase[c] * (1.0 - tl), a1 = gbase[c] * tl;
+                guu += a0 * B0.du[c] + a1 * B1.du[c];
+                gvv += a0 * B0.dv[c] + a1 * B1.dv[c];
+                if (g_mips)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        addf(&m0[B0.idx[q] + c], a0 * B0.wgt[q]);
+                        addf(&m1[B1.idx[q] + c], a1 * B1.wgt[q]);
+                    }
+            }
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                gb[k] += uvk[k][0] * guu + uvk[k][1] * gvv;
+                if (g_uv) {
+                    addf(&g_uv[ti[k]], bb[k] * guu);
+                    addf(&g_uv[P.Vt + ti[k]], bb[k] * gvv);
+                }
+            }
+        } else if (P.vcolor) {
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+#pragma unroll
+                for (int c = 0; c < 3; ++c) {
+                    gb[k] += P.vcolor[c * P.V + vi[k]] * gbase[c];
+                    if (g_vcolor) addf(&g_vcolor[c * P.V + vi[k]], bb[k] * gbase[c]);
+                }
+        }
+
+        // ---- vertex positions: b_k = w_k z, z = 1/W, w_k = lam_k / z_k, lam_k = E_k / A
+        if (g_verts) {
+            double gw[3];
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                gw[k] = gb[k] * zz;
+                gz += gb[k] * w[k];
+            }
+            const double gW = -gz * zz * zz;
+            double glam[3], gzk[3], gu[3] = {0.0, 0.0, 0.0}, gv[3] = {0.0, 0.0, 0.0}, gA = 0.0;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                gw[k] += gW;
+                glam[k] = gw[k] / z[k];
+                gzk[k] = -gw[k] * lam[k] / (z[k] * z[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                const double gE = glam[k] / A;
+                gA -= glam[k] * lam[k] / A;
+                const int a = ea[k], b = eb[k];
+                gu[a] += gE * (v[b] - pv);
+                gu[b] += gE * (pv - v[a]);
+                gv[a] += gE * (pu - u[b]);
+                gv[b] += gE * (u[a] - pu);
+            }
+            gu[0] += gA * (v[1] - v[2]);
+            gu[1] += gA * (v[2] - v[0]);
+            gu[2] += gA * (v[0] - v[1]);
+            gv[0] += gA * (u[2] - u[1]);
+            gv[1] += gA * (u[0] - u[2]);
+            gv[2] += gA * (u[1] - u[0]);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                const double zc = xc[k][2];
+                const double gxc = gu[k] * fx / zc, gyc = gv[k] * fy / zc;
+                const double gzc = gzk[k] - gu[k] * fx * xc[k][0] / (zc * zc) - gv[k] * fy * xc[k][1] / (zc * zc);
+#pragma unroll
+                for (int j = 0; j < 3; ++j)
+                    addf(&g_verts[j * P.V + vi[k]], R[j] * gxc + R[3 + j] * gyc + R[6 + j] * gzc);
+            }
+        }
+    }
+    // light: per-wave sums, then per-block atomics
+    if (g_light) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+        for (int i = 0; i < 13; ++i) {
+            float s = (float)gl[i];
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+            if (lane == 0) s_light[i][wave] = s;
+        }
+        __syncthreads();
+        if (threadIdx.x < 13) {
+            float s = 0.0f;
+#pragma unroll
+            for (int w = 0; w < MB_THREADS / 64; ++w) s += s_light[threadIdx.x][w];
+            if (s != 0.0f) unsafeAtomicAdd(&g_light[threadIdx.x], s);
+        }
+    }
+}
+
+// Adjoint of one pyramid step: fine[2y + a][2x + b] += coarse[y][x] / 4.
+__global__ void k_pyramid_adjoint(float* __restrict__ fine, const float* __restrict__ coarse, int s)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const int sf = 2 * s;
+    if (i >= sf * sf * 3) return;
+    const int c = i % 3, x = (i / 3) % sf, y = i / (3 * sf);
+    fine[i] += 0.25f * coarse[((y >> 1) * s + (x >> 1)) * 3 + c];
+}
+
+__global__ void k_zero(float* __restrict__ p, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+static gm_status zero(float* p, int64_t n, hipStream_t stream)
+{
+    if (!p || n <= 0) return GM_OK;
+    k_zero<<<(unsigned)div_up(n, 256), 256, 0, stream>>>(p, n);
+    GM_LAUNCH_CHECK();
+    return GM_OK;
+}
+
+}  // namespace gm
+
+using namespace gm;
+
+extern "C" gm_status gm_mesh_bwd(const gm_camera* cam, const gm_mesh* mesh, const gm_light* light,
+                                 const int32_t* face_id, const float* g_mesh_rgb, const float* g_mesh_depth,
+                                 float* g_verts, float* g_vcolor, float* g_vnormal, float* g_uv, float* g_mips,
+                                 float* g_light, hipStream_t stream)
+{
+    clear_error();
+    if (gm_status s = check_camera(cam)) return s;
+    GM_ARG_CHECK(mesh != nullptr && face_id != nullptr, "mesh / face_id is NULL");
+    GM_ARG_CHECK(mesh->V >= 0 && mesh->F >= 0, "negative mesh size");
+    GM_ARG_CHECK(mesh->F == 0 || (mesh->verts && mesh->faces), "verts / faces is NULL");
+    GM_ARG_CHECK(!g_vcolor || mesh->vcolor, "g_vcolor needs vertex colours");
+    GM_ARG_CHECK(!g_vnormal || (mesh->vnormal && light), "g_vnormal needs normals and a light");
+    GM_ARG_CHECK(!g_light || light, "g_light needs a light");
+    GM_ARG_CHECK(!(g_uv || g_mips) || mesh->mips, "g_uv / g_mips need a textured mesh");
+    MeshBwdParams P{};
+    P.cam = dev_camera(*cam);
+    P.V = mesh->V;
+    P.F = mesh->F;
+    P.verts = mesh->verts;
+    P.faces = mesh->faces;
+    P.vcolor = mesh->vcolor;
+    P.vnormal = mesh->vnormal;
+    if (mesh->mips) {
+        GM_ARG_CHECK(mesh->uv && mesh->faces_uv, "textured mesh needs uv and faces_uv");
+        GM_ARG_CHECK(mesh->tex_size > 0 && (mesh->tex_size & (mesh->tex_size - 1)) == 0,
+                     "tex_size %d is not a power of two", mesh->tex_size);
+        P.Vt = mesh->Vt;
+        P.S = mesh->tex_size;
+        P.uv = mesh->uv;
+        P.faces_uv = mesh->faces_uv;
+        P.mips = mesh->mips;
+        for (int s = P.S; s >= 1; s >>= 1) ++P.nlev;
+    }
+    if (light) {
+        P.lit = 1;
+        for (int i = 0; i < 3; ++i) {
+            P.lpos[i] = light->pos[i];
+            P.lamb[i] = light->ambient[i];
+            P.ldif[i] = light->diffuse[i];
+            P.lspec[i] = light->specular[i];
+        }
+        P.lshin = light->shininess;
+    }
+    const size_t nmips = P.mips ? gm_mipmaps_floats(P.S) : 0;
+    if (gm_status s = zero(g_verts, 3 * (int64_t)P.V, stream)) return s;
+    if (gm_status s = zero(g_vcolor, 3 * (int64_t)P.V, stream)) return s;
+    if (gm_status s = zero(g_vnormal, 3 * (int64_t)P.V, stream)) return s;
+    if (gm_status s = zero(g_uv, 2 * (int64_t)P.Vt, stream)) return s;
+    if (gm_status s = zero(g_mips, (int64_t)nmips, stream)) return s;
+    if (gm_status s = zero(g_light, 13, stream)) return s;
+    const int64_t HW = (int64_t)cam->width * cam->height;
+    if (P.F > 0) {
+        k_mesh_bwd<<<(unsigned)div_up(HW, MB_THREADS), MB_THREADS, 0, stream>>>(
+            P, face_id, g_mesh_rgb, g_mesh_depth, g_verts, g_vcolor, P.lit ? g_vnormal : nullptr, g_uv, g_mips,
+            g_light);
+        GM_LAUNCH_CHECK();
+    }
+    if (g_mips && P.nlev > 1) {  // coarse to fine: level l - 1 += adjoint(level l)
+        for (int l = P.nlev - 1; l >= 1; --l) {
+            const int s = P.S >> l;
+            const int64_t nf = (int64_t)(2 * s) * (2 * s) * 3;
+            k_pyramid_adjoint<<<(unsigned)div_up(nf, 256), 256, 0, stream>>>(g_mips + level_offset(P.S, l - 1),
+                                                                            g_mips + level_offset(P.S, l), s);
+            GM_LAUNCH_CHECK();
+        }
+    }
+    return GM_OK;
+}

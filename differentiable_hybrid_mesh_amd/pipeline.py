@@ -215,6 +215,35 @@ class Renderer:
         return {"means": self.g_means[:, :N], "quats": self.g_quats[:, :N], "scales": self.g_scales[:, :N],
                 "opacity": self.g_opacity[:N], "sh": self.g_sh[..., :N]}
 
+    def mesh_bwd(self, view: int, g_mesh_rgb=None, g_mesh_depth=None):
+        """Gradients of the mesh parameters from per-pixel dL/dc_m and dL/dD (default:
+        the last composite backward's).  Buffers are allocated on first use."""
+        ds, s = self.ds, self.ds.scene
+        dev, f32 = ds.device, torch.float32
+        if not hasattr(self, "gm_verts"):
+            V = max(s.V, 1)
+            self.gm_verts = torch.empty((3, V), dtype=f32, device=dev)
+            self.gm_vcolor = torch.empty((3, V), dtype=f32, device=dev) if s.vcolor is not None else None
+            lit = ds.light is not None and s.vnormal is not None
+            self.gm_vnormal = torch.empty((3, V), dtype=f32, device=dev) if lit else None
+            self.gm_light = torch.empty(13, dtype=f32, device=dev) if lit else None
+            tex = ds.mips is not None
+            self.gm_uv = torch.empty((2, max(ds.mesh.Vt, 1)), dtype=f32, device=dev) if tex else None
+            self.gm_mips = torch.empty(G.gm_mipmaps_floats(ds.tex_size), dtype=f32, device=dev) if tex else None
+        G.gm_mesh_bwd(ds.cams[view], ds.mesh, ds.light, self.face_id,
+                      self.g_mesh_rgb if g_mesh_rgb is None else g_mesh_rgb,
+                      self.g_mesh_depth if g_mesh_depth is None else g_mesh_depth, self.gm_verts, self.gm_vcolor,
+                      self.gm_vnormal, self.gm_uv, self.gm_mips, self.gm_light, _stream())
+        out = {"verts": self.gm_verts[:, : s.V]}
+        if self.gm_vcolor is not None:
+            out["vcolor"] = self.gm_vcolor[:, : s.V]
+        if self.gm_vnormal is not None:
+            out["vnormal"], out["light"] = self.gm_vnormal[:, : s.V], self.gm_light
+        if self.gm_mips is not None:
+            S = ds.tex_size
+            out["uv"], out["tex"] = self.gm_uv[:, : ds.mesh.Vt], self.gm_mips[: S * S * 3].view(S, S, 3)
+        return out
+
     # -- whole passes -----------------------------------------------------------
     def forward_async(self, view: int = 0, cull: bool = True):
         """Queue one forward pass and the copy of the list lengths; no synchronisation.

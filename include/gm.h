@@ -267,6 +267,33 @@ gm_status gm_project_gaussians_bwd(const gm_camera* cam, int32_t N, const float*
                                    float* g_log_scales, float* g_logit_opacity, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * 8. gm_mesh_bwd — gradients of the mesh's own parameters.
+ * README "Design Details": the surface colour c_m comes from perspective-correct
+ * barycentrics of the nearest triangle (vertex colours, or the trilinear mip-mapped
+ * texture at the interpolated texture coordinate), lit per pixel by Phong shading of
+ * interpolated normals (v1.1 notes); the mesh depth D enters the composite through
+ * the split; the renderer is differentiable with respect to the mesh as well.
+ *
+ * Given g_mesh_rgb [H][W][3] = dL/dc_m and g_mesh_depth [H][W] = dL/dD (outputs of
+ * call 6; either may be NULL) and the face_id buffer of call 2, writes the gradients
+ * of the inputs of the surface colour and depth: g_verts [3][V] (world positions,
+ * through the barycentrics, D and the lighting's view vectors), g_vcolor [3][V],
+ * g_vnormal [3][V], g_uv [2][Vt], g_mips (gm_mipmaps_floats(S) floats; on return
+ * its first S*S*3 floats hold dL/dtexture [S][S][3], the coarser levels hold the
+ * intermediate sums of the pyramid's adjoint) and g_light [13] (pos[3], ambient[3],
+ * diffuse[3], specular[3], shininess).  Outputs are zero-filled by the call; NULL
+ * ones are skipped (g_vcolor needs vertex colours, g_vnormal and g_light a light and
+ * normals, g_uv and g_mips a textured mesh).  Which face covers a pixel and the
+ * texture's level of detail are taken as given (no gradient through them); a clamp
+ * passes no gradient on its clamped side.  Vertex positions are taken in fp64
+ * through the same camera as call 1.
+ * ------------------------------------------------------------------------- */
+gm_status gm_mesh_bwd(const gm_camera* cam, const gm_mesh* mesh, const gm_light* light,
+                      const int32_t* face_id, const float* g_mesh_rgb, const float* g_mesh_depth,
+                      float* g_verts, float* g_vcolor, float* g_vnormal, float* g_uv, float* g_mips,
+                      float* g_light, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Auxiliary.
  * gm_build_mipmaps: README v1.1 (trilinear mipmapping by default): box-filter
  * pyramid of a square power-of-two texture tex [S][S][3] (HWC, values in [0, 1]);
