@@ -210,6 +210,8 @@ def main():
     roof["launch_ms"] = round(stage_ms[dom], 4)
 
     next_stages = {"project_bwd": time_project_bwd(r, scene, view, args.steps)} if N else {}
+    if scene.F:
+        next_stages["mesh_bwd"] = time_mesh_bwd(r, scene, view, args.steps)
 
     total_alg = sum(alg_bytes.values())
     out = {
@@ -260,6 +262,33 @@ def time_project_bwd(r, scene, view, steps):
     return {"kernel": "k_project_bwd", "ms": round(ms, 4), "bound": "hbm", "achieved": round(gbs, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
             "algorithmic_bytes": nbytes, "listed": nl}
+
+
+def time_mesh_bwd(r, scene, view, steps):
+    """The mesh-side backward (gradients of vertex positions, colours, normals, texels
+    and light from the composite backward's per-pixel dL/dc_m and dL/dD), timed on its
+    own like the projection backward.  Algorithmic bytes: the face-id buffer, the two
+    per-pixel gradients at covered pixels, the mesh's faces and per-vertex inputs once,
+    and the per-vertex gradients written once (the float atomics' traffic is the
+    implementation's, not the algorithm's)."""
+    import torch
+    V, F = scene.V, scene.F
+    covered = int((r.face_id >= 0).sum().item())
+    per_vertex = 12 * (1 + (scene.vcolor is not None) + (scene.vnormal is not None))
+    nbytes = (4 * scene.width * scene.height + 16 * covered + 12 * F + per_vertex * V + per_vertex * V)
+    r.mesh_bwd(view)  # allocates the gradient buffers
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        r.mesh_bwd(view)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": "k_mesh_bwd", "ms": round(ms, 4), "bound": "hbm", "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": nbytes, "covered_pixels": covered}
 
 
 def included_fraction(scene, view, ntiles=48):

@@ -85,7 +85,7 @@ __device__ __forceinline__ void addf(float* p, double v)
     if (v != 0.0) unsafeAtomicAdd(p, (float)v);
 }
 
-__global__ void __launch_bounds__(MB_THREADS)
+__global__ void __launch_bounds__(MB_THREADS, 2)
 k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __restrict__ g_rgb,
            const float* __restrict__ g_depth, float* __restrict__ g_verts, float* __restrict__ g_vcolor,
            float* __restrict__ g_vnormal, float* __restrict__ g_uv, float* __restrict__ g_mips,
@@ -94,9 +94,16 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
     __shared__ float s_light[13][MB_THREADS / 64];
     const int pix = blockIdx.x * blockDim.x + threadIdx.x;
     const int W = P.cam.width, H = P.cam.height;
-    double gl[13];
+    float gl[13];
 #pragma unroll
-    for (int i = 0; i < 13; ++i) gl[i] = 0.0;
+    for (int i = 0; i < 13; ++i) gl[i] = 0.0f;
+    // per-corner gradients of this pixel: position (3), colour (3), normal (3), uv (2)
+    float acc[3][11];
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+        for (int j = 0; j < 11; ++j) acc[k][j] = 0.0f;
+    int vi[3] = {0, 0, 0}, ti[3] = {0, 0, 0};
     const int f = pix < W * H ? face_id[pix] : -1;
     if (f >= 0) {
         const int px = pix % W, py = pix / W;
@@ -108,7 +115,6 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
         for (int i = 0; i < 3; ++i) t[i] = P.cam.t[i];
         const double fx = P.cam.fx, fy = P.cam.fy, cx = P.cam.cx, cy = P.cam.cy;
         // ---- forward ---------------------------------------------------------------
-        int vi[3];
         double xc[3][3], u[3], v[3], z[3];
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
@@ -145,7 +151,7 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
         double base[3] = {0.0, 0.0, 0.0};
         const bool textured = P.mips != nullptr;
         Bilin B0, B1;
-        int l0 = 0, l1 = 0, ti[3] = {0, 0, 0};
+        int l0 = 0, l1 = 0;
         double tl = 0.0, uvk[3][2], uu = 0.0, vv = 0.0;
         if (textured) {
 #pragma unroll
@@ -187,71 +193,76 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
                 for (int k = 0; k < 3; ++k) base[c] += bb[k] * P.vcolor[c * P.V + vi[k]];
         }
 
-        // ---- lighting: forward values, then reverse -------------------------------------
+        // ---- lighting (fp32: well conditioned): forward values, then reverse ---------------
         if (P.lit && P.vnormal) {
-            double nw[3], nt[3], L[3], x[3], lt[3], et[3];
+            const float* Rf = P.cam.R;
+            float nw[3], nt[3], L[3], x[3], lt[3], et[3];
 #pragma unroll
             for (int c = 0; c < 3; ++c) {
-                nw[c] = 0.0;
+                nw[c] = 0.0f;
 #pragma unroll
-                for (int k = 0; k < 3; ++k) nw[c] += bb[k] * P.vnormal[c * P.V + vi[k]];
+                for (int k = 0; k < 3; ++k) nw[c] += (float)bb[k] * P.vnormal[c * P.V + vi[k]];
             }
 #pragma unroll
             for (int r = 0; r < 3; ++r) {
-                nt[r] = R[3 * r] * nw[0] + R[3 * r + 1] * nw[1] + R[3 * r + 2] * nw[2];
-                L[r] = R[3 * r] * P.lpos[0] + R[3 * r + 1] * P.lpos[1] + R[3 * r + 2] * P.lpos[2] + t[r];
+                nt[r] = Rf[3 * r] * nw[0] + Rf[3 * r + 1] * nw[1] + Rf[3 * r + 2] * nw[2];
+                L[r] = Rf[3 * r] * (float)P.lpos[0] + Rf[3 * r + 1] * (float)P.lpos[1] + Rf[3 * r + 2] * (float)P.lpos[2] +
+                       P.cam.t[r];
             }
-            x[0] = (pu - cx) / fx * zz;
-            x[1] = (pv - cy) / fy * zz;
-            x[2] = zz;
+            const float zf = (float)zz;
+            x[0] = (float)((pu - cx) / fx) * zf;
+            x[1] = (float)((pv - cy) / fy) * zf;
+            x[2] = zf;
 #pragma unroll
             for (int r = 0; r < 3; ++r) {
                 lt[r] = L[r] - x[r];
                 et[r] = -x[r];
             }
-            const double nn = sqrt(nt[0] * nt[0] + nt[1] * nt[1] + nt[2] * nt[2]);
-            const double ln = sqrt(lt[0] * lt[0] + lt[1] * lt[1] + lt[2] * lt[2]);
-            const double en = sqrt(et[0] * et[0] + et[1] * et[1] + et[2] * et[2]);
-            double n[3], l[3], e[3], rv[3];
+            const float nn = sqrtf(nt[0] * nt[0] + nt[1] * nt[1] + nt[2] * nt[2]);
+            const float ln = sqrtf(lt[0] * lt[0] + lt[1] * lt[1] + lt[2] * lt[2]);
+            const float en = sqrtf(et[0] * et[0] + et[1] * et[1] + et[2] * et[2]);
+            float n[3], l[3], e[3], rv[3];
 #pragma unroll
             for (int r = 0; r < 3; ++r) {
                 n[r] = nt[r] / nn;
                 l[r] = lt[r] / ln;
                 e[r] = et[r] / en;
             }
-            const double ndl = n[0] * l[0] + n[1] * l[1] + n[2] * l[2];
+            const float ndl = n[0] * l[0] + n[1] * l[1] + n[2] * l[2];
 #pragma unroll
-            for (int r = 0; r < 3; ++r) rv[r] = 2.0 * ndl * n[r] - l[r];
-            const double rde = rv[0] * e[0] + rv[1] * e[1] + rv[2] * e[2];
-            const double diff = ndl > 0.0 ? ndl : 0.0;
-            const bool spec_on = ndl > 0.0 && rde > 0.0;
-            const double spec = spec_on ? pow(rde, P.lshin) : 0.0;
-            double gdiff = 0.0, gspec = 0.0;
+            for (int r = 0; r < 3; ++r) rv[r] = 2.0f * ndl * n[r] - l[r];
+            const float rde = rv[0] * e[0] + rv[1] * e[1] + rv[2] * e[2];
+            const float diff = ndl > 0.0f ? ndl : 0.0f;
+            const bool spec_on = ndl > 0.0f && rde > 0.0f;
+            const float shin = (float)P.lshin;
+            const float spec = spec_on ? __powf(rde, shin) : 0.0f;
+            float gdiff = 0.0f, gspec = 0.0f;
 #pragma unroll
             for (int c = 0; c < 3; ++c) {
+                const float g = (float)gc[c], bs = (float)base[c];
                 gbase[c] = gc[c] * (P.lamb[c] + P.ldif[c] * diff);
-                gl[3 + c] = gc[c] * base[c];
-                gl[6 + c] = gc[c] * base[c] * diff;
-                gl[9 + c] = gc[c] * spec;
-                gdiff += gc[c] * base[c] * P.ldif[c];
-                gspec += gc[c] * P.lspec[c];
+                gl[3 + c] = g * bs;
+                gl[6 + c] = g * bs * diff;
+                gl[9 + c] = g * spec;
+                gdiff += g * bs * (float)P.ldif[c];
+                gspec += g * (float)P.lspec[c];
             }
-            double gndl = ndl > 0.0 ? gdiff : 0.0, grde = 0.0;
+            float gndl = ndl > 0.0f ? gdiff : 0.0f, grde = 0.0f;
             if (spec_on) {
-                grde = gspec * P.lshin * pow(rde, P.lshin - 1.0);
-                gl[12] = gspec * spec * log(rde);
+                grde = gspec * shin * (spec / rde);  // d rde^s / d rde = s rde^(s-1)
+                gl[12] = gspec * spec * __logf(rde);
             }
-            double gn[3], glv[3], ge[3], rn = 0.0;
+            float gn[3], glv[3], ge[3], rn = 0.0f;
 #pragma unroll
             for (int r = 0; r < 3; ++r) {  // rde = r . e, r = 2 ndl n - l
-                const double grr = grde * e[r];
+                const float grr = grde * e[r];
                 ge[r] = grde * rv[r];
                 rn += grr * n[r];
-                gn[r] = 2.0 * ndl * grr;
+                gn[r] = 2.0f * ndl * grr;
                 glv[r] = -grr;
             }
-            gndl += 2.0 * rn;
-            double dn = 0.0, dl = 0.0, de = 0.0;
+            gndl += 2.0f * rn;
+            float dn = 0.0f, dl = 0.0f, de = 0.0f;
 #pragma unroll
             for (int r = 0; r < 3; ++r) {  // ndl = n . l
                 gn[r] += gndl * l[r];
@@ -260,31 +271,31 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
                 dl += l[r] * glv[r];
                 de += e[r] * ge[r];
             }
-            double gnt[3], glt[3], get[3];
+            float gnt[3], glt[3], get[3];
 #pragma unroll
             for (int r = 0; r < 3; ++r) {  // normalisations
                 gnt[r] = (gn[r] - n[r] * dn) / nn;
                 glt[r] = (glv[r] - l[r] * dl) / ln;
                 get[r] = (ge[r] - e[r] * de) / en;
             }
-            double gnw[3];
+            float gnw[3];
 #pragma unroll
             for (int j = 0; j < 3; ++j) {  // nt = R nw, L = R pos + t
-                gnw[j] = R[j] * gnt[0] + R[3 + j] * gnt[1] + R[6 + j] * gnt[2];
-                gl[j] = R[j] * glt[0] + R[3 + j] * glt[1] + R[6 + j] * glt[2];
+                gnw[j] = Rf[j] * gnt[0] + Rf[3 + j] * gnt[1] + Rf[6 + j] * gnt[2];
+                gl[j] = Rf[j] * glt[0] + Rf[3 + j] * glt[1] + Rf[6 + j] * glt[2];
             }
 #pragma unroll
             for (int k = 0; k < 3; ++k) {  // nw = sum b_k normal_k
-                double acc = 0.0;
+                float sum = 0.0f;
 #pragma unroll
                 for (int c = 0; c < 3; ++c) {
-                    acc += P.vnormal[c * P.V + vi[k]] * gnw[c];
-                    if (g_vnormal) addf(&g_vnormal[c * P.V + vi[k]], bb[k] * gnw[c]);
+                    sum += P.vnormal[c * P.V + vi[k]] * gnw[c];
+                    acc[k][6 + c] = (float)bb[k] * gnw[c];
                 }
-                gb[k] += acc;
+                gb[k] += sum;
             }
             // x = ((pu - cx)/fx z, (pv - cy)/fy z, z); lt = L - x, et = -x
-            const double gx0 = -glt[0] - get[0], gx1 = -glt[1] - get[1], gx2 = -glt[2] - get[2];
+            const float gx0 = -glt[0] - get[0], gx1 = -glt[1] - get[1], gx2 = -glt[2] - get[2];
             gz += gx0 * (pu - cx) / fx + gx1 * (pv - cy) / fy + gx2;
         } else {
 #pragma unroll
@@ -311,10 +322,8 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
 #pragma unroll
             for (int k = 0; k < 3; ++k) {
                 gb[k] += uvk[k][0] * guu + uvk[k][1] * gvv;
-                if (g_uv) {
-                    addf(&g_uv[ti[k]], bb[k] * guu);
-                    addf(&g_uv[P.Vt + ti[k]], bb[k] * gvv);
-                }
+                acc[k][9] = (float)(bb[k] * guu);
+                acc[k][10] = (float)(bb[k] * gvv);
             }
         } else if (P.vcolor) {
 #pragma unroll
@@ -322,7 +331,7 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
 #pragma unroll
                 for (int c = 0; c < 3; ++c) {
                     gb[k] += P.vcolor[c * P.V + vi[k]] * gbase[c];
-                    if (g_vcolor) addf(&g_vcolor[c * P.V + vi[k]], bb[k] * gbase[c]);
+                    acc[k][3 + c] = (float)(bb[k] * gbase[c]);
                 }
         }
 
@@ -364,8 +373,46 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
                 const double gxc = gu[k] * fx / zc, gyc = gv[k] * fy / zc;
                 const double gzc = gzk[k] - gu[k] * fx * xc[k][0] / (zc * zc) - gv[k] * fy * xc[k][1] / (zc * zc);
 #pragma unroll
-                for (int j = 0; j < 3; ++j)
-                    addf(&g_verts[j * P.V + vi[k]], R[j] * gxc + R[3 + j] * gyc + R[6 + j] * gzc);
+                for (int j = 0; j < 3; ++j) acc[k][j] = (float)(R[j] * gxc + R[3 + j] * gyc + R[6 + j] * gzc);
+            }
+        }
+    }
+    // Pixels of one face are runs of neighbouring lanes (a triangle meets a row in an
+    // interval): a segmented sum over each run leaves the run's total in its last lane,
+    // which alone adds it to the face's corners (one set of atomics per run).
+    {
+        const int lane = threadIdx.x & 63;
+        const int prev = __shfl_up(f, 1, 64);
+        const unsigned long long heads = __ballot(lane == 0 || prev != f);
+        const unsigned long long upto = lane == 63 ? ~0ull : ((2ull << lane) - 1ull);
+        const int start = 63 - __builtin_clzll(heads & upto);
+        const bool tail = lane == 63 || ((heads >> (lane + 1)) & 1ull);
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+#pragma unroll
+            for (int j = 0; j < 11; ++j) {
+                float x = acc[k][j];
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const float y = __shfl_up(x, d, 64);
+                    if (lane - d >= start) x += y;
+                }
+                acc[k][j] = x;
+            }
+        if (tail && f >= 0) {
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    if (g_verts && acc[k][j] != 0.0f) unsafeAtomicAdd(&g_verts[j * P.V + vi[k]], acc[k][j]);
+                    if (g_vcolor && acc[k][3 + j] != 0.0f) unsafeAtomicAdd(&g_vcolor[j * P.V + vi[k]], acc[k][3 + j]);
+                    if (g_vnormal && acc[k][6 + j] != 0.0f)
+                        unsafeAtomicAdd(&g_vnormal[j * P.V + vi[k]], acc[k][6 + j]);
+                }
+                if (g_uv) {
+                    if (acc[k][9] != 0.0f) unsafeAtomicAdd(&g_uv[ti[k]], acc[k][9]);
+                    if (acc[k][10] != 0.0f) unsafeAtomicAdd(&g_uv[P.Vt + ti[k]], acc[k][10]);
+                }
             }
         }
     }
@@ -374,7 +421,7 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
         for (int i = 0; i < 13; ++i) {
-            float s = (float)gl[i];
+            float s = gl[i];
 #pragma unroll
             for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
             if (lane == 0) s_light[i][wave] = s;
