@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--cpu-tiles", type=int, default=0,
                     help="tiles in the oracle's timed sample (0: every tile of the view)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--batch-views", action="store_true",
+                    help="one step = every view of the workload with one batched projection")
     return ap.parse_args()
 
 
@@ -107,6 +109,9 @@ def main():
 
     torch.cuda.set_device(0)
     scene = scenes.make_scene(args.config)
+    if args.batch_views:
+        main_batch(args, scene)
+        return
     view = args.view % len(scene.views)
     ds = DeviceScene(scene)
     r = Renderer(ds)
@@ -231,6 +236,75 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(scene, view, args.cpu_tiles)
+    print(json.dumps(out), flush=True)
+
+
+def main_batch(args, scene):
+    """Every view of the workload per step: one gm_project_gaussians_multi for all
+    views, then per view the lists, composite forward and backward.  Also times the
+    batched projection against the per-view projection loop it replaces."""
+    import torch
+    from differentiable_hybrid_mesh_amd.pipeline import DeviceScene, Renderer
+    ds = DeviceScene(scene)
+    r = Renderer(ds)
+    views = list(range(len(scene.views)))
+    grads = [ds.grads(v) for v in views]
+    r.fit_lists_views(views)
+    for _ in range(max(args.warmup, 1)):
+        r.views_step_async(views, grads)
+    torch.cuda.synchronize()
+    if not r.read_counts():
+        raise RuntimeError("a list outgrew its capacity after fitting")
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(args.steps):
+        r.views_step_async(views, grads)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    if not r.read_counts():
+        raise RuntimeError("a list outgrew its capacity inside the timed region")
+    ms = t0.elapsed_time(t1) / args.steps
+    px = len(views) * scene.width * scene.height
+    value = px / (ms * 1e-3) / 1e6
+
+    # the projection alone: batched call vs one call per view (events on the stream)
+    N, d = scene.N, scene.sh_degree
+    shb = 12 * (d + 1) ** 2 if d >= 0 else 12
+    per_in = 12 + 16 + 12 + 4 + shb
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record()
+    for _ in range(args.steps):
+        r.project_views(views)
+    e[1].record()
+    for _ in range(args.steps):
+        for v in views:
+            r.project(v)
+    e[2].record()
+    torch.cuda.synchronize()
+    ms_multi = e[0].elapsed_time(e[1]) / args.steps
+    ms_loop = e[1].elapsed_time(e[2]) / args.steps
+    b_multi = N * (per_in + 64 * len(views))
+    b_loop = len(views) * N * (per_in + 64)
+    ach = b_multi / (ms_multi * 1e-3) / 1e9
+    out = {
+        "metric": "hybrid render Mpixels/s fwd+bwd at 1080p",
+        "value": round(value, 3), "unit": "Mpixels/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded PCG64 scene generators)",
+        "config": {"workload": f"{args.config}: {WORKLOADS[args.config]}; all {len(views)} views per step, "
+                               "one batched projection", "views": len(views), "width": scene.width,
+                   "height": scene.height, "faces": scene.F, "gaussians": N, "parallelism": "single GPU"},
+        "roofline": {"kernel": "k_project_gaussians_multi", "bound": "hbm", "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "units": {"algorithmic_bytes": b_multi}, "launch_ms": round(ms_multi, 4)},
+        "projection": {"batched_ms": round(ms_multi, 4), "per_view_loop_ms": round(ms_loop, 4),
+                       "batched_algorithmic_bytes": b_multi, "loop_algorithmic_bytes": b_loop,
+                       "speedup": round(ms_loop / ms_multi, 3)},
+        "wall_s": round(wall, 3),
+    }
     print(json.dumps(out), flush=True)
 
 

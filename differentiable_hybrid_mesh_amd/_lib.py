@@ -44,6 +44,7 @@ class GmMesh(C.Structure):
 
 
 EXPORTS = ["gm_bin_triangles_ws", "gm_bin_triangles", "gm_raster_zbuffer", "gm_project_gaussians",
+           "gm_project_gaussians_multi",
            "gm_sort_tile_keys_ws", "gm_sort_tile_keys", "gm_composite_hybrid_fwd",
            "gm_composite_hybrid_bwd", "gm_project_gaussians_bwd", "gm_mesh_bwd", "gm_mipmaps_floats",
            "gm_build_mipmaps", "gm_last_error", "gm_version"]
@@ -67,6 +68,7 @@ def lib():
     L.gm_bin_triangles.argtypes = [cam, mesh, P, P, P, I64, P, P, SZ, P]
     L.gm_raster_zbuffer.argtypes = [cam, mesh, P, P, P, P, P, P, P]
     L.gm_project_gaussians.argtypes = [cam, I32, P, P, P, P, P, I32, P, P]
+    L.gm_project_gaussians_multi.argtypes = [cam, I32, I32, P, P, P, P, P, I32, P, P]
     L.gm_sort_tile_keys_ws.argtypes = [I32, I64, I32, I32]
     L.gm_sort_tile_keys_ws.restype = SZ
     L.gm_sort_tile_keys.argtypes = [cam, I32, P, P, F32, P, P, I64, P, P, SZ, P]
@@ -84,7 +86,8 @@ def lib():
     for name in EXPORTS:
         if not hasattr(L, name):
             raise ImportError(f"{LIB_PATH} does not export {name}")
-    for name in ("gm_bin_triangles", "gm_raster_zbuffer", "gm_project_gaussians", "gm_sort_tile_keys",
+    for name in ("gm_bin_triangles", "gm_raster_zbuffer", "gm_project_gaussians", "gm_project_gaussians_multi",
+                 "gm_sort_tile_keys",
                  "gm_composite_hybrid_fwd", "gm_composite_hybrid_bwd", "gm_project_gaussians_bwd",
                  "gm_mesh_bwd", "gm_build_mipmaps"):
         getattr(L, name).restype = C.c_int
@@ -128,6 +131,13 @@ def gm_raster_zbuffer(cam, mesh, vscreen, tile_offsets, tile_tris, face_id, dept
 def gm_project_gaussians(cam, N, means, quats, scales, opacity, sh, sh_degree, rec, stream):
     check(lib().gm_project_gaussians(C.byref(cam), int(N), ptr(means), ptr(quats), ptr(scales),
                                      ptr(opacity), ptr(sh), int(sh_degree), ptr(rec), stream))
+
+
+def gm_project_gaussians_multi(cams, N, means, quats, scales, opacity, sh, sh_degree, rec, stream):
+    """cams: sequence of GmCamera; rec holds len(cams) * N records."""
+    arr = (GmCamera * max(len(cams), 1))(*cams)
+    check(lib().gm_project_gaussians_multi(arr, len(cams), int(N), ptr(means), ptr(quats), ptr(scales),
+                                           ptr(opacity), ptr(sh), int(sh_degree), ptr(rec), stream))
 
 
 def gm_sort_tile_keys_ws(N, cap, width, height) -> int:

@@ -7,6 +7,8 @@
 // that every implementation of the same order gets the same bits.
 #pragma clang fp contract(off)
 
+#include <algorithm>
+
 #include "gm_internal.h"
 #include "gm_sh.h"
 
@@ -14,24 +16,23 @@ namespace gm {
 
 constexpr float EPS2D = 0.3f;  // px^2: low-pass dilation, also the eps of the depth model
 
-__global__ void __launch_bounds__(256)
-k_project_gaussians(DevCamera cam, int N, const float* __restrict__ means,
-                    const float* __restrict__ quats, const float* __restrict__ scales,
-                    const float* __restrict__ opacity, const float* __restrict__ sh, int sh_degree,
-                    float* __restrict__ rec)
-{
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= N) return;
-    const float* W = cam.R;
-    const float mx = means[i], my = means[N + i], mz = means[2 * N + i];
-    const float xc = ((W[0] * mx + W[1] * my) + W[2] * mz) + cam.t[0];
-    const float yc = ((W[3] * mx + W[4] * my) + W[5] * mz) + cam.t[1];
-    const float zc = ((W[6] * mx + W[7] * my) + W[8] * mz) + cam.t[2];
-    bool ok = zc >= cam.near_z;
+// World covariance Sigma = M M^T, M = R(q / |q|) diag(s): view independent.
+struct WorldGauss {
+    float mx, my, mz;
+    float S[9];
+    bool ok;  // |q| > 0
+};
 
+__device__ inline WorldGauss world_gaussian(int N, int i, const float* __restrict__ means,
+                                            const float* __restrict__ quats, const float* __restrict__ scales)
+{
+    WorldGauss g;
+    g.mx = means[i];
+    g.my = means[N + i];
+    g.mz = means[2 * N + i];
     float qw = quats[i], qx = quats[N + i], qy = quats[2 * N + i], qz = quats[3 * N + i];
     const float qq = ((qw * qw + qx * qx) + qy * qy) + qz * qz;
-    if (!(qq > 0.0f)) ok = false;
+    g.ok = qq > 0.0f;
     const float qn = sqrtf(qq);
     qw = qw / qn;
     qx = qx / qn;
@@ -53,15 +54,29 @@ k_project_gaussians(DevCamera cam, int N, const float* __restrict__ means,
     for (int r = 0; r < 3; ++r)
 #pragma unroll
         for (int c = 0; c < 3; ++c) M[r * 3 + c] = Rq[r * 3 + c] * s[c];
-    float S[9];  // Sigma = M M^T (world)
 #pragma unroll
     for (int r = 0; r < 3; ++r)
 #pragma unroll
         for (int c = r; c < 3; ++c) {
             const float v = (M[r * 3 + 0] * M[c * 3 + 0] + M[r * 3 + 1] * M[c * 3 + 1]) + M[r * 3 + 2] * M[c * 3 + 2];
-            S[r * 3 + c] = v;
-            S[c * 3 + r] = v;
+            g.S[r * 3 + c] = v;
+            g.S[c * 3 + r] = v;
         }
+    return g;
+}
+
+// The record of Gaussian i in one view.  shc: its colour coefficients, read once by
+// the caller ([k][3] for degree d >= 0, RGB for d = -1).
+__device__ inline void project_view(const DevCamera& cam, const WorldGauss& g, float opacity, const float* shc,
+                                    int sh_degree, float* __restrict__ rec_i)
+{
+    const float* W = cam.R;
+    const float mx = g.mx, my = g.my, mz = g.mz;
+    const float xc = ((W[0] * mx + W[1] * my) + W[2] * mz) + cam.t[0];
+    const float yc = ((W[3] * mx + W[4] * my) + W[5] * mz) + cam.t[1];
+    const float zc = ((W[6] * mx + W[7] * my) + W[8] * mz) + cam.t[2];
+    bool ok = zc >= cam.near_z && g.ok;
+    const float* S = g.S;
     float A[9], C[9];  // Sigma_c = (W Sigma) W^T
 #pragma unroll
     for (int r = 0; r < 3; ++r)
@@ -125,9 +140,9 @@ k_project_gaussians(DevCamera cam, int N, const float* __restrict__ means,
     // colour (value arithmetic, fp32)
     float col[3];
     if (sh_degree < 0) {
-        col[0] = sh[i];
-        col[1] = sh[N + i];
-        col[2] = sh[2 * N + i];
+        col[0] = shc[0];
+        col[1] = shc[1];
+        col[2] = shc[2];
     } else {
         float cw[3];
 #pragma unroll
@@ -143,17 +158,67 @@ k_project_gaussians(DevCamera cam, int N, const float* __restrict__ means,
 #pragma unroll
         for (int ch = 0; ch < 3; ++ch) {
             float acc = 0.0f;
-            for (int k = 0; k < K; ++k) acc += Y[k] * sh[((size_t)k * 3 + ch) * N + i];
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                if (k < K) acc += Y[k] * shc[k * 3 + ch];
             acc += 0.5f;
             col[ch] = acc > 0.0f ? acc : 0.0f;
         }
     }
-    float4* o = reinterpret_cast<float4*>(rec + (size_t)i * GM_REC);
+    float4* o = reinterpret_cast<float4*>(rec_i);
     o[0] = make_float4(u, v, Q00, Q01);
-    o[1] = make_float4(Q11, opacity[i], col[0], col[1]);
+    o[1] = make_float4(Q11, opacity, col[0], col[1]);
     o[2] = make_float4(col[2], zc, g0, g1);
     o[3] = make_float4(sig, __int_as_float(r0 | (r1 << 16)), __int_as_float(r2 | (r3 << 16)),
                        __int_as_float(ntiles));
+}
+
+__device__ inline void load_colour(int N, int i, const float* __restrict__ sh, int sh_degree, float* shc)
+{
+    const int K = sh_degree < 0 ? 1 : (sh_degree + 1) * (sh_degree + 1);
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+#pragma unroll
+        for (int ch = 0; ch < 3; ++ch) shc[k * 3 + ch] = k < K ? sh[((size_t)k * 3 + ch) * N + i] : 0.0f;
+}
+
+__global__ void __launch_bounds__(256)
+k_project_gaussians(DevCamera cam, int N, const float* __restrict__ means,
+                    const float* __restrict__ quats, const float* __restrict__ scales,
+                    const float* __restrict__ opacity, const float* __restrict__ sh, int sh_degree,
+                    float* __restrict__ rec)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= N) return;
+    const WorldGauss g = world_gaussian(N, i, means, quats, scales);
+    float shc[48];
+    load_colour(N, i, sh, sh_degree, shc);
+    project_view(cam, g, opacity[i], shc, sh_degree, rec + (size_t)i * GM_REC);
+}
+
+// Several views of the same Gaussians: the inputs are read and the world covariance
+// formed once, then every view's record is written ([view][N][GM_REC]).  Each view's
+// record is computed by the same code as the single-view kernel, so it is bitwise
+// the same.
+constexpr int PROJ_MAX_VIEWS = 16;
+struct ViewSet {
+    DevCamera cam[PROJ_MAX_VIEWS];
+};
+
+__global__ void __launch_bounds__(256)
+k_project_gaussians_multi(ViewSet views, int nviews, int N, const float* __restrict__ means,
+                          const float* __restrict__ quats, const float* __restrict__ scales,
+                          const float* __restrict__ opacity, const float* __restrict__ sh, int sh_degree,
+                          float* __restrict__ rec)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= N) return;
+    const WorldGauss g = world_gaussian(N, i, means, quats, scales);
+    float shc[48];
+    load_colour(N, i, sh, sh_degree, shc);
+    const float o = opacity[i];
+    for (int v = 0; v < nviews; ++v)
+        project_view(views.cam[v], g, o, shc, sh_degree, rec + ((size_t)v * N + i) * GM_REC);
 }
 
 }  // namespace gm
@@ -176,5 +241,29 @@ extern "C" gm_status gm_project_gaussians(const gm_camera* cam, int32_t N, const
     k_project_gaussians<<<(unsigned)div_up(N, 256), 256, 0, stream>>>(dc, N, means, quats, scales, opacity,
                                                                       sh, sh_degree, rec);
     GM_LAUNCH_CHECK();
+    return GM_OK;
+}
+
+extern "C" gm_status gm_project_gaussians_multi(const gm_camera* cams, int32_t nviews, int32_t N, const float* means,
+                                                const float* quats, const float* scales, const float* opacity,
+                                                const float* sh, int32_t sh_degree, float* rec, hipStream_t stream)
+{
+    clear_error();
+    GM_ARG_CHECK(cams != nullptr && nviews >= 0, "cams is NULL or nviews negative");
+    for (int v = 0; v < nviews; ++v)
+        if (gm_status s = check_camera(&cams[v])) return s;
+    GM_ARG_CHECK(N >= 0, "N = %d is negative", N);
+    GM_ARG_CHECK(sh_degree >= -1 && sh_degree <= 3, "sh_degree %d outside -1..3", sh_degree);
+    if (N == 0 || nviews == 0) return GM_OK;
+    GM_ARG_CHECK(means && quats && scales && opacity && sh && rec, "an input or rec is NULL");
+    GM_ARG_CHECK(((uintptr_t)rec & 15) == 0, "rec must be 16-byte aligned");
+    for (int v0 = 0; v0 < nviews; v0 += PROJ_MAX_VIEWS) {
+        const int nv = std::min(PROJ_MAX_VIEWS, nviews - v0);
+        ViewSet vs{};
+        for (int v = 0; v < nv; ++v) vs.cam[v] = dev_camera(cams[v0 + v]);
+        k_project_gaussians_multi<<<(unsigned)div_up(N, 256), 256, 0, stream>>>(
+            vs, nv, N, means, quats, scales, opacity, sh, sh_degree, rec + (size_t)v0 * N * GM_REC);
+        GM_LAUNCH_CHECK();
+    }
     return GM_OK;
 }

@@ -94,6 +94,8 @@ class DeviceScene:
 class Renderer:
     """Per-view device buffers and the call sequence of one forward / backward."""
 
+    MAX_BATCH = 64  # views of one batched pass
+
     def __init__(self, ds: DeviceScene, pair_cap: Optional[int] = None, key_cap: Optional[int] = None):
         s = ds.scene
         self.ds = ds
@@ -112,6 +114,8 @@ class Renderer:
         self.depth = torch.empty((self.H, self.W), dtype=f32, device=dev)
         self.tile_dmax = torch.empty(self.T, dtype=f32, device=dev)
         self.rec = torch.empty((max(self.N, 1), G.GM_REC), dtype=f32, device=dev)
+        self._rec_own = self.rec
+        self.rec_views = None  # [views][N][GM_REC] of project_views()
         self.tile_ranges = torch.empty((self.T, 2), dtype=i32, device=dev)
         self.key_cap = key_cap if key_cap is not None else 8 * self.N + 1024
         self._alloc_keys(self.key_cap)
@@ -126,8 +130,11 @@ class Renderer:
         self.g_mesh_depth = torch.empty((self.H, self.W), dtype=f32, device=dev)
         self.n_pairs = 0
         self.n_keys = 0
-        self.counts = torch.zeros(2, dtype=torch.int64, device=dev)  # device: n_pairs, n_keys
-        self.counts_host = torch.zeros(2, dtype=torch.int64, pin_memory=True)
+        # device list lengths (n_pairs, n_keys), one row per view of a batched pass
+        self.counts_all = torch.zeros((self.MAX_BATCH, 2), dtype=torch.int64, device=dev)
+        self.counts_host = torch.zeros((self.MAX_BATCH, 2), dtype=torch.int64, pin_memory=True)
+        self.counts = self.counts_all[0]
+        self._rows = 1
         self.view = 0
         self.cull = True
 
@@ -148,6 +155,7 @@ class Renderer:
 
     def project(self, view: int):
         ds, s = self.ds, self.ds.scene
+        self.rec = self._rec_own
         G.gm_project_gaussians(ds.cams[view], self.N, ds.means, ds.quats, ds.scales, ds.opacity, ds.sh,
                                s.sh_degree, self.rec, _stream())
 
@@ -158,15 +166,17 @@ class Renderer:
                             self.key_cap, self.counts[1:2], self.ws_sort, _stream())
 
     def fetch_counts(self):
-        """Queue a copy of the two list lengths to pinned host memory (no wait)."""
-        self.counts_host.copy_(self.counts, non_blocking=True)
+        """Queue a copy of the list lengths to pinned host memory (no wait)."""
+        self.counts_host[: self._rows].copy_(self.counts_all[: self._rows], non_blocking=True)
 
     def read_counts(self) -> bool:
-        """After the stream has passed fetch_counts(): store the lengths, grow any list
-        that overflowed; True when both fitted."""
-        n_pairs, n_keys = (int(x) for x in self.counts_host.tolist())
-        if n_pairs < 0 or n_keys < 0:
+        """After the stream has passed fetch_counts(): store the lengths (the largest
+        over the views of a batched pass), grow any list that overflowed; True when
+        every list fitted."""
+        rows = self.counts_host[: self._rows]
+        if bool((rows < 0).any()):
             raise RuntimeError("list construction reported a failure (negative length)")
+        n_pairs, n_keys = (int(x) for x in rows.max(0).values.tolist())
         self.n_pairs, self.n_keys = n_pairs, n_keys
         ok = True
         if n_pairs > self.pair_cap:
@@ -244,10 +254,70 @@ class Renderer:
             out["uv"], out["tex"] = self.gm_uv[:, : ds.mesh.Vt], self.gm_mips[: S * S * 3].view(S, S, 3)
         return out
 
+    # -- several views -----------------------------------------------------------
+    def project_views(self, views):
+        """Project the Gaussians into every view of ``views`` in one pass
+        (gm_project_gaussians_multi: the parameters are read once for all views);
+        use_view(k) then makes the k-th view's records the current ones."""
+        ds, s = self.ds, self.ds.scene
+        nv = len(views)
+        if self.rec_views is None or self.rec_views.shape[0] < nv:
+            self.rec_views = torch.empty((nv, max(self.N, 1), G.GM_REC), dtype=torch.float32, device=ds.device)
+        G.gm_project_gaussians_multi([ds.cams[v] for v in views], self.N, ds.means, ds.quats, ds.scales,
+                                     ds.opacity, ds.sh, s.sh_degree, self.rec_views, _stream())
+
+    def use_view(self, k: int):
+        """Select the records of the k-th view of the last project_views() and the k-th
+        row of list lengths."""
+        self.rec = self.rec_views[k]
+        self.counts = self.counts_all[k]
+
+    def _single(self):
+        self.rec = self._rec_own
+        self.counts = self.counts_all[0]
+        self._rows = 1
+
+    def views_step_async(self, views, grads, cull: bool = True, backward: bool = True, hook=None):
+        """Forward (+ backward) of several views with one batched projection; no
+        synchronisation.  grads[k] holds view k's upstream gradients.  The lists are
+        rebuilt per view in the same buffers, so only the last view's outputs remain;
+        hook(k), if given, runs after view k (e.g. to copy its outputs).  Check the
+        lengths with read_counts() once the stream has run."""
+        if len(views) > self.MAX_BATCH:
+            raise ValueError(f"at most {self.MAX_BATCH} views per batch")
+        self.project_views(views)
+        self._rows = len(views)
+        for k, v in enumerate(views):
+            self.use_view(k)
+            self.view, self.cull = v, cull
+            self.bin_and_zbuffer(v)
+            self.sort(v, cull)
+            self.composite_fwd(v)
+            if backward:
+                self.composite_bwd(v, grads[k]["rgb"], grads[k].get("depth"), grads[k].get("alpha"))
+            if hook is not None:
+                hook(k)
+        self.fetch_counts()
+
+    def fit_lists_views(self, views, cull: bool = True):
+        """fit_lists() for a batched pass: grow the lists until every view's fit."""
+        while True:
+            self.project_views(views)
+            self._rows = len(views)
+            for k, v in enumerate(views):
+                self.use_view(k)
+                self.bin_and_zbuffer(v)
+                self.sort(v, cull)
+            self.fetch_counts()
+            torch.cuda.current_stream().synchronize()
+            if self.read_counts():
+                return
+
     # -- whole passes -----------------------------------------------------------
     def forward_async(self, view: int = 0, cull: bool = True):
         """Queue one forward pass and the copy of the list lengths; no synchronisation.
         The outputs are valid once read_counts() returns True for this pass."""
+        self._single()
         self.view, self.cull = view, cull
         self.bin_and_zbuffer(view)
         self.project(view)
@@ -257,6 +327,7 @@ class Renderer:
 
     def fit_lists(self, view: int = 0, cull: bool = True):
         """Run the list-producing calls (no compositing) until both lists fit."""
+        self._single()
         while True:
             self.bin_and_zbuffer(view)
             self.project(view)

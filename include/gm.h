@@ -163,6 +163,23 @@ gm_status gm_project_gaussians(const gm_camera* cam, int32_t N, const float* mea
                                const float* quats, const float* scales, const float* opacity,
                                const float* sh, int32_t sh_degree, float* rec, hipStream_t stream);
 
+/* gm_project_gaussians_multi — the projection of the same Gaussians into several
+ * views in one pass.  README "Limitations and Todos": rendering a batch of camera
+ * poses is listed as not yet supported; the world-space work (reading the parameters and colour
+ * coefficients, normalising q, forming Sigma) does not depend on the view, so it is
+ * done once per Gaussian and every view's record follows from it.
+ *
+ * cams: host array of nviews cameras.  Inputs as gm_project_gaussians.  Output rec
+ * [nviews][N][GM_REC]: the records of view v start at rec + v N GM_REC and are
+ * bitwise equal to those gm_project_gaussians writes for cams[v].  Views are
+ * processed 16 to a launch.  GM_ERR_ARG on a NULL or invalid camera, negative N or
+ * nviews, sh_degree outside -1..3 or misaligned rec; nviews = 0 or N = 0 does
+ * nothing.  Asynchronous on stream.
+ * ------------------------------------------------------------------------- */
+gm_status gm_project_gaussians_multi(const gm_camera* cams, int32_t nviews, int32_t N, const float* means,
+                                     const float* quats, const float* scales, const float* opacity,
+                                     const float* sh, int32_t sh_degree, float* rec, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * 4. gm_sort_tile_keys — occlusion cull, per-tile lists in depth order.
  * README "Hybrid rendering": Gaussians are composited "in the usual sorted 3DGS

@@ -89,3 +89,15 @@ def test_argument_errors_before_any_launch(G):
     assert L.gm_project_gaussians_bwd(C.byref(cam), 1, 16, 16, 16, None, 16, 0, 16, 16, *bw, None, 16,
                                       None) == G.GM_ERR_ARG
     assert b"opacity" in L.gm_last_error()
+    # batched projection: NULL camera array, negative view count, an invalid camera
+    # among valid ones, degree out of range, misaligned rec
+    cams = (G.GmCamera * 3)(_cam(G), _cam(G, 64, 0), _cam(G))
+    assert L.gm_project_gaussians_multi(None, 1, 1, 16, 16, 16, 16, 16, 0, 16, None) == G.GM_ERR_ARG
+    assert L.gm_project_gaussians_multi(cams, -1, 1, 16, 16, 16, 16, 16, 0, 16, None) == G.GM_ERR_ARG
+    assert L.gm_project_gaussians_multi(cams, 3, 1, 16, 16, 16, 16, 16, 0, 16, None) == G.GM_ERR_ARG
+    assert L.gm_project_gaussians_multi(cams, 1, 1, 16, 16, 16, 16, 16, 4, 16, None) == G.GM_ERR_ARG
+    assert b"sh_degree" in L.gm_last_error()
+    assert L.gm_project_gaussians_multi(cams, 1, 1, 16, 16, 16, 16, 16, 0, 17, None) == G.GM_ERR_ARG
+    # nothing to do: no views, or no Gaussians (no pointer is touched)
+    assert L.gm_project_gaussians_multi(cams, 0, 5, None, None, None, None, None, 0, None, None) == G.GM_OK
+    assert L.gm_project_gaussians_multi(cams, 1, 0, None, None, None, None, None, 0, None, None) == G.GM_OK
