@@ -2,7 +2,7 @@
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  It loads ``liboracle.so`` built from
-``gm_oracle.c``, ``project_bwd.c`` and ``mesh_bwd.c`` with gcc (``-O2 -fopenmp
+``gm_oracle.c``, ``project_bwd.c``, ``mesh_bwd.c`` and ``antialias.c`` with gcc (``-O2 -fopenmp
 -ffp-contract=off``) and shares no code with the HIP library; the two meet only at
 the seeded inputs of ``scenes``.
 
@@ -21,7 +21,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRCS = [os.path.join(_HERE, "gm_oracle.c"), os.path.join(_HERE, "project_bwd.c"),
-         os.path.join(_HERE, "mesh_bwd.c")]
+         os.path.join(_HERE, "mesh_bwd.c"), os.path.join(_HERE, "antialias.c")]
 _LIB = os.path.join(_HERE, "liboracle.so")
 NREC = 13
 
@@ -68,7 +68,8 @@ class Comp(C.Structure):
                 ("T_final", C.c_void_p), ("n_last", C.c_void_p), ("n_incl", C.c_void_p),
                 ("margin", C.c_void_p), ("clamp_margin", C.c_void_p), ("grad", C.c_void_p),
                 ("g_mesh_rgb", C.c_void_p), ("g_mesh_depth", C.c_void_p),
-                ("pairs_evaluated", C.c_void_p)]
+                ("pairs_evaluated", C.c_void_p), ("layer", C.c_void_p), ("g_layer", C.c_void_p),
+                ("T_back", C.c_void_p), ("n_last_back", C.c_void_p)]
 
 
 _lib = None
@@ -108,6 +109,10 @@ def lib():
         _lib.oc_project_bwd.argtypes = [cam, I, P, P, P, P, I, P, P, P, P, P, P, P]
         _lib.oc_mesh_fwd64.argtypes = [cam, C.POINTER(MeshB), I, P, P, P, P]
         _lib.oc_mesh_bwd.argtypes = [cam, C.POINTER(MeshB), I, P, P, P, P, P, P, P, P, P, P]
+        _lib.oc_vscreen_bwd.argtypes = [cam, C.POINTER(MeshB), P, P]
+        _lib.oc_edge_adjacency.argtypes = [I, P, P]
+        _lib.oc_antialias.argtypes = [cam, I, I, P, P, P, P, P, P, P, P, P]
+        _lib.oc_antialias_bwd.argtypes = [cam, I, I, P, P, P, P, P, P, P, P, P, P, P]
     return _lib
 
 
@@ -308,8 +313,11 @@ def shade_pixels(meshref: MeshRef, pix, face_id):
 
 
 def composite(cam: Camera, meshref: Optional[MeshRef], rec64, tiles, offsets, ids, face_id, depth,
-              bg=(1.0, 1.0, 1.0), softness=1.0, grads=None):
-    """Forward (both layer forms) and, when ``grads`` is given, the reverse mode."""
+              bg=(1.0, 1.0, 1.0), softness=1.0, grads=None, layer=None):
+    """Forward (both layer forms) and, when ``grads`` is given, the reverse mode.
+    With ``layer`` ([H][W][6] antialiased mesh layer from ``antialias``) the mesh
+    enters through it and the general two-layer form is computed, forward and
+    reverse (``g_layer``, ``T_back``, ``n_last_back`` are returned as well)."""
     H, W = cam.height, cam.width
     N = rec64.shape[0]
     rec64 = _c(rec64, np.float64)
@@ -354,6 +362,14 @@ def composite(cam: Camera, meshref: Optional[MeshRef], rec64, tiles, offsets, id
         setattr(a, k, _p(out[k]))
     a.out_depth = _p(out["depth"])
     a.pairs_evaluated = _p(out["pairs"])
+    if layer is not None:
+        layer = _c(layer, np.float64)
+        keep.append(layer)
+        out["g_layer"] = np.zeros((H, W, 6))
+        out["T_back"] = np.full((H, W), np.nan)
+        out["n_last_back"] = np.full((H, W), -1, np.int32)
+        a.layer, a.g_layer = _p(layer), _p(out["g_layer"])
+        a.T_back, a.n_last_back = _p(out["T_back"]), _p(out["n_last_back"])
     lib().oc_composite(C.byref(a))
     out["pairs"] = int(out["pairs"][0])
     return out
@@ -383,14 +399,30 @@ def tiles_of_pixels(cam: Camera, pix: Sequence[int]) -> np.ndarray:
 # whole view
 # ---------------------------------------------------------------------------
 
+def _with_neighbour_tiles(cam: Camera, tiles) -> np.ndarray:
+    TX, TY, _ = n_tiles(cam)
+    t = np.asarray(tiles, np.int64)
+    tx, ty = t % TX, t // TX
+    out = set()
+    for dy in (-1, 0, 1):
+        for dx in (-1, 0, 1):
+            x, y = tx + dx, ty + dy
+            ok = (x >= 0) & (x < TX) & (y >= 0) & (y < TY)
+            out.update((y[ok] * TX + x[ok]).tolist())
+    return np.array(sorted(out), np.int32)
+
+
 def render_view(scene, view_index: int = 0, tiles=None, cull: bool = True, backward: bool = True,
-                prefilter: Optional[bool] = None, grads=None, mips=None):
+                prefilter: Optional[bool] = None, grads=None, mips=None, antialias: bool = False):
     """The whole definition for one view on ``tiles`` (all tiles when None).
 
     Returns a dict with the z-buffer, records, per-tile lists (pre- and post-cull),
     the composite outputs and, with ``backward``, the gradients of the 13 record
     fields and of the mesh colour / depth, for the upstream gradients ``grads``
-    (the scene's own when None)."""
+    (the scene's own when None).  With ``antialias`` the mesh enters through the
+    antialiased layer (``layer``, with ``adj`` and ``colour``); the z-buffer then
+    also covers the neighbouring tiles, whose border pixels the pairs reach, and the
+    composite's reverse mode returns ``g_layer``."""
     cam = camera(scene, view_index)
     TX, TY, T = n_tiles(cam)
     tiles = np.arange(T, dtype=np.int32) if tiles is None else np.asarray(tiles, np.int32)
@@ -399,7 +431,8 @@ def render_view(scene, view_index: int = 0, tiles=None, cull: bool = True, backw
     res = {"cam": cam, "tiles": tiles}
     if scene.F > 0:
         vs = project_vertices(cam, scene.verts)
-        zb = zbuffer(cam, vs, scene.faces, scene.face_mask, tiles=tiles, prefilter=prefilter)
+        zt = _with_neighbour_tiles(cam, tiles) if antialias else tiles
+        zb = zbuffer(cam, vs, scene.faces, scene.face_mask, tiles=zt, prefilter=prefilter)
     else:
         vs = np.zeros((3, 0), np.float32)
         zb = {"face_id": np.full((scene.height, scene.width), -1, np.int32),
@@ -415,6 +448,23 @@ def render_view(scene, view_index: int = 0, tiles=None, cull: bool = True, backw
     order = depth_order(pg["rec"], pg["valid"])
     res["order"] = order
     dm = np.where(np.isnan(zb["tile_dmax"]), np.inf, zb["tile_dmax"]).astype(np.float32)
+    if scene.texture is not None and mips is None:
+        mips = build_mips(scene.texture)
+    mref = MeshRef(cam, scene, vs, mips=mips) if scene.F > 0 else None
+    layer = None
+    if antialias:
+        if scene.F > 0:
+            adj = edge_adjacency(scene.faces)
+            colour = surface_colours(mref, zb["face_id"])
+            layer = aa_layer(cam, vs.astype(np.float64), scene.faces, scene.face_mask, adj, zb["face_id"],
+                             zb["depth"], colour)
+            res.update(adj=adj, colour=colour)
+        else:
+            layer = np.zeros((scene.height, scene.width, 6))
+            layer[..., 5] = np.inf
+        res["layer"] = layer
+        dm = aa_tile_dmax(cam, dm, layer)
+        res["tile_dmax_aa"] = dm
     off, ids, cq = tile_lists(cam, pg["rec"], pg["rect"], order, tiles,
                               tile_dmax=dm if cull else None, softness=scene.softness)
     res["lists_pre"] = (off, ids, cq)
@@ -423,17 +473,105 @@ def render_view(scene, view_index: int = 0, tiles=None, cull: bool = True, backw
     else:
         off2, ids2 = off, ids
     res["lists"] = (off2, ids2)
-    if scene.texture is not None and mips is None:
-        mips = build_mips(scene.texture)
-    mref = MeshRef(cam, scene, vs, mips=mips) if scene.F > 0 else None
     rec64 = pg["rec"].astype(np.float64)
     g = None
     if backward:
         g = grads if grads is not None else scene.grads[view_index]
     comp = composite(cam, mref, rec64, tiles, off2, ids2, zb["face_id"], zb["depth"],
-                     bg=scene.bg, softness=scene.softness, grads=g)
+                     bg=scene.bg, softness=scene.softness, grads=g, layer=layer)
     res["comp"] = comp
     return res
+
+
+# ---------------------------------------------------------------------------
+# analytic edge antialiasing (antialias.c)
+# ---------------------------------------------------------------------------
+
+def edge_adjacency(faces) -> np.ndarray:
+    """[3][F] int32: for edge k of face f (corner k+1 -> k+2) the one other face with
+    the same two vertex indices, -1 if none, -2 if several."""
+    faces = _c(faces, np.int32)
+    F = faces.shape[1]
+    adj = np.zeros((3, max(F, 1)), np.int32)
+    lib().oc_edge_adjacency(F, _p(faces), _p(adj))
+    return adj[:, :F]
+
+
+def _aa_args(cam, vs, faces, mask, adj, face_id, depth, colour):
+    vs = _c(vs, np.float64)
+    faces = _c(faces, np.int32)
+    mask = _c(mask, np.uint8)
+    adj = _c(adj, np.int32)
+    face_id = _c(face_id, np.int32)
+    depth = _c(depth, np.float32)
+    colour = _c(colour, np.float64)
+    return vs, faces, mask, adj, face_id, depth, colour
+
+
+def antialias(cam: Camera, vs, faces, mask, adj, face_id, depth, colour, raw: bool = False):
+    """Antialiased mesh layer [H][W][6] = (M_rgb, M_D premultiplied, a_m, D_split) from
+    the z-buffer (face_id, fp32 depth), the surface colour at covered pixels
+    (colour [H][W][3]) and the screen vertices vs [3][V] (fp64; the fp32 buffer
+    upcast).  raw=True also returns [H][W][6] (w_self, w_left, w_right, w_up,
+    w_down, raw coverage)."""
+    H, W = cam.height, cam.width
+    args = _aa_args(cam, vs, faces, mask, adj, face_id, depth, colour)
+    vs, faces = args[0], args[1]
+    layer = np.zeros((H, W, 6))
+    rw = np.zeros((H, W, 6)) if raw else None
+    lib().oc_antialias(C.byref(cam), vs.shape[1], faces.shape[1], *(_p(x) for x in args), _p(layer), _p(rw))
+    return (layer, rw) if raw else layer
+
+
+aa_layer = antialias  # the name render_view's flag shadows
+
+
+def antialias_bwd(cam: Camera, vs, faces, mask, adj, face_id, depth, colour, g_layer) -> dict:
+    """Reverse mode of ``antialias``: dL/d(colour) [H][W][3], dL/dD [H][W] (at covered
+    pixels' own centres) and dL/d(u, v) of the screen vertices [2][V]."""
+    H, W = cam.height, cam.width
+    args = _aa_args(cam, vs, faces, mask, adj, face_id, depth, colour)
+    vs, faces = args[0], args[1]
+    V = vs.shape[1]
+    out = {"colour": np.zeros((H, W, 3)), "depth": np.zeros((H, W)), "vs": np.zeros((2, max(V, 1)))}
+    g_layer = _c(g_layer, np.float64)
+    lib().oc_antialias_bwd(C.byref(cam), V, faces.shape[1], *(_p(x) for x in args), _p(g_layer),
+                           _p(out["colour"]), _p(out["depth"]), _p(out["vs"]))
+    out["vs"] = out["vs"][:, :V]
+    return out
+
+
+def surface_colours(meshref: "MeshRef", face_id) -> np.ndarray:
+    """[H][W][3] surface colour c at covered pixels (0 elsewhere)."""
+    fid = np.asarray(face_id).reshape(-1)
+    H, W = face_id.shape
+    pix = np.nonzero(fid >= 0)[0].astype(np.int32)
+    col = np.zeros((H * W, 3))
+    if len(pix):
+        cm, _ = shade_pixels(meshref, pix, fid[pix])
+        col[pix] = cm
+    return col.reshape(H, W, 3)
+
+
+def aa_tile_dmax(cam: Camera, tile_dmax, layer) -> np.ndarray:
+    """The cull bound with antialiasing: +inf on every tile that holds a pixel with
+    coverage below 1 (there the back layer is visible)."""
+    TX, TY, T = n_tiles(cam)
+    H, W = cam.height, cam.width
+    dm = np.array(tile_dmax, np.float32).copy()
+    low = np.zeros((TY * 16, TX * 16), bool)
+    low[:H, :W] = layer[..., 4] < 1.0
+    part = low.reshape(TY, 16, TX, 16).any(axis=(1, 3)).reshape(-1)
+    dm[part] = np.inf
+    return dm
+
+
+def vscreen_bwd(cam: Camera, mesh: "MeshB64", g_vs) -> np.ndarray:
+    """dL/d(world vertex) [3][V] from dL/d(u, v) [2][V] through the fp64 projection."""
+    g_vs = _c(g_vs, np.float64)
+    out = np.zeros((3, mesh.struct.V))
+    lib().oc_vscreen_bwd(C.byref(cam), C.byref(mesh.struct), _p(g_vs), _p(out))
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -778,6 +778,11 @@ typedef struct {
     double* g_mesh_rgb;         /* [H][W][3] */
     double* g_mesh_depth;       /* [H][W] */
     long long* pairs_evaluated; /* scalar */
+    /* antialiased mesh layer (NULL: binary coverage from face_id / depth / mesh) */
+    const double* layer;        /* [H][W][6]: M_rgb, M_D (premultiplied), a_m, D_split */
+    double* g_layer;            /* [H][W][6] dL/d(layer) (written when g_rgb is given) */
+    double* T_back;             /* [H][W] back-layer transmittance (may be NULL) */
+    int* n_last_back;           /* [H][W] index + 1 of the back layer's last included entry */
 } oc_comp;
 
 typedef struct {
@@ -813,6 +818,157 @@ static void eval_pair(const double* r, double px, double py, int on_mesh, double
 
 static double reld(double x, double thr) { return fabs(x - thr) / thr; }
 
+/* One pixel with an antialiased mesh layer: the general two-layer form
+ * C = C_F + T_F (M + (1 - a_m)(C_B + T_B bg)), alpha = 1 - T_F (1 - a_m) T_B,
+ * depth = Z_F + T_F (M_D + (1 - a_m) Z_B), with M, M_D the premultiplied mesh colour
+ * and depth.  Both layers follow the 3DGS rules on their own (skip below 1/255,
+ * stop before T < 1e-4).  The back layer is composited only where it is visible
+ * (a_m < 1 and a finite split depth); elsewhere it is empty (C_B = 0, Z_B = 0,
+ * T_B = 1).  The reverse mode is exact for both layers: the back layer sees the
+ * upstream gradients scaled by k = T_F (1 - a_m), with behind it bg (depth 0) and
+ * the alpha term; per entry dL/dalpha = f dL/dalpha_F + (1 - f) dL/dalpha_B and
+ * dL/df = alpha (dL/dalpha_F - dL/dalpha_B). */
+static void composite_pixel_aa(const oc_comp* a, int p, double pu, double pv, long long o0, int n,
+                               oc_entry* entF, oc_entry* entB, double* daFj, double* daBj,
+                               long long* pairs_total)
+{
+    const double thr_skip = 1.0 / 255.0, thr_stop = 1e-4;
+    const double* L = a->layer + 6 * (size_t)p;
+    double Mc[3] = {L[0], L[1], L[2]}, MD = L[3], am = L[4], D = L[5];
+    int on = isfinite(D);
+    double TF = 1.0, TB = 1.0, CF[3] = {0, 0, 0}, CB[3] = {0, 0, 0}, ZF = 0, ZB = 0;
+    int aliveF = 1, aliveB = on && am < 1.0, lastF = 0, lastB = 0, nF = 0, nB = 0;
+    double mg = INFINITY, cmg = INFINITY;
+    for (int j = 0; j < n && (aliveF || aliveB); ++j) {
+        const double* r = a->rec + (size_t)a->ids[o0 + j] * OC_NREC;
+        double al, ao, G, f, s, dx, dy;
+        eval_pair(r, pu, pv, on, D, a->softness, &al, &ao, &G, &f, &s, &dx, &dy);
+        ++*pairs_total;
+        for (int layer = 0; layer < 2; ++layer) {
+            int* alive = layer == 0 ? &aliveF : &aliveB;
+            if (!*alive) continue;
+            double aL = layer == 0 ? al * f : al * (1.0 - f);
+            double* T = layer == 0 ? &TF : &TB;
+            double m1 = reld(aL, thr_skip);
+            if (m1 < mg) mg = m1;
+            if (!(aL >= thr_skip)) continue;
+            double Tn = *T * (1.0 - aL);
+            double m2 = reld(Tn, thr_stop);
+            if (m2 < mg) mg = m2;
+            if (Tn < thr_stop) {
+                *alive = 0;
+                continue;
+            }
+            double w = aL * *T;
+            oc_entry* e = layer == 0 ? &entF[nF++] : &entB[nB++];
+            e->idx = j; e->T = *T; e->aF = aL; e->alpha = al; e->ao = ao; e->G = G; e->f = f; e->s = s;
+            e->dx = dx; e->dy = dy;
+            double m3 = reld(ao, 0.99);
+            if (m3 < cmg) cmg = m3;
+            double* Cc = layer == 0 ? CF : CB;
+            for (int c = 0; c < 3; ++c) Cc[c] += w * r[6 + c];
+            if (layer == 0) ZF += w * r[9]; else ZB += w * r[9];
+            *T = Tn;
+            if (layer == 0) lastF = j + 1; else lastB = j + 1;
+        }
+    }
+    double Y[3];
+    for (int c = 0; c < 3; ++c) {
+        Y[c] = CB[c] + TB * a->bg[c];
+        double v = CF[c] + TF * (Mc[c] + (1.0 - am) * Y[c]);
+        a->rgb[p * 3 + c] = v;
+        if (a->rgb2) a->rgb2[p * 3 + c] = v;
+    }
+    a->alpha[p] = 1.0 - TF * (1.0 - am) * TB;
+    a->out_depth[p] = ZF + TF * (MD + (1.0 - am) * ZB);
+    if (a->alpha2) a->alpha2[p] = a->alpha[p];
+    if (a->depth2) a->depth2[p] = a->out_depth[p];
+    a->T_final[p] = TF;
+    a->n_last[p] = lastF;
+    if (a->T_back) a->T_back[p] = TB;
+    if (a->n_last_back) a->n_last_back[p] = lastB;
+    if (a->n_incl) a->n_incl[p] = nF;
+    if (a->margin) a->margin[p] = mg;
+    if (a->clamp_margin) a->clamp_margin[p] = cmg;
+    if (!a->g_rgb) return;
+
+    /* ---- reverse mode ---- */
+    double GC[3] = {a->g_rgb[p * 3 + 0], a->g_rgb[p * 3 + 1], a->g_rgb[p * 3 + 2]};
+    double GZ = a->g_depth ? a->g_depth[p] : 0.0;
+    double GA = a->g_alpha ? a->g_alpha[p] : 0.0;
+    double k = TF * (1.0 - am);
+    /* dL/dT_F: everything behind the front layer */
+    double BF = GZ * (MD + (1.0 - am) * ZB) - GA * (1.0 - am) * TB;
+    for (int c = 0; c < 3; ++c) BF += GC[c] * (Mc[c] + (1.0 - am) * Y[c]);
+    /* dL/dT_B, scaled: the background behind the back layer */
+    double BB = -GA * k;
+    for (int c = 0; c < 3; ++c) BB += GC[c] * k * a->bg[c];
+    for (int j = 0; j < n; ++j) daFj[j] = daBj[j] = 0.0;
+    double acc = TF * BF;
+    for (int e = nF - 1; e >= 0; --e) {
+        const oc_entry* en = &entF[e];
+        const double* r = a->rec + (size_t)a->ids[o0 + en->idx] * OC_NREC;
+        double Vv = GC[0] * r[6] + GC[1] * r[7] + GC[2] * r[8] + GZ * r[9];
+        daFj[en->idx] = en->T * Vv - acc / (1.0 - en->aF);
+        acc += en->aF * en->T * Vv;
+    }
+    acc = TB * BB;
+    for (int e = nB - 1; e >= 0; --e) {
+        const oc_entry* en = &entB[e];
+        const double* r = a->rec + (size_t)a->ids[o0 + en->idx] * OC_NREC;
+        double Vv = k * (GC[0] * r[6] + GC[1] * r[7] + GC[2] * r[8] + GZ * r[9]);
+        daBj[en->idx] = en->T * Vv - acc / (1.0 - en->aF);
+        acc += en->aF * en->T * Vv;
+    }
+    double gD = 0.0;
+    int iF = 0, iB = 0;
+    for (int j = 0; j < n; ++j) {
+        const oc_entry* eF = (iF < nF && entF[iF].idx == j) ? &entF[iF++] : NULL;
+        const oc_entry* eB = (iB < nB && entB[iB].idx == j) ? &entB[iB++] : NULL;
+        if (!eF && !eB) continue;
+        const oc_entry* en = eF ? eF : eB; /* alpha, G, f, s, dx, dy are the same in both */
+        int id = a->ids[o0 + j];
+        const double* r = a->rec + (size_t)id * OC_NREC;
+        double wF = eF ? eF->aF * eF->T : 0.0, wB = eB ? eB->aF * eB->T : 0.0;
+        double gr[OC_NREC];
+        memset(gr, 0, sizeof(gr));
+        for (int c = 0; c < 3; ++c) gr[6 + c] = (wF + k * wB) * GC[c];
+        gr[9] = (wF + k * wB) * GZ;
+        double daF = daFj[j], daB = daBj[j];
+        double da = en->f * daF + (1.0 - en->f) * daB;
+        if (en->ao <= 0.99) {
+            gr[5] = en->G * da;
+            double Hh = r[5] * en->G * da;
+            gr[2] = -0.5 * en->dx * en->dx * Hh;
+            gr[3] = -en->dx * en->dy * Hh;
+            gr[4] = -0.5 * en->dy * en->dy * Hh;
+            gr[0] = Hh * (r[2] * en->dx + r[3] * en->dy);
+            gr[1] = Hh * (r[3] * en->dx + r[4] * en->dy);
+        }
+        if (on && a->softness > 0.0) {
+            double ds = en->alpha * phi(en->s) * (daF - daB);
+            double kap = 1.0 / (r[12] * a->softness);
+            gr[9] -= kap * ds;
+            gr[10] -= kap * ds * en->dx;
+            gr[11] -= kap * ds * en->dy;
+            gr[0] += kap * ds * r[10];
+            gr[1] += kap * ds * r[11];
+            gr[12] -= ds * en->s / r[12];
+            gD += kap * ds;
+        }
+        double* dst = a->grad + (size_t)id * OC_NREC;
+        for (int c = 0; c < OC_NREC; ++c) {
+#pragma omp atomic
+            dst[c] += gr[c];
+        }
+    }
+    double* gl = a->g_layer + 6 * (size_t)p;
+    for (int c = 0; c < 3; ++c) gl[c] = TF * GC[c];
+    gl[3] = TF * GZ;
+    gl[4] = TF * (GA * TB - (GC[0] * Y[0] + GC[1] * Y[1] + GC[2] * Y[2]) - GZ * ZB);
+    gl[5] = gD;
+}
+
 void oc_composite(oc_comp* a)
 {
     const oc_camera* cam = a->cam;
@@ -827,10 +983,21 @@ void oc_composite(oc_comp* a)
         long long o0 = a->offsets[k], o1 = a->offsets[k + 1];
         int n = (int)(o1 - o0);
         oc_entry* ent = (oc_entry*)malloc(sizeof(oc_entry) * (size_t)(n > 0 ? n : 1));
+        oc_entry* entB = NULL;
+        double *daF = NULL, *daB = NULL;
+        if (a->layer) {
+            entB = (oc_entry*)malloc(sizeof(oc_entry) * (size_t)(n > 0 ? n : 1));
+            daF = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+            daB = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+        }
         for (int py = ty * OC_TILE; py < ty * OC_TILE + OC_TILE && py < H; ++py)
             for (int px = tx * OC_TILE; px < tx * OC_TILE + OC_TILE && px < W; ++px) {
                 int p = py * W + px;
                 double pu = px + 0.5, pv = py + 0.5;
+                if (a->layer) {
+                    composite_pixel_aa(a, p, pu, pv, o0, n, ent, entB, daF, daB, &pairs_total);
+                    continue;
+                }
                 int fid = a->face_id[p];
                 int on = fid >= 0;
                 double am = on ? 1.0 : 0.0;
@@ -957,6 +1124,9 @@ void oc_composite(oc_comp* a)
                 a->g_mesh_depth[p] = TF * am * GZ + gD;
             }
         free(ent);
+        free(entB);
+        free(daF);
+        free(daB);
     }
     if (a->pairs_evaluated) *a->pairs_evaluated = pairs_total;
 }

@@ -455,3 +455,25 @@ void oc_mesh_bwd(const mb_camera* cam, const mb_mesh* m, int npix, const int* pi
     free(gmips);
     free(mips);
 }
+
+/* Gradients of the screen positions of the vertices (dL/du, dL/dv per vertex, [2][V],
+ * e.g. from the antialiased silhouettes) carried to the world positions through the
+ * fp64 pinhole projection u = fx x_c / z_c + cx, v = fy y_c / z_c + cy, x_c = R X + t.
+ * Accumulated into g_verts [3][V]. */
+void oc_vscreen_bwd(const mb_camera* cam, const mb_mesh* m, const double* g_vs, double* g_verts)
+{
+    const int V = m->V;
+    for (int i = 0; i < V; ++i) {
+        const double gu = g_vs[i], gv = g_vs[V + i];
+        if (gu == 0.0 && gv == 0.0) continue;
+        double xc[3];
+        for (int r = 0; r < 3; ++r)
+            xc[r] = (double)cam->R[3 * r] * m->verts[i] + (double)cam->R[3 * r + 1] * m->verts[V + i] +
+                    (double)cam->R[3 * r + 2] * m->verts[2 * V + i] + (double)cam->t[r];
+        const double z = xc[2];
+        const double gx = gu * cam->fx / z, gy = gv * cam->fy / z;
+        const double gzc = -gu * cam->fx * xc[0] / (z * z) - gv * cam->fy * xc[1] / (z * z);
+        for (int j = 0; j < 3; ++j)
+            g_verts[(size_t)j * V + i] += (double)cam->R[j] * gx + (double)cam->R[3 + j] * gy + (double)cam->R[6 + j] * gzc;
+    }
+}
