@@ -47,7 +47,9 @@ EXPORTS = ["gm_bin_triangles_ws", "gm_bin_triangles", "gm_raster_zbuffer", "gm_p
            "gm_project_gaussians_multi",
            "gm_sort_tile_keys_ws", "gm_sort_tile_keys", "gm_composite_hybrid_fwd",
            "gm_composite_hybrid_bwd", "gm_project_gaussians_bwd", "gm_mesh_bwd", "gm_mipmaps_floats",
-           "gm_build_mipmaps", "gm_last_error", "gm_version"]
+           "gm_build_mipmaps", "gm_last_error", "gm_version", "gm_edge_adjacency_ws", "gm_edge_adjacency",
+           "gm_antialias", "gm_composite_hybrid_fwd_aa", "gm_composite_hybrid_bwd_aa", "gm_antialias_bwd_ws",
+           "gm_antialias_bwd", "gm_vscreen_bwd"]
 
 _lib = None
 
@@ -76,6 +78,16 @@ def lib():
     L.gm_composite_hybrid_bwd.argtypes = [cam, I32, P, P, P, P, P, F32, P, P, P, P, P, P, P, P, P, P]
     L.gm_project_gaussians_bwd.argtypes = [cam, I32, P, P, P, P, P, I32, P, P, P, P, P, P, P, P, P, P]
     L.gm_mesh_bwd.argtypes = [cam, mesh, light, P, P, P, P, P, P, P, P, P, P]
+    L.gm_edge_adjacency_ws.argtypes = [I32]
+    L.gm_edge_adjacency_ws.restype = SZ
+    L.gm_edge_adjacency.argtypes = [mesh, P, P, SZ, P]
+    L.gm_antialias.argtypes = [cam, mesh, P, P, light, P, P, P, P, P, P]
+    L.gm_composite_hybrid_fwd_aa.argtypes = [cam, P, P, P, P, P, F32, P, P, P, P, P]
+    L.gm_composite_hybrid_bwd_aa.argtypes = [cam, I32, P, P, P, P, P, F32, P, P, P, P, P, P, P]
+    L.gm_antialias_bwd_ws.argtypes = [I32, I32]
+    L.gm_antialias_bwd_ws.restype = SZ
+    L.gm_antialias_bwd.argtypes = [cam, mesh, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    L.gm_vscreen_bwd.argtypes = [cam, mesh, P, P, P]
     L.gm_mipmaps_floats.argtypes = [I32]
     L.gm_mipmaps_floats.restype = SZ
     L.gm_build_mipmaps.argtypes = [P, I32, P, P]
@@ -89,7 +101,8 @@ def lib():
     for name in ("gm_bin_triangles", "gm_raster_zbuffer", "gm_project_gaussians", "gm_project_gaussians_multi",
                  "gm_sort_tile_keys",
                  "gm_composite_hybrid_fwd", "gm_composite_hybrid_bwd", "gm_project_gaussians_bwd",
-                 "gm_mesh_bwd", "gm_build_mipmaps"):
+                 "gm_mesh_bwd", "gm_build_mipmaps", "gm_edge_adjacency", "gm_antialias", "gm_composite_hybrid_fwd_aa",
+                 "gm_composite_hybrid_bwd_aa", "gm_antialias_bwd", "gm_vscreen_bwd"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -198,3 +211,50 @@ def gm_build_mipmaps(tex, S, mips, stream):
 
 def gm_version() -> int:
     return lib().gm_version()
+
+
+# analytic edge antialiasing
+
+def gm_edge_adjacency_ws(F) -> int:
+    return lib().gm_edge_adjacency_ws(int(F))
+
+
+def gm_edge_adjacency(mesh, adj, ws, stream):
+    check(lib().gm_edge_adjacency(C.byref(mesh), ptr(adj), ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                  stream))
+
+
+def gm_antialias(cam, mesh, vscreen, adj, light, face_id, depth, colour, layer, tile_dmax, stream):
+    check(lib().gm_antialias(C.byref(cam), C.byref(mesh), ptr(vscreen), ptr(adj), _light_ref(light), ptr(face_id),
+                             ptr(depth), ptr(colour), ptr(layer), ptr(tile_dmax), stream))
+
+
+def gm_composite_hybrid_fwd_aa(cam, rec, tile_ranges, sorted_ids, layer, bg, softness, out_rgb, out_depth, out_alpha,
+                               state, stream):
+    bgv = (C.c_float * 3)(*[float(x) for x in bg])  # host array, alive for the call
+    check(lib().gm_composite_hybrid_fwd_aa(C.byref(cam), ptr(rec), ptr(tile_ranges), ptr(sorted_ids), ptr(layer),
+                                           C.cast(bgv, C.c_void_p), float(softness), ptr(out_rgb), ptr(out_depth),
+                                           ptr(out_alpha), ptr(state), stream))
+
+
+def gm_composite_hybrid_bwd_aa(cam, N, rec, tile_ranges, sorted_ids, layer, bg, softness, state, g_rgb, g_depth,
+                               g_alpha, g_rec, g_layer, stream):
+    bgv = (C.c_float * 3)(*[float(x) for x in bg])
+    check(lib().gm_composite_hybrid_bwd_aa(C.byref(cam), int(N), ptr(rec), ptr(tile_ranges), ptr(sorted_ids),
+                                           ptr(layer), C.cast(bgv, C.c_void_p), float(softness), ptr(state), ptr(g_rgb),
+                                           ptr(g_depth), ptr(g_alpha), ptr(g_rec), ptr(g_layer), stream))
+
+
+def gm_antialias_bwd_ws(width, height) -> int:
+    return lib().gm_antialias_bwd_ws(int(width), int(height))
+
+
+def gm_antialias_bwd(cam, mesh, vscreen, adj, face_id, depth, colour, g_layer, g_mesh_rgb, g_mesh_depth, g_vscreen,
+                     ws, stream):
+    check(lib().gm_antialias_bwd(C.byref(cam), C.byref(mesh), ptr(vscreen), ptr(adj), ptr(face_id), ptr(depth),
+                                 ptr(colour), ptr(g_layer), ptr(g_mesh_rgb), ptr(g_mesh_depth), ptr(g_vscreen), ptr(ws),
+                                 0 if ws is None else ws.numel() * ws.element_size(), stream))
+
+
+def gm_vscreen_bwd(cam, mesh, g_vscreen, g_verts, stream):
+    check(lib().gm_vscreen_bwd(C.byref(cam), C.byref(mesh), ptr(g_vscreen), ptr(g_verts), stream))

@@ -233,7 +233,7 @@ __device__ __forceinline__ float quad_form(float hq00, float q01, float hq11, fl
 // Functions, formula 7.1.26 (|error| <= 1.5e-7): erfc(z) = t P(t) exp(-z^2),
 // t = 1 / (1 + p z).  With z = |s| / sqrt(2), exp(-z^2) = exp(-s^2 / 2), which is
 // also what phi needs, so the backward gets both for the price of one exp.
-__device__ __forceinline__ float normal_cdf_pdf(float s, float& pdf)
+__device__ __forceinline__ float normal_cdf_pdf(float s, float& pdf, float& comp)
 {
     const float e = __expf(-0.5f * s * s);
     pdf = 0.39894228040143268f * e;
@@ -245,6 +245,7 @@ __device__ __forceinline__ float normal_cdf_pdf(float s, float& pdf)
     poly = __builtin_fmaf(t, poly, 0.254829592f);
     poly *= t;
     const float half_tail = 0.5f * poly * e;  // Phi(-|s|)
+    comp = s <= 0.0f ? 1.0f - half_tail : half_tail;  // 1 - Phi(s), without cancellation
     return s <= 0.0f ? half_tail : 1.0f - half_tail;
 }
 
@@ -256,8 +257,8 @@ __device__ __forceinline__ float normal_cdf_pdf(float s, float& pdf)
 // alpha_F >= 1/255.  Both walks call this one function, so the forward and the
 // backward take the same decisions bit for bit.
 struct Pair {
-    float dx, dy, q, oG, al, f, pdf, s, aF;
-    bool ok;  // passes the skip rules
+    float dx, dy, q, oG, al, f, fb, pdf, s, aF;  // fb = 1 - f (the back share)
+    bool ok;  // passes the skip rules of the front layer
 };
 
 __device__ __forceinline__ Pair eval_pair(const Staged& g, float pxc, float pyc, bool on, bool wave_on, float D,
@@ -270,18 +271,22 @@ __device__ __forceinline__ Pair eval_pair(const Staged& g, float pxc, float pyc,
     p.oG = g.b.y * __expf(-p.q);
     p.al = fminf(p.oG, ALPHA_MAX);
     p.f = 1.0f;
+    p.fb = 0.0f;
     p.pdf = 0.0f;
     p.s = 0.0f;
     if (wave_on) {  // uniform: some pixel of the wave is on the mesh
         const float num = (D - g.c.y) - __builtin_fmaf(g.c.z, p.dx, g.c.w * p.dy);
         if (softness > 0.0f) {
             p.s = on ? num * g.d.y : 0.0f;  // off the mesh D = +inf: keep s finite
-            float pd;
-            const float fo = normal_cdf_pdf(p.s, pd);
+            float pd, fc;
+            const float fo = normal_cdf_pdf(p.s, pd, fc);
             p.f = on ? fo : 1.0f;
+            p.fb = on ? fc : 0.0f;
             p.pdf = on ? pd : 0.0f;
         } else {
-            p.f = (on && !(num > 0.0f)) ? 0.0f : 1.0f;
+            const bool behind = on && !(num > 0.0f);
+            p.f = behind ? 0.0f : 1.0f;
+            p.fb = behind ? 1.0f : 0.0f;
         }
     }
     p.aF = p.al * p.f;
@@ -390,10 +395,29 @@ __device__ __forceinline__ void wave_dmax(bool inside, bool on, float D, float* 
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
+// AA = false: binary mesh coverage from the z-buffer; the back layer is inert
+// (off the mesh f = 1, on it the weight 1 - a_m = 0), so only the front layer is
+// composited: C = C_F + T_F c_m (c_m = bg off the mesh).
+// AA = true: the antialiased mesh layer (premultiplied colour M and depth M_D,
+// coverage a_m, split depth D) and the general two-layer form
+// C = C_F + T_F (M + (1 - a_m)(C_B + T_B bg)); the back layer is composited where
+// it is visible (a_m < 1, finite D), with the same per-layer rules.
+struct AaLayer {
+    float M0, M1, M2, MD, am, D;
+};
+
+__device__ __forceinline__ AaLayer load_layer(const float* __restrict__ layer, int pix)
+{
+    const float4 l0 = reinterpret_cast<const float4*>(layer)[2 * pix];
+    const float4 l1 = reinterpret_cast<const float4*>(layer)[2 * pix + 1];
+    return AaLayer{l0.x, l0.y, l0.z, l0.w, l1.x, l1.y};
+}
+
+template <bool AA>
 __global__ void __launch_bounds__(CT)
-k_composite_fwd(CompParams P, const float* __restrict__ state_cm, float* __restrict__ out_rgb,
-                float* __restrict__ out_depth, float* __restrict__ out_alpha, float* __restrict__ state_T,
-                int32_t* __restrict__ state_last)
+k_composite_fwd(CompParams P, const float* __restrict__ state_cm, const float* __restrict__ layer,
+                float* __restrict__ out_rgb, float* __restrict__ out_depth, float* __restrict__ out_alpha,
+                float* __restrict__ state_T, int32_t* __restrict__ state_last, float* __restrict__ state_aa)
 {
     __shared__ Staged s_g[CB];
     __shared__ uint8_t s_m[CB];
@@ -407,24 +431,40 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, float* __restr
     const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
     const int start = P.ranges[2 * tile], end = P.ranges[2 * tile + 1];
 
-    const int fid = inside ? P.face_id[pix] : -1;
-    const bool on = fid >= 0;
-    const float D = on ? P.depth[pix] : INFINITY;
-    wave_dmax(inside, on, D, s_wd);
+    bool on;
+    float D;
+    AaLayer ml{};
+    if constexpr (AA) {
+        ml = inside ? load_layer(layer, pix) : AaLayer{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, INFINITY};
+        D = ml.D;
+        on = D < INFINITY;
+        // the wave's depth bound only counts pixels the mesh covers completely
+        wave_dmax(inside, on && ml.am >= 1.0f, D, s_wd);
+    } else {
+        const int fid = inside ? P.face_id[pix] : -1;
+        on = fid >= 0;
+        D = on ? P.depth[pix] : INFINITY;
+        wave_dmax(inside, on, D, s_wd);
+    }
     const bool wave_on = __ballot(on) != 0;
 
     float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f, Z = 0.0f;
     int last = 0;
     bool done = !inside;
+    // back layer (AA only)
+    float TB = 1.0f, B0 = 0.0f, B1 = 0.0f, B2 = 0.0f, ZB = 0.0f;
+    int lastB = 0;
+    bool doneB = true;
+    if constexpr (AA) doneB = !(inside && on && ml.am < 1.0f);
     float4 ra, rb, rc, rd;
     if (start + (int)threadIdx.x < end) load_record(P.rec, P.ids[start + threadIdx.x], ra, rb, rc, rd);
     for (int b0 = start; b0 < end; b0 += CB) {
-        if (__syncthreads_count(done) == CT) break;
+        if (__syncthreads_count(done & doneB) == CT) break;
         const int nb = min(CB, end - b0);
         s_m[threadIdx.x] = threadIdx.x < nb ? (uint8_t)stage_record(P, ra, rb, rc, rd, tx, ty, s_wd, s_g[threadIdx.x]) : 0;
         if (b0 + CB + (int)threadIdx.x < end) load_record(P.rec, P.ids[b0 + CB + threadIdx.x], ra, rb, rc, rd);
         __syncthreads();
-        bool wdone = __ballot(!done) == 0;
+        bool wdone = __ballot(!(done & doneB)) == 0;
         for (int i = 0; i < CB / 64 && !wdone; ++i) {
             unsigned long long m = __ballot((s_m[i * 64 + lane] >> wave) & 1);
             while (m) {
@@ -445,7 +485,22 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, float* __restr
                 T = inc ? Tn : T;
                 last = inc ? b0 + k - start + 1 : last;
                 done = done | stop;
-                if (__ballot(!done) == 0) {
+                if constexpr (AA) {
+                    const float aB = pr.al * pr.fb;
+                    const bool liveB = !doneB & !(pr.q > g.d.z) & (pr.al >= SKIP_ALPHA) & (aB >= SKIP_ALPHA);
+                    const float TnB = TB * (1.0f - aB);
+                    const bool stopB = liveB & (TnB < STOP_T);
+                    const bool incB = liveB & !stopB;
+                    const float wB = incB ? aB * TB : 0.0f;
+                    B0 = __builtin_fmaf(wB, g.b.z, B0);
+                    B1 = __builtin_fmaf(wB, g.b.w, B1);
+                    B2 = __builtin_fmaf(wB, g.c.x, B2);
+                    ZB = __builtin_fmaf(wB, g.c.y, ZB);
+                    TB = incB ? TnB : TB;
+                    lastB = incB ? b0 + k - start + 1 : lastB;
+                    doneB = doneB | stopB;
+                }
+                if (__ballot(!(done & doneB)) == 0) {
                     wdone = true;
                     break;
                 }
@@ -453,13 +508,26 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, float* __restr
         }
     }
     if (!inside) return;
-    out_rgb[3 * pix + 0] = C0 + T * state_cm[3 * pix + 0];
-    out_rgb[3 * pix + 1] = C1 + T * state_cm[3 * pix + 1];
-    out_rgb[3 * pix + 2] = C2 + T * state_cm[3 * pix + 2];
-    out_alpha[pix] = on ? 1.0f : 1.0f - T;
-    out_depth[pix] = Z + (on ? T * D : 0.0f);
-    state_T[pix] = T;
-    state_last[pix] = last;
+    if constexpr (AA) {
+        const float ob = 1.0f - ml.am;
+        const float Y0 = B0 + TB * P.bg[0], Y1 = B1 + TB * P.bg[1], Y2 = B2 + TB * P.bg[2];
+        out_rgb[3 * pix + 0] = C0 + T * (ml.M0 + ob * Y0);
+        out_rgb[3 * pix + 1] = C1 + T * (ml.M1 + ob * Y1);
+        out_rgb[3 * pix + 2] = C2 + T * (ml.M2 + ob * Y2);
+        out_alpha[pix] = 1.0f - T * ob * TB;
+        out_depth[pix] = Z + T * (ml.MD + ob * ZB);
+        float4* st = reinterpret_cast<float4*>(state_aa) + 2 * pix;
+        st[0] = make_float4(T, __int_as_float(last), TB, __int_as_float(lastB));
+        st[1] = make_float4(B0, B1, B2, ZB);
+    } else {
+        out_rgb[3 * pix + 0] = C0 + T * state_cm[3 * pix + 0];
+        out_rgb[3 * pix + 1] = C1 + T * state_cm[3 * pix + 1];
+        out_rgb[3 * pix + 2] = C2 + T * state_cm[3 * pix + 2];
+        out_alpha[pix] = on ? 1.0f : 1.0f - T;
+        out_depth[pix] = Z + (on ? T * D : 0.0f);
+        state_T[pix] = T;
+        state_last[pix] = last;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -508,11 +576,19 @@ __device__ __forceinline__ float wave_sum16(const float* v, int lane)
     return d;
 }
 
+// AA = true: the reverse mode of the two-layer form.  The back layer sees the
+// upstream gradients scaled by k = T_F (1 - a_m) and, behind it, bg (depth 0) and
+// the alpha term; per entry dL/dalpha = f dL/dalpha_F + (1 - f) dL/dalpha_B and
+// dL/ds = alpha phi(s) (dL/dalpha_F - dL/dalpha_B).  Both layers recover their
+// transmittance by division while walking back from max(last_F, last_B).  The
+// per-pixel outputs are dL/d(M, M_D, a_m, D) of the mesh layer.
+template <bool AA>
 __global__ void __launch_bounds__(CT)
 k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* __restrict__ state_last,
-                const float* __restrict__ state_cm, const float* __restrict__ g_rgb,
+                const float* __restrict__ state_cm, const float* __restrict__ layer,
+                const float* __restrict__ state_aa, const float* __restrict__ g_rgb,
                 const float* __restrict__ g_depth, const float* __restrict__ g_alpha, float* __restrict__ g_rec,
-                float* __restrict__ g_mesh_rgb, float* __restrict__ g_mesh_depth)
+                float* __restrict__ g_mesh_rgb, float* __restrict__ g_mesh_depth, float* __restrict__ g_layer)
 {
     __shared__ Staged s_g[CB];
     __shared__ int s_id[CB];
@@ -529,29 +605,68 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
     const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
     const int start = P.ranges[2 * tile];
 
-    const int fid = inside ? P.face_id[pix] : -1;
-    const bool on = fid >= 0;
-    const float D = on ? P.depth[pix] : INFINITY;
-    const float TF = inside ? state_T[pix] : 1.0f;
-    const int last = inside ? state_last[pix] : 0;
-    float GC0 = 0.0f, GC1 = 0.0f, GC2 = 0.0f, GZ = 0.0f, GA = 0.0f, Bt = 0.0f;
+    bool on;
+    float D, TF;
+    int last;
+    AaLayer ml{};
+    float TB = 1.0f, Y0 = 0.0f, Y1 = 0.0f, Y2 = 0.0f, ZB = 0.0f, kB = 0.0f;
+    int lastB = 0;
+    if constexpr (AA) {
+        ml = inside ? load_layer(layer, pix) : AaLayer{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, INFINITY};
+        D = ml.D;
+        on = D < INFINITY;
+        float4 s0 = make_float4(1.0f, 0.0f, 1.0f, 0.0f), s1 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (inside) {
+            s0 = reinterpret_cast<const float4*>(state_aa)[2 * pix];
+            s1 = reinterpret_cast<const float4*>(state_aa)[2 * pix + 1];
+        }
+        TF = s0.x;
+        last = __float_as_int(s0.y);
+        TB = s0.z;
+        lastB = __float_as_int(s0.w);
+        Y0 = s1.x + TB * P.bg[0];
+        Y1 = s1.y + TB * P.bg[1];
+        Y2 = s1.z + TB * P.bg[2];
+        ZB = s1.w;
+        kB = TF * (1.0f - ml.am);
+    } else {
+        const int fid = inside ? P.face_id[pix] : -1;
+        on = fid >= 0;
+        D = on ? P.depth[pix] : INFINITY;
+        TF = inside ? state_T[pix] : 1.0f;
+        last = inside ? state_last[pix] : 0;
+    }
+    float GC0 = 0.0f, GC1 = 0.0f, GC2 = 0.0f, GZ = 0.0f, GA = 0.0f, Bt = 0.0f, BtB = 0.0f;
     if (inside) {
         GC0 = g_rgb[3 * pix + 0];
         GC1 = g_rgb[3 * pix + 1];
         GC2 = g_rgb[3 * pix + 2];
         if (g_depth) GZ = g_depth[pix];
         if (g_alpha) GA = g_alpha[pix];
-        // B = dL/dT_F: the colour behind the Gaussians, the mesh depth and the alpha
-        Bt = GC0 * state_cm[3 * pix + 0] + GC1 * state_cm[3 * pix + 1] + GC2 * state_cm[3 * pix + 2] +
-             (on ? GZ * D : -GA);
+        if constexpr (AA) {
+            // dL/dT_F: everything behind the front layer; dL/dT_B (scaled by kB): bg and alpha
+            const float ob = 1.0f - ml.am;
+            Bt = GC0 * (ml.M0 + ob * Y0) + GC1 * (ml.M1 + ob * Y1) + GC2 * (ml.M2 + ob * Y2) +
+                 GZ * (ml.MD + ob * ZB) - GA * ob * TB;
+            BtB = kB * (GC0 * P.bg[0] + GC1 * P.bg[1] + GC2 * P.bg[2] - GA);
+        } else {
+            // B = dL/dT_F: the colour behind the Gaussians, the mesh depth and the alpha
+            Bt = GC0 * state_cm[3 * pix + 0] + GC1 * state_cm[3 * pix + 1] + GC2 * state_cm[3 * pix + 2] +
+                 (on ? GZ * D : -GA);
+        }
     }
     float acc = TF * Bt;
     float T = TF;
+    float accB = TB * BtB;
+    float TBw = TB;
     float gD = 0.0f;
 
-    wave_dmax(inside, on, D, s_wd);
+    if constexpr (AA)
+        wave_dmax(inside, on && ml.am >= 1.0f, D, s_wd);
+    else
+        wave_dmax(inside, on, D, s_wd);
     const bool wave_on = __ballot(on) != 0;
-    int m = last;
+    int m = AA ? max(last, lastB) : last;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o, 64));
     if (lane == 0) s_wl[wave] = m;
@@ -604,7 +719,7 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
                 const Pair pr = eval_pair(g, pxc, pyc, on, wave_on, D, P.softness);
                 const float dx = pr.dx, dy = pr.dy, oG = pr.oG, al = pr.al, f = pr.f, pdf = pr.pdf, sv = pr.s;
                 const float aF = pr.aF;
-                const bool act = (rel < last) & pr.ok;
+                bool act = (rel < last) & pr.ok;
                 // per-pixel basis sums; the 13 record gradients are linear in them
                 // (formed once per entry at the flush):
                 //  0-2 w GC, 3 w GZ, 4 H, 5 H dx, 6 H dy, 7 H dx^2, 8 H dx dy, 9 H dy^2,
@@ -619,12 +734,29 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
                 const float daF = act ? __builtin_fmaf(Ti, Vv, -acc * iom) : 0.0f;
                 acc = __builtin_fmaf(w, Vv, acc);
                 T = Ti;
+                float wt = w, da = f * daF, dsF = daF;
+                if constexpr (AA) {
+                    const float aB = al * pr.fb;
+                    const bool actB = (rel < lastB) & !(pr.q > g.d.z) & (al >= SKIP_ALPHA) & (aB >= SKIP_ALPHA);
+                    const float aBe = actB ? aB : 0.0f;
+                    const float iomB = __builtin_amdgcn_rcpf(1.0f - aBe);
+                    const float TiB = TBw * iomB;
+                    const float wB = aBe * TiB;
+                    const float VB = kB * Vv;
+                    const float daB = actB ? __builtin_fmaf(TiB, VB, -accB * iomB) : 0.0f;
+                    accB = __builtin_fmaf(wB, VB, accB);
+                    TBw = TiB;
+                    wt = __builtin_fmaf(kB, wB, w);
+                    da = __builtin_fmaf(pr.fb, daB, da);
+                    dsF = daF - daB;
+                    act = act | actB;
+                }
                 float gr[16];
-                gr[0] = w * GC0;
-                gr[1] = w * GC1;
-                gr[2] = w * GC2;
-                gr[3] = w * GZ;
-                const float H = oG <= ALPHA_MAX ? oG * (f * daF) : 0.0f;
+                gr[0] = wt * GC0;
+                gr[1] = wt * GC1;
+                gr[2] = wt * GC2;
+                gr[3] = wt * GZ;
+                const float H = oG <= ALPHA_MAX ? oG * da : 0.0f;
                 const float Hx = H * dx, Hy = H * dy;
                 gr[4] = H;
                 gr[5] = Hx;
@@ -632,7 +764,7 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
                 gr[7] = Hx * dx;
                 gr[8] = Hx * dy;
                 gr[9] = Hy * dy;
-                const float ds = (al * pdf) * daF;
+                const float ds = (al * pdf) * dsF;
                 gr[10] = ds;
                 gr[11] = ds * dx;
                 gr[12] = ds * dy;
@@ -684,6 +816,12 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
         }
     }
     if (!inside) return;
+    if constexpr (AA) {
+        float4* gl = reinterpret_cast<float4*>(g_layer) + 2 * pix;
+        gl[0] = make_float4(TF * GC0, TF * GC1, TF * GC2, TF * GZ);
+        gl[1] = make_float4(TF * (GA * TB - (GC0 * Y0 + GC1 * Y1 + GC2 * Y2) - GZ * ZB), gD, 0.0f, 0.0f);
+        return;
+    }
     const float am = on ? 1.0f : 0.0f;
     if (g_mesh_rgb) {
         g_mesh_rgb[3 * pix + 0] = TF * am * GC0;
@@ -699,22 +837,9 @@ __global__ void k_zero_f32(float* __restrict__ p, int64_t n)
     if (i < n) p[i] = 0.0f;
 }
 
-static gm_status fill_params(CompParams& P, const gm_camera* cam, const float* rec, const int32_t* ranges,
-                             const int32_t* ids, const int32_t* face_id, const float* depth,
-                             const gm_mesh* mesh, const float* vscreen, const gm_light* light,
-                             const float* bg, float softness)
+// Mesh surface and light fields of the parameters (for the colour prepass).
+static gm_status fill_surface(CompParams& P, const gm_mesh* mesh, const float* vscreen, const gm_light* light)
 {
-    if (gm_status s = check_camera(cam)) return s;
-    GM_ARG_CHECK(ranges && face_id && depth && bg, "tile_ranges / face_id / depth / bg is NULL");
-    GM_ARG_CHECK(softness >= 0.0f, "softness must be >= 0");
-    GM_ARG_CHECK(((uintptr_t)rec & 15) == 0, "rec must be 16-byte aligned");
-    P = CompParams{};
-    P.cam = dev_camera(*cam);
-    P.rec = rec;
-    P.ranges = ranges;
-    P.ids = ids;
-    P.face_id = face_id;
-    P.depth = depth;
     if (mesh && mesh->F > 0) {
         GM_ARG_CHECK(mesh->faces && vscreen, "mesh faces / vscreen is NULL");
         P.V = mesh->V;
@@ -747,8 +872,61 @@ static gm_status fill_params(CompParams& P, const gm_camera* cam, const float* r
         }
         P.lshin = light->shininess;
     }
+    return GM_OK;
+}
+
+static gm_status fill_params(CompParams& P, const gm_camera* cam, const float* rec, const int32_t* ranges,
+                             const int32_t* ids, const int32_t* face_id, const float* depth,
+                             const gm_mesh* mesh, const float* vscreen, const gm_light* light,
+                             const float* bg, float softness)
+{
+    if (gm_status s = check_camera(cam)) return s;
+    GM_ARG_CHECK(ranges && face_id && depth && bg, "tile_ranges / face_id / depth / bg is NULL");
+    GM_ARG_CHECK(softness >= 0.0f, "softness must be >= 0");
+    GM_ARG_CHECK(((uintptr_t)rec & 15) == 0, "rec must be 16-byte aligned");
+    P = CompParams{};
+    P.cam = dev_camera(*cam);
+    P.rec = rec;
+    P.ranges = ranges;
+    P.ids = ids;
+    P.face_id = face_id;
+    P.depth = depth;
+    if (gm_status s = fill_surface(P, mesh, vscreen, light)) return s;
     for (int i = 0; i < 3; ++i) P.bg[i] = bg[i];
     P.softness = softness;
+    return GM_OK;
+}
+
+// Parameters of the two-layer kernels: the mesh enters through its layer only.
+static gm_status fill_params_aa(CompParams& P, const gm_camera* cam, const float* rec, const int32_t* ranges,
+                                const int32_t* ids, const float* layer, const float* bg, float softness)
+{
+    if (gm_status s = check_camera(cam)) return s;
+    GM_ARG_CHECK(ranges && layer && bg, "tile_ranges / layer / bg is NULL");
+    GM_ARG_CHECK(softness >= 0.0f, "softness must be >= 0");
+    GM_ARG_CHECK(((uintptr_t)rec & 15) == 0 && ((uintptr_t)layer & 15) == 0, "rec and layer must be 16-byte aligned");
+    P = CompParams{};
+    P.cam = dev_camera(*cam);
+    P.rec = rec;
+    P.ranges = ranges;
+    P.ids = ids;
+    for (int i = 0; i < 3; ++i) P.bg[i] = bg[i];
+    P.softness = softness;
+    return GM_OK;
+}
+
+gm_status launch_surface_colour(const gm_camera* cam, const gm_mesh* mesh, const float* vscreen,
+                                const gm_light* light, const int32_t* face_id, const float* bg, float* colour,
+                                hipStream_t stream)
+{
+    CompParams P{};
+    P.cam = dev_camera(*cam);
+    P.face_id = face_id;
+    if (gm_status s = fill_surface(P, mesh, vscreen, light)) return s;
+    for (int i = 0; i < 3; ++i) P.bg[i] = bg ? bg[i] : 0.0f;
+    const int64_t HW = (int64_t)P.cam.width * P.cam.height;
+    k_shade<<<(unsigned)div_up(HW, 256), 256, 0, stream>>>(P, colour);
+    GM_LAUNCH_CHECK();
     return GM_OK;
 }
 
@@ -775,8 +953,25 @@ gm_status gm_composite_hybrid_fwd(const gm_camera* cam, const float* rec, const 
     const int64_t HW = (int64_t)P.cam.width * P.cam.height;
     k_shade<<<(unsigned)div_up(HW, 256), 256, 0, stream>>>(P, state_cm);
     GM_LAUNCH_CHECK();
-    k_composite_fwd<<<(unsigned)T, CT, 0, stream>>>(P, state_cm, out_rgb, out_depth, out_alpha, state_T,
-                                                   state_last);
+    k_composite_fwd<false><<<(unsigned)T, CT, 0, stream>>>(P, state_cm, nullptr, out_rgb, out_depth, out_alpha,
+                                                          state_T, state_last, nullptr);
+    GM_LAUNCH_CHECK();
+    return GM_OK;
+}
+
+gm_status gm_composite_hybrid_fwd_aa(const gm_camera* cam, const float* rec, const int32_t* tile_ranges,
+                                     const int32_t* sorted_ids, const float* layer, const float* bg, float softness,
+                                     float* out_rgb, float* out_depth, float* out_alpha, float* state,
+                                     hipStream_t stream)
+{
+    clear_error();
+    CompParams P;
+    if (gm_status s = fill_params_aa(P, cam, rec, tile_ranges, sorted_ids, layer, bg, softness)) return s;
+    GM_ARG_CHECK(out_rgb && out_depth && out_alpha && state, "an output is NULL");
+    GM_ARG_CHECK(((uintptr_t)state & 15) == 0, "state must be 16-byte aligned");
+    const int64_t T = (int64_t)P.cam.tx * P.cam.ty;
+    k_composite_fwd<true><<<(unsigned)T, CT, 0, stream>>>(P, nullptr, layer, out_rgb, out_depth, out_alpha, nullptr,
+                                                         nullptr, state);
     GM_LAUNCH_CHECK();
     return GM_OK;
 }
@@ -803,8 +998,34 @@ gm_status gm_composite_hybrid_bwd(const gm_camera* cam, int32_t N, const float* 
         k_zero_f32<<<(unsigned)div_up(n, 256), 256, 0, stream>>>(g_rec, n);
         GM_LAUNCH_CHECK();
     }
-    k_composite_bwd<<<(unsigned)T, CT, 0, stream>>>(P, state_T, state_last, state_cm, g_rgb, g_depth, g_alpha,
-                                                   g_rec, g_mesh_rgb, g_mesh_depth);
+    k_composite_bwd<false><<<(unsigned)T, CT, 0, stream>>>(P, state_T, state_last, state_cm, nullptr, nullptr,
+                                                          g_rgb, g_depth, g_alpha, g_rec, g_mesh_rgb, g_mesh_depth,
+                                                          nullptr);
+    GM_LAUNCH_CHECK();
+    return GM_OK;
+}
+
+gm_status gm_composite_hybrid_bwd_aa(const gm_camera* cam, int32_t N, const float* rec, const int32_t* tile_ranges,
+                                     const int32_t* sorted_ids, const float* layer, const float* bg, float softness,
+                                     const float* state, const float* g_rgb, const float* g_depth,
+                                     const float* g_alpha, float* g_rec, float* g_layer, hipStream_t stream)
+{
+    clear_error();
+    CompParams P;
+    if (gm_status s = fill_params_aa(P, cam, rec, tile_ranges, sorted_ids, layer, bg, softness)) return s;
+    GM_ARG_CHECK(N >= 0, "N = %d is negative", N);
+    GM_ARG_CHECK(state && g_rgb && g_layer, "state, g_rgb or g_layer is NULL");
+    GM_ARG_CHECK(((uintptr_t)state & 15) == 0 && ((uintptr_t)g_layer & 15) == 0,
+                 "state and g_layer must be 16-byte aligned");
+    GM_ARG_CHECK(N == 0 || g_rec, "g_rec is NULL");
+    const int64_t T = (int64_t)P.cam.tx * P.cam.ty;
+    if (N > 0) {
+        const int64_t n = (int64_t)N * GM_GRAD;
+        k_zero_f32<<<(unsigned)div_up(n, 256), 256, 0, stream>>>(g_rec, n);
+        GM_LAUNCH_CHECK();
+    }
+    k_composite_bwd<true><<<(unsigned)T, CT, 0, stream>>>(P, nullptr, nullptr, nullptr, layer, state, g_rgb, g_depth,
+                                                         g_alpha, g_rec, nullptr, nullptr, g_layer);
     GM_LAUNCH_CHECK();
     return GM_OK;
 }

@@ -79,6 +79,12 @@ size_t scan_ws_bytes(int64_t n);
 gm_status exclusive_scan(const int32_t* in, int32_t* out, int64_t n, long long* total, void* ws,
                          hipStream_t stream);
 
+// Surface colour prepass of the composite (gm_composite.hip): colour [H][W][3] =
+// the shaded mesh colour at covered pixels, bg (or 0 when bg is NULL) elsewhere.
+gm_status launch_surface_colour(const gm_camera* cam, const gm_mesh* mesh, const float* vscreen,
+                                const gm_light* light, const int32_t* face_id, const float* bg, float* colour,
+                                hipStream_t stream);
+
 // Read a device int64 into host memory (synchronises the stream).
 gm_status read_back_i64(const long long* dev, int64_t* host, hipStream_t stream);
 

@@ -86,6 +86,15 @@ class DeviceScene:
         self.cams = [make_camera(scene.width, scene.height, scene.fx, scene.fy, scene.cx, scene.cy,
                                  v.R, v.t, scene.near_z) for v in scene.views]
 
+    def adjacency(self):
+        """Edge adjacency [3][F] of the mesh (built once, on first use)."""
+        if getattr(self, "_adj", None) is None:
+            F = self.scene.F
+            self._adj = torch.empty((3, max(F, 1)), dtype=torch.int32, device=self.device)
+            ws = torch.empty(G.gm_edge_adjacency_ws(F), dtype=torch.uint8, device=self.device)
+            G.gm_edge_adjacency(self.mesh, self._adj, ws, _stream())
+        return self._adj
+
     def grads(self, view: int):
         g = self.scene.grads[view]
         return {k: torch.from_numpy(np.ascontiguousarray(v)).to(self.device) for k, v in g.items()}
@@ -225,9 +234,10 @@ class Renderer:
         return {"means": self.g_means[:, :N], "quats": self.g_quats[:, :N], "scales": self.g_scales[:, :N],
                 "opacity": self.g_opacity[:N], "sh": self.g_sh[..., :N]}
 
-    def mesh_bwd(self, view: int, g_mesh_rgb=None, g_mesh_depth=None):
+    def mesh_bwd(self, view: int, g_mesh_rgb=None, g_mesh_depth=None, g_vscreen=None):
         """Gradients of the mesh parameters from per-pixel dL/dc_m and dL/dD (default:
-        the last composite backward's).  Buffers are allocated on first use."""
+        the last backward's, with the silhouette gradients g_vscreen when it was
+        antialiased).  Buffers are allocated on first use."""
         ds, s = self.ds, self.ds.scene
         dev, f32 = ds.device, torch.float32
         if not hasattr(self, "gm_verts"):
@@ -244,6 +254,10 @@ class Renderer:
                       self.g_mesh_rgb if g_mesh_rgb is None else g_mesh_rgb,
                       self.g_mesh_depth if g_mesh_depth is None else g_mesh_depth, self.gm_verts, self.gm_vcolor,
                       self.gm_vnormal, self.gm_uv, self.gm_mips, self.gm_light, _stream())
+        if g_vscreen is not None or (g_mesh_rgb is None and getattr(self, "aa", False)):
+            # silhouettes: the crossings' screen-vertex gradients
+            G.gm_vscreen_bwd(ds.cams[view], ds.mesh, self.g_vscreen if g_vscreen is None else g_vscreen,
+                             self.gm_verts, _stream())
         out = {"verts": self.gm_verts[:, : s.V]}
         if self.gm_vcolor is not None:
             out["vcolor"] = self.gm_vcolor[:, : s.V]
@@ -253,6 +267,47 @@ class Renderer:
             S = ds.tex_size
             out["uv"], out["tex"] = self.gm_uv[:, : ds.mesh.Vt], self.gm_mips[: S * S * 3].view(S, S, 3)
         return out
+
+    # -- analytic edge antialiasing ---------------------------------------------
+    def _aa_buffers(self):
+        if getattr(self, "layer", None) is not None:
+            return
+        dev, f32 = self.ds.device, torch.float32
+        H, W = self.H, self.W
+        self.colour = torch.empty((H, W, 3), dtype=f32, device=dev)
+        self.layer = torch.empty((H, W, 8), dtype=f32, device=dev)
+        self.state_aa = torch.empty((H, W, 8), dtype=f32, device=dev)
+        self.g_layer = torch.empty((H, W, 8), dtype=f32, device=dev)
+        self.ws_aa_bwd = torch.empty(G.gm_antialias_bwd_ws(W, H), dtype=torch.uint8, device=dev)
+        self.g_vscreen = torch.empty((2, max(self.ds.scene.V, 1)), dtype=f32, device=dev)
+
+    def antialias(self, view: int):
+        """Antialiased mesh layer of the current z-buffer; marks the tiles whose back
+        layer shows so that the cull skips them."""
+        self._aa_buffers()
+        ds = self.ds
+        G.gm_antialias(ds.cams[view], ds.mesh, self.vscreen, ds.adjacency(), ds.light, self.face_id, self.depth,
+                       self.colour, self.layer, self.tile_dmax, _stream())
+
+    def composite_fwd_aa(self, view: int):
+        ds, s = self.ds, self.ds.scene
+        G.gm_composite_hybrid_fwd_aa(ds.cams[view], self.rec, self.tile_ranges, self.sorted_ids, self.layer, s.bg,
+                                     s.softness, self.out_rgb, self.out_depth, self.out_alpha, self.state_aa,
+                                     _stream())
+
+    def composite_bwd_aa(self, view: int, g_rgb, g_depth=None, g_alpha=None):
+        ds, s = self.ds, self.ds.scene
+        G.gm_composite_hybrid_bwd_aa(ds.cams[view], self.N, self.rec, self.tile_ranges, self.sorted_ids, self.layer,
+                                     s.bg, s.softness, self.state_aa, g_rgb, g_depth, g_alpha, self.g_rec,
+                                     self.g_layer, _stream())
+
+    def antialias_bwd(self, view: int, g_layer=None):
+        """dL/dc and dL/dD at covered pixels (into g_mesh_rgb / g_mesh_depth) and
+        dL/d(u, v) of the screen vertices (g_vscreen) from dL/d(layer)."""
+        ds = self.ds
+        G.gm_antialias_bwd(ds.cams[view], ds.mesh, self.vscreen, ds.adjacency(), self.face_id, self.depth,
+                           self.colour, self.g_layer if g_layer is None else g_layer, self.g_mesh_rgb,
+                           self.g_mesh_depth, self.g_vscreen, self.ws_aa_bwd, _stream())
 
     # -- several views -----------------------------------------------------------
     def project_views(self, views):
@@ -314,22 +369,29 @@ class Renderer:
                 return
 
     # -- whole passes -----------------------------------------------------------
-    def forward_async(self, view: int = 0, cull: bool = True):
+    def forward_async(self, view: int = 0, cull: bool = True, antialias: bool = False):
         """Queue one forward pass and the copy of the list lengths; no synchronisation.
         The outputs are valid once read_counts() returns True for this pass."""
         self._single()
-        self.view, self.cull = view, cull
+        self.view, self.cull, self.aa = view, cull, antialias
         self.bin_and_zbuffer(view)
+        if antialias:
+            self.antialias(view)
         self.project(view)
         self.sort(view, cull)
-        self.composite_fwd(view)
+        if antialias:
+            self.composite_fwd_aa(view)
+        else:
+            self.composite_fwd(view)
         self.fetch_counts()
 
-    def fit_lists(self, view: int = 0, cull: bool = True):
+    def fit_lists(self, view: int = 0, cull: bool = True, antialias: bool = False):
         """Run the list-producing calls (no compositing) until both lists fit."""
         self._single()
         while True:
             self.bin_and_zbuffer(view)
+            if antialias:
+                self.antialias(view)
             self.project(view)
             self.sort(view, cull)
             self.fetch_counts()
@@ -337,25 +399,34 @@ class Renderer:
             if self.read_counts():
                 return
 
-    def forward(self, view: int = 0, cull: bool = True):
+    def forward(self, view: int = 0, cull: bool = True, antialias: bool = False):
         while True:
-            self.forward_async(view, cull)
+            self.forward_async(view, cull, antialias)
             torch.cuda.current_stream().synchronize()
             if self.read_counts():
                 break
         return {"rgb": self.out_rgb, "depth": self.out_depth, "alpha": self.out_alpha}
 
     def backward(self, g_rgb, g_depth=None, g_alpha=None):
-        self.composite_bwd(self.view, g_rgb, g_depth, g_alpha)
+        """Reverse mode of the last forward: record gradients and dL/dc, dL/dD at the
+        covered pixels (with antialiasing through the layer, plus g_vscreen)."""
+        if getattr(self, "aa", False):
+            self.composite_bwd_aa(self.view, g_rgb, g_depth, g_alpha)
+            self.antialias_bwd(self.view)
+        else:
+            self.composite_bwd(self.view, g_rgb, g_depth, g_alpha)
         return {"rec": self.g_rec[: self.N], "mesh_rgb": self.g_mesh_rgb, "mesh_depth": self.g_mesh_depth}
 
-    def step(self, view: int, grads: dict, cull: bool = True):
+    def step(self, view: int, grads: dict, cull: bool = True, antialias: bool = False):
         """One forward + backward of one view (the benchmark's unit of work)."""
-        self.forward(view, cull)
+        self.forward(view, cull, antialias)
         return self.backward(grads["rgb"], grads.get("depth"), grads.get("alpha"))
 
-    def step_async(self, view: int, grads: dict, cull: bool = True):
+    def step_async(self, view: int, grads: dict, cull: bool = True, antialias: bool = False):
         """step() without synchronisation: the lengths are checked by the caller with
         read_counts() after the stream has run (the lists must already be large enough)."""
-        self.forward_async(view, cull)
-        self.composite_bwd(view, grads["rgb"], grads.get("depth"), grads.get("alpha"))
+        self.forward_async(view, cull, antialias)
+        if antialias:
+            self.composite_bwd_aa(view, grads["rgb"], grads.get("depth"), grads.get("alpha"))
+        else:
+            self.composite_bwd(view, grads["rgb"], grads.get("depth"), grads.get("alpha"))

@@ -311,6 +311,97 @@ gm_status gm_mesh_bwd(const gm_camera* cam, const gm_mesh* mesh, const gm_light*
                       float* g_light, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * 9. Analytic edge antialiasing (README "Design Details > Mesh rasterizer", step 3,
+ * and "Limitations and Todos": as in nvdiffrast, wherever two neighbouring pixels
+ * see a silhouette, the point where the front surface's edge crosses between the
+ * two pixel centres gives a fractional coverage and blends the colour over the
+ * farther surface; internal edges of a connected surface are left alone; a
+ * per-axis one-dimensional approximation, exact for straight edges away from
+ * corners.  "Hybrid rendering": the mesh coverage a_m is then fractional at
+ * silhouettes and the general two-layer composite
+ * C = C_front + T_front (a_m c_m + (1 - a_m)(C_back + T_back bg)) applies).
+ *
+ * Readings (what the README leaves open):
+ *  - Pairs: horizontally and vertically adjacent pixels whose z-buffer faces
+ *    differ.  The front pixel a is the covered one, or the one with the smaller
+ *    depth-buffer value (equal: smaller face id); b is the other.
+ *  - The segment from a's centre to b's is followed over the front surface: it
+ *    leaves a triangle through the edge whose inside-positive edge function falls
+ *    to zero first, t = e(a) / (e(a) - e(b)) (edges with e(b) < e(a); ties: lower
+ *    edge index); an internal edge passes it to the neighbouring face; the first
+ *    silhouette edge gives the crossing t in [0, 1).  No effect when a triangle
+ *    holds the rest of the segment or after 16 triangles.
+ *  - Silhouette edge (edge k of face f runs from corner k+1 to corner k+2): no
+ *    other face has its two vertex indices, several do, the one that does is not
+ *    drawn in this view (masked, behind the near plane, zero area), or it faces
+ *    the other way (opposite sign of the screen-space area).
+ *  - Horizontal pairs take edges at least as steep as 45 degrees (|dv| >= |du|),
+ *    vertical pairs the others.
+ *  - 1D box filter: d = t - 1/2 < 0 moves the fraction -d of a to b's surface;
+ *    d > 0 gives b the fraction d of a's surface.  A pixel's surface is its
+ *    z-buffer colour c and depth D; an uncovered pixel has none.
+ *  - Per pixel the pairs' effects add up into weights of its own and its four
+ *    neighbours' surfaces: coverage a = sum of weights, premultiplied colour
+ *    M = sum w c, depth M_D = sum w D.  a is clamped to [0, 1] with M and M_D
+ *    scaled by (clamped / raw) (0 for raw <= 0).
+ *  - The depth that splits the Gaussians: D on a covered pixel; on an uncovered
+ *    pixel that receives coverage, the smallest D of the neighbours giving it;
+ *    +inf otherwise.
+ * Decisions and crossings are fp64 from the fp32 screen vertices (no contraction).
+ *
+ * gm_edge_adjacency: adj [3][F] int32, for edge k of face f the one other face with
+ * the same two vertex indices, -1 if none, -2 if several; view independent, once
+ * per mesh.  Workspace gm_edge_adjacency_ws(F) bytes (a hash table).
+ *
+ * gm_antialias: from the z-buffer of call 2 (face_id, depth), vscreen of call 1 and
+ * adj, writes colour [H][W][3] (the shaded surface colour at covered pixels, 0
+ * elsewhere; needed again by the reverse mode) and the mesh layer [H][W][8] =
+ * (M_r, M_g, M_b, M_D, a_m, D_split, 0, 0) (16-byte aligned).  When tile_dmax (the
+ * cull bound of call 2) is given, every tile holding a covered pixel with a_m < 1
+ * gets +inf, so that call 4 culls only where the back layer is hidden.
+ *
+ * gm_composite_hybrid_fwd_aa / _bwd_aa: calls 5 and 6 with the mesh given by its
+ * layer (bg: host, 3 floats, as in call 5).  Both layers follow the per-layer rules of call 5; the back layer is
+ * composited where it is visible (a_m < 1 and a finite D_split).  Outputs as call
+ * 5: rgb = C_F + T_F (M + (1 - a_m)(C_B + T_B bg)), alpha = 1 - T_F (1 - a_m) T_B,
+ * depth = Z_F + T_F (M_D + (1 - a_m) Z_B).  state [H][W][8] = (T_F, last_F as
+ * int32, T_B, last_B as int32, C_B rgb, Z_B).  The reverse mode writes g_rec as
+ * call 6 (zero-filled first) and g_layer [H][W][8] = dL/d(M_rgb, M_D, a_m,
+ * D_split), 0, 0.
+ *
+ * gm_antialias_bwd: reverse mode of gm_antialias.  From g_layer it writes
+ * g_mesh_rgb [H][W][3] and g_mesh_depth [H][W] (dL/dc and dL/dD at covered pixels'
+ * own centres, 0 elsewhere: the inputs of call 8) and g_vscreen [2][V] (dL/du,
+ * dL/dv of the screen vertices through the crossings; zero-filled first).  The
+ * decisions (front pixel, edge, silhouette, axis, clamp branch, split neighbour)
+ * carry no gradient.  Workspace gm_antialias_bwd_ws(width, height) bytes.
+ *
+ * gm_vscreen_bwd: adds to g_verts [3][V] the chain of g_vscreen through the
+ * camera projection of call 1 (after call 8, which zero-fills g_verts).
+ * ------------------------------------------------------------------------- */
+size_t gm_edge_adjacency_ws(int32_t F);
+gm_status gm_edge_adjacency(const gm_mesh* mesh, int32_t* adj, void* ws, size_t ws_bytes, hipStream_t stream);
+gm_status gm_antialias(const gm_camera* cam, const gm_mesh* mesh, const float* vscreen, const int32_t* adj,
+                       const gm_light* light, const int32_t* face_id, const float* depth, float* colour,
+                       float* layer, float* tile_dmax, hipStream_t stream);
+gm_status gm_composite_hybrid_fwd_aa(const gm_camera* cam, const float* rec, const int32_t* tile_ranges,
+                                     const int32_t* sorted_ids, const float* layer, const float* bg,
+                                     float softness, float* out_rgb, float* out_depth, float* out_alpha,
+                                     float* state, hipStream_t stream);
+gm_status gm_composite_hybrid_bwd_aa(const gm_camera* cam, int32_t N, const float* rec,
+                                     const int32_t* tile_ranges, const int32_t* sorted_ids, const float* layer,
+                                     const float* bg, float softness, const float* state, const float* g_rgb,
+                                     const float* g_depth, const float* g_alpha, float* g_rec, float* g_layer,
+                                     hipStream_t stream);
+size_t gm_antialias_bwd_ws(int32_t width, int32_t height);
+gm_status gm_antialias_bwd(const gm_camera* cam, const gm_mesh* mesh, const float* vscreen, const int32_t* adj,
+                           const int32_t* face_id, const float* depth, const float* colour,
+                           const float* g_layer, float* g_mesh_rgb, float* g_mesh_depth, float* g_vscreen,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+gm_status gm_vscreen_bwd(const gm_camera* cam, const gm_mesh* mesh, const float* g_vscreen, float* g_verts,
+                         hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Auxiliary.
  * gm_build_mipmaps: README v1.1 (trilinear mipmapping by default): box-filter
  * pyramid of a square power-of-two texture tex [S][S][3] (HWC, values in [0, 1]);
