@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector (counts packed FMA)
 STAGES = ["bin", "zbuffer", "project", "sort", "fwd", "bwd"]
+STAGES_AA = ["bin", "zbuffer", "antialias", "project", "sort", "fwd", "bwd", "antialias_bwd"]
 
 WORKLOADS = {
     "c3": "1920x1080, 200k-face displaced sphere (vertex colour + Phong), 1M Gaussians SH3",
@@ -60,6 +61,8 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--batch-views", action="store_true",
                     help="one step = every view of the workload with one batched projection")
+    ap.add_argument("--antialias", action="store_true",
+                    help="the path with analytic edge antialiasing (two-layer composite)")
     return ap.parse_args()
 
 
@@ -119,32 +122,48 @@ def main():
     cam = ds.cams[view]
     torch.cuda.synchronize()
 
+    aa = args.antialias and scene.F > 0
+    stages = STAGES_AA if aa else STAGES
+
     def step(ev=None):
         st = torch.cuda.current_stream().cuda_stream
+        i = [0]
 
-        def mark(i):
+        def mark():
             if ev is not None:
-                ev[i].record()
-        mark(0)
+                ev[i[0]].record()
+            i[0] += 1
+        mark()
         G.gm_bin_triangles(cam, ds.mesh, r.vscreen, r.tile_offsets, r.tile_tris, r.pair_cap, r.counts[0:1],
                            r.ws_bin, st)
-        mark(1)
+        mark()
         G.gm_raster_zbuffer(cam, ds.mesh, r.vscreen, r.tile_offsets, r.tile_tris, r.face_id, r.depth,
                             r.tile_dmax, st)
-        mark(2)
+        mark()
+        if aa:
+            r.antialias(view)
+            mark()
         r.project(view)
-        mark(3)
+        mark()
         r.sort(view, True)
-        mark(4)
-        r.composite_fwd(view)
-        mark(5)
-        r.composite_bwd(view, g["rgb"], g["depth"], g["alpha"])
-        mark(6)
+        mark()
+        if aa:
+            r.composite_fwd_aa(view)
+            mark()
+            r.composite_bwd_aa(view, g["rgb"], g["depth"], g["alpha"])
+            mark()
+            r.antialias_bwd(view)
+            mark()
+        else:
+            r.composite_fwd(view)
+            mark()
+            r.composite_bwd(view, g["rgb"], g["depth"], g["alpha"])
+            mark()
         r.fetch_counts()  # list lengths to pinned host memory, checked after the run
 
     # list capacities first (binning, projection and sorting only), then the warm-up;
     # no step synchronises: the lengths are read back once the stream has finished
-    r.fit_lists(view, True)
+    r.fit_lists(view, True, antialias=aa)
     for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()
@@ -153,7 +172,7 @@ def main():
         torch.cuda.synchronize()
 
     # timed region: K whole steps; stage events on the library's (current) stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -167,13 +186,17 @@ def main():
     if not r.read_counts():  # every timed step used the same capacities as the warm-up
         raise RuntimeError("a list outgrew its capacity inside the timed region")
     ms = t0.elapsed_time(t1) / args.steps
-    stage_ms = {s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, s in enumerate(STAGES)}
+    stage_ms = {s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, s in enumerate(stages)}
 
     px = scene.width * scene.height
     value = px / (ms * 1e-3) / 1e6
     N = scene.N
     nvis = int((r.rec[:N, 15].view(torch.int32) > 0).sum().item()) if N else 0
-    walked = int(r.state_last.sum().item())  # pairs up to each pixel's last included entry
+    if aa:  # pairs up to each pixel's last included entry of either layer
+        st_aa = r.state_aa.view(-1, 8)
+        walked = int(torch.maximum(st_aa[:, 1].view(torch.int32), st_aa[:, 3].view(torch.int32)).sum().item())
+    else:
+        walked = int(r.state_last.sum().item())  # pairs up to each pixel's last included entry
     incl_frac = included_fraction(scene, view) if N else 0.0
 
     # compulsory HBM bytes per stage (each input read once, each output written once)
@@ -188,6 +211,15 @@ def main():
         "fwd": 4 * K + 64 * nvis + 8 * HW + 12 * HW + 20 * HW + 20 * HW,
         "bwd": 4 * K + 64 * nvis + 8 * HW + 8 * HW + 12 * HW + 20 * HW + 52 * nvis + 16 * HW,
     }
+    if aa:
+        # the layer: face ids, depths and colours of each pixel and its neighbours
+        # (one read each), screen vertices and faces once, the layer written (32 B)
+        alg_bytes["antialias"] = 4 * HW + 4 * HW + 12 * HW + 12 * V + 12 * F + 32 * HW
+        # the two-layer composite reads the layer instead of face id, depth and colour,
+        # and keeps 32 B of state instead of 8
+        alg_bytes["fwd"] += 32 * HW - 20 * HW + 24 * HW
+        alg_bytes["bwd"] += 32 * HW - 20 * HW + 24 * HW + 32 * HW
+        alg_bytes["antialias_bwd"] = 4 * HW + 4 * HW + 12 * HW + 32 * HW + 12 * V + 12 * F + 16 * HW + 8 * V
     alg_flops = {
         "fwd": walked * FLOPS_EVAL + walked * incl_frac * FLOPS_ACCUM,
         "bwd": walked * FLOPS_EVAL + walked * incl_frac * FLOPS_GRAD,
@@ -209,7 +241,11 @@ def main():
         ach = alg_bytes[dom] / dom_s / 1e9
         roof = {"kernel": kname, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = measured_traffic(kname, kfile, args.config)
+    tname = kname
+    if aa and dom in ("fwd", "bwd"):  # the two-layer instantiation of the composite kernel
+        roof["kernel"] = kname + "<two-layer>"
+        tname = kname + "_aa"
+    roof["traffic"] = measured_traffic(tname, kfile, args.config)
     roof["units"] = {"walked_pairs": walked, "included_fraction": round(incl_frac, 4)} if dom in alg_flops \
         else {"algorithmic_bytes": alg_bytes[dom]}
     roof["launch_ms"] = round(stage_ms[dom], 4)
@@ -217,6 +253,9 @@ def main():
     next_stages = {"project_bwd": time_project_bwd(r, scene, view, args.steps)} if N else {}
     if scene.F:
         next_stages["mesh_bwd"] = time_mesh_bwd(r, scene, view, args.steps)
+        if aa:
+            next_stages["vscreen_bwd_ms"] = time_call(lambda: G.gm_vscreen_bwd(
+                cam, ds.mesh, r.g_vscreen, r.gm_verts, torch.cuda.current_stream().cuda_stream), args.steps)
 
     total_alg = sum(alg_bytes.values())
     out = {
@@ -224,7 +263,8 @@ def main():
         "value": round(value, 3), "unit": "Mpixels/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded PCG64 scene generators)",
-        "config": {"workload": f"{args.config}: {WORKLOADS[args.config]}", "view": view,
+        "config": {"workload": f"{args.config}: {WORKLOADS[args.config]}" + (", edge antialiasing" if aa else ""),
+                   "view": view,
                    "width": scene.width, "height": scene.height, "faces": scene.F, "gaussians": N,
                    "tri_tile_pairs": r.n_pairs, "keys": r.n_keys, "visible": nvis, "parallelism": "single GPU"},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
@@ -306,6 +346,18 @@ def main_batch(args, scene):
         "wall_s": round(wall, 3),
     }
     print(json.dumps(out), flush=True)
+
+
+def time_call(fn, steps):
+    import torch
+    fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) / steps, 4)
 
 
 def time_project_bwd(r, scene, view, steps):
