@@ -101,3 +101,38 @@ def test_argument_errors_before_any_launch(G):
     # nothing to do: no views, or no Gaussians (no pointer is touched)
     assert L.gm_project_gaussians_multi(cams, 0, 5, None, None, None, None, None, 0, None, None) == G.GM_OK
     assert L.gm_project_gaussians_multi(cams, 1, 0, None, None, None, None, None, 0, None, None) == G.GM_OK
+
+
+def test_antialias_argument_errors(G):
+    L = G.lib()
+    cam = _cam(G)
+    m = G.GmMesh()
+    m.V, m.F = 3, 1
+    # adjacency: NULL faces / adj, workspace too small
+    assert L.gm_edge_adjacency(C.byref(m), 16, 16, 1, None) == G.GM_ERR_ARG
+    assert L.gm_edge_adjacency(None, 16, 16, 1 << 20, None) == G.GM_ERR_ARG
+    m0 = G.GmMesh()
+    assert L.gm_edge_adjacency(C.byref(m0), None, None, 0, None) == G.GM_OK  # F = 0: nothing to do
+    m.faces, m.verts = 16, 16
+    # the layer: missing adjacency, misaligned layer
+    assert L.gm_antialias(C.byref(cam), C.byref(m), 16, None, None, 16, 16, 16, 16, None, None) == G.GM_ERR_ARG
+    assert L.gm_antialias(C.byref(cam), C.byref(m), 16, 16, None, 16, 16, 16, 17, None, None) == G.GM_ERR_ARG
+    # two-layer composite: NULL layer, misaligned state, negative softness
+    assert L.gm_composite_hybrid_fwd_aa(C.byref(cam), 16, 16, 16, None, 16, C.c_float(1.0), 16, 16, 16, 16,
+                                        None) == G.GM_ERR_ARG
+    assert L.gm_composite_hybrid_fwd_aa(C.byref(cam), 16, 16, 16, 16, 16, C.c_float(1.0), 16, 16, 16, 17,
+                                        None) == G.GM_ERR_ARG
+    assert L.gm_composite_hybrid_bwd_aa(C.byref(cam), 1, 16, 16, 16, 16, 16, C.c_float(-1.0), 16, 16, None, None, 16,
+                                        16, None) == G.GM_ERR_ARG
+    assert b"softness" in L.gm_last_error()
+    # antialiasing reverse mode: workspace too small, NULL screen-vertex gradient
+    ws = G.gm_antialias_bwd_ws(64, 64)
+    assert ws == 64 * 64 * 32
+    assert L.gm_antialias_bwd(C.byref(cam), C.byref(m), 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, ws - 1,
+                              None) == G.GM_ERR_ARG
+    assert L.gm_antialias_bwd(C.byref(cam), C.byref(m), 16, 16, 16, 16, 16, 16, 16, 16, None, 16, ws,
+                              None) == G.GM_ERR_ARG
+    # the vertex chain: NULL verts
+    m.verts = None
+    assert L.gm_vscreen_bwd(C.byref(cam), C.byref(m), 16, 16, None) == G.GM_ERR_ARG
+    assert G.gm_edge_adjacency_ws(10) > 0
