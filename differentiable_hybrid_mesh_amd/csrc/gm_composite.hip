@@ -401,7 +401,9 @@ __device__ __forceinline__ void wave_dmax(bool inside, bool on, float D, float* 
 // AA = true: the antialiased mesh layer (premultiplied colour M and depth M_D,
 // coverage a_m, split depth D) and the general two-layer form
 // C = C_F + T_F (M + (1 - a_m)(C_B + T_B bg)); the back layer is composited where
-// it is visible (a_m < 1, finite D), with the same per-layer rules.
+// it is visible (a_m < 1, finite D), with the same per-layer rules, and stops when
+// the front layer stops (the 3DGS stop is per pixel; the back layer is seen only
+// through T_F).
 struct AaLayer {
     float M0, M1, M2, MD, am, D;
 };
@@ -487,6 +489,7 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, const float* _
                 done = done | stop;
                 if constexpr (AA) {
                     const float aB = pr.al * pr.fb;
+                    doneB = doneB | done;  // the pixel stops with its front layer
                     const bool liveB = !doneB & !(pr.q > g.d.z) & (pr.al >= SKIP_ALPHA) & (aB >= SKIP_ALPHA);
                     const float TnB = TB * (1.0f - aB);
                     const bool stopB = liveB & (TnB < STOP_T);

@@ -361,8 +361,10 @@ gm_status gm_mesh_bwd(const gm_camera* cam, const gm_mesh* mesh, const gm_light*
  * gets +inf, so that call 4 culls only where the back layer is hidden.
  *
  * gm_composite_hybrid_fwd_aa / _bwd_aa: calls 5 and 6 with the mesh given by its
- * layer (bg: host, 3 floats, as in call 5).  Both layers follow the per-layer rules of call 5; the back layer is
- * composited where it is visible (a_m < 1 and a finite D_split).  Outputs as call
+ * layer (bg: host, 3 floats, as in call 5).  Both layers follow the per-layer
+ * rules of call 5; the back layer is composited where it is visible (a_m < 1 and a
+ * finite D_split), and the pixel stops when its front layer stops (the 3DGS stop
+ * is per pixel, and the back layer is seen only through T_F).  Outputs as call
  * 5: rgb = C_F + T_F (M + (1 - a_m)(C_B + T_B bg)), alpha = 1 - T_F (1 - a_m) T_B,
  * depth = Z_F + T_F (M_D + (1 - a_m) Z_B).  state [H][W][8] = (T_F, last_F as
  * int32, T_B, last_B as int32, C_B rgb, Z_B).  The reverse mode writes g_rec as

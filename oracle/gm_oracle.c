@@ -822,9 +822,11 @@ static double reld(double x, double thr) { return fabs(x - thr) / thr; }
  * C = C_F + T_F (M + (1 - a_m)(C_B + T_B bg)), alpha = 1 - T_F (1 - a_m) T_B,
  * depth = Z_F + T_F (M_D + (1 - a_m) Z_B), with M, M_D the premultiplied mesh colour
  * and depth.  Both layers follow the 3DGS rules on their own (skip below 1/255,
- * stop before T < 1e-4).  The back layer is composited only where it is visible
- * (a_m < 1 and a finite split depth); elsewhere it is empty (C_B = 0, Z_B = 0,
- * T_B = 1).  The reverse mode is exact for both layers: the back layer sees the
+ * stop before T < 1e-4), and the pixel stops when its front layer stops: the back
+ * layer is seen only through T_front, and the 3DGS stop is per pixel (nothing after
+ * it counts), so neither layer takes that entry or any later one.  The back layer
+ * is composited only where it is visible (a_m < 1 and a finite split depth);
+ * elsewhere it is empty (C_B = 0, Z_B = 0, T_B = 1).  The reverse mode is exact for both layers: the back layer sees the
  * upstream gradients scaled by k = T_F (1 - a_m), with behind it bg (depth 0) and
  * the alpha term; per entry dL/dalpha = f dL/dalpha_F + (1 - f) dL/dalpha_B and
  * dL/df = alpha (dL/dalpha_F - dL/dalpha_B). */
@@ -857,6 +859,7 @@ static void composite_pixel_aa(const oc_comp* a, int p, double pu, double pv, lo
             if (m2 < mg) mg = m2;
             if (Tn < thr_stop) {
                 *alive = 0;
+                if (layer == 0) aliveB = 0; /* the pixel stops with its front layer */
                 continue;
             }
             double w = aL * *T;
