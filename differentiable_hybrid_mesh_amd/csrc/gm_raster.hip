@@ -145,13 +145,22 @@ __global__ void k_bin_scatter(DevCamera cam, int F, int T, const int2* __restric
     }
 }
 
-// Triangle setup as staged in LDS: one 128-byte record.
-struct TriSetup {
-    double u[3], v[3];   // screen vertices
-    double du[3], dv[3]; // edge deltas b - a of edges (v1,v2), (v2,v0), (v0,v1)
-    double z[3];         // camera depths
-    double A;            // twice the signed area
-};
+// Triangle setup as staged in LDS, one plane per field (structure of arrays), so
+// that lanes reading the setups of different triangles hit consecutive banks:
+// screen vertices u, v; camera depths z; twice the signed area A.  The edge
+// deltas b - a of edges (v1,v2), (v2,v0), (v0,v1) are formed where they are used.
+enum TriField { TU = 0, TV = 3, TZ = 6, TA = 9, TFIELDS = 10 };
+
+// E_k = (b.u - a.u)(p.v - a.v) - (b.v - a.v)(p.u - a.u) for the edges above.
+__device__ __forceinline__ void edge_functions(const double (*s_t)[ZB_BATCH], int j, double pu, double pv,
+                                               double& E0, double& E1, double& E2)
+{
+    const double u0 = s_t[TU][j], u1 = s_t[TU + 1][j], u2 = s_t[TU + 2][j];
+    const double v0 = s_t[TV][j], v1 = s_t[TV + 1][j], v2 = s_t[TV + 2][j];
+    E0 = (u2 - u1) * (pv - v1) - (v2 - v1) * (pu - u1);
+    E1 = (u0 - u2) * (pv - v2) - (v0 - v2) * (pu - u2);
+    E2 = (u1 - u0) * (pv - v0) - (v1 - v0) * (pu - u0);
+}
 
 constexpr int ZB_CHUNK = 1024;  // candidates per round (bounds the covered list)
 constexpr int ZB_PER_THREAD = ZB_CHUNK / ZB_THREADS;
@@ -173,7 +182,7 @@ k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
           const int32_t* __restrict__ tile_tris, int32_t* __restrict__ face_id,
           float* __restrict__ depth, float* __restrict__ tile_dmax)
 {
-    __shared__ TriSetup s_t[ZB_BATCH];
+    __shared__ double s_t[TFIELDS][ZB_BATCH];
     __shared__ int s_f[ZB_BATCH];
     __shared__ int4 s_box[ZB_BATCH];       // clipped box in tile-local pixels: x0, w, y0, bits of 1/w
     __shared__ int s_coff[ZB_BATCH + 1];   // candidate prefix sums
@@ -206,21 +215,22 @@ k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
         if (threadIdx.x < nb) {
             const int j = threadIdx.x;
             const int f = tile_tris[b0 + j];
-            TriSetup t;
+            struct {
+                double u[3], v[3], z[3];
+            } t;
             for (int k = 0; k < 3; ++k) {
                 const int vi = faces[k * F + f];
                 t.u[k] = (double)vs[vi];
                 t.v[k] = (double)vs[V + vi];
                 t.z[k] = (double)vs[2 * V + vi];
             }
-            t.du[0] = t.u[2] - t.u[1];
-            t.dv[0] = t.v[2] - t.v[1];
-            t.du[1] = t.u[0] - t.u[2];
-            t.dv[1] = t.v[0] - t.v[2];
-            t.du[2] = t.u[1] - t.u[0];
-            t.dv[2] = t.v[1] - t.v[0];
-            t.A = (t.u[1] - t.u[0]) * (t.v[2] - t.v[0]) - (t.v[1] - t.v[0]) * (t.u[2] - t.u[0]);
-            s_t[j] = t;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                s_t[TU + k][j] = t.u[k];
+                s_t[TV + k][j] = t.v[k];
+                s_t[TZ + k][j] = t.z[k];
+            }
+            s_t[TA][j] = (t.u[1] - t.u[0]) * (t.v[2] - t.v[0]) - (t.v[1] - t.v[0]) * (t.u[2] - t.u[0]);
             s_f[j] = f;
             // a pixel centre covered by the triangle lies in its bounding box; the box
             // is widened by a pixel so that it never excludes a pixel the fp64 edge
@@ -279,12 +289,9 @@ k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
                     const int qy = (int)(((float)loc + 0.5f) * __int_as_float(bx.w));
                     const int ly = bx.z + qy, lx = bx.x + (loc - qy * bx.y);
                     const double pu = ox + lx + 0.5, pv = oy + ly + 0.5;
-                    const TriSetup& t = s_t[j];
-                    // E_k = (b.u - a.u)(p.v - a.v) - (b.v - a.v)(p.u - a.u)
-                    const double E0 = t.du[0] * (pv - t.v[1]) - t.dv[0] * (pu - t.u[1]);
-                    const double E1 = t.du[1] * (pv - t.v[2]) - t.dv[1] * (pu - t.u[2]);
-                    const double E2 = t.du[2] * (pv - t.v[0]) - t.dv[2] * (pu - t.u[0]);
-                    cov = t.A > 0 ? (E0 >= 0 && E1 >= 0 && E2 >= 0) : (E0 <= 0 && E1 <= 0 && E2 <= 0);
+                    double E0, E1, E2;
+                    edge_functions(s_t, j, pu, pv, E0, E1, E2);
+                    cov = s_t[TA][j] > 0 ? (E0 >= 0 && E1 >= 0 && E2 >= 0) : (E0 <= 0 && E1 <= 0 && E2 <= 0);
                     p = ly * GM_TILE + lx;
                 }
                 const unsigned long long m = __ballot(cov);
@@ -304,13 +311,11 @@ k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
                 const int e = s_cov[q];
                 const int p = e & 0xff, jj = e >> 8;
                 const double pu = ox + (p & 15) + 0.5, pv = oy + (p >> 4) + 0.5;
-                const TriSetup& t = s_t[jj];
-                const double E0 = t.du[0] * (pv - t.v[1]) - t.dv[0] * (pu - t.u[1]);
-                const double E1 = t.du[1] * (pv - t.v[2]) - t.dv[1] * (pu - t.u[2]);
-                const double E2 = t.du[2] * (pv - t.v[0]) - t.dv[2] * (pu - t.u[0]);
-                const double A = t.A;
+                double E0, E1, E2;
+                edge_functions(s_t, jj, pu, pv, E0, E1, E2);
+                const double A = s_t[TA][jj];
                 const double l0 = E0 / A, l1 = E1 / A, l2 = E2 / A;
-                const double inv = (l0 / t.z[0] + l1 / t.z[1]) + l2 / t.z[2];
+                const double inv = (l0 / s_t[TZ + 0][jj] + l1 / s_t[TZ + 1][jj]) + l2 / s_t[TZ + 2][jj];
                 const double z = 1.0 / inv;
                 const unsigned long long zb = (unsigned long long)__double_as_longlong(z);
                 atomicMin(&s_minz[p], zb);
