@@ -130,6 +130,46 @@ __global__ void __launch_bounds__(SCAN_THREADS) k_scan_apply(const int32_t* __re
     if (blockIdx.x == 0 && threadIdx.x == 0) out[n] = (int32_t)*total;
 }
 
+// Apply pass that forms its own block offset: the sum of the block sums before it
+// (read by the whole block; used when there are few blocks, so the extra reads are
+// small and the single-block pass over the sums is not needed).  The last block
+// writes the grand total.
+constexpr int64_t SCAN2_MAX_BLOCKS = 1024;
+
+__global__ void __launch_bounds__(SCAN_THREADS) k_scan_apply_self(const int32_t* __restrict__ in, int64_t n,
+                                                                  const long long* __restrict__ sums,
+                                                                  long long* __restrict__ total,
+                                                                  int32_t* __restrict__ out)
+{
+    __shared__ long long lds[SCAN_THREADS / 64];
+    long long p = 0;
+    for (int64_t i = threadIdx.x; i < (int64_t)blockIdx.x; i += SCAN_THREADS) p += sums[i];
+    long long pre;
+    block_incl_scan(p, lds, &pre);
+    const int64_t base = (int64_t)blockIdx.x * SCAN_CHUNK + (int64_t)threadIdx.x * SCAN_ITEMS;
+    int32_t v[SCAN_ITEMS];
+    long long s = 0;
+#pragma unroll
+    for (int k = 0; k < SCAN_ITEMS; ++k) {
+        int64_t i = base + k;
+        v[k] = i < n ? in[i] : 0;
+        s += v[k];
+    }
+    long long btot;
+    long long inc = block_incl_scan(s, lds, &btot);
+    long long run = pre + inc - s;
+#pragma unroll
+    for (int k = 0; k < SCAN_ITEMS; ++k) {
+        int64_t i = base + k;
+        if (i < n) out[i] = (int32_t)run;
+        run += v[k];
+    }
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
+        out[n] = (int32_t)(pre + btot);
+        *total = pre + btot;
+    }
+}
+
 // Single block of 1024 threads: the whole scan for short inputs (one launch).
 // Thread t owns items [16 t, 16 t + 16), read as four 16-byte loads when both
 // arrays are 16-byte aligned.
@@ -206,6 +246,11 @@ gm_status exclusive_scan(const int32_t* in, int32_t* out, int64_t n, long long* 
     long long* sums = (long long*)ws;
     k_scan_block_sums<<<(unsigned)nb, SCAN_THREADS, 0, stream>>>(in, n, sums);
     GM_LAUNCH_CHECK();
+    if (nb <= SCAN2_MAX_BLOCKS) {
+        k_scan_apply_self<<<(unsigned)nb, SCAN_THREADS, 0, stream>>>(in, n, sums, total, out);
+        GM_LAUNCH_CHECK();
+        return GM_OK;
+    }
     k_scan_sums<<<1, 1024, 0, stream>>>(sums, nb, total);
     GM_LAUNCH_CHECK();
     k_scan_apply<<<(unsigned)nb, SCAN_THREADS, 0, stream>>>(in, n, sums, total, out);
