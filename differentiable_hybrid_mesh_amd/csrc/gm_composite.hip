@@ -278,11 +278,24 @@ __device__ __forceinline__ Pair eval_pair(const Staged& g, float pxc, float pyc,
         const float num = (D - g.c.y) - __builtin_fmaf(g.c.z, p.dx, g.c.w * p.dy);
         if (softness > 0.0f) {
             p.s = on ? num * g.d.y : 0.0f;  // off the mesh D = +inf: keep s finite
-            float pd, fc;
-            const float fo = normal_cdf_pdf(p.s, pd, fc);
-            p.f = on ? fo : 1.0f;
-            p.fb = on ? fc : 0.0f;
-            p.pdf = on ? pd : 0.0f;
+            if (__ballot(on & (fabsf(p.s) <= 6.0f))) {
+                float pd, fc;
+                const float fo = normal_cdf_pdf(p.s, pd, fc);
+                p.f = on ? fo : 1.0f;
+                p.fb = on ? fc : 0.0f;
+                p.pdf = on ? pd : 0.0f;
+            } else {
+                // every lane of the wave is off the mesh or has |s| > 6: there the
+                // tail Phi(-|s|) <= exp(-18)/2 < 2^-25, so the evaluation above gives
+                // exactly 1 for the larger share and, for the smaller one, a value
+                // whose product with alpha is far below the 1/255 skip threshold; the
+                // same decisions and, with the density computed as above, the same
+                // gradients, without the erfc polynomial
+                const bool behind = on && !(p.s > 0.0f);
+                p.f = behind ? 0.0f : 1.0f;
+                p.fb = behind ? 1.0f : 0.0f;
+                p.pdf = on ? 0.39894228040143268f * __expf(-0.5f * p.s * p.s) : 0.0f;
+            }
         } else {
             const bool behind = on && !(num > 0.0f);
             p.f = behind ? 0.0f : 1.0f;
