@@ -85,7 +85,17 @@ __device__ __forceinline__ void addf(float* p, double v)
     if (v != 0.0) unsafeAtomicAdd(p, (float)v);
 }
 
-__global__ void __launch_bounds__(MB_THREADS, 2)
+// Which per-corner gradient planes a variant produces: position (0-2) always,
+// vertex colour (3-5) when untextured, normal (6-8) when lit, uv (9-10) when textured.
+template <bool TEX, bool LIT>
+__device__ __forceinline__ constexpr bool plane_live(int j)
+{
+    return j < 3 || (j < 6 ? !TEX : (j < 9 ? LIT : TEX));
+}
+
+// One variant per (textured, lit) pair, so that each holds only its own state.
+template <bool TEX, bool LIT>
+__global__ void __launch_bounds__(MB_THREADS, TEX ? 2 : 3)
 k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __restrict__ g_rgb,
            const float* __restrict__ g_depth, float* __restrict__ g_verts, float* __restrict__ g_vcolor,
            float* __restrict__ g_vnormal, float* __restrict__ g_uv, float* __restrict__ g_mips,
@@ -114,27 +124,32 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
 #pragma unroll
         for (int i = 0; i < 3; ++i) t[i] = P.cam.t[i];
         const double fx = P.cam.fx, fy = P.cam.fy, cx = P.cam.cx, cy = P.cam.cy;
+        const double rx = (pu - cx) / fx, ry = (pv - cy) / fy;  // the pixel's ray, z = 1
         // ---- forward ---------------------------------------------------------------
-        double xc[3][3], u[3], v[3], z[3];
+        // reciprocals taken once (the chain below multiplies by them: these are
+        // values, not decisions, so the rounding order is free)
+        double xc[3][3], u[3], v[3], z[3], iz[3];
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
             vi[k] = P.faces[k * P.F + f];
             const double X0 = P.verts[vi[k]], X1 = P.verts[P.V + vi[k]], X2 = P.verts[2 * P.V + vi[k]];
 #pragma unroll
             for (int r = 0; r < 3; ++r) xc[k][r] = R[3 * r] * X0 + R[3 * r + 1] * X1 + R[3 * r + 2] * X2 + t[r];
-            u[k] = fx * xc[k][0] / xc[k][2] + cx;
-            v[k] = fy * xc[k][1] / xc[k][2] + cy;
             z[k] = xc[k][2];
+            iz[k] = 1.0 / z[k];
+            u[k] = fx * xc[k][0] * iz[k] + cx;
+            v[k] = fy * xc[k][1] * iz[k] + cy;
         }
         const int ea[3] = {1, 2, 0}, eb[3] = {2, 0, 1};  // edge opposite corner k
         double lam[3], w[3], Wsum = 0.0;
         const double A = (u[1] - u[0]) * (v[2] - v[0]) - (v[1] - v[0]) * (u[2] - u[0]);
+        const double iA = 1.0 / A;
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
             const int a = ea[k], b = eb[k];
             const double E = (u[b] - u[a]) * (pv - v[a]) - (v[b] - v[a]) * (pu - u[a]);
-            lam[k] = E / A;
-            w[k] = lam[k] / z[k];
+            lam[k] = E * iA;
+            w[k] = lam[k] * iz[k];
             Wsum += w[k];
         }
         const double zz = 1.0 / Wsum;
@@ -149,11 +164,11 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
 
         // base colour (forward values needed by the lighting's backward)
         double base[3] = {0.0, 0.0, 0.0};
-        const bool textured = P.mips != nullptr;
+        constexpr bool textured = TEX;
         Bilin B0, B1;
         int l0 = 0, l1 = 0;
         double tl = 0.0, uvk[3][2], uu = 0.0, vv = 0.0;
-        if (textured) {
+        if constexpr (textured) {
 #pragma unroll
             for (int k = 0; k < 3; ++k) {
                 ti[k] = P.faces_uv[k * P.F + f];
@@ -165,12 +180,12 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
             double dux = 0.0, dvx = 0.0, duy = 0.0, dvy = 0.0;
 #pragma unroll
             for (int k = 0; k < 3; ++k) {
-                const double dwx = (-(v[eb[k]] - v[ea[k]]) / A) / z[k];
-                const double dwy = ((u[eb[k]] - u[ea[k]]) / A) / z[k];
-                dux += dwx * (uvk[k][0] - uu) / Wsum;
-                dvx += dwx * (uvk[k][1] - vv) / Wsum;
-                duy += dwy * (uvk[k][0] - uu) / Wsum;
-                dvy += dwy * (uvk[k][1] - vv) / Wsum;
+                const double dwx = (-(v[eb[k]] - v[ea[k]]) * iA) * iz[k];
+                const double dwy = ((u[eb[k]] - u[ea[k]]) * iA) * iz[k];
+                dux += dwx * (uvk[k][0] - uu) * zz;
+                dvx += dwx * (uvk[k][1] - vv) * zz;
+                duy += dwy * (uvk[k][0] - uu) * zz;
+                dvy += dwy * (uvk[k][1] - vv) * zz;
             }
             const double S0 = P.S;
             const double lx = sqrt(S0 * dux * S0 * dux + S0 * dvx * S0 * dvx);
@@ -194,7 +209,7 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
         }
 
         // ---- lighting (fp32: well conditioned): forward values, then reverse ---------------
-        if (P.lit && P.vnormal) {
+        if constexpr (LIT) {
             const float* Rf = P.cam.R;
             float nw[3], nt[3], L[3], x[3], lt[3], et[3];
 #pragma unroll
@@ -210,8 +225,8 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
                        P.cam.t[r];
             }
             const float zf = (float)zz;
-            x[0] = (float)((pu - cx) / fx) * zf;
-            x[1] = (float)((pv - cy) / fy) * zf;
+            x[0] = (float)rx * zf;
+            x[1] = (float)ry * zf;
             x[2] = zf;
 #pragma unroll
             for (int r = 0; r < 3; ++r) {
@@ -221,12 +236,13 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
             const float nn = sqrtf(nt[0] * nt[0] + nt[1] * nt[1] + nt[2] * nt[2]);
             const float ln = sqrtf(lt[0] * lt[0] + lt[1] * lt[1] + lt[2] * lt[2]);
             const float en = sqrtf(et[0] * et[0] + et[1] * et[1] + et[2] * et[2]);
+            const float inn = 1.0f / nn, iln = 1.0f / ln, ien = 1.0f / en;
             float n[3], l[3], e[3], rv[3];
 #pragma unroll
             for (int r = 0; r < 3; ++r) {
-                n[r] = nt[r] / nn;
-                l[r] = lt[r] / ln;
-                e[r] = et[r] / en;
+                n[r] = nt[r] * inn;
+                l[r] = lt[r] * iln;
+                e[r] = et[r] * ien;
             }
             const float ndl = n[0] * l[0] + n[1] * l[1] + n[2] * l[2];
 #pragma unroll
@@ -274,9 +290,9 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
             float gnt[3], glt[3], get[3];
 #pragma unroll
             for (int r = 0; r < 3; ++r) {  // normalisations
-                gnt[r] = (gn[r] - n[r] * dn) / nn;
-                glt[r] = (glv[r] - l[r] * dl) / ln;
-                get[r] = (ge[r] - e[r] * de) / en;
+                gnt[r] = (gn[r] - n[r] * dn) * inn;
+                glt[r] = (glv[r] - l[r] * dl) * iln;
+                get[r] = (ge[r] - e[r] * de) * ien;
             }
             float gnw[3];
 #pragma unroll
@@ -296,14 +312,14 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
             }
             // x = ((pu - cx)/fx z, (pv - cy)/fy z, z); lt = L - x, et = -x
             const float gx0 = -glt[0] - get[0], gx1 = -glt[1] - get[1], gx2 = -glt[2] - get[2];
-            gz += gx0 * (pu - cx) / fx + gx1 * (pv - cy) / fy + gx2;
+            gz += gx0 * rx + gx1 * ry + gx2;
         } else {
 #pragma unroll
             for (int c = 0; c < 3; ++c) gbase[c] = gc[c];
         }
 
         // ---- base colour ---------------------------------------------------------------
-        if (textured) {
+        if constexpr (textured) {
             double guu = 0.0, gvv = 0.0;
             float* m0 = g_mips ? g_mips + level_offset(P.S, l0) : nullptr;
             float* m1 = g_mips ? g_mips + level_offset(P.S, l1) : nullptr;
@@ -348,13 +364,13 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
 #pragma unroll
             for (int k = 0; k < 3; ++k) {
                 gw[k] += gW;
-                glam[k] = gw[k] / z[k];
-                gzk[k] = -gw[k] * lam[k] / (z[k] * z[k]);
+                glam[k] = gw[k] * iz[k];
+                gzk[k] = -gw[k] * lam[k] * (iz[k] * iz[k]);
             }
 #pragma unroll
             for (int k = 0; k < 3; ++k) {
-                const double gE = glam[k] / A;
-                gA -= glam[k] * lam[k] / A;
+                const double gE = glam[k] * iA;
+                gA -= glam[k] * lam[k] * iA;
                 const int a = ea[k], b = eb[k];
                 gu[a] += gE * (v[b] - pv);
                 gu[b] += gE * (pv - v[a]);
@@ -369,9 +385,9 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
             gv[2] += gA * (u[1] - u[0]);
 #pragma unroll
             for (int k = 0; k < 3; ++k) {
-                const double zc = xc[k][2];
-                const double gxc = gu[k] * fx / zc, gyc = gv[k] * fy / zc;
-                const double gzc = gzk[k] - gu[k] * fx * xc[k][0] / (zc * zc) - gv[k] * fy * xc[k][1] / (zc * zc);
+                const double i2 = iz[k] * iz[k];
+                const double gxc = gu[k] * fx * iz[k], gyc = gv[k] * fy * iz[k];
+                const double gzc = gzk[k] - gu[k] * fx * xc[k][0] * i2 - gv[k] * fy * xc[k][1] * i2;
 #pragma unroll
                 for (int j = 0; j < 3; ++j) acc[k][j] = (float)(R[j] * gxc + R[3 + j] * gyc + R[6 + j] * gzc);
             }
@@ -380,7 +396,7 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
     // Pixels of one face are runs of neighbouring lanes (a triangle meets a row in an
     // interval): a segmented sum over each run leaves the run's total in its last lane,
     // which alone adds it to the face's corners (one set of atomics per run).
-    {
+    if (__ballot(f >= 0)) {  // a wave with no covered pixel has nothing to add
         const int lane = threadIdx.x & 63;
         const int prev = __shfl_up(f, 1, 64);
         const unsigned long long heads = __ballot(lane == 0 || prev != f);
@@ -391,6 +407,7 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
         for (int k = 0; k < 3; ++k)
 #pragma unroll
             for (int j = 0; j < 11; ++j) {
+                if (!plane_live<TEX, LIT>(j)) continue;
                 float x = acc[k][j];
 #pragma unroll
                 for (int d = 1; d < 64; d <<= 1) {
@@ -405,11 +422,12 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
 #pragma unroll
                 for (int j = 0; j < 3; ++j) {
                     if (g_verts && acc[k][j] != 0.0f) unsafeAtomicAdd(&g_verts[j * P.V + vi[k]], acc[k][j]);
-                    if (g_vcolor && acc[k][3 + j] != 0.0f) unsafeAtomicAdd(&g_vcolor[j * P.V + vi[k]], acc[k][3 + j]);
-                    if (g_vnormal && acc[k][6 + j] != 0.0f)
+                    if (!TEX && g_vcolor && acc[k][3 + j] != 0.0f)
+                        unsafeAtomicAdd(&g_vcolor[j * P.V + vi[k]], acc[k][3 + j]);
+                    if (LIT && g_vnormal && acc[k][6 + j] != 0.0f)
                         unsafeAtomicAdd(&g_vnormal[j * P.V + vi[k]], acc[k][6 + j]);
                 }
-                if (g_uv) {
+                if (TEX && g_uv) {
                     if (acc[k][9] != 0.0f) unsafeAtomicAdd(&g_uv[ti[k]], acc[k][9]);
                     if (acc[k][10] != 0.0f) unsafeAtomicAdd(&g_uv[P.Vt + ti[k]], acc[k][10]);
                 }
@@ -516,9 +534,12 @@ extern "C" gm_status gm_mesh_bwd(const gm_camera* cam, const gm_mesh* mesh, cons
     if (gm_status s = zero(g_light, 13, stream)) return s;
     const int64_t HW = (int64_t)cam->width * cam->height;
     if (P.F > 0) {
-        k_mesh_bwd<<<(unsigned)div_up(HW, MB_THREADS), MB_THREADS, 0, stream>>>(
-            P, face_id, g_mesh_rgb, g_mesh_depth, g_verts, g_vcolor, P.lit ? g_vnormal : nullptr, g_uv, g_mips,
-            g_light);
+        const bool tex = P.mips != nullptr, lit = P.lit && P.vnormal;
+        auto kern = tex ? (lit ? k_mesh_bwd<true, true> : k_mesh_bwd<true, false>)
+                        : (lit ? k_mesh_bwd<false, true> : k_mesh_bwd<false, false>);
+        kern<<<(unsigned)div_up(HW, MB_THREADS), MB_THREADS, 0, stream>>>(
+            P, face_id, g_mesh_rgb, g_mesh_depth, g_verts, g_vcolor, lit ? g_vnormal : nullptr, g_uv, g_mips,
+            lit ? g_light : nullptr);
         GM_LAUNCH_CHECK();
     }
     if (g_mips && P.nlev > 1) {  // coarse to fine: level l - 1 += adjoint(level l)
