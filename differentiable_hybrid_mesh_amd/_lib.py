@@ -81,7 +81,7 @@ def lib():
     L.gm_edge_adjacency_ws.argtypes = [I32]
     L.gm_edge_adjacency_ws.restype = SZ
     L.gm_edge_adjacency.argtypes = [mesh, P, P, SZ, P]
-    L.gm_antialias.argtypes = [cam, mesh, P, P, light, P, P, P, P, P, P]
+    L.gm_antialias.argtypes = [cam, mesh, P, P, light, P, P, P, P, P, P, P]
     L.gm_composite_hybrid_fwd_aa.argtypes = [cam, P, P, P, P, P, F32, P, P, P, P, P]
     L.gm_composite_hybrid_bwd_aa.argtypes = [cam, I32, P, P, P, P, P, F32, P, P, P, P, P, P, P]
     L.gm_antialias_bwd_ws.argtypes = [I32, I32]
@@ -224,9 +224,9 @@ def gm_edge_adjacency(mesh, adj, ws, stream):
                                   stream))
 
 
-def gm_antialias(cam, mesh, vscreen, adj, light, face_id, depth, colour, layer, tile_dmax, stream):
+def gm_antialias(cam, mesh, vscreen, adj, light, face_id, depth, colour, layer, pairs, tile_dmax, stream):
     check(lib().gm_antialias(C.byref(cam), C.byref(mesh), ptr(vscreen), ptr(adj), _light_ref(light), ptr(face_id),
-                             ptr(depth), ptr(colour), ptr(layer), ptr(tile_dmax), stream))
+                             ptr(depth), ptr(colour), ptr(layer), ptr(pairs), ptr(tile_dmax), stream))
 
 
 def gm_composite_hybrid_fwd_aa(cam, rec, tile_ranges, sorted_ids, layer, bg, softness, out_rgb, out_depth, out_alpha,
@@ -249,9 +249,9 @@ def gm_antialias_bwd_ws(width, height) -> int:
     return lib().gm_antialias_bwd_ws(int(width), int(height))
 
 
-def gm_antialias_bwd(cam, mesh, vscreen, adj, face_id, depth, colour, g_layer, g_mesh_rgb, g_mesh_depth, g_vscreen,
+def gm_antialias_bwd(cam, mesh, vscreen, pairs, face_id, depth, colour, g_layer, g_mesh_rgb, g_mesh_depth, g_vscreen,
                      ws, stream):
-    check(lib().gm_antialias_bwd(C.byref(cam), C.byref(mesh), ptr(vscreen), ptr(adj), ptr(face_id), ptr(depth),
+    check(lib().gm_antialias_bwd(C.byref(cam), C.byref(mesh), ptr(vscreen), ptr(pairs), ptr(face_id), ptr(depth),
                                  ptr(colour), ptr(g_layer), ptr(g_mesh_rgb), ptr(g_mesh_depth), ptr(g_vscreen), ptr(ws),
                                  0 if ws is None else ws.numel() * ws.element_size(), stream))
 

@@ -329,8 +329,18 @@ __device__ __forceinline__ int neighbour_index(int x, int d, int W)
 // ---------------------------------------------------------------------------
 // forward: layer [H][W][8] = (M_r, M_g, M_b, M_D, a_m, D_split, 0, 0)
 // ---------------------------------------------------------------------------
+// Per-pixel record of the pairs for the reverse mode, [H][W][12]:
+//   (w_self, w_left, w_right, w_up), (w_down, clamp branch as int32, raw coverage, 0),
+//   four int32 codes, one per direction: -1 when that pair does not change the pixel,
+//   else ((3 face + edge) << 2) | (area sign > 0) << 1 | (the pixel is the front one).
+// clamp branch: 0 coverage used as is, 1 scaled down from above 1, 2 below 0 (zero).
+__device__ __forceinline__ int pair_code(const AaPair& r, int x)
+{
+    return ((3 * r.face + r.k) << 2) | ((r.sgn > 0.0 ? 1 : 0) << 1) | (r.a == x ? 1 : 0);
+}
+
 __global__ void __launch_bounds__(256) k_antialias(AaParams P, float* __restrict__ layer,
-                                                   float* __restrict__ tile_dmax)
+                                                   float* __restrict__ tile_dmax, float* __restrict__ pairs)
 {
     const int W = P.cam.width, H = P.cam.height;
     const int x = blockIdx.x * blockDim.x + threadIdx.x;
@@ -365,6 +375,17 @@ __global__ void __launch_bounds__(256) k_antialias(AaParams P, float* __restrict
     float4* o = reinterpret_cast<float4*>(layer) + 2 * (size_t)x;
     o[0] = make_float4((float)(s * M0), (float)(s * M1), (float)(s * M2), (float)(s * MD));
     o[1] = make_float4((float)ac, (float)Ds, 0.0f, 0.0f);
+    if (pairs) {
+        const int branch = a > 1.0 ? 1 : (a < 0.0 ? 2 : 0);
+        int code[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) code[d] = w.mod[d] ? pair_code(w.pr[d], x) : -1;
+        float4* q = reinterpret_cast<float4*>(pairs) + 3 * (size_t)x;
+        q[0] = make_float4((float)w.wself, (float)w.wn[0], (float)w.wn[1], (float)w.wn[2]);
+        q[1] = make_float4((float)w.wn[3], __int_as_float(branch), (float)a, 0.0f);
+        q[2] = make_float4(__int_as_float(code[0]), __int_as_float(code[1]), __int_as_float(code[2]),
+                           __int_as_float(code[3]));
+    }
     // the back layer is visible here: no occlusion cull on this tile
     if (tile_dmax && cov && ac < 1.0) tile_dmax[(py / GM_TILE) * P.cam.tx + px / GM_TILE] = INFINITY;
 }
@@ -372,11 +393,13 @@ __global__ void __launch_bounds__(256) k_antialias(AaParams P, float* __restrict
 // ---------------------------------------------------------------------------
 // reverse mode
 // ---------------------------------------------------------------------------
-// Pass 1, per pixel x: dL/d(M, M_D) and dL/da before the clamp (kept in scratch
-// [H][W][8] = (gM_r, gM_g, gM_b, gM_D, g_split of an uncovered pixel, direction of
-// the neighbour giving its split depth, -, -)), and the crossing gradients of the
-// pairs that change x, carried to the edge's screen vertices.
-__global__ void __launch_bounds__(256) k_antialias_bwd1(AaParams P, const float* __restrict__ g_layer,
+// Pass 1, per pixel x, from the forward's pair record: dL/d(M, M_D) and dL/da
+// before the clamp (kept in scratch [H][W][8] = (gM_r, gM_g, gM_b, gM_D, g_split
+// of an uncovered pixel, direction of the neighbour giving its split depth, -, -)),
+// and the crossing gradients of the pairs that change x, carried to the crossed
+// edge's two screen vertices (the crossing is recomputed from the edge alone).
+__global__ void __launch_bounds__(256) k_antialias_bwd1(AaParams P, const float* __restrict__ pairs,
+                                                        const float* __restrict__ g_layer,
                                                         float* __restrict__ scratch, float* __restrict__ g_vs)
 {
     const int W = P.cam.width, H = P.cam.height;
@@ -384,8 +407,13 @@ __global__ void __launch_bounds__(256) k_antialias_bwd1(AaParams P, const float*
     if (x >= W * H) return;
     const int px = x % W, py = x / W;
     const bool cov = P.face_id[x] >= 0;
-    AaPixel w;
-    pixel_weights(P, x, px, py, cov, w);
+    const float4 q0 = reinterpret_cast<const float4*>(pairs)[3 * (size_t)x];
+    const float4 q1 = reinterpret_cast<const float4*>(pairs)[3 * (size_t)x + 1];
+    const float4 q2 = reinterpret_cast<const float4*>(pairs)[3 * (size_t)x + 2];
+    const double wself = q0.x;
+    const double wn[4] = {q0.y, q0.z, q0.w, q1.x};
+    const int branch = __float_as_int(q1.y);
+    const int code[4] = {__float_as_int(q2.x), __float_as_int(q2.y), __float_as_int(q2.z), __float_as_int(q2.w)};
     const float4 g0 = reinterpret_cast<const float4*>(g_layer)[2 * (size_t)x];
     const float4 g1 = reinterpret_cast<const float4*>(g_layer)[2 * (size_t)x + 1];
     double c[3] = {0.0, 0.0, 0.0}, Dx = 0.0;
@@ -395,21 +423,23 @@ __global__ void __launch_bounds__(256) k_antialias_bwd1(AaParams P, const float*
         c[2] = P.colour[3 * x + 2];
         Dx = P.depth[x];
     }
-    double a = w.wself, M0 = w.wself * c[0], M1 = w.wself * c[1], M2 = w.wself * c[2], MD = w.wself * Dx;
+    double M0 = wself * c[0], M1 = wself * c[1], M2 = wself * c[2], MD = wself * Dx;
     double cn[4][4];  // neighbour colour and depth
+    int nb[4];
     int dsel = -1;
     double Ds = cov ? Dx : INFINITY;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        const int n = w.nb[d];
+        const bool has = d == 0 ? px > 0 : (d == 1 ? px < W - 1 : (d == 2 ? py > 0 : py < H - 1));
+        const int n = has ? neighbour_index(x, d, W) : -1;
+        nb[d] = n;
         const bool ncov = n >= 0 && P.face_id[n] >= 0;
         cn[d][0] = ncov ? (double)P.colour[3 * n] : 0.0;
         cn[d][1] = ncov ? (double)P.colour[3 * n + 1] : 0.0;
         cn[d][2] = ncov ? (double)P.colour[3 * n + 2] : 0.0;
         cn[d][3] = ncov ? (double)P.depth[n] : 0.0;
-        const double wd = w.wn[d];
+        const double wd = wn[d];
         if (wd == 0.0) continue;
-        a += wd;
         M0 += wd * cn[d][0];
         M1 += wd * cn[d][1];
         M2 += wd * cn[d][2];
@@ -420,14 +450,14 @@ __global__ void __launch_bounds__(256) k_antialias_bwd1(AaParams P, const float*
         }
     }
     double gM[4] = {0.0, 0.0, 0.0, 0.0}, ga = 0.0;
-    if (a > 1.0) {
-        const double s = 1.0 / a;
+    if (branch == 1) {
+        const double s = 1.0 / (double)q1.z;
         gM[0] = s * g0.x;
         gM[1] = s * g0.y;
         gM[2] = s * g0.z;
         gM[3] = s * g0.w;
         ga = -s * s * ((double)g0.x * M0 + (double)g0.y * M1 + (double)g0.z * M2 + (double)g0.w * MD);
-    } else if (a >= 0.0) {
+    } else if (branch == 0) {
         gM[0] = g0.x;
         gM[1] = g0.y;
         gM[2] = g0.z;
@@ -441,23 +471,27 @@ __global__ void __launch_bounds__(256) k_antialias_bwd1(AaParams P, const float*
     const double gws = cov ? gM[0] * c[0] + gM[1] * c[1] + gM[2] * c[2] + gM[3] * Dx + ga : 0.0;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        if (!w.mod[d]) continue;
-        const AaPair& r = w.pr[d];
-        const int n = w.nb[d];
+        if (code[d] < 0) continue;
+        const int n = nb[d];
         const bool ncov = P.face_id[n] >= 0;
+        const bool front = code[d] & 1;
+        const double sg = (code[d] & 2) ? 1.0 : -1.0;
+        const int fk = code[d] >> 2, face = fk / 3, k = fk - 3 * face;
         const double gwn = ncov ? gM[0] * cn[d][0] + gM[1] * cn[d][1] + gM[2] * cn[d][2] + gM[3] * cn[d][3] + ga : 0.0;
-        const double gt = r.t < 0.5 ? gws - (ncov ? gwn : 0.0) : gwn - (cov ? gws : 0.0);
+        const double gt = front ? gws - (ncov ? gwn : 0.0) : gwn - (cov ? gws : 0.0);
         if (gt == 0.0) continue;
-        const double den = r.ea - r.eb;
-        const double dt_dea = -r.eb / (den * den), dt_deb = r.ea / (den * den);
-        const int ci = r.k == 2 ? 0 : r.k + 1, cj = r.k == 0 ? 2 : r.k - 1;
-        const int vi = P.faces[ci * P.F + r.face], vj = P.faces[cj * P.F + r.face];
+        const int ci = k == 2 ? 0 : k + 1, cj = k == 0 ? 2 : k - 1;
+        const int vi = P.faces[ci * P.F + face], vj = P.faces[cj * P.F + face];
         const double ui = (double)P.vs[vi], uj = (double)P.vs[vj];
         const double vvi = (double)P.vs[P.V + vi], vvj = (double)P.vs[P.V + vj];
-        const double au = (double)(r.a % W) + 0.5, av = (double)(r.a / W) + 0.5;
-        const double bu = (double)(r.b % W) + 0.5, bv = (double)(r.b / W) + 0.5;
-        const double sg = r.sgn;
-        // e(p) = sgn((u_j - u_i)(p_v - v_i) - (v_j - v_i)(p_u - u_i))
+        const int pa = front ? x : n, pb = front ? n : x;
+        const double au = (double)(pa % W) + 0.5, av = (double)(pa / W) + 0.5;
+        const double bu = (double)(pb % W) + 0.5, bv = (double)(pb / W) + 0.5;
+        // the crossing, as in the forward: e(p) = sgn((u_j - u_i)(p_v - v_i) - (v_j - v_i)(p_u - u_i))
+        const double ea = sg * ((uj - ui) * (av - vvi) - (vvj - vvi) * (au - ui));
+        const double eb = sg * ((uj - ui) * (bv - vvi) - (vvj - vvi) * (bu - ui));
+        const double den = ea - eb;
+        const double dt_dea = -eb / (den * den), dt_deb = ea / (den * den);
         const double dui = dt_dea * sg * (vvj - av) + dt_deb * sg * (vvj - bv);
         const double dvi = dt_dea * sg * (au - uj) + dt_deb * sg * (bu - uj);
         const double duj = dt_dea * sg * (av - vvi) + dt_deb * sg * (bv - vvi);
@@ -470,8 +504,10 @@ __global__ void __launch_bounds__(256) k_antialias_bwd1(AaParams P, const float*
 }
 
 // Pass 2, per pixel x: the gradients of its own surface colour and depth, from its
-// own layer and from every neighbour whose layer weighs x's surface.
-__global__ void __launch_bounds__(256) k_antialias_bwd2(AaParams P, const float* __restrict__ g_layer,
+// own layer and from every neighbour whose layer weighs x's surface (the weight a
+// neighbour gives x is in the neighbour's record, in the direction of x).
+__global__ void __launch_bounds__(256) k_antialias_bwd2(AaParams P, const float* __restrict__ pairs,
+                                                        const float* __restrict__ g_layer,
                                                         const float* __restrict__ scratch,
                                                         float* __restrict__ g_mesh_rgb,
                                                         float* __restrict__ g_mesh_depth)
@@ -483,25 +519,22 @@ __global__ void __launch_bounds__(256) k_antialias_bwd2(AaParams P, const float*
     const bool cov = P.face_id[x] >= 0;
     float gc0 = 0.0f, gc1 = 0.0f, gc2 = 0.0f, gd = 0.0f;
     if (cov) {
-        AaPixel w;
-        pixel_weights(P, x, px, py, cov, w);
+        const float ws = pairs[12 * (size_t)x];
         const float4 s0 = reinterpret_cast<const float4*>(scratch)[2 * (size_t)x];
-        const float ws = (float)w.wself;
         gc0 = ws * s0.x;
         gc1 = ws * s0.y;
         gc2 = ws * s0.z;
         gd = ws * s0.w + g_layer[8 * (size_t)x + 5];  // own depth also splits the Gaussians
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            const int n = w.nb[d];
-            if (n < 0) continue;
-            const float4 n0 = reinterpret_cast<const float4*>(scratch)[2 * (size_t)n];
+            const bool has = d == 0 ? px > 0 : (d == 1 ? px < W - 1 : (d == 2 ? py > 0 : py < H - 1));
+            if (!has) continue;
+            const int n = neighbour_index(x, d, W);
+            // the neighbour's weight of x's surface: its entry in the direction of x
+            const float wf = pairs[12 * (size_t)n + 1 + (d ^ 1)];
             const float4 n1 = reinterpret_cast<const float4*>(scratch)[2 * (size_t)n + 1];
-            if (!w.mod[d]) {
-                // the pair changes the neighbour: the weight it gives x's surface
-                // (x is covered: a lost fraction goes to x, a gained one comes from x)
-                const AaPair& r = w.pr[d];
-                const float wf = (float)(r.t < 0.5 ? 0.5 - r.t : r.t - 0.5);
+            if (wf != 0.0f) {
+                const float4 n0 = reinterpret_cast<const float4*>(scratch)[2 * (size_t)n];
                 gc0 += wf * n0.x;
                 gc1 += wf * n0.y;
                 gc2 += wf * n0.z;
@@ -544,11 +577,13 @@ __global__ void k_zero_vs(float* __restrict__ p, int64_t n)
 }
 
 static gm_status aa_params(AaParams& P, const gm_camera* cam, const gm_mesh* mesh, const float* vscreen,
-                           const int32_t* adj, const int32_t* face_id, const float* depth, const float* colour)
+                           const int32_t* adj, const int32_t* face_id, const float* depth, const float* colour,
+                           bool need_adj)
 {
     if (gm_status s = check_camera(cam)) return s;
     GM_ARG_CHECK(mesh != nullptr, "mesh is NULL");
-    GM_ARG_CHECK(mesh->F == 0 || (mesh->faces && vscreen && adj), "mesh faces / vscreen / adjacency is NULL");
+    GM_ARG_CHECK(mesh->F == 0 || (mesh->faces && vscreen && (adj || !need_adj)),
+                 "mesh faces / vscreen / adjacency is NULL");
     GM_ARG_CHECK(face_id && depth && colour, "face_id / depth / colour is NULL");
     P = AaParams{};
     P.cam = dev_camera(*cam);
@@ -598,15 +633,16 @@ gm_status gm_edge_adjacency(const gm_mesh* mesh, int32_t* adj, void* ws, size_t 
 
 gm_status gm_antialias(const gm_camera* cam, const gm_mesh* mesh, const float* vscreen, const int32_t* adj,
                        const gm_light* light, const int32_t* face_id, const float* depth, float* colour, float* layer,
-                       float* tile_dmax, hipStream_t stream)
+                       float* pairs, float* tile_dmax, hipStream_t stream)
 {
     clear_error();
     AaParams P;
-    if (gm_status s = aa_params(P, cam, mesh, vscreen, adj, face_id, depth, colour)) return s;
+    if (gm_status s = aa_params(P, cam, mesh, vscreen, adj, face_id, depth, colour, true)) return s;
     GM_ARG_CHECK(layer != nullptr && ((uintptr_t)layer & 15) == 0, "layer is NULL or not 16-byte aligned");
+    GM_ARG_CHECK(((uintptr_t)pairs & 15) == 0, "pairs must be 16-byte aligned");
     const int64_t HW = (int64_t)P.cam.width * P.cam.height;
     if (gm_status s = launch_surface_colour(cam, mesh, vscreen, light, face_id, nullptr, colour, stream)) return s;
-    k_antialias<<<(unsigned)div_up(HW, 256), 256, 0, stream>>>(P, layer, tile_dmax);
+    k_antialias<<<(unsigned)div_up(HW, 256), 256, 0, stream>>>(P, layer, tile_dmax, pairs);
     GM_LAUNCH_CHECK();
     return GM_OK;
 }
@@ -616,17 +652,19 @@ size_t gm_antialias_bwd_ws(int32_t width, int32_t height)
     return (size_t)(width > 0 ? width : 0) * (size_t)(height > 0 ? height : 0) * 8 * sizeof(float);
 }
 
-gm_status gm_antialias_bwd(const gm_camera* cam, const gm_mesh* mesh, const float* vscreen, const int32_t* adj,
+gm_status gm_antialias_bwd(const gm_camera* cam, const gm_mesh* mesh, const float* vscreen, const float* pairs,
                            const int32_t* face_id, const float* depth, const float* colour, const float* g_layer,
                            float* g_mesh_rgb, float* g_mesh_depth, float* g_vscreen, void* ws, size_t ws_bytes,
                            hipStream_t stream)
 {
     clear_error();
     AaParams P;
-    if (gm_status s = aa_params(P, cam, mesh, vscreen, adj, face_id, depth, colour)) return s;
+    GM_ARG_CHECK(pairs != nullptr, "pairs (the forward's record) is NULL");
+    // the walk over internal edges is not repeated: no adjacency
+    if (gm_status s = aa_params(P, cam, mesh, vscreen, nullptr, face_id, depth, colour, false)) return s;
     GM_ARG_CHECK(g_layer && g_mesh_rgb && g_mesh_depth && ws, "g_layer / outputs / workspace is NULL");
-    GM_ARG_CHECK(((uintptr_t)g_layer & 15) == 0 && ((uintptr_t)ws & 15) == 0,
-                 "g_layer and the workspace must be 16-byte aligned");
+    GM_ARG_CHECK(((uintptr_t)g_layer & 15) == 0 && ((uintptr_t)ws & 15) == 0 && ((uintptr_t)pairs & 15) == 0,
+                 "g_layer, pairs and the workspace must be 16-byte aligned");
     GM_ARG_CHECK(ws_bytes >= gm_antialias_bwd_ws(cam->width, cam->height), "workspace of %zu bytes is too small",
                  ws_bytes);
     GM_ARG_CHECK(mesh->V == 0 || g_vscreen, "g_vscreen is NULL");
@@ -635,9 +673,9 @@ gm_status gm_antialias_bwd(const gm_camera* cam, const gm_mesh* mesh, const floa
         k_zero_vs<<<(unsigned)div_up(2 * (int64_t)mesh->V, 256), 256, 0, stream>>>(g_vscreen, 2 * (int64_t)mesh->V);
         GM_LAUNCH_CHECK();
     }
-    k_antialias_bwd1<<<(unsigned)div_up(HW, 256), 256, 0, stream>>>(P, g_layer, (float*)ws, g_vscreen);
+    k_antialias_bwd1<<<(unsigned)div_up(HW, 256), 256, 0, stream>>>(P, pairs, g_layer, (float*)ws, g_vscreen);
     GM_LAUNCH_CHECK();
-    k_antialias_bwd2<<<(unsigned)div_up(HW, 256), 256, 0, stream>>>(P, g_layer, (const float*)ws, g_mesh_rgb,
+    k_antialias_bwd2<<<(unsigned)div_up(HW, 256), 256, 0, stream>>>(P, pairs, g_layer, (const float*)ws, g_mesh_rgb,
                                                                     g_mesh_depth);
     GM_LAUNCH_CHECK();
     return GM_OK;

@@ -276,6 +276,7 @@ class Renderer:
         H, W = self.H, self.W
         self.colour = torch.empty((H, W, 3), dtype=f32, device=dev)
         self.layer = torch.empty((H, W, 8), dtype=f32, device=dev)
+        self.aa_pairs = torch.empty((H, W, 12), dtype=f32, device=dev)
         self.state_aa = torch.empty((H, W, 8), dtype=f32, device=dev)
         self.g_layer = torch.empty((H, W, 8), dtype=f32, device=dev)
         self.ws_aa_bwd = torch.empty(G.gm_antialias_bwd_ws(W, H), dtype=torch.uint8, device=dev)
@@ -287,7 +288,7 @@ class Renderer:
         self._aa_buffers()
         ds = self.ds
         G.gm_antialias(ds.cams[view], ds.mesh, self.vscreen, ds.adjacency(), ds.light, self.face_id, self.depth,
-                       self.colour, self.layer, self.tile_dmax, _stream())
+                       self.colour, self.layer, self.aa_pairs, self.tile_dmax, _stream())
 
     def composite_fwd_aa(self, view: int):
         ds, s = self.ds, self.ds.scene
@@ -305,7 +306,7 @@ class Renderer:
         """dL/dc and dL/dD at covered pixels (into g_mesh_rgb / g_mesh_depth) and
         dL/d(u, v) of the screen vertices (g_vscreen) from dL/d(layer)."""
         ds = self.ds
-        G.gm_antialias_bwd(ds.cams[view], ds.mesh, self.vscreen, ds.adjacency(), self.face_id, self.depth,
+        G.gm_antialias_bwd(ds.cams[view], ds.mesh, self.vscreen, self.aa_pairs, self.face_id, self.depth,
                            self.colour, self.g_layer if g_layer is None else g_layer, self.g_mesh_rgb,
                            self.g_mesh_depth, self.g_vscreen, self.ws_aa_bwd, _stream())
 

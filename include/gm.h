@@ -355,10 +355,16 @@ gm_status gm_mesh_bwd(const gm_camera* cam, const gm_mesh* mesh, const gm_light*
  *
  * gm_antialias: from the z-buffer of call 2 (face_id, depth), vscreen of call 1 and
  * adj, writes colour [H][W][3] (the shaded surface colour at covered pixels, 0
- * elsewhere; needed again by the reverse mode) and the mesh layer [H][W][8] =
- * (M_r, M_g, M_b, M_D, a_m, D_split, 0, 0) (16-byte aligned).  When tile_dmax (the
- * cull bound of call 2) is given, every tile holding a covered pixel with a_m < 1
- * gets +inf, so that call 4 culls only where the back layer is hidden.
+ * elsewhere; needed again by the reverse mode), the mesh layer [H][W][8] =
+ * (M_r, M_g, M_b, M_D, a_m, D_split, 0, 0) and, when pairs is not NULL, the
+ * per-pixel record of the pairs the reverse mode reads instead of repeating the
+ * analysis, [H][W][12]: the five weights (own surface, left, right, up, down), the
+ * clamp branch (int32: 0 unclamped, 1 scaled down from above 1, 2 zero) and the raw
+ * coverage, then per direction an int32 code, -1 when that pair does not change the
+ * pixel, else ((3 face + edge) << 2) | (screen area > 0) << 1 | (pixel is the front
+ * one).  layer and pairs are 16-byte aligned.  When tile_dmax (the cull bound of
+ * call 2) is given, every tile holding a covered pixel with a_m < 1 gets +inf, so
+ * that call 4 culls only where the back layer is hidden.
  *
  * gm_composite_hybrid_fwd_aa / _bwd_aa: calls 5 and 6 with the mesh given by its
  * layer (bg: host, 3 floats, as in call 5).  Both layers follow the per-layer
@@ -371,7 +377,8 @@ gm_status gm_mesh_bwd(const gm_camera* cam, const gm_mesh* mesh, const gm_light*
  * call 6 (zero-filled first) and g_layer [H][W][8] = dL/d(M_rgb, M_D, a_m,
  * D_split), 0, 0.
  *
- * gm_antialias_bwd: reverse mode of gm_antialias.  From g_layer it writes
+ * gm_antialias_bwd: reverse mode of gm_antialias, from its pairs record (the
+ * crossings are recomputed from the recorded silhouette edges).  From g_layer it writes
  * g_mesh_rgb [H][W][3] and g_mesh_depth [H][W] (dL/dc and dL/dD at covered pixels'
  * own centres, 0 elsewhere: the inputs of call 8) and g_vscreen [2][V] (dL/du,
  * dL/dv of the screen vertices through the crossings; zero-filled first).  The
@@ -385,7 +392,7 @@ size_t gm_edge_adjacency_ws(int32_t F);
 gm_status gm_edge_adjacency(const gm_mesh* mesh, int32_t* adj, void* ws, size_t ws_bytes, hipStream_t stream);
 gm_status gm_antialias(const gm_camera* cam, const gm_mesh* mesh, const float* vscreen, const int32_t* adj,
                        const gm_light* light, const int32_t* face_id, const float* depth, float* colour,
-                       float* layer, float* tile_dmax, hipStream_t stream);
+                       float* layer, float* pairs, float* tile_dmax, hipStream_t stream);
 gm_status gm_composite_hybrid_fwd_aa(const gm_camera* cam, const float* rec, const int32_t* tile_ranges,
                                      const int32_t* sorted_ids, const float* layer, const float* bg,
                                      float softness, float* out_rgb, float* out_depth, float* out_alpha,
@@ -396,7 +403,7 @@ gm_status gm_composite_hybrid_bwd_aa(const gm_camera* cam, int32_t N, const floa
                                      const float* g_depth, const float* g_alpha, float* g_rec, float* g_layer,
                                      hipStream_t stream);
 size_t gm_antialias_bwd_ws(int32_t width, int32_t height);
-gm_status gm_antialias_bwd(const gm_camera* cam, const gm_mesh* mesh, const float* vscreen, const int32_t* adj,
+gm_status gm_antialias_bwd(const gm_camera* cam, const gm_mesh* mesh, const float* vscreen, const float* pairs,
                            const int32_t* face_id, const float* depth, const float* colour,
                            const float* g_layer, float* g_mesh_rgb, float* g_mesh_depth, float* g_vscreen,
                            void* ws, size_t ws_bytes, hipStream_t stream);

@@ -115,8 +115,9 @@ def test_antialias_argument_errors(G):
     assert L.gm_edge_adjacency(C.byref(m0), None, None, 0, None) == G.GM_OK  # F = 0: nothing to do
     m.faces, m.verts = 16, 16
     # the layer: missing adjacency, misaligned layer
-    assert L.gm_antialias(C.byref(cam), C.byref(m), 16, None, None, 16, 16, 16, 16, None, None) == G.GM_ERR_ARG
-    assert L.gm_antialias(C.byref(cam), C.byref(m), 16, 16, None, 16, 16, 16, 17, None, None) == G.GM_ERR_ARG
+    assert L.gm_antialias(C.byref(cam), C.byref(m), 16, None, None, 16, 16, 16, 16, None, None, None) == G.GM_ERR_ARG
+    assert L.gm_antialias(C.byref(cam), C.byref(m), 16, 16, None, 16, 16, 16, 17, None, None, None) == G.GM_ERR_ARG
+    assert L.gm_antialias(C.byref(cam), C.byref(m), 16, 16, None, 16, 16, 16, 16, 17, None, None) == G.GM_ERR_ARG
     # two-layer composite: NULL layer, misaligned state, negative softness
     assert L.gm_composite_hybrid_fwd_aa(C.byref(cam), 16, 16, 16, None, 16, C.c_float(1.0), 16, 16, 16, 16,
                                         None) == G.GM_ERR_ARG
@@ -132,6 +133,9 @@ def test_antialias_argument_errors(G):
                               None) == G.GM_ERR_ARG
     assert L.gm_antialias_bwd(C.byref(cam), C.byref(m), 16, 16, 16, 16, 16, 16, 16, 16, None, 16, ws,
                               None) == G.GM_ERR_ARG
+    assert L.gm_antialias_bwd(C.byref(cam), C.byref(m), 16, None, 16, 16, 16, 16, 16, 16, 16, 16, ws,
+                              None) == G.GM_ERR_ARG
+    assert b"pairs" in L.gm_last_error()
     # the vertex chain: NULL verts
     m.verts = None
     assert L.gm_vscreen_bwd(C.byref(cam), C.byref(m), 16, 16, None) == G.GM_ERR_ARG
