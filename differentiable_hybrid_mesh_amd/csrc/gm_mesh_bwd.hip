@@ -6,11 +6,14 @@
 // the mesh depth D enters the hybrid composite through the split; the renderer is
 // differentiable with respect to the mesh as well).
 //
-// One thread per pixel; a covered pixel re-evaluates its surface in fp64 (the
-// barycentric chain divides by the triangle's area and by depths, and the level of
-// detail must select the same pyramid levels as the forward's definition) and runs
-// the reverse mode, adding into the per-vertex and per-texel gradients with float
-// atomics; the light's 13 gradients are summed per block first.  Texel gradients
+// One block per 16 x 16 pixel tile, one thread per pixel; a covered pixel
+// re-evaluates its surface in fp64 (the barycentric chain divides by the triangle's
+// area and by depths, and the level of detail must select the same pyramid levels as
+// the forward's definition) and runs the reverse mode.  Corner gradients are summed
+// over each run of one face within a wave, then per vertex (and texture vertex) in an
+// LDS table of the block, which adds its totals to global memory with float atomics;
+// texel gradients go straight to global atomics; the light's 13 gradients are summed
+// per block first.  Texel gradients
 // land on the two pyramid levels each lookup used, and a level-by-level pass then
 // hands every coarse texel's gradient down to its 2x2 children (the adjoint of the
 // box-filter pyramid), so level 0 ends up holding dL/dtexture.  Visibility and the
@@ -21,6 +24,11 @@
 namespace gm {
 
 constexpr int MB_THREADS = 256;
+constexpr int MB_TILE = 16;  // a block covers a 16 x 16 pixel tile, a wave 16 x 4 of it
+constexpr int MB_SLOTS_LOG2 = 10;
+constexpr int MB_SLOTS = 1 << MB_SLOTS_LOG2;
+static_assert(MB_TILE * MB_TILE == MB_THREADS, "one thread per pixel of the tile");
+static_assert(3 * MB_THREADS < MB_SLOTS, "the corner table never fills");
 
 struct MeshBwdParams {
     DevCamera cam;
@@ -93,6 +101,40 @@ __device__ __forceinline__ constexpr bool plane_live(int j)
     return j < 3 || (j < 6 ? !TEX : (j < 9 ? LIT : TEX));
 }
 
+// Per-vertex planes a variant sums in its LDS table: position, then colour when
+// untextured, then normal when lit.
+template <bool TEX, bool LIT>
+__device__ __forceinline__ constexpr int vertex_planes()
+{
+    return 3 + (TEX ? 0 : 3) + (LIT ? 3 : 0);
+}
+
+// Table plane of corner-gradient plane j (0-8; not uv).
+template <bool TEX, bool LIT>
+__device__ __forceinline__ constexpr int vertex_plane(int j)
+{
+    return j < 3 ? j : (j < 6 ? j : (TEX ? j - 3 : j));
+}
+
+// Slot of `key` in an open-addressed LDS table of MB_SLOTS entries (empty = -1),
+// claiming a free one on first sight.  A block touches at most 3 x MB_THREADS keys,
+// fewer than MB_SLOTS, so the probe always ends on a free or matching slot; the
+// bound only makes the loop's end explicit (-1: the caller adds to global memory).
+__device__ __forceinline__ int table_slot(int* keys, int key)
+{
+    unsigned h = ((unsigned)key * 2654435761u) >> (32 - MB_SLOTS_LOG2);
+    for (int probe = 0; probe < MB_SLOTS; ++probe) {
+        const int seen = keys[h];
+        if (seen == key) return (int)h;
+        if (seen == -1) {
+            const int old = atomicCAS(&keys[h], -1, key);
+            if (old == -1 || old == key) return (int)h;
+        }
+        h = (h + 1) & (MB_SLOTS - 1);
+    }
+    return -1;
+}
+
 // One variant per (textured, lit) pair, so that each holds only its own state.
 template <bool TEX, bool LIT>
 __global__ void __launch_bounds__(MB_THREADS, TEX ? 2 : 3)
@@ -101,9 +143,27 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
            float* __restrict__ g_vnormal, float* __restrict__ g_uv, float* __restrict__ g_mips,
            float* __restrict__ g_light)
 {
+    constexpr int NVP = vertex_planes<TEX, LIT>();
     __shared__ float s_light[13][MB_THREADS / 64];
-    const int pix = blockIdx.x * blockDim.x + threadIdx.x;
+    __shared__ int s_vkey[MB_SLOTS];
+    __shared__ float s_vval[NVP][MB_SLOTS];
+    __shared__ int s_tkey[TEX ? MB_SLOTS : 1];
+    __shared__ float s_tval[2][TEX ? MB_SLOTS : 1];
+    for (int s = threadIdx.x; s < MB_SLOTS; s += MB_THREADS) {
+        s_vkey[s] = -1;
+#pragma unroll
+        for (int p = 0; p < NVP; ++p) s_vval[p][s] = 0.0f;
+        if (TEX) {
+            s_tkey[s] = -1;
+            s_tval[0][s] = 0.0f;
+            s_tval[1][s] = 0.0f;
+        }
+    }
     const int W = P.cam.width, H = P.cam.height;
+    const int tiles_x = (W + MB_TILE - 1) / MB_TILE;
+    const int px = (int)(blockIdx.x % tiles_x) * MB_TILE + (int)(threadIdx.x % MB_TILE);
+    const int py = (int)(blockIdx.x / tiles_x) * MB_TILE + (int)(threadIdx.x / MB_TILE);
+    const int pix = py * W + px;
     float gl[13];
 #pragma unroll
     for (int i = 0; i < 13; ++i) gl[i] = 0.0f;
@@ -114,9 +174,8 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
 #pragma unroll
         for (int j = 0; j < 11; ++j) acc[k][j] = 0.0f;
     int vi[3] = {0, 0, 0}, ti[3] = {0, 0, 0};
-    const int f = pix < W * H ? face_id[pix] : -1;
+    const int f = (px < W && py < H) ? face_id[pix] : -1;
     if (f >= 0) {
-        const int px = pix % W, py = pix / W;
         const double pu = px + 0.5, pv = py + 0.5;
         double R[9], t[3];
 #pragma unroll
@@ -396,6 +455,7 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
     // Pixels of one face are runs of neighbouring lanes (a triangle meets a row in an
     // interval): a segmented sum over each run leaves the run's total in its last lane,
     // which alone adds it to the face's corners (one set of atomics per run).
+    __syncthreads();  // the tables are cleared
     if (__ballot(f >= 0)) {  // a wave with no covered pixel has nothing to add
         const int lane = threadIdx.x & 63;
         const int prev = __shfl_up(f, 1, 64);
@@ -416,21 +476,53 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
                 }
                 acc[k][j] = x;
             }
+        // Run totals go into the block's LDS tables keyed by vertex (and texture
+        // vertex): a vertex's faces meet inside one tile, so its many runs become one
+        // set of global atomics when the block flushes.
         if (tail && f >= 0) {
 #pragma unroll
             for (int k = 0; k < 3; ++k) {
+                const int s = table_slot(s_vkey, vi[k]);
 #pragma unroll
-                for (int j = 0; j < 3; ++j) {
-                    if (g_verts && acc[k][j] != 0.0f) unsafeAtomicAdd(&g_verts[j * P.V + vi[k]], acc[k][j]);
-                    if (!TEX && g_vcolor && acc[k][3 + j] != 0.0f)
-                        unsafeAtomicAdd(&g_vcolor[j * P.V + vi[k]], acc[k][3 + j]);
-                    if (LIT && g_vnormal && acc[k][6 + j] != 0.0f)
-                        unsafeAtomicAdd(&g_vnormal[j * P.V + vi[k]], acc[k][6 + j]);
+                for (int j = 0; j < 9; ++j) {
+                    if (!plane_live<TEX, LIT>(j) || acc[k][j] == 0.0f) continue;
+                    if (s >= 0) {
+                        atomicAdd(&s_vval[vertex_plane<TEX, LIT>(j)][s], acc[k][j]);
+                    } else {
+                        float* g = j < 3 ? g_verts : (j < 6 ? g_vcolor : g_vnormal);
+                        if (g) unsafeAtomicAdd(&g[(j % 3) * P.V + vi[k]], acc[k][j]);
+                    }
                 }
-                if (TEX && g_uv) {
-                    if (acc[k][9] != 0.0f) unsafeAtomicAdd(&g_uv[ti[k]], acc[k][9]);
-                    if (acc[k][10] != 0.0f) unsafeAtomicAdd(&g_uv[P.Vt + ti[k]], acc[k][10]);
+                if (TEX) {
+                    const int st = table_slot(s_tkey, ti[k]);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        if (acc[k][9 + j] == 0.0f) continue;
+                        if (st >= 0) atomicAdd(&s_tval[j][st], acc[k][9 + j]);
+                        else if (g_uv) unsafeAtomicAdd(&g_uv[j * P.Vt + ti[k]], acc[k][9 + j]);
+                    }
                 }
+            }
+        }
+    }
+    __syncthreads();
+    for (int s = threadIdx.x; s < MB_SLOTS; s += MB_THREADS) {
+        const int v = s_vkey[s];
+        if (v >= 0) {
+#pragma unroll
+            for (int j = 0; j < 9; ++j) {
+                if (!plane_live<TEX, LIT>(j)) continue;
+                float* g = j < 3 ? g_verts : (j < 6 ? g_vcolor : g_vnormal);
+                const float x = s_vval[vertex_plane<TEX, LIT>(j)][s];
+                if (g && x != 0.0f) unsafeAtomicAdd(&g[(j % 3) * P.V + v], x);
+            }
+        }
+        if (TEX) {
+            const int t = s_tkey[s];
+            if (t >= 0 && g_uv) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    if (s_tval[j][s] != 0.0f) unsafeAtomicAdd(&g_uv[j * P.Vt + t], s_tval[j][s]);
             }
         }
     }
@@ -532,12 +624,12 @@ extern "C" gm_status gm_mesh_bwd(const gm_camera* cam, const gm_mesh* mesh, cons
     if (gm_status s = zero(g_uv, 2 * (int64_t)P.Vt, stream)) return s;
     if (gm_status s = zero(g_mips, (int64_t)nmips, stream)) return s;
     if (gm_status s = zero(g_light, 13, stream)) return s;
-    const int64_t HW = (int64_t)cam->width * cam->height;
     if (P.F > 0) {
         const bool tex = P.mips != nullptr, lit = P.lit && P.vnormal;
         auto kern = tex ? (lit ? k_mesh_bwd<true, true> : k_mesh_bwd<true, false>)
                         : (lit ? k_mesh_bwd<false, true> : k_mesh_bwd<false, false>);
-        kern<<<(unsigned)div_up(HW, MB_THREADS), MB_THREADS, 0, stream>>>(
+        const int64_t tiles = div_up(cam->width, MB_TILE) * div_up(cam->height, MB_TILE);
+        kern<<<(unsigned)tiles, MB_THREADS, 0, stream>>>(
             P, face_id, g_mesh_rgb, g_mesh_depth, g_verts, g_vcolor, lit ? g_vnormal : nullptr, g_uv, g_mips,
             lit ? g_light : nullptr);
         GM_LAUNCH_CHECK();
