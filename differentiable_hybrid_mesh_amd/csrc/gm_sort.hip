@@ -268,7 +268,6 @@ __global__ void k_depth_keys(int N, const float* __restrict__ rec, uint32_t* __r
 struct CullParams {
     const float* tile_dmax;  // nullptr: no culling
     float softness;
-    int lds;                 // 1: tile_dmax is staged in dynamic LDS (T floats)
 };
 
 // f must reach (1/255)(1 - 1e-3) / min(0.99, o) for the pair to matter anywhere;
@@ -290,7 +289,9 @@ __device__ inline float cull_scrit(float o)
 __device__ inline bool culled(const DevCamera& cam, float softness, float dmax, int tx, int ty, float u, float v,
                               float zc, float g0, float g1, float sig_soft, float scrit)
 {
-    if (!(dmax < INFINITY)) return false;
+    // evaluated whatever dmax is (so its operands load alongside dmax); an uncovered
+    // tile (dmax = +inf) keeps the pair
+    const bool covered = dmax < INFINITY;
     const float xa = tx * GM_TILE + 0.5f, ya = ty * GM_TILE + 0.5f;
     const float xb = (float)min((tx + 1) * GM_TILE, cam.width) - 0.5f;
     const float yb = (float)min((ty + 1) * GM_TILE, cam.height) - 0.5f;
@@ -298,8 +299,8 @@ __device__ inline bool culled(const DevCamera& cam, float softness, float dmax, 
     const float ay = g1 * (ya - v), by = g1 * (yb - v);
     const float zmin = zc + (fminf(ax, bx) + fminf(ay, by));
     const float lim = dmax + 1e-5f * fabsf(dmax);
-    if (softness > 0.0f) return lim - zmin < scrit * sig_soft;
-    return !(zmin < lim) || scrit == INFINITY;
+    if (softness > 0.0f) return covered && lim - zmin < scrit * sig_soft;
+    return covered && (!(zmin < lim) || scrit == INFINITY);
 }
 
 // Pairs of the visible Gaussians in depth order: a counting pass, a scan of the
@@ -330,7 +331,7 @@ struct ChunkCtx {
 
 // Owner Gaussian (lane index in the chunk) of flat index f = f0 + lane, given the
 // owner of f0 - 1 (carry); returns the owner of f0 + 63 in carry.
-__device__ __forceinline__ int step_owner(const int (*s_start)[64], const ChunkCtx& c, int f0, int& carry)
+__device__ __forceinline__ int step_owner(const int4 (*s_gi)[64], const ChunkCtx& c, int f0, int& carry)
 {
     const int f = f0 + c.lane;
     unsigned long long m = __ballot(c.nt > 0 && c.start >= f0 && c.start < f0 + 64);
@@ -345,7 +346,7 @@ __device__ __forceinline__ int step_owner(const int (*s_start)[64], const ChunkC
         int lo = 0, hi = 63;
         while (lo < hi) {  // last g with start[g] <= f
             const int mid = (lo + hi + 1) >> 1;
-            if (s_start[c.wave][mid] <= f) lo = mid;
+            if (s_gi[c.wave][mid].x <= f) lo = mid;
             else hi = mid - 1;
         }
         g = lo;
@@ -362,7 +363,9 @@ __device__ __forceinline__ void skip_owner(const ChunkCtx& c, int f0, int& carry
     if (m) carry = 63 - __builtin_clzll(m);
 }
 
-template <bool EMIT>
+// LDS: tile_dmax is staged in LDS (a compile-time choice, so the cull's read is a
+// plain LDS load rather than a generic one through a pointer picked at run time).
+template <bool EMIT, bool LDS>
 __global__ void __launch_bounds__(64 * PW_WAVES)
 k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nchunks,
         const int32_t* __restrict__ order, const float* __restrict__ rec, int32_t* __restrict__ chunk_cnt,
@@ -370,10 +373,10 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
         const long long* __restrict__ d_total, long long cap, uint32_t* __restrict__ tkeys,
         int32_t* __restrict__ tvals)
 {
-    extern __shared__ float s_dmax[];       // tile_dmax when cp.lds
-    __shared__ float s_f[PW_WAVES][7][64];  // u, v, z_c, g0, g1, sigma softness, s_crit
-    __shared__ int s_i[PW_WAVES][3][64];    // rect lo, rect hi, id
-    __shared__ int s_start[PW_WAVES][64];   // first flat index of each Gaussian of the chunk
+    extern __shared__ float s_dmax[];       // tile_dmax when LDS
+    __shared__ int4 s_gi[PW_WAVES][64];     // first flat index in the chunk, rect lo, rect hi, id
+    __shared__ float4 s_ga[PW_WAVES][64];   // u, v, z_c, g0
+    __shared__ float4 s_gb[PW_WAVES][64];   // g1, sigma softness, s_crit
     ChunkCtx c;
     c.lane = threadIdx.x & 63;
     c.wave = threadIdx.x >> 6;
@@ -382,7 +385,7 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
     const int nvis = *d_nvis;
     if (EMIT && *d_total > cap) return;  // over capacity: nothing is written (uniform)
     const int T = cam.tx * cam.ty;
-    if (cp.tile_dmax && cp.lds && !EMIT) {
+    if (LDS) {
         for (int i = threadIdx.x; i < T; i += blockDim.x) s_dmax[i] = cp.tile_dmax[i];
         __syncthreads();
     }
@@ -391,19 +394,20 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
     auto keep_of = [&](int f0, int g, int& tile, int& id, bool decide) -> bool {
         const int f = f0 + lane;
         if (f >= c.total) return false;
-        const int t = f - s_start[wave][g];
-        const int rlo = s_i[wave][0][g], rhi = s_i[wave][1][g];
+        const int4 gi = s_gi[wave][g];
+        const int t = f - gi.x;
+        const int rlo = gi.y, rhi = gi.z;
         const int x0 = rlo & 0xffff, y0 = rlo >> 16, w = (rhi & 0xffff) - x0;
         // row = floor(t / w): the quotient's fraction is at least 1/(2w) away from an
         // integer and t < 2^20, so one reciprocal multiply is exact enough
         const int q = (int)(((float)t + 0.5f) * __builtin_amdgcn_rcpf((float)w));
         const int ty = y0 + q, tx = x0 + (t - q * w);
         tile = ty * cam.tx + tx;
-        id = s_i[wave][2][g];
+        id = gi.w;
         if (!decide || !cp.tile_dmax) return true;
-        const float dmax = (cp.lds && !EMIT) ? s_dmax[tile] : cp.tile_dmax[tile];
-        return !culled(cam, cp.softness, dmax, tx, ty, s_f[wave][0][g], s_f[wave][1][g], s_f[wave][2][g],
-                       s_f[wave][3][g], s_f[wave][4][g], s_f[wave][5][g], s_f[wave][6][g]);
+        const float4 ga = s_ga[wave][g], gb = s_gb[wave][g];
+        const float dmax = LDS ? s_dmax[tile] : cp.tile_dmax[tile];
+        return !culled(cam, cp.softness, dmax, tx, ty, ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z);
     };
     for (int chunk = blockIdx.x * PW_WAVES + wave; chunk < nchunks; chunk += gridDim.x * PW_WAVES) {
         const int jl = chunk * 64 + lane;
@@ -414,16 +418,11 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
             const float4 a = r[0], b = r[1], cc = r[2], d = r[3];
             const int lo = __float_as_int(d.y), hi = __float_as_int(d.z);
             nt = ((hi & 0xffff) - (lo & 0xffff)) * ((hi >> 16) - (lo >> 16));
-            s_f[wave][0][lane] = a.x;
-            s_f[wave][1][lane] = a.y;
-            s_f[wave][2][lane] = cc.y;
-            s_f[wave][3][lane] = cc.z;
-            s_f[wave][4][lane] = cc.w;
-            s_f[wave][5][lane] = d.x * cp.softness;
-            s_f[wave][6][lane] = cull_scrit(b.y);
-            s_i[wave][0][lane] = lo;
-            s_i[wave][1][lane] = hi;
-            s_i[wave][2][lane] = id;
+            s_ga[wave][lane] = make_float4(a.x, a.y, cc.y, cc.z);
+            s_gb[wave][lane] = make_float4(cc.w, d.x * cp.softness, cull_scrit(b.y), 0.0f);
+            s_gi[wave][lane].y = lo;
+            s_gi[wave][lane].z = hi;
+            s_gi[wave][lane].w = id;
         }
         int P = nt;
 #pragma unroll
@@ -433,7 +432,7 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
         }
         c.nt = nt;
         c.start = P - nt;
-        s_start[wave][lane] = c.start;
+        s_gi[wave][lane].x = c.start;
         c.total = __builtin_amdgcn_readlane(P, 63);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -443,7 +442,7 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
         if (!EMIT) {
             int cnt = 0;
             for (int f0 = 0, st = 0; f0 < c.total; f0 += 64, ++st) {
-                const int g = step_owner(s_start, c, f0, carry);
+                const int g = step_owner(s_gi, c, f0, carry);
                 int tile, id;
                 const unsigned long long km = __ballot(keep_of(f0, g, tile, id, true));
                 if (st < PW_WORDS && lane == 0) cbits[st] = km;
@@ -466,10 +465,10 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
                         skip_owner(c, f0, carry);
                         continue;
                     }
-                    g = step_owner(s_start, c, f0, carry);
+                    g = step_owner(s_gi, c, f0, carry);
                     if ((km >> lane) & 1ull) keep_of(f0, g, tile, id, false);
                 } else {
-                    g = step_owner(s_start, c, f0, carry);
+                    g = step_owner(s_gi, c, f0, carry);
                     km = __ballot(keep_of(f0, g, tile, id, true));
                 }
                 if ((km >> lane) & 1ull) {
@@ -602,12 +601,13 @@ gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec, c
     const int32_t* d_nvis = offs + (size_t)(RS_RADIX - 1) * div_up(N, RS_CHUNK);
     // 2. surviving (Gaussian, tile) pairs per chunk of 64 Gaussians in depth order, scan
     const bool lds = tile_dmax && T <= PW_LDS_MAX_TILES;
-    CullParams cp{tile_dmax, softness, lds ? 1 : 0};
+    CullParams cp{tile_dmax, softness};
     const size_t shm = lds ? sizeof(float) * (size_t)T : 0;
     const int nchunks = (int)div_up(N, 64);
     const unsigned gW = (unsigned)std::min<int64_t>(div_up(nchunks, PW_WAVES), 512);
-    k_pairs<false><<<gW, 64 * PW_WAVES, shm, stream>>>(dc, cp, d_nvis, nchunks, order, rec, w.cnt, nullptr, w.bits,
-                                                      nullptr, 0, nullptr, nullptr);
+    auto count = lds ? k_pairs<false, true> : k_pairs<false, false>;
+    count<<<gW, 64 * PW_WAVES, shm, stream>>>(dc, cp, d_nvis, nchunks, order, rec, w.cnt, nullptr, w.bits, nullptr, 0,
+                                              nullptr, nullptr);
     GM_LAUNCH_CHECK();
     if (gm_status s = exclusive_scan(w.cnt, w.off, nchunks, total, w.scan, stream)) return s;
     // 3. emit (tile, id) in depth order; 4. stable sort by tile; 5. tile ranges.
@@ -621,7 +621,7 @@ gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec, c
     uint32_t* ka = w.tka;
     int32_t* va = (npass % 2 == 0) ? sorted_ids : w.tva;
     int32_t* vb = (npass % 2 == 0) ? w.tva : sorted_ids;
-    k_pairs<true><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, d_nvis, nchunks, order, rec, nullptr, w.off, w.bits,
+    k_pairs<true, false><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, d_nvis, nchunks, order, rec, nullptr, w.off, w.bits,
                                                    total, kcap, ka, va);
     GM_LAUNCH_CHECK();
     if (gm_status s = radix_sort(ka, va, w.tkb, vb, tbits, total, kcap, w.aux, stream)) return s;
