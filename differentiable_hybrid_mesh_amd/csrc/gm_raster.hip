@@ -14,6 +14,7 @@ namespace gm {
 
 constexpr int ZB_THREADS = 256;  // one thread per pixel of a 16x16 tile
 constexpr int ZB_BATCH = 128;    // triangles staged in LDS per round
+constexpr double ZB_MARGIN = 1.0 / 64.0;  // candidate box margin d around the bounding box, pixels
 
 __global__ void k_fill_i32(int32_t* __restrict__ p, int64_t n, int32_t v)
 {
@@ -230,18 +231,39 @@ k_zbuffer(DevCamera cam, int V, int F, const int32_t* __restrict__ faces,
                 s_t[TV + k][j] = t.v[k];
                 s_t[TZ + k][j] = t.z[k];
             }
-            s_t[TA][j] = (t.u[1] - t.u[0]) * (t.v[2] - t.v[0]) - (t.v[1] - t.v[0]) * (t.u[2] - t.u[0]);
+            const double A = (t.u[1] - t.u[0]) * (t.v[2] - t.v[0]) - (t.v[1] - t.v[0]) * (t.u[2] - t.u[0]);
+            s_t[TA][j] = A;
             s_f[j] = f;
-            // a pixel centre covered by the triangle lies in its bounding box; the box
-            // is widened by a pixel so that it never excludes a pixel the fp64 edge
-            // test would accept
+            // Candidates: the tile's pixel centres within ZB_MARGIN of the triangle's
+            // bounding box, which hold every centre the fp64 edge test accepts when the
+            // triangle is not too thin.  A centre p at distance >= d from the triangle
+            // has an edge k with E_k(p) beyond |e_k| d sin(theta_min / 2) on the outer
+            // side (the nearest point of the triangle is on edge k, or at a vertex whose
+            // normal cone holds p), while the rounding of E_k (two differences, two
+            // products, one subtraction) is below 8 eps |e_k| R, R bounding |p - vertex|
+            // in the L1 norm over the tile.  With sin(theta_min / 2) >= |A| / (2 L^2)
+            // (A twice the signed area, L the longest edge) the sign is exact once
+            // |A| > 16 eps R L^2 / d = 2^-43 R L^2 at d = 1/64 px; the test uses 2^-40.
+            // Thinner triangles test every pixel of the tile, as the definition does.
             const double umin = fmin(fmin(t.u[0], t.u[1]), t.u[2]), umax = fmax(fmax(t.u[0], t.u[1]), t.u[2]);
             const double vmin = fmin(fmin(t.v[0], t.v[1]), t.v[2]), vmax = fmax(fmax(t.v[0], t.v[1]), t.v[2]);
-            // pixel-centre range [ceil(min - 1/2), floor(max - 1/2)], widened by one pixel
-            const int x0 = (int)fmax(ceil(umin - 0.5) - 1.0 - ox, 0.0);
-            const int x1 = (int)fmin(floor(umax - 0.5) + 1.0 - ox, xlim - 1.0);
-            const int y0 = (int)fmax(ceil(vmin - 0.5) - 1.0 - oy, 0.0);
-            const int y1 = (int)fmin(floor(vmax - 0.5) + 1.0 - oy, ylim - 1.0);
+            double L2 = 0.0, R = 0.0;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                const int k1 = k == 2 ? 0 : k + 1;
+                const double du = t.u[k1] - t.u[k], dv = t.v[k1] - t.v[k];
+                L2 = fmax(L2, du * du + dv * dv);
+                R = fmax(R, fabs(t.u[k] - (ox + 8.0)) + fabs(t.v[k] - (oy + 8.0)));
+            }
+            R += 16.0;
+            int x0 = 0, x1 = xlim - 1, y0 = 0, y1 = ylim - 1;
+            if (fabs(A) > 0x1p-40 * R * L2) {
+                // pixel-centre range [ceil(min - 1/2 - d), floor(max - 1/2 + d)]
+                x0 = (int)fmax(ceil(umin - 0.5 - ZB_MARGIN) - ox, 0.0);
+                x1 = (int)fmin(floor(umax - 0.5 + ZB_MARGIN) - ox, xlim - 1.0);
+                y0 = (int)fmax(ceil(vmin - 0.5 - ZB_MARGIN) - oy, 0.0);
+                y1 = (int)fmin(floor(vmax - 0.5 + ZB_MARGIN) - oy, ylim - 1.0);
+            }
             const int w = max(x1 - x0 + 1, 1);
             if (x0 <= x1 && y0 <= y1) cnt = w * (y1 - y0 + 1);
             s_box[j] = make_int4(x0, w, y0, __float_as_int(1.0f / (float)w));

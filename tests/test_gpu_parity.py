@@ -163,6 +163,60 @@ def test_tiny_random_scenes(seed):
     _check_all(s, 0, gpu, ora, tiles, True, "tiny %d" % seed)
 
 
+def _screen_soup(s, tris, rng):
+    """Soup of triangles given in screen space (u, v, z) for the scene's identity camera."""
+    pts = np.asarray(tris, np.float64).reshape(-1, 3)
+    x = (pts[:, 0] - s.cx) * pts[:, 2] / s.fx
+    y = (pts[:, 1] - s.cy) * pts[:, 2] / s.fy
+    tiny.set_mesh(s, np.stack([x, y, pts[:, 2]], 1), np.arange(len(pts)).reshape(-1, 3),
+                  vcolor=rng.uniform(size=(len(pts), 3)))
+
+
+def test_thin_triangles_zbuffer():
+    """Slivers: long thin triangles with a vertex far off screen (the z-buffer tests
+    every pixel of their tiles), thin ones inside the image (tested on the pixels
+    near their bounding box) and right triangles whose legs run along pixel-centre
+    rows and columns (edge functions exactly zero there): face ids and depths equal
+    the oracle's, which tests every pixel of every binned tile."""
+    s = tiny.random_tiny(23, n_tri=2, n_gauss=10, size=48)
+    rng = np.random.default_rng(23)
+    tris = []
+    for k in range(6):  # far vertex nearly on the line through two on-screen ones
+        p0 = rng.uniform(2, 46, 2)
+        p1 = rng.uniform(2, 46, 2)
+        d = p1 - p0
+        n = np.array([-d[1], d[0]]) / np.linalg.norm(d)
+        p2 = p0 + 1e6 * d + rng.uniform(0.3e6, 1.5e6) * rng.choice([-1.0, 1.0]) * n  # 0.3-1.5 px wide on screen
+        z = rng.uniform(2.5, 3.5)
+        tris.append([[p0[0], p0[1], z], [p1[0], p1[1], z + 0.2], [p2[0], p2[1], z]])
+    for k in range(10):  # thin slivers inside the image
+        p0 = rng.uniform(1, 47, 2)
+        p1 = rng.uniform(1, 47, 2)
+        d = p1 - p0
+        n = np.array([-d[1], d[0]]) / np.linalg.norm(d)
+        p2 = p0 + rng.uniform(-1.0, 2.0) * d + rng.uniform(-0.05, 0.05) * n
+        zz = rng.uniform(2.0, 4.0, 3)
+        tris.append([[p0[0], p0[1], zz[0]], [p1[0], p1[1], zz[1]], [p2[0], p2[1], zz[2]]])
+    for k in range(6):  # legs on pixel-centre lines
+        x0, y0 = rng.integers(0, 40, 2) + 0.5
+        a, b = rng.integers(1, 9, 2) * (1 if k % 2 else -1)
+        z = 3.0 + 0.1 * k
+        tris.append([[x0, y0, z], [x0 + a, y0, z], [x0, y0 + b, z]])
+    _screen_soup(s, tris, rng)
+    gpu, ora, tiles = _run(s, 0, cull=True)
+    _check_all(s, 0, gpu, ora, tiles, True, "thin triangles")
+    # the far-vertex slivers are thin enough that their tiles are tested in full
+    vs = gpu["vscreen"].astype(np.float64)
+    u, v = vs[0][s.faces], vs[1][s.faces]
+    A = (u[1] - u[0]) * (v[2] - v[0]) - (v[1] - v[0]) * (u[2] - u[0])
+    L2 = np.max([(u[(k + 1) % 3] - u[k]) ** 2 + (v[(k + 1) % 3] - v[k]) ** 2 for k in range(3)], 0)
+    R_low = np.max(np.abs(u - 24.0) + np.abs(v - 24.0), 0) - 48.0  # below R for any tile
+    full = np.abs(A) <= 2.0 ** -40 * R_low * L2
+    assert full[:6].sum() >= 3, (A[:6], L2[:6])
+    covered = np.unique(ora["face_id"][ora["face_id"] >= 0])
+    assert np.isin(np.arange(6)[full[:6]], covered).any()  # some fully tested sliver is visible
+
+
 def test_no_mesh_plain_splatting():
     s = tiny.random_tiny(5, n_tri=1, n_gauss=40, size=48)
     s.verts, s.faces, s.vcolor = None, None, None
