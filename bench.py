@@ -27,8 +27,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector (counts packed FMA)
-STAGES = ["bin", "zbuffer", "project", "sort", "fwd", "bwd"]
-STAGES_AA = ["bin", "zbuffer", "antialias", "project", "sort", "fwd", "bwd", "antialias_bwd"]
+# Stages of one step on the library's (main) stream, and on the second stream that
+# runs the projection and the depth half of the sort beside the mesh's binning and
+# z-buffer; "wait_lists" is the time the main stream waits for the second one.
+STAGES = ["bin", "zbuffer", "wait_lists", "sort", "fwd", "bwd"]
+STAGES_AA = ["bin", "zbuffer", "antialias", "wait_lists", "sort", "fwd", "bwd", "antialias_bwd"]
+SIDE_STAGES = ["project", "sort_depth"]
 
 WORKLOADS = {
     "c3": "1920x1080, 200k-face displaced sphere (vertex colour + Phong), 1M Gaussians SH3",
@@ -125,14 +129,30 @@ def main():
     aa = args.antialias and scene.F > 0
     stages = STAGES_AA if aa else STAGES
 
-    def step(ev=None):
-        st = torch.cuda.current_stream().cuda_stream
-        i = [0]
+    def step(ev=None, ev_side=None):
+        # the calls of Renderer.lists() with the overlap, spelled out to mark stages
+        main, side = torch.cuda.current_stream(), r._side_stream()
+        st = main.cuda_stream
+        i, j = [0], [0]
 
         def mark():
             if ev is not None:
-                ev[i[0]].record()
+                ev[i[0]].record(main)
             i[0] += 1
+
+        def mark_side():
+            if ev_side is not None:
+                ev_side[j[0]].record(side)
+            j[0] += 1
+        r._ev_main.record(main)
+        side.wait_event(r._ev_main)
+        with torch.cuda.stream(side):
+            mark_side()
+            r.project(view)
+            mark_side()
+            r.sort_depth(view)
+            mark_side()
+            r._ev_side.record(side)
         mark()
         G.gm_bin_triangles(cam, ds.mesh, r.vscreen, r.tile_offsets, r.tile_tris, r.pair_cap, r.counts[0:1],
                            r.ws_bin, st)
@@ -143,9 +163,9 @@ def main():
         if aa:
             r.antialias(view)
             mark()
-        r.project(view)
+        main.wait_event(r._ev_side)
         mark()
-        r.sort(view, True)
+        r.sort_tiles(view, True)
         mark()
         if aa:
             r.composite_fwd_aa(view)
@@ -173,13 +193,15 @@ def main():
 
     # timed region: K whole steps; stage events on the library's (current) stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    evs_side = [[torch.cuda.Event(enable_timing=True) for _ in range(len(SIDE_STAGES) + 1)]
+                for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
     for k in range(args.steps):
-        step(evs[k])
+        step(evs[k], evs_side[k])
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -187,6 +209,8 @@ def main():
         raise RuntimeError("a list outgrew its capacity inside the timed region")
     ms = t0.elapsed_time(t1) / args.steps
     stage_ms = {s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, s in enumerate(stages)}
+    stage_ms.update({s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs_side]))
+                     for i, s in enumerate(SIDE_STAGES)})
 
     px = scene.width * scene.height
     value = px / (ms * 1e-3) / 1e6
@@ -207,7 +231,8 @@ def main():
         "bin": 12 * V + 12 * V + 12 * F + 8 * Pp + 4 * T,
         "zbuffer": 4 * Pp + 12 * F + 12 * V + 8 * HW + 4 * T,
         "project": N * (12 + 16 + 12 + 4 + shb + 64),
-        "sort": 64 * N + 28 * K + 8 * T,
+        "sort_depth": 64 * N,
+        "sort": 28 * K + 8 * T,
         "fwd": 4 * K + 64 * nvis + 8 * HW + 12 * HW + 20 * HW + 20 * HW,
         "bwd": 4 * K + 64 * nvis + 8 * HW + 8 * HW + 12 * HW + 20 * HW + 52 * nvis + 16 * HW,
     }
@@ -228,7 +253,7 @@ def main():
     # stages are one main kernel each (the composite stages add a zero-fill or a
     # shading prepass of a few percent)
     dom = max(["zbuffer", "project", "fwd", "bwd"], key=stage_ms.get)
-    kname = {"bwd": "k_composite_bwd", "fwd": "k_composite_fwd", "sort": "gm_sort_tile_keys",
+    kname = {"bwd": "k_composite_bwd", "fwd": "k_composite_fwd", "sort": "gm_sort_tiles",
              "project": "k_project_gaussians", "zbuffer": "k_zbuffer", "bin": "gm_bin_triangles"}[dom]
     kfile = {"bwd": "gm_composite.hip", "fwd": "gm_composite.hip", "sort": "gm_sort.hip",
              "project": "gm_project.hip", "zbuffer": "gm_raster.hip", "bin": "gm_raster.hip"}[dom]

@@ -45,7 +45,7 @@ class GmMesh(C.Structure):
 
 EXPORTS = ["gm_bin_triangles_ws", "gm_bin_triangles", "gm_raster_zbuffer", "gm_project_gaussians",
            "gm_project_gaussians_multi",
-           "gm_sort_tile_keys_ws", "gm_sort_tile_keys", "gm_composite_hybrid_fwd",
+           "gm_sort_tile_keys_ws", "gm_sort_tile_keys", "gm_sort_depth", "gm_sort_tiles", "gm_composite_hybrid_fwd",
            "gm_composite_hybrid_bwd", "gm_project_gaussians_bwd", "gm_mesh_bwd", "gm_mipmaps_floats",
            "gm_build_mipmaps", "gm_last_error", "gm_version", "gm_edge_adjacency_ws", "gm_edge_adjacency",
            "gm_antialias", "gm_composite_hybrid_fwd_aa", "gm_composite_hybrid_bwd_aa", "gm_antialias_bwd_ws",
@@ -74,6 +74,8 @@ def lib():
     L.gm_sort_tile_keys_ws.argtypes = [I32, I64, I32, I32]
     L.gm_sort_tile_keys_ws.restype = SZ
     L.gm_sort_tile_keys.argtypes = [cam, I32, P, P, F32, P, P, I64, P, P, SZ, P]
+    L.gm_sort_depth.argtypes = [cam, I32, P, I64, P, SZ, P]
+    L.gm_sort_tiles.argtypes = [cam, I32, P, P, F32, P, P, I64, P, P, SZ, P]
     L.gm_composite_hybrid_fwd.argtypes = [cam, P, P, P, P, P, mesh, P, light, P, F32, P, P, P, P, P, P, P]
     L.gm_composite_hybrid_bwd.argtypes = [cam, I32, P, P, P, P, P, F32, P, P, P, P, P, P, P, P, P, P]
     L.gm_project_gaussians_bwd.argtypes = [cam, I32, P, P, P, P, P, I32, P, P, P, P, P, P, P, P, P, P]
@@ -99,7 +101,7 @@ def lib():
         if not hasattr(L, name):
             raise ImportError(f"{LIB_PATH} does not export {name}")
     for name in ("gm_bin_triangles", "gm_raster_zbuffer", "gm_project_gaussians", "gm_project_gaussians_multi",
-                 "gm_sort_tile_keys",
+                 "gm_sort_tile_keys", "gm_sort_depth", "gm_sort_tiles",
                  "gm_composite_hybrid_fwd", "gm_composite_hybrid_bwd", "gm_project_gaussians_bwd",
                  "gm_mesh_bwd", "gm_build_mipmaps", "gm_edge_adjacency", "gm_antialias", "gm_composite_hybrid_fwd_aa",
                  "gm_composite_hybrid_bwd_aa", "gm_antialias_bwd", "gm_vscreen_bwd"):
@@ -162,6 +164,19 @@ def gm_sort_tile_keys(cam, N, rec, tile_dmax, softness, tile_ranges, sorted_ids,
     check(lib().gm_sort_tile_keys(C.byref(cam), int(N), ptr(rec), ptr(tile_dmax), float(softness),
                                   ptr(tile_ranges), ptr(sorted_ids), int(cap), ptr(n_keys), ptr(ws),
                                   0 if ws is None else ws.numel() * ws.element_size(), stream))
+
+
+def gm_sort_depth(cam, N, rec, cap, ws, stream):
+    """First half of gm_sort_tile_keys: the depth order, kept in ws for gm_sort_tiles."""
+    check(lib().gm_sort_depth(C.byref(cam), int(N), ptr(rec), int(cap), ptr(ws),
+                              0 if ws is None else ws.numel() * ws.element_size(), stream))
+
+
+def gm_sort_tiles(cam, N, rec, tile_dmax, softness, tile_ranges, sorted_ids, cap, n_keys, ws, stream):
+    """Second half of gm_sort_tile_keys, ordered after gm_sort_depth on the same ws."""
+    check(lib().gm_sort_tiles(C.byref(cam), int(N), ptr(rec), ptr(tile_dmax), float(softness),
+                              ptr(tile_ranges), ptr(sorted_ids), int(cap), ptr(n_keys), ptr(ws),
+                              0 if ws is None else ws.numel() * ws.element_size(), stream))
 
 
 def _light_ref(light):

@@ -22,15 +22,11 @@ constexpr int RS_ITEMS = 16;
 constexpr int RS_CHUNK = RS_THREADS * RS_ITEMS;  // keys per block
 constexpr int RS_RADIX = 256;
 
-__global__ void k_sort_init(int32_t* __restrict__ ranges, int64_t n2, long long* __restrict__ n_keys,
-                            long long* __restrict__ d_n, long long n)
+__global__ void k_sort_init(int32_t* __restrict__ ranges, int64_t n2, long long* __restrict__ n_keys)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n2) ranges[i] = 0;
-    if (i == 0) {
-        *n_keys = 0;
-        *d_n = n;
-    }
+    if (i == 0) *n_keys = 0;
 }
 
 // Live key count of a pass.  A count above the buffers' capacity means the
@@ -194,22 +190,28 @@ static gm_status radix_pass(const uint32_t* kin, const int32_t* vin, uint32_t* k
     return GM_OK;
 }
 
+// Offsets ([digit][block], exclusive) of the last pass of a radix sort over at most
+// n_max keys, where radix_sort leaves them in its workspace.
+static int32_t* radix_last_offsets(void* ws, int64_t n_max)
+{
+    const int64_t nb = div_up(n_max > 0 ? n_max : 1, RS_CHUNK);
+    return (int32_t*)((char*)ws + align_up(sizeof(int32_t) * (size_t)(RS_RADIX * nb + 1), 256));
+}
+
 // Sorts n_max-bounded (keys, vals) by key bits [0, nbits) with LSD passes of at most 8
 // bits, split as evenly as possible (fewer digit values per pass than 256 give longer
 // runs of equal digits and so longer contiguous stores); the live count is *d_count
 // (device), zero when above n_max.  Ping-pongs between (ka, va) and (kb, vb): an even
-// number of passes ends in (ka, va), an odd one in (kb, vb).  *last_offs receives the
-// [digit][block] exclusive offsets of the last pass.
+// number of passes ends in (ka, va), an odd one in (kb, vb).  The last pass's
+// offsets stay in ws (radix_last_offsets) until the workspace is used again.
 static gm_status radix_sort(uint32_t* ka, int32_t* va, uint32_t* kb, int32_t* vb, int nbits,
-                            const long long* d_count, int64_t n_max, void* ws, hipStream_t stream,
-                            const int32_t** last_offs = nullptr)
+                            const long long* d_count, int64_t n_max, void* ws, hipStream_t stream)
 {
     const int nb = (int)div_up(n_max > 0 ? n_max : 1, RS_CHUNK);
     char* w = (char*)ws;
     int32_t* hist = (int32_t*)w;
-    w += align_up(sizeof(int32_t) * (size_t)(RS_RADIX * nb + 1), 256);
-    int32_t* offs = (int32_t*)w;
-    w += align_up(sizeof(int32_t) * (size_t)(RS_RADIX * nb + 1), 256);
+    int32_t* offs = radix_last_offsets(ws, n_max);
+    w = (char*)offs + align_up(sizeof(int32_t) * (size_t)(RS_RADIX * nb + 1), 256);
     long long* tot = (long long*)w;
     w += align_up(sizeof(long long), 256);
     void* scan_ws = w;
@@ -241,7 +243,6 @@ static gm_status radix_sort(uint32_t* ka, int32_t* va, uint32_t* kb, int32_t* vb
         kout = tk;
         vout = tv;
     }
-    if (last_offs) *last_offs = offs;
     return GM_OK;
 }
 
@@ -253,9 +254,10 @@ static gm_status radix_sort(uint32_t* ka, int32_t* va, uint32_t* kb, int32_t* vb
 // stable sort then puts the listed Gaussians first in (z_c, id) order, and the last
 // pass's offset of top byte 0xff is their number.
 __global__ void k_depth_keys(int N, const float* __restrict__ rec, uint32_t* __restrict__ keys,
-                             int32_t* __restrict__ vals)
+                             int32_t* __restrict__ vals, long long* __restrict__ d_n)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i == 0) *d_n = N;  // the key count of the sort that follows
     if (i >= N) return;
     const bool vis = __float_as_int(rec[(size_t)i * GM_REC + 15]) > 0;
     keys[i] = vis ? __float_as_uint(rec[(size_t)i * GM_REC + 9]) : 0xffffffffu;
@@ -567,39 +569,47 @@ size_t gm_sort_tile_keys_ws(int32_t N, int64_t cap, int32_t width, int32_t heigh
     return sort_layout(N, cap, T, nullptr, nullptr);
 }
 
-gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec, const float* tile_dmax,
-                            float softness, int32_t* tile_ranges, int32_t* sorted_ids, int64_t cap,
-                            int64_t* n_keys, void* ws, size_t ws_bytes, hipStream_t stream)
+// Host checks shared by the sort calls; fills the workspace layout.
+static gm_status sort_args(const gm_camera* cam, int32_t N, const float* rec, int64_t cap, void* ws,
+                           size_t ws_bytes, DevCamera* dc, SortWs* w)
 {
-    clear_error();
     if (gm_status s = check_camera(cam)) return s;
     GM_ARG_CHECK(N >= 0, "N = %d is negative", N);
-    GM_ARG_CHECK(softness >= 0.0f, "softness must be >= 0");
-    GM_ARG_CHECK(tile_ranges && n_keys && ws, "tile_ranges / n_keys / ws is NULL");
+    GM_ARG_CHECK(ws, "ws is NULL");
     GM_ARG_CHECK(N == 0 || rec, "rec is NULL");
-    GM_ARG_CHECK(cap >= 0 && (cap == 0 || sorted_ids), "sorted_ids is NULL or cap negative");
-    const DevCamera dc = dev_camera(*cam);
-    const int64_t T = (int64_t)dc.tx * dc.ty;
+    GM_ARG_CHECK(cap >= 0, "cap negative");
+    *dc = dev_camera(*cam);
+    const int64_t T = (int64_t)dc->tx * dc->ty;
     const size_t need = sort_layout(N, cap, T, nullptr, nullptr);
     GM_ARG_CHECK(ws_bytes >= need, "workspace %zu bytes, %zu needed", ws_bytes, need);
-    SortWs w;
-    sort_layout(N, cap, T, (char*)ws, &w);
+    sort_layout(N, cap, T, (char*)ws, w);
+    return GM_OK;
+}
 
-    long long* total = reinterpret_cast<long long*>(n_keys);
-    k_sort_init<<<(unsigned)div_up(2 * T, 256), 256, 0, stream>>>(tile_ranges, 2 * T, total, w.n, N);
+// 1. stable sort of all Gaussians by depth key; the listed ones come first.  The
+// order stays in (w.dka, w.dva), the histogram offsets of the last pass in w.aux.
+static gm_status sort_depth(const DevCamera& dc, int32_t N, const float* rec, const SortWs& w, hipStream_t stream)
+{
+    if (N == 0) return GM_OK;
+    k_depth_keys<<<(unsigned)div_up(N, 256), 256, 0, stream>>>(N, rec, w.dka, w.dva, w.n);
+    GM_LAUNCH_CHECK();
+    return radix_sort(w.dka, w.dva, w.dkb, w.dvb, 32, w.n, N, w.aux, stream);
+}
+
+// 2.-5. after sort_depth: pairs per chunk of 64 Gaussians in depth order (count, scan,
+// emit), stable sort by tile, tile ranges.
+static gm_status sort_tiles(const DevCamera& dc, int32_t N, const float* rec, const float* tile_dmax,
+                            float softness, int32_t* tile_ranges, int32_t* sorted_ids, int64_t cap,
+                            long long* total, const SortWs& w, hipStream_t stream)
+{
+    const int64_t T = (int64_t)dc.tx * dc.ty;
+    k_sort_init<<<(unsigned)div_up(2 * T, 256), 256, 0, stream>>>(tile_ranges, 2 * T, total);
     GM_LAUNCH_CHECK();
     if (N == 0) return GM_OK;
-    const unsigned gN = (unsigned)div_up(N, 256);
-    // 1. stable sort of all Gaussians by depth key; the listed ones come first
-    k_depth_keys<<<gN, 256, 0, stream>>>(N, rec, w.dka, w.dva);
-    GM_LAUNCH_CHECK();
-    const int32_t* offs = nullptr;
-    if (gm_status s = radix_sort(w.dka, w.dva, w.dkb, w.dvb, 32, w.n, N, w.aux, stream, &offs)) return s;
     const int32_t* order = w.dva;  // 4 passes: back in the first buffer pair
-    // number of listed Gaussians = offset of top byte 0xff in the last pass, block 0;
-    // it stays valid until the tile sort below reuses the histogram buffers
-    const int32_t* d_nvis = offs + (size_t)(RS_RADIX - 1) * div_up(N, RS_CHUNK);
-    // 2. surviving (Gaussian, tile) pairs per chunk of 64 Gaussians in depth order, scan
+    // number of listed Gaussians = offset of top byte 0xff in the depth sort's last
+    // pass, block 0; valid until the tile sort below reuses the histogram buffers
+    const int32_t* d_nvis = radix_last_offsets(w.aux, N) + (size_t)(RS_RADIX - 1) * div_up(N, RS_CHUNK);
     const bool lds = tile_dmax && T <= PW_LDS_MAX_TILES;
     CullParams cp{tile_dmax, softness};
     const size_t shm = lds ? sizeof(float) * (size_t)T : 0;
@@ -622,13 +632,54 @@ gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec, c
     int32_t* va = (npass % 2 == 0) ? sorted_ids : w.tva;
     int32_t* vb = (npass % 2 == 0) ? w.tva : sorted_ids;
     k_pairs<true, false><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, d_nvis, nchunks, order, rec, nullptr, w.off, w.bits,
-                                                   total, kcap, ka, va);
+                                                           total, kcap, ka, va);
     GM_LAUNCH_CHECK();
     if (gm_status s = radix_sort(ka, va, w.tkb, vb, tbits, total, kcap, w.aux, stream)) return s;
     const uint32_t* kfin = (npass % 2 == 0) ? w.tka : w.tkb;
     k_tile_ranges<<<(unsigned)div_up(div_up(kcap, 4), 256), 256, 0, stream>>>(kfin, total, kcap, tile_ranges);
     GM_LAUNCH_CHECK();
     return GM_OK;
+}
+
+gm_status gm_sort_depth(const gm_camera* cam, int32_t N, const float* rec, int64_t cap, void* ws, size_t ws_bytes,
+                        hipStream_t stream)
+{
+    clear_error();
+    DevCamera dc;
+    SortWs w;
+    if (gm_status s = sort_args(cam, N, rec, cap, ws, ws_bytes, &dc, &w)) return s;
+    return sort_depth(dc, N, rec, w, stream);
+}
+
+gm_status gm_sort_tiles(const gm_camera* cam, int32_t N, const float* rec, const float* tile_dmax, float softness,
+                        int32_t* tile_ranges, int32_t* sorted_ids, int64_t cap, int64_t* n_keys, void* ws,
+                        size_t ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    DevCamera dc;
+    SortWs w;
+    if (gm_status s = sort_args(cam, N, rec, cap, ws, ws_bytes, &dc, &w)) return s;
+    GM_ARG_CHECK(softness >= 0.0f, "softness must be >= 0");
+    GM_ARG_CHECK(tile_ranges && n_keys, "tile_ranges / n_keys is NULL");
+    GM_ARG_CHECK(cap == 0 || sorted_ids, "sorted_ids is NULL");
+    return sort_tiles(dc, N, rec, tile_dmax, softness, tile_ranges, sorted_ids, cap,
+                      reinterpret_cast<long long*>(n_keys), w, stream);
+}
+
+gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec, const float* tile_dmax,
+                            float softness, int32_t* tile_ranges, int32_t* sorted_ids, int64_t cap,
+                            int64_t* n_keys, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    DevCamera dc;
+    SortWs w;
+    if (gm_status s = sort_args(cam, N, rec, cap, ws, ws_bytes, &dc, &w)) return s;
+    GM_ARG_CHECK(softness >= 0.0f, "softness must be >= 0");
+    GM_ARG_CHECK(tile_ranges && n_keys, "tile_ranges / n_keys is NULL");
+    GM_ARG_CHECK(cap == 0 || sorted_ids, "sorted_ids is NULL");
+    if (gm_status s = sort_depth(dc, N, rec, w, stream)) return s;
+    return sort_tiles(dc, N, rec, tile_dmax, softness, tile_ranges, sorted_ids, cap,
+                      reinterpret_cast<long long*>(n_keys), w, stream);
 }
 
 }  // extern "C"

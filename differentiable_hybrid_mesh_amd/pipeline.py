@@ -146,6 +146,7 @@ class Renderer:
         self._rows = 1
         self.view = 0
         self.cull = True
+        self._side = None  # second stream of lists(), made on first use
 
     def _alloc_keys(self, cap):
         s = self.ds.scene
@@ -173,6 +174,52 @@ class Renderer:
         dmax = self.tile_dmax if cull else None
         G.gm_sort_tile_keys(ds.cams[view], self.N, self.rec, dmax, s.softness, self.tile_ranges, self.sorted_ids,
                             self.key_cap, self.counts[1:2], self.ws_sort, _stream())
+
+    def sort_depth(self, view: int):
+        """First half of sort(): the depth order (reads the records only)."""
+        ds, s = self.ds, self.ds.scene
+        G.gm_sort_depth(ds.cams[view], self.N, self.rec, self.key_cap, self.ws_sort, _stream())
+
+    def sort_tiles(self, view: int, cull: bool = True):
+        """Second half of sort(): cull, lists, tile order (after sort_depth and the z-buffer)."""
+        ds, s = self.ds, self.ds.scene
+        dmax = self.tile_dmax if cull else None
+        G.gm_sort_tiles(ds.cams[view], self.N, self.rec, dmax, s.softness, self.tile_ranges, self.sorted_ids,
+                        self.key_cap, self.counts[1:2], self.ws_sort, _stream())
+
+    def _side_stream(self):
+        if self._side is None:  # default priority, like every stream here
+            self._side = torch.cuda.Stream(device=self.ds.device)
+            self._ev_main = torch.cuda.Event()
+            self._ev_side = torch.cuda.Event()
+        return self._side
+
+    def lists(self, view: int, cull: bool = True, antialias: bool = False, overlap: bool = True):
+        """Mesh visibility (bin, z-buffer, antialiased layer) and Gaussian lists
+        (projection, sort).  With overlap the projection and the depth sort run on a
+        second stream beside the binning and z-buffer: the two branches share no
+        buffer, and only the tile lists need both (tile_dmax and the depth order).  The
+        side stream first waits for everything queued before (the previous step's
+        composite still reads the records and the lists)."""
+        if not overlap:
+            self.bin_and_zbuffer(view)
+            if antialias:
+                self.antialias(view)
+            self.project(view)
+            self.sort(view, cull)
+            return
+        main, side = torch.cuda.current_stream(), self._side_stream()
+        self._ev_main.record(main)
+        side.wait_event(self._ev_main)
+        with torch.cuda.stream(side):
+            self.project(view)
+            self.sort_depth(view)
+            self._ev_side.record(side)
+        self.bin_and_zbuffer(view)
+        if antialias:
+            self.antialias(view)
+        main.wait_event(self._ev_side)
+        self.sort_tiles(view, cull)
 
     def fetch_counts(self):
         """Queue a copy of the list lengths to pinned host memory (no wait)."""
@@ -375,11 +422,7 @@ class Renderer:
         The outputs are valid once read_counts() returns True for this pass."""
         self._single()
         self.view, self.cull, self.aa = view, cull, antialias
-        self.bin_and_zbuffer(view)
-        if antialias:
-            self.antialias(view)
-        self.project(view)
-        self.sort(view, cull)
+        self.lists(view, cull, antialias)
         if antialias:
             self.composite_fwd_aa(view)
         else:
@@ -390,11 +433,7 @@ class Renderer:
         """Run the list-producing calls (no compositing) until both lists fit."""
         self._single()
         while True:
-            self.bin_and_zbuffer(view)
-            if antialias:
-                self.antialias(view)
-            self.project(view)
-            self.sort(view, cull)
+            self.lists(view, cull, antialias)
             self.fetch_counts()
             torch.cuda.current_stream().synchronize()
             if self.read_counts():

@@ -207,6 +207,20 @@ gm_status gm_sort_tile_keys(const gm_camera* cam, int32_t N, const float* rec,
                             int32_t* sorted_ids, int64_t cap, int64_t* n_keys, void* ws,
                             size_t ws_bytes, hipStream_t stream);
 
+/* The two halves of gm_sort_tile_keys, which is gm_sort_depth followed by
+ * gm_sort_tiles with the same arguments.  gm_sort_depth orders the N Gaussians by
+ * (bits of z_c, i) and keeps that order in ws; it reads rec only (not tile_dmax), so
+ * a caller may run it on another stream than the mesh's z-buffer.  gm_sort_tiles
+ * then culls, lists and sorts by tile; it must be ordered after gm_sort_depth on the
+ * same ws, rec, N, cap and image size (same ws_bytes rule), and after whatever
+ * wrote tile_dmax.  Between the two calls ws belongs to the pair: no other call may
+ * use it.  Arguments, outputs and errors as for gm_sort_tile_keys. */
+gm_status gm_sort_depth(const gm_camera* cam, int32_t N, const float* rec, int64_t cap, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+gm_status gm_sort_tiles(const gm_camera* cam, int32_t N, const float* rec, const float* tile_dmax,
+                        float softness, int32_t* tile_ranges, int32_t* sorted_ids, int64_t cap,
+                        int64_t* n_keys, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * 5. gm_composite_hybrid_fwd — depth-tested front-to-back composite.
  * README "Hybrid rendering": per pixel each Gaussian is split at the mesh surface,

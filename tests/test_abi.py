@@ -76,6 +76,12 @@ def test_argument_errors_before_any_launch(G):
     # negative softness
     assert L.gm_sort_tile_keys(C.byref(cam), 0, None, None, C.c_float(-1.0), 16, None, 0, 16, 16,
                                1 << 20, None) == G.GM_ERR_ARG
+    # the two halves of the sort: workspace too small, negative softness
+    assert L.gm_sort_depth(C.byref(cam), 10, 16, 100, 16, 16, None) == G.GM_ERR_ARG
+    assert b"workspace" in L.gm_last_error()
+    assert L.gm_sort_tiles(C.byref(cam), 0, None, None, C.c_float(-1.0), 16, None, 0, 16, 16,
+                           1 << 20, None) == G.GM_ERR_ARG
+    assert b"softness" in L.gm_last_error()
     # texture side not a power of two
     assert L.gm_build_mipmaps(16, 100, 16, None) == G.GM_ERR_ARG
     # rec misaligned
