@@ -100,6 +100,31 @@ def measured_traffic(kernel, kernel_file, config):
     return float(b.group(1))
 
 
+def sources_digest():
+    """SHA-256 (first 16 hex digits) of all kernel sources, *.hip then *.h in name order."""
+    import glob
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "differentiable_hybrid_mesh_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(d, "*.hip"))) + sorted(glob.glob(os.path.join(d, "*.h"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_step_traffic(config):
+    """HBM bytes of one whole step (every kernel) from the committed FETCH_SIZE /
+    WRITE_SIZE summary, or None when any kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_step_{config}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"sources_sha256_16:\s*([0-9a-f]+)", text)
+    b = re.search(r"hbm_bytes_per_step:\s*([0-9.e+]+)", text)
+    if not m or not b or m.group(1) != sources_digest():
+        return None
+    return float(b.group(1))
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -283,6 +308,13 @@ def main():
                 cam, ds.mesh, r.g_vscreen, r.gm_verts, torch.cuda.current_stream().cuda_stream), args.steps)
 
     total_alg = sum(alg_bytes.values())
+    # measured HBM traffic of a whole step (rocprofv3 counters, separate run) over the
+    # unprofiled step time; only for the default-path workload it was taken on
+    step_bytes = None if aa else measured_step_traffic(args.config)
+    hbm_measured = None if step_bytes is None else {
+        "bytes_per_step": step_bytes, "GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "source": f"profiles/traffic_step_{args.config}.md"}
     out = {
         "metric": "hybrid render Mpixels/s fwd+bwd at 1080p",
         "value": round(value, 3), "unit": "Mpixels/s", "n_gpus": 1, "steps": args.steps,
@@ -295,6 +327,7 @@ def main():
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "hbm_algorithmic_GBps": round(total_alg / (ms * 1e-3) / 1e9, 1),
         "hbm_algorithmic_frac": round(total_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "hbm_measured": hbm_measured,
         "roofline": roof,
         "next_stages": next_stages,
         "wall_s": round(wall, 3),
