@@ -40,9 +40,9 @@ __device__ inline long long live_count(const long long* __restrict__ d_count, lo
 // ---------------------------------------------------------------------------
 // stable LSD radix sort pass over a digit of BITS <= 8 bits
 // ---------------------------------------------------------------------------
-template <int BITS>
+template <int BITS, typename KT>
 __global__ void __launch_bounds__(RS_THREADS)
-k_radix_hist(const uint32_t* __restrict__ keys, const long long* __restrict__ d_count, long long n_max,
+k_radix_hist(const KT* __restrict__ keys, const long long* __restrict__ d_count, long long n_max,
              int shift, int nblocks, int32_t* __restrict__ hist)
 {
     constexpr int R = 1 << BITS;
@@ -56,7 +56,7 @@ k_radix_hist(const uint32_t* __restrict__ keys, const long long* __restrict__ d_
 #pragma unroll 4
     for (int k = 0; k < RS_ITEMS; ++k) {
         const long long e = base + (long long)k * RS_THREADS + threadIdx.x;
-        if (e < n) atomicAdd(&h[wave][(keys[e] >> shift) & (R - 1)], 1);
+        if (e < n) atomicAdd(&h[wave][((uint32_t)keys[e] >> shift) & (R - 1)], 1);
     }
     __syncthreads();
     if (threadIdx.x < R) {
@@ -74,13 +74,13 @@ k_radix_hist(const uint32_t* __restrict__ keys, const long long* __restrict__ d_
 // program order).  One block scan then turns the per-wave counts into bases, keys
 // are placed in LDS in digit order, and each digit's run leaves the block as
 // contiguous stores.
-template <int BITS>
+template <int BITS, typename KT>
 __global__ void __launch_bounds__(RS_THREADS)
-k_radix_scatter(const uint32_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
+k_radix_scatter(const KT* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
                 const long long* __restrict__ d_count, long long n_max, int shift, int nblocks,
-                const int32_t* __restrict__ offs, uint32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out)
+                const int32_t* __restrict__ offs, KT* __restrict__ keys_out, int32_t* __restrict__ vals_out)
 {
-    __shared__ uint32_t s_k[RS_CHUNK];
+    __shared__ KT s_k[RS_CHUNK];
     __shared__ int32_t s_v[RS_CHUNK];
     __shared__ int32_t s_wc[RS_WAVES][RS_RADIX];  // running counts per wave, then per-wave bases
     __shared__ int32_t s_lstart[RS_RADIX], s_goff[RS_RADIX];
@@ -95,7 +95,7 @@ k_radix_scatter(const uint32_t* __restrict__ keys_in, const int32_t* __restrict_
     for (int w = 0; w < RS_WAVES; ++w) s_wc[w][t] = 0;
     if (t < R) s_goff[t] = offs[t * nblocks + blockIdx.x];
     __syncthreads();
-    uint32_t key[RS_ITEMS];
+    uint32_t key[RS_ITEMS];  // KT widened
     int32_t val[RS_ITEMS];
     int rank[RS_ITEMS];
     const long long wbase = base + (long long)wave * (RS_CHUNK / RS_WAVES);
@@ -153,14 +153,14 @@ k_radix_scatter(const uint32_t* __restrict__ keys_in, const int32_t* __restrict_
     for (int r = 0; r < RS_ITEMS; ++r) {
         if (wbase + r * 64 + lane < n) {
             const int pos = s_wc[wave][(key[r] >> shift) & (R - 1)] + rank[r];
-            s_k[pos] = key[r];
+            s_k[pos] = (KT)key[r];
             s_v[pos] = val[r];
         }
     }
     __syncthreads();
     const int nvalid = (int)min((long long)RS_CHUNK, n - base);
     for (int p = t; p < nvalid; p += RS_THREADS) {
-        const uint32_t k = s_k[p];
+        const KT k = s_k[p];
         const int d = (k >> shift) & (R - 1);
         const int g = s_goff[d] + (p - s_lstart[d]);
         keys_out[g] = k;
@@ -177,15 +177,15 @@ size_t radix_ws_bytes(int64_t n)
            align_up(sizeof(long long), 256);
 }
 
-template <int BITS>
-static gm_status radix_pass(const uint32_t* kin, const int32_t* vin, uint32_t* kout, int32_t* vout, int shift,
+template <int BITS, typename KT>
+static gm_status radix_pass(const KT* kin, const int32_t* vin, KT* kout, int32_t* vout, int shift,
                             const long long* d_count, int64_t n_max, int nb, int32_t* hist, int32_t* offs,
                             long long* tot, void* scan_ws, hipStream_t stream)
 {
-    k_radix_hist<BITS><<<nb, RS_THREADS, 0, stream>>>(kin, d_count, n_max, shift, nb, hist);
+    k_radix_hist<BITS, KT><<<nb, RS_THREADS, 0, stream>>>(kin, d_count, n_max, shift, nb, hist);
     GM_LAUNCH_CHECK();
     if (gm_status s = exclusive_scan(hist, offs, (int64_t)(1 << BITS) * nb, tot, scan_ws, stream)) return s;
-    k_radix_scatter<BITS><<<nb, RS_THREADS, 0, stream>>>(kin, vin, d_count, n_max, shift, nb, offs, kout, vout);
+    k_radix_scatter<BITS, KT><<<nb, RS_THREADS, 0, stream>>>(kin, vin, d_count, n_max, shift, nb, offs, kout, vout);
     GM_LAUNCH_CHECK();
     return GM_OK;
 }
@@ -204,7 +204,8 @@ static int32_t* radix_last_offsets(void* ws, int64_t n_max)
 // (device), zero when above n_max.  Ping-pongs between (ka, va) and (kb, vb): an even
 // number of passes ends in (ka, va), an odd one in (kb, vb).  The last pass's
 // offsets stay in ws (radix_last_offsets) until the workspace is used again.
-static gm_status radix_sort(uint32_t* ka, int32_t* va, uint32_t* kb, int32_t* vb, int nbits,
+template <typename KT>
+static gm_status radix_sort(KT* ka, int32_t* va, KT* kb, int32_t* vb, int nbits,
                             const long long* d_count, int64_t n_max, void* ws, hipStream_t stream)
 {
     const int nb = (int)div_up(n_max > 0 ? n_max : 1, RS_CHUNK);
@@ -215,9 +216,9 @@ static gm_status radix_sort(uint32_t* ka, int32_t* va, uint32_t* kb, int32_t* vb
     long long* tot = (long long*)w;
     w += align_up(sizeof(long long), 256);
     void* scan_ws = w;
-    uint32_t* kin = ka;
+    KT* kin = ka;
     int32_t* vin = va;
-    uint32_t* kout = kb;
+    KT* kout = kb;
     int32_t* vout = vb;
     const int npass = radix_passes(nbits);
     int shift = 0;
@@ -225,18 +226,18 @@ static gm_status radix_sort(uint32_t* ka, int32_t* va, uint32_t* kb, int32_t* vb
         const int bits = (nbits - shift + (npass - p) - 1) / (npass - p);  // ceil(remaining / passes left)
         gm_status s = GM_OK;
         switch (bits) {
-        case 1: s = radix_pass<1>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        case 2: s = radix_pass<2>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        case 3: s = radix_pass<3>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        case 4: s = radix_pass<4>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        case 5: s = radix_pass<5>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        case 6: s = radix_pass<6>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        case 7: s = radix_pass<7>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        default: s = radix_pass<8>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 1: s = radix_pass<1, KT>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 2: s = radix_pass<2, KT>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 3: s = radix_pass<3, KT>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 4: s = radix_pass<4, KT>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 5: s = radix_pass<5, KT>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 6: s = radix_pass<6, KT>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 7: s = radix_pass<7, KT>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        default: s = radix_pass<8, KT>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
         }
         if (s) return s;
         shift += bits;
-        uint32_t* tk = kin;
+        KT* tk = kin;
         int32_t* tv = vin;
         kin = kout;
         vin = vout;
@@ -367,12 +368,12 @@ __device__ __forceinline__ void skip_owner(const ChunkCtx& c, int f0, int& carry
 
 // LDS: tile_dmax is staged in LDS (a compile-time choice, so the cull's read is a
 // plain LDS load rather than a generic one through a pointer picked at run time).
-template <bool EMIT, bool LDS>
+template <bool EMIT, bool LDS, typename KT>
 __global__ void __launch_bounds__(64 * PW_WAVES)
 k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nchunks,
         const int32_t* __restrict__ order, const float* __restrict__ rec, int32_t* __restrict__ chunk_cnt,
         const int32_t* __restrict__ chunk_off, unsigned long long* __restrict__ bits,
-        const long long* __restrict__ d_total, long long cap, uint32_t* __restrict__ tkeys,
+        const long long* __restrict__ d_total, long long cap, KT* __restrict__ tkeys,
         int32_t* __restrict__ tvals)
 {
     extern __shared__ float s_dmax[];       // tile_dmax when LDS
@@ -475,7 +476,7 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
                 }
                 if ((km >> lane) & 1ull) {
                     const int q = p + __popcll(km & c.lt);
-                    tkeys[q] = (uint32_t)tile;
+                    tkeys[q] = (KT)tile;
                     tvals[q] = id;
                 }
                 p += __popcll(km);
@@ -486,8 +487,10 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
     }
 }
 
-// Tile ranges from the tile-sorted keys, four keys per thread.
-__global__ void k_tile_ranges(const uint32_t* __restrict__ keys, const long long* __restrict__ d_count,
+// Tile ranges from the tile-sorted keys, four keys per thread (KT: 16-bit tile ids
+// when the image has at most 65536 tiles, else 32-bit).
+template <typename KT>
+__global__ void k_tile_ranges(const KT* __restrict__ keys, const long long* __restrict__ d_count,
                               long long n_max, int32_t* __restrict__ ranges)
 {
     const long long K = live_count(d_count, n_max);
@@ -495,12 +498,20 @@ __global__ void k_tile_ranges(const uint32_t* __restrict__ keys, const long long
     if (k0 >= K) return;
     uint32_t v[6];  // keys k0 - 1 .. k0 + 4, all ones outside [0, K)
     v[0] = k0 > 0 ? keys[k0 - 1] : 0xffffffffu;
-    if (k0 + 4 <= K) {
-        const uint4 q = *reinterpret_cast<const uint4*>(keys + k0);  // k0 % 4 == 0, buffer 16-B aligned
-        v[1] = q.x;
-        v[2] = q.y;
-        v[3] = q.z;
-        v[4] = q.w;
+    if (k0 + 4 <= K) {  // k0 % 4 == 0, buffer 256-B aligned: one 4-key vector load
+        if constexpr (sizeof(KT) == 4) {
+            const uint4 q = *reinterpret_cast<const uint4*>(keys + k0);
+            v[1] = q.x;
+            v[2] = q.y;
+            v[3] = q.z;
+            v[4] = q.w;
+        } else {
+            const uint2 q = *reinterpret_cast<const uint2*>(keys + k0);
+            v[1] = q.x & 0xffffu;
+            v[2] = q.x >> 16;
+            v[3] = q.y & 0xffffu;
+            v[4] = q.y >> 16;
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[1 + i] = k0 + i < K ? keys[k0 + i] : 0xffffffffu;
@@ -557,18 +568,6 @@ static size_t sort_layout(int64_t N, int64_t cap, int64_t T, char* base, SortWs*
     return o;
 }
 
-}  // namespace gm
-
-using namespace gm;
-
-extern "C" {
-
-size_t gm_sort_tile_keys_ws(int32_t N, int64_t cap, int32_t width, int32_t height)
-{
-    const int64_t T = div_up(width, GM_TILE) * div_up(height, GM_TILE);
-    return sort_layout(N, cap, T, nullptr, nullptr);
-}
-
 // Host checks shared by the sort calls; fills the workspace layout.
 static gm_status sort_args(const gm_camera* cam, int32_t N, const float* rec, int64_t cap, void* ws,
                            size_t ws_bytes, DevCamera* dc, SortWs* w)
@@ -596,6 +595,31 @@ static gm_status sort_depth(const DevCamera& dc, int32_t N, const float* rec, co
     return radix_sort(w.dka, w.dva, w.dkb, w.dvb, 32, w.n, N, w.aux, stream);
 }
 
+// Emission of the (tile, id) pairs with tile keys of type KT, their stable sort by
+// tile and the tile ranges.
+template <typename KT>
+static gm_status emit_and_sort(const DevCamera& dc, const CullParams& cp, const int32_t* d_nvis, int nchunks,
+                               unsigned gW, const int32_t* order, const float* rec, long long* total, int64_t kcap,
+                               int64_t T, int32_t* sorted_ids, int32_t* tile_ranges, const SortWs& w,
+                               hipStream_t stream)
+{
+    int tbits = 0;
+    while (tbits < 31 && ((T - 1) >> tbits)) ++tbits;
+    const int npass = radix_passes(tbits);
+    KT* ka = reinterpret_cast<KT*>(w.tka);
+    KT* kb = reinterpret_cast<KT*>(w.tkb);
+    int32_t* va = (npass % 2 == 0) ? sorted_ids : w.tva;
+    int32_t* vb = (npass % 2 == 0) ? w.tva : sorted_ids;
+    k_pairs<true, false, KT><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, d_nvis, nchunks, order, rec, nullptr, w.off,
+                                                               w.bits, total, kcap, ka, va);
+    GM_LAUNCH_CHECK();
+    if (gm_status s = radix_sort<KT>(ka, va, kb, vb, tbits, total, kcap, w.aux, stream)) return s;
+    const KT* kfin = (npass % 2 == 0) ? ka : kb;
+    k_tile_ranges<KT><<<(unsigned)div_up(div_up(kcap, 4), 256), 256, 0, stream>>>(kfin, total, kcap, tile_ranges);
+    GM_LAUNCH_CHECK();
+    return GM_OK;
+}
+
 // 2.-5. after sort_depth: pairs per chunk of 64 Gaussians in depth order (count, scan,
 // emit), stable sort by tile, tile ranges.
 static gm_status sort_tiles(const DevCamera& dc, int32_t N, const float* rec, const float* tile_dmax,
@@ -615,7 +639,7 @@ static gm_status sort_tiles(const DevCamera& dc, int32_t N, const float* rec, co
     const size_t shm = lds ? sizeof(float) * (size_t)T : 0;
     const int nchunks = (int)div_up(N, 64);
     const unsigned gW = (unsigned)std::min<int64_t>(div_up(nchunks, PW_WAVES), 512);
-    auto count = lds ? k_pairs<false, true> : k_pairs<false, false>;
+    auto count = lds ? k_pairs<false, true, uint16_t> : k_pairs<false, false, uint16_t>;  // no keys written
     count<<<gW, 64 * PW_WAVES, shm, stream>>>(dc, cp, d_nvis, nchunks, order, rec, w.cnt, nullptr, w.bits, nullptr, 0,
                                               nullptr, nullptr);
     GM_LAUNCH_CHECK();
@@ -625,20 +649,23 @@ static gm_status sort_tiles(const DevCamera& dc, int32_t N, const float* rec, co
     //    writes nothing above it.
     const int64_t kcap = std::min<int64_t>(cap, INT32_MAX);
     if (kcap == 0) return GM_OK;
-    int tbits = 0;
-    while (tbits < 31 && ((T - 1) >> tbits)) ++tbits;
-    const int npass = radix_passes(tbits);
-    uint32_t* ka = w.tka;
-    int32_t* va = (npass % 2 == 0) ? sorted_ids : w.tva;
-    int32_t* vb = (npass % 2 == 0) ? w.tva : sorted_ids;
-    k_pairs<true, false><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, d_nvis, nchunks, order, rec, nullptr, w.off, w.bits,
-                                                           total, kcap, ka, va);
-    GM_LAUNCH_CHECK();
-    if (gm_status s = radix_sort(ka, va, w.tkb, vb, tbits, total, kcap, w.aux, stream)) return s;
-    const uint32_t* kfin = (npass % 2 == 0) ? w.tka : w.tkb;
-    k_tile_ranges<<<(unsigned)div_up(div_up(kcap, 4), 256), 256, 0, stream>>>(kfin, total, kcap, tile_ranges);
-    GM_LAUNCH_CHECK();
-    return GM_OK;
+    if (T <= 65536)  // 16-bit tile keys: 12 instead of 16 bytes per key and pass
+        return emit_and_sort<uint16_t>(dc, cp, d_nvis, nchunks, gW, order, rec, total, kcap, T, sorted_ids,
+                                       tile_ranges, w, stream);
+    return emit_and_sort<uint32_t>(dc, cp, d_nvis, nchunks, gW, order, rec, total, kcap, T, sorted_ids, tile_ranges,
+                                   w, stream);
+}
+
+}  // namespace gm
+
+using namespace gm;
+
+extern "C" {
+
+size_t gm_sort_tile_keys_ws(int32_t N, int64_t cap, int32_t width, int32_t height)
+{
+    const int64_t T = div_up(width, GM_TILE) * div_up(height, GM_TILE);
+    return sort_layout(N, cap, T, nullptr, nullptr);
 }
 
 gm_status gm_sort_depth(const gm_camera* cam, int32_t N, const float* rec, int64_t cap, void* ws, size_t ws_bytes,

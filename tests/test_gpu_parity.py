@@ -217,6 +217,63 @@ def test_thin_triangles_zbuffer():
     assert np.isin(np.arange(6)[full[:6]], covered).any()  # some fully tested sliver is visible
 
 
+def test_lists_above_65536_tiles():
+    """A 4112 x 4096 image has 257 x 256 = 65792 tiles: the tile sort keeps 32-bit
+    keys (16-bit at most 65536 tiles) and the count pass reads tile_dmax from memory
+    (staged in LDS up to 10240 tiles).  Lists on sampled tiles, ids above 65535
+    among them, are the oracle's; culling is on, with triangles covering whole tiles."""
+    import torch
+    from differentiable_hybrid_mesh_amd.pipeline import DeviceScene, Renderer
+    W, H = 4112, 4096
+    rng = np.random.default_rng(41)
+    s = tiny.empty_scene(W, H, 2000.0, 2000.0, W / 2, H / 2, name="65792 tiles")
+    n = 3000
+    u = np.concatenate([rng.uniform(0, W, n - 300), rng.uniform(0, W, 300)])
+    v = np.concatenate([rng.uniform(0, H, n - 300), rng.uniform(H - 20, H, 300)])  # the last tile row too
+    z = rng.uniform(2.0, 4.0, n)
+    means = np.stack([(u - s.cx) * z / s.fx, (v - s.cy) * z / s.fy, z], 1)
+    q = rng.normal(size=(n, 4))
+    q /= np.linalg.norm(q, axis=1, keepdims=True)
+    sc = np.exp(rng.normal(-6.0, 0.4, size=(n, 3)))  # a few pixels on screen
+    op = 1.0 / (1.0 + np.exp(-rng.normal(size=n)))
+    tiny.set_gaussians(s, means, q, sc, op, rgb=rng.uniform(size=(n, 3)))
+    tris = []
+    for k in range(60):  # large triangles: fully covered tiles for the cull
+        c = rng.uniform([0, 0], [W, H])
+        r = rng.uniform(100, 400)
+        a = rng.uniform(0, 2 * np.pi) + np.array([0, 2.1, 4.2])
+        zz = rng.uniform(2.5, 3.5)
+        tris.append([[c[0] + r * np.cos(t), c[1] + r * np.sin(t), zz] for t in a])
+    _screen_soup(s, tris, rng)
+    r = Renderer(DeviceScene(s))
+    r.fit_lists(0, cull=True)
+    torch.cuda.synchronize()
+    T = r.T
+    assert T == 65792
+    ranges = P.to_np(r.tile_ranges).reshape(-1, 2)
+    ids = P.to_np(r.sorted_ids)
+    tx = (u // 16).astype(int)
+    ty = (v // 16).astype(int)
+    near = np.unique(np.clip(ty, 0, 255) * 257 + np.clip(tx, 0, 256))
+    tiles = np.unique(np.concatenate([rng.choice(near, 250, replace=False), rng.integers(0, T, 50),
+                                      near[near >= 65536][:40]])).astype(np.int32)
+    assert (tiles >= 65536).sum() >= 20
+    cam = oracle.camera(s, 0)
+    vs = oracle.project_vertices(cam, s.verts)
+    zb = oracle.zbuffer(cam, vs, s.faces, s.face_mask, tiles=tiles, prefilter=True)
+    dm = np.where(np.isnan(zb["tile_dmax"]), np.inf, zb["tile_dmax"]).astype(np.float32)
+    assert np.array_equal(P.to_np(r.tile_dmax)[tiles].view(np.uint32), dm[tiles].view(np.uint32))
+    pg = oracle.project_gaussians(cam, s.means, s.quats, s.scales, s.opacity, s.sh, s.sh_degree)
+    order = oracle.depth_order(pg["rec"], pg["valid"])
+    pre = oracle.tile_lists(cam, pg["rec"], pg["rect"], order, tiles, tile_dmax=dm, softness=s.softness)
+    rep = P.compare_lists(s, {"ranges": ranges, "ids": ids}, {"lists_pre": pre}, tiles, True)
+    print("65792 tiles", rep, flush=True)
+    assert rep["list_mismatch"] == 0 and rep["entries"] > 300
+    hi = tiles[tiles >= 65536]
+    assert (ranges[hi, 1] > ranges[hi, 0]).sum() >= 10  # lists of tiles past 16-bit ids
+    assert int((dm[tiles] < np.inf).sum()) >= 5  # some sampled tiles are fully covered
+
+
 def test_no_mesh_plain_splatting():
     s = tiny.random_tiny(5, n_tri=1, n_gauss=40, size=48)
     s.verts, s.faces, s.vcolor = None, None, None
