@@ -46,7 +46,7 @@ class GmMesh(C.Structure):
 EXPORTS = ["gm_bin_triangles_ws", "gm_bin_triangles", "gm_raster_zbuffer", "gm_project_gaussians",
            "gm_project_gaussians_multi",
            "gm_sort_tile_keys_ws", "gm_sort_tile_keys", "gm_sort_depth", "gm_sort_tiles", "gm_composite_hybrid_fwd",
-           "gm_composite_hybrid_bwd", "gm_project_gaussians_bwd", "gm_mesh_bwd", "gm_mipmaps_floats",
+           "gm_composite_hybrid_bwd", "gm_composite_hybrid_bwd_ws", "gm_project_gaussians_bwd", "gm_mesh_bwd", "gm_mipmaps_floats",
            "gm_build_mipmaps", "gm_last_error", "gm_version", "gm_edge_adjacency_ws", "gm_edge_adjacency",
            "gm_antialias", "gm_composite_hybrid_fwd_aa", "gm_composite_hybrid_bwd_aa", "gm_antialias_bwd_ws",
            "gm_antialias_bwd", "gm_vscreen_bwd"]
@@ -77,7 +77,9 @@ def lib():
     L.gm_sort_depth.argtypes = [cam, I32, P, I64, P, SZ, P]
     L.gm_sort_tiles.argtypes = [cam, I32, P, P, F32, P, P, I64, P, P, SZ, P]
     L.gm_composite_hybrid_fwd.argtypes = [cam, P, P, P, P, P, mesh, P, light, P, F32, P, P, P, P, P, P, P]
-    L.gm_composite_hybrid_bwd.argtypes = [cam, I32, P, P, P, P, P, F32, P, P, P, P, P, P, P, P, P, P]
+    L.gm_composite_hybrid_bwd.argtypes = [cam, I32, P, P, P, P, P, F32, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    L.gm_composite_hybrid_bwd_ws.argtypes = [I32, I32]
+    L.gm_composite_hybrid_bwd_ws.restype = SZ
     L.gm_project_gaussians_bwd.argtypes = [cam, I32, P, P, P, P, P, I32, P, P, P, P, P, P, P, P, P, P]
     L.gm_mesh_bwd.argtypes = [cam, mesh, light, P, P, P, P, P, P, P, P, P, P]
     L.gm_edge_adjacency_ws.argtypes = [I32]
@@ -85,7 +87,7 @@ def lib():
     L.gm_edge_adjacency.argtypes = [mesh, P, P, SZ, P]
     L.gm_antialias.argtypes = [cam, mesh, P, P, light, P, P, P, P, P, P, P]
     L.gm_composite_hybrid_fwd_aa.argtypes = [cam, P, P, P, P, P, F32, P, P, P, P, P]
-    L.gm_composite_hybrid_bwd_aa.argtypes = [cam, I32, P, P, P, P, P, F32, P, P, P, P, P, P, P]
+    L.gm_composite_hybrid_bwd_aa.argtypes = [cam, I32, P, P, P, P, P, F32, P, P, P, P, P, P, P, SZ, P]
     L.gm_antialias_bwd_ws.argtypes = [I32, I32]
     L.gm_antialias_bwd_ws.restype = SZ
     L.gm_antialias_bwd.argtypes = [cam, mesh, P, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -193,12 +195,18 @@ def gm_composite_hybrid_fwd(cam, rec, tile_ranges, sorted_ids, face_id, depth, m
                                         ptr(state_last), ptr(state_cm), stream))
 
 
+def gm_composite_hybrid_bwd_ws(width, height) -> int:
+    return lib().gm_composite_hybrid_bwd_ws(int(width), int(height))
+
+
 def gm_composite_hybrid_bwd(cam, N, rec, tile_ranges, sorted_ids, face_id, depth, softness, state_T, state_last,
-                            state_cm, g_rgb, g_depth, g_alpha, g_rec, g_mesh_rgb, g_mesh_depth, stream):
+                            state_cm, g_rgb, g_depth, g_alpha, g_rec, g_mesh_rgb, g_mesh_depth, ws, stream):
+    """ws: device scratch of gm_composite_hybrid_bwd_ws(width, height) bytes."""
     check(lib().gm_composite_hybrid_bwd(C.byref(cam), int(N), ptr(rec), ptr(tile_ranges), ptr(sorted_ids),
                                         ptr(face_id), ptr(depth), float(softness), ptr(state_T),
                                         ptr(state_last), ptr(state_cm), ptr(g_rgb), ptr(g_depth),
-                                        ptr(g_alpha), ptr(g_rec), ptr(g_mesh_rgb), ptr(g_mesh_depth), stream))
+                                        ptr(g_alpha), ptr(g_rec), ptr(g_mesh_rgb), ptr(g_mesh_depth), ptr(ws),
+                                        0 if ws is None else ws.numel() * ws.element_size(), stream))
 
 
 def gm_project_gaussians_bwd(cam, N, means, quats, scales, opacity, sh, sh_degree, rec, g_rec, g_means, g_quats,
@@ -253,11 +261,12 @@ def gm_composite_hybrid_fwd_aa(cam, rec, tile_ranges, sorted_ids, layer, bg, sof
 
 
 def gm_composite_hybrid_bwd_aa(cam, N, rec, tile_ranges, sorted_ids, layer, bg, softness, state, g_rgb, g_depth,
-                               g_alpha, g_rec, g_layer, stream):
+                               g_alpha, g_rec, g_layer, ws, stream):
     bgv = (C.c_float * 3)(*[float(x) for x in bg])
     check(lib().gm_composite_hybrid_bwd_aa(C.byref(cam), int(N), ptr(rec), ptr(tile_ranges), ptr(sorted_ids),
                                            ptr(layer), C.cast(bgv, C.c_void_p), float(softness), ptr(state), ptr(g_rgb),
-                                           ptr(g_depth), ptr(g_alpha), ptr(g_rec), ptr(g_layer), stream))
+                                           ptr(g_depth), ptr(g_alpha), ptr(g_rec), ptr(g_layer), ptr(ws),
+                                           0 if ws is None else ws.numel() * ws.element_size(), stream))
 
 
 def gm_antialias_bwd_ws(width, height) -> int:

@@ -598,13 +598,75 @@ __device__ __forceinline__ float wave_sum16(const float* v, int lane)
 // dL/ds = alpha phi(s) (dL/dalpha_F - dL/dalpha_B).  Both layers recover their
 // transmittance by division while walking back from max(last_F, last_B).  The
 // per-pixel outputs are dL/d(M, M_D, a_m, D) of the mesh layer.
+// Order in which the backward takes the tiles: longest walk first.  A tile's walk is
+// the sum over its four waves of the longest pixel walk (entries up to the last
+// included one, of either layer); walks differ by an order of magnitude across an
+// image, and blocks taken in raster order leave long tiles for the end of the grid.
+template <bool AA>
+__global__ void __launch_bounds__(CT)
+k_tile_walk(CompParams P, const int32_t* __restrict__ state_last, const float* __restrict__ state_aa,
+            int32_t* __restrict__ walk)
+{
+    __shared__ int s_w[CT / 64];
+    const int tile = blockIdx.x;
+    const int tx = tile % P.cam.tx, ty = tile / P.cam.tx;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int px = tx * GM_TILE + 8 * (wave & 1) + (lane & 7), py = ty * GM_TILE + 8 * (wave >> 1) + (lane >> 3);
+    int m = 0;
+    if (px < P.cam.width && py < P.cam.height) {
+        const int pix = py * P.cam.width + px;
+        if constexpr (AA) {
+            const float4 s0 = reinterpret_cast<const float4*>(state_aa)[2 * pix];
+            m = max(__float_as_int(s0.y), __float_as_int(s0.w));
+        } else {
+            m = state_last[pix];
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o, 64));
+    if (lane == 0) s_w[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) walk[tile] = s_w[0] + s_w[1] + s_w[2] + s_w[3];
+}
+
+// Counting sort of the tiles into TO_BUCKETS buckets of walk length, longest first
+// (one block; the order inside a bucket is unspecified).
+constexpr int TO_BUCKETS = 64;
+
+__global__ void __launch_bounds__(1024) k_tile_order(int T, const int32_t* __restrict__ walk,
+                                                     int32_t* __restrict__ order)
+{
+    __shared__ int s_cnt[TO_BUCKETS], s_base[TO_BUCKETS], s_max;
+    if (threadIdx.x < TO_BUCKETS) s_cnt[threadIdx.x] = 0;
+    if (threadIdx.x == 0) s_max = 0;
+    __syncthreads();
+    int m = 0;
+    for (int t = threadIdx.x; t < T; t += blockDim.x) m = max(m, walk[t]);
+    atomicMax(&s_max, m);
+    __syncthreads();
+    const long long den = (long long)s_max + 1;  // bucket = floor(walk * buckets / den) < buckets
+    auto bucket = [&](int t) { return TO_BUCKETS - 1 - (int)((long long)walk[t] * TO_BUCKETS / den); };
+    for (int t = threadIdx.x; t < T; t += blockDim.x) atomicAdd(&s_cnt[bucket(t)], 1);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int b = 0; b < TO_BUCKETS; ++b) {
+            s_base[b] = run;
+            run += s_cnt[b];
+        }
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < T; t += blockDim.x) order[atomicAdd(&s_base[bucket(t)], 1)] = t;
+}
+
 template <bool AA>
 __global__ void __launch_bounds__(CT)
 k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* __restrict__ state_last,
                 const float* __restrict__ state_cm, const float* __restrict__ layer,
                 const float* __restrict__ state_aa, const float* __restrict__ g_rgb,
                 const float* __restrict__ g_depth, const float* __restrict__ g_alpha, float* __restrict__ g_rec,
-                float* __restrict__ g_mesh_rgb, float* __restrict__ g_mesh_depth, float* __restrict__ g_layer)
+                float* __restrict__ g_mesh_rgb, float* __restrict__ g_mesh_depth, float* __restrict__ g_layer,
+                const int32_t* __restrict__ order)
 {
     __shared__ Staged s_g[CB];
     __shared__ int s_id[CB];
@@ -612,7 +674,7 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
     __shared__ float s_acc[CB][NBASIS];
     __shared__ float s_wd[CT / 64];
     __shared__ int s_wl[CT / 64];
-    const int tile = blockIdx.x;
+    const int tile = order[blockIdx.x];  // longest walks first
     const int tx = tile % P.cam.tx, ty = tile / P.cam.tx;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int px = tx * GM_TILE + 8 * (wave & 1) + (lane & 7), py = ty * GM_TILE + 8 * (wave >> 1) + (lane >> 3);
@@ -950,6 +1012,17 @@ gm_status launch_surface_colour(const gm_camera* cam, const gm_mesh* mesh, const
 
 using namespace gm;
 
+// The backward's workspace: per-tile walk lengths, then the tile order.
+static gm_status tile_order_ws(const gm_camera* cam, void* ws, size_t ws_bytes, int32_t** walk, int32_t** order)
+{
+    const size_t need = gm_composite_hybrid_bwd_ws(cam->width, cam->height);
+    GM_ARG_CHECK(ws != nullptr && ws_bytes >= need, "workspace %zu bytes, %zu needed", ws_bytes, need);
+    const int64_t T = div_up(cam->width, GM_TILE) * div_up(cam->height, GM_TILE);
+    *walk = static_cast<int32_t*>(ws);
+    *order = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up(sizeof(int32_t) * (size_t)T, 256));
+    return GM_OK;
+}
+
 extern "C" {
 
 gm_status gm_composite_hybrid_fwd(const gm_camera* cam, const float* rec, const int32_t* tile_ranges,
@@ -992,12 +1065,18 @@ gm_status gm_composite_hybrid_fwd_aa(const gm_camera* cam, const float* rec, con
     return GM_OK;
 }
 
+size_t gm_composite_hybrid_bwd_ws(int32_t width, int32_t height)
+{
+    const int64_t T = div_up(width > 0 ? width : 1, GM_TILE) * div_up(height > 0 ? height : 1, GM_TILE);
+    return 2 * align_up(sizeof(int32_t) * (size_t)T, 256);
+}
+
 gm_status gm_composite_hybrid_bwd(const gm_camera* cam, int32_t N, const float* rec, const int32_t* tile_ranges,
                                   const int32_t* sorted_ids, const int32_t* face_id, const float* depth,
                                   float softness, const float* state_T, const int32_t* state_last,
                                   const float* state_cm, const float* g_rgb, const float* g_depth,
                                   const float* g_alpha, float* g_rec, float* g_mesh_rgb, float* g_mesh_depth,
-                                  hipStream_t stream)
+                                  void* ws, size_t ws_bytes, hipStream_t stream)
 {
     clear_error();
     CompParams P;
@@ -1009,14 +1088,20 @@ gm_status gm_composite_hybrid_bwd(const gm_camera* cam, int32_t N, const float* 
     GM_ARG_CHECK(state_T && state_last && state_cm && g_rgb, "state or g_rgb is NULL");
     GM_ARG_CHECK(N == 0 || g_rec, "g_rec is NULL");
     const int64_t T = (int64_t)P.cam.tx * P.cam.ty;
+    int32_t *walk, *order;
+    if (gm_status s = tile_order_ws(cam, ws, ws_bytes, &walk, &order)) return s;
     if (N > 0) {
         const int64_t n = (int64_t)N * GM_GRAD;
         k_zero_f32<<<(unsigned)div_up(n, 256), 256, 0, stream>>>(g_rec, n);
         GM_LAUNCH_CHECK();
     }
+    k_tile_walk<false><<<(unsigned)T, CT, 0, stream>>>(P, state_last, nullptr, walk);
+    GM_LAUNCH_CHECK();
+    k_tile_order<<<1, 1024, 0, stream>>>((int)T, walk, order);
+    GM_LAUNCH_CHECK();
     k_composite_bwd<false><<<(unsigned)T, CT, 0, stream>>>(P, state_T, state_last, state_cm, nullptr, nullptr,
                                                           g_rgb, g_depth, g_alpha, g_rec, g_mesh_rgb, g_mesh_depth,
-                                                          nullptr);
+                                                          nullptr, order);
     GM_LAUNCH_CHECK();
     return GM_OK;
 }
@@ -1024,7 +1109,8 @@ gm_status gm_composite_hybrid_bwd(const gm_camera* cam, int32_t N, const float* 
 gm_status gm_composite_hybrid_bwd_aa(const gm_camera* cam, int32_t N, const float* rec, const int32_t* tile_ranges,
                                      const int32_t* sorted_ids, const float* layer, const float* bg, float softness,
                                      const float* state, const float* g_rgb, const float* g_depth,
-                                     const float* g_alpha, float* g_rec, float* g_layer, hipStream_t stream)
+                                     const float* g_alpha, float* g_rec, float* g_layer, void* ws, size_t ws_bytes,
+                                     hipStream_t stream)
 {
     clear_error();
     CompParams P;
@@ -1035,13 +1121,19 @@ gm_status gm_composite_hybrid_bwd_aa(const gm_camera* cam, int32_t N, const floa
                  "state and g_layer must be 16-byte aligned");
     GM_ARG_CHECK(N == 0 || g_rec, "g_rec is NULL");
     const int64_t T = (int64_t)P.cam.tx * P.cam.ty;
+    int32_t *walk, *order;
+    if (gm_status s = tile_order_ws(cam, ws, ws_bytes, &walk, &order)) return s;
     if (N > 0) {
         const int64_t n = (int64_t)N * GM_GRAD;
         k_zero_f32<<<(unsigned)div_up(n, 256), 256, 0, stream>>>(g_rec, n);
         GM_LAUNCH_CHECK();
     }
+    k_tile_walk<true><<<(unsigned)T, CT, 0, stream>>>(P, nullptr, state, walk);
+    GM_LAUNCH_CHECK();
+    k_tile_order<<<1, 1024, 0, stream>>>((int)T, walk, order);
+    GM_LAUNCH_CHECK();
     k_composite_bwd<true><<<(unsigned)T, CT, 0, stream>>>(P, nullptr, nullptr, nullptr, layer, state, g_rgb, g_depth,
-                                                         g_alpha, g_rec, nullptr, nullptr, g_layer);
+                                                         g_alpha, g_rec, nullptr, nullptr, g_layer, order);
     GM_LAUNCH_CHECK();
     return GM_OK;
 }

@@ -137,6 +137,8 @@ class Renderer:
         self.g_rec = torch.empty((max(self.N, 1), G.GM_GRAD), dtype=f32, device=dev)
         self.g_mesh_rgb = torch.empty((self.H, self.W, 3), dtype=f32, device=dev)
         self.g_mesh_depth = torch.empty((self.H, self.W), dtype=f32, device=dev)
+        self.ws_comp_bwd = torch.empty(G.gm_composite_hybrid_bwd_ws(s.width, s.height), dtype=torch.uint8,
+                                       device=dev)
         self.n_pairs = 0
         self.n_keys = 0
         # device list lengths (n_pairs, n_keys), one row per view of a batched pass
@@ -256,7 +258,7 @@ class Renderer:
         G.gm_composite_hybrid_bwd(ds.cams[view], self.N, self.rec, self.tile_ranges, self.sorted_ids,
                                   self.face_id, self.depth, s.softness, self.state_T, self.state_last,
                                   self.state_cm, g_rgb, g_depth, g_alpha, self.g_rec, self.g_mesh_rgb,
-                                  self.g_mesh_depth, _stream())
+                                  self.g_mesh_depth, self.ws_comp_bwd, _stream())
 
     def project_bwd(self, view: int, g_rec=None, log_params: bool = False):
         """Gradients of the Gaussian parameters from record gradients (default: the
@@ -347,7 +349,7 @@ class Renderer:
         ds, s = self.ds, self.ds.scene
         G.gm_composite_hybrid_bwd_aa(ds.cams[view], self.N, self.rec, self.tile_ranges, self.sorted_ids, self.layer,
                                      s.bg, s.softness, self.state_aa, g_rgb, g_depth, g_alpha, self.g_rec,
-                                     self.g_layer, _stream())
+                                     self.g_layer, self.ws_comp_bwd, _stream())
 
     def antialias_bwd(self, view: int, g_layer=None):
         """dL/dc and dL/dD at covered pixels (into g_mesh_rgb / g_mesh_depth) and

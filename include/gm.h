@@ -264,14 +264,19 @@ gm_status gm_composite_hybrid_fwd(const gm_camera* cam, const float* rec,
  * Skipped and stopped entries get no gradient; the clamp at 0.99 has zero
  * derivative; the decisions are not differentiated.  The transmittance before each
  * entry is recovered from the final one by division (1 - alpha_F >= 0.01).
+ * ws: at least gm_composite_hybrid_bwd_ws(W, H) bytes of device scratch (every tile's
+ * walk length from the forward state and the order in which the tiles are taken,
+ * longest first); its contents are not kept between calls.  The outputs do not
+ * depend on that order beyond the summation order of the float atomics.
  * ------------------------------------------------------------------------- */
+size_t gm_composite_hybrid_bwd_ws(int32_t width, int32_t height);
 gm_status gm_composite_hybrid_bwd(const gm_camera* cam, int32_t N, const float* rec,
                                   const int32_t* tile_ranges, const int32_t* sorted_ids,
                                   const int32_t* face_id, const float* depth, float softness,
                                   const float* state_T, const int32_t* state_last,
                                   const float* state_cm, const float* g_rgb, const float* g_depth,
                                   const float* g_alpha, float* g_rec, float* g_mesh_rgb,
-                                  float* g_mesh_depth, hipStream_t stream);
+                                  float* g_mesh_depth, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * 7. gm_project_gaussians_bwd — gradients of the Gaussians' own parameters.
@@ -389,7 +394,8 @@ gm_status gm_mesh_bwd(const gm_camera* cam, const gm_mesh* mesh, const gm_light*
  * depth = Z_F + T_F (M_D + (1 - a_m) Z_B).  state [H][W][8] = (T_F, last_F as
  * int32, T_B, last_B as int32, C_B rgb, Z_B).  The reverse mode writes g_rec as
  * call 6 (zero-filled first) and g_layer [H][W][8] = dL/d(M_rgb, M_D, a_m,
- * D_split), 0, 0.
+ * D_split), 0, 0; its ws is call 6's (gm_composite_hybrid_bwd_ws bytes), the walk
+ * length of a pixel being the longer of its two layers'.
  *
  * gm_antialias_bwd: reverse mode of gm_antialias, from its pairs record (the
  * crossings are recomputed from the recorded silhouette edges).  From g_layer it writes
@@ -415,7 +421,7 @@ gm_status gm_composite_hybrid_bwd_aa(const gm_camera* cam, int32_t N, const floa
                                      const int32_t* tile_ranges, const int32_t* sorted_ids, const float* layer,
                                      const float* bg, float softness, const float* state, const float* g_rgb,
                                      const float* g_depth, const float* g_alpha, float* g_rec, float* g_layer,
-                                     hipStream_t stream);
+                                     void* ws, size_t ws_bytes, hipStream_t stream);
 size_t gm_antialias_bwd_ws(int32_t width, int32_t height);
 gm_status gm_antialias_bwd(const gm_camera* cam, const gm_mesh* mesh, const float* vscreen, const float* pairs,
                            const int32_t* face_id, const float* depth, const float* colour,

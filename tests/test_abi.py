@@ -130,8 +130,17 @@ def test_antialias_argument_errors(G):
     assert L.gm_composite_hybrid_fwd_aa(C.byref(cam), 16, 16, 16, 16, 16, C.c_float(1.0), 16, 16, 16, 17,
                                         None) == G.GM_ERR_ARG
     assert L.gm_composite_hybrid_bwd_aa(C.byref(cam), 1, 16, 16, 16, 16, 16, C.c_float(-1.0), 16, 16, None, None, 16,
-                                        16, None) == G.GM_ERR_ARG
+                                        16, 16, 1 << 20, None) == G.GM_ERR_ARG
     assert b"softness" in L.gm_last_error()
+    # composite reverse modes: workspace missing or too small
+    need = G.gm_composite_hybrid_bwd_ws(64, 64)
+    assert need >= 2 * 16 * 4
+    assert L.gm_composite_hybrid_bwd_aa(C.byref(cam), 1, 16, 16, 16, 16, 16, C.c_float(1.0), 16, 16, None, None, 16,
+                                        16, 16, need - 1, None) == G.GM_ERR_ARG
+    assert b"workspace" in L.gm_last_error()
+    assert L.gm_composite_hybrid_bwd(C.byref(cam), 1, 16, 16, 16, 16, 16, C.c_float(1.0), 16, 16, 16, 16, None,
+                                     None, 16, None, None, None, need, None) == G.GM_ERR_ARG
+    assert b"workspace" in L.gm_last_error()
     # antialiasing reverse mode: workspace too small, NULL screen-vertex gradient
     ws = G.gm_antialias_bwd_ws(64, 64)
     assert ws == 64 * 64 * 32
