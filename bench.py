@@ -1,12 +1,15 @@
 """Benchmark: hybrid render fwd+bwd throughput at 1080p on one MI355X.
 
 One step = the whole hot path over one view of the workload, inputs resident in
-HBM: gm_bin_triangles -> gm_raster_zbuffer -> gm_project_gaussians ->
-gm_sort_tile_keys -> gm_composite_hybrid_fwd -> gm_composite_hybrid_bwd.
+HBM: gm_bin_triangles -> gm_raster_zbuffer, beside them on a second stream
+gm_project_gaussians -> gm_sort_depth, then gm_sort_tiles -> gm_composite_hybrid_fwd
+-> gm_composite_hybrid_bwd.
 
-Prints one JSON line with the metric, per-stage times (HIP events on the library's
-stream, recorded inside the timed region), a roofline entry for the dominant
-kernel and the CPU oracle's throughput on a bounded sample of the same workload.
+Prints one JSON line with the metric, per-stage times (HIP events on the two
+streams, recorded inside the timed region), a roofline entry for the dominant
+kernel, the measured HBM traffic of a whole step when its counter summary matches
+the kernel sources, and the CPU oracle's throughput on a bounded sample of the same
+workload.
 
 ``--copy-calibration`` instead runs a plain device copy of known size; profiled
 with ``rocprofv3 --pmc FETCH_SIZE`` / ``WRITE_SIZE`` it gives the factors that turn

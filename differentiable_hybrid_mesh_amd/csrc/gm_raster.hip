@@ -167,8 +167,9 @@ constexpr int ZB_CHUNK = 1024;  // candidates per round (bounds the covered list
 constexpr int ZB_PER_THREAD = ZB_CHUNK / ZB_THREADS;
 constexpr unsigned long long ZB_INF = 0x7FF0000000000000ull;  // +inf as fp64 bits
 
-// One block per tile.  Each staged triangle contributes the pixels of its box
-// (widened by a pixel, clipped to the tile and the image) as candidates; the
+// One block per tile.  Each staged triangle contributes as candidates the tile's
+// pixel centres within ZB_MARGIN of its bounding box (the whole tile for a triangle
+// too thin for that margin to be exact; see the staging code); the
 // candidates of a batch form one flat sequence, walked in rounds of ZB_CHUNK with
 // four consecutive candidates per thread, so lanes stay busy whatever the triangle
 // size.  A round runs in three phases: the fp64 edge test appends covered

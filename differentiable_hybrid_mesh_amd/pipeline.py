@@ -5,11 +5,14 @@ per-view device buffers (torch tensors used as plain device memory), reads the t
 list lengths back once per forward pass (the calls themselves never synchronise),
 grows a list that overflowed and runs the pass again, and runs
 
-    gm_bin_triangles -> gm_raster_zbuffer -> gm_project_gaussians ->
-    gm_sort_tile_keys -> gm_composite_hybrid_fwd   (forward)
+    gm_bin_triangles -> gm_raster_zbuffer ----------.
+    gm_project_gaussians -> gm_sort_depth ----------+-> gm_sort_tiles ->
+    gm_composite_hybrid_fwd                          (forward)
     gm_composite_hybrid_bwd                          (backward)
 
-on the current torch stream.  Every step of the path runs in libgm's kernels.
+on the current torch stream, except the projection and the depth sort, which run
+on a second stream beside the binning and z-buffer (``Renderer.lists``; the batched
+multi-view pass keeps one stream).  Every step of the path runs in libgm's kernels.
 """
 from __future__ import annotations
 
