@@ -11,8 +11,9 @@ grows a list that overflowed and runs the pass again, and runs
     gm_composite_hybrid_bwd                          (backward)
 
 on the current torch stream, except the projection and the depth sort, which run
-on a second stream beside the binning and z-buffer (``Renderer.lists``; the batched
-multi-view pass keeps one stream).  Every step of the path runs in libgm's kernels.
+on a second stream beside the binning and z-buffer (``Renderer.lists``; in the
+batched multi-view pass the depth sort of each view does).  Every step of the path
+runs in libgm's kernels.
 """
 from __future__ import annotations
 
@@ -199,25 +200,29 @@ class Renderer:
             self._ev_side = torch.cuda.Event()
         return self._side
 
-    def lists(self, view: int, cull: bool = True, antialias: bool = False, overlap: bool = True):
+    def lists(self, view: int, cull: bool = True, antialias: bool = False, overlap: bool = True,
+              project: bool = True):
         """Mesh visibility (bin, z-buffer, antialiased layer) and Gaussian lists
-        (projection, sort).  With overlap the projection and the depth sort run on a
-        second stream beside the binning and z-buffer: the two branches share no
-        buffer, and only the tile lists need both (tile_dmax and the depth order).  The
-        side stream first waits for everything queued before (the previous step's
-        composite still reads the records and the lists)."""
+        (projection unless the records are already there, sort).  With overlap the
+        projection and the depth sort run on a second stream beside the binning and
+        z-buffer: the two branches share no buffer, and only the tile lists need both
+        (tile_dmax and the depth order).  The side stream first waits for everything
+        queued before (the previous step's composite still reads the records and the
+        lists)."""
         if not overlap:
             self.bin_and_zbuffer(view)
             if antialias:
                 self.antialias(view)
-            self.project(view)
+            if project:
+                self.project(view)
             self.sort(view, cull)
             return
         main, side = torch.cuda.current_stream(), self._side_stream()
         self._ev_main.record(main)
         side.wait_event(self._ev_main)
         with torch.cuda.stream(side):
-            self.project(view)
+            if project:
+                self.project(view)
             self.sort_depth(view)
             self._ev_side.record(side)
         self.bin_and_zbuffer(view)
@@ -398,8 +403,7 @@ class Renderer:
         for k, v in enumerate(views):
             self.use_view(k)
             self.view, self.cull = v, cull
-            self.bin_and_zbuffer(v)
-            self.sort(v, cull)
+            self.lists(v, cull, project=False)  # the records come from the batched projection
             self.composite_fwd(v)
             if backward:
                 self.composite_bwd(v, grads[k]["rgb"], grads[k].get("depth"), grads[k].get("alpha"))
@@ -414,8 +418,7 @@ class Renderer:
             self._rows = len(views)
             for k, v in enumerate(views):
                 self.use_view(k)
-                self.bin_and_zbuffer(v)
-                self.sort(v, cull)
+                self.lists(v, cull, project=False)
             self.fetch_counts()
             torch.cuda.current_stream().synchronize()
             if self.read_counts():
