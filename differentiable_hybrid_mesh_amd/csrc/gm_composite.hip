@@ -631,33 +631,57 @@ k_tile_walk(CompParams P, const int32_t* __restrict__ state_last, const float* _
 }
 
 // Counting sort of the tiles into TO_BUCKETS buckets of walk length, longest first
-// (one block; the order inside a bucket is unspecified).
+// (one block; the order inside a bucket is unspecified).  Counts and slots are taken
+// per wave: thousands of empty tiles share one bucket, and one counter for the block
+// serialised their LDS atomics.
 constexpr int TO_BUCKETS = 64;
+constexpr int TO_THREADS = 1024;
 
-__global__ void __launch_bounds__(1024) k_tile_order(int T, const int32_t* __restrict__ walk,
-                                                     int32_t* __restrict__ order)
+__global__ void __launch_bounds__(TO_THREADS) k_tile_order(int T, const int32_t* __restrict__ walk,
+                                                           int32_t* __restrict__ order)
 {
-    __shared__ int s_cnt[TO_BUCKETS], s_base[TO_BUCKETS], s_max;
-    if (threadIdx.x < TO_BUCKETS) s_cnt[threadIdx.x] = 0;
+    constexpr int NW = TO_THREADS / 64;
+    __shared__ int s_cnt[NW][TO_BUCKETS];  // per-wave counts, then per-wave next slots
+    __shared__ int s_max;
+    const int wave = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < NW * TO_BUCKETS; i += TO_THREADS) (&s_cnt[0][0])[i] = 0;
     if (threadIdx.x == 0) s_max = 0;
     __syncthreads();
     int m = 0;
-    for (int t = threadIdx.x; t < T; t += blockDim.x) m = max(m, walk[t]);
-    atomicMax(&s_max, m);
+    for (int t = threadIdx.x; t < T; t += TO_THREADS) m = max(m, walk[t]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o, 64));
+    if ((threadIdx.x & 63) == 0) atomicMax(&s_max, m);
     __syncthreads();
-    const long long den = (long long)s_max + 1;  // bucket = floor(walk * buckets / den) < buckets
-    auto bucket = [&](int t) { return TO_BUCKETS - 1 - (int)((long long)walk[t] * TO_BUCKETS / den); };
-    for (int t = threadIdx.x; t < T; t += blockDim.x) atomicAdd(&s_cnt[bucket(t)], 1);
+    const float scale = (float)TO_BUCKETS / ((float)s_max + 1.0f);
+    auto bucket = [&](int t) {
+        return TO_BUCKETS - 1 - min(TO_BUCKETS - 1, (int)((float)walk[t] * scale));
+    };
+    for (int t = threadIdx.x; t < T; t += TO_THREADS) atomicAdd(&s_cnt[wave][bucket(t)], 1);
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int run = 0;
-        for (int b = 0; b < TO_BUCKETS; ++b) {
-            s_base[b] = run;
-            run += s_cnt[b];
+    if (threadIdx.x < TO_BUCKETS) {  // bucket-major exclusive offsets, waves in order
+        const int b = threadIdx.x;
+        int c[NW], tot = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            c[w] = s_cnt[w][b];
+            tot += c[w];
+        }
+        int x = tot;  // inclusive scan of the bucket totals over the 64 lanes of wave 0
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(x, d, 64);
+            if ((int)threadIdx.x >= d) x += y;
+        }
+        int run = x - tot;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            s_cnt[w][b] = run;
+            run += c[w];
         }
     }
     __syncthreads();
-    for (int t = threadIdx.x; t < T; t += blockDim.x) order[atomicAdd(&s_base[bucket(t)], 1)] = t;
+    for (int t = threadIdx.x; t < T; t += TO_THREADS) order[atomicAdd(&s_cnt[wave][bucket(t)], 1)] = t;
 }
 
 template <bool AA>
@@ -1098,7 +1122,7 @@ gm_status gm_composite_hybrid_bwd(const gm_camera* cam, int32_t N, const float* 
     }
     k_tile_walk<false><<<(unsigned)T, CT, 0, stream>>>(P, state_last, nullptr, walk);
     GM_LAUNCH_CHECK();
-    k_tile_order<<<1, 1024, 0, stream>>>((int)T, walk, order);
+    k_tile_order<<<1, TO_THREADS, 0, stream>>>((int)T, walk, order);
     GM_LAUNCH_CHECK();
     k_composite_bwd<false><<<(unsigned)T, CT, 0, stream>>>(P, state_T, state_last, state_cm, nullptr, nullptr,
                                                           g_rgb, g_depth, g_alpha, g_rec, g_mesh_rgb, g_mesh_depth,
@@ -1131,7 +1155,7 @@ gm_status gm_composite_hybrid_bwd_aa(const gm_camera* cam, int32_t N, const floa
     }
     k_tile_walk<true><<<(unsigned)T, CT, 0, stream>>>(P, nullptr, state, walk);
     GM_LAUNCH_CHECK();
-    k_tile_order<<<1, 1024, 0, stream>>>((int)T, walk, order);
+    k_tile_order<<<1, TO_THREADS, 0, stream>>>((int)T, walk, order);
     GM_LAUNCH_CHECK();
     k_composite_bwd<true><<<(unsigned)T, CT, 0, stream>>>(P, nullptr, nullptr, nullptr, layer, state, g_rgb, g_depth,
                                                          g_alpha, g_rec, nullptr, nullptr, g_layer, order);
