@@ -217,16 +217,13 @@ def test_thin_triangles_zbuffer():
     assert np.isin(np.arange(6)[full[:6]], covered).any()  # some fully tested sliver is visible
 
 
-def test_lists_above_65536_tiles():
-    """A 4112 x 4096 image has 257 x 256 = 65792 tiles: the tile sort keeps 32-bit
-    keys (16-bit at most 65536 tiles) and the count pass reads tile_dmax from memory
-    (staged in LDS up to 10240 tiles).  Lists on sampled tiles, ids above 65535
-    among them, are the oracle's; culling is on, with triangles covering whole tiles."""
+def _lists_large_image(W, H, seed, name):
+    """Lists of a large image on sampled tiles against the oracle's, culling on, with
+    triangles covering whole tiles; returns (tiles, ranges, tile_dmax sample)."""
     import torch
     from differentiable_hybrid_mesh_amd.pipeline import DeviceScene, Renderer
-    W, H = 4112, 4096
-    rng = np.random.default_rng(41)
-    s = tiny.empty_scene(W, H, 2000.0, 2000.0, W / 2, H / 2, name="65792 tiles")
+    rng = np.random.default_rng(seed)
+    s = tiny.empty_scene(W, H, 2000.0, 2000.0, W / 2, H / 2, name=name)
     n = 3000
     u = np.concatenate([rng.uniform(0, W, n - 300), rng.uniform(0, W, 300)])
     v = np.concatenate([rng.uniform(0, H, n - 300), rng.uniform(H - 20, H, 300)])  # the last tile row too
@@ -249,15 +246,15 @@ def test_lists_above_65536_tiles():
     r.fit_lists(0, cull=True)
     torch.cuda.synchronize()
     T = r.T
-    assert T == 65792
+    txn = (W + 15) // 16
+    assert T == txn * ((H + 15) // 16)
     ranges = P.to_np(r.tile_ranges).reshape(-1, 2)
     ids = P.to_np(r.sorted_ids)
     tx = (u // 16).astype(int)
     ty = (v // 16).astype(int)
-    near = np.unique(np.clip(ty, 0, 255) * 257 + np.clip(tx, 0, 256))
+    near = np.unique(np.clip(ty, 0, (H + 15) // 16 - 1) * txn + np.clip(tx, 0, txn - 1))
     tiles = np.unique(np.concatenate([rng.choice(near, 250, replace=False), rng.integers(0, T, 50),
-                                      near[near >= 65536][:40]])).astype(np.int32)
-    assert (tiles >= 65536).sum() >= 20
+                                      near[near >= 65536][:40], near[-40:]])).astype(np.int32)
     cam = oracle.camera(s, 0)
     vs = oracle.project_vertices(cam, s.verts)
     zb = oracle.zbuffer(cam, vs, s.faces, s.face_mask, tiles=tiles, prefilter=True)
@@ -267,11 +264,31 @@ def test_lists_above_65536_tiles():
     order = oracle.depth_order(pg["rec"], pg["valid"])
     pre = oracle.tile_lists(cam, pg["rec"], pg["rect"], order, tiles, tile_dmax=dm, softness=s.softness)
     rep = P.compare_lists(s, {"ranges": ranges, "ids": ids}, {"lists_pre": pre}, tiles, True)
-    print("65792 tiles", rep, flush=True)
+    print(name, rep, flush=True)
     assert rep["list_mismatch"] == 0 and rep["entries"] > 300
-    hi = tiles[tiles >= 65536]
-    assert (ranges[hi, 1] > ranges[hi, 0]).sum() >= 10  # lists of tiles past 16-bit ids
     assert int((dm[tiles] < np.inf).sum()) >= 5  # some sampled tiles are fully covered
+    return tiles, ranges
+
+
+def test_lists_above_65536_tiles():
+    """A 4112 x 4096 image has 257 x 256 = 65792 tiles: the tile sort keeps 32-bit
+    keys (16-bit at most 65536 tiles) and the count pass reads tile_dmax from memory
+    (staged in LDS up to 10240 tiles).  Lists on sampled tiles, ids above 65535
+    among them, are the oracle's."""
+    tiles, ranges = _lists_large_image(4112, 4096, 41, "65792 tiles")
+    hi = tiles[tiles >= 65536]
+    assert len(hi) >= 20
+    assert (ranges[hi, 1] > ranges[hi, 0]).sum() >= 10  # lists of tiles past 16-bit ids
+
+
+def test_lists_above_10240_tiles():
+    """A 2064 x 1296 image has 129 x 81 = 10449 tiles: 16-bit tile keys over 14 bits
+    (two 7-bit passes), and more tiles than the count pass stages in LDS, so it reads
+    tile_dmax from memory.  Lists on sampled tiles, the last ones among them, are the
+    oracle's."""
+    tiles, ranges = _lists_large_image(2064, 1296, 43, "10449 tiles")
+    assert tiles.max() >= 10449 - 200
+    assert (ranges[tiles[tiles >= 10240], 1] > 0).sum() >= 1
 
 
 def test_no_mesh_plain_splatting():
