@@ -2,8 +2,9 @@
 
 One step = the whole hot path over one view of the workload, inputs resident in
 HBM: gm_bin_triangles -> gm_raster_zbuffer, beside them on a second stream
-gm_project_gaussians -> gm_sort_depth, then gm_sort_tiles -> gm_composite_hybrid_fwd
--> gm_composite_hybrid_bwd.
+gm_project_gaussians -> gm_sort_depth (then gm_shade_surface once the z-buffer is
+done), then gm_sort_tiles -> gm_composite_hybrid_fwd_shaded ->
+gm_composite_hybrid_bwd.
 
 Prints one JSON line with the metric, per-stage times (HIP events on the two
 streams, recorded inside the timed region), a roofline entry for the dominant
@@ -32,10 +33,13 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector (counts packed FMA)
 # Stages of one step on the library's (main) stream, and on the second stream that
 # runs the projection and the depth half of the sort beside the mesh's binning and
-# z-buffer; "wait_lists" is the time the main stream waits for the second one.
+# z-buffer, then the mesh shading beside the tile sort; "wait_lists" is the time the
+# main stream waits for the second one, "wait_zbuffer" the second one's wait for the
+# z-buffer.
 STAGES = ["bin", "zbuffer", "wait_lists", "sort", "fwd", "bwd"]
 STAGES_AA = ["bin", "zbuffer", "antialias", "wait_lists", "sort", "fwd", "bwd", "antialias_bwd"]
-SIDE_STAGES = ["project", "sort_depth"]
+SIDE_STAGES = ["project", "sort_depth", "wait_zbuffer", "shade"]  # shade: the composite's first half
+SIDE_STAGES_AA = ["project", "sort_depth"]  # the layer call shades the mesh on the main stream
 
 WORKLOADS = {
     "c3": "1920x1080, 200k-face displaced sphere (vertex colour + Phong), 1M Gaussians SH3",
@@ -156,6 +160,7 @@ def main():
 
     aa = args.antialias and scene.F > 0
     stages = STAGES_AA if aa else STAGES
+    side_stages = SIDE_STAGES_AA if aa else SIDE_STAGES
 
     def step(ev=None, ev_side=None):
         # the calls of Renderer.lists() with the overlap, spelled out to mark stages
@@ -191,6 +196,15 @@ def main():
         if aa:
             r.antialias(view)
             mark()
+        else:
+            r._ev_zb.record(main)
+            side.wait_event(r._ev_zb)
+            with torch.cuda.stream(side):
+                mark_side()
+                r.shade(view)
+                mark_side()
+                r._ev_shade.record(side)
+            r._shaded = view
         main.wait_event(r._ev_side)
         mark()
         r.sort_tiles(view, True)
@@ -221,7 +235,7 @@ def main():
 
     # timed region: K whole steps; stage events on the library's (current) stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
-    evs_side = [[torch.cuda.Event(enable_timing=True) for _ in range(len(SIDE_STAGES) + 1)]
+    evs_side = [[torch.cuda.Event(enable_timing=True) for _ in range(len(side_stages) + 1)]
                 for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -238,7 +252,7 @@ def main():
     ms = t0.elapsed_time(t1) / args.steps
     stage_ms = {s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, s in enumerate(stages)}
     stage_ms.update({s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs_side]))
-                     for i, s in enumerate(SIDE_STAGES)})
+                     for i, s in enumerate(side_stages)})
 
     px = scene.width * scene.height
     value = px / (ms * 1e-3) / 1e6
@@ -261,9 +275,13 @@ def main():
         "project": N * (12 + 16 + 12 + 4 + shb + 64),
         "sort_depth": 64 * N,
         "sort": 28 * K + 8 * T,
-        "fwd": 4 * K + 64 * nvis + 8 * HW + 12 * HW + 20 * HW + 20 * HW,
+        # the composite forward: ids, records, face id + depth, colour behind (state_cm),
+        # rgb + depth + alpha, state_T + state_last
+        "fwd": 4 * K + 64 * nvis + 8 * HW + 12 * HW + 20 * HW + 8 * HW,
         "bwd": 4 * K + 64 * nvis + 8 * HW + 8 * HW + 12 * HW + 20 * HW + 52 * nvis + 16 * HW,
     }
+    if not aa:  # face ids read, state_cm written, screen vertices, colours and faces once
+        alg_bytes["shade"] = 4 * HW + 12 * HW + 24 * V + 12 * F
     if aa:
         # the layer: face ids, depths and colours of each pixel and its neighbours
         # (one read each), screen vertices and faces once, the layer written (32 B)
@@ -278,8 +296,8 @@ def main():
         "bwd": walked * FLOPS_EVAL + walked * incl_frac * FLOPS_GRAD,
     }
     # dominant single kernel: bin and sort are chains of many small kernels, the other
-    # stages are one main kernel each (the composite stages add a zero-fill or a
-    # shading prepass of a few percent)
+    # stages are one main kernel each (the backward adds the tile walk, which also
+    # clears the record gradients, and the tile order: a few percent)
     dom = max(["zbuffer", "project", "fwd", "bwd"], key=stage_ms.get)
     kname = {"bwd": "k_composite_bwd", "fwd": "k_composite_fwd", "sort": "gm_sort_tiles",
              "project": "k_project_gaussians", "zbuffer": "k_zbuffer", "bin": "gm_bin_triangles"}[dom]

@@ -6,12 +6,13 @@ device buffers with torch and calls the entry points in order.
 """
 from . import _lib
 from ._lib import (GM_GRAD, GM_REC, GM_TILE, GmCamera, GmError, GmLight, GmMesh, gm_bin_triangles,
-                   gm_build_mipmaps, gm_composite_hybrid_bwd, gm_composite_hybrid_fwd, gm_project_gaussians,
-                   gm_mesh_bwd, gm_project_gaussians_bwd, gm_project_gaussians_multi, gm_raster_zbuffer,
-                   gm_sort_depth, gm_sort_tile_keys, gm_sort_tiles, gm_version)
+                   gm_build_mipmaps, gm_composite_hybrid_bwd, gm_composite_hybrid_fwd,
+                   gm_composite_hybrid_fwd_shaded, gm_project_gaussians, gm_mesh_bwd, gm_project_gaussians_bwd,
+                   gm_project_gaussians_multi, gm_raster_zbuffer, gm_shade_surface, gm_sort_depth,
+                   gm_sort_tile_keys, gm_sort_tiles, gm_version)
 
 __all__ = ["_lib", "GM_GRAD", "GM_REC", "GM_TILE", "GmCamera", "GmError", "GmLight", "GmMesh",
            "gm_bin_triangles", "gm_build_mipmaps", "gm_composite_hybrid_bwd", "gm_composite_hybrid_fwd",
-           "gm_mesh_bwd", "gm_project_gaussians", "gm_project_gaussians_bwd", "gm_project_gaussians_multi",
-           "gm_raster_zbuffer",
+           "gm_composite_hybrid_fwd_shaded", "gm_mesh_bwd", "gm_project_gaussians", "gm_project_gaussians_bwd",
+           "gm_project_gaussians_multi", "gm_raster_zbuffer", "gm_shade_surface",
            "gm_sort_depth", "gm_sort_tile_keys", "gm_sort_tiles", "gm_version"]

@@ -49,7 +49,7 @@ EXPORTS = ["gm_bin_triangles_ws", "gm_bin_triangles", "gm_raster_zbuffer", "gm_p
            "gm_composite_hybrid_bwd", "gm_composite_hybrid_bwd_ws", "gm_project_gaussians_bwd", "gm_mesh_bwd", "gm_mipmaps_floats",
            "gm_build_mipmaps", "gm_last_error", "gm_version", "gm_edge_adjacency_ws", "gm_edge_adjacency",
            "gm_antialias", "gm_composite_hybrid_fwd_aa", "gm_composite_hybrid_bwd_aa", "gm_antialias_bwd_ws",
-           "gm_antialias_bwd", "gm_vscreen_bwd"]
+           "gm_antialias_bwd", "gm_vscreen_bwd", "gm_shade_surface", "gm_composite_hybrid_fwd_shaded"]
 
 _lib = None
 
@@ -77,6 +77,8 @@ def lib():
     L.gm_sort_depth.argtypes = [cam, I32, P, I64, P, SZ, P]
     L.gm_sort_tiles.argtypes = [cam, I32, P, P, F32, P, P, I64, P, P, SZ, P]
     L.gm_composite_hybrid_fwd.argtypes = [cam, P, P, P, P, P, mesh, P, light, P, F32, P, P, P, P, P, P, P]
+    L.gm_shade_surface.argtypes = [cam, P, mesh, P, light, P, P, P]
+    L.gm_composite_hybrid_fwd_shaded.argtypes = [cam, P, P, P, P, P, F32, P, P, P, P, P, P, P]
     L.gm_composite_hybrid_bwd.argtypes = [cam, I32, P, P, P, P, P, F32, P, P, P, P, P, P, P, P, P, P, SZ, P]
     L.gm_composite_hybrid_bwd_ws.argtypes = [I32, I32]
     L.gm_composite_hybrid_bwd_ws.restype = SZ
@@ -106,7 +108,8 @@ def lib():
                  "gm_sort_tile_keys", "gm_sort_depth", "gm_sort_tiles",
                  "gm_composite_hybrid_fwd", "gm_composite_hybrid_bwd", "gm_project_gaussians_bwd",
                  "gm_mesh_bwd", "gm_build_mipmaps", "gm_edge_adjacency", "gm_antialias", "gm_composite_hybrid_fwd_aa",
-                 "gm_composite_hybrid_bwd_aa", "gm_antialias_bwd", "gm_vscreen_bwd"):
+                 "gm_composite_hybrid_bwd_aa", "gm_antialias_bwd", "gm_vscreen_bwd", "gm_shade_surface",
+                 "gm_composite_hybrid_fwd_shaded"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -193,6 +196,20 @@ def gm_composite_hybrid_fwd(cam, rec, tile_ranges, sorted_ids, face_id, depth, m
                                         _light_ref(light), C.cast(bgv, C.c_void_p), float(softness),
                                         ptr(out_rgb), ptr(out_depth), ptr(out_alpha), ptr(state_T),
                                         ptr(state_last), ptr(state_cm), stream))
+
+
+def gm_shade_surface(cam, face_id, mesh, vscreen, light, bg, state_cm, stream):
+    bgv = (C.c_float * 3)(*[float(x) for x in bg])
+    check(lib().gm_shade_surface(C.byref(cam), ptr(face_id), C.byref(mesh), ptr(vscreen), _light_ref(light),
+                                 C.cast(bgv, C.c_void_p), ptr(state_cm), stream))
+
+
+def gm_composite_hybrid_fwd_shaded(cam, rec, tile_ranges, sorted_ids, face_id, depth, softness, state_cm, out_rgb,
+                                   out_depth, out_alpha, state_T, state_last, stream):
+    check(lib().gm_composite_hybrid_fwd_shaded(C.byref(cam), ptr(rec), ptr(tile_ranges), ptr(sorted_ids),
+                                               ptr(face_id), ptr(depth), float(softness), ptr(state_cm),
+                                               ptr(out_rgb), ptr(out_depth), ptr(out_alpha), ptr(state_T),
+                                               ptr(state_last), stream))
 
 
 def gm_composite_hybrid_bwd_ws(width, height) -> int:

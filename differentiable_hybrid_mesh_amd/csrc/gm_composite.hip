@@ -603,13 +603,27 @@ __device__ __forceinline__ float wave_sum16(const float* v, int lane)
 // its four waves, which run side by side, one per SIMD (ordering by their sum was
 // 1.7% slower); walks differ by an order of magnitude across an image, and blocks
 // taken in raster order leave long tiles for the end of the grid.
+//
+// The same launch clears the n record gradients the composite kernel accumulates
+// into (a grid-stride fill: the walk reads are latency-bound, the fill is
+// store-bound, and one launch overlaps the two).
 template <bool AA>
 __global__ void __launch_bounds__(CT)
 k_tile_walk(CompParams P, const int32_t* __restrict__ state_last, const float* __restrict__ state_aa,
-            int32_t* __restrict__ walk)
+            int32_t* __restrict__ walk, float* __restrict__ g_rec, int64_t n)
 {
     __shared__ int s_w[CT / 64];
     const int tile = blockIdx.x;
+    {
+        const int64_t stride = (int64_t)gridDim.x * CT, me = (int64_t)tile * CT + threadIdx.x;
+        // floats before the first 16-byte boundary, whole float4s, the rest
+        const int64_t head = min(n, (int64_t)(((16u - ((uintptr_t)g_rec & 15u)) & 15u) >> 2));
+        const int64_t n4 = (n - head) >> 2;
+        if (me < head) g_rec[me] = 0.0f;
+        float4* body = reinterpret_cast<float4*>(g_rec + head);
+        for (int64_t i = me; i < n4; i += stride) body[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        for (int64_t i = head + (n4 << 2) + me; i < n; i += stride) g_rec[i] = 0.0f;
+    }
     const int tx = tile % P.cam.tx, ty = tile / P.cam.tx;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int px = tx * GM_TILE + 8 * (wave & 1) + (lane & 7), py = ty * GM_TILE + 8 * (wave >> 1) + (lane >> 3);
@@ -934,12 +948,6 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
     if (g_mesh_depth) g_mesh_depth[pix] = TF * am * GZ + gD;
 }
 
-__global__ void k_zero_f32(float* __restrict__ p, int64_t n)
-{
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0.0f;
-}
-
 // Mesh surface and light fields of the parameters (for the colour prepass).
 static gm_status fill_surface(CompParams& P, const gm_mesh* mesh, const float* vscreen, const gm_light* light)
 {
@@ -1073,6 +1081,35 @@ gm_status gm_composite_hybrid_fwd(const gm_camera* cam, const float* rec, const 
     return GM_OK;
 }
 
+gm_status gm_shade_surface(const gm_camera* cam, const int32_t* face_id, const gm_mesh* mesh, const float* vscreen,
+                           const gm_light* light, const float* bg, float* state_cm, hipStream_t stream)
+{
+    clear_error();
+    if (gm_status s = check_camera(cam)) return s;
+    GM_ARG_CHECK(face_id && bg && state_cm, "face_id / bg / state_cm is NULL");
+    return launch_surface_colour(cam, mesh, vscreen, light, face_id, bg, state_cm, stream);
+}
+
+gm_status gm_composite_hybrid_fwd_shaded(const gm_camera* cam, const float* rec, const int32_t* tile_ranges,
+                                         const int32_t* sorted_ids, const int32_t* face_id, const float* depth,
+                                         float softness, const float* state_cm, float* out_rgb, float* out_depth,
+                                         float* out_alpha, float* state_T, int32_t* state_last, hipStream_t stream)
+{
+    clear_error();
+    CompParams P;
+    const float zero3[3] = {0.0f, 0.0f, 0.0f};  // bg enters through state_cm
+    if (gm_status s = fill_params(P, cam, rec, tile_ranges, sorted_ids, face_id, depth, nullptr, nullptr, nullptr,
+                                  zero3, softness))
+        return s;
+    GM_ARG_CHECK(state_cm, "state_cm is NULL");
+    GM_ARG_CHECK(out_rgb && out_depth && out_alpha && state_T && state_last, "an output is NULL");
+    const int64_t T = (int64_t)P.cam.tx * P.cam.ty;
+    k_composite_fwd<false><<<(unsigned)T, CT, 0, stream>>>(P, state_cm, nullptr, out_rgb, out_depth, out_alpha,
+                                                          state_T, state_last, nullptr);
+    GM_LAUNCH_CHECK();
+    return GM_OK;
+}
+
 gm_status gm_composite_hybrid_fwd_aa(const gm_camera* cam, const float* rec, const int32_t* tile_ranges,
                                      const int32_t* sorted_ids, const float* layer, const float* bg, float softness,
                                      float* out_rgb, float* out_depth, float* out_alpha, float* state,
@@ -1115,12 +1152,8 @@ gm_status gm_composite_hybrid_bwd(const gm_camera* cam, int32_t N, const float* 
     const int64_t T = (int64_t)P.cam.tx * P.cam.ty;
     int32_t *walk, *order;
     if (gm_status s = tile_order_ws(cam, ws, ws_bytes, &walk, &order)) return s;
-    if (N > 0) {
-        const int64_t n = (int64_t)N * GM_GRAD;
-        k_zero_f32<<<(unsigned)div_up(n, 256), 256, 0, stream>>>(g_rec, n);
-        GM_LAUNCH_CHECK();
-    }
-    k_tile_walk<false><<<(unsigned)T, CT, 0, stream>>>(P, state_last, nullptr, walk);
+    const int64_t n = N > 0 ? (int64_t)N * GM_GRAD : 0;
+    k_tile_walk<false><<<(unsigned)T, CT, 0, stream>>>(P, state_last, nullptr, walk, g_rec, n);
     GM_LAUNCH_CHECK();
     k_tile_order<<<1, TO_THREADS, 0, stream>>>((int)T, walk, order);
     GM_LAUNCH_CHECK();
@@ -1148,12 +1181,8 @@ gm_status gm_composite_hybrid_bwd_aa(const gm_camera* cam, int32_t N, const floa
     const int64_t T = (int64_t)P.cam.tx * P.cam.ty;
     int32_t *walk, *order;
     if (gm_status s = tile_order_ws(cam, ws, ws_bytes, &walk, &order)) return s;
-    if (N > 0) {
-        const int64_t n = (int64_t)N * GM_GRAD;
-        k_zero_f32<<<(unsigned)div_up(n, 256), 256, 0, stream>>>(g_rec, n);
-        GM_LAUNCH_CHECK();
-    }
-    k_tile_walk<true><<<(unsigned)T, CT, 0, stream>>>(P, nullptr, state, walk);
+    const int64_t n = N > 0 ? (int64_t)N * GM_GRAD : 0;
+    k_tile_walk<true><<<(unsigned)T, CT, 0, stream>>>(P, nullptr, state, walk, g_rec, n);
     GM_LAUNCH_CHECK();
     k_tile_order<<<1, TO_THREADS, 0, stream>>>((int)T, walk, order);
     GM_LAUNCH_CHECK();

@@ -153,6 +153,7 @@ class Renderer:
         self.view = 0
         self.cull = True
         self._side = None  # second stream of lists(), made on first use
+        self._shaded = None  # view whose state_cm lists() queued on the second stream
 
     def _alloc_keys(self, cap):
         s = self.ds.scene
@@ -198,7 +199,16 @@ class Renderer:
             self._side = torch.cuda.Stream(device=self.ds.device)
             self._ev_main = torch.cuda.Event()
             self._ev_side = torch.cuda.Event()
+            self._ev_zb = torch.cuda.Event()
+            self._ev_shade = torch.cuda.Event()
         return self._side
+
+    def shade(self, view: int):
+        """The colour behind the Gaussians (state_cm) from the z-buffer: the first half
+        of the composite forward."""
+        ds, s = self.ds, self.ds.scene
+        G.gm_shade_surface(ds.cams[view], self.face_id, ds.mesh, self.vscreen, ds.light, s.bg, self.state_cm,
+                           _stream())
 
     def lists(self, view: int, cull: bool = True, antialias: bool = False, overlap: bool = True,
               project: bool = True):
@@ -206,9 +216,12 @@ class Renderer:
         (projection unless the records are already there, sort).  With overlap the
         projection and the depth sort run on a second stream beside the binning and
         z-buffer: the two branches share no buffer, and only the tile lists need both
-        (tile_dmax and the depth order).  The side stream first waits for everything
-        queued before (the previous step's composite still reads the records and the
-        lists)."""
+        (tile_dmax and the depth order).  Once the z-buffer is done, the side stream
+        also shades the mesh (state_cm, needed by the composite, not by the sort) beside
+        the tile sort; composite_fwd() then waits for it.  The side stream first waits
+        for everything queued before (the previous step's composite still reads the
+        records, the lists and state_cm)."""
+        self._shaded = None
         if not overlap:
             self.bin_and_zbuffer(view)
             if antialias:
@@ -228,6 +241,13 @@ class Renderer:
         self.bin_and_zbuffer(view)
         if antialias:
             self.antialias(view)
+        else:
+            self._ev_zb.record(main)
+            side.wait_event(self._ev_zb)
+            with torch.cuda.stream(side):
+                self.shade(view)
+                self._ev_shade.record(side)
+            self._shaded = view
         main.wait_event(self._ev_side)
         self.sort_tiles(view, cull)
 
@@ -255,7 +275,17 @@ class Renderer:
         return ok
 
     def composite_fwd(self, view: int):
+        """The composite forward; when lists() has queued this view's shading on the
+        side stream, only its second half, after that shading."""
         ds, s = self.ds, self.ds.scene
+        if self._shaded == view:
+            self._shaded = None
+            torch.cuda.current_stream().wait_event(self._ev_shade)
+            G.gm_composite_hybrid_fwd_shaded(ds.cams[view], self.rec, self.tile_ranges, self.sorted_ids,
+                                             self.face_id, self.depth, s.softness, self.state_cm, self.out_rgb,
+                                             self.out_depth, self.out_alpha, self.state_T, self.state_last,
+                                             _stream())
+            return
         G.gm_composite_hybrid_fwd(ds.cams[view], self.rec, self.tile_ranges, self.sorted_ids, self.face_id,
                                   self.depth, ds.mesh, self.vscreen, ds.light, s.bg, s.softness, self.out_rgb,
                                   self.out_depth, self.out_alpha, self.state_T, self.state_last, self.state_cm,

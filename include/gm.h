@@ -250,6 +250,24 @@ gm_status gm_composite_hybrid_fwd(const gm_camera* cam, const float* rec,
                                   float* out_alpha, float* state_T, int32_t* state_last,
                                   float* state_cm, hipStream_t stream);
 
+/* The two halves of gm_composite_hybrid_fwd, which is gm_shade_surface followed by
+ * gm_composite_hybrid_fwd_shaded with the same arguments.  gm_shade_surface writes
+ * state_cm [H][W][3] (c_m where face_id >= 0, bg elsewhere); it reads the z-buffer's
+ * face_id, the mesh, vscreen and light, not the lists, so a caller may run it on
+ * another stream beside the tile sort.  gm_composite_hybrid_fwd_shaded takes that
+ * state_cm as input (ordered after gm_shade_surface; bg enters only through it) and
+ * writes the other outputs of gm_composite_hybrid_fwd, bit for bit the same.
+ * Errors as for gm_composite_hybrid_fwd. */
+gm_status gm_shade_surface(const gm_camera* cam, const int32_t* face_id, const gm_mesh* mesh,
+                           const float* vscreen, const gm_light* light, const float* bg,
+                           float* state_cm, hipStream_t stream);
+gm_status gm_composite_hybrid_fwd_shaded(const gm_camera* cam, const float* rec,
+                                         const int32_t* tile_ranges, const int32_t* sorted_ids,
+                                         const int32_t* face_id, const float* depth, float softness,
+                                         const float* state_cm, float* out_rgb, float* out_depth,
+                                         float* out_alpha, float* state_T, int32_t* state_last,
+                                         hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * 6. gm_composite_hybrid_bwd — reverse mode of call 5.
  * README "Hybrid rendering": everything is differentiable, Gaussian parameters

@@ -82,6 +82,27 @@ def test_argument_errors_before_any_launch(G):
     assert L.gm_sort_tiles(C.byref(cam), 0, None, None, C.c_float(-1.0), 16, None, 0, 16, 16,
                            1 << 20, None) == G.GM_ERR_ARG
     assert b"softness" in L.gm_last_error()
+    # the two halves of the composite forward: NULL face_id / bg / state_cm, a textured
+    # mesh without uv; NULL state_cm, negative softness, a NULL output
+    m3 = G.GmMesh()
+    bg = (C.c_float * 3)(0.0, 0.0, 0.0)
+    assert L.gm_shade_surface(C.byref(cam), None, C.byref(m3), None, None, bg, 16, None) == G.GM_ERR_ARG
+    assert L.gm_shade_surface(C.byref(cam), 16, C.byref(m3), None, None, None, 16, None) == G.GM_ERR_ARG
+    assert L.gm_shade_surface(C.byref(cam), 16, C.byref(m3), None, None, bg, None, None) == G.GM_ERR_ARG
+    assert b"state_cm" in L.gm_last_error()
+    m3.F, m3.faces, m3.mips, m3.tex_size = 1, 16, 16, 8
+    assert L.gm_shade_surface(C.byref(cam), 16, C.byref(m3), 16, None, bg, 16, None) == G.GM_ERR_ARG
+    assert b"uv" in L.gm_last_error()
+    assert L.gm_shade_surface(C.byref(_cam(G, 64, 0)), 16, C.byref(m3), 16, None, bg, 16, None) == G.GM_ERR_ARG
+    assert L.gm_composite_hybrid_fwd_shaded(C.byref(cam), 16, 16, 16, 16, 16, C.c_float(1.0), None, 16, 16, 16, 16,
+                                            16, None) == G.GM_ERR_ARG
+    assert b"state_cm" in L.gm_last_error()
+    assert L.gm_composite_hybrid_fwd_shaded(C.byref(cam), 16, 16, 16, 16, 16, C.c_float(-1.0), 16, 16, 16, 16, 16,
+                                            16, None) == G.GM_ERR_ARG
+    assert b"softness" in L.gm_last_error()
+    assert L.gm_composite_hybrid_fwd_shaded(C.byref(cam), 16, 16, 16, 16, 16, C.c_float(1.0), 16, 16, None, 16, 16,
+                                            16, None) == G.GM_ERR_ARG
+    assert b"output" in L.gm_last_error()
     # texture side not a power of two
     assert L.gm_build_mipmaps(16, 100, 16, None) == G.GM_ERR_ARG
     # rec misaligned
