@@ -52,11 +52,30 @@ k_radix_hist(const KT* __restrict__ keys, const long long* __restrict__ d_count,
 #pragma unroll
     for (int w = 0; w < RS_WAVES; ++w) h[w][threadIdx.x] = 0;
     __syncthreads();
-    const long long base = (long long)blockIdx.x * RS_CHUNK;
-#pragma unroll 4
-    for (int k = 0; k < RS_ITEMS; ++k) {
-        const long long e = base + (long long)k * RS_THREADS + threadIdx.x;
-        if (e < n) atomicAdd(&h[wave][((uint32_t)keys[e] >> shift) & (R - 1)], 1);
+    // thread t counts the RS_ITEMS consecutive keys from e0, read with 16-byte loads
+    // (keys are 256-byte aligned and e0 is a multiple of RS_ITEMS): all of a block's
+    // loads are in flight together, where one key per load left it latency-bound
+    const long long e0 = (long long)blockIdx.x * RS_CHUNK + (long long)threadIdx.x * RS_ITEMS;
+    if (e0 + RS_ITEMS <= n) {
+        static_assert(RS_ITEMS * sizeof(KT) % 16 == 0, "whole 16-byte loads per thread");
+        constexpr int NV = RS_ITEMS * (int)sizeof(KT) / 16;
+        constexpr int PER = 16 / (int)sizeof(KT);  // keys per 16-byte load
+        uint4 q[NV];
+        const uint4* src = reinterpret_cast<const uint4*>(keys + e0);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) q[v] = src[v];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const uint32_t w4[4] = {q[v].x, q[v].y, q[v].z, q[v].w};
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const uint32_t key = sizeof(KT) == 2 ? (w4[k >> 1] >> (16 * (k & 1))) & 0xffffu : w4[k];
+                atomicAdd(&h[wave][(key >> shift) & (R - 1)], 1);
+            }
+        }
+    } else {
+        for (int k = 0; k < RS_ITEMS; ++k)
+            if (e0 + k < n) atomicAdd(&h[wave][((uint32_t)keys[e0 + k] >> shift) & (R - 1)], 1);
     }
     __syncthreads();
     if (threadIdx.x < R) {
@@ -496,43 +515,44 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
     }
 }
 
-// Tile ranges from the tile-sorted keys, four keys per thread (KT: 16-bit tile ids
-// when the image has at most 65536 tiles, else 32-bit).
+// Tile ranges from the tile-sorted keys, TR_KEYS consecutive keys per thread read
+// with 16-byte loads (KT: 16-bit tile ids when the image has at most 65536 tiles,
+// else 32-bit).  Key k starts its tile's range when key k - 1 differs and ends it
+// when key k + 1 differs.
+constexpr int TR_KEYS = 16;
 template <typename KT>
 __global__ void k_tile_ranges(const KT* __restrict__ keys, const long long* __restrict__ d_count,
                               long long n_max, int32_t* __restrict__ ranges)
 {
     const long long K = live_count(d_count, n_max);
-    const long long k0 = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    const long long k0 = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * TR_KEYS;
     if (k0 >= K) return;
-    uint32_t v[6];  // keys k0 - 1 .. k0 + 4, all ones outside [0, K)
+    uint32_t v[TR_KEYS + 2];  // keys k0 - 1 .. k0 + TR_KEYS, all ones outside [0, K)
     v[0] = k0 > 0 ? keys[k0 - 1] : 0xffffffffu;
-    if (k0 + 4 <= K) {  // k0 % 4 == 0, buffer 256-B aligned: one 4-key vector load
-        if constexpr (sizeof(KT) == 4) {
-            const uint4 q = *reinterpret_cast<const uint4*>(keys + k0);
-            v[1] = q.x;
-            v[2] = q.y;
-            v[3] = q.z;
-            v[4] = q.w;
-        } else {
-            const uint2 q = *reinterpret_cast<const uint2*>(keys + k0);
-            v[1] = q.x & 0xffffu;
-            v[2] = q.x >> 16;
-            v[3] = q.y & 0xffffu;
-            v[4] = q.y >> 16;
+    if (k0 + TR_KEYS <= K) {  // k0 % TR_KEYS == 0, buffer 256-B aligned: whole vector loads
+        constexpr int NV = TR_KEYS * (int)sizeof(KT) / 16, PER = 16 / (int)sizeof(KT);
+        const uint4* src = reinterpret_cast<const uint4*>(keys + k0);
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            const uint4 w = src[q];
+            const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int k = 0; k < PER; ++k)
+                v[1 + q * PER + k] = sizeof(KT) == 2 ? (w4[k >> 1] >> (16 * (k & 1))) & 0xffffu : w4[k];
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[1 + i] = k0 + i < K ? keys[k0 + i] : 0xffffffffu;
+        for (int i = 0; i < TR_KEYS; ++i) v[1 + i] = k0 + i < K ? keys[k0 + i] : 0xffffffffu;
     }
-    v[5] = k0 + 4 < K ? keys[k0 + 4] : 0xffffffffu;
+    v[TR_KEYS + 1] = k0 + TR_KEYS < K ? keys[k0 + TR_KEYS] : 0xffffffffu;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TR_KEYS; ++i) {
         const long long k = k0 + i;
-        if (k >= K) break;
         const uint32_t t = v[1 + i];
-        if (v[i] != t) ranges[2 * t] = (int32_t)k;
-        if (v[2 + i] != t) ranges[2 * t + 1] = (int32_t)(k + 1);
+        if (k < K) {
+            if (v[i] != t) ranges[2 * t] = (int32_t)k;
+            if (v[2 + i] != t) ranges[2 * t + 1] = (int32_t)(k + 1);
+        }
     }
 }
 
@@ -624,7 +644,8 @@ static gm_status emit_and_sort(const DevCamera& dc, const CullParams& cp, const 
     GM_LAUNCH_CHECK();
     if (gm_status s = radix_sort<KT>(ka, va, kb, vb, tbits, total, kcap, w.aux, stream)) return s;
     const KT* kfin = (npass % 2 == 0) ? ka : kb;
-    k_tile_ranges<KT><<<(unsigned)div_up(div_up(kcap, 4), 256), 256, 0, stream>>>(kfin, total, kcap, tile_ranges);
+    k_tile_ranges<KT><<<(unsigned)div_up(div_up(kcap, TR_KEYS), 256), 256, 0, stream>>>(kfin, total, kcap,
+                                                                                        tile_ranges);
     GM_LAUNCH_CHECK();
     return GM_OK;
 }
