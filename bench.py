@@ -371,8 +371,11 @@ def main():
 
 def main_batch(args, scene):
     """Every view of the workload per step: one gm_project_gaussians_multi for all
-    views, then per view the lists, composite forward and backward.  Also times the
-    batched projection against the per-view projection loop it replaces."""
+    views, then per view the lists, composite forward and backward, with each view's
+    mesh half and depth sort overlapped with the previous view's tile sort and
+    composite (Renderer.views_step_pipelined).  Also times the views one after
+    another, and the batched projection against the per-view projection loop it
+    replaces."""
     import torch
     from differentiable_hybrid_mesh_amd.pipeline import DeviceScene, Renderer
     ds = DeviceScene(scene)
@@ -381,7 +384,7 @@ def main_batch(args, scene):
     grads = [ds.grads(v) for v in views]
     r.fit_lists_views(views)
     for _ in range(max(args.warmup, 1)):
-        r.views_step_async(views, grads)
+        r.views_step_pipelined(views, grads)
     torch.cuda.synchronize()
     if not r.read_counts():
         raise RuntimeError("a list outgrew its capacity after fitting")
@@ -390,13 +393,23 @@ def main_batch(args, scene):
     wall0 = time.perf_counter()
     t0.record()
     for _ in range(args.steps):
-        r.views_step_async(views, grads)
+        r.views_step_pipelined(views, grads)
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     if not r.read_counts():
         raise RuntimeError("a list outgrew its capacity inside the timed region")
     ms = t0.elapsed_time(t1) / args.steps
+    # the same views one after another (each view's halves overlapped only with each
+    # other), for comparison
+    t0.record()
+    for _ in range(args.steps):
+        r.views_step_async(views, grads)
+    t1.record()
+    torch.cuda.synchronize()
+    if not r.read_counts():
+        raise RuntimeError("a list outgrew its capacity inside the timed region")
+    ms_serial = t0.elapsed_time(t1) / args.steps
     px = len(views) * scene.width * scene.height
     value = px / (ms * 1e-3) / 1e6
 
@@ -425,11 +438,12 @@ def main_batch(args, scene):
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded PCG64 scene generators)",
         "config": {"workload": f"{args.config}: {WORKLOADS[args.config]}; all {len(views)} views per step, "
-                               "one batched projection", "views": len(views), "width": scene.width,
+                               "one batched projection, views pipelined", "views": len(views), "width": scene.width,
                    "height": scene.height, "faces": scene.F, "gaussians": N, "parallelism": "single GPU"},
         "roofline": {"kernel": "k_project_gaussians_multi", "bound": "hbm", "achieved": round(ach, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
                      "units": {"algorithmic_bytes": b_multi}, "launch_ms": round(ms_multi, 4)},
+        "views_one_after_another_ms_per_step": round(ms_serial, 4),
         "projection": {"batched_ms": round(ms_multi, 4), "per_view_loop_ms": round(ms_loop, 4),
                        "batched_algorithmic_bytes": b_multi, "loop_algorithmic_bytes": b_loop,
                        "speedup": round(ms_loop / ms_multi, 3)},

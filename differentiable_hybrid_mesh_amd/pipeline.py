@@ -5,15 +5,18 @@ per-view device buffers (torch tensors used as plain device memory), reads the t
 list lengths back once per forward pass (the calls themselves never synchronise),
 grows a list that overflowed and runs the pass again, and runs
 
-    gm_bin_triangles -> gm_raster_zbuffer ----------.
-    gm_project_gaussians -> gm_sort_depth ----------+-> gm_sort_tiles ->
-    gm_composite_hybrid_fwd                          (forward)
+    gm_bin_triangles -> gm_raster_zbuffer ----------.----------> gm_shade_surface --.
+    gm_project_gaussians -> gm_sort_depth ----------+-> gm_sort_tiles ---------------+->
+    gm_composite_hybrid_fwd_shaded                   (forward)
     gm_composite_hybrid_bwd                          (backward)
 
 on the current torch stream, except the projection and the depth sort, which run
-on a second stream beside the binning and z-buffer (``Renderer.lists``; in the
-batched multi-view pass the depth sort of each view does).  Every step of the path
-runs in libgm's kernels.
+on a second stream beside the binning and z-buffer, followed there by the mesh
+shading (the composite forward's first half) beside the tile sort
+(``Renderer.lists``).  In the pipelined multi-view pass
+(``Renderer.views_step_pipelined``) each view's mesh half and depth sort run on two
+producer streams beside the previous view's tile sort and composite.  Every step
+of the path runs in libgm's kernels.
 """
 from __future__ import annotations
 
@@ -154,6 +157,8 @@ class Renderer:
         self.cull = True
         self._side = None  # second stream of lists(), made on first use
         self._shaded = None  # view whose state_cm lists() queued on the second stream
+        self._slots = None  # two buffer sets of views_step_pipelined(), made on first use
+        self._mesh_stream = None
 
     def _alloc_keys(self, cap):
         s = self.ds.scene
@@ -272,6 +277,8 @@ class Renderer:
         if n_keys > self.key_cap:
             self._alloc_keys(int(n_keys * 1.25) + 1024)
             ok = False
+        if not ok:
+            self._slots = None  # rebuilt at the new capacities
         return ok
 
     def composite_fwd(self, view: int):
@@ -281,15 +288,20 @@ class Renderer:
         if self._shaded == view:
             self._shaded = None
             torch.cuda.current_stream().wait_event(self._ev_shade)
-            G.gm_composite_hybrid_fwd_shaded(ds.cams[view], self.rec, self.tile_ranges, self.sorted_ids,
-                                             self.face_id, self.depth, s.softness, self.state_cm, self.out_rgb,
-                                             self.out_depth, self.out_alpha, self.state_T, self.state_last,
-                                             _stream())
+            self.composite_fwd_shaded(view)
             return
         G.gm_composite_hybrid_fwd(ds.cams[view], self.rec, self.tile_ranges, self.sorted_ids, self.face_id,
                                   self.depth, ds.mesh, self.vscreen, ds.light, s.bg, s.softness, self.out_rgb,
                                   self.out_depth, self.out_alpha, self.state_T, self.state_last, self.state_cm,
                                   _stream())
+
+    def composite_fwd_shaded(self, view: int):
+        """The composite forward's second half: state_cm must already hold this view's
+        shading, ordered before on the current stream."""
+        ds, s = self.ds, self.ds.scene
+        G.gm_composite_hybrid_fwd_shaded(ds.cams[view], self.rec, self.tile_ranges, self.sorted_ids, self.face_id,
+                                         self.depth, s.softness, self.state_cm, self.out_rgb, self.out_depth,
+                                         self.out_alpha, self.state_T, self.state_last, _stream())
 
     def composite_bwd(self, view: int, g_rgb, g_depth=None, g_alpha=None):
         ds, s = self.ds, self.ds.scene
@@ -439,6 +451,69 @@ class Renderer:
                 self.composite_bwd(v, grads[k]["rgb"], grads[k].get("depth"), grads[k].get("alpha"))
             if hook is not None:
                 hook(k)
+        self.fetch_counts()
+
+    # buffers written by the first half of a view (mesh visibility, shading, depth
+    # order, lists); the second half's outputs and gradients are shared
+    _SLOT_KEYS = ("vscreen", "tile_offsets", "ws_bin", "tile_tris", "face_id", "depth", "tile_dmax", "state_cm",
+                  "tile_ranges", "sorted_ids", "ws_sort")
+
+    def _use_slot(self, i: int):
+        if self._slots is None:
+            a = {k: getattr(self, k) for k in self._SLOT_KEYS}
+            self._slots = [a, {k: torch.empty_like(t) for k, t in a.items()}]
+        for k, t in self._slots[i].items():
+            setattr(self, k, t)
+
+    def views_step_pipelined(self, views, grads, cull: bool = True, backward: bool = True, hook=None):
+        """views_step_async() with the views' halves overlapped: the mesh half of view
+        k (binning, z-buffer, shading) and its depth sort run on two producer streams
+        into one of two buffer sets while the main stream sorts and composites view
+        k - 1 from the other set.  A producer waits for the main stream to be done with
+        view k - 2 (the last user of its set) and the main stream for both producers
+        before view k's tile sort.  Same results as views_step_async(), bit for bit;
+        hook(k) runs on the main stream after view k."""
+        if len(views) > self.MAX_BATCH:
+            raise ValueError(f"at most {self.MAX_BATCH} views per batch")
+        main, gs = torch.cuda.current_stream(), self._side_stream()
+        if self._mesh_stream is None:  # default priority, like every stream here
+            self._mesh_stream = torch.cuda.Stream(device=self.ds.device)
+            self._ev_slot_free = [torch.cuda.Event(), torch.cuda.Event()]
+            self._ev_mesh = [torch.cuda.Event(), torch.cuda.Event()]
+            self._ev_gauss = [torch.cuda.Event(), torch.cuda.Event()]
+            self._ev_start = torch.cuda.Event()
+        ms = self._mesh_stream
+        # everything queued before (readers of either buffer set) precedes the producers
+        self._ev_start.record(main)
+        ms.wait_event(self._ev_start)
+        self.project_views(views)
+        self._ev_main.record(main)  # the records of every view
+        gs.wait_event(self._ev_main)
+        self._rows = len(views)
+        for k, v in enumerate(views):
+            slot = k & 1
+            self._use_slot(slot)
+            self.use_view(k)
+            self.view, self.cull = v, cull
+            if k >= 2:
+                ms.wait_event(self._ev_slot_free[slot])
+                gs.wait_event(self._ev_slot_free[slot])
+            with torch.cuda.stream(gs):
+                self.sort_depth(v)
+                self._ev_gauss[slot].record(gs)
+            with torch.cuda.stream(ms):
+                self.bin_and_zbuffer(v)
+                self.shade(v)
+                self._ev_mesh[slot].record(ms)
+            main.wait_event(self._ev_gauss[slot])
+            main.wait_event(self._ev_mesh[slot])
+            self.sort_tiles(v, cull)
+            self.composite_fwd_shaded(v)
+            if backward:
+                self.composite_bwd(v, grads[k]["rgb"], grads[k].get("depth"), grads[k].get("alpha"))
+            if hook is not None:
+                hook(k)
+            self._ev_slot_free[slot].record(main)
         self.fetch_counts()
 
     def fit_lists_views(self, views, cull: bool = True):

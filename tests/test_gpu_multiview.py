@@ -8,7 +8,9 @@ alone (whose own parity against the oracle the other GPU tests establish).  A wh
 batched pass (one projection, then per view the lists, composite forward and
 backward) gives the per-view loop's images, mesh-side gradients and list lengths
 bit for bit, and its record gradients up to the summation order of the float
-atomics (|d| <= 1e-3 (|ref| + rms), the gradient rule of the parity tests).
+atomics (|d| <= 1e-3 (|ref| + rms), the gradient rule of the parity tests).  So
+does the pipelined pass, which overlaps one view's mesh half and depth sort with the
+previous view's tile sort and composite in two alternating buffer sets.
 """
 import functools
 import math
@@ -126,8 +128,9 @@ def _outputs(r):
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("method", ["views_step_async", "views_step_pipelined"])
 @pytest.mark.parametrize("name", ["c5", "c2"])
-def test_batched_pass_matches_per_view_loop(name):
+def test_batched_pass_matches_per_view_loop(name, method):
     import torch
     from differentiable_hybrid_mesh_amd.pipeline import DeviceScene, Renderer
     s = _scene(name)
@@ -149,7 +152,10 @@ def test_batched_pass_matches_per_view_loop(name):
     r = Renderer(ds)
     r.fit_lists_views(views)
     got = []
-    r.views_step_async(views, grads, hook=lambda k: got.append(_outputs(r)))
+    # the pipelined pass twice: the second reuses both buffer sets
+    for _ in range(2 if method == "views_step_pipelined" else 1):
+        got = []
+        getattr(r, method)(views, grads, hook=lambda k: got.append(_outputs(r)))
     torch.cuda.synchronize()
     assert r.read_counts()
     assert r.n_pairs == max(c[0] for c in ref_counts) and r.n_keys == max(c[1] for c in ref_counts)
