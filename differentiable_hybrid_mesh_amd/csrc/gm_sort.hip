@@ -345,6 +345,8 @@ __device__ inline bool culled(const DevCamera& cam, float softness, float dmax, 
 constexpr int PW_WAVES = 8;              // waves per 512-thread block
 constexpr int PW_LDS_MAX_TILES = 10240;  // tile_dmax staged in LDS up to this many tiles
 constexpr int PW_WORDS = 64;             // stored step ballots per chunk (4096 pairs)
+constexpr int PW_COUNT_BLOCKS = 512;     // grid of the counting pass (two blocks per CU with tile_dmax in LDS)
+constexpr int PW_EMIT_BLOCKS = 1024;     // grid of the emitting pass (no tile_dmax in LDS: four blocks per CU)
 
 struct ChunkCtx {
     int wave, lane, total, start, nt;
@@ -668,7 +670,8 @@ static gm_status sort_tiles(const DevCamera& dc, int32_t N, const float* rec, co
     CullParams cp{tile_dmax, softness};
     const size_t shm = lds ? sizeof(float) * (size_t)T : 0;
     const int nchunks = (int)div_up(N, 64);
-    const unsigned gW = (unsigned)std::min<int64_t>(div_up(nchunks, PW_WAVES), 512);
+    const unsigned gW = (unsigned)std::min<int64_t>(div_up(nchunks, PW_WAVES), PW_COUNT_BLOCKS);
+    const unsigned gE = (unsigned)std::min<int64_t>(div_up(nchunks, PW_WAVES), PW_EMIT_BLOCKS);
     auto count = lds ? k_pairs<false, true, uint16_t> : k_pairs<false, false, uint16_t>;  // no keys written
     count<<<gW, 64 * PW_WAVES, shm, stream>>>(dc, cp, d_nvis, nchunks, order, rec, w.cnt, nullptr, w.bits, nullptr, 0,
                                               nullptr, nullptr);
@@ -680,9 +683,9 @@ static gm_status sort_tiles(const DevCamera& dc, int32_t N, const float* rec, co
     const int64_t kcap = std::min<int64_t>(cap, INT32_MAX);
     if (kcap == 0) return GM_OK;
     if (T <= 65536)  // 16-bit tile keys: 12 instead of 16 bytes per key and pass
-        return emit_and_sort<uint16_t>(dc, cp, d_nvis, nchunks, gW, order, rec, total, kcap, T, sorted_ids,
+        return emit_and_sort<uint16_t>(dc, cp, d_nvis, nchunks, gE, order, rec, total, kcap, T, sorted_ids,
                                        tile_ranges, w, stream);
-    return emit_and_sort<uint32_t>(dc, cp, d_nvis, nchunks, gW, order, rec, total, kcap, T, sorted_ids, tile_ranges,
+    return emit_and_sort<uint32_t>(dc, cp, d_nvis, nchunks, gE, order, rec, total, kcap, T, sorted_ids, tile_ranges,
                                    w, stream);
 }
 
