@@ -291,6 +291,44 @@ def test_lists_above_10240_tiles():
     assert (ranges[tiles[tiles >= 10240], 1] > 0).sum() >= 1
 
 
+def test_backward_above_16384_tiles():
+    """A 2080 x 2080 image has 130 x 130 = 16900 tiles, more than the backward's tile
+    order keeps in registers (it reads the walk lengths in loops instead).  Forward
+    and backward on sampled tiles against the oracle, upstream gradients zero
+    elsewhere, so every Gaussian's gradient comes from the sampled tiles only."""
+    W = H = 2080
+    rng = np.random.default_rng(47)
+    s = tiny.empty_scene(W, H, 1500.0, 1500.0, W / 2, H / 2, name="16900 tiles")
+    n = 400
+    u, v = rng.uniform(0, W, n), rng.uniform(0, H, n)
+    z = rng.uniform(2.0, 4.0, n)
+    means = np.stack([(u - s.cx) * z / s.fx, (v - s.cy) * z / s.fy, z], 1)
+    q = rng.normal(size=(n, 4))
+    q /= np.linalg.norm(q, axis=1, keepdims=True)
+    sc = np.exp(rng.normal(-4.5, 0.4, size=(n, 3)))  # a few tiles across on screen
+    op = 1.0 / (1.0 + np.exp(-rng.normal(1.0, 1.0, size=n)))
+    tiny.set_gaussians(s, means, q, sc, op, rgb=rng.uniform(size=(n, 3)))
+    tris = []
+    for k in range(40):
+        c = rng.uniform([0, 0], [W, H])
+        r = rng.uniform(60, 300)
+        a = rng.uniform(0, 2 * np.pi) + np.array([0, 2.1, 4.2])
+        zz = rng.uniform(2.5, 3.5)
+        tris.append([[c[0] + r * np.cos(t), c[1] + r * np.sin(t), zz] for t in a])
+    _screen_soup(s, tris, rng)
+    s.grads = [scenes.upstream_grads(s, 0, 47)]
+    T = s.tiles_x * s.tiles_y
+    assert T == 16900
+    txn = s.tiles_x
+    near = np.unique(np.clip(v // 16, 0, s.tiles_y - 1).astype(int) * txn + np.clip(u // 16, 0, txn - 1).astype(int))
+    tiles = np.unique(np.concatenate([rng.choice(near, 150, replace=False), rng.integers(0, T, 50),
+                                      [T - 1]])).astype(np.int32)
+    gpu, ora, tiles = _run(s, 0, tiles, masked=True)
+    rep = _check_all(s, 0, gpu, ora, tiles, True, "16900 tiles")
+    assert rep["entries"] > 150  # the sample reaches a couple of hundred list entries
+    assert np.abs(gpu["g_rec"]).max() > 0
+
+
 def test_no_mesh_plain_splatting():
     s = tiny.random_tiny(5, n_tri=1, n_gauss=40, size=48)
     s.verts, s.faces, s.vcolor = None, None, None
