@@ -16,17 +16,14 @@ constexpr int ZB_THREADS = 256;  // one thread per pixel of a 16x16 tile
 constexpr int ZB_BATCH = 128;    // triangles staged in LDS per round
 constexpr double ZB_MARGIN = 1.0 / 64.0;  // candidate box margin d around the bounding box, pixels
 
-__global__ void k_fill_i32(int32_t* __restrict__ p, int64_t n, int32_t v)
-{
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = v;
-}
-
 // vscreen = (u, v, z_c) planes: x_c = ((R0 x + R1 y) + R2 z) + t0, u = (fx x_c)/z_c + cx.
+// Also clears nz ints at zero (the per-tile counters of the binning that follows:
+// one launch fewer).
 __global__ void k_project_vertices(DevCamera cam, int V, const float* __restrict__ verts,
-                                   float* __restrict__ vscreen)
+                                   float* __restrict__ vscreen, int32_t* __restrict__ zero, int64_t nz)
 {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < nz) zero[i] = 0;
     if (i >= V) return;
     const float x = verts[i], y = verts[V + i], z = verts[2 * V + i];
     const float xc = ((cam.R[0] * x + cam.R[1] * y) + cam.R[2] * z) + cam.t[0];
@@ -423,12 +420,10 @@ gm_status gm_bin_triangles(const gm_camera* cam, const gm_mesh* mesh, float* vsc
     void* scan_ws = w;
     long long* total = reinterpret_cast<long long*>(n_pairs);
 
-    k_fill_i32<<<(unsigned)div_up(2 * T + 64, 256), 256, 0, stream>>>(tile_cnt, (cursor - tile_cnt) + T, 0);
+    const int64_t nz = (cursor - tile_cnt) + T;  // tile_cnt and cursor
+    k_project_vertices<<<(unsigned)div_up(std::max<int64_t>(V, nz), 256), 256, 0, stream>>>(dc, V, mesh->verts,
+                                                                                         vscreen, tile_cnt, nz);
     GM_LAUNCH_CHECK();
-    if (V > 0) {
-        k_project_vertices<<<(unsigned)div_up(V, 256), 256, 0, stream>>>(dc, V, mesh->verts, vscreen);
-        GM_LAUNCH_CHECK();
-    }
     if (F > 0) {
         k_bin_count<<<(unsigned)div_up(F, 256), 256, 0, stream>>>(dc, V, F, mesh->faces, mesh->face_mask,
                                                                  vscreen, face_rect, tile_cnt);

@@ -389,14 +389,19 @@ __device__ __forceinline__ void skip_owner(const ChunkCtx& c, int f0, int& carry
 
 // LDS: tile_dmax is staged in LDS (a compile-time choice, so the cull's read is a
 // plain LDS load rather than a generic one through a pointer picked at run time).
+// The counting pass also clears the tile ranges (n2 ints; grid-stride), which
+// only the range kernel at the end writes again (one launch fewer).
 template <bool EMIT, bool LDS, typename KT>
 __global__ void __launch_bounds__(64 * PW_WAVES)
 k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nchunks,
         const int32_t* __restrict__ order, const float* __restrict__ rec, int32_t* __restrict__ chunk_cnt,
         const int32_t* __restrict__ chunk_off, unsigned long long* __restrict__ bits,
         const long long* __restrict__ d_total, long long cap, KT* __restrict__ tkeys,
-        int32_t* __restrict__ tvals)
+        int32_t* __restrict__ tvals, int32_t* __restrict__ ranges, int64_t n2)
 {
+    if (!EMIT)
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n2; i += (int64_t)gridDim.x * blockDim.x)
+            ranges[i] = 0;
     extern __shared__ float s_dmax[];       // tile_dmax when LDS
     __shared__ int4 s_gi[PW_WAVES][64];     // first flat index in the chunk, rect lo, rect hi, id
     __shared__ float4 s_ga[PW_WAVES][64];   // u, v, z_c, g0
@@ -642,7 +647,7 @@ static gm_status emit_and_sort(const DevCamera& dc, const CullParams& cp, const 
     int32_t* va = (npass % 2 == 0) ? sorted_ids : w.tva;
     int32_t* vb = (npass % 2 == 0) ? w.tva : sorted_ids;
     k_pairs<true, false, KT><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, d_nvis, nchunks, order, rec, nullptr, w.off,
-                                                               w.bits, total, kcap, ka, va);
+                                                               w.bits, total, kcap, ka, va, nullptr, 0);
     GM_LAUNCH_CHECK();
     if (gm_status s = radix_sort<KT>(ka, va, kb, vb, tbits, total, kcap, w.aux, stream)) return s;
     const KT* kfin = (npass % 2 == 0) ? ka : kb;
@@ -659,9 +664,11 @@ static gm_status sort_tiles(const DevCamera& dc, int32_t N, const float* rec, co
                             long long* total, const SortWs& w, hipStream_t stream)
 {
     const int64_t T = (int64_t)dc.tx * dc.ty;
-    k_sort_init<<<(unsigned)div_up(2 * T, 256), 256, 0, stream>>>(tile_ranges, 2 * T, total);
-    GM_LAUNCH_CHECK();
-    if (N == 0) return GM_OK;
+    if (N == 0) {  // no lists: empty ranges, no keys
+        k_sort_init<<<(unsigned)div_up(2 * T, 256), 256, 0, stream>>>(tile_ranges, 2 * T, total);
+        GM_LAUNCH_CHECK();
+        return GM_OK;
+    }
     const int32_t* order = w.dva;  // 4 passes: back in the first buffer pair
     // number of listed Gaussians = offset of top byte 0xff in the depth sort's last
     // pass, block 0; valid until the tile sort below reuses the histogram buffers
@@ -674,7 +681,7 @@ static gm_status sort_tiles(const DevCamera& dc, int32_t N, const float* rec, co
     const unsigned gE = (unsigned)std::min<int64_t>(div_up(nchunks, PW_WAVES), PW_EMIT_BLOCKS);
     auto count = lds ? k_pairs<false, true, uint16_t> : k_pairs<false, false, uint16_t>;  // no keys written
     count<<<gW, 64 * PW_WAVES, shm, stream>>>(dc, cp, d_nvis, nchunks, order, rec, w.cnt, nullptr, w.bits, nullptr, 0,
-                                              nullptr, nullptr);
+                                              nullptr, nullptr, tile_ranges, 2 * T);  // also clears the ranges
     GM_LAUNCH_CHECK();
     if (gm_status s = exclusive_scan(w.cnt, w.off, nchunks, total, w.scan, stream)) return s;
     // 3. emit (tile, id) in depth order; 4. stable sort by tile; 5. tile ranges.
