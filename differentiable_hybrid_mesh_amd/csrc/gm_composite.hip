@@ -22,7 +22,7 @@ namespace gm {
 
 constexpr int CT = 256;     // threads per block = pixels per tile
 constexpr int CB = 256;     // records per LDS batch
-constexpr int CBB = 192;    // records per LDS batch of the backward (<= CT, a multiple of 64): 24 KB of
+constexpr int CBB = 192;    // records per LDS batch of the backward (<= CT, a multiple of 32): 24 KB of
                             // LDS per block, six blocks per CU (five at 256: 0.550 -> 0.509 ms at C3)
 constexpr float SKIP_ALPHA = 1.0f / 255.0f;
 constexpr float STOP_T = 1e-4f;
@@ -850,8 +850,8 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
             }
         }
         __syncthreads();
-        for (int i = CBB / 64 - 1; i >= 0; --i) {
-            unsigned long long mm = __ballot((s_m[i * 64 + lane] >> wave) & 1);
+        for (int i = (CBB + 63) / 64 - 1; i >= 0; --i) {
+            unsigned long long mm = __ballot(i * 64 + lane < CBB && ((s_m[i * 64 + lane] >> wave) & 1));
             while (mm) {
                 const int kk = 63 - __builtin_clzll(mm);
                 mm &= ~(1ull << kk);
