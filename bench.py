@@ -372,8 +372,8 @@ def main():
 def main_batch(args, scene):
     """Every view of the workload per step: one gm_project_gaussians_multi for all
     views, then per view the lists, composite forward and backward, with each view's
-    mesh half and depth sort overlapped with the previous view's tile sort and
-    composite (Renderer.views_step_pipelined).  Also times the views one after
+    mesh half and lists overlapped with the previous view's composite
+    (Renderer.views_step_pipelined).  Also times the views one after
     another, and the batched projection against the per-view projection loop it
     replaces."""
     import torch

@@ -14,8 +14,8 @@ on the current torch stream, except the projection and the depth sort, which run
 on a second stream beside the binning and z-buffer, followed there by the mesh
 shading (the composite forward's first half) beside the tile sort
 (``Renderer.lists``).  In the pipelined multi-view pass
-(``Renderer.views_step_pipelined``) each view's mesh half and depth sort run on two
-producer streams beside the previous view's tile sort and composite.  Every step
+(``Renderer.views_step_pipelined``) each view's mesh half and lists run on two
+producer streams beside the previous view's composite.  Every step
 of the path runs in libgm's kernels.
 """
 from __future__ import annotations
@@ -467,12 +467,13 @@ class Renderer:
 
     def views_step_pipelined(self, views, grads, cull: bool = True, backward: bool = True, hook=None):
         """views_step_async() with the views' halves overlapped: the mesh half of view
-        k (binning, z-buffer, shading) and its depth sort run on two producer streams
-        into one of two buffer sets while the main stream sorts and composites view
-        k - 1 from the other set.  A producer waits for the main stream to be done with
-        view k - 2 (the last user of its set) and the main stream for both producers
-        before view k's tile sort.  Same results as views_step_async(), bit for bit;
-        hook(k) runs on the main stream after view k."""
+        k (binning, z-buffer, shading) and its lists (depth sort, then the tile sort
+        once the z-buffer is done) run on two producer streams into one of two buffer
+        sets while the main stream composites view k - 1 from the other set.  A
+        producer waits for the main stream to be done with view k - 2 (the last user of
+        its set) and the main stream for both producers before view k's composite.
+        Same results as views_step_async(), bit for bit; hook(k) runs on the main
+        stream after view k."""
         if len(views) > self.MAX_BATCH:
             raise ValueError(f"at most {self.MAX_BATCH} views per batch")
         main, gs = torch.cuda.current_stream(), self._side_stream()
@@ -498,16 +499,18 @@ class Renderer:
             if k >= 2:
                 ms.wait_event(self._ev_slot_free[slot])
                 gs.wait_event(self._ev_slot_free[slot])
-            with torch.cuda.stream(gs):
-                self.sort_depth(v)
-                self._ev_gauss[slot].record(gs)
             with torch.cuda.stream(ms):
                 self.bin_and_zbuffer(v)
+                self._ev_zb.record(ms)
                 self.shade(v)
                 self._ev_mesh[slot].record(ms)
+            with torch.cuda.stream(gs):
+                self.sort_depth(v)
+                gs.wait_event(self._ev_zb)
+                self.sort_tiles(v, cull)
+                self._ev_gauss[slot].record(gs)
             main.wait_event(self._ev_gauss[slot])
             main.wait_event(self._ev_mesh[slot])
-            self.sort_tiles(v, cull)
             self.composite_fwd_shaded(v)
             if backward:
                 self.composite_bwd(v, grads[k]["rgb"], grads[k].get("depth"), grads[k].get("alpha"))

@@ -9,8 +9,8 @@ batched pass (one projection, then per view the lists, composite forward and
 backward) gives the per-view loop's images, mesh-side gradients and list lengths
 bit for bit, and its record gradients up to the summation order of the float
 atomics (|d| <= 1e-3 (|ref| + rms), the gradient rule of the parity tests).  So
-does the pipelined pass, which overlaps one view's mesh half and depth sort with the
-previous view's tile sort and composite in two alternating buffer sets.
+does the pipelined pass, which overlaps one view's mesh half and lists with the
+previous view's composite in two alternating buffer sets.
 """
 import functools
 import math
