@@ -192,7 +192,7 @@ def main():
                            r.ws_bin, st)
         mark()
         G.gm_raster_zbuffer(cam, ds.mesh, r.vscreen, r.tile_offsets, r.tile_tris, r.face_id, r.depth,
-                            r.tile_dmax, st)
+                            r.tile_dmax, r.ws_zb, st)
         mark()
         if aa:
             r.antialias(view)

@@ -43,7 +43,8 @@ class GmMesh(C.Structure):
                 ("faces_uv", C.c_void_p), ("mips", C.c_void_p)]
 
 
-EXPORTS = ["gm_bin_triangles_ws", "gm_bin_triangles", "gm_raster_zbuffer", "gm_project_gaussians",
+EXPORTS = ["gm_bin_triangles_ws", "gm_bin_triangles", "gm_raster_zbuffer_ws", "gm_raster_zbuffer",
+           "gm_project_gaussians",
            "gm_project_gaussians_multi",
            "gm_sort_tile_keys_ws", "gm_sort_tile_keys", "gm_sort_depth", "gm_sort_tiles", "gm_composite_hybrid_fwd",
            "gm_composite_hybrid_bwd", "gm_composite_hybrid_bwd_ws", "gm_project_gaussians_bwd", "gm_mesh_bwd", "gm_mipmaps_floats",
@@ -68,7 +69,9 @@ def lib():
     L.gm_bin_triangles_ws.argtypes = [I32, I32, I32, I32]
     L.gm_bin_triangles_ws.restype = SZ
     L.gm_bin_triangles.argtypes = [cam, mesh, P, P, P, I64, P, P, SZ, P]
-    L.gm_raster_zbuffer.argtypes = [cam, mesh, P, P, P, P, P, P, P]
+    L.gm_raster_zbuffer_ws.argtypes = [I32, I32]
+    L.gm_raster_zbuffer_ws.restype = SZ
+    L.gm_raster_zbuffer.argtypes = [cam, mesh, P, P, P, P, P, P, P, SZ, P]
     L.gm_project_gaussians.argtypes = [cam, I32, P, P, P, P, P, I32, P, P]
     L.gm_project_gaussians_multi.argtypes = [cam, I32, I32, P, P, P, P, P, I32, P, P]
     L.gm_sort_tile_keys_ws.argtypes = [I32, I64, I32, I32]
@@ -143,9 +146,14 @@ def gm_bin_triangles(cam, mesh, vscreen, tile_offsets, tile_tris, cap, n_pairs, 
                                  0 if ws is None else ws.numel() * ws.element_size(), stream))
 
 
-def gm_raster_zbuffer(cam, mesh, vscreen, tile_offsets, tile_tris, face_id, depth, tile_dmax, stream):
+def gm_raster_zbuffer_ws(width, height) -> int:
+    return lib().gm_raster_zbuffer_ws(int(width), int(height))
+
+
+def gm_raster_zbuffer(cam, mesh, vscreen, tile_offsets, tile_tris, face_id, depth, tile_dmax, ws, stream):
     check(lib().gm_raster_zbuffer(C.byref(cam), C.byref(mesh), ptr(vscreen), ptr(tile_offsets),
-                                  ptr(tile_tris), ptr(face_id), ptr(depth), ptr(tile_dmax), stream))
+                                  ptr(tile_tris), ptr(face_id), ptr(depth), ptr(tile_dmax), ptr(ws),
+                                  0 if ws is None else ws.numel() * ws.element_size(), stream))
 
 
 def gm_project_gaussians(cam, N, means, quats, scales, opacity, sh, sh_degree, rec, stream):

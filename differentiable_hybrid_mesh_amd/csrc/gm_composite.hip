@@ -646,82 +646,12 @@ k_tile_walk(CompParams P, const int32_t* __restrict__ state_last, const float* _
     if (threadIdx.x == 0) walk[tile] = max(max(s_w[0], s_w[1]), max(s_w[2], s_w[3]));
 }
 
-// Counting sort of the tiles into TO_BUCKETS buckets of walk length, longest first
-// (one block; the order inside a bucket is unspecified).  Counts and slots are taken
-// per wave: thousands of empty tiles share one bucket, and one counter for the block
-// serialised their LDS atomics.
-constexpr int TO_BUCKETS = 64;
-constexpr int TO_THREADS = 1024;
-constexpr int TO_PER = 16;  // walks held in registers per thread (16384 tiles)
-
+// Order in which the backward takes the tiles: longest walk first (the shared
+// counting sort of the tiles by a per-tile key, one block).
 __global__ void __launch_bounds__(TO_THREADS) k_tile_order(int T, const int32_t* __restrict__ walk,
                                                            int32_t* __restrict__ order)
 {
-    constexpr int NW = TO_THREADS / 64;
-    __shared__ int s_cnt[NW][TO_BUCKETS];  // per-wave counts, then per-wave next slots
-    __shared__ int s_max;
-    const int wave = threadIdx.x >> 6;
-    for (int i = threadIdx.x; i < NW * TO_BUCKETS; i += TO_THREADS) (&s_cnt[0][0])[i] = 0;
-    if (threadIdx.x == 0) s_max = 0;
-    __syncthreads();
-    // up to TO_PER walks per thread stay in registers (one read of the array);
-    // larger images read it again in each loop
-    const bool held = T <= TO_THREADS * TO_PER;
-    int wv[TO_PER];
-    int m = 0;
-#pragma unroll
-    for (int k = 0; k < TO_PER; ++k) {
-        const int t = threadIdx.x + k * TO_THREADS;
-        wv[k] = held && t < T ? walk[t] : 0;
-        m = max(m, wv[k]);
-    }
-    if (!held)
-        for (int t = threadIdx.x; t < T; t += TO_THREADS) m = max(m, walk[t]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o, 64));
-    if ((threadIdx.x & 63) == 0) atomicMax(&s_max, m);
-    __syncthreads();
-    const float scale = (float)TO_BUCKETS / ((float)s_max + 1.0f);
-    auto bucket_of = [&](int w) { return TO_BUCKETS - 1 - min(TO_BUCKETS - 1, (int)((float)w * scale)); };
-    if (held) {
-#pragma unroll
-        for (int k = 0; k < TO_PER; ++k)
-            if (threadIdx.x + k * TO_THREADS < T) atomicAdd(&s_cnt[wave][bucket_of(wv[k])], 1);
-    } else {
-        for (int t = threadIdx.x; t < T; t += TO_THREADS) atomicAdd(&s_cnt[wave][bucket_of(walk[t])], 1);
-    }
-    __syncthreads();
-    if (threadIdx.x < TO_BUCKETS) {  // bucket-major exclusive offsets, waves in order
-        const int b = threadIdx.x;
-        int c[NW], tot = 0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            c[w] = s_cnt[w][b];
-            tot += c[w];
-        }
-        int x = tot;  // inclusive scan of the bucket totals over the 64 lanes of wave 0
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int y = __shfl_up(x, d, 64);
-            if ((int)threadIdx.x >= d) x += y;
-        }
-        int run = x - tot;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            s_cnt[w][b] = run;
-            run += c[w];
-        }
-    }
-    __syncthreads();
-    if (held) {
-#pragma unroll
-        for (int k = 0; k < TO_PER; ++k) {
-            const int t = threadIdx.x + k * TO_THREADS;
-            if (t < T) order[atomicAdd(&s_cnt[wave][bucket_of(wv[k])], 1)] = t;
-        }
-    } else {
-        for (int t = threadIdx.x; t < T; t += TO_THREADS) order[atomicAdd(&s_cnt[wave][bucket_of(walk[t])], 1)] = t;
-    }
+    order_tiles_desc(T, [=](int t) { return walk[t]; }, order);
 }
 
 template <bool AA>

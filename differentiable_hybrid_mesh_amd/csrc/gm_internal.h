@@ -88,4 +88,87 @@ gm_status launch_surface_colour(const gm_camera* cam, const gm_mesh* mesh, const
 // Read a device int64 into host memory (synchronises the stream).
 gm_status read_back_i64(const long long* dev, int64_t* host, hipStream_t stream);
 
+// ---------------------------------------------------------------------------
+// tile order: largest per-tile key first (one block of TO_THREADS)
+// ---------------------------------------------------------------------------
+// Blocks of a grid start in launch order, and per-tile work differs by an order of
+// magnitude across an image, so a grid taken in raster order leaves its longest
+// tiles for the end.  A counting sort of the T tiles into TO_BUCKETS buckets of
+// key(t) >= 0, largest first, gives a launch order (the order inside a bucket is
+// unspecified).  Counts and slots are taken per wave: thousands of empty tiles share
+// one bucket, and one counter for the block serialised their LDS atomics.  Up to
+// TO_PER keys per thread stay in registers (one evaluation of key); larger images
+// evaluate it again in each loop.
+constexpr int TO_BUCKETS = 64;
+constexpr int TO_THREADS = 1024;
+constexpr int TO_PER = 16;  // keys held in registers per thread (16384 tiles)
+
+template <class Key>
+__device__ inline void order_tiles_desc(int T, Key key, int32_t* __restrict__ order)
+{
+    constexpr int NW = TO_THREADS / 64;
+    __shared__ int s_cnt[NW][TO_BUCKETS];  // per-wave counts, then per-wave next slots
+    __shared__ int s_max;
+    const int wave = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < NW * TO_BUCKETS; i += TO_THREADS) (&s_cnt[0][0])[i] = 0;
+    if (threadIdx.x == 0) s_max = 0;
+    __syncthreads();
+    const bool held = T <= TO_THREADS * TO_PER;
+    int kv[TO_PER];
+    int m = 0;
+#pragma unroll
+    for (int k = 0; k < TO_PER; ++k) {
+        const int t = threadIdx.x + k * TO_THREADS;
+        kv[k] = held && t < T ? key(t) : 0;
+        m = max(m, kv[k]);
+    }
+    if (!held)
+        for (int t = threadIdx.x; t < T; t += TO_THREADS) m = max(m, key(t));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o, 64));
+    if ((threadIdx.x & 63) == 0) atomicMax(&s_max, m);
+    __syncthreads();
+    const float scale = (float)TO_BUCKETS / ((float)s_max + 1.0f);
+    auto bucket_of = [&](int v) { return TO_BUCKETS - 1 - min(TO_BUCKETS - 1, (int)((float)v * scale)); };
+    if (held) {
+#pragma unroll
+        for (int k = 0; k < TO_PER; ++k)
+            if (threadIdx.x + k * TO_THREADS < T) atomicAdd(&s_cnt[wave][bucket_of(kv[k])], 1);
+    } else {
+        for (int t = threadIdx.x; t < T; t += TO_THREADS) atomicAdd(&s_cnt[wave][bucket_of(key(t))], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x < TO_BUCKETS) {  // bucket-major exclusive offsets, waves in order
+        const int b = threadIdx.x;
+        int c[NW], tot = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            c[w] = s_cnt[w][b];
+            tot += c[w];
+        }
+        int x = tot;  // inclusive scan of the bucket totals over the 64 lanes of wave 0
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(x, d, 64);
+            if ((int)threadIdx.x >= d) x += y;
+        }
+        int run = x - tot;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            s_cnt[w][b] = run;
+            run += c[w];
+        }
+    }
+    __syncthreads();
+    if (held) {
+#pragma unroll
+        for (int k = 0; k < TO_PER; ++k) {
+            const int t = threadIdx.x + k * TO_THREADS;
+            if (t < T) order[atomicAdd(&s_cnt[wave][bucket_of(kv[k])], 1)] = t;
+        }
+    } else {
+        for (int t = threadIdx.x; t < T; t += TO_THREADS) order[atomicAdd(&s_cnt[wave][bucket_of(key(t))], 1)] = t;
+    }
+}
+
 }  // namespace gm

@@ -129,6 +129,7 @@ class Renderer:
         self.face_id = torch.empty((self.H, self.W), dtype=i32, device=dev)
         self.depth = torch.empty((self.H, self.W), dtype=f32, device=dev)
         self.tile_dmax = torch.empty(self.T, dtype=f32, device=dev)
+        self.ws_zb = torch.empty(G.gm_raster_zbuffer_ws(s.width, s.height), dtype=torch.uint8, device=dev)
         self.rec = torch.empty((max(self.N, 1), G.GM_REC), dtype=f32, device=dev)
         self._rec_own = self.rec
         self.rec_views = None  # [views][N][GM_REC] of project_views()
@@ -173,7 +174,7 @@ class Renderer:
         G.gm_bin_triangles(cam, ds.mesh, self.vscreen, self.tile_offsets, self.tile_tris, self.pair_cap,
                            self.counts[0:1], self.ws_bin, st)
         G.gm_raster_zbuffer(cam, ds.mesh, self.vscreen, self.tile_offsets, self.tile_tris, self.face_id,
-                            self.depth, self.tile_dmax, st)
+                            self.depth, self.tile_dmax, self.ws_zb, st)
 
     def project(self, view: int):
         ds, s = self.ds, self.ds.scene
@@ -455,8 +456,8 @@ class Renderer:
 
     # buffers written by the first half of a view (mesh visibility, shading, depth
     # order, lists); the second half's outputs and gradients are shared
-    _SLOT_KEYS = ("vscreen", "tile_offsets", "ws_bin", "tile_tris", "face_id", "depth", "tile_dmax", "state_cm",
-                  "tile_ranges", "sorted_ids", "ws_sort")
+    _SLOT_KEYS = ("vscreen", "tile_offsets", "ws_bin", "tile_tris", "face_id", "depth", "tile_dmax", "ws_zb",
+                  "state_cm", "tile_ranges", "sorted_ids", "ws_sort")
 
     def _use_slot(self, i: int):
         if self._slots is None:

@@ -132,10 +132,16 @@ gm_status gm_bin_triangles(const gm_camera* cam, const gm_mesh* mesh, float* vsc
  * to the smaller face id.  Outputs: face_id [H][W] (-1 = empty), depth [H][W] =
  * fp32 rounding of z (+inf = empty), tile_dmax [T] = max depth over the tile's
  * in-image pixels, +inf when any of them is empty (input of the occlusion cull).
+ * Inputs: vscreen, tile_offsets [T+1] and tile_tris of call 1 for the same camera
+ * and mesh.  ws: device scratch of at least gm_raster_zbuffer_ws(W, H) bytes, owned
+ * by the caller (the tiles' launch order, largest bin first; it does not change the
+ * result); too small or NULL is GM_ERR_ARG.
  * ------------------------------------------------------------------------- */
+size_t gm_raster_zbuffer_ws(int32_t width, int32_t height);
 gm_status gm_raster_zbuffer(const gm_camera* cam, const gm_mesh* mesh, const float* vscreen,
                             const int32_t* tile_offsets, const int32_t* tile_tris,
-                            int32_t* face_id, float* depth, float* tile_dmax, hipStream_t stream);
+                            int32_t* face_id, float* depth, float* tile_dmax, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * 3. gm_project_gaussians — EWA projection, conditional depth model, colour.

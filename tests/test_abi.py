@@ -66,7 +66,15 @@ def test_argument_errors_before_any_launch(G):
     assert L.gm_project_gaussians(C.byref(cam), -1, 1, 1, 1, 1, 1, 0, 1, None) == G.GM_ERR_ARG
     # zero-sized image
     bad = _cam(G, 0, 64)
-    assert L.gm_raster_zbuffer(C.byref(bad), None, None, None, None, None, None, None, None) == G.GM_ERR_ARG
+    assert L.gm_raster_zbuffer(C.byref(bad), None, None, None, None, None, None, None, None, 0, None) == G.GM_ERR_ARG
+    # z-buffer workspace missing or too small
+    mz = G.GmMesh()
+    zws = G.gm_raster_zbuffer_ws(64, 64)
+    assert zws == 256  # 16 tiles of int32, one 256-byte block
+    assert L.gm_raster_zbuffer(C.byref(cam), C.byref(mz), None, 16, None, 16, 16, 16, None, zws, None) == G.GM_ERR_ARG
+    assert L.gm_raster_zbuffer(C.byref(cam), C.byref(mz), None, 16, None, 16, 16, 16, 16, zws - 1,
+                               None) == G.GM_ERR_ARG
+    assert b"workspace" in L.gm_last_error()
     # workspace too small
     m = G.GmMesh()
     assert L.gm_bin_triangles(C.byref(cam), C.byref(m), 16, 16, 16, 0, 16, 16, 1, None) == G.GM_ERR_ARG
