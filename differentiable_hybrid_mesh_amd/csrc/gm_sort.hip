@@ -18,8 +18,9 @@ namespace gm {
 
 constexpr int RS_THREADS = 256;
 constexpr int RS_WAVES = RS_THREADS / 64;
-constexpr int RS_ITEMS = 16;
-constexpr int RS_CHUNK = RS_THREADS * RS_ITEMS;  // keys per block
+constexpr int RS_ITEMS = 16;  // keys per thread of the pair sort (4096 per block)
+constexpr int DS_ITEMS = 8;   // of the depth sort: 2048 per block, about 490 blocks for 1M keys (4096 per
+                              // block left fewer blocks than CUs: 0.21 -> 0.19 ms; 1024: 0.206 ms)
 constexpr int RS_RADIX = 256;
 
 __global__ void k_sort_init(int32_t* __restrict__ ranges, int64_t n2, long long* __restrict__ n_keys)
@@ -40,7 +41,7 @@ __device__ inline long long live_count(const long long* __restrict__ d_count, lo
 // ---------------------------------------------------------------------------
 // stable LSD radix sort pass over a digit of BITS <= 8 bits
 // ---------------------------------------------------------------------------
-template <int BITS, typename KT>
+template <int BITS, typename KT, int ITEMS>
 __global__ void __launch_bounds__(RS_THREADS)
 k_radix_hist(const KT* __restrict__ keys, const long long* __restrict__ d_count, long long n_max,
              int shift, int nblocks, int32_t* __restrict__ hist)
@@ -52,13 +53,14 @@ k_radix_hist(const KT* __restrict__ keys, const long long* __restrict__ d_count,
 #pragma unroll
     for (int w = 0; w < RS_WAVES; ++w) h[w][threadIdx.x] = 0;
     __syncthreads();
-    // thread t counts the RS_ITEMS consecutive keys from e0, read with 16-byte loads
-    // (keys are 256-byte aligned and e0 is a multiple of RS_ITEMS): all of a block's
+    // thread t counts the ITEMS consecutive keys from e0, read with 16-byte loads
+    // (keys are 256-byte aligned and e0 is a multiple of ITEMS): all of a block's
     // loads are in flight together, where one key per load left it latency-bound
-    const long long e0 = (long long)blockIdx.x * RS_CHUNK + (long long)threadIdx.x * RS_ITEMS;
-    if (e0 + RS_ITEMS <= n) {
-        static_assert(RS_ITEMS * sizeof(KT) % 16 == 0, "whole 16-byte loads per thread");
-        constexpr int NV = RS_ITEMS * (int)sizeof(KT) / 16;
+    constexpr int CHUNK = RS_THREADS * ITEMS;
+    const long long e0 = (long long)blockIdx.x * CHUNK + (long long)threadIdx.x * ITEMS;
+    if (e0 + ITEMS <= n) {
+        static_assert(ITEMS * sizeof(KT) % 16 == 0, "whole 16-byte loads per thread");
+        constexpr int NV = ITEMS * (int)sizeof(KT) / 16;
         constexpr int PER = 16 / (int)sizeof(KT);  // keys per 16-byte load
         uint4 q[NV];
         const uint4* src = reinterpret_cast<const uint4*>(keys + e0);
@@ -74,7 +76,7 @@ k_radix_hist(const KT* __restrict__ keys, const long long* __restrict__ d_count,
             }
         }
     } else {
-        for (int k = 0; k < RS_ITEMS; ++k)
+        for (int k = 0; k < ITEMS; ++k)
             if (e0 + k < n) atomicAdd(&h[wave][((uint32_t)keys[e0 + k] >> shift) & (R - 1)], 1);
     }
     __syncthreads();
@@ -86,21 +88,23 @@ k_radix_hist(const KT* __restrict__ keys, const long long* __restrict__ d_count,
     }
 }
 
-// Stable scatter of one LSD pass over a block of RS_CHUNK keys.  Wave w ranks its
-// own 1024 consecutive keys in 16 rounds of 64 without block barriers: 8 ballots
+// Stable scatter of one LSD pass over a block of RS_THREADS * ITEMS keys.  Wave w
+// ranks its own 64 * ITEMS consecutive keys in ITEMS rounds of 64 without block
+// barriers: BITS ballots
 // give each lane the lanes holding the same digit, and a per-wave running count per
 // digit in LDS carries the rank across rounds (a wave's LDS operations complete in
 // program order).  One block scan then turns the per-wave counts into bases, keys
 // are placed in LDS in digit order, and each digit's run leaves the block as
 // contiguous stores.
-template <int BITS, typename KT>
+template <int BITS, typename KT, int ITEMS>
 __global__ void __launch_bounds__(RS_THREADS)
 k_radix_scatter(const KT* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
                 const long long* __restrict__ d_count, long long n_max, int shift, int nblocks,
                 const int32_t* __restrict__ offs, KT* __restrict__ keys_out, int32_t* __restrict__ vals_out)
 {
-    __shared__ KT s_k[RS_CHUNK];
-    __shared__ int32_t s_v[RS_CHUNK];
+    constexpr int CHUNK = RS_THREADS * ITEMS;
+    __shared__ KT s_k[CHUNK];
+    __shared__ int32_t s_v[CHUNK];
     __shared__ int32_t s_wc[RS_WAVES][RS_RADIX];  // running counts per wave, then per-wave bases
     __shared__ int32_t s_lstart[RS_RADIX], s_goff[RS_RADIX];
     __shared__ int32_t s_wsum[RS_WAVES];
@@ -108,25 +112,25 @@ k_radix_scatter(const KT* __restrict__ keys_in, const int32_t* __restrict__ vals
     const long long n = live_count(d_count, n_max);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const unsigned long long lt = (1ull << lane) - 1ull;
-    const long long base = (long long)blockIdx.x * RS_CHUNK;
+    const long long base = (long long)blockIdx.x * CHUNK;
     if (base >= n) return;
 #pragma unroll
     for (int w = 0; w < RS_WAVES; ++w) s_wc[w][t] = 0;
     if (t < R) s_goff[t] = offs[t * nblocks + blockIdx.x];
     __syncthreads();
-    uint32_t key[RS_ITEMS];  // KT widened
-    int32_t val[RS_ITEMS];
-    int rank[RS_ITEMS];
-    const long long wbase = base + (long long)wave * (RS_CHUNK / RS_WAVES);
+    uint32_t key[ITEMS];  // KT widened
+    int32_t val[ITEMS];
+    int rank[ITEMS];
+    const long long wbase = base + (long long)wave * (CHUNK / RS_WAVES);
 #pragma unroll
-    for (int r = 0; r < RS_ITEMS; ++r) {
+    for (int r = 0; r < ITEMS; ++r) {
         const long long e = wbase + r * 64 + lane;
         const bool act = e < n;
         key[r] = act ? keys_in[e] : 0u;
         val[r] = act ? vals_in[e] : 0;
     }
 #pragma unroll
-    for (int r = 0; r < RS_ITEMS; ++r) {
+    for (int r = 0; r < ITEMS; ++r) {
         const bool act = wbase + r * 64 + lane < n;
         const int d = (key[r] >> shift) & (R - 1);
         unsigned long long peers = __ballot(act);
@@ -169,7 +173,7 @@ k_radix_scatter(const KT* __restrict__ keys_in, const int32_t* __restrict__ vals
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < RS_ITEMS; ++r) {
+    for (int r = 0; r < ITEMS; ++r) {
         if (wbase + r * 64 + lane < n) {
             const int pos = s_wc[wave][(key[r] >> shift) & (R - 1)] + rank[r];
             s_k[pos] = (KT)key[r];
@@ -177,7 +181,7 @@ k_radix_scatter(const KT* __restrict__ keys_in, const int32_t* __restrict__ vals
         }
     }
     __syncthreads();
-    const int nvalid = (int)min((long long)RS_CHUNK, n - base);
+    const int nvalid = (int)min((long long)CHUNK, n - base);
     for (int p = t; p < nvalid; p += RS_THREADS) {
         const KT k = s_k[p];
         const int d = (k >> shift) & (R - 1);
@@ -189,31 +193,32 @@ k_radix_scatter(const KT* __restrict__ keys_in, const int32_t* __restrict__ vals
 
 static int radix_passes(int nbits) { return nbits <= 0 ? 1 : (nbits + 7) / 8; }
 
-size_t radix_ws_bytes(int64_t n)
+size_t radix_ws_bytes(int64_t n, int items)
 {
-    const int64_t nb = div_up(n > 0 ? n : 1, RS_CHUNK);
+    const int64_t nb = div_up(n > 0 ? n : 1, (int64_t)RS_THREADS * items);
     return 2 * align_up(sizeof(int32_t) * (size_t)(RS_RADIX * nb + 1), 256) + scan_ws_bytes(RS_RADIX * nb) +
            align_up(sizeof(long long), 256);
 }
 
-template <int BITS, typename KT>
+template <int BITS, typename KT, int ITEMS>
 static gm_status radix_pass(const KT* kin, const int32_t* vin, KT* kout, int32_t* vout, int shift,
                             const long long* d_count, int64_t n_max, int nb, int32_t* hist, int32_t* offs,
                             long long* tot, void* scan_ws, hipStream_t stream)
 {
-    k_radix_hist<BITS, KT><<<nb, RS_THREADS, 0, stream>>>(kin, d_count, n_max, shift, nb, hist);
+    k_radix_hist<BITS, KT, ITEMS><<<nb, RS_THREADS, 0, stream>>>(kin, d_count, n_max, shift, nb, hist);
     GM_LAUNCH_CHECK();
     if (gm_status s = exclusive_scan(hist, offs, (int64_t)(1 << BITS) * nb, tot, scan_ws, stream)) return s;
-    k_radix_scatter<BITS, KT><<<nb, RS_THREADS, 0, stream>>>(kin, vin, d_count, n_max, shift, nb, offs, kout, vout);
+    k_radix_scatter<BITS, KT, ITEMS><<<nb, RS_THREADS, 0, stream>>>(kin, vin, d_count, n_max, shift, nb, offs, kout,
+                                                                     vout);
     GM_LAUNCH_CHECK();
     return GM_OK;
 }
 
 // Offsets ([digit][block], exclusive) of the last pass of a radix sort over at most
-// n_max keys, where radix_sort leaves them in its workspace.
-static int32_t* radix_last_offsets(void* ws, int64_t n_max)
+// n_max keys, `items` per thread, where radix_sort leaves them in its workspace.
+static int32_t* radix_last_offsets(void* ws, int64_t n_max, int items)
 {
-    const int64_t nb = div_up(n_max > 0 ? n_max : 1, RS_CHUNK);
+    const int64_t nb = div_up(n_max > 0 ? n_max : 1, (int64_t)RS_THREADS * items);
     return (int32_t*)((char*)ws + align_up(sizeof(int32_t) * (size_t)(RS_RADIX * nb + 1), 256));
 }
 
@@ -223,14 +228,14 @@ static int32_t* radix_last_offsets(void* ws, int64_t n_max)
 // (device), zero when above n_max.  Ping-pongs between (ka, va) and (kb, vb): an even
 // number of passes ends in (ka, va), an odd one in (kb, vb).  The last pass's
 // offsets stay in ws (radix_last_offsets) until the workspace is used again.
-template <typename KT>
+template <typename KT, int ITEMS>
 static gm_status radix_sort(KT* ka, int32_t* va, KT* kb, int32_t* vb, int nbits,
                             const long long* d_count, int64_t n_max, void* ws, hipStream_t stream)
 {
-    const int nb = (int)div_up(n_max > 0 ? n_max : 1, RS_CHUNK);
+    const int nb = (int)div_up(n_max > 0 ? n_max : 1, (int64_t)RS_THREADS * ITEMS);
     char* w = (char*)ws;
     int32_t* hist = (int32_t*)w;
-    int32_t* offs = radix_last_offsets(ws, n_max);
+    int32_t* offs = radix_last_offsets(ws, n_max, ITEMS);
     w = (char*)offs + align_up(sizeof(int32_t) * (size_t)(RS_RADIX * nb + 1), 256);
     long long* tot = (long long*)w;
     w += align_up(sizeof(long long), 256);
@@ -245,14 +250,14 @@ static gm_status radix_sort(KT* ka, int32_t* va, KT* kb, int32_t* vb, int nbits,
         const int bits = (nbits - shift + (npass - p) - 1) / (npass - p);  // ceil(remaining / passes left)
         gm_status s = GM_OK;
         switch (bits) {
-        case 1: s = radix_pass<1, KT>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        case 2: s = radix_pass<2, KT>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        case 3: s = radix_pass<3, KT>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        case 4: s = radix_pass<4, KT>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        case 5: s = radix_pass<5, KT>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        case 6: s = radix_pass<6, KT>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        case 7: s = radix_pass<7, KT>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        default: s = radix_pass<8, KT>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 1: s = radix_pass<1, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 2: s = radix_pass<2, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 3: s = radix_pass<3, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 4: s = radix_pass<4, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 5: s = radix_pass<5, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 6: s = radix_pass<6, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 7: s = radix_pass<7, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        default: s = radix_pass<8, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
         }
         if (s) return s;
         shift += bits;
@@ -599,7 +604,7 @@ static size_t sort_layout(int64_t N, int64_t cap, int64_t T, char* base, SortWs*
     s.n = (long long*)take(8);
     const int64_t m = std::max<int64_t>(std::max<int64_t>(n1, c1), T);
     s.scan = take(scan_ws_bytes(nch));
-    s.aux = take(radix_ws_bytes(m));
+    s.aux = take(std::max(radix_ws_bytes(n1, DS_ITEMS), radix_ws_bytes(m, RS_ITEMS)));
     if (w) *w = s;
     return o;
 }
@@ -628,7 +633,7 @@ static gm_status sort_depth(const DevCamera& dc, int32_t N, const float* rec, co
     if (N == 0) return GM_OK;
     k_depth_keys<<<(unsigned)div_up(N, 256), 256, 0, stream>>>(N, rec, w.dka, w.dva, w.n);
     GM_LAUNCH_CHECK();
-    return radix_sort(w.dka, w.dva, w.dkb, w.dvb, 32, w.n, N, w.aux, stream);
+    return radix_sort<uint32_t, DS_ITEMS>(w.dka, w.dva, w.dkb, w.dvb, 32, w.n, N, w.aux, stream);
 }
 
 // Emission of the (tile, id) pairs with tile keys of type KT, their stable sort by
@@ -649,7 +654,7 @@ static gm_status emit_and_sort(const DevCamera& dc, const CullParams& cp, const 
     k_pairs<true, false, KT><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, d_nvis, nchunks, order, rec, nullptr, w.off,
                                                                w.bits, total, kcap, ka, va, nullptr, 0);
     GM_LAUNCH_CHECK();
-    if (gm_status s = radix_sort<KT>(ka, va, kb, vb, tbits, total, kcap, w.aux, stream)) return s;
+    if (gm_status s = radix_sort<KT, RS_ITEMS>(ka, va, kb, vb, tbits, total, kcap, w.aux, stream)) return s;
     const KT* kfin = (npass % 2 == 0) ? ka : kb;
     k_tile_ranges<KT><<<(unsigned)div_up(div_up(kcap, TR_KEYS), 256), 256, 0, stream>>>(kfin, total, kcap,
                                                                                         tile_ranges);
@@ -672,7 +677,8 @@ static gm_status sort_tiles(const DevCamera& dc, int32_t N, const float* rec, co
     const int32_t* order = w.dva;  // 4 passes: back in the first buffer pair
     // number of listed Gaussians = offset of top byte 0xff in the depth sort's last
     // pass, block 0; valid until the tile sort below reuses the histogram buffers
-    const int32_t* d_nvis = radix_last_offsets(w.aux, N) + (size_t)(RS_RADIX - 1) * div_up(N, RS_CHUNK);
+    const int32_t* d_nvis = radix_last_offsets(w.aux, N, DS_ITEMS) +
+                            (size_t)(RS_RADIX - 1) * div_up(N, (int64_t)RS_THREADS * DS_ITEMS);
     const bool lds = tile_dmax && T <= PW_LDS_MAX_TILES;
     CullParams cp{tile_dmax, softness};
     const size_t shm = lds ? sizeof(float) * (size_t)T : 0;
