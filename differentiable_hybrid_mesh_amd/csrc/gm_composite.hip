@@ -21,7 +21,7 @@
 namespace gm {
 
 constexpr int CT = 256;     // threads per block = pixels per tile
-constexpr int CB = 256;     // records per LDS batch
+constexpr int CBF = 256;    // records per LDS batch of the forward (<= CT, a multiple of 64)
 constexpr int CBB = 192;    // records per LDS batch of the backward (<= CT, a multiple of 32): 24 KB of
                             // LDS per block, six blocks per CU (five at 256: 0.550 -> 0.509 ms at C3)
 constexpr float SKIP_ALPHA = 1.0f / 255.0f;
@@ -436,8 +436,8 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, const float* _
                 float* __restrict__ out_rgb, float* __restrict__ out_depth, float* __restrict__ out_alpha,
                 float* __restrict__ state_T, int32_t* __restrict__ state_last, float* __restrict__ state_aa)
 {
-    __shared__ Staged s_g[CB];
-    __shared__ uint8_t s_m[CB];
+    __shared__ Staged s_g[CBF];
+    __shared__ uint8_t s_m[CBF];
     __shared__ float s_wd[CT / 64];
     const int tile = blockIdx.x;
     const int tx = tile % P.cam.tx, ty = tile / P.cam.tx;
@@ -474,15 +474,18 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, const float* _
     bool doneB = true;
     if constexpr (AA) doneB = !(inside && on && ml.am < 1.0f);
     float4 ra, rb, rc, rd;
-    if (start + (int)threadIdx.x < end) load_record(P.rec, P.ids[start + threadIdx.x], ra, rb, rc, rd);
-    for (int b0 = start; b0 < end; b0 += CB) {
+    if ((int)threadIdx.x < CBF && start + (int)threadIdx.x < end)
+        load_record(P.rec, P.ids[start + threadIdx.x], ra, rb, rc, rd);
+    for (int b0 = start; b0 < end; b0 += CBF) {
         if (__syncthreads_count(done & doneB) == CT) break;
-        const int nb = min(CB, end - b0);
-        s_m[threadIdx.x] = threadIdx.x < nb ? (uint8_t)stage_record(P, ra, rb, rc, rd, tx, ty, s_wd, s_g[threadIdx.x]) : 0;
-        if (b0 + CB + (int)threadIdx.x < end) load_record(P.rec, P.ids[b0 + CB + threadIdx.x], ra, rb, rc, rd);
+        const int nb = min(CBF, end - b0);
+        if ((int)threadIdx.x < CBF)
+            s_m[threadIdx.x] = (int)threadIdx.x < nb ? (uint8_t)stage_record(P, ra, rb, rc, rd, tx, ty, s_wd, s_g[threadIdx.x]) : 0;
+        if ((int)threadIdx.x < CBF && b0 + CBF + (int)threadIdx.x < end)
+            load_record(P.rec, P.ids[b0 + CBF + threadIdx.x], ra, rb, rc, rd);
         __syncthreads();
         bool wdone = __ballot(!(done & doneB)) == 0;
-        for (int i = 0; i < CB / 64 && !wdone; ++i) {
+        for (int i = 0; i < CBF / 64 && !wdone; ++i) {
             unsigned long long m = __ballot((s_m[i * 64 + lane] >> wave) & 1);
             while (m) {
                 const int k = i * 64 + __builtin_ctzll(m);
