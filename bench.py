@@ -136,7 +136,7 @@ def measured_step_traffic(config):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only (the renderer has no multi-GPU path); "
+        print("bench.py: measures one GPU only (the renderer has no multi-GPU path); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
