@@ -487,11 +487,9 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, const float* _
         bool wdone = __ballot(!(done & doneB)) == 0;
         for (int i = 0; i < CBF / 64 && !wdone; ++i) {
             unsigned long long m = __ballot((s_m[i * 64 + lane] >> wave) & 1);
-            while (m) {
-                const int k = i * 64 + __builtin_ctzll(m);
-                m &= m - 1;
-                const Staged g = s_g[k];  // one 64-byte LDS broadcast read
-                const Pair pr = eval_pair(g, pxc, pyc, on, wave_on, D, P.softness);
+            // two entries per iteration: their evaluations are independent of the
+            // pixel state, the compositing takes them in order
+            auto composite_entry = [&](const Staged& g, const Pair& pr, int k) {
                 const float aF = pr.aF;
                 const bool live = !done & pr.ok;
                 const float Tn = T * (1.0f - aF);
@@ -521,6 +519,19 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, const float* _
                     lastB = incB ? b0 + k - start + 1 : lastB;
                     doneB = doneB | stopB;
                 }
+            };
+            while (m) {
+                const int k = i * 64 + __builtin_ctzll(m);
+                m &= m - 1;
+                const bool two = m != 0;
+                const int k2 = two ? i * 64 + __builtin_ctzll(m) : k;
+                if (two) m &= m - 1;
+                const Staged g = s_g[k];  // one 64-byte LDS broadcast read
+                const Staged g2 = s_g[k2];
+                const Pair pr = eval_pair(g, pxc, pyc, on, wave_on, D, P.softness);
+                const Pair pr2 = eval_pair(g2, pxc, pyc, on, wave_on, D, P.softness);
+                composite_entry(g, pr, k);
+                if (two) composite_entry(g2, pr2, k2);
                 if (__ballot(!(done & doneB)) == 0) {
                     wdone = true;
                     break;
