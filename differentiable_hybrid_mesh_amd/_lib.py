@@ -1,8 +1,11 @@
 """ctypes binding of libgm.so (include/gm.h): same names, argument marshalling only.
 
-Every array argument is a torch tensor on the GPU (or None); the binding passes its
-data pointer.  No computation happens here.  Importing this module does not touch
-the GPU; ``lib()`` raises if libgm.so has not been built.
+Every array argument is a torch tensor on the GPU (or None where the C call takes
+NULL); the binding checks that each one is a contiguous tensor of the expected dtype
+on the current GPU holding at least the elements the call reads or writes (exactly
+that many for per-pixel images), raises ValueError before anything is launched
+otherwise, and passes its data pointer.  No computation happens here.  Importing
+this module does not touch the GPU; ``lib()`` raises if libgm.so has not been built.
 """
 from __future__ import annotations
 
@@ -125,6 +128,65 @@ def ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
+F32, I32, I64, U8 = "float32", "int32", "int64", "uint8"
+
+
+def dev(t, name: str, dtype: str, n: int, exact: bool = False, optional: bool = False) -> Optional[int]:
+    """Data pointer of tensor ``t`` after checking it: a contiguous torch tensor of
+    ``dtype`` on the current GPU with at least ``n`` elements (exactly ``n`` when
+    ``exact``); None passes NULL when ``optional``.  Raises ValueError otherwise, so a
+    host tensor, a wrongly typed or permuted one, or one too small never reaches a
+    kernel."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name}: a tensor is required")
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: tensor is on {t.device}, a GPU tensor is required")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name}: tensor is on {t.device}, the current device is cuda:{torch.cuda.current_device()}")
+    if t.dtype is not getattr(torch, dtype):
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: tensor is not contiguous (shape {tuple(t.shape)}, strides {t.stride()})")
+    if exact and t.numel() != n:
+        raise ValueError(f"{name}: {t.numel()} elements, expected exactly {n} (shape {tuple(t.shape)})")
+    if t.numel() < n:
+        raise ValueError(f"{name}: {t.numel()} elements, at least {n} needed")
+    return t.data_ptr()
+
+
+def _ws(t, need: int, name: str = "ws"):
+    """Pointer and byte size of a workspace tensor of at least ``need`` bytes."""
+    p = dev(t, name, U8, need)
+    return p, t.numel()
+
+
+def _tiles(cam) -> int:
+    return ((cam.width + GM_TILE - 1) // GM_TILE) * ((cam.height + GM_TILE - 1) // GM_TILE)
+
+
+def _hw(cam) -> int:
+    return cam.width * cam.height
+
+
+def _sh_planes(sh_degree: int) -> int:
+    return 1 if sh_degree < 0 else (sh_degree + 1) ** 2
+
+
+def img(t, name: str, cam, k: int, dtype: str = F32, optional: bool = False) -> Optional[int]:
+    """dev() for a per-pixel image of ``k`` values per pixel: exactly H*W*k elements
+    and, when it has more than one dimension, shape (H, W) (k = 1) or (H, W, k)."""
+    if t is not None and getattr(t, "dim", None) is not None and t.dim() > 1:
+        want = (cam.height, cam.width) if k == 1 else (cam.height, cam.width, k)
+        if tuple(t.shape) != want:
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {want}")
+    return dev(t, name, dtype, cam.width * cam.height * k, exact=True, optional=optional)
+
+
 def check(status: int):
     if status != GM_OK:
         raise GmError(status, lib().gm_last_error().decode(errors="replace"))
@@ -141,9 +203,11 @@ def gm_bin_triangles_ws(V, F, width, height) -> int:
 
 def gm_bin_triangles(cam, mesh, vscreen, tile_offsets, tile_tris, cap, n_pairs, ws, stream):
     """n_pairs: device int64 tensor that receives the pair count (asynchronously)."""
-    check(lib().gm_bin_triangles(C.byref(cam), C.byref(mesh), ptr(vscreen), ptr(tile_offsets),
-                                 ptr(tile_tris), int(cap), ptr(n_pairs), ptr(ws),
-                                 0 if ws is None else ws.numel() * ws.element_size(), stream))
+    wp, wb = _ws(ws, gm_bin_triangles_ws(mesh.V, mesh.F, cam.width, cam.height))
+    check(lib().gm_bin_triangles(C.byref(cam), C.byref(mesh), dev(vscreen, "vscreen", F32, 3 * mesh.V),
+                                 dev(tile_offsets, "tile_offsets", I32, _tiles(cam) + 1),
+                                 dev(tile_tris, "tile_tris", I32, int(cap), optional=int(cap) == 0), int(cap),
+                                 dev(n_pairs, "n_pairs", I64, 1), wp, wb, stream))
 
 
 def gm_raster_zbuffer_ws(width, height) -> int:
@@ -151,102 +215,167 @@ def gm_raster_zbuffer_ws(width, height) -> int:
 
 
 def gm_raster_zbuffer(cam, mesh, vscreen, tile_offsets, tile_tris, face_id, depth, tile_dmax, ws, stream):
-    check(lib().gm_raster_zbuffer(C.byref(cam), C.byref(mesh), ptr(vscreen), ptr(tile_offsets),
-                                  ptr(tile_tris), ptr(face_id), ptr(depth), ptr(tile_dmax), ptr(ws),
-                                  0 if ws is None else ws.numel() * ws.element_size(), stream))
+    wp, wb = _ws(ws, gm_raster_zbuffer_ws(cam.width, cam.height))
+    check(lib().gm_raster_zbuffer(C.byref(cam), C.byref(mesh), dev(vscreen, "vscreen", F32, 3 * mesh.V),
+                                  dev(tile_offsets, "tile_offsets", I32, _tiles(cam) + 1),
+                                  dev(tile_tris, "tile_tris", I32, 0, optional=True),
+                                  img(face_id, "face_id", cam, 1, I32), img(depth, "depth", cam, 1),
+                                  dev(tile_dmax, "tile_dmax", F32, _tiles(cam)), wp, wb, stream))
+
+
+def _gauss_in(N, means, quats, scales, opacity, sh, sh_degree):
+    n = int(N)
+    return (dev(means, "means", F32, 3 * n), dev(quats, "quats", F32, 4 * n), dev(scales, "scales", F32, 3 * n),
+            dev(opacity, "opacity", F32, n), dev(sh, "sh", F32, 3 * _sh_planes(int(sh_degree)) * n))
 
 
 def gm_project_gaussians(cam, N, means, quats, scales, opacity, sh, sh_degree, rec, stream):
-    check(lib().gm_project_gaussians(C.byref(cam), int(N), ptr(means), ptr(quats), ptr(scales),
-                                     ptr(opacity), ptr(sh), int(sh_degree), ptr(rec), stream))
+    check(lib().gm_project_gaussians(C.byref(cam), int(N), *_gauss_in(N, means, quats, scales, opacity, sh, sh_degree),
+                                     int(sh_degree), dev(rec, "rec", F32, GM_REC * int(N)), stream))
 
 
 def gm_project_gaussians_multi(cams, N, means, quats, scales, opacity, sh, sh_degree, rec, stream):
     """cams: sequence of GmCamera; rec holds len(cams) * N records."""
     arr = (GmCamera * max(len(cams), 1))(*cams)
-    check(lib().gm_project_gaussians_multi(arr, len(cams), int(N), ptr(means), ptr(quats), ptr(scales),
-                                           ptr(opacity), ptr(sh), int(sh_degree), ptr(rec), stream))
+    check(lib().gm_project_gaussians_multi(arr, len(cams), int(N),
+                                           *_gauss_in(N, means, quats, scales, opacity, sh, sh_degree),
+                                           int(sh_degree), dev(rec, "rec", F32, GM_REC * int(N) * len(cams)),
+                                           stream))
 
 
 def gm_sort_tile_keys_ws(N, cap, width, height) -> int:
     return lib().gm_sort_tile_keys_ws(int(N), int(cap), width, height)
 
 
+def _sort_common(cam, N, rec, cap, ws):
+    wp, wb = _ws(ws, gm_sort_tile_keys_ws(N, cap, cam.width, cam.height))
+    return dev(rec, "rec", F32, GM_REC * int(N), optional=int(N) == 0), wp, wb
+
+
 def gm_sort_tile_keys(cam, N, rec, tile_dmax, softness, tile_ranges, sorted_ids, cap, n_keys, ws, stream):
     """n_keys: device int64 tensor that receives the key count (asynchronously)."""
-    check(lib().gm_sort_tile_keys(C.byref(cam), int(N), ptr(rec), ptr(tile_dmax), float(softness),
-                                  ptr(tile_ranges), ptr(sorted_ids), int(cap), ptr(n_keys), ptr(ws),
-                                  0 if ws is None else ws.numel() * ws.element_size(), stream))
+    rp, wp, wb = _sort_common(cam, N, rec, cap, ws)
+    check(lib().gm_sort_tile_keys(C.byref(cam), int(N), rp,
+                                  dev(tile_dmax, "tile_dmax", F32, _tiles(cam), optional=True), float(softness),
+                                  dev(tile_ranges, "tile_ranges", I32, 2 * _tiles(cam)),
+                                  dev(sorted_ids, "sorted_ids", I32, int(cap), optional=int(cap) == 0), int(cap),
+                                  dev(n_keys, "n_keys", I64, 1), wp, wb, stream))
 
 
 def gm_sort_depth(cam, N, rec, cap, ws, stream):
     """First half of gm_sort_tile_keys: the depth order, kept in ws for gm_sort_tiles."""
-    check(lib().gm_sort_depth(C.byref(cam), int(N), ptr(rec), int(cap), ptr(ws),
-                              0 if ws is None else ws.numel() * ws.element_size(), stream))
+    rp, wp, wb = _sort_common(cam, N, rec, cap, ws)
+    check(lib().gm_sort_depth(C.byref(cam), int(N), rp, int(cap), wp, wb, stream))
 
 
 def gm_sort_tiles(cam, N, rec, tile_dmax, softness, tile_ranges, sorted_ids, cap, n_keys, ws, stream):
     """Second half of gm_sort_tile_keys, ordered after gm_sort_depth on the same ws."""
-    check(lib().gm_sort_tiles(C.byref(cam), int(N), ptr(rec), ptr(tile_dmax), float(softness),
-                              ptr(tile_ranges), ptr(sorted_ids), int(cap), ptr(n_keys), ptr(ws),
-                              0 if ws is None else ws.numel() * ws.element_size(), stream))
+    rp, wp, wb = _sort_common(cam, N, rec, cap, ws)
+    check(lib().gm_sort_tiles(C.byref(cam), int(N), rp, dev(tile_dmax, "tile_dmax", F32, _tiles(cam), optional=True),
+                              float(softness), dev(tile_ranges, "tile_ranges", I32, 2 * _tiles(cam)),
+                              dev(sorted_ids, "sorted_ids", I32, int(cap), optional=int(cap) == 0), int(cap),
+                              dev(n_keys, "n_keys", I64, 1), wp, wb, stream))
 
 
 def _light_ref(light):
     return None if light is None else C.byref(light)
 
 
+def _bg(bg):
+    vals = [float(x) for x in bg]
+    if len(vals) != 3:
+        raise ValueError(f"bg: 3 values expected, got {len(vals)}")
+    return (C.c_float * 3)(*vals)
+
+
+def _lists(cam, rec, tile_ranges, sorted_ids):
+    # rec and sorted_ids: the kernels read the entries the tile ranges name, which
+    # were written by the sort for these buffers; only their type and place are checked
+    return (dev(rec, "rec", F32, 0), dev(tile_ranges, "tile_ranges", I32, 2 * _tiles(cam)),
+            dev(sorted_ids, "sorted_ids", I32, 0))
+
+
+def _fwd_out(cam, out_rgb, out_depth, out_alpha, state_T, state_last):
+    return (img(out_rgb, "out_rgb", cam, 3), img(out_depth, "out_depth", cam, 1),
+            img(out_alpha, "out_alpha", cam, 1), img(state_T, "state_T", cam, 1),
+            img(state_last, "state_last", cam, 1, I32))
+
+
 def gm_composite_hybrid_fwd(cam, rec, tile_ranges, sorted_ids, face_id, depth, mesh, vscreen, light, bg,
                             softness, out_rgb, out_depth, out_alpha, state_T, state_last, state_cm, stream):
-    bgv = (C.c_float * 3)(*[float(x) for x in bg])
-    check(lib().gm_composite_hybrid_fwd(C.byref(cam), ptr(rec), ptr(tile_ranges), ptr(sorted_ids),
-                                        ptr(face_id), ptr(depth), C.byref(mesh), ptr(vscreen),
+    bgv = _bg(bg)
+    check(lib().gm_composite_hybrid_fwd(C.byref(cam), *_lists(cam, rec, tile_ranges, sorted_ids),
+                                        img(face_id, "face_id", cam, 1, I32), img(depth, "depth", cam, 1),
+                                        C.byref(mesh), dev(vscreen, "vscreen", F32, 3 * mesh.V, optional=mesh.F == 0),
                                         _light_ref(light), C.cast(bgv, C.c_void_p), float(softness),
-                                        ptr(out_rgb), ptr(out_depth), ptr(out_alpha), ptr(state_T),
-                                        ptr(state_last), ptr(state_cm), stream))
+                                        *_fwd_out(cam, out_rgb, out_depth, out_alpha, state_T, state_last),
+                                        img(state_cm, "state_cm", cam, 3), stream))
 
 
 def gm_shade_surface(cam, face_id, mesh, vscreen, light, bg, state_cm, stream):
-    bgv = (C.c_float * 3)(*[float(x) for x in bg])
-    check(lib().gm_shade_surface(C.byref(cam), ptr(face_id), C.byref(mesh), ptr(vscreen), _light_ref(light),
-                                 C.cast(bgv, C.c_void_p), ptr(state_cm), stream))
+    bgv = _bg(bg)
+    check(lib().gm_shade_surface(C.byref(cam), img(face_id, "face_id", cam, 1, I32), C.byref(mesh),
+                                 dev(vscreen, "vscreen", F32, 3 * mesh.V, optional=mesh.F == 0), _light_ref(light),
+                                 C.cast(bgv, C.c_void_p), img(state_cm, "state_cm", cam, 3), stream))
 
 
 def gm_composite_hybrid_fwd_shaded(cam, rec, tile_ranges, sorted_ids, face_id, depth, softness, state_cm, out_rgb,
                                    out_depth, out_alpha, state_T, state_last, stream):
-    check(lib().gm_composite_hybrid_fwd_shaded(C.byref(cam), ptr(rec), ptr(tile_ranges), ptr(sorted_ids),
-                                               ptr(face_id), ptr(depth), float(softness), ptr(state_cm),
-                                               ptr(out_rgb), ptr(out_depth), ptr(out_alpha), ptr(state_T),
-                                               ptr(state_last), stream))
+    check(lib().gm_composite_hybrid_fwd_shaded(C.byref(cam), *_lists(cam, rec, tile_ranges, sorted_ids),
+                                               img(face_id, "face_id", cam, 1, I32), img(depth, "depth", cam, 1),
+                                               float(softness), img(state_cm, "state_cm", cam, 3),
+                                               *_fwd_out(cam, out_rgb, out_depth, out_alpha, state_T, state_last),
+                                               stream))
 
 
 def gm_composite_hybrid_bwd_ws(width, height) -> int:
     return lib().gm_composite_hybrid_bwd_ws(int(width), int(height))
 
 
+def _bwd_args(cam, N, rec, tile_ranges, sorted_ids, face_id, depth, softness, state_T, state_last, state_cm, g_rgb,
+              g_depth, g_alpha, g_rec, g_mesh_rgb, g_mesh_depth):
+    return (C.byref(cam), int(N), *_lists(cam, rec, tile_ranges, sorted_ids), img(face_id, "face_id", cam, 1, I32),
+            img(depth, "depth", cam, 1), float(softness), img(state_T, "state_T", cam, 1),
+            img(state_last, "state_last", cam, 1, I32), img(state_cm, "state_cm", cam, 3), img(g_rgb, "g_rgb", cam, 3),
+            img(g_depth, "g_depth", cam, 1, optional=True), img(g_alpha, "g_alpha", cam, 1, optional=True),
+            dev(g_rec, "g_rec", F32, GM_GRAD * int(N), optional=int(N) == 0),
+            img(g_mesh_rgb, "g_mesh_rgb", cam, 3, optional=True), img(g_mesh_depth, "g_mesh_depth", cam, 1, optional=True))
+
+
 def gm_composite_hybrid_bwd(cam, N, rec, tile_ranges, sorted_ids, face_id, depth, softness, state_T, state_last,
                             state_cm, g_rgb, g_depth, g_alpha, g_rec, g_mesh_rgb, g_mesh_depth, ws, stream):
     """ws: device scratch of gm_composite_hybrid_bwd_ws(width, height) bytes."""
-    check(lib().gm_composite_hybrid_bwd(C.byref(cam), int(N), ptr(rec), ptr(tile_ranges), ptr(sorted_ids),
-                                        ptr(face_id), ptr(depth), float(softness), ptr(state_T),
-                                        ptr(state_last), ptr(state_cm), ptr(g_rgb), ptr(g_depth),
-                                        ptr(g_alpha), ptr(g_rec), ptr(g_mesh_rgb), ptr(g_mesh_depth), ptr(ws),
-                                        0 if ws is None else ws.numel() * ws.element_size(), stream))
+    wp, wb = _ws(ws, gm_composite_hybrid_bwd_ws(cam.width, cam.height))
+    check(lib().gm_composite_hybrid_bwd(*_bwd_args(cam, N, rec, tile_ranges, sorted_ids, face_id, depth, softness,
+                                                   state_T, state_last, state_cm, g_rgb, g_depth, g_alpha, g_rec,
+                                                   g_mesh_rgb, g_mesh_depth), wp, wb, stream))
 
 
 def gm_project_gaussians_bwd(cam, N, means, quats, scales, opacity, sh, sh_degree, rec, g_rec, g_means, g_quats,
                              g_scales, g_opacity, g_sh, g_log_scales, g_logit_opacity, stream):
-    check(lib().gm_project_gaussians_bwd(C.byref(cam), int(N), ptr(means), ptr(quats), ptr(scales), ptr(opacity),
-                                         ptr(sh), int(sh_degree), ptr(rec), ptr(g_rec), ptr(g_means), ptr(g_quats),
-                                         ptr(g_scales), ptr(g_opacity), ptr(g_sh), ptr(g_log_scales),
-                                         ptr(g_logit_opacity), stream))
+    n, K = int(N), _sh_planes(int(sh_degree))
+    check(lib().gm_project_gaussians_bwd(C.byref(cam), n, *_gauss_in(N, means, quats, scales, opacity, sh, sh_degree),
+                                         int(sh_degree), dev(rec, "rec", F32, GM_REC * n),
+                                         dev(g_rec, "g_rec", F32, GM_GRAD * n), dev(g_means, "g_means", F32, 3 * n),
+                                         dev(g_quats, "g_quats", F32, 4 * n), dev(g_scales, "g_scales", F32, 3 * n),
+                                         dev(g_opacity, "g_opacity", F32, n), dev(g_sh, "g_sh", F32, 3 * K * n),
+                                         dev(g_log_scales, "g_log_scales", F32, 3 * n, optional=True),
+                                         dev(g_logit_opacity, "g_logit_opacity", F32, n, optional=True), stream))
 
 
 def gm_mesh_bwd(cam, mesh, light, face_id, g_mesh_rgb, g_mesh_depth, g_verts, g_vcolor, g_vnormal, g_uv, g_mips,
                 g_light, stream):
-    check(lib().gm_mesh_bwd(C.byref(cam), C.byref(mesh), _light_ref(light), ptr(face_id), ptr(g_mesh_rgb),
-                            ptr(g_mesh_depth), ptr(g_verts), ptr(g_vcolor), ptr(g_vnormal), ptr(g_uv), ptr(g_mips),
-                            ptr(g_light), stream))
+    V = mesh.V
+    check(lib().gm_mesh_bwd(C.byref(cam), C.byref(mesh), _light_ref(light), img(face_id, "face_id", cam, 1, I32),
+                            img(g_mesh_rgb, "g_mesh_rgb", cam, 3, optional=True),
+                            img(g_mesh_depth, "g_mesh_depth", cam, 1, optional=True),
+                            dev(g_verts, "g_verts", F32, 3 * V, optional=True),
+                            dev(g_vcolor, "g_vcolor", F32, 3 * V, optional=True),
+                            dev(g_vnormal, "g_vnormal", F32, 3 * V, optional=True),
+                            dev(g_uv, "g_uv", F32, 2 * mesh.Vt, optional=True),
+                            dev(g_mips, "g_mips", F32, gm_mipmaps_floats(mesh.tex_size) if mesh.tex_size else 0,
+                                optional=True),
+                            dev(g_light, "g_light", F32, 13, optional=True), stream))
 
 
 def gm_mipmaps_floats(S) -> int:
@@ -254,7 +383,8 @@ def gm_mipmaps_floats(S) -> int:
 
 
 def gm_build_mipmaps(tex, S, mips, stream):
-    check(lib().gm_build_mipmaps(ptr(tex), int(S), ptr(mips), stream))
+    check(lib().gm_build_mipmaps(dev(tex, "tex", F32, int(S) * int(S) * 3), int(S),
+                                 dev(mips, "mips", F32, gm_mipmaps_floats(S)), stream))
 
 
 def gm_version() -> int:
@@ -268,30 +398,38 @@ def gm_edge_adjacency_ws(F) -> int:
 
 
 def gm_edge_adjacency(mesh, adj, ws, stream):
-    check(lib().gm_edge_adjacency(C.byref(mesh), ptr(adj), ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-                                  stream))
+    wp, wb = _ws(ws, gm_edge_adjacency_ws(mesh.F))
+    check(lib().gm_edge_adjacency(C.byref(mesh), dev(adj, "adj", I32, 3 * mesh.F), wp, wb, stream))
 
 
 def gm_antialias(cam, mesh, vscreen, adj, light, face_id, depth, colour, layer, pairs, tile_dmax, stream):
-    check(lib().gm_antialias(C.byref(cam), C.byref(mesh), ptr(vscreen), ptr(adj), _light_ref(light), ptr(face_id),
-                             ptr(depth), ptr(colour), ptr(layer), ptr(pairs), ptr(tile_dmax), stream))
+    check(lib().gm_antialias(C.byref(cam), C.byref(mesh), dev(vscreen, "vscreen", F32, 3 * mesh.V),
+                             dev(adj, "adj", I32, 3 * mesh.F), _light_ref(light), img(face_id, "face_id", cam, 1, I32),
+                             img(depth, "depth", cam, 1), img(colour, "colour", cam, 3), img(layer, "layer", cam, 8),
+                             img(pairs, "pairs", cam, 12, optional=True),
+                             dev(tile_dmax, "tile_dmax", F32, _tiles(cam), optional=True), stream))
 
 
 def gm_composite_hybrid_fwd_aa(cam, rec, tile_ranges, sorted_ids, layer, bg, softness, out_rgb, out_depth, out_alpha,
                                state, stream):
-    bgv = (C.c_float * 3)(*[float(x) for x in bg])  # host array, alive for the call
-    check(lib().gm_composite_hybrid_fwd_aa(C.byref(cam), ptr(rec), ptr(tile_ranges), ptr(sorted_ids), ptr(layer),
-                                           C.cast(bgv, C.c_void_p), float(softness), ptr(out_rgb), ptr(out_depth),
-                                           ptr(out_alpha), ptr(state), stream))
+    bgv = _bg(bg)  # host array, alive for the call
+    check(lib().gm_composite_hybrid_fwd_aa(C.byref(cam), *_lists(cam, rec, tile_ranges, sorted_ids),
+                                           img(layer, "layer", cam, 8), C.cast(bgv, C.c_void_p), float(softness),
+                                           img(out_rgb, "out_rgb", cam, 3), img(out_depth, "out_depth", cam, 1),
+                                           img(out_alpha, "out_alpha", cam, 1), img(state, "state", cam, 8), stream))
 
 
 def gm_composite_hybrid_bwd_aa(cam, N, rec, tile_ranges, sorted_ids, layer, bg, softness, state, g_rgb, g_depth,
                                g_alpha, g_rec, g_layer, ws, stream):
-    bgv = (C.c_float * 3)(*[float(x) for x in bg])
-    check(lib().gm_composite_hybrid_bwd_aa(C.byref(cam), int(N), ptr(rec), ptr(tile_ranges), ptr(sorted_ids),
-                                           ptr(layer), C.cast(bgv, C.c_void_p), float(softness), ptr(state), ptr(g_rgb),
-                                           ptr(g_depth), ptr(g_alpha), ptr(g_rec), ptr(g_layer), ptr(ws),
-                                           0 if ws is None else ws.numel() * ws.element_size(), stream))
+    bgv = _bg(bg)
+    wp, wb = _ws(ws, gm_composite_hybrid_bwd_ws(cam.width, cam.height))
+    check(lib().gm_composite_hybrid_bwd_aa(C.byref(cam), int(N), *_lists(cam, rec, tile_ranges, sorted_ids),
+                                           img(layer, "layer", cam, 8), C.cast(bgv, C.c_void_p), float(softness),
+                                           img(state, "state", cam, 8), img(g_rgb, "g_rgb", cam, 3),
+                                           img(g_depth, "g_depth", cam, 1, optional=True),
+                                           img(g_alpha, "g_alpha", cam, 1, optional=True),
+                                           dev(g_rec, "g_rec", F32, GM_GRAD * int(N), optional=int(N) == 0),
+                                           img(g_layer, "g_layer", cam, 8), wp, wb, stream))
 
 
 def gm_antialias_bwd_ws(width, height) -> int:
@@ -300,10 +438,15 @@ def gm_antialias_bwd_ws(width, height) -> int:
 
 def gm_antialias_bwd(cam, mesh, vscreen, pairs, face_id, depth, colour, g_layer, g_mesh_rgb, g_mesh_depth, g_vscreen,
                      ws, stream):
-    check(lib().gm_antialias_bwd(C.byref(cam), C.byref(mesh), ptr(vscreen), ptr(pairs), ptr(face_id), ptr(depth),
-                                 ptr(colour), ptr(g_layer), ptr(g_mesh_rgb), ptr(g_mesh_depth), ptr(g_vscreen), ptr(ws),
-                                 0 if ws is None else ws.numel() * ws.element_size(), stream))
+    wp, wb = _ws(ws, gm_antialias_bwd_ws(cam.width, cam.height))
+    check(lib().gm_antialias_bwd(C.byref(cam), C.byref(mesh), dev(vscreen, "vscreen", F32, 3 * mesh.V),
+                                 img(pairs, "pairs", cam, 12), img(face_id, "face_id", cam, 1, I32),
+                                 img(depth, "depth", cam, 1), img(colour, "colour", cam, 3),
+                                 img(g_layer, "g_layer", cam, 8), img(g_mesh_rgb, "g_mesh_rgb", cam, 3, optional=True),
+                                 img(g_mesh_depth, "g_mesh_depth", cam, 1, optional=True),
+                                 dev(g_vscreen, "g_vscreen", F32, 2 * mesh.V), wp, wb, stream))
 
 
 def gm_vscreen_bwd(cam, mesh, g_vscreen, g_verts, stream):
-    check(lib().gm_vscreen_bwd(C.byref(cam), C.byref(mesh), ptr(g_vscreen), ptr(g_verts), stream))
+    check(lib().gm_vscreen_bwd(C.byref(cam), C.byref(mesh), dev(g_vscreen, "g_vscreen", F32, 2 * mesh.V),
+                               dev(g_verts, "g_verts", F32, 3 * mesh.V), stream))

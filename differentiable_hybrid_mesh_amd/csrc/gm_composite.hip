@@ -1026,6 +1026,42 @@ static gm_status tile_order_ws(const gm_camera* cam, void* ws, size_t ws_bytes, 
     return GM_OK;
 }
 
+// Host checks of the one-layer reverse mode; fills its kernel parameters.
+static gm_status bwd_params(CompParams& P, const gm_camera* cam, int32_t N, const float* rec,
+                            const int32_t* tile_ranges, const int32_t* sorted_ids, const int32_t* face_id,
+                            const float* depth, float softness, const float* state_T, const int32_t* state_last,
+                            const float* state_cm, const float* g_rgb, const float* g_rec)
+{
+    const float zero3[3] = {0.0f, 0.0f, 0.0f};
+    if (gm_status s = fill_params(P, cam, rec, tile_ranges, sorted_ids, face_id, depth, nullptr, nullptr, nullptr,
+                                  zero3, softness))
+        return s;
+    GM_ARG_CHECK(N >= 0, "N = %d is negative", N);
+    GM_ARG_CHECK(state_T && state_last && state_cm && g_rgb, "state or g_rgb is NULL");
+    GM_ARG_CHECK(N == 0 || g_rec, "g_rec is NULL");
+    return GM_OK;
+}
+
+// Reverse mode of the one-layer composite with the tile walk lengths and order in
+// walk [T] and order [T] (device scratch; every entry is written before it is read).
+static gm_status bwd_launch(const CompParams& P, int32_t N, const float* state_T, const int32_t* state_last,
+                            const float* state_cm, const float* g_rgb, const float* g_depth, const float* g_alpha,
+                            float* g_rec, float* g_mesh_rgb, float* g_mesh_depth, int32_t* walk, int32_t* order,
+                            hipStream_t stream)
+{
+    const int64_t T = (int64_t)P.cam.tx * P.cam.ty;
+    const int64_t n = N > 0 ? (int64_t)N * GM_GRAD : 0;
+    k_tile_walk<false><<<(unsigned)T, CT, 0, stream>>>(P, state_last, nullptr, walk, g_rec, n);
+    GM_LAUNCH_CHECK();
+    k_tile_order<<<1, TO_THREADS, 0, stream>>>((int)T, walk, order);
+    GM_LAUNCH_CHECK();
+    k_composite_bwd<false><<<(unsigned)T, CT, 0, stream>>>(P, state_T, state_last, state_cm, nullptr, nullptr,
+                                                          g_rgb, g_depth, g_alpha, g_rec, g_mesh_rgb, g_mesh_depth,
+                                                          nullptr, order);
+    GM_LAUNCH_CHECK();
+    return GM_OK;
+}
+
 extern "C" {
 
 gm_status gm_composite_hybrid_fwd(const gm_camera* cam, const float* rec, const int32_t* tile_ranges,
@@ -1112,26 +1148,13 @@ gm_status gm_composite_hybrid_bwd(const gm_camera* cam, int32_t N, const float* 
 {
     clear_error();
     CompParams P;
-    const float zero3[3] = {0.0f, 0.0f, 0.0f};
-    if (gm_status s = fill_params(P, cam, rec, tile_ranges, sorted_ids, face_id, depth, nullptr, nullptr, nullptr,
-                                  zero3, softness))
+    if (gm_status s = bwd_params(P, cam, N, rec, tile_ranges, sorted_ids, face_id, depth, softness, state_T,
+                                 state_last, state_cm, g_rgb, g_rec))
         return s;
-    GM_ARG_CHECK(N >= 0, "N = %d is negative", N);
-    GM_ARG_CHECK(state_T && state_last && state_cm && g_rgb, "state or g_rgb is NULL");
-    GM_ARG_CHECK(N == 0 || g_rec, "g_rec is NULL");
-    const int64_t T = (int64_t)P.cam.tx * P.cam.ty;
     int32_t *walk, *order;
     if (gm_status s = tile_order_ws(cam, ws, ws_bytes, &walk, &order)) return s;
-    const int64_t n = N > 0 ? (int64_t)N * GM_GRAD : 0;
-    k_tile_walk<false><<<(unsigned)T, CT, 0, stream>>>(P, state_last, nullptr, walk, g_rec, n);
-    GM_LAUNCH_CHECK();
-    k_tile_order<<<1, TO_THREADS, 0, stream>>>((int)T, walk, order);
-    GM_LAUNCH_CHECK();
-    k_composite_bwd<false><<<(unsigned)T, CT, 0, stream>>>(P, state_T, state_last, state_cm, nullptr, nullptr,
-                                                          g_rgb, g_depth, g_alpha, g_rec, g_mesh_rgb, g_mesh_depth,
-                                                          nullptr, order);
-    GM_LAUNCH_CHECK();
-    return GM_OK;
+    return bwd_launch(P, N, state_T, state_last, state_cm, g_rgb, g_depth, g_alpha, g_rec, g_mesh_rgb, g_mesh_depth,
+                      walk, order, stream);
 }
 
 gm_status gm_composite_hybrid_bwd_aa(const gm_camera* cam, int32_t N, const float* rec, const int32_t* tile_ranges,

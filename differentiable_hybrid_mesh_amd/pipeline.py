@@ -85,9 +85,15 @@ class DeviceScene:
         m.V, m.F = scene.V, scene.F
         m.Vt = 0 if scene.uv is None else int(scene.uv.shape[1])
         m.tex_size = self.tex_size
-        m.verts, m.faces, m.face_mask = G.ptr(self.verts), G.ptr(self.faces), G.ptr(self.face_mask)
-        m.vcolor, m.vnormal = G.ptr(self.vcolor), G.ptr(self.vnormal)
-        m.uv, m.faces_uv, m.mips = G.ptr(self.uv), G.ptr(self.faces_uv), G.ptr(self.mips)
+        V, F = scene.V, scene.F
+        m.verts = G.dev(self.verts, "verts", G.F32, 3 * V, optional=V == 0)
+        m.faces = G.dev(self.faces, "faces", G.I32, 3 * F, optional=F == 0)
+        m.face_mask = G.dev(self.face_mask, "face_mask", G.U8, F, optional=True)
+        m.vcolor = G.dev(self.vcolor, "vcolor", G.F32, 3 * V, optional=True)
+        m.vnormal = G.dev(self.vnormal, "vnormal", G.F32, 3 * V, optional=True)
+        m.uv = G.dev(self.uv, "uv", G.F32, 2 * m.Vt, optional=True)
+        m.faces_uv = G.dev(self.faces_uv, "faces_uv", G.I32, 3 * F, optional=True)
+        m.mips = G.dev(self.mips, "mips", G.F32, 0, optional=True)
         self.mesh = m
         self.light = make_light(scene.light)
         self.cams = [make_camera(scene.width, scene.height, scene.fx, scene.fy, scene.cx, scene.cy,

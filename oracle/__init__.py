@@ -84,9 +84,12 @@ class MeshB(C.Structure):
 
 
 def lib():
+    """The loaded oracle library.  ``GM_ORACLE_LIB`` names another build of the same
+    sources to load instead (the mutation tests load copies with a planted mistake
+    this way, in a child process)."""
     global _lib
     if _lib is None:
-        _lib = C.CDLL(build())
+        _lib = C.CDLL(os.environ.get("GM_ORACLE_LIB") or build())
         P, I, D = C.c_void_p, C.c_int, C.c_double
         cam = C.POINTER(Camera)
         _lib.oc_project_vertices.argtypes = [cam, I, P, P]

@@ -184,3 +184,30 @@ def test_antialias_argument_errors(G):
     m.verts = None
     assert L.gm_vscreen_bwd(C.byref(cam), C.byref(m), 16, 16, None) == G.GM_ERR_ARG
     assert G.gm_edge_adjacency_ws(10) > 0
+
+
+def test_binding_rejects_bad_tensors_before_the_call(G):
+    """The Python binding refuses host tensors, non-tensors, missing required tensors
+    and images of the wrong shape with ValueError (a GPU would fault on a host
+    pointer or read past a short buffer)."""
+    import torch
+    from differentiable_hybrid_mesh_amd.pipeline import make_camera
+    cam = make_camera(64, 48, 64.0, 64.0, 32.0, 24.0, [1, 0, 0, 0, 1, 0, 0, 0, 1], [0, 0, 0])
+    with pytest.raises(ValueError, match="GPU tensor"):
+        G.dev(torch.zeros(4), "x", G.F32, 4)
+    with pytest.raises(ValueError, match="torch tensor"):
+        G.dev(np_array := __import__("numpy").zeros(4, "float32"), "x", G.F32, 4)
+    assert np_array.shape == (4,)
+    with pytest.raises(ValueError, match="required"):
+        G.dev(None, "x", G.F32, 4)
+    assert G.dev(None, "x", G.F32, 4, optional=True) is None
+    # an image laid out (3, H, W) instead of (H, W, 3) is caught by its shape
+    with pytest.raises(ValueError, match="shape"):
+        G.img(torch.zeros(3, 48, 64), "g_rgb", cam, 3)
+    with pytest.raises(ValueError, match="shape"):
+        G.img(torch.zeros(64, 48), "g_depth", cam, 1)
+    # whole calls: a host upstream gradient never reaches the library
+    t = torch.zeros(48, 64)
+    with pytest.raises(ValueError):
+        G.gm_composite_hybrid_bwd(cam, 1, t, t, t, t, t, 1.0, t, t, t, torch.zeros(48, 64, 3), None, None, t, None,
+                                  None, torch.zeros(G.gm_composite_hybrid_bwd_ws(64, 48), dtype=torch.uint8), None)

@@ -170,3 +170,72 @@ def test_batched_pass_matches_per_view_loop(name, method):
         rms = float(b.pow(2).mean().sqrt())
         err = float(((a - b).abs() / (b.abs() + rms + 1e-30)).max())
         assert err <= 1e-3, (name, v, "g_rec", err)
+
+
+# ---------------------------------------------------------------------------
+# the batched path against the oracle directly
+# ---------------------------------------------------------------------------
+
+def test_batched_records_against_oracle_c5():
+    """Every view of the 4-view 1080p workload: the records written by the batched
+    projection against the oracle's projection of that view (decision fields bit
+    for bit, colour within 1e-6, validity, rect and tile count exact)."""
+    import torch
+    import oracle
+    import parity as P
+    from differentiable_hybrid_mesh_amd.pipeline import DeviceScene
+    s = _scene("c5")
+    ds = DeviceScene(s)
+    views = list(range(len(s.views)))
+    multi = _multi_records(ds, views)
+    torch.cuda.synchronize()
+    for v in views:
+        o = oracle.project_gaussians(oracle.camera(s, v), s.means, s.quats, s.scales, s.opacity, s.sh, s.sh_degree)
+        rep = P.compare_records({"rec": P.to_np(multi[v, : s.N])}, o)
+        print("c5 batched view", v, rep, flush=True)
+        assert rep["valid_mismatch"] == 0 and rep["rect_mismatch"] == 0 and rep["ntiles_mismatch"] == 0
+        assert rep["field_mismatch"] == 0 and rep["rgb_ok"], rep
+        assert int(o["valid"].sum()) > 100_000
+
+
+@pytest.mark.slow
+def test_batched_pipelined_pass_against_oracle_c2():
+    """A pipelined batched pass over four views of the 512x512 workload: each view's
+    images, record gradients and mesh gradients against the oracle on every tile,
+    under the rules of the parity tests."""
+    import torch
+    import oracle
+    import parity as P
+    from differentiable_hybrid_mesh_amd.pipeline import DeviceScene, Renderer
+    s = _scene("c2")
+    s = scenes.Scene(**{**s.__dict__, "views": _orbit(4, float(np.median(s.means[2])), 2.5)})
+    s.grads = [scenes.upstream_grads(s, k) for k in range(4)]
+    ds = DeviceScene(s)
+    views = list(range(4))
+    grads = [ds.grads(v) for v in views]
+    r = Renderer(ds)
+    r.fit_lists_views(views)
+    got = []
+
+    def keep(k):
+        got.append({"rgb": r.out_rgb.clone(), "depth": r.out_depth.clone(), "alpha": r.out_alpha.clone(),
+                    "face_id": r.face_id.clone(), "zdepth": r.depth.clone(), "tile_dmax": r.tile_dmax.clone(),
+                    "g_rec": r.g_rec[: r.N].clone(),
+                    "g_mesh_rgb": r.g_mesh_rgb.clone(), "g_mesh_depth": r.g_mesh_depth.clone()})
+    r.views_step_pipelined(views, grads, hook=keep)
+    torch.cuda.synchronize()
+    assert r.read_counts()
+    T = s.tiles_x * s.tiles_y
+    tiles = np.arange(T, dtype=np.int32)
+    for v in views:
+        gpu = {k: P.to_np(t) for k, t in got[v].items()}
+        ora = oracle.render_view(s, v, tiles=tiles, cull=True, backward=True, grads=s.grads[v])
+        zb = P.compare_zbuffer(s, gpu, ora, tiles)
+        im = P.compare_images(s, gpu, ora, tiles, ties=zb["ties"])
+        gr = P.compare_grads(s, gpu, ora, tiles, im["straddle_mask"])
+        print("c2 batched view", v, {k: x for k, x in {**zb, **im, **gr}.items() if not k.endswith("mask")
+                                     and k != "ties"}, flush=True)
+        assert zb["face_mismatch"] == 0 and zb["depth_mismatch"] == 0
+        assert im["img_bad"] == 0 and im["straddle"] <= 2
+        assert not gr["planes_bad"] and gr["elem_bad"] == 0 and gr["grad_exempt"] <= 2
+        assert gr["mesh_rgb_bad"] == 0 and gr["mesh_depth_bad"] == 0

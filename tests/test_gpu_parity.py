@@ -1,9 +1,9 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
-Small workloads (64x64 random soup, 512x512 icosphere, 800x800 textured soup, tiny
-edge cases) are compared on every tile.  The 1080p workloads are compared on a
-sample of tiles, with upstream gradients zero outside the sample so that the
-oracle can produce the full gradient of every Gaussian.
+Every workload is compared on every tile: the 64x64 random soup, the 512x512
+icosphere, three views of the 800x800 textured soup, the 1080p sphere with 1M
+Gaussians and all four views of the 1080p four-sphere scene with 3M Gaussians, and
+tiny edge cases, with the workloads' full upstream gradients.
 """
 import numpy as np
 import pytest
@@ -108,20 +108,28 @@ def _sample_tiles(scene, n, seed=0):
 
 
 @pytest.mark.slow
-def test_c3_sampled():
+def test_c3_full():
+    """The 1080p hybrid workload on every tile: z-buffer, records of all 1M
+    Gaussians, every per-tile list, every pixel of rgb / depth / alpha and every
+    gradient with the full upstream gradients."""
     s = _scene("c3")
-    tiles = _sample_tiles(s, 24)
-    gpu, ora, tiles = _run(s, 0, tiles=tiles, cull=True, masked=True)
-    _check_all(s, 0, gpu, ora, tiles, True, "c3 sampled")
+    print("c3 full: GPU pass and oracle on all %d tiles" % (s.tiles_x * s.tiles_y), flush=True)
+    gpu, ora, tiles = _run(s, 0, cull=True)
+    rep = _check_all(s, 0, gpu, ora, tiles, True, "c3 full")
+    assert P.compare_bins(s, 0, gpu) == 0
+    assert rep["entries"] > 10_000_000
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("view", [0, 1, 2, 3])
-def test_c5_sampled(view):
+def test_c5_full(view):
+    """Each view of the 4-view 1080p workload (3M Gaussians, 499,280 faces) on every
+    tile, as for C3."""
     s = _scene("c5")
-    tiles = _sample_tiles(s, 12, seed=view)
-    gpu, ora, tiles = _run(s, view, tiles=tiles, cull=True, masked=True)
-    _check_all(s, view, gpu, ora, tiles, True, "c5 view %d sampled" % view)
+    print("c5 view %d full: GPU pass and oracle on all %d tiles" % (view, s.tiles_x * s.tiles_y), flush=True)
+    gpu, ora, tiles = _run(s, view, cull=True)
+    _check_all(s, view, gpu, ora, tiles, True, "c5 view %d full" % view)
+    assert P.compare_bins(s, view, gpu) == 0
 
 
 # ---------------------------------------------------------------------------
