@@ -53,7 +53,8 @@ EXPORTS = ["gm_bin_triangles_ws", "gm_bin_triangles", "gm_raster_zbuffer_ws", "g
            "gm_composite_hybrid_bwd", "gm_composite_hybrid_bwd_ws", "gm_project_gaussians_bwd", "gm_mesh_bwd", "gm_mipmaps_floats",
            "gm_build_mipmaps", "gm_last_error", "gm_version", "gm_edge_adjacency_ws", "gm_edge_adjacency",
            "gm_antialias", "gm_composite_hybrid_fwd_aa", "gm_composite_hybrid_bwd_aa", "gm_antialias_bwd_ws",
-           "gm_antialias_bwd", "gm_vscreen_bwd", "gm_shade_surface", "gm_composite_hybrid_fwd_shaded"]
+           "gm_antialias_bwd", "gm_vscreen_bwd", "gm_shade_surface", "gm_composite_hybrid_fwd_shaded",
+           "gm_composite_hybrid_bwd_noalloc"]
 
 _lib = None
 
@@ -86,6 +87,7 @@ def lib():
     L.gm_shade_surface.argtypes = [cam, P, mesh, P, light, P, P, P]
     L.gm_composite_hybrid_fwd_shaded.argtypes = [cam, P, P, P, P, P, F32, P, P, P, P, P, P, P]
     L.gm_composite_hybrid_bwd.argtypes = [cam, I32, P, P, P, P, P, F32, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    L.gm_composite_hybrid_bwd_noalloc.argtypes = [cam, I32, P, P, P, P, P, F32, P, P, P, P, P, P, P, P, P, P]
     L.gm_composite_hybrid_bwd_ws.argtypes = [I32, I32]
     L.gm_composite_hybrid_bwd_ws.restype = SZ
     L.gm_project_gaussians_bwd.argtypes = [cam, I32, P, P, P, P, P, I32, P, P, P, P, P, P, P, P, P, P]
@@ -115,7 +117,7 @@ def lib():
                  "gm_composite_hybrid_fwd", "gm_composite_hybrid_bwd", "gm_project_gaussians_bwd",
                  "gm_mesh_bwd", "gm_build_mipmaps", "gm_edge_adjacency", "gm_antialias", "gm_composite_hybrid_fwd_aa",
                  "gm_composite_hybrid_bwd_aa", "gm_antialias_bwd", "gm_vscreen_bwd", "gm_shade_surface",
-                 "gm_composite_hybrid_fwd_shaded"):
+                 "gm_composite_hybrid_fwd_shaded", "gm_composite_hybrid_bwd_noalloc"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -349,6 +351,15 @@ def gm_composite_hybrid_bwd(cam, N, rec, tile_ranges, sorted_ids, face_id, depth
     check(lib().gm_composite_hybrid_bwd(*_bwd_args(cam, N, rec, tile_ranges, sorted_ids, face_id, depth, softness,
                                                    state_T, state_last, state_cm, g_rgb, g_depth, g_alpha, g_rec,
                                                    g_mesh_rgb, g_mesh_depth), wp, wb, stream))
+
+
+def gm_composite_hybrid_bwd_noalloc(cam, N, rec, tile_ranges, sorted_ids, face_id, depth, softness, state_T,
+                                    state_last, state_cm, g_rgb, g_depth, g_alpha, g_rec, g_mesh_rgb, g_mesh_depth,
+                                    stream):
+    """gm_composite_hybrid_bwd with the library's fixed scratch instead of ws."""
+    check(lib().gm_composite_hybrid_bwd_noalloc(*_bwd_args(cam, N, rec, tile_ranges, sorted_ids, face_id, depth,
+                                                           softness, state_T, state_last, state_cm, g_rgb, g_depth,
+                                                           g_alpha, g_rec, g_mesh_rgb, g_mesh_depth), stream))
 
 
 def gm_project_gaussians_bwd(cam, N, means, quats, scales, opacity, sh, sh_degree, rec, g_rec, g_means, g_quats,

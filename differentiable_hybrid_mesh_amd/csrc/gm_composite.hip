@@ -16,6 +16,8 @@
 // decisions bit for bit.
 #pragma clang fp contract(off)
 
+#include <mutex>
+
 #include "gm_internal.h"
 
 namespace gm {
@@ -1062,6 +1064,38 @@ static gm_status bwd_launch(const CompParams& P, int32_t N, const float* state_T
     return GM_OK;
 }
 
+// Fixed scratch of gm_composite_hybrid_bwd_noalloc, for callers that cannot
+// allocate: the walk lengths (first GM_NOALLOC_MAX_TILES ints) and the tile order
+// (next GM_NOALLOC_MAX_TILES) of one image.  Every GPU the library runs on holds its
+// own copy, at its own address, until the process ends.  In host code the array's
+// name is not a device address: the kernels receive the address that
+// hipGetSymbolAddress gives on that device, looked up once per device.
+static __device__ __align__(256) int32_t scratch[2 * GM_NOALLOC_MAX_TILES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static int32_t* g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+
+// Device address of `scratch` on the device that owns `stream`, which must be the
+// current device (the symbol address is looked up with that device current).
+static gm_status noalloc_scratch(hipStream_t stream, int32_t** out)
+{
+    int cur = -1, dev = -1;
+    GM_HIP_CHECK(hipGetDevice(&cur));
+    GM_HIP_CHECK(hipStreamGetDevice(stream, &dev));
+    GM_ARG_CHECK(dev == cur, "stream belongs to device %d, current device is %d", dev, cur);
+    GM_ARG_CHECK(cur >= 0 && cur < NOALLOC_MAX_DEVICES, "device %d above %d", cur, NOALLOC_MAX_DEVICES);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[cur]) {
+        void* p = nullptr;
+        GM_HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        GM_ARG_CHECK(p != nullptr, "no device address for the fixed scratch on device %d", cur);
+        g_scratch_ptr[cur] = static_cast<int32_t*>(p);
+    }
+    *out = g_scratch_ptr[cur];
+    return GM_OK;
+}
+
 extern "C" {
 
 gm_status gm_composite_hybrid_fwd(const gm_camera* cam, const float* rec, const int32_t* tile_ranges,
@@ -1155,6 +1189,27 @@ gm_status gm_composite_hybrid_bwd(const gm_camera* cam, int32_t N, const float* 
     if (gm_status s = tile_order_ws(cam, ws, ws_bytes, &walk, &order)) return s;
     return bwd_launch(P, N, state_T, state_last, state_cm, g_rgb, g_depth, g_alpha, g_rec, g_mesh_rgb, g_mesh_depth,
                       walk, order, stream);
+}
+
+gm_status gm_composite_hybrid_bwd_noalloc(const gm_camera* cam, int32_t N, const float* rec,
+                                          const int32_t* tile_ranges, const int32_t* sorted_ids,
+                                          const int32_t* face_id, const float* depth, float softness,
+                                          const float* state_T, const int32_t* state_last, const float* state_cm,
+                                          const float* g_rgb, const float* g_depth, const float* g_alpha,
+                                          float* g_rec, float* g_mesh_rgb, float* g_mesh_depth, hipStream_t stream)
+{
+    clear_error();
+    CompParams P;
+    if (gm_status s = bwd_params(P, cam, N, rec, tile_ranges, sorted_ids, face_id, depth, softness, state_T,
+                                 state_last, state_cm, g_rgb, g_rec))
+        return s;
+    const int64_t T = (int64_t)P.cam.tx * P.cam.ty;
+    GM_ARG_CHECK(T <= GM_NOALLOC_MAX_TILES, "%dx%d image has %lld tiles, above the fixed scratch's %d", cam->width,
+                 cam->height, (long long)T, GM_NOALLOC_MAX_TILES);
+    int32_t* base = nullptr;
+    if (gm_status s = noalloc_scratch(stream, &base)) return s;
+    return bwd_launch(P, N, state_T, state_last, state_cm, g_rgb, g_depth, g_alpha, g_rec, g_mesh_rgb, g_mesh_depth,
+                      base, base + GM_NOALLOC_MAX_TILES, stream);
 }
 
 gm_status gm_composite_hybrid_bwd_aa(const gm_camera* cam, int32_t N, const float* rec, const int32_t* tile_ranges,

@@ -302,6 +302,27 @@ gm_status gm_composite_hybrid_bwd(const gm_camera* cam, int32_t N, const float* 
                                   const float* g_alpha, float* g_rec, float* g_mesh_rgb,
                                   float* g_mesh_depth, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* gm_composite_hybrid_bwd_noalloc — call 6 for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, results and errors as gm_composite_hybrid_bwd
+ * without ws / ws_bytes.  Its scratch (tile walk lengths and tile order) is a fixed
+ * device array inside the library, GM_NOALLOC_MAX_TILES * 8 bytes (512 KiB), held
+ * by every GPU the library runs on until the process ends; its address on a device
+ * is looked up on the first call there.  The call allocates nothing (no hipMalloc,
+ * no library allocation) and never clears that scratch with a memset (every entry
+ * is written before it is read).  Images of more than GM_NOALLOC_MAX_TILES 16x16
+ * tiles (above 4096 x 4096 pixels) are GM_ERR_ARG.  `stream` must belong to the
+ * current device (GM_ERR_ARG otherwise).  All calls on one GPU share the one
+ * scratch: calls that overlap on one GPU (other streams, other host threads) race
+ * and must be ordered by the caller. */
+#define GM_NOALLOC_MAX_TILES 65536
+gm_status gm_composite_hybrid_bwd_noalloc(const gm_camera* cam, int32_t N, const float* rec,
+                                          const int32_t* tile_ranges, const int32_t* sorted_ids,
+                                          const int32_t* face_id, const float* depth, float softness,
+                                          const float* state_T, const int32_t* state_last, const float* state_cm,
+                                          const float* g_rgb, const float* g_depth, const float* g_alpha,
+                                          float* g_rec, float* g_mesh_rgb, float* g_mesh_depth, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * 7. gm_project_gaussians_bwd — gradients of the Gaussians' own parameters.
  * README "Hybrid rendering": the renderer is differentiable end to end, through the

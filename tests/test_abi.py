@@ -186,6 +186,28 @@ def test_antialias_argument_errors(G):
     assert G.gm_edge_adjacency_ws(10) > 0
 
 
+def test_noalloc_backward_rejects_on_the_host(G):
+    """The fixed-scratch backward checks its arguments and the image size (at most
+    GM_NOALLOC_MAX_TILES tiles) before it touches the device."""
+    L = G.lib()
+    text = open(HEADER).read()
+    assert re.search(r"#define GM_NOALLOC_MAX_TILES 65536", text)
+    args = (1, 16, 16, 16, 16, 16, C.c_float(1.0), 16, 16, 16, 16, None, None, 16, None, None, None)
+    big = G.GmCamera(4112, 4096, 4000.0, 4000.0, 2056.0, 2048.0)
+    big.R[0] = big.R[4] = big.R[8] = 1.0
+    big.near_z = 0.01
+    assert L.gm_composite_hybrid_bwd_noalloc(C.byref(big), *args) == G.GM_ERR_ARG
+    assert b"tiles" in L.gm_last_error()
+    cam = _cam(G)
+    # NULL upstream gradient, NULL record gradients, negative softness: rejected first
+    assert L.gm_composite_hybrid_bwd_noalloc(C.byref(cam), 1, 16, 16, 16, 16, 16, C.c_float(1.0), 16, 16, 16, None,
+                                             None, None, 16, None, None, None) == G.GM_ERR_ARG
+    assert L.gm_composite_hybrid_bwd_noalloc(C.byref(cam), 1, 16, 16, 16, 16, 16, C.c_float(1.0), 16, 16, 16, 16,
+                                             None, None, None, None, None, None) == G.GM_ERR_ARG
+    assert L.gm_composite_hybrid_bwd_noalloc(C.byref(cam), 1, 16, 16, 16, 16, 16, C.c_float(-1.0), 16, 16, 16, 16,
+                                             None, None, 16, None, None, None) == G.GM_ERR_ARG
+
+
 def test_binding_rejects_bad_tensors_before_the_call(G):
     """The Python binding refuses host tensors, non-tensors, missing required tensors
     and images of the wrong shape with ValueError (a GPU would fault on a host
@@ -211,3 +233,6 @@ def test_binding_rejects_bad_tensors_before_the_call(G):
     with pytest.raises(ValueError):
         G.gm_composite_hybrid_bwd(cam, 1, t, t, t, t, t, 1.0, t, t, t, torch.zeros(48, 64, 3), None, None, t, None,
                                   None, torch.zeros(G.gm_composite_hybrid_bwd_ws(64, 48), dtype=torch.uint8), None)
+    with pytest.raises(ValueError):
+        G.gm_composite_hybrid_bwd_noalloc(cam, 1, t, t, t, t, t, 1.0, t, t, t, torch.zeros(48, 64, 3), None, None,
+                                          t, None, None, None)
