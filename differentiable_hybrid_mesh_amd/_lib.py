@@ -54,7 +54,7 @@ EXPORTS = ["gm_bin_triangles_ws", "gm_bin_triangles", "gm_raster_zbuffer_ws", "g
            "gm_build_mipmaps", "gm_last_error", "gm_version", "gm_edge_adjacency_ws", "gm_edge_adjacency",
            "gm_antialias", "gm_composite_hybrid_fwd_aa", "gm_composite_hybrid_bwd_aa", "gm_antialias_bwd_ws",
            "gm_antialias_bwd", "gm_vscreen_bwd", "gm_shade_surface", "gm_composite_hybrid_fwd_shaded",
-           "gm_composite_hybrid_bwd_noalloc"]
+           "gm_composite_hybrid_bwd_noalloc", "gm_composite_hybrid_fwd_stats"]
 
 _lib = None
 
@@ -86,6 +86,7 @@ def lib():
     L.gm_composite_hybrid_fwd.argtypes = [cam, P, P, P, P, P, mesh, P, light, P, F32, P, P, P, P, P, P, P]
     L.gm_shade_surface.argtypes = [cam, P, mesh, P, light, P, P, P]
     L.gm_composite_hybrid_fwd_shaded.argtypes = [cam, P, P, P, P, P, F32, P, P, P, P, P, P, P]
+    L.gm_composite_hybrid_fwd_stats.argtypes = [cam, P, P, P, P, P, F32, P, P, P, P, P, P, P, P]
     L.gm_composite_hybrid_bwd.argtypes = [cam, I32, P, P, P, P, P, F32, P, P, P, P, P, P, P, P, P, P, SZ, P]
     L.gm_composite_hybrid_bwd_noalloc.argtypes = [cam, I32, P, P, P, P, P, F32, P, P, P, P, P, P, P, P, P, P]
     L.gm_composite_hybrid_bwd_ws.argtypes = [I32, I32]
@@ -117,7 +118,7 @@ def lib():
                  "gm_composite_hybrid_fwd", "gm_composite_hybrid_bwd", "gm_project_gaussians_bwd",
                  "gm_mesh_bwd", "gm_build_mipmaps", "gm_edge_adjacency", "gm_antialias", "gm_composite_hybrid_fwd_aa",
                  "gm_composite_hybrid_bwd_aa", "gm_antialias_bwd", "gm_vscreen_bwd", "gm_shade_surface",
-                 "gm_composite_hybrid_fwd_shaded", "gm_composite_hybrid_bwd_noalloc"):
+                 "gm_composite_hybrid_fwd_shaded", "gm_composite_hybrid_bwd_noalloc", "gm_composite_hybrid_fwd_stats"):
         getattr(L, name).restype = C.c_int
     _lib = L
     return L
@@ -328,6 +329,16 @@ def gm_composite_hybrid_fwd_shaded(cam, rec, tile_ranges, sorted_ids, face_id, d
                                                float(softness), img(state_cm, "state_cm", cam, 3),
                                                *_fwd_out(cam, out_rgb, out_depth, out_alpha, state_T, state_last),
                                                stream))
+
+
+def gm_composite_hybrid_fwd_stats(cam, rec, tile_ranges, sorted_ids, face_id, depth, softness, state_cm, out_rgb,
+                                  out_depth, out_alpha, state_T, state_last, stats, stream):
+    """gm_composite_hybrid_fwd_shaded with counters added to stats (device int64 [3])."""
+    check(lib().gm_composite_hybrid_fwd_stats(C.byref(cam), *_lists(cam, rec, tile_ranges, sorted_ids),
+                                              img(face_id, "face_id", cam, 1, I32), img(depth, "depth", cam, 1),
+                                              float(softness), img(state_cm, "state_cm", cam, 3),
+                                              *_fwd_out(cam, out_rgb, out_depth, out_alpha, state_T, state_last),
+                                              dev(stats, "stats", I64, 3), stream))
 
 
 def gm_composite_hybrid_bwd_ws(width, height) -> int:

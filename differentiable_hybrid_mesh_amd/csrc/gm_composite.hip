@@ -220,8 +220,8 @@ __global__ void __launch_bounds__(256) k_shade(CompParams P, float* __restrict__
 // the per-pair evaluation shared by both walks
 // ---------------------------------------------------------------------------
 struct Staged {
-    float4 a;  // u, v, Q00/2, Q01
-    float4 b;  // Q11/2, opacity, r, g
+    float4 a;  // u, v, l0, l1 (Cholesky factor of Q / 2, see conic_cholesky)
+    float4 b;  // l2, opacity, r, g
     float4 c;  // b, z_c, g0, g1
     float4 d;  // sigma, kappa = 1/(sigma softness), q_skip, 1/sigma
 };
@@ -230,6 +230,34 @@ struct Staged {
 __device__ __forceinline__ float quad_form(float hq00, float q01, float hq11, float dx, float dy)
 {
     return __builtin_fmaf(dx, __builtin_fmaf(hq00, dx, q01 * dy), (hq11 * dy) * dy);
+}
+
+// The same q from the Cholesky factor of Q / 2 = L L^T, L = [[l0, 0], [l1, l2]]:
+// q = |L^T d|^2 = (l0 dx + l1 dy)^2 + (l2 dy)^2, a sum of two squares.  For a
+// Gaussian that is long and thin on screen the three terms of the expanded form
+// cancel, and in fp32 their rounding grows with the conic's condition number (up to
+// 4e-4 in q, i.e. in log alpha, at 100-200 px offsets in the 1080p four-sphere
+// scene); the squares' error grows only with its square root.  Five operations, as
+// for the expanded form.
+__device__ __forceinline__ float chol_form(float l0, float l1, float l2, float dx, float dy)
+{
+    const float t1 = __builtin_fmaf(l0, dx, l1 * dy);
+    const float t2 = l2 * dy;
+    return __builtin_fmaf(t1, t1, t2 * t2);
+}
+
+// Cholesky factor of Q / 2 from the conic (Q00 > 0 on a listed record): l0 =
+// sqrt(Q00 / 2), l1 = (Q01 / 2) / l0, l2 = sqrt(det Q / (2 Q00)).  det Q = Q00 Q11 -
+// Q01^2 is formed with the exact error of the product Q01^2 (Kahan's difference of
+// products), so it keeps its relative accuracy when the two products nearly cancel.
+__device__ __forceinline__ void conic_cholesky(float Q00, float Q01, float Q11, float& l0, float& l1, float& l2)
+{
+    const float p = Q01 * Q01;
+    const float e = __builtin_fmaf(Q01, Q01, -p);
+    const float det = fmaxf(__builtin_fmaf(Q00, Q11, -p) - e, 0.0f);
+    l0 = sqrtf(0.5f * Q00);
+    l1 = l0 > 0.0f ? (0.5f * Q01) / l0 : 0.0f;
+    l2 = Q00 > 0.0f ? sqrtf((0.5f * det) / Q00) : 0.0f;
 }
 
 // Standard normal CDF Phi(s) and density phi(s) from one exponential.
@@ -271,7 +299,7 @@ __device__ __forceinline__ Pair eval_pair(const Staged& g, float pxc, float pyc,
     Pair p;
     p.dx = pxc - g.a.x;
     p.dy = pyc - g.a.y;
-    p.q = quad_form(g.a.z, g.a.w, g.b.x, p.dx, p.dy);
+    p.q = chol_form(g.a.z, g.a.w, g.b.x, p.dx, p.dy);
     p.oG = g.b.y * __expf(-p.q);
     p.al = fminf(p.oG, ALPHA_MAX);
     p.f = 1.0f;
@@ -344,8 +372,10 @@ __device__ __forceinline__ uint32_t stage_record(const CompParams& P, float4 ra,
                                                  float4 rd, int tx, int ty, const float* wdmax, Staged& st)
 {
     const float Q00 = ra.z, Q01 = ra.w, Q11 = rb.x;
-    st.a = make_float4(ra.x, ra.y, 0.5f * Q00, Q01);
-    st.b = make_float4(0.5f * Q11, rb.y, rb.z, rb.w);
+    float l0, l1, l2;
+    conic_cholesky(Q00, Q01, Q11, l0, l1, l2);
+    st.a = make_float4(ra.x, ra.y, l0, l1);
+    st.b = make_float4(l2, rb.y, rb.z, rb.w);
     st.c = rc;
     const float o = rb.y;
     const float lq = o > 0.0f ? logf(255.0f * o) : -1.0f;
@@ -373,7 +403,7 @@ __device__ __forceinline__ uint32_t stage_record(const CompParams& P, float4 ra,
         const float gxm = fminf(g0 * xa, g0 * xb);
         const float dm = wdmax[w];
         if (dm < 0.0f) continue;  // no pixel of this wave is in the image
-        if (quad_min_rect(st.a.z, Q01, st.b.x, xa, xb, ya, yb) * (1.0f - 1e-5f) > qe) continue;
+        if (quad_min_rect(0.5f * Q00, Q01, 0.5f * Q11, xa, xb, ya, yb) * (1.0f - 1e-5f) > qe) continue;
         if (dm < INFINITY) {
             const float zmin = zc + (gxm + fminf(g1 * ya, g1 * yb));
             const float lim = dm + 1e-5f * fabsf(dm);
@@ -432,11 +462,16 @@ __device__ __forceinline__ AaLayer load_layer(const float* __restrict__ layer, i
     return AaLayer{l0.x, l0.y, l0.z, l0.w, l1.x, l1.y};
 }
 
-template <bool AA>
+// STATS = true (a measurement build of the same kernel): adds to stats[0] the
+// included (pixel, entry) pairs, to stats[1] the entries the waves evaluate (each
+// wave-wide evaluation of one entry counts once) and to stats[2] the list entries
+// staged; the outputs are those of STATS = false.
+template <bool AA, bool STATS = false>
 __global__ void __launch_bounds__(CT)
 k_composite_fwd(CompParams P, const float* __restrict__ state_cm, const float* __restrict__ layer,
                 float* __restrict__ out_rgb, float* __restrict__ out_depth, float* __restrict__ out_alpha,
-                float* __restrict__ state_T, int32_t* __restrict__ state_last, float* __restrict__ state_aa)
+                float* __restrict__ state_T, int32_t* __restrict__ state_last, float* __restrict__ state_aa,
+                unsigned long long* __restrict__ stats = nullptr)
 {
     __shared__ Staged s_g[CBF];
     __shared__ uint8_t s_m[CBF];
@@ -475,12 +510,14 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, const float* _
     int lastB = 0;
     bool doneB = true;
     if constexpr (AA) doneB = !(inside && on && ml.am < 1.0f);
+    int ninc = 0, nev = 0, nst = 0;  // STATS only
     float4 ra, rb, rc, rd;
     if ((int)threadIdx.x < CBF && start + (int)threadIdx.x < end)
         load_record(P.rec, P.ids[start + threadIdx.x], ra, rb, rc, rd);
     for (int b0 = start; b0 < end; b0 += CBF) {
         if (__syncthreads_count(done & doneB) == CT) break;
         const int nb = min(CBF, end - b0);
+        if constexpr (STATS) nst += nb;
         if ((int)threadIdx.x < CBF)
             s_m[threadIdx.x] = (int)threadIdx.x < nb ? (uint8_t)stage_record(P, ra, rb, rc, rd, tx, ty, s_wd, s_g[threadIdx.x]) : 0;
         if ((int)threadIdx.x < CBF && b0 + CBF + (int)threadIdx.x < end)
@@ -505,6 +542,7 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, const float* _
                 T = inc ? Tn : T;
                 last = inc ? b0 + k - start + 1 : last;
                 done = done | stop;
+                if constexpr (STATS) ninc += inc ? 1 : 0;
                 if constexpr (AA) {
                     const float aB = pr.al * pr.fb;
                     doneB = doneB | done;  // the pixel stops with its front layer
@@ -534,12 +572,22 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, const float* _
                 const Pair pr2 = eval_pair(g2, pxc, pyc, on, wave_on, D, P.softness);
                 composite_entry(g, pr, k);
                 if (two) composite_entry(g2, pr2, k2);
+                if constexpr (STATS) nev += two ? 2 : 1;
                 if (__ballot(!(done & doneB)) == 0) {
                     wdone = true;
                     break;
                 }
             }
         }
+    }
+    if constexpr (STATS) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) ninc += __shfl_xor(ninc, o, 64);
+        if (lane == 0) {
+            atomicAdd(&stats[0], (unsigned long long)ninc);
+            atomicAdd(&stats[1], (unsigned long long)nev);
+        }
+        if (threadIdx.x == 0) atomicAdd(&stats[2], (unsigned long long)nst);
     }
     if (!inside) return;
     if constexpr (AA) {
@@ -873,7 +921,9 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
             const float* S = s_acc[threadIdx.x];
             const Staged& g = s_g[threadIdx.x];
             const float kap = g.d.y;
-            const float q00 = 2.0f * g.a.z, q01 = g.a.w, q11 = 2.0f * g.b.x;
+            // the conic from its staged Cholesky factor: Q = 2 L L^T
+            const float q00 = 2.0f * (g.a.z * g.a.z), q01 = 2.0f * (g.a.z * g.a.w),
+                        q11 = 2.0f * __builtin_fmaf(g.a.w, g.a.w, g.b.x * g.b.x);
             float gv[GM_GRAD];
             gv[0] = __builtin_fmaf(q00, S[5], __builtin_fmaf(q01, S[6], kap * g.c.z * S[10]));
             gv[1] = __builtin_fmaf(q01, S[5], __builtin_fmaf(q11, S[6], kap * g.c.w * S[10]));
@@ -1146,6 +1196,28 @@ gm_status gm_composite_hybrid_fwd_shaded(const gm_camera* cam, const float* rec,
     const int64_t T = (int64_t)P.cam.tx * P.cam.ty;
     k_composite_fwd<false><<<(unsigned)T, CT, 0, stream>>>(P, state_cm, nullptr, out_rgb, out_depth, out_alpha,
                                                           state_T, state_last, nullptr);
+    GM_LAUNCH_CHECK();
+    return GM_OK;
+}
+
+gm_status gm_composite_hybrid_fwd_stats(const gm_camera* cam, const float* rec, const int32_t* tile_ranges,
+                                        const int32_t* sorted_ids, const int32_t* face_id, const float* depth,
+                                        float softness, const float* state_cm, float* out_rgb, float* out_depth,
+                                        float* out_alpha, float* state_T, int32_t* state_last, int64_t* stats,
+                                        hipStream_t stream)
+{
+    clear_error();
+    CompParams P;
+    const float zero3[3] = {0.0f, 0.0f, 0.0f};
+    if (gm_status s = fill_params(P, cam, rec, tile_ranges, sorted_ids, face_id, depth, nullptr, nullptr, nullptr,
+                                  zero3, softness))
+        return s;
+    GM_ARG_CHECK(state_cm && stats, "state_cm / stats is NULL");
+    GM_ARG_CHECK(out_rgb && out_depth && out_alpha && state_T && state_last, "an output is NULL");
+    const int64_t T = (int64_t)P.cam.tx * P.cam.ty;
+    k_composite_fwd<false, true><<<(unsigned)T, CT, 0, stream>>>(P, state_cm, nullptr, out_rgb, out_depth, out_alpha,
+                                                                state_T, state_last, nullptr,
+                                                                reinterpret_cast<unsigned long long*>(stats));
     GM_LAUNCH_CHECK();
     return GM_OK;
 }

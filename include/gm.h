@@ -274,6 +274,19 @@ gm_status gm_composite_hybrid_fwd_shaded(const gm_camera* cam, const float* rec,
                                          float* out_alpha, float* state_T, int32_t* state_last,
                                          hipStream_t stream);
 
+/* gm_composite_hybrid_fwd_stats — a measurement aid: gm_composite_hybrid_fwd_shaded
+ * (same arguments, same outputs bit for bit) built with counters, which it ADDS to
+ * stats (device int64 [3], zeroed by the caller): [0] included (pixel, entry) pairs
+ * (the pairs the composite accumulates), [1] list entries evaluated wave-wide (one
+ * per wave and entry: the unit of the kernel's per-entry instruction count), [2]
+ * list entries staged into LDS.  Slower than the uncounted call; not part of the
+ * rendering path. */
+gm_status gm_composite_hybrid_fwd_stats(const gm_camera* cam, const float* rec, const int32_t* tile_ranges,
+                                        const int32_t* sorted_ids, const int32_t* face_id, const float* depth,
+                                        float softness, const float* state_cm, float* out_rgb, float* out_depth,
+                                        float* out_alpha, float* state_T, int32_t* state_last, int64_t* stats,
+                                        hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * 6. gm_composite_hybrid_bwd — reverse mode of call 5.
  * README "Hybrid rendering": everything is differentiable, Gaussian parameters

@@ -236,6 +236,7 @@ def test_batched_pipelined_pass_against_oracle_c2():
         print("c2 batched view", v, {k: x for k, x in {**zb, **im, **gr}.items() if not k.endswith("mask")
                                      and k != "ties"}, flush=True)
         assert zb["face_mismatch"] == 0 and zb["depth_mismatch"] == 0
-        assert im["img_bad"] == 0 and im["straddle"] <= 2
-        assert not gr["planes_bad"] and gr["elem_bad"] == 0 and gr["grad_exempt"] <= 2
+        # the exemption budgets of the parity tests
+        assert im["img_bad"] == 0 and im["straddle"] <= max(2, 1e-4 * s.width * s.height)
+        assert not gr["planes_bad"] and gr["elem_bad"] == 0 and gr["grad_exempt"] <= max(2, 1e-4 * s.N)
         assert gr["mesh_rgb_bad"] == 0 and gr["mesh_depth_bad"] == 0
