@@ -30,15 +30,6 @@ gm_status check_camera(const gm_camera* cam)
     return GM_OK;
 }
 
-gm_status read_back_i64(const long long* dev, int64_t* host, hipStream_t stream)
-{
-    long long v = 0;
-    GM_HIP_CHECK(hipMemcpyAsync(&v, dev, sizeof(v), hipMemcpyDeviceToHost, stream));
-    GM_HIP_CHECK(hipStreamSynchronize(stream));
-    *host = (int64_t)v;
-    return GM_OK;
-}
-
 // ---------------------------------------------------------------------------
 // exclusive scan: 256 threads x 16 items per block
 // ---------------------------------------------------------------------------

@@ -71,7 +71,7 @@ inline DevCamera dev_camera(const gm_camera& c)
 gm_status check_camera(const gm_camera* cam);
 
 // ---------------------------------------------------------------------------
-// device-wide exclusive scan of int32 counts (gm_scan.hip)
+// device-wide exclusive scan of int32 counts (gm_api.hip)
 // ---------------------------------------------------------------------------
 // out[i] = sum_{j<i} in[i] for i in [0, n]; out has n + 1 entries; *total (device,
 // int64) receives the full sum.  Workspace: scan_ws_bytes(n).
@@ -84,9 +84,6 @@ gm_status exclusive_scan(const int32_t* in, int32_t* out, int64_t n, long long* 
 gm_status launch_surface_colour(const gm_camera* cam, const gm_mesh* mesh, const float* vscreen,
                                 const gm_light* light, const int32_t* face_id, const float* bg, float* colour,
                                 hipStream_t stream);
-
-// Read a device int64 into host memory (synchronises the stream).
-gm_status read_back_i64(const long long* dev, int64_t* host, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // tile order: largest per-tile key first (one block of TO_THREADS)

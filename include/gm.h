@@ -34,6 +34,16 @@
  * length once the stream has reached it, and on overflow enlarges the list and
  * calls again.
  *
+ * Layout choices.  Three choices shape the signatures below.  (1) No call reads a
+ * count back to the host: a list's length goes to a device int64 and an overflow is
+ * visible there (there is no capacity error status), so a whole forward and
+ * backward can be queued without a synchronisation.  (2) The projected Gaussians
+ * are one 64-byte record each ([N][16] floats) rather than separate planes: the
+ * composite gathers one record per list entry, a single 64-byte load.  (3) The
+ * forward keeps the colour behind the Gaussians of every pixel (state_cm) for the
+ * backward, which then needs no mesh attributes, and its shading half can run on
+ * another stream beside the tile sort.
+ *
  * Errors.  Every call returns a gm_status.  GM_ERR_ARG: a required pointer is
  * NULL, a size is negative or out of range, the workspace is too small; checked on
  * the host before anything is launched.  GM_ERR_HIP: a HIP call failed.  gm_last_error() returns a
