@@ -1,21 +1,27 @@
-"""Benchmark: hybrid render fwd+bwd throughput at 1080p on one MI355X.
+"""Benchmark: hybrid render fwd+bwd throughput on one MI355X.
 
-One step = the whole hot path over one view of the workload, inputs resident in
-HBM: gm_bin_triangles -> gm_raster_zbuffer, beside them on a second stream
-gm_project_gaussians -> gm_sort_depth (then gm_shade_surface once the z-buffer is
-done), then gm_sort_tiles -> gm_composite_hybrid_fwd_shaded ->
-gm_composite_hybrid_bwd.
+One step = the whole hot path over every view of the workload, inputs resident in
+HBM.  Per view: gm_bin_triangles -> gm_raster_zbuffer, beside them on a second
+stream gm_project_gaussians -> gm_sort_depth (then gm_shade_surface once the
+z-buffer is done), then gm_sort_tiles -> gm_composite_hybrid_fwd_shaded ->
+gm_composite_hybrid_bwd.  The one-view workloads (64x64, 512x512 and the default
+1920x1080 sphere) time that sequence; the multi-view ones (the 800x800 soup's 16
+views, the 1920x1080 four-sphere scene's 4 views) time the pipelined pass that
+projects every view in one launch and overlaps each view's mesh half and lists with
+the previous view's composite.
 
-Prints one JSON line with the metric (K steps timed with no event inside them),
-per-stage times (HIP events between the stages on the two streams, over K further
-steps, whose own time is reported beside), a roofline entry for the dominant
-kernel, the measured HBM traffic of a whole step when its counter summary matches
-the kernel sources, and the CPU oracle's throughput on a bounded sample of the same
-workload.
+Prints one JSON line per workload: the metric over K steps timed with no event
+inside them; the median and 10th / 90th percentiles of the step time and of every
+stage (HIP events between the stages, over K further steps whose own mean is
+reported beside); a roofline entry for the dominant kernel, timed on its own stream
+with HIP events, with its work units counted on the GPU by the counting build of
+the composite; the measured HBM traffic of a whole step when its counter summary
+matches the kernel sources; and the CPU oracle's throughput on a bounded sample of
+the same workload.
 
-``--copy-calibration`` instead runs a plain device copy of known size; profiled
-with ``rocprofv3 --pmc FETCH_SIZE`` / ``WRITE_SIZE`` it gives the factors that turn
-those counters into bytes.
+``--all-configs`` prints one line for each workload.  ``--copy-calibration`` instead
+runs a plain device copy of known size; profiled with ``rocprofv3 --pmc FETCH_SIZE``
+/ ``WRITE_SIZE`` it gives the factors that turn those counters into bytes.
 """
 import argparse
 import hashlib
@@ -30,9 +36,12 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
-FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector (counts packed FMA)
-# Stages of one step on the library's (main) stream, and on the second stream that
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+# fp32 vector peak attainable without packed fp32 instructions (disabled in this
+# build): 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz
+FP32_VALU_PEAK_TFLOPS = 78.6
+FP32_VALU_PACKED_TFLOPS = 157.3  # the published fp32 vector figure (packed FMA)
+# Stages of one view on the library's (main) stream, and on the second stream that
 # runs the projection and the depth half of the sort beside the mesh's binning and
 # z-buffer, then the mesh shading beside the tile sort; "wait_lists" is the time the
 # main stream waits for the second one, "wait_zbuffer" the second one's wait for the
@@ -43,11 +52,13 @@ SIDE_STAGES = ["project", "sort_depth", "wait_zbuffer", "shade"]  # shade: the c
 SIDE_STAGES_AA = ["project", "sort_depth"]  # the layer call shades the mesh on the main stream
 
 WORKLOADS = {
+    "c1": "64x64, 200 random triangles (vertex colour), 500 Gaussians",
+    "c2": "512x512, 5120-face icosphere (vertex colour), 100k Gaussians",
     "c3": "1920x1080, 200k-face displaced sphere (vertex colour + Phong), 1M Gaussians SH3",
-    "c5": "1920x1080, 4 displaced spheres (499,280 faces, Phong), 3M Gaussians SH3, one of 4 views",
-    "c2": "512x512, 5120-face icosphere, 100k Gaussians",
-    "c4": "800x800 textured 4096-triangle soup, no Gaussians, one of 16 views",
+    "c4": "800x800 textured 4096-triangle soup (stochastic masks), no Gaussians, 16 views per step",
+    "c5": "1920x1080, 4 displaced spheres (499,280 faces, Phong), 3M Gaussians SH3, 4 views per step",
 }
+MULTI_VIEW = ("c4", "c5")
 
 # Algorithmic flops of the composite per (pixel, list entry) pair, counted on the
 # definition (transcendentals count 1): evaluating a pair (offset, quadratic form,
@@ -66,15 +77,18 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="c3", choices=sorted(WORKLOADS))
-    ap.add_argument("--view", type=int, default=0)
+    ap.add_argument("--all-configs", action="store_true", help="one JSON line per workload")
+    ap.add_argument("--view", type=int, default=0, help="view of a one-view run (--single-view)")
+    ap.add_argument("--single-view", action="store_true",
+                    help="time one view of a multi-view workload instead of all its views per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tiles", type=int, default=0,
-                    help="tiles in the oracle's timed sample (0: every tile of the view)")
+                    help="tiles in the oracle's timed sample (0: every tile of one view)")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--batch-views", action="store_true",
-                    help="one step = every view of the workload with one batched projection")
+    ap.add_argument("--batch-views", action="store_true", help="kept for compatibility: the multi-view "
+                                                                "workloads always time all their views per step")
     ap.add_argument("--antialias", action="store_true",
-                    help="the path with analytic edge antialiasing (two-layer composite)")
+                    help="the path with analytic edge antialiasing (two-layer composite), one view")
     return ap.parse_args()
 
 
@@ -133,6 +147,23 @@ def measured_step_traffic(config):
     return float(b.group(1))
 
 
+def pct(xs):
+    """Median, 10th and 90th percentiles (ms)."""
+    a = np.asarray(xs, np.float64)
+    return {"p50": round(float(np.percentile(a, 50)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4)}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -143,28 +174,35 @@ def main():
         copy_calibration()
         return
     import torch
-    import scenes
-    from differentiable_hybrid_mesh_amd import _lib as G
-    from differentiable_hybrid_mesh_amd.pipeline import DeviceScene, Renderer
-
     torch.cuda.set_device(0)
-    scene = scenes.make_scene(args.config)
-    if args.batch_views:
-        main_batch(args, scene)
-        return
-    view = args.view % len(scene.views)
-    ds = DeviceScene(scene)
-    r = Renderer(ds)
-    g = ds.grads(view)
-    cam = ds.cams[view]
-    torch.cuda.synchronize()
+    configs = list(WORKLOADS) if args.all_configs else [args.config]
+    for name in configs:
+        out = run_config(args, name)
+        print(json.dumps(out), flush=True)
 
-    aa = args.antialias and scene.F > 0
-    stages = STAGES_AA if aa else STAGES
-    side_stages = SIDE_STAGES_AA if aa else SIDE_STAGES
 
-    def step(ev=None, ev_side=None):
-        # the calls of Renderer.lists() with the overlap, spelled out to mark stages
+class Bench:
+    """One workload's device state and its per-view step with stage events."""
+
+    def __init__(self, scene, antialias=False):
+        import torch
+        from differentiable_hybrid_mesh_amd.pipeline import DeviceScene, Renderer
+        self.torch = torch
+        self.scene = scene
+        self.ds = DeviceScene(scene)
+        self.r = Renderer(self.ds)
+        self.grads = [self.ds.grads(v) for v in range(len(scene.views))]
+        self.aa = antialias and scene.F > 0
+        self.stages = STAGES_AA if self.aa else STAGES
+        self.side_stages = SIDE_STAGES_AA if self.aa else SIDE_STAGES
+
+    def step_view(self, view, ev=None, ev_side=None):
+        """The calls of Renderer.lists() with the overlap, then the composite forward and
+        backward, spelled out to mark stages with events."""
+        from differentiable_hybrid_mesh_amd import _lib as G
+        torch, r, ds = self.torch, self.r, self.ds
+        g = self.grads[view]
+        cam = ds.cams[view]
         main, side = torch.cuda.current_stream(), r._side_stream()
         st = main.cuda_stream
         i, j = [0], [0]
@@ -178,6 +216,7 @@ def main():
             if ev_side is not None:
                 ev_side[j[0]].record(side)
             j[0] += 1
+        r._single()
         r._ev_main.record(main)
         side.wait_event(r._ev_main)
         with torch.cuda.stream(side):
@@ -194,7 +233,7 @@ def main():
         G.gm_raster_zbuffer(cam, ds.mesh, r.vscreen, r.tile_offsets, r.tile_tris, r.face_id, r.depth,
                             r.tile_dmax, r.ws_zb, st)
         mark()
-        if aa:
+        if self.aa:
             r.antialias(view)
             mark()
         else:
@@ -210,7 +249,7 @@ def main():
         mark()
         r.sort_tiles(view, True)
         mark()
-        if aa:
+        if self.aa:
             r.composite_fwd_aa(view)
             mark()
             r.composite_bwd_aa(view, g["rgb"], g["depth"], g["alpha"])
@@ -224,9 +263,25 @@ def main():
             mark()
         r.fetch_counts()  # list lengths to pinned host memory, checked after the run
 
-    # list capacities first (binning, projection and sorting only), then the warm-up;
-    # no step synchronises: the lengths are read back once the stream has finished
-    r.fit_lists(view, True, antialias=aa)
+
+def run_config(args, name):
+    import torch
+    import scenes
+    scene = scenes.make_scene(name)
+    multi = name in MULTI_VIEW and not args.single_view and not args.antialias
+    views = list(range(len(scene.views))) if multi else [args.view % len(scene.views)]
+    b = Bench(scene, antialias=args.antialias)
+    r = b.r
+    if multi:
+        def step():
+            r.views_step_pipelined(views, b.grads)
+        r.fit_lists_views(views)
+    else:
+        def step():
+            b.step_view(views[0])
+        r.fit_lists(views[0], True, antialias=b.aa)
+    # warm-up; no step synchronises: the list lengths are read back once the stream
+    # has finished, and a list that outgrew its capacity is enlarged before timing
     for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()
@@ -234,15 +289,13 @@ def main():
         step()
         torch.cuda.synchronize()
 
-    # timed region: K whole steps, no events inside (each event is one more packet
-    # for the command processor); then K more steps with events between the stages
-    # on both streams for the per-stage times
+    # timed region: K whole steps, no events inside
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
-    for k in range(args.steps):
+    for _ in range(args.steps):
         step()
     t1.record()
     torch.cuda.synchronize()
@@ -250,206 +303,221 @@ def main():
     if not r.read_counts():  # every timed step used the same capacities as the warm-up
         raise RuntimeError("a list outgrew its capacity inside the timed region")
     ms = t0.elapsed_time(t1) / args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
-    evs_side = [[torch.cuda.Event(enable_timing=True) for _ in range(len(side_stages) + 1)]
-                for _ in range(args.steps)]
+    counts = r.counts_host[: r._rows].tolist()
+
+    # step-time distribution: K more steps, one event between consecutive steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
+    for k in range(args.steps):
+        step()
+        evs[k + 1].record()
+    torch.cuda.synchronize()
+    step_dist = [evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps)]
+
+    # per-stage times: every view one after another with events between the stages on
+    # both streams (the instrumented steps' own time is reported beside)
+    nst = max(1, args.steps // len(views))
+    ev_main = [[[torch.cuda.Event(enable_timing=True) for _ in range(len(b.stages) + 1)] for _ in views]
+               for _ in range(nst)]
+    ev_side = [[[torch.cuda.Event(enable_timing=True) for _ in range(len(b.side_stages) + 1)] for _ in views]
+               for _ in range(nst)]
     e_inst = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     e_inst[0].record()
-    for k in range(args.steps):
-        step(evs[k], evs_side[k])
+    for k in range(nst):
+        for j, v in enumerate(views):
+            b.step_view(v, ev_main[k][j], ev_side[k][j])
     e_inst[1].record()
     torch.cuda.synchronize()
-    ms_instrumented = e_inst[0].elapsed_time(e_inst[1]) / args.steps
-    stage_ms = {s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, s in enumerate(stages)}
-    stage_ms.update({s: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs_side]))
-                     for i, s in enumerate(side_stages)})
+    ms_instrumented = e_inst[0].elapsed_time(e_inst[1]) / nst
+    stage_times = {s: [e[i].elapsed_time(e[i + 1]) for row in ev_main for e in row] for i, s in enumerate(b.stages)}
+    stage_times.update({s: [e[i].elapsed_time(e[i + 1]) for row in ev_side for e in row]
+                        for i, s in enumerate(b.side_stages)})
+    stage_ms = {s: pct(x) for s, x in stage_times.items()}
+    stage_mean = {s: float(np.mean(x)) for s, x in stage_times.items()}
 
-    px = scene.width * scene.height
-    value = px / (ms * 1e-3) / 1e6
+    # the last view's buffers hold its lists and state: work units and the dominant
+    # kernel's launch time are taken there
+    last_view = views[-1]
+    px_view = scene.width * scene.height
+    value = len(views) * px_view / (ms * 1e-3) / 1e6
     N = scene.N
-    nvis = int((r.rec[:N, 15].view(torch.int32) > 0).sum().item()) if N else 0
-    if aa:  # pairs up to each pixel's last included entry of either layer
+    recs = [r.rec_views[k] for k in range(len(views))] if multi else [r.rec]
+    nvis = [int((x[:N, 15].view(torch.int32) > 0).sum().item()) if N else 0 for x in recs]
+    if b.aa:  # pairs up to each pixel's last included entry of either layer
         st_aa = r.state_aa.view(-1, 8)
         walked = int(torch.maximum(st_aa[:, 1].view(torch.int32), st_aa[:, 3].view(torch.int32)).sum().item())
+        units = {"walked_pairs": walked}
     else:
         walked = int(r.state_last.sum().item())  # pairs up to each pixel's last included entry
-    incl_frac = included_fraction(scene, view) if N else 0.0
+        units = composite_units(b, last_view) if N else {"walked_pairs": walked}
+    incl = units.get("included_pairs", 0)
 
-    # compulsory HBM bytes per stage (each input read once, each output written once)
-    V, F, HW, T, K, Pp = scene.V, scene.F, px, r.T, r.n_keys, r.n_pairs
-    d = scene.sh_degree
-    shb = 12 * (d + 1) ** 2 if d >= 0 else 12
-    alg_bytes = {
-        "bin": 12 * V + 12 * V + 12 * F + 8 * Pp + 4 * T,
-        "zbuffer": 4 * Pp + 12 * F + 12 * V + 8 * HW + 4 * T,
-        "project": N * (12 + 16 + 12 + 4 + shb + 64),
-        "sort_depth": 64 * N,
-        "sort": 28 * K + 8 * T,
-        # the composite forward: ids, records, face id + depth, colour behind (state_cm),
-        # rgb + depth + alpha, state_T + state_last
-        "fwd": 4 * K + 64 * nvis + 8 * HW + 12 * HW + 20 * HW + 8 * HW,
-        "bwd": 4 * K + 64 * nvis + 8 * HW + 8 * HW + 12 * HW + 20 * HW + 52 * nvis + 16 * HW,
-    }
-    if not aa:  # face ids read, state_cm written, screen vertices, colours and faces once
-        alg_bytes["shade"] = 4 * HW + 12 * HW + 24 * V + 12 * F
-    if aa:
-        # the layer: face ids, depths and colours of each pixel and its neighbours
-        # (one read each), screen vertices and faces once, the layer written (32 B)
-        alg_bytes["antialias"] = 4 * HW + 4 * HW + 12 * HW + 12 * V + 12 * F + 32 * HW
-        # the two-layer composite reads the layer instead of face id, depth and colour,
-        # and keeps 32 B of state instead of 8
-        alg_bytes["fwd"] += 32 * HW - 20 * HW + 24 * HW
-        alg_bytes["bwd"] += 32 * HW - 20 * HW + 24 * HW + 32 * HW
-        alg_bytes["antialias_bwd"] = 4 * HW + 4 * HW + 12 * HW + 32 * HW + 12 * V + 12 * F + 16 * HW + 8 * V
-    alg_flops = {
-        "fwd": walked * FLOPS_EVAL + walked * incl_frac * FLOPS_ACCUM,
-        "bwd": walked * FLOPS_EVAL + walked * incl_frac * FLOPS_GRAD,
-    }
-    # dominant single kernel: bin and sort are chains of many small kernels, the other
-    # stages are one main kernel each (the backward adds the tile walk, which also
-    # clears the record gradients, and the tile order: a few percent)
-    dom = max(["zbuffer", "project", "fwd", "bwd"], key=stage_ms.get)
-    kname = {"bwd": "k_composite_bwd", "fwd": "k_composite_fwd", "sort": "gm_sort_tiles",
-             "project": "k_project_gaussians", "zbuffer": "k_zbuffer", "bin": "gm_bin_triangles"}[dom]
-    kfile = {"bwd": "gm_composite.hip", "fwd": "gm_composite.hip", "sort": "gm_sort.hip",
-             "project": "gm_project.hip", "zbuffer": "gm_raster.hip", "bin": "gm_raster.hip"}[dom]
-    dom_s = stage_ms[dom] * 1e-3
-    if dom in alg_flops:
-        ach = alg_flops[dom] / dom_s / 1e12
-        roof = {"kernel": kname, "bound": "alu", "achieved": round(ach, 3), "peak": FP32_VALU_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / FP32_VALU_PEAK_TFLOPS, 4)}
-    else:
-        ach = alg_bytes[dom] / dom_s / 1e9
-        roof = {"kernel": kname, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4)}
-    tname = kname
-    if aa and dom in ("fwd", "bwd"):  # the two-layer instantiation of the composite kernel
-        roof["kernel"] = kname + "<two-layer>"
-        tname = kname + "_aa"
-    roof["traffic"] = measured_traffic(tname, kfile, args.config)
-    roof["units"] = {"walked_pairs": walked, "included_fraction": round(incl_frac, 4)} if dom in alg_flops \
-        else {"algorithmic_bytes": alg_bytes[dom]}
-    roof["launch_ms"] = round(stage_ms[dom], 4)
+    alg = algorithmic_bytes(scene, r, counts, nvis, b.aa)
+    total_alg = sum(sum(v.values()) for v in alg)
+    alg_flops = {"fwd": walked * FLOPS_EVAL + incl * FLOPS_ACCUM, "bwd": walked * FLOPS_EVAL + incl * FLOPS_GRAD}
 
-    next_stages = {"project_bwd": time_project_bwd(r, scene, view, args.steps)} if N else {}
-    if scene.F:
-        next_stages["mesh_bwd"] = time_mesh_bwd(r, scene, view, args.steps)
-        if aa:
-            next_stages["vscreen_bwd_ms"] = time_call(lambda: G.gm_vscreen_bwd(
-                cam, ds.mesh, r.g_vscreen, r.gm_verts, torch.cuda.current_stream().cuda_stream), args.steps)
+    # dominant single kernel by stage time (the sort and binning are chains of many
+    # small kernels; the other stages are one main kernel each)
+    dom = max(["zbuffer", "project", "fwd", "bwd"], key=lambda s: stage_mean.get(s, 0.0))
+    roof = roofline(b, dom, last_view, alg[-1], alg_flops, units, args)
 
-    total_alg = sum(alg_bytes.values())
-    # measured HBM traffic of a whole step (rocprofv3 counters, separate run) over the
-    # unprofiled step time; only for the default-path workload it was taken on
-    step_bytes = None if aa else measured_step_traffic(args.config)
+    step_bytes = None if b.aa else measured_step_traffic(name)
     hbm_measured = None if step_bytes is None else {
         "bytes_per_step": step_bytes, "GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "source": f"profiles/traffic_step_{args.config}.md"}
+        "source": f"profiles/traffic_step_{name}.md"}
     out = {
-        "metric": "hybrid render Mpixels/s fwd+bwd at 1080p",
+        "metric": "hybrid render Mpixels/s fwd+bwd at 1080p" if scene.height == 1080
+        else "hybrid render Mpixels/s fwd+bwd",
         "value": round(value, 3), "unit": "Mpixels/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded PCG64 scene generators)",
-        "config": {"workload": f"{args.config}: {WORKLOADS[args.config]}" + (", edge antialiasing" if aa else ""),
-                   "view": view,
-                   "width": scene.width, "height": scene.height, "faces": scene.F, "gaussians": N,
-                   "tri_tile_pairs": r.n_pairs, "keys": r.n_keys, "visible": nvis, "parallelism": "single GPU"},
-        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "ms_per_step_with_stage_events": round(ms_instrumented, 4),
+        "config": {"workload": f"{name}: {WORKLOADS[name]}" + (", edge antialiasing" if b.aa else "")
+                   + ("" if multi or len(scene.views) == 1 else f", view {views[0]} of {len(scene.views)}"),
+                   "views_per_step": len(views), "width": scene.width, "height": scene.height,
+                   "faces": scene.F, "gaussians": N, "tri_tile_pairs": [c[0] for c in counts],
+                   "keys": [c[1] for c in counts], "visible": nvis, "parallelism": "single GPU"},
+        "step_ms": pct(step_dist),
+        "view_ms": round(ms / len(views), 4),
+        "stage_ms": stage_ms,
+        "ms_per_view_with_stage_events": round(ms_instrumented / len(views), 4),
         "hbm_algorithmic_GBps": round(total_alg / (ms * 1e-3) / 1e9, 1),
         "hbm_algorithmic_frac": round(total_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "hbm_measured": hbm_measured,
         "roofline": roof,
-        "next_stages": next_stages,
         "wall_s": round(wall, 3),
     }
+    if multi and N:
+        out["projection"] = time_projection(b, views, args.steps)
+    if not multi:
+        ns = {"project_bwd": time_project_bwd(r, scene, views[0], args.steps)} if N else {}
+        if scene.F:
+            ns["mesh_bwd"] = time_mesh_bwd(r, scene, views[0], args.steps)
+        out["next_stages"] = ns
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(scene, view, args.cpu_tiles)
-    print(json.dumps(out), flush=True)
+        out["cpu_baseline"] = cpu_baseline(scene, views[0], args.cpu_tiles, len(views))
+    return out
 
 
-def main_batch(args, scene):
-    """Every view of the workload per step: one gm_project_gaussians_multi for all
-    views, then per view the lists, composite forward and backward, with each view's
-    mesh half and lists overlapped with the previous view's composite
-    (Renderer.views_step_pipelined).  Also times the views one after
-    another, and the batched projection against the per-view projection loop it
-    replaces."""
+def composite_units(b, view):
+    """Work units of the composite on the view whose state the renderer holds,
+    counted on the GPU: walked pairs (sum over pixels of the index of the last
+    included entry) from the forward state, and the counting build of the forward
+    (gm_composite_hybrid_fwd_stats, one launch outside the timed region): included
+    pairs, entries evaluated wave-wide, entries staged."""
     import torch
-    from differentiable_hybrid_mesh_amd.pipeline import DeviceScene, Renderer
-    ds = DeviceScene(scene)
-    r = Renderer(ds)
-    views = list(range(len(scene.views)))
-    grads = [ds.grads(v) for v in views]
-    r.fit_lists_views(views)
-    for _ in range(max(args.warmup, 1)):
-        r.views_step_pipelined(views, grads)
+    from differentiable_hybrid_mesh_amd import _lib as G
+    from differentiable_hybrid_mesh_amd.pipeline import _stream
+    r, s = b.r, b.scene
+    stats = torch.zeros(3, dtype=torch.int64, device="cuda")
+    out = [torch.empty_like(t) for t in (r.out_rgb, r.out_depth, r.out_alpha, r.state_T, r.state_last)]
+    G.gm_composite_hybrid_fwd_stats(b.ds.cams[view], r.rec, r.tile_ranges, r.sorted_ids, r.face_id, r.depth,
+                                    s.softness, r.state_cm, *out, stats, _stream())
     torch.cuda.synchronize()
-    if not r.read_counts():
-        raise RuntimeError("a list outgrew its capacity after fitting")
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record()
-    for _ in range(args.steps):
-        r.views_step_pipelined(views, grads)
-    t1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    if not r.read_counts():
-        raise RuntimeError("a list outgrew its capacity inside the timed region")
-    ms = t0.elapsed_time(t1) / args.steps
-    # the same views one after another (each view's halves overlapped only with each
-    # other), for comparison
-    t0.record()
-    for _ in range(args.steps):
-        r.views_step_async(views, grads)
-    t1.record()
-    torch.cuda.synchronize()
-    if not r.read_counts():
-        raise RuntimeError("a list outgrew its capacity inside the timed region")
-    ms_serial = t0.elapsed_time(t1) / args.steps
-    px = len(views) * scene.width * scene.height
-    value = px / (ms * 1e-3) / 1e6
+    inc, ev, staged = (int(x) for x in stats.tolist())
+    walked = int(r.state_last.sum().item())
+    return {"walked_pairs": walked, "included_pairs": inc, "included_fraction": round(inc / max(walked, 1), 4),
+            "wave_entries_fwd": ev, "entries_staged_fwd": staged, "counted_by": "gm_composite_hybrid_fwd_stats"}
 
-    # the projection alone: batched call vs one call per view (events on the stream)
+
+def algorithmic_bytes(scene, r, counts, nvis, aa):
+    """Compulsory HBM bytes per stage and view (each input read once, each output
+    written once), from each view's own counts."""
+    out = []
+    V, F, HW, T = scene.V, scene.F, scene.width * scene.height, r.T
+    N, d = scene.N, scene.sh_degree
+    shb = 12 * (d + 1) ** 2 if d >= 0 else 12
+    for (Pp, K), nv in zip(counts, nvis):
+        a = {
+            "bin": 12 * V + 12 * V + 12 * F + 8 * Pp + 4 * T,
+            "zbuffer": 4 * Pp + 12 * F + 12 * V + 8 * HW + 4 * T,
+            "project": N * (12 + 16 + 12 + 4 + shb + 64),
+            "sort_depth": 64 * N,
+            "sort": 28 * K + 8 * T,
+            # the composite forward: ids, records, face id + depth, colour behind (state_cm),
+            # rgb + depth + alpha, state_T + state_last
+            "fwd": 4 * K + 64 * nv + 8 * HW + 12 * HW + 20 * HW + 8 * HW,
+            "bwd": 4 * K + 64 * nv + 8 * HW + 8 * HW + 12 * HW + 20 * HW + 52 * nv + 16 * HW,
+        }
+        if not aa:  # face ids read, state_cm written, screen vertices, colours and faces once
+            a["shade"] = 4 * HW + 12 * HW + 24 * V + 12 * F
+        else:
+            # the layer: face ids, depths and colours of each pixel and its neighbours
+            # (one read each), screen vertices and faces once, the layer written (32 B)
+            a["antialias"] = 4 * HW + 4 * HW + 12 * HW + 12 * V + 12 * F + 32 * HW
+            # the two-layer composite reads the layer instead of face id, depth and colour,
+            # and keeps 32 B of state instead of 8
+            a["fwd"] += 32 * HW - 20 * HW + 24 * HW
+            a["bwd"] += 32 * HW - 20 * HW + 24 * HW + 32 * HW
+            a["antialias_bwd"] = 4 * HW + 4 * HW + 12 * HW + 32 * HW + 12 * V + 12 * F + 16 * HW + 8 * V
+        out.append(a)
+    return out
+
+
+KERNEL_OF = {"bwd": ("k_composite_bwd", "gm_composite.hip"), "fwd": ("k_composite_fwd", "gm_composite.hip"),
+             "project": ("k_project_gaussians", "gm_project.hip"), "zbuffer": ("k_zbuffer", "gm_raster.hip")}
+
+
+def roofline(b, dom, view, alg_bytes, alg_flops, units, args):
+    """Roofline entry of the dominant kernel, its launch timed on its own (K launches
+    on the current stream between two HIP events, after the timed steps, on the
+    buffers of ``view``)."""
+    import torch
+    r = b.r
+    g = b.grads[view]
+    launch = {
+        "bwd": (lambda: r.composite_bwd_aa(view, g["rgb"], g["depth"], g["alpha"])) if b.aa else
+               (lambda: r.composite_bwd(view, g["rgb"], g["depth"], g["alpha"])),
+        "fwd": (lambda: r.composite_fwd_aa(view)) if b.aa else (lambda: r.composite_fwd_shaded(view)),
+        "project": lambda: r.project(view),
+        "zbuffer": lambda: r.bin_and_zbuffer(view),
+    }[dom]
+    launch_ms = time_call(launch, args.steps)
+    kname, kfile = KERNEL_OF[dom]
+    if dom in alg_flops and units.get("included_pairs") is not None:
+        ach = alg_flops[dom] / (launch_ms * 1e-3) / 1e12
+        roof = {"kernel": kname, "bound": "alu", "achieved": round(ach, 3), "peak": FP32_VALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / FP32_VALU_PEAK_TFLOPS, 4),
+                "frac_of_packed_fp32_peak": round(ach / FP32_VALU_PACKED_TFLOPS, 4)}
+    else:
+        nbytes = alg_bytes[dom] if dom != "zbuffer" else alg_bytes["bin"] + alg_bytes["zbuffer"]
+        ach = nbytes / (launch_ms * 1e-3) / 1e9
+        roof = {"kernel": kname, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+        units = {"algorithmic_bytes": nbytes}
+    tname = kname + ("_aa" if b.aa and dom in ("fwd", "bwd") else "")
+    roof["traffic"] = measured_traffic(tname, kfile, b.scene.name)
+    roof["units"] = units
+    roof["launch_ms"] = round(launch_ms, 4)
+    roof["launch"] = "gm_composite_hybrid_bwd (tile walk + order + composite)" if dom == "bwd" else dom
+    return roof
+
+
+def time_projection(b, views, steps):
+    """The batched projection of every view against one projection call per view."""
+    import torch
+    r, scene = b.r, b.scene
     N, d = scene.N, scene.sh_degree
     shb = 12 * (d + 1) ** 2 if d >= 0 else 12
     per_in = 12 + 16 + 12 + 4 + shb
     e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     e[0].record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         r.project_views(views)
     e[1].record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         for v in views:
             r.project(v)
     e[2].record()
     torch.cuda.synchronize()
-    ms_multi = e[0].elapsed_time(e[1]) / args.steps
-    ms_loop = e[1].elapsed_time(e[2]) / args.steps
+    ms_multi = e[0].elapsed_time(e[1]) / steps
+    ms_loop = e[1].elapsed_time(e[2]) / steps
     b_multi = N * (per_in + 64 * len(views))
-    b_loop = len(views) * N * (per_in + 64)
     ach = b_multi / (ms_multi * 1e-3) / 1e9
-    out = {
-        "metric": "hybrid render Mpixels/s fwd+bwd at 1080p",
-        "value": round(value, 3), "unit": "Mpixels/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded PCG64 scene generators)",
-        "config": {"workload": f"{args.config}: {WORKLOADS[args.config]}; all {len(views)} views per step, "
-                               "one batched projection, views pipelined", "views": len(views), "width": scene.width,
-                   "height": scene.height, "faces": scene.F, "gaussians": N, "parallelism": "single GPU"},
-        "roofline": {"kernel": "k_project_gaussians_multi", "bound": "hbm", "achieved": round(ach, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-                     "units": {"algorithmic_bytes": b_multi}, "launch_ms": round(ms_multi, 4)},
-        "views_one_after_another_ms_per_step": round(ms_serial, 4),
-        "projection": {"batched_ms": round(ms_multi, 4), "per_view_loop_ms": round(ms_loop, 4),
-                       "batched_algorithmic_bytes": b_multi, "loop_algorithmic_bytes": b_loop,
-                       "speedup": round(ms_loop / ms_multi, 3)},
-        "wall_s": round(wall, 3),
-    }
-    print(json.dumps(out), flush=True)
+    return {"kernel": "k_project_gaussians_multi", "batched_ms": round(ms_multi, 4),
+            "per_view_loop_ms": round(ms_loop, 4), "batched_algorithmic_bytes": b_multi,
+            "loop_algorithmic_bytes": len(views) * N * (per_in + 64), "achieved_GBps": round(ach, 1),
+            "frac": round(ach / HBM_PEAK_GBS, 4), "speedup": round(ms_loop / ms_multi, 3)}
 
 
 def time_call(fn, steps):
@@ -461,7 +529,7 @@ def time_call(fn, steps):
         fn()
     e1.record()
     torch.cuda.synchronize()
-    return round(e0.elapsed_time(e1) / steps, 4)
+    return e0.elapsed_time(e1) / steps
 
 
 def time_project_bwd(r, scene, view, steps):
@@ -480,14 +548,7 @@ def time_project_bwd(r, scene, view, steps):
     per_unlisted = 4 + 4 * (3 + 4 + 3 + 1 + 3 * K)
     nbytes = nl * per_listed + (N - nl) * per_unlisted
     r.project_bwd(view)  # allocates the gradient buffers
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        r.project_bwd(view)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = time_call(lambda: r.project_bwd(view), steps)
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"kernel": "k_project_bwd", "ms": round(ms, 4), "bound": "hbm", "achieved": round(gbs, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -507,36 +568,16 @@ def time_mesh_bwd(r, scene, view, steps):
     per_vertex = 12 * (1 + (scene.vcolor is not None) + (scene.vnormal is not None))
     nbytes = (4 * scene.width * scene.height + 16 * covered + 12 * F + per_vertex * V + per_vertex * V)
     r.mesh_bwd(view)  # allocates the gradient buffers
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        r.mesh_bwd(view)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms = time_call(lambda: r.mesh_bwd(view), steps)
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"kernel": "k_mesh_bwd", "ms": round(ms, 4), "bound": "hbm", "achieved": round(gbs, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
             "algorithmic_bytes": nbytes, "covered_pixels": covered}
 
 
-def included_fraction(scene, view, ntiles=48):
-    """Included / walked pairs of the reverse pass, counted by the oracle on a fixed
-    sample of tiles of the same view (used to weight the per-pair flop figures)."""
-    import oracle
-    T = scene.tiles_x * scene.tiles_y
-    rng = np.random.default_rng(5)
-    tiles = np.sort(rng.choice(T, size=min(ntiles, T), replace=False)).astype(np.int32)
-    res = oracle.render_view(scene, view, tiles=tiles, cull=True, backward=False)
-    c = res["comp"]
-    m = c["n_last"] >= 0
-    w = int(c["n_last"][m].sum())
-    return float(c["n_incl"][m].sum()) / w if w else 0.0
-
-
-def cpu_baseline(scene, view, ntiles):
-    """The oracle (fwd+bwd, OpenMP on the host cores) on a bounded sample of tiles."""
+def cpu_baseline(scene, view, ntiles, views_per_step):
+    """The oracle (fwd+bwd, OpenMP on the host cores) on a bounded sample of tiles of
+    one view; seconds per view scaled from the sample to every tile."""
     import oracle
     T = scene.tiles_x * scene.tiles_y
     rng = np.random.default_rng(123)
@@ -547,8 +588,10 @@ def cpu_baseline(scene, view, ntiles):
     dt = time.perf_counter() - t
     px = len(tiles) * 256
     return {"value": round(px / dt / 1e6, 6), "unit": "Mpixels/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(), "s_per_view": round(dt * T / len(tiles), 3),
             "sample": f"{len(tiles)} of {T} 16x16 tiles of view {view} ({px} px): projection and depth order of "
-                      f"all Gaussians, z-buffer, lists, composite and reverse mode of those tiles; {dt:.1f} s"}
+                      f"all Gaussians, z-buffer, lists, composite and reverse mode of those tiles; {dt:.1f} s"
+                      + (f"; a step renders {views_per_step} views" if views_per_step > 1 else "")}
 
 
 if __name__ == "__main__":
