@@ -19,7 +19,8 @@ the composite; the measured HBM traffic of a whole step when its counter summary
 matches the kernel sources; and the CPU oracle's throughput on a bounded sample of
 the same workload.
 
-``--all-configs`` prints one line for each workload.  ``--copy-calibration`` instead
+``--all-configs`` prints one line for each workload (each measured in a process of
+its own).  ``--copy-calibration`` instead
 runs a plain device copy of known size; profiled with ``rocprofv3 --pmc FETCH_SIZE``
 / ``WRITE_SIZE`` it gives the factors that turn those counters into bytes.
 """
@@ -173,12 +174,22 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.all_configs:
+        # one child process per workload: the streams a process creates are spread
+        # over the GPU's hardware queues in creation order, so a workload measured
+        # after others in one process can find its streams sharing a queue
+        import subprocess
+        rc = 0
+        for name in WORKLOADS:
+            argv = [sys.executable, "-u", os.path.abspath(__file__), "--config", name, "--steps", str(args.steps),
+                    "--warmup", str(args.warmup), "--cpu-tiles", str(args.cpu_tiles)]
+            if args.no_cpu_baseline:
+                argv.append("--no-cpu-baseline")
+            rc |= subprocess.run(argv).returncode
+        sys.exit(rc)
     import torch
     torch.cuda.set_device(0)
-    configs = list(WORKLOADS) if args.all_configs else [args.config]
-    for name in configs:
-        out = run_config(args, name)
-        print(json.dumps(out), flush=True)
+    print(json.dumps(run_config(args, args.config)), flush=True)
 
 
 class Bench:

@@ -25,10 +25,12 @@ namespace gm {
 
 constexpr int MB_THREADS = 256;
 constexpr int MB_TILE = 16;  // a block covers a 16 x 16 pixel tile, a wave 16 x 4 of it
-constexpr int MB_SLOTS_LOG2 = 10;
+// LDS table slots per block: a 16 x 16 tile of a dense mesh shows a few dozen
+// vertices (hundreds at a limb of tiny, foreshortened triangles); a key that finds
+// the table full goes straight to a global atomic.
+constexpr int MB_SLOTS_LOG2 = 9;
 constexpr int MB_SLOTS = 1 << MB_SLOTS_LOG2;
 static_assert(MB_TILE * MB_TILE == MB_THREADS, "one thread per pixel of the tile");
-static_assert(3 * MB_THREADS < MB_SLOTS, "the corner table never fills");
 
 struct MeshBwdParams {
     DevCamera cam;
@@ -117,9 +119,8 @@ __device__ __forceinline__ constexpr int vertex_plane(int j)
 }
 
 // Slot of `key` in an open-addressed LDS table of MB_SLOTS entries (empty = -1),
-// claiming a free one on first sight.  A block touches at most 3 x MB_THREADS keys,
-// fewer than MB_SLOTS, so the probe always ends on a free or matching slot; the
-// bound only makes the loop's end explicit (-1: the caller adds to global memory).
+// claiming a free one on first sight; -1 when a whole probe sequence finds neither
+// the key nor a free slot (the caller then adds to global memory).
 __device__ __forceinline__ int table_slot(int* keys, int key)
 {
     unsigned h = ((unsigned)key * 2654435761u) >> (32 - MB_SLOTS_LOG2);
@@ -149,6 +150,15 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
     __shared__ float s_vval[NVP][MB_SLOTS];
     __shared__ int s_tkey[TEX ? MB_SLOTS : 1];
     __shared__ float s_tval[2][TEX ? MB_SLOTS : 1];
+    const int W = P.cam.width, H = P.cam.height;
+    const int tiles_x = (W + MB_TILE - 1) / MB_TILE;
+    const int px = (int)(blockIdx.x % tiles_x) * MB_TILE + (int)(threadIdx.x % MB_TILE);
+    const int py = (int)(blockIdx.x / tiles_x) * MB_TILE + (int)(threadIdx.x / MB_TILE);
+    const int pix = py * W + px;
+    const int f = (px < W && py < H) ? face_id[pix] : -1;
+    // a tile the mesh does not reach has nothing to add (uniform exit, before any
+    // table work)
+    if (!__syncthreads_or(f >= 0)) return;
     for (int s = threadIdx.x; s < MB_SLOTS; s += MB_THREADS) {
         s_vkey[s] = -1;
 #pragma unroll
@@ -159,11 +169,6 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
             s_tval[1][s] = 0.0f;
         }
     }
-    const int W = P.cam.width, H = P.cam.height;
-    const int tiles_x = (W + MB_TILE - 1) / MB_TILE;
-    const int px = (int)(blockIdx.x % tiles_x) * MB_TILE + (int)(threadIdx.x % MB_TILE);
-    const int py = (int)(blockIdx.x / tiles_x) * MB_TILE + (int)(threadIdx.x / MB_TILE);
-    const int pix = py * W + px;
     float gl[13];
 #pragma unroll
     for (int i = 0; i < 13; ++i) gl[i] = 0.0f;
@@ -174,7 +179,6 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
 #pragma unroll
         for (int j = 0; j < 11; ++j) acc[k][j] = 0.0f;
     int vi[3] = {0, 0, 0}, ti[3] = {0, 0, 0};
-    const int f = (px < W && py < H) ? face_id[pix] : -1;
     if (f >= 0) {
         const double pu = px + 0.5, pv = py + 0.5;
         double R[9], t[3];
