@@ -370,14 +370,15 @@ void oc_project_gaussians(const oc_camera* cam, int N, const float* means, const
         float sig = sqrtf(var > 1e-12f ? var : 1e-12f);
         float u = (fx * xc) / zc + cx;
         float v = (fy * yc) / zc + cy;
-        float m = (a + c) * 0.5f;
-        float disc = m * m - det;
-        float lam = m + sqrtf(disc > 0.1f ? disc : 0.1f);
-        float rad = ceilf(3.0f * sqrtf(lam));
+        /* tile rect: the bounding box of the 3-sigma ellipse of the dilated 2D
+         * covariance, half-widths ceil(3 sqrt(a)) and ceil(3 sqrt(c)) pixels along
+         * x and y (the ellipse (d^T Sigma2D^-1 d) <= 9 reaches |dx| = 3 sqrt(a)) */
+        float radx = ceilf(3.0f * sqrtf(a));
+        float rady = ceilf(3.0f * sqrtf(c));
         int r4[4] = {0, 0, 0, 0};
         if (ok) {
-            float fx0 = floorf((u - rad) / 16.0f), fx1 = ceilf((u + rad) / 16.0f);
-            float fy0 = floorf((v - rad) / 16.0f), fy1 = ceilf((v + rad) / 16.0f);
+            float fx0 = floorf((u - radx) / 16.0f), fx1 = ceilf((u + radx) / 16.0f);
+            float fy0 = floorf((v - rady) / 16.0f), fy1 = ceilf((v + rady) / 16.0f);
             fx0 = fminf(fmaxf(fx0, 0.0f), (float)TX);
             fx1 = fminf(fmaxf(fx1, 0.0f), (float)TX);
             fy0 = fminf(fmaxf(fy0, 0.0f), (float)TY);
