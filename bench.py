@@ -104,21 +104,17 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
 
 
-def source_digest(kernel_file):
-    with open(os.path.join(ROOT, "differentiable_hybrid_mesh_amd", "csrc", kernel_file), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
-def measured_traffic(kernel, kernel_file, config):
+def measured_traffic(kernel, config):
     """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary of this
-    kernel, or None when the kernel source changed since it was taken."""
+    kernel, or None when any kernel source changed since it was taken (a kernel's
+    traffic also depends on what the kernels before it produce, e.g. the lists)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{config}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    m = re.search(r"sources_sha256_16:\s*([0-9a-f]+)", text)
     b = re.search(r"hbm_bytes_per_launch:\s*([0-9.e+]+)", text)
-    if not m or not b or m.group(1) != source_digest(kernel_file):
+    if not m or not b or m.group(1) != sources_digest():
         return None
     return float(b.group(1))
 
@@ -465,8 +461,8 @@ def algorithmic_bytes(scene, r, counts, nvis, aa):
     return out
 
 
-KERNEL_OF = {"bwd": ("k_composite_bwd", "gm_composite.hip"), "fwd": ("k_composite_fwd", "gm_composite.hip"),
-             "project": ("k_project_gaussians", "gm_project.hip"), "zbuffer": ("k_zbuffer", "gm_raster.hip")}
+KERNEL_OF = {"bwd": "k_composite_bwd", "fwd": "k_composite_fwd", "project": "k_project_gaussians",
+             "zbuffer": "k_zbuffer"}
 
 
 def roofline(b, dom, view, alg_bytes, alg_flops, units, args):
@@ -484,7 +480,7 @@ def roofline(b, dom, view, alg_bytes, alg_flops, units, args):
         "zbuffer": lambda: r.bin_and_zbuffer(view),
     }[dom]
     launch_ms = time_call(launch, args.steps)
-    kname, kfile = KERNEL_OF[dom]
+    kname = KERNEL_OF[dom]
     if dom in alg_flops and units.get("included_pairs") is not None:
         ach = alg_flops[dom] / (launch_ms * 1e-3) / 1e12
         roof = {"kernel": kname, "bound": "alu", "achieved": round(ach, 3), "peak": FP32_VALU_PEAK_TFLOPS,
@@ -497,7 +493,7 @@ def roofline(b, dom, view, alg_bytes, alg_flops, units, args):
                 "frac": round(ach / HBM_PEAK_GBS, 4)}
         units = {"algorithmic_bytes": nbytes}
     tname = kname + ("_aa" if b.aa and dom in ("fwd", "bwd") else "")
-    roof["traffic"] = measured_traffic(tname, kfile, b.scene.name)
+    roof["traffic"] = measured_traffic(tname, b.scene.name)
     roof["units"] = units
     roof["launch_ms"] = round(launch_ms, 4)
     roof["launch"] = "gm_composite_hybrid_bwd (tile walk + order + composite)" if dom == "bwd" else dom

@@ -117,14 +117,14 @@ __device__ inline void project_view(const DevCamera& cam, const WorldGauss& g, f
     const float sig = sqrtf(var > 1e-12f ? var : 1e-12f);
     const float u = (cam.fx * xc) / zc + cam.cx;
     const float v = (cam.fy * yc) / zc + cam.cy;
-    const float m = (a + c) * 0.5f;
-    const float disc = m * m - det;
-    const float lam = m + sqrtf(disc > 0.1f ? disc : 0.1f);
-    const float rad = ceilf(3.0f * sqrtf(lam));
+    // tile rect: the box of the 3-sigma ellipse of the dilated 2D covariance, whose
+    // half-widths along x and y are 3 sqrt(a) and 3 sqrt(c), rounded up to pixels
+    const float radx = ceilf(3.0f * sqrtf(a));
+    const float rady = ceilf(3.0f * sqrtf(c));
     int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
     if (ok) {
-        float fx0 = floorf((u - rad) / 16.0f), fx1 = ceilf((u + rad) / 16.0f);
-        float fy0 = floorf((v - rad) / 16.0f), fy1 = ceilf((v + rad) / 16.0f);
+        float fx0 = floorf((u - radx) / 16.0f), fx1 = ceilf((u + radx) / 16.0f);
+        float fy0 = floorf((v - rady) / 16.0f), fy1 = ceilf((v + rady) / 16.0f);
         fx0 = fminf(fmaxf(fx0, 0.0f), (float)cam.tx);
         fx1 = fminf(fmaxf(fx1, 0.0f), (float)cam.tx);
         fy0 = fminf(fmaxf(fy0, 0.0f), (float)cam.ty);

@@ -172,7 +172,8 @@ gm_status gm_raster_zbuffer(const gm_camera* cam, const gm_mesh* mesh, const flo
  *   13 int32 tx0 | ty0 << 16, 14 int32 tx1 | ty1 << 16 (tile rect, exclusive),
  *   15 int32 number of tiles in the rect (0 = not listed).
  * The decision fields (0..5, 9..15) are evaluated in fp32 in a fixed order with no
- * fused multiply-add; the rect uses radius ceil(3 sqrt(lambda_max)).  A Gaussian is
+ * fused multiply-add; the rect covers the box of the 3-sigma ellipse, half-widths
+ * ceil(3 sqrt(Sigma2D_xx)) and ceil(3 sqrt(Sigma2D_yy)) pixels.  A Gaussian is
  * not listed when z_c < near_z, det <= 0 or its rect misses the image.
  * ------------------------------------------------------------------------- */
 gm_status gm_project_gaussians(const gm_camera* cam, int32_t N, const float* means,
