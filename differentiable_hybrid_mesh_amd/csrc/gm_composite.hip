@@ -658,6 +658,46 @@ __device__ __forceinline__ float wave_sum16(const float* v, int lane)
     return d;
 }
 
+// The same reduction of the first 10 values only (a wave off the mesh, where the
+// four depth-density sums are zero): 5 + 3 + 2 + 1 exchanges before the quad steps.
+// Every value meets the lanes in the same pairing order as in wave_sum16 (l ^ 32,
+// l ^ 16, l ^ 8, the half-row mirror, the quad), so its total is bit-identical.
+// On return lane l holds the total of value basis10(l) when (l & 3) == 0 and that
+// index is not negative.
+__device__ __forceinline__ float wave_sum10(const float* v, int lane)
+{
+    float a[5], b[3];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {  // lanes 0-31 keep v[i], lanes 32-63 keep v[5+i]
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[5 + i]), false,
+                                                        false);
+        a[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {  // even rows keep a[i], odd rows a[3+i] (a[2] alone: odd rows unused)
+        const float hi = i < 2 ? a[3 + i] : a[2];
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[i]), __float_as_uint(hi), false, false);
+        b[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    const bool h3 = lane & 8, h2 = lane & 4;
+    // partner lane ^ 8: pair (b0, b2) split by bit 3; b1 alone (lanes with bit 3 unused)
+    const float c0 = (h3 ? b[2] : b[0]) + dpp<0x128>(h3 ? b[0] : b[2]);
+    const float c1 = b[1] + dpp<0x128>(b[1]);
+    const float send = h2 ? c0 : c1;
+    float d = (h2 ? c1 : c0) + dpp<0x141>(send);
+    d += dpp<0x4E>(d);
+    d += dpp<0xB1>(d);
+    return d;
+}
+
+// Value index whose total wave_sum10 leaves in lane l (l & 3 == 0), or -1.
+__device__ __forceinline__ int basis10(int lane)
+{
+    const bool H = lane & 32, R = lane & 16, h3 = lane & 8, h2 = lane & 4;
+    const int ai = h3 ? ((h2 || R) ? -1 : 2) : ((R ? 3 : 0) + (h2 ? 1 : 0));
+    return ai < 0 ? -1 : ai + (H ? 5 : 0);
+}
+
 // AA = true: the reverse mode of the two-layer form.  The back layer sees the
 // upstream gradients scaled by k = T_F (1 - a_m) and, behind it, bg (depth 0) and
 // the alpha term; per entry dL/dalpha = f dL/dalpha_F + (1 - f) dL/dalpha_B and
@@ -718,8 +758,10 @@ __global__ void __launch_bounds__(TO_THREADS) k_tile_order(int T, const int32_t*
     order_tiles_desc(T, [=](int t) { return walk[t]; }, order);
 }
 
+// Six blocks of the backward fit a CU's LDS; the register budget is held to the
+// same six waves per SIMD (80 VGPRs; the two-layer form needs more and runs five).
 template <bool AA>
-__global__ void __launch_bounds__(CT)
+__global__ void __launch_bounds__(CT) __attribute__((amdgpu_waves_per_eu(AA ? 5 : 6, AA ? 5 : 6)))
 k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* __restrict__ state_last,
                 const float* __restrict__ state_cm, const float* __restrict__ layer,
                 const float* __restrict__ state_aa, const float* __restrict__ g_rgb,
@@ -901,18 +943,24 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
                 gr[7] = Hx * dx;
                 gr[8] = Hx * dy;
                 gr[9] = Hy * dy;
-                const float ds = (al * pdf) * dsF;
-                gr[10] = ds;
-                gr[11] = ds * dx;
-                gr[12] = ds * dy;
-                gr[13] = ds * sv;
-                gr[14] = 0.0f;
-                gr[15] = 0.0f;
-                gD = __builtin_fmaf(g.d.y, ds, gD);
-                if (__ballot(act)) {
-                    const float v = wave_sum16(gr, lane);
-                    const int c = lane >> 2;
-                    if ((lane & 3) == 0 && c < NBASIS && v != 0.0f) atomicAdd(&s_acc[k][c], v);
+                if (wave_on) {  // uniform; off the mesh the density (and so ds) is zero
+                    const float ds = (al * pdf) * dsF;
+                    gr[10] = ds;
+                    gr[11] = ds * dx;
+                    gr[12] = ds * dy;
+                    gr[13] = ds * sv;
+                    gr[14] = 0.0f;
+                    gr[15] = 0.0f;
+                    gD = __builtin_fmaf(g.d.y, ds, gD);
+                    if (__ballot(act)) {
+                        const float v = wave_sum16(gr, lane);
+                        const int c = lane >> 2;
+                        if ((lane & 3) == 0 && c < NBASIS && v != 0.0f) atomicAdd(&s_acc[k][c], v);
+                    }
+                } else if (__ballot(act)) {
+                    const float v = wave_sum10(gr, lane);
+                    const int c = basis10(lane);
+                    if ((lane & 3) == 0 && c >= 0 && v != 0.0f) atomicAdd(&s_acc[k][c], v);
                 }
             }
         }
