@@ -17,6 +17,7 @@
 #pragma clang fp contract(off)
 
 #include <mutex>
+#include <type_traits>
 
 #include "gm_internal.h"
 
@@ -886,84 +887,93 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
             }
         }
         __syncthreads();
-        for (int i = (CBB + 63) / 64 - 1; i >= 0; --i) {
-            unsigned long long mm = __ballot(i * 64 + lane < CBB && ((s_m[i * 64 + lane] >> wave) & 1));
-            while (mm) {
-                const int kk = 63 - __builtin_clzll(mm);
-                mm &= ~(1ull << kk);
-                const int k = i * 64 + kk;
-                const Staged g = s_g[k];  // one 64-byte LDS broadcast read
-                const int rel = b0 + k - start;
-                // inactive lanes carry zeros through the same arithmetic
-                const Pair pr = eval_pair(g, pxc, pyc, on, wave_on, D, P.softness);
-                const float dx = pr.dx, dy = pr.dy, oG = pr.oG, al = pr.al, f = pr.f, pdf = pr.pdf, sv = pr.s;
-                const float aF = pr.aF;
-                bool act = (rel < last) & pr.ok;
-                // per-pixel basis sums; the 13 record gradients are linear in them
-                // (formed once per entry at the flush):
-                //  0-2 w GC, 3 w GZ, 4 H, 5 H dx, 6 H dy, 7 H dx^2, 8 H dx dy, 9 H dy^2,
-                //  10 ds, 11 ds dx, 12 ds dy, 13 ds s   (H = o G dL/dalpha, ds = dL/ds)
-                const float aFe = act ? aF : 0.0f;
-                // 1 - alpha_F >= 0.01: a hardware reciprocal (1 ulp) keeps the
-                // recovered transmittance far inside the gradient tolerance
-                const float iom = __builtin_amdgcn_rcpf(1.0f - aFe);
-                const float Ti = T * iom;
-                const float w = aFe * Ti;
-                const float Vv = __builtin_fmaf(GC0, g.b.z, __builtin_fmaf(GC1, g.b.w, __builtin_fmaf(GC2, g.c.x, GZ * g.c.y)));
-                const float daF = act ? __builtin_fmaf(Ti, Vv, -acc * iom) : 0.0f;
-                acc = __builtin_fmaf(w, Vv, acc);
-                T = Ti;
-                float wt = w, da = f * daF, dsF = daF;
-                if constexpr (AA) {
-                    const float aB = al * pr.fb;
-                    const bool actB = (rel < lastB) & !(pr.q > g.d.z) & (al >= SKIP_ALPHA) & (aB >= SKIP_ALPHA);
-                    const float aBe = actB ? aB : 0.0f;
-                    const float iomB = __builtin_amdgcn_rcpf(1.0f - aBe);
-                    const float TiB = TBw * iomB;
-                    const float wB = aBe * TiB;
-                    const float VB = kB * Vv;
-                    const float daB = actB ? __builtin_fmaf(TiB, VB, -accB * iomB) : 0.0f;
-                    accB = __builtin_fmaf(wB, VB, accB);
-                    TBw = TiB;
-                    wt = __builtin_fmaf(kB, wB, w);
-                    da = __builtin_fmaf(pr.fb, daB, da);
-                    dsF = daF - daB;
-                    act = act | actB;
-                }
-                float gr[16];
-                gr[0] = wt * GC0;
-                gr[1] = wt * GC1;
-                gr[2] = wt * GC2;
-                gr[3] = wt * GZ;
-                const float H = oG <= ALPHA_MAX ? oG * da : 0.0f;
-                const float Hx = H * dx, Hy = H * dy;
-                gr[4] = H;
-                gr[5] = Hx;
-                gr[6] = Hy;
-                gr[7] = Hx * dx;
-                gr[8] = Hx * dy;
-                gr[9] = Hy * dy;
-                if (wave_on) {  // uniform; off the mesh the density (and so ds) is zero
-                    const float ds = (al * pdf) * dsF;
-                    gr[10] = ds;
-                    gr[11] = ds * dx;
-                    gr[12] = ds * dy;
-                    gr[13] = ds * sv;
-                    gr[14] = 0.0f;
-                    gr[15] = 0.0f;
-                    gD = __builtin_fmaf(g.d.y, ds, gD);
-                    if (__ballot(act)) {
-                        const float v = wave_sum16(gr, lane);
-                        const int c = lane >> 2;
-                        if ((lane & 3) == 0 && c < NBASIS && v != 0.0f) atomicAdd(&s_acc[k][c], v);
+        // the entries of the batch, back to front; instantiated apart for waves with
+        // and without a pixel on the mesh (a uniform choice made once per wave), so
+        // each form is one straight-line loop body
+        auto entries = [&](auto on_mesh) {
+            constexpr bool ON = decltype(on_mesh)::value;
+            for (int i = (CBB + 63) / 64 - 1; i >= 0; --i) {
+                unsigned long long mm = __ballot(i * 64 + lane < CBB && ((s_m[i * 64 + lane] >> wave) & 1));
+                while (mm) {
+                    const int kk = 63 - __builtin_clzll(mm);
+                    mm &= ~(1ull << kk);
+                    const int k = i * 64 + kk;
+                    const Staged g = s_g[k];  // one 64-byte LDS broadcast read
+                    const int rel = b0 + k - start;
+                    // inactive lanes carry zeros through the same arithmetic
+                    const Pair pr = eval_pair(g, pxc, pyc, on, ON, D, P.softness);
+                    const float dx = pr.dx, dy = pr.dy, oG = pr.oG, al = pr.al, f = pr.f, pdf = pr.pdf, sv = pr.s;
+                    const float aF = pr.aF;
+                    bool act = (rel < last) & pr.ok;
+                    // per-pixel basis sums; the 13 record gradients are linear in them
+                    // (formed once per entry at the flush):
+                    //  0-2 w GC, 3 w GZ, 4 H, 5 H dx, 6 H dy, 7 H dx^2, 8 H dx dy, 9 H dy^2,
+                    //  10 ds, 11 ds dx, 12 ds dy, 13 ds s   (H = o G dL/dalpha, ds = dL/ds)
+                    const float aFe = act ? aF : 0.0f;
+                    // 1 - alpha_F >= 0.01: a hardware reciprocal (1 ulp) keeps the
+                    // recovered transmittance far inside the gradient tolerance
+                    const float iom = __builtin_amdgcn_rcpf(1.0f - aFe);
+                    const float Ti = T * iom;
+                    const float w = aFe * Ti;
+                    const float Vv = __builtin_fmaf(GC0, g.b.z,
+                                                    __builtin_fmaf(GC1, g.b.w, __builtin_fmaf(GC2, g.c.x, GZ * g.c.y)));
+                    const float daF = act ? __builtin_fmaf(Ti, Vv, -acc * iom) : 0.0f;
+                    acc = __builtin_fmaf(w, Vv, acc);
+                    T = Ti;
+                    float wt = w, da = f * daF, dsF = daF;
+                    if constexpr (AA) {
+                        const float aB = al * pr.fb;
+                        const bool actB = (rel < lastB) & !(pr.q > g.d.z) & (al >= SKIP_ALPHA) & (aB >= SKIP_ALPHA);
+                        const float aBe = actB ? aB : 0.0f;
+                        const float iomB = __builtin_amdgcn_rcpf(1.0f - aBe);
+                        const float TiB = TBw * iomB;
+                        const float wB = aBe * TiB;
+                        const float VB = kB * Vv;
+                        const float daB = actB ? __builtin_fmaf(TiB, VB, -accB * iomB) : 0.0f;
+                        accB = __builtin_fmaf(wB, VB, accB);
+                        TBw = TiB;
+                        wt = __builtin_fmaf(kB, wB, w);
+                        da = __builtin_fmaf(pr.fb, daB, da);
+                        dsF = daF - daB;
+                        act = act | actB;
                     }
-                } else if (__ballot(act)) {
-                    const float v = wave_sum10(gr, lane);
-                    const int c = basis10(lane);
-                    if ((lane & 3) == 0 && c >= 0 && v != 0.0f) atomicAdd(&s_acc[k][c], v);
+                    float gr[16];
+                    gr[0] = wt * GC0;
+                    gr[1] = wt * GC1;
+                    gr[2] = wt * GC2;
+                    gr[3] = wt * GZ;
+                    const float H = oG <= ALPHA_MAX ? oG * da : 0.0f;
+                    const float Hx = H * dx, Hy = H * dy;
+                    gr[4] = H;
+                    gr[5] = Hx;
+                    gr[6] = Hy;
+                    gr[7] = Hx * dx;
+                    gr[8] = Hx * dy;
+                    gr[9] = Hy * dy;
+                    if constexpr (ON) {
+                        const float ds = (al * pdf) * dsF;
+                        gr[10] = ds;
+                        gr[11] = ds * dx;
+                        gr[12] = ds * dy;
+                        gr[13] = ds * sv;
+                        gr[14] = 0.0f;
+                        gr[15] = 0.0f;
+                        gD = __builtin_fmaf(g.d.y, ds, gD);
+                        if (__ballot(act)) {
+                            const float v = wave_sum16(gr, lane);
+                            const int c = lane >> 2;
+                            if ((lane & 3) == 0 && c < NBASIS && v != 0.0f) atomicAdd(&s_acc[k][c], v);
+                        }
+                    } else if (__ballot(act)) {  // off the mesh the density (and so ds) is zero
+                        const float v = wave_sum10(gr, lane);
+                        const int c = basis10(lane);
+                        if ((lane & 3) == 0 && c >= 0 && v != 0.0f) atomicAdd(&s_acc[k][c], v);
+                    }
                 }
             }
-        }
+        };
+        if (wave_on) entries(std::true_type{});
+        else entries(std::false_type{});
         __syncthreads();
         if ((int)threadIdx.x < nb) {
             const float* S = s_acc[threadIdx.x];
