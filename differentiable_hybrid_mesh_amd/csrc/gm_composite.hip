@@ -616,49 +616,6 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, const float* _
 // ---------------------------------------------------------------------------
 // backward
 // ---------------------------------------------------------------------------
-// Sum 16 per-lane values over the 64 lanes of a wave with a halving ("transpose")
-// reduction: at each butterfly step a lane keeps half of its values and receives its
-// partner's copy of them, so 16 values need 8+4+2+1 exchanges plus two full steps
-// instead of 16*6.  The exchanges use gfx950's cross-half lane swaps (lanes 32-63
-// with 0-31, odd 16-lane rows with even ones) and DPP row/quad moves, all VALU.
-// On return lane l holds the wave total of value (l >> 2) when (l & 3) == 0.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v)
-{
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-
-__device__ __forceinline__ float wave_sum16(const float* v, int lane)
-{
-    float a[8], b[4], c[2];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {  // lanes 0-31 keep v[i], lanes 32-63 keep v[8+i]
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[8 + i]), false,
-                                                        false);
-        a[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {  // even 16-lane rows keep a[i], odd rows a[4+i]
-        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[i]), __float_as_uint(a[4 + i]), false,
-                                                        false);
-        b[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    }
-    const bool h3 = lane & 8, h2 = lane & 4;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {  // partner: lane ^ 8 (rotate a 16-lane row by 8)
-        const float send = h3 ? b[i] : b[2 + i];
-        const float keep = h3 ? b[2 + i] : b[i];
-        c[i] = keep + dpp<0x128>(send);
-    }
-    // partner: the mirrored lane in the 8-lane half row (bit 2 flipped); the two
-    // quad steps below sum the four lanes of each half, so the pairing is exact
-    const float send = h2 ? c[0] : c[1];
-    float d = (h2 ? c[1] : c[0]) + dpp<0x141>(send);
-    d += dpp<0x4E>(d);  // quad_perm [2,3,0,1]
-    d += dpp<0xB1>(d);  // quad_perm [1,0,3,2]
-    return d;
-}
-
 // The same reduction of the first 10 values only (a wave off the mesh, where the
 // four depth-density sums are zero): 5 + 3 + 2 + 1 exchanges before the quad steps.
 // Every value meets the lanes in the same pairing order as in wave_sum16 (l ^ 32,

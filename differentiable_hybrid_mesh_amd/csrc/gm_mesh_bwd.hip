@@ -136,6 +136,36 @@ __device__ __forceinline__ int table_slot(int* keys, int key)
     return -1;
 }
 
+// DPP move of v (CTRL) into the rows of ROWMASK; lanes without a source read 0.
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ float dpp0(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWMASK, 0xf, false));
+}
+
+// Sum of x over lanes [start, lane] of the wave (start <= lane, the first lane of
+// the lane's run), with DPP moves only: shifts by 1, 2, 4 and 8 inside each 16-lane
+// row (Hillis-Steele, each step adding only within the run), then lane 15 of each
+// even row into the next row and lane 31 into rows 2 and 3, each added when the run
+// reaches back to that lane.
+__device__ __forceinline__ float seg_sum(float x, int lane, int start)
+{
+    const int r = lane & 15;
+    float y = dpp0<0x111>(x);  // row_shr:1
+    if (r >= 1 && lane - 1 >= start) x += y;
+    y = dpp0<0x112>(x);  // row_shr:2
+    if (r >= 2 && lane - 2 >= start) x += y;
+    y = dpp0<0x114>(x);  // row_shr:4
+    if (r >= 4 && lane - 4 >= start) x += y;
+    y = dpp0<0x118>(x);  // row_shr:8
+    if (r >= 8 && lane - 8 >= start) x += y;
+    y = dpp0<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+    if ((lane & 16) && start <= (lane & ~15) - 1) x += y;
+    y = dpp0<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+    if (lane >= 32 && start <= 31) x += y;
+    return x;
+}
+
 // One variant per (textured, lit) pair, so that each holds only its own state.
 template <bool TEX, bool LIT>
 __global__ void __launch_bounds__(MB_THREADS, TEX ? 2 : 3)
@@ -472,13 +502,7 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
 #pragma unroll
             for (int j = 0; j < 11; ++j) {
                 if (!plane_live<TEX, LIT>(j)) continue;
-                float x = acc[k][j];
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const float y = __shfl_up(x, d, 64);
-                    if (lane - d >= start) x += y;
-                }
-                acc[k][j] = x;
+                acc[k][j] = seg_sum(acc[k][j], lane, start);
             }
         // Run totals go into the block's LDS tables keyed by vertex (and texture
         // vertex): a vertex's faces meet inside one tile, so its many runs become one
@@ -530,16 +554,14 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
             }
         }
     }
-    // light: per-wave sums, then per-block atomics
+    // light: per-wave sums (one halving reduction of the 13 values), then per-block atomics
     if (g_light) {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        float g16[16];
 #pragma unroll
-        for (int i = 0; i < 13; ++i) {
-            float s = gl[i];
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
-            if (lane == 0) s_light[i][wave] = s;
-        }
+        for (int i = 0; i < 16; ++i) g16[i] = i < 13 ? gl[i] : 0.0f;
+        const float s = wave_sum16(g16, lane);
+        if ((lane & 3) == 0 && (lane >> 2) < 13) s_light[lane >> 2][wave] = s;
         __syncthreads();
         if (threadIdx.x < 13) {
             float s = 0.0f;
