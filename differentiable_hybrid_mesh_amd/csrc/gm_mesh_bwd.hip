@@ -143,29 +143,6 @@ __device__ __forceinline__ float dpp0(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWMASK, 0xf, false));
 }
 
-// Sum of x over lanes [start, lane] of the wave (start <= lane, the first lane of
-// the lane's run), with DPP moves only: shifts by 1, 2, 4 and 8 inside each 16-lane
-// row (Hillis-Steele, each step adding only within the run), then lane 15 of each
-// even row into the next row and lane 31 into rows 2 and 3, each added when the run
-// reaches back to that lane.
-__device__ __forceinline__ float seg_sum(float x, int lane, int start)
-{
-    const int r = lane & 15;
-    float y = dpp0<0x111>(x);  // row_shr:1
-    if (r >= 1 && lane - 1 >= start) x += y;
-    y = dpp0<0x112>(x);  // row_shr:2
-    if (r >= 2 && lane - 2 >= start) x += y;
-    y = dpp0<0x114>(x);  // row_shr:4
-    if (r >= 4 && lane - 4 >= start) x += y;
-    y = dpp0<0x118>(x);  // row_shr:8
-    if (r >= 8 && lane - 8 >= start) x += y;
-    y = dpp0<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
-    if ((lane & 16) && start <= (lane & ~15) - 1) x += y;
-    y = dpp0<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
-    if (lane >= 32 && start <= 31) x += y;
-    return x;
-}
-
 // One variant per (textured, lit) pair, so that each holds only its own state.
 template <bool TEX, bool LIT>
 __global__ void __launch_bounds__(MB_THREADS, TEX ? 2 : 3)
@@ -497,13 +474,30 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
         const unsigned long long upto = lane == 63 ? ~0ull : ((2ull << lane) - 1ull);
         const int start = 63 - __builtin_clzll(heads & upto);
         const bool tail = lane == 63 || ((heads >> (lane + 1)) & 1ull);
+        // Segmented sums over [start, lane] with DPP moves only: shifts by 1, 2, 4
+        // and 8 inside each 16-lane row (Hillis-Steele, each step adding only within
+        // the run), then lane 15 of each even row into the next row and lane 31 into
+        // rows 2 and 3, each added where the run reaches back to that lane.  Each step
+        // is taken for all planes at once and skipped (uniformly) when no run of the
+        // wave reaches back that far: runs are mostly shorter than 8 lanes and rarely
+        // cross a 16-lane row.
+        auto each = [&](auto step) {
 #pragma unroll
-        for (int k = 0; k < 3; ++k)
+            for (int k = 0; k < 3; ++k)
 #pragma unroll
-            for (int j = 0; j < 11; ++j) {
-                if (!plane_live<TEX, LIT>(j)) continue;
-                acc[k][j] = seg_sum(acc[k][j], lane, start);
-            }
+                for (int j = 0; j < 11; ++j)
+                    if (plane_live<TEX, LIT>(j)) acc[k][j] = step(acc[k][j]);
+        };
+        const int r = lane & 15;
+        const bool s1 = r >= 1 && lane - 1 >= start, s2 = r >= 2 && lane - 2 >= start,
+                   s4 = r >= 4 && lane - 4 >= start, s8 = r >= 8 && lane - 8 >= start,
+                   b15 = (lane & 16) && start <= (lane & ~15) - 1, b31 = lane >= 32 && start <= 31;
+        if (__ballot(s1)) each([&](float x) { const float y = dpp0<0x111>(x); return s1 ? x + y : x; });
+        if (__ballot(s2)) each([&](float x) { const float y = dpp0<0x112>(x); return s2 ? x + y : x; });
+        if (__ballot(s4)) each([&](float x) { const float y = dpp0<0x114>(x); return s4 ? x + y : x; });
+        if (__ballot(s8)) each([&](float x) { const float y = dpp0<0x118>(x); return s8 ? x + y : x; });
+        if (__ballot(b15)) each([&](float x) { const float y = dpp0<0x142, 0xa>(x); return b15 ? x + y : x; });
+        if (__ballot(b31)) each([&](float x) { const float y = dpp0<0x143, 0xc>(x); return b31 ? x + y : x; });
         // Run totals go into the block's LDS tables keyed by vertex (and texture
         // vertex): a vertex's faces meet inside one tile, so its many runs become one
         // set of global atomics when the block flushes.
