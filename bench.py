@@ -400,6 +400,8 @@ def run_config(args, name):
         ns = {"project_bwd": time_project_bwd(r, scene, views[0], args.steps)} if N else {}
         if scene.F:
             ns["mesh_bwd"] = time_mesh_bwd(r, scene, views[0], args.steps)
+        for st in ns.values():  # HBM bytes per launch from the committed counters, when current
+            st["traffic"] = measured_traffic(st["kernel"], name)
         out["next_stages"] = ns
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(scene, views[0], args.cpu_tiles, len(views))
