@@ -217,6 +217,108 @@ __global__ void __launch_bounds__(SCAN1_THREADS) k_scan_single(const int32_t* __
     }
 }
 
+// ---------------------------------------------------------------------------
+// single-launch scan with a decoupled look-back
+// ---------------------------------------------------------------------------
+// Blocks take tickets in start order; block b sums its SCAN_CHUNK items, publishes
+// the sum (flag AGG), and one wave walks back over the blocks before it, 64 status
+// words per round trip, adding aggregates up to the first inclusive prefix (flag
+// PREFIX); it then publishes its own prefix and writes its items.  A block waits
+// only for blocks with smaller tickets, which run already and publish before they
+// wait, so every wait ends; it is still bounded (SCAN_SPIN_LIMIT polls).
+constexpr unsigned long long SC_AGG = 1ull << 62, SC_PREFIX = 2ull << 62, SC_VALUE = SC_AGG - 1ull;
+constexpr int SCAN_SPIN_LIMIT = 1 << 18;
+
+__device__ __forceinline__ unsigned long long sc_load(const unsigned long long* p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void sc_store(unsigned long long* p, unsigned long long v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// status: one word per block, then the ticket counter (low 32 bits of one more word);
+// all zero on entry.
+__global__ void __launch_bounds__(SCAN_THREADS) k_scan_lb(const int32_t* __restrict__ in, int64_t n,
+                                                          int32_t* __restrict__ out, long long* __restrict__ total,
+                                                          unsigned long long* __restrict__ status)
+{
+    __shared__ long long lds[SCAN_THREADS / 64];
+    __shared__ int s_blk;
+    __shared__ long long s_pre;
+    if (threadIdx.x == 0) s_blk = (int)atomicAdd(reinterpret_cast<unsigned int*>(status + gridDim.x), 1u);
+    __syncthreads();
+    const int blk = s_blk;
+    const int64_t base = (int64_t)blk * SCAN_CHUNK + (int64_t)threadIdx.x * SCAN_ITEMS;
+    int32_t v[SCAN_ITEMS];
+    long long s = 0;
+#pragma unroll
+    for (int k = 0; k < SCAN_ITEMS; ++k) {
+        const int64_t i = base + k;
+        v[k] = i < n ? in[i] : 0;
+        s += v[k];
+    }
+    long long btot;
+    const long long inc = block_incl_scan(s, lds, &btot);
+    if (threadIdx.x == 0) sc_store(status + blk, (blk == 0 ? SC_PREFIX : SC_AGG) | (unsigned long long)btot);
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        long long excl = 0;
+        int spins = 0;
+        for (int j = blk - 1; j >= 0;) {  // uniform over the wave
+            const unsigned long long st = j - lane >= 0 ? sc_load(status + (j - lane)) : SC_PREFIX;
+            const unsigned long long pm = __ballot((st & SC_PREFIX) != 0);
+            const unsigned long long zm = __ballot((st & (SC_PREFIX | SC_AGG)) == 0);
+            const int p = pm ? __builtin_ctzll(pm) : 64, z = zm ? __builtin_ctzll(zm) : 64;
+            const int take = min(p + 1, z);  // published words, up to and including the first prefix
+            long long x = lane < take ? (long long)(st & SC_VALUE) : 0;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+            excl += x;
+            if (p < z) break;
+            j -= take;
+            if (z < 64) {  // an unpublished word: wait for it
+                if (++spins > SCAN_SPIN_LIMIT) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        if (lane == 0) {
+            if (blk > 0) sc_store(status + blk, SC_PREFIX | (unsigned long long)(excl + btot));
+            s_pre = excl;
+        }
+    }
+    __syncthreads();
+    long long run = s_pre + inc - s;
+#pragma unroll
+    for (int k = 0; k < SCAN_ITEMS; ++k) {
+        const int64_t i = base + k;
+        if (i < n) out[i] = (int32_t)run;
+        run += v[k];
+    }
+    if (blk == (int)gridDim.x - 1 && threadIdx.x == 0) {
+        out[n] = (int32_t)(s_pre + btot);
+        *total = s_pre + btot;
+    }
+}
+
+int64_t scan_lb_clear_words(int64_t n) { return n <= SCAN1_MAX ? 0 : div_up(n, SCAN_CHUNK) + 1; }
+
+gm_status exclusive_scan_lb(const int32_t* in, int32_t* out, int64_t n, long long* total, void* ws,
+                            hipStream_t stream)
+{
+    if (n <= SCAN1_MAX) {
+        k_scan_single<<<1, SCAN1_THREADS, 0, stream>>>(in, n, out, total);
+        GM_LAUNCH_CHECK();
+        return GM_OK;
+    }
+    k_scan_lb<<<(unsigned)div_up(n, SCAN_CHUNK), SCAN_THREADS, 0, stream>>>(in, n, out, total,
+                                                                         (unsigned long long*)ws);
+    GM_LAUNCH_CHECK();
+    return GM_OK;
+}
+
 size_t scan_ws_bytes(int64_t n)
 {
     int64_t nb = div_up(n > 0 ? n : 1, SCAN_CHUNK);

@@ -79,6 +79,14 @@ size_t scan_ws_bytes(int64_t n);
 gm_status exclusive_scan(const int32_t* in, int32_t* out, int64_t n, long long* total, void* ws,
                          hipStream_t stream);
 
+// The same scan in one launch for callers whose previous kernel on the stream
+// cleared the first scan_lb_clear_words(n) 64-bit words of ws (the blocks find their
+// offsets by a decoupled look-back over those words; a single block does it all for
+// short inputs).  Workspace: scan_ws_bytes(n).
+int64_t scan_lb_clear_words(int64_t n);
+gm_status exclusive_scan_lb(const int32_t* in, int32_t* out, int64_t n, long long* total, void* ws,
+                            hipStream_t stream);
+
 // Surface colour prepass of the composite (gm_composite.hip): colour [H][W][3] =
 // the shaded mesh colour at covered pixels, bg (or 0 when bg is NULL) elsewhere.
 gm_status launch_surface_colour(const gm_camera* cam, const gm_mesh* mesh, const float* vscreen,

@@ -44,12 +44,17 @@ __device__ inline long long live_count(const long long* __restrict__ d_count, lo
 template <int BITS, typename KT, int ITEMS>
 __global__ void __launch_bounds__(RS_THREADS)
 k_radix_hist(const KT* __restrict__ keys, const long long* __restrict__ d_count, long long n_max,
-             int shift, int nblocks, int32_t* __restrict__ hist)
+             int shift, int nblocks, int32_t* __restrict__ hist, unsigned long long* __restrict__ scan_clear,
+             int64_t scan_words)
 {
     constexpr int R = 1 << BITS;
     __shared__ int32_t h[RS_WAVES][RS_RADIX];  // one histogram per wave: fewer colliding LDS atomics
     const long long n = live_count(d_count, n_max);
     const int wave = threadIdx.x >> 6;
+    {  // the status words of the single-launch scan that follows
+        const int64_t gid = (int64_t)blockIdx.x * RS_THREADS + threadIdx.x;
+        if (gid < scan_words) scan_clear[gid] = 0ull;
+    }
 #pragma unroll
     for (int w = 0; w < RS_WAVES; ++w) h[w][threadIdx.x] = 0;
     __syncthreads();
@@ -205,9 +210,12 @@ static gm_status radix_pass(const KT* kin, const int32_t* vin, KT* kout, int32_t
                             const long long* d_count, int64_t n_max, int nb, int32_t* hist, int32_t* offs,
                             long long* tot, void* scan_ws, hipStream_t stream)
 {
-    k_radix_hist<BITS, KT, ITEMS><<<nb, RS_THREADS, 0, stream>>>(kin, d_count, n_max, shift, nb, hist);
+    const int64_t nscan = (int64_t)(1 << BITS) * nb;
+    k_radix_hist<BITS, KT, ITEMS><<<nb, RS_THREADS, 0, stream>>>(kin, d_count, n_max, shift, nb, hist,
+                                                                  (unsigned long long*)scan_ws,
+                                                                  scan_lb_clear_words(nscan));
     GM_LAUNCH_CHECK();
-    if (gm_status s = exclusive_scan(hist, offs, (int64_t)(1 << BITS) * nb, tot, scan_ws, stream)) return s;
+    if (gm_status s = exclusive_scan_lb(hist, offs, nscan, tot, scan_ws, stream)) return s;
     k_radix_scatter<BITS, KT, ITEMS><<<nb, RS_THREADS, 0, stream>>>(kin, vin, d_count, n_max, shift, nb, offs, kout,
                                                                      vout);
     GM_LAUNCH_CHECK();
