@@ -2,8 +2,8 @@
 
 One step = the whole hot path over every view of the workload, inputs resident in
 HBM.  Per view: gm_bin_triangles -> gm_raster_zbuffer, beside them on a second
-stream gm_project_gaussians -> gm_sort_depth (then gm_shade_surface once the
-z-buffer is done), then gm_sort_tiles -> gm_composite_hybrid_fwd_shaded ->
+stream gm_project_sort_depth (then gm_shade_surface once the z-buffer is done),
+then gm_sort_tiles -> gm_composite_hybrid_fwd_shaded ->
 gm_composite_hybrid_bwd.  The one-view workloads (64x64, 512x512 and the default
 1920x1080 sphere) time that sequence; the multi-view ones (the 800x800 soup's 16
 views, the 1920x1080 four-sphere scene's 4 views) time the pipelined pass that
@@ -49,8 +49,8 @@ FP32_VALU_PACKED_TFLOPS = 157.3  # the published fp32 vector figure (packed FMA)
 # z-buffer.
 STAGES = ["bin", "zbuffer", "wait_lists", "sort", "fwd", "bwd"]
 STAGES_AA = ["bin", "zbuffer", "antialias", "wait_lists", "sort", "fwd", "bwd", "antialias_bwd"]
-SIDE_STAGES = ["project", "sort_depth", "wait_zbuffer", "shade"]  # shade: the composite's first half
-SIDE_STAGES_AA = ["project", "sort_depth"]  # the layer call shades the mesh on the main stream
+SIDE_STAGES = ["project_sort_depth", "wait_zbuffer", "shade"]  # shade: the composite's first half
+SIDE_STAGES_AA = ["project_sort_depth"]  # the layer call shades the mesh on the main stream
 
 WORKLOADS = {
     "c1": "64x64, 200 random triangles (vertex colour), 500 Gaussians",
@@ -228,9 +228,7 @@ class Bench:
         side.wait_event(r._ev_main)
         with torch.cuda.stream(side):
             mark_side()
-            r.project(view)
-            mark_side()
-            r.sort_depth(view)
+            r.project_sort_depth(view)
             mark_side()
             r._ev_side.record(side)
         mark()
@@ -365,7 +363,7 @@ def run_config(args, name):
 
     # dominant single kernel by stage time (the sort and binning are chains of many
     # small kernels; the other stages are one main kernel each)
-    dom = max(["zbuffer", "project", "fwd", "bwd"], key=lambda s: stage_mean.get(s, 0.0))
+    dom = max(["zbuffer", "project_sort_depth", "fwd", "bwd"], key=lambda s: stage_mean.get(s, 0.0))
     roof = roofline(b, dom, last_view, alg[-1], alg_flops, units, args)
 
     step_bytes = None if b.aa else measured_step_traffic(name)
@@ -440,8 +438,8 @@ def algorithmic_bytes(scene, r, counts, nvis, aa):
         a = {
             "bin": 12 * V + 12 * V + 12 * F + 8 * Pp + 4 * T,
             "zbuffer": 4 * Pp + 12 * F + 12 * V + 8 * HW + 4 * T,
-            "project": N * (12 + 16 + 12 + 4 + shb + 64),
-            "sort_depth": 64 * N,
+            # the projection's inputs and records, and the depth sort's keys and ids
+            "project_sort_depth": N * (12 + 16 + 12 + 4 + shb + 64) + 8 * N,
             "sort": 28 * K + 8 * T,
             # the composite forward: ids, records, face id + depth, colour behind (state_cm),
             # rgb + depth + alpha, state_T + state_last
@@ -463,7 +461,7 @@ def algorithmic_bytes(scene, r, counts, nvis, aa):
     return out
 
 
-KERNEL_OF = {"bwd": "k_composite_bwd", "fwd": "k_composite_fwd", "project": "k_project_gaussians",
+KERNEL_OF = {"bwd": "k_composite_bwd", "fwd": "k_composite_fwd", "project_sort_depth": "k_project_gaussians",
              "zbuffer": "k_zbuffer"}
 
 
@@ -478,7 +476,7 @@ def roofline(b, dom, view, alg_bytes, alg_flops, units, args):
         "bwd": (lambda: r.composite_bwd_aa(view, g["rgb"], g["depth"], g["alpha"])) if b.aa else
                (lambda: r.composite_bwd(view, g["rgb"], g["depth"], g["alpha"])),
         "fwd": (lambda: r.composite_fwd_aa(view)) if b.aa else (lambda: r.composite_fwd_shaded(view)),
-        "project": lambda: r.project(view),
+        "project_sort_depth": lambda: r.project_sort_depth(view),
         "zbuffer": lambda: r.bin_and_zbuffer(view),
     }[dom]
     launch_ms = time_call(launch, args.steps)

@@ -49,7 +49,8 @@ class GmMesh(C.Structure):
 EXPORTS = ["gm_bin_triangles_ws", "gm_bin_triangles", "gm_raster_zbuffer_ws", "gm_raster_zbuffer",
            "gm_project_gaussians",
            "gm_project_gaussians_multi",
-           "gm_sort_tile_keys_ws", "gm_sort_tile_keys", "gm_sort_depth", "gm_sort_tiles", "gm_composite_hybrid_fwd",
+           "gm_sort_tile_keys_ws", "gm_sort_tile_keys", "gm_sort_depth", "gm_sort_tiles", "gm_project_sort_depth",
+           "gm_composite_hybrid_fwd",
            "gm_composite_hybrid_bwd", "gm_composite_hybrid_bwd_ws", "gm_project_gaussians_bwd", "gm_mesh_bwd", "gm_mipmaps_floats",
            "gm_build_mipmaps", "gm_last_error", "gm_version", "gm_edge_adjacency_ws", "gm_edge_adjacency",
            "gm_antialias", "gm_composite_hybrid_fwd_aa", "gm_composite_hybrid_bwd_aa", "gm_antialias_bwd_ws",
@@ -82,6 +83,7 @@ def lib():
     L.gm_sort_tile_keys_ws.restype = SZ
     L.gm_sort_tile_keys.argtypes = [cam, I32, P, P, F32, P, P, I64, P, P, SZ, P]
     L.gm_sort_depth.argtypes = [cam, I32, P, I64, P, SZ, P]
+    L.gm_project_sort_depth.argtypes = [cam, I32, P, P, P, P, P, I32, P, I64, P, SZ, P]
     L.gm_sort_tiles.argtypes = [cam, I32, P, P, F32, P, P, I64, P, P, SZ, P]
     L.gm_composite_hybrid_fwd.argtypes = [cam, P, P, P, P, P, mesh, P, light, P, F32, P, P, P, P, P, P, P]
     L.gm_shade_surface.argtypes = [cam, P, mesh, P, light, P, P, P]
@@ -114,7 +116,7 @@ def lib():
         if not hasattr(L, name):
             raise ImportError(f"{LIB_PATH} does not export {name}")
     for name in ("gm_bin_triangles", "gm_raster_zbuffer", "gm_project_gaussians", "gm_project_gaussians_multi",
-                 "gm_sort_tile_keys", "gm_sort_depth", "gm_sort_tiles",
+                 "gm_sort_tile_keys", "gm_sort_depth", "gm_sort_tiles", "gm_project_sort_depth",
                  "gm_composite_hybrid_fwd", "gm_composite_hybrid_bwd", "gm_project_gaussians_bwd",
                  "gm_mesh_bwd", "gm_build_mipmaps", "gm_edge_adjacency", "gm_antialias", "gm_composite_hybrid_fwd_aa",
                  "gm_composite_hybrid_bwd_aa", "gm_antialias_bwd", "gm_vscreen_bwd", "gm_shade_surface",
@@ -269,6 +271,14 @@ def gm_sort_depth(cam, N, rec, cap, ws, stream):
     """First half of gm_sort_tile_keys: the depth order, kept in ws for gm_sort_tiles."""
     rp, wp, wb = _sort_common(cam, N, rec, cap, ws)
     check(lib().gm_sort_depth(C.byref(cam), int(N), rp, int(cap), wp, wb, stream))
+
+
+def gm_project_sort_depth(cam, N, means, quats, scales, opacity, sh, sh_degree, rec, cap, ws, stream):
+    """gm_project_gaussians then gm_sort_depth in one call (the projection also writes the
+    depth sort's keys into ws)."""
+    gin = _gauss_in(N, means, quats, scales, opacity, sh, sh_degree)
+    rp, wp, wb = _sort_common(cam, N, rec, cap, ws)
+    check(lib().gm_project_sort_depth(C.byref(cam), int(N), *gin, int(sh_degree), rp, int(cap), wp, wb, stream))
 
 
 def gm_sort_tiles(cam, N, rec, tile_dmax, softness, tile_ranges, sorted_ids, cap, n_keys, ws, stream):

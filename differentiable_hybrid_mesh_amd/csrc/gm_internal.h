@@ -87,6 +87,16 @@ int64_t scan_lb_clear_words(int64_t n);
 gm_status exclusive_scan_lb(const int32_t* in, int32_t* out, int64_t n, long long* total, void* ws,
                             hipStream_t stream);
 
+// Projection (gm_project.hip): the argument checks of gm_project_gaussians, and its
+// kernel with the depth sort's input written beside the records (keys[i] = the bits
+// of z_c when Gaussian i is listed, all ones otherwise; ids[i] = i; *d_n = N).
+gm_status check_project_args(const gm_camera* cam, int32_t N, const float* means, const float* quats,
+                             const float* scales, const float* opacity, const float* sh, int32_t sh_degree,
+                             const float* rec);
+gm_status launch_project_keys(const DevCamera& dc, int32_t N, const float* means, const float* quats,
+                              const float* scales, const float* opacity, const float* sh, int32_t sh_degree,
+                              float* rec, uint32_t* keys, int32_t* ids, long long* d_n, hipStream_t stream);
+
 // Surface colour prepass of the composite (gm_composite.hip): colour [H][W][3] =
 // the shaded mesh colour at covered pixels, bg (or 0 when bg is NULL) elsewhere.
 gm_status launch_surface_colour(const gm_camera* cam, const gm_mesh* mesh, const float* vscreen,

@@ -67,8 +67,10 @@ __device__ inline WorldGauss world_gaussian(int N, int i, const float* __restric
 
 // The record of Gaussian i in one view.  shc: its colour coefficients, read once by
 // the caller ([k][3] for degree d >= 0, RGB for d = -1).
-__device__ inline void project_view(const DevCamera& cam, const WorldGauss& g, float opacity, const float* shc,
-                                    int sh_degree, float* __restrict__ rec_i)
+// Writes the record; returns its key for the depth sort: the bits of z_c when the
+// Gaussian is listed (z_c > 0, so the bits order like the values), all ones otherwise.
+__device__ inline uint32_t project_view(const DevCamera& cam, const WorldGauss& g, float opacity, const float* shc,
+                                        int sh_degree, float* __restrict__ rec_i)
 {
     const float* W = cam.R;
     const float mx = g.mx, my = g.my, mz = g.mz;
@@ -171,6 +173,7 @@ __device__ inline void project_view(const DevCamera& cam, const WorldGauss& g, f
     o[2] = make_float4(col[2], zc, g0, g1);
     o[3] = make_float4(sig, __int_as_float(r0 | (r1 << 16)), __int_as_float(r2 | (r3 << 16)),
                        __int_as_float(ntiles));
+    return ntiles > 0 ? __float_as_uint(zc) : 0xffffffffu;
 }
 
 __device__ inline void load_colour(int N, int i, const float* __restrict__ sh, int sh_degree, float* shc)
@@ -182,18 +185,50 @@ __device__ inline void load_colour(int N, int i, const float* __restrict__ sh, i
         for (int ch = 0; ch < 3; ++ch) shc[k * 3 + ch] = k < K ? sh[((size_t)k * 3 + ch) * N + i] : 0.0f;
 }
 
+// KEYS: also the depth sort's input (key and id of every Gaussian, and the key
+// count), which the sort otherwise extracts from the records in a kernel of its own.
+template <bool KEYS>
 __global__ void __launch_bounds__(256)
 k_project_gaussians(DevCamera cam, int N, const float* __restrict__ means,
                     const float* __restrict__ quats, const float* __restrict__ scales,
                     const float* __restrict__ opacity, const float* __restrict__ sh, int sh_degree,
-                    float* __restrict__ rec)
+                    float* __restrict__ rec, uint32_t* __restrict__ keys = nullptr, int32_t* __restrict__ ids = nullptr,
+                    long long* __restrict__ d_n = nullptr)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (KEYS && i == 0) *d_n = N;
     if (i >= N) return;
     const WorldGauss g = world_gaussian(N, i, means, quats, scales);
     float shc[48];
     load_colour(N, i, sh, sh_degree, shc);
-    project_view(cam, g, opacity[i], shc, sh_degree, rec + (size_t)i * GM_REC);
+    const uint32_t key = project_view(cam, g, opacity[i], shc, sh_degree, rec + (size_t)i * GM_REC);
+    if constexpr (KEYS) {
+        keys[i] = key;
+        ids[i] = i;
+    }
+}
+
+gm_status check_project_args(const gm_camera* cam, int32_t N, const float* means, const float* quats,
+                             const float* scales, const float* opacity, const float* sh, int32_t sh_degree,
+                             const float* rec)
+{
+    if (gm_status s = check_camera(cam)) return s;
+    GM_ARG_CHECK(N >= 0, "N = %d is negative", N);
+    GM_ARG_CHECK(sh_degree >= -1 && sh_degree <= 3, "sh_degree %d outside -1..3", sh_degree);
+    if (N == 0) return GM_OK;
+    GM_ARG_CHECK(means && quats && scales && opacity && sh && rec, "an input or rec is NULL");
+    GM_ARG_CHECK(((uintptr_t)rec & 15) == 0, "rec must be 16-byte aligned");
+    return GM_OK;
+}
+
+gm_status launch_project_keys(const DevCamera& dc, int32_t N, const float* means, const float* quats,
+                              const float* scales, const float* opacity, const float* sh, int32_t sh_degree,
+                              float* rec, uint32_t* keys, int32_t* ids, long long* d_n, hipStream_t stream)
+{
+    k_project_gaussians<true><<<(unsigned)div_up(N, 256), 256, 0, stream>>>(dc, N, means, quats, scales, opacity, sh,
+                                                                            sh_degree, rec, keys, ids, d_n);
+    GM_LAUNCH_CHECK();
+    return GM_OK;
 }
 
 // Several views of the same Gaussians: the inputs are read and the world covariance
@@ -231,15 +266,11 @@ extern "C" gm_status gm_project_gaussians(const gm_camera* cam, int32_t N, const
                                           float* rec, hipStream_t stream)
 {
     clear_error();
-    if (gm_status s = check_camera(cam)) return s;
-    GM_ARG_CHECK(N >= 0, "N = %d is negative", N);
-    GM_ARG_CHECK(sh_degree >= -1 && sh_degree <= 3, "sh_degree %d outside -1..3", sh_degree);
+    if (gm_status s = check_project_args(cam, N, means, quats, scales, opacity, sh, sh_degree, rec)) return s;
     if (N == 0) return GM_OK;
-    GM_ARG_CHECK(means && quats && scales && opacity && sh && rec, "an input or rec is NULL");
-    GM_ARG_CHECK(((uintptr_t)rec & 15) == 0, "rec must be 16-byte aligned");
     const DevCamera dc = dev_camera(*cam);
-    k_project_gaussians<<<(unsigned)div_up(N, 256), 256, 0, stream>>>(dc, N, means, quats, scales, opacity,
-                                                                      sh, sh_degree, rec);
+    k_project_gaussians<false><<<(unsigned)div_up(N, 256), 256, 0, stream>>>(dc, N, means, quats, scales, opacity,
+                                                                             sh, sh_degree, rec);
     GM_LAUNCH_CHECK();
     return GM_OK;
 }

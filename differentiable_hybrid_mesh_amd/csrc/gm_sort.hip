@@ -732,6 +732,22 @@ gm_status gm_sort_depth(const gm_camera* cam, int32_t N, const float* rec, int64
     return sort_depth(dc, N, rec, w, stream);
 }
 
+gm_status gm_project_sort_depth(const gm_camera* cam, int32_t N, const float* means, const float* quats,
+                                const float* scales, const float* opacity, const float* sh, int32_t sh_degree,
+                                float* rec, int64_t cap, void* ws, size_t ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    if (gm_status s = check_project_args(cam, N, means, quats, scales, opacity, sh, sh_degree, rec)) return s;
+    DevCamera dc;
+    SortWs w;
+    if (gm_status s = sort_args(cam, N, rec, cap, ws, ws_bytes, &dc, &w)) return s;
+    if (N == 0) return GM_OK;
+    if (gm_status s = launch_project_keys(dc, N, means, quats, scales, opacity, sh, sh_degree, rec, w.dka, w.dva,
+                                          w.n, stream))
+        return s;
+    return radix_sort<uint32_t, DS_ITEMS>(w.dka, w.dva, w.dkb, w.dvb, 32, w.n, N, w.aux, stream);
+}
+
 gm_status gm_sort_tiles(const gm_camera* cam, int32_t N, const float* rec, const float* tile_dmax, float softness,
                         int32_t* tile_ranges, int32_t* sorted_ids, int64_t cap, int64_t* n_keys, void* ws,
                         size_t ws_bytes, hipStream_t stream)

@@ -6,7 +6,7 @@ list lengths back once per forward pass (the calls themselves never synchronise)
 grows a list that overflowed and runs the pass again, and runs
 
     gm_bin_triangles -> gm_raster_zbuffer ----------.----------> gm_shade_surface --.
-    gm_project_gaussians -> gm_sort_depth ----------+-> gm_sort_tiles ---------------+->
+    gm_project_sort_depth --------------------------+-> gm_sort_tiles ---------------+->
     gm_composite_hybrid_fwd_shaded                   (forward)
     gm_composite_hybrid_bwd                          (backward)
 
@@ -188,6 +188,14 @@ class Renderer:
         G.gm_project_gaussians(ds.cams[view], self.N, ds.means, ds.quats, ds.scales, ds.opacity, ds.sh,
                                s.sh_degree, self.rec, _stream())
 
+    def project_sort_depth(self, view: int):
+        """project() then sort_depth() in one call (the projection also writes the depth
+        sort's keys, one kernel fewer)."""
+        ds, s = self.ds, self.ds.scene
+        self.rec = self._rec_own
+        G.gm_project_sort_depth(ds.cams[view], self.N, ds.means, ds.quats, ds.scales, ds.opacity, ds.sh,
+                                s.sh_degree, self.rec, self.key_cap, self.ws_sort, _stream())
+
     def sort(self, view: int, cull: bool = True):
         ds, s = self.ds, self.ds.scene
         dmax = self.tile_dmax if cull else None
@@ -247,8 +255,9 @@ class Renderer:
         side.wait_event(self._ev_main)
         with torch.cuda.stream(side):
             if project:
-                self.project(view)
-            self.sort_depth(view)
+                self.project_sort_depth(view)
+            else:
+                self.sort_depth(view)
             self._ev_side.record(side)
         self.bin_and_zbuffer(view)
         if antialias:

@@ -238,6 +238,17 @@ gm_status gm_sort_tiles(const gm_camera* cam, int32_t N, const float* rec, const
                         float softness, int32_t* tile_ranges, int32_t* sorted_ids, int64_t cap,
                         int64_t* n_keys, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* gm_project_gaussians followed by gm_sort_depth, in fewer launches: the projection
+ * kernel also writes the depth sort's keys and ids into ws, so the sort does not
+ * read them back from rec.  rec and ws end as after the two calls with the same
+ * arguments (the records and the depth order bit for bit), and gm_sort_tiles follows
+ * on the same ws as after gm_sort_depth.  Arguments as for those two calls (cap and
+ * ws as for gm_sort_depth); errors as for either. */
+gm_status gm_project_sort_depth(const gm_camera* cam, int32_t N, const float* means,
+                                const float* quats, const float* scales, const float* opacity,
+                                const float* sh, int32_t sh_degree, float* rec, int64_t cap,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * 5. gm_composite_hybrid_fwd — depth-tested front-to-back composite.
  * README "Hybrid rendering": per pixel each Gaussian is split at the mesh surface,

@@ -87,6 +87,14 @@ def test_argument_errors_before_any_launch(G):
     # the two halves of the sort: workspace too small, negative softness
     assert L.gm_sort_depth(C.byref(cam), 10, 16, 100, 16, 16, None) == G.GM_ERR_ARG
     assert b"workspace" in L.gm_last_error()
+    # projection and depth sort in one call: the projection's checks, then the sort's
+    assert L.gm_project_sort_depth(C.byref(cam), -1, 16, 16, 16, 16, 16, 0, 16, 100, 16, 1 << 20,
+                                   None) == G.GM_ERR_ARG
+    assert L.gm_project_sort_depth(C.byref(cam), 10, 16, 16, 16, 16, 16, 4, 16, 100, 16, 1 << 20,
+                                   None) == G.GM_ERR_ARG
+    assert b"sh_degree" in L.gm_last_error()
+    assert L.gm_project_sort_depth(C.byref(cam), 10, 16, 16, 16, 16, 16, 0, 16, 100, 16, 16, None) == G.GM_ERR_ARG
+    assert b"workspace" in L.gm_last_error()
     assert L.gm_sort_tiles(C.byref(cam), 0, None, None, C.c_float(-1.0), 16, None, 0, 16, 16,
                            1 << 20, None) == G.GM_ERR_ARG
     assert b"softness" in L.gm_last_error()
