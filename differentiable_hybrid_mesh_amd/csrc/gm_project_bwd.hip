@@ -29,25 +29,23 @@ k_project_bwd(DevCamera cam, int N, const float* __restrict__ means, const float
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= N) return;
     const int K = sh_degree < 0 ? 1 : (sh_degree + 1) * (sh_degree + 1);
+    // An unlisted Gaussian (no record gradient) gets zero gradients.  It runs the same
+    // arithmetic, with its outputs replaced by zeros at the stores (its forward values
+    // may be infinite), so that every load is issued at once, none behind the test.
+    // unrolled over the 16 coefficients (K of them live), issued with every other load
+    float shv[48];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+#pragma unroll
+        for (int ch = 0; ch < 3; ++ch) shv[k * 3 + ch] = k < K ? sh[((size_t)k * 3 + ch) * N + i] : 0.0f;
     const bool listed = __float_as_int(rec[(size_t)i * GM_REC + 15]) > 0;
     float gr[GM_GRAD];
 #pragma unroll
-    for (int k = 0; k < GM_GRAD; ++k) gr[k] = listed ? g_rec[(size_t)i * GM_GRAD + k] : 0.0f;
-    if (!listed) {
+    for (int k = 0; k < GM_GRAD; ++k) gr[k] = g_rec[(size_t)i * GM_GRAD + k];
+    const int keep = listed ? -1 : 0;  // a mask rather than a select, which the compiler
+                                       // would turn back into loads behind the test
 #pragma unroll
-        for (int j = 0; j < 3; ++j) g_means[(size_t)j * N + i] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) g_quats[(size_t)j * N + i] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 3; ++j) g_scales[(size_t)j * N + i] = 0.0f;
-        g_opacity[i] = 0.0f;
-        for (int k = 0; k < 3 * K; ++k) g_sh[(size_t)k * N + i] = 0.0f;
-        if (g_log_scales)
-#pragma unroll
-            for (int j = 0; j < 3; ++j) g_log_scales[(size_t)j * N + i] = 0.0f;
-        if (g_logit) g_logit[i] = 0.0f;
-        return;
-    }
+    for (int k = 0; k < GM_GRAD; ++k) gr[k] = __int_as_float(__float_as_int(gr[k]) & keep);
     double W[9];
 #pragma unroll
     for (int k = 0; k < 9; ++k) W[k] = cam.R[k];
@@ -118,7 +116,7 @@ k_project_bwd(DevCamera cam, int N, const float* __restrict__ means, const float
     double gmu[3] = {0.0, 0.0, 0.0};
     if (sh_degree < 0) {
 #pragma unroll
-        for (int ch = 0; ch < 3; ++ch) g_sh[(size_t)ch * N + i] = gr[6 + ch];
+        for (int ch = 0; ch < 3; ++ch) g_sh[(size_t)ch * N + i] = gr[6 + ch];  // zero when unlisted
     } else {
         const float* Wf = cam.R;
         float cw[3];
@@ -135,19 +133,21 @@ k_project_bwd(DevCamera cam, int N, const float* __restrict__ means, const float
         const float rc = rec[(size_t)i * GM_REC + 8];
         const float gacc[3] = {rb.z > 0.0f ? gr[6] : 0.0f, rb.w > 0.0f ? gr[7] : 0.0f, rc > 0.0f ? gr[8] : 0.0f};
         float gdx = 0.0f, gdy = 0.0f, gdz = 0.0f;
-        for (int k = 0; k < K; ++k) {
-            float gY = 0.0f;
 #pragma unroll
-            for (int ch = 0; ch < 3; ++ch) {
-                const size_t o = ((size_t)k * 3 + ch) * N + i;
-                g_sh[o] = Y[k] * gacc[ch];
-                gY += sh[o] * gacc[ch];
+        for (int k = 0; k < 16; ++k) {
+            if (k < K) {  // K is the same for every thread
+                float gY = 0.0f;
+#pragma unroll
+                for (int ch = 0; ch < 3; ++ch) {
+                    g_sh[((size_t)k * 3 + ch) * N + i] = listed ? Y[k] * gacc[ch] : 0.0f;
+                    gY += shv[k * 3 + ch] * gacc[ch];
+                }
+                float ex, ey, ez;
+                sh_basis_grad_f(k, dx, dy, dz, ex, ey, ez);
+                gdx += gY * ex;
+                gdy += gY * ey;
+                gdz += gY * ez;
             }
-            float ex, ey, ez;
-            sh_basis_grad_f(k, dx, dy, dz, ex, ey, ez);
-            gdx += gY * ex;
-            gdy += gY * ey;
-            gdz += gY * ez;
         }
         // dir = d / |d|: d dir / d d = (I - dir dir^T) / |d|
         const float dd = dx * gdx + dy * gdy + dz * gdz;
@@ -235,15 +235,15 @@ k_project_bwd(DevCamera cam, int N, const float* __restrict__ means, const float
     const double qh[4] = {w, x, y, z};
 
 #pragma unroll
-    for (int j = 0; j < 3; ++j) g_means[(size_t)j * N + i] = (float)gmu[j];
+    for (int j = 0; j < 3; ++j) g_means[(size_t)j * N + i] = listed ? (float)gmu[j] : 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) g_quats[(size_t)j * N + i] = (float)((gqh[j] - qh[j] * dq) * iqn);
+    for (int j = 0; j < 4; ++j) g_quats[(size_t)j * N + i] = listed ? (float)((gqh[j] - qh[j] * dq) * iqn) : 0.0f;
 #pragma unroll
-    for (int j = 0; j < 3; ++j) g_scales[(size_t)j * N + i] = (float)gs[j];
+    for (int j = 0; j < 3; ++j) g_scales[(size_t)j * N + i] = listed ? (float)gs[j] : 0.0f;
     g_opacity[i] = gr[5];
     if (g_log_scales)  // scale = exp(log scale)
 #pragma unroll
-        for (int j = 0; j < 3; ++j) g_log_scales[(size_t)j * N + i] = (float)(gs[j] * s[j]);
+        for (int j = 0; j < 3; ++j) g_log_scales[(size_t)j * N + i] = listed ? (float)(gs[j] * s[j]) : 0.0f;
     if (g_logit) {  // opacity = sigmoid(logit)
         const float o = opacity[i];
         g_logit[i] = gr[5] * o * (1.0f - o);
