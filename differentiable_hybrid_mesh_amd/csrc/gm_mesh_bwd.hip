@@ -162,7 +162,16 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
     const int px = (int)(blockIdx.x % tiles_x) * MB_TILE + (int)(threadIdx.x % MB_TILE);
     const int py = (int)(blockIdx.x / tiles_x) * MB_TILE + (int)(threadIdx.x / MB_TILE);
     const int pix = py * W + px;
-    const int f = (px < W && py < H) ? face_id[pix] : -1;
+    const bool inside = px < W && py < H;
+    const int f = inside ? face_id[pix] : -1;
+    // the upstream gradients depend on the pixel only: loaded beside its face id
+    float gzf = 0.0f, gcf[3] = {0.0f, 0.0f, 0.0f};
+    if (inside) {
+        if (g_depth) gzf = g_depth[pix];
+        if (g_rgb)
+#pragma unroll
+            for (int c = 0; c < 3; ++c) gcf[c] = g_rgb[3 * pix + c];
+    }
     // a tile the mesh does not reach has nothing to add (uniform exit, before any
     // table work)
     if (!__syncthreads_or(f >= 0)) return;
@@ -200,8 +209,9 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
         // values, not decisions, so the rounding order is free)
         double xc[3][3], u[3], v[3], z[3], iz[3];
 #pragma unroll
+        for (int k = 0; k < 3; ++k) vi[k] = P.faces[k * P.F + f];
+#pragma unroll
         for (int k = 0; k < 3; ++k) {
-            vi[k] = P.faces[k * P.F + f];
             const double X0 = P.verts[vi[k]], X1 = P.verts[P.V + vi[k]], X2 = P.verts[2 * P.V + vi[k]];
 #pragma unroll
             for (int r = 0; r < 3; ++r) xc[k][r] = R[3 * r] * X0 + R[3 * r + 1] * X1 + R[3 * r + 2] * X2 + t[r];
@@ -227,9 +237,22 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
 #pragma unroll
         for (int k = 0; k < 3; ++k) bb[k] = w[k] * zz;
 
-        double gc[3], gz = g_depth ? (double)g_depth[pix] : 0.0;
+        // the corners' colours and normals, in one batch (one round trip rather than
+        // one per use in the sums below)
+        float vcol[3][3] = {}, vnor[3][3] = {};
+        if (!TEX && P.vcolor)  // the same for every thread
 #pragma unroll
-        for (int c = 0; c < 3; ++c) gc[c] = g_rgb ? (double)g_rgb[3 * pix + c] : 0.0;
+            for (int k = 0; k < 3; ++k)
+#pragma unroll
+                for (int c = 0; c < 3; ++c) vcol[k][c] = P.vcolor[c * P.V + vi[k]];
+        if constexpr (LIT)
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+#pragma unroll
+                for (int c = 0; c < 3; ++c) vnor[k][c] = P.vnormal[c * P.V + vi[k]];
+        double gc[3], gz = gzf;
+#pragma unroll
+        for (int c = 0; c < 3; ++c) gc[c] = gcf[c];
         double gb[3] = {0.0, 0.0, 0.0}, gbase[3];
 
         // base colour (forward values needed by the lighting's backward)
@@ -275,7 +298,7 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
 #pragma unroll
             for (int c = 0; c < 3; ++c)
 #pragma unroll
-                for (int k = 0; k < 3; ++k) base[c] += bb[k] * P.vcolor[c * P.V + vi[k]];
+                for (int k = 0; k < 3; ++k) base[c] += bb[k] * vcol[k][c];
         }
 
         // ---- lighting (fp32: well conditioned): forward values, then reverse ---------------
@@ -286,7 +309,7 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
             for (int c = 0; c < 3; ++c) {
                 nw[c] = 0.0f;
 #pragma unroll
-                for (int k = 0; k < 3; ++k) nw[c] += (float)bb[k] * P.vnormal[c * P.V + vi[k]];
+                for (int k = 0; k < 3; ++k) nw[c] += (float)bb[k] * vnor[k][c];
             }
 #pragma unroll
             for (int r = 0; r < 3; ++r) {
@@ -375,7 +398,7 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
                 float sum = 0.0f;
 #pragma unroll
                 for (int c = 0; c < 3; ++c) {
-                    sum += P.vnormal[c * P.V + vi[k]] * gnw[c];
+                    sum += vnor[k][c] * gnw[c];
                     acc[k][6 + c] = (float)bb[k] * gnw[c];
                 }
                 gb[k] += sum;
@@ -416,7 +439,7 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
             for (int k = 0; k < 3; ++k)
 #pragma unroll
                 for (int c = 0; c < 3; ++c) {
-                    gb[k] += P.vcolor[c * P.V + vi[k]] * gbase[c];
+                    gb[k] += vcol[k][c] * gbase[c];
                     acc[k][3 + c] = (float)(bb[k] * gbase[c]);
                 }
         }
