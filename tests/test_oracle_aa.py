@@ -8,8 +8,10 @@ per-pixel bound for slanted edges; supersampling convergence on a sphere (the
 README's test suite checks antialiasing against supersampling); the topology rules
 (internal edges untouched, boundary and back-facing neighbours are silhouettes,
 farther surfaces are blended over); the reduction of the two-layer composite to
-the one-layer one under binary coverage; closed forms for a mesh-only image and
-for one Gaussian behind a fractional pixel; central finite differences of every
+the one-layer one under binary coverage; closed forms for a mesh-only image, for
+one Gaussian behind a fractional pixel and for a pixel whose front layer stops
+before the Gaussians behind the mesh (the pixel stops with it, so the back layer
+takes none of them); central finite differences of every
 reverse mode; the scaling invariance of the screen-to-world vertex chain.
 """
 import numpy as np
@@ -527,3 +529,54 @@ def test_vscreen_chain_scaling_invariance(seed):
     cam2 = oracle.camera(s2, 0)
     g2 = oracle.vscreen_bwd(cam2, oracle.MeshB64(s2), np.array([[1.0, 0, 0], [0.0, 0, 0]]))
     np.testing.assert_allclose(g2[:, 0], [40.0 / 2.5, 0.0, 0.0], rtol=1e-15)
+
+
+def _one_pixel_layer_composite(zs, cols, am=0.5, D=5.0, M=(0.1, 0.2, 0.3), MD=0.7, bg=(0.9, 0.8, 0.7)):
+    """The two-layer composite of Gaussians centred on pixel (8, 8) of a 16x16 image
+    (G = 1 there, alpha = 0.99, hard split: softness 0), listed in the given order,
+    over a mesh layer (premultiplied colour M, depth MD, coverage am, split depth D)."""
+    s = _scene(16)
+    cam = oracle.camera(s, 0)
+    n = len(zs)
+    rec = np.zeros((n, oracle.NREC))
+    rec[:, 0] = rec[:, 1] = 8.5                # centred on the pixel centre
+    rec[:, 2] = rec[:, 4] = 1.0                # conic: q = (dx^2 + dy^2) / 2
+    rec[:, 5] = 1.0                            # opacity (alpha clamps to 0.99)
+    rec[:, 6:9] = cols
+    rec[:, 9] = zs                             # z_c; depth slopes g0 = g1 = 0
+    rec[:, 12] = 0.5                           # sigma
+    L = np.zeros((16, 16, 6))
+    L[..., 5] = np.inf
+    L[8, 8] = [M[0], M[1], M[2], MD, am, D]
+    fid = np.full((16, 16), -1, np.int32)
+    depth = np.full((16, 16), np.inf, np.float32)
+    c = oracle.composite(cam, None, rec, np.array([0], np.int32), np.array([0, n], np.int64),
+                         np.arange(n, dtype=np.int32), fid, depth, bg=bg, softness=0.0, layer=L)
+    return c, np.array(M), MD, am, np.array(bg)
+
+
+def test_pixel_stops_with_its_front_layer():
+    # Three Gaussians in front of the split depth D = 5, then two behind it, in depth
+    # order.  The front layer takes the first two (T_F = 0.01, then 1e-4) and stops at
+    # the third (T would fall to 1e-6 < 1e-4); the 3DGS stop ends the pixel, so the back
+    # layer, seen through T_F, takes neither Gaussian behind the mesh.
+    cols = np.array([[1, 0, 0], [0, 1, 0], [0, 0, 1], [1, 1, 0], [0, 1, 1]], float)
+    zs = [1.0, 2.0, 3.0, 6.0, 7.0]
+    c, M, MD, am, bg = _one_pixel_layer_composite(zs, cols)
+    TF = 0.01 * 0.01
+    CF = 0.99 * cols[0] + 0.99 * 0.01 * cols[1]
+    ZF = 0.99 * zs[0] + 0.99 * 0.01 * zs[1]
+    np.testing.assert_allclose(c["rgb"][8, 8], CF + TF * (M + (1 - am) * bg), rtol=1e-12)
+    np.testing.assert_allclose(c["alpha"][8, 8], 1 - TF * (1 - am), rtol=1e-12)
+    np.testing.assert_allclose(c["depth"][8, 8], ZF + TF * MD, rtol=1e-12)
+    assert c["n_last"][8, 8] == 2
+    # and the same front entries with the back layer composited when the front does
+    # not stop: one Gaussian in front (T_F = 0.01), two behind (T_B = 0.01, 1e-4)
+    c2, M, MD, am, bg = _one_pixel_layer_composite([1.0, 6.0, 7.0], cols[[0, 3, 4]])
+    TF2, TB2 = 0.01, 0.01 * 0.01
+    CB2 = 0.99 * cols[3] + 0.99 * 0.01 * cols[4]
+    ZB2 = 0.99 * 6.0 + 0.99 * 0.01 * 7.0
+    want = 0.99 * cols[0] + TF2 * (M + (1 - am) * (CB2 + TB2 * bg))
+    np.testing.assert_allclose(c2["rgb"][8, 8], want, rtol=1e-12)
+    np.testing.assert_allclose(c2["alpha"][8, 8], 1 - TF2 * (1 - am) * TB2, rtol=1e-12)
+    np.testing.assert_allclose(c2["depth"][8, 8], 0.99 * 1.0 + TF2 * (MD + (1 - am) * ZB2), rtol=1e-12)

@@ -8,7 +8,9 @@ tracked oracle is never modified.  Mistakes planted:
 * the camera-frame covariance formed as W^T Sigma W instead of W Sigma W^T;
 * the camera centre taken as -W t instead of -W^T t (the colour's view direction);
 * Blinn-Phong's half vector in place of Phong's reflected light vector;
-* the light position used as a camera-space point, not carried by W L + t.
+* the light position used as a camera-space point, not carried by W L + t;
+* the back layer of the two-layer composite going on after its pixel's front layer
+  has stopped.
 """
 import os
 import shutil
@@ -43,6 +45,10 @@ MUTANTS = {
          "                   R[r * 3 + 2] * (double)m->light->pos[2] + cam->t[r];",
          "L[r] = (double)m->light->pos[r];"),
     ], "phong_off_axis"),
+    "back_layer_outlives_front": ([
+        ("if (layer == 0) aliveB = 0; /* the pixel stops with its front layer */",
+         "(void)0;"),
+    ], "front_layer", "test_oracle_aa.py"),
 }
 
 
@@ -63,27 +69,27 @@ def _build_mutant(tmp, edits):
     return so
 
 
-def _run_pins(selector, lib=None):
+def _run_pins(selector, lib=None, test_file="test_oracle_camera_pins.py"):
     env = dict(os.environ)
     env.pop("GM_ORACLE_LIB", None)
     if lib:
         env["GM_ORACLE_LIB"] = lib
     env["OMP_NUM_THREADS"] = env.get("OMP_NUM_THREADS", "4")
-    cmd = [sys.executable, "-m", "pytest", os.path.join(ROOT, "tests", "test_oracle_camera_pins.py"), "-q", "-x",
+    cmd = [sys.executable, "-m", "pytest", os.path.join(ROOT, "tests", test_file), "-q", "-x",
            "-k", selector, "-p", "no:cacheprovider", "-m", "not gpu"]
     return subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=900)
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_fails_a_pin(name, tmp_path, oracle_lib):
-    edits, selector = MUTANTS[name]
+    edits, selector, *test_file = MUTANTS[name]
     so = _build_mutant(str(tmp_path), edits)
-    res = _run_pins(selector, so)
+    res = _run_pins(selector, so, *test_file)
     assert res.returncode == 1, (name, res.returncode, res.stdout[-2000:], res.stderr[-2000:])
     assert "failed" in res.stdout
 
 
 def test_pins_pass_on_the_oracle(oracle_lib):
-    for sel in sorted({s for _, s in MUTANTS.values()}):
-        res = _run_pins(sel)
+    for sel, *test_file in sorted({tuple(m[1:]) for m in MUTANTS.values()}):
+        res = _run_pins(sel, None, *test_file)
         assert res.returncode == 0, (sel, res.stdout[-2000:])
