@@ -8,7 +8,11 @@ gradient rule |d| <= 1e-3 (|ref| + rms) plus a 1e-3 relative L2 bound, for the
 record gradients, dL/d(layer), dL/dc and dL/dD at covered pixels and the screen
 vertex gradients of the silhouettes); the end-to-end vertex gradients through the
 mesh backward; culling invariance.  Each side computes its own z-buffer, colours
-and layer; only the seeded scene inputs and upstream gradients are shared.
+and layer; only the seeded scene inputs and upstream gradients are shared.  Where a
+straddle pixel's dL/d(layer) does differ (a decision taken the other way), the
+surface and screen-vertex gradients it reaches through the antialiasing's reverse
+mode (found by the oracle's own reverse mode, fed at those pixels only) are exempt,
+counted and bounded.
 """
 import numpy as np
 import pytest
@@ -120,17 +124,52 @@ def _check(scene, view, gpu, ora, tiles, label):
     # dL/d(layer), away from straddles and from the fp32/fp64 visibility boundary
     ok = m & ~im["straddle_mask"] & ~near1
     c = ora["comp"]
+    # exempt pixels whose dL/d(layer) differs beyond fp32 rounding (1e-4 of its own
+    # value: a decision taken the other way; a difference within the 1e-3 rule, whose
+    # scale is the whole image's rms, can still exceed it in a neighbour's colour
+    # gradient, which is small where Gaussians cover the mesh)
+    differs = np.zeros(m.shape, bool)
     for ch, nm in enumerate(("gM_r", "gM_g", "gM_b", "gM_D", "g_a", "g_Dsplit")):
         ref = c["g_layer"][..., ch]
-        _grad_check(nm, gpu["g_layer"][..., ch], np.where(np.isfinite(ref), ref, 0.0), ok)
+        ref = np.where(np.isfinite(ref), ref, 0.0)
+        _grad_check(nm, gpu["g_layer"][..., ch], ref, ok)
+        differs |= ~(np.abs(gpu["g_layer"][..., ch] - ref) <= 1e-4 * np.abs(ref) + 1e-12)
     if scene.F:
         bw = ora["aa_bwd"]
-        _grad_check("g_mesh_rgb", gpu["g_mesh_rgb"], bw["colour"], ok)
-        _grad_check("g_mesh_depth", gpu["g_mesh_depth"], bw["depth"], ok)
-        if not im["straddle_mask"][m].any():
-            _grad_check("g_vscreen", gpu["g_vscreen"], bw["vs"])
+        ex_pix, ex_vert = _straddle_reach(scene, ora, m & ~ok & differs)
+        print(label, "exempt pixels", int(np.count_nonzero(m & ~ok)), "of which dL/d(layer) differs",
+              int(np.count_nonzero(m & ~ok & differs)), "reach", int(np.count_nonzero(ex_pix)), flush=True)
+        okm = ok & ~ex_pix
+        _grad_check("g_mesh_rgb", gpu["g_mesh_rgb"], bw["colour"], okm)
+        _grad_check("g_mesh_depth", gpu["g_mesh_depth"], bw["depth"], okm)
+        _grad_check("g_vscreen", gpu["g_vscreen"], bw["vs"], np.broadcast_to(~ex_vert, bw["vs"].shape))
         rep["silhouette_vertices"] = int(np.count_nonzero(np.abs(bw["vs"]).sum(0)))
+        rep["surface_exempt_px"] = int(np.count_nonzero(ok & ex_pix))
+        rep["vertex_exempt"] = int(np.count_nonzero(ex_vert))
+        print(label, "surface gradients exempt at", rep["surface_exempt_px"], "pixels,",
+              rep["vertex_exempt"], "of", rep["silhouette_vertices"], "silhouette vertices", flush=True)
+        assert rep["surface_exempt_px"] <= 8 * max(1, int(np.count_nonzero(m & ~ok & differs)))
+        assert rep["vertex_exempt"] <= max(8, rep["silhouette_vertices"] // 100)
     return rep
+
+
+def _straddle_reach(scene, ora, exempt):
+    """Pixels and screen vertices whose oracle surface gradients receive anything
+    from the layer gradients of the exempt pixels (straddles and the fp32 coverage
+    boundary whose dL/d(layer) differs between the two sides): the oracle's own reverse
+    mode of the antialiasing, fed seeded positive values at those pixels only (the
+    layer of a pixel gathers from its neighbours, so a straddle reaches their colour
+    and the edges crossed between them)."""
+    V = scene.V
+    if not exempt.any():
+        return np.zeros(exempt.shape, bool), np.zeros(V, bool)
+    rng = np.random.default_rng(1)
+    probe = np.zeros(exempt.shape + (6,))
+    probe[exempt] = rng.uniform(0.5, 1.5, size=(int(np.count_nonzero(exempt)), 6))
+    reach = oracle.antialias_bwd(ora["cam"], ora["vscreen"].astype(np.float64), scene.faces, scene.face_mask,
+                                 ora["adj"], ora["face_id"], ora["depth"], ora["colour"], probe)
+    ex_pix = exempt | (np.abs(reach["colour"]).sum(-1) > 0) | (reach["depth"] != 0)
+    return ex_pix, np.abs(reach["vs"]).sum(0) > 0
 
 
 @pytest.mark.parametrize("name", ["c2", "c3", "c4"])
@@ -192,24 +231,16 @@ def test_aa_no_gaussians_and_no_mesh():
     _check(s, 0, gpu, ora, tiles, "aa N=0")
 
 
-def _sample_tiles(scene, n, seed=0):
-    rng = np.random.default_rng(seed)
-    T = scene.tiles_x * scene.tiles_y
-    t = set(rng.choice(T, size=n, replace=False).tolist())
-    mid = scene.tiles_y // 2
-    t.update(range(mid * scene.tiles_x + scene.tiles_x // 2 - 8, mid * scene.tiles_x + scene.tiles_x // 2 + 8))
-    # tiles on the outline of the sphere (silhouettes)
-    t.update(range(mid * scene.tiles_x, mid * scene.tiles_x + scene.tiles_x))
-    return np.array(sorted(t), np.int32)
-
-
 @pytest.mark.slow
-def test_aa_c3_sampled():
+def test_aa_c3_full():
+    """The 1080p sphere workload antialiased, every tile: adjacency, z-buffer, the
+    layer of every pixel, the two-layer composite and its reverse mode with the full
+    upstream gradients, and the silhouettes' screen-vertex gradients."""
     s = _scene("c3")
-    tiles = _sample_tiles(s, 16)
-    r, gpu, ora, tiles = _run(s, 0, tiles=tiles, masked=True)
-    rep = _check(s, 0, gpu, ora, tiles, "c3 aa sampled")
-    assert rep["a_frac_pixels"] > 20 and rep["silhouette_vertices"] > 10
+    print("c3 aa full: GPU pass and oracle on all %d tiles" % (s.tiles_x * s.tiles_y), flush=True)
+    r, gpu, ora, tiles = _run(s, 0)
+    rep = _check(s, 0, gpu, ora, tiles, "c3 aa full")
+    assert rep["a_frac_pixels"] > 1000 and rep["silhouette_vertices"] > 100
 
 
 def test_aa_cull_invariance():
