@@ -80,6 +80,14 @@ def test_c3_lit():
     assert _run(scenes.make_scene("c3"), seed=3) > 100000
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("view", [1, 3])
+def test_c5_lit_rotated_views(view):
+    """The four-sphere workload under its rotated and translated cameras (views 1
+    and 3), Phong lit: the light and normals seen from off the optical axis."""
+    assert _run(scenes.make_scene("c5"), view, seed=50 + view) > 100000
+
+
 def test_tiny_lit():
     s = tiny.random_tiny(61, n_tri=12, n_gauss=0, size=64)
     rng = np.random.default_rng(61)
