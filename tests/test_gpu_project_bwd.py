@@ -80,6 +80,15 @@ def test_c3_all_gaussians():
     _run(scenes.make_scene("c3"), seed=3)
 
 
+@pytest.mark.slow
+def test_c5_rotated_view():
+    """3M Gaussians (SH 3) under a rotated and translated camera (view 2 of the
+    four-sphere workload): the world-to-camera rotation in the covariance chain and
+    the SH view direction from the camera centre."""
+    listed = _run(scenes.make_scene("c5"), view=2, seed=5)
+    assert listed.sum() > 1_000_000
+
+
 def test_empty():
     s = tiny.random_tiny(7, n_gauss=0)
     from differentiable_hybrid_mesh_amd.pipeline import DeviceScene, Renderer
