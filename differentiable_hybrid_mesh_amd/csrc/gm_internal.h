@@ -195,10 +195,16 @@ __device__ inline void order_tiles_desc(int T, Key key, int32_t* __restrict__ or
 // instead of 16*6.  The exchanges use gfx950's cross-half lane swaps (lanes 32-63
 // with 0-31, odd 16-lane rows with even ones) and DPP row/quad moves, all VALU.
 // On return lane l holds the wave total of value (l >> 2) when (l & 3) == 0.
+//
+// dpp<CTRL>: a lane-permuting move for the controls used here (row rotate, half-row
+// mirror, quad permutations), which read a valid lane everywhere, so bound_ctrl (zero
+// for an invalid source lane) changes no value; with it set and all rows enabled the
+// compiler folds the move into the add that consumes it (one v_add_f32_dpp instead
+// of a move, a hazard wait and an add).
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v)
 {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
 }
 
 __device__ __forceinline__ float wave_sum16(const float* v, int lane)
