@@ -656,6 +656,45 @@ __device__ __forceinline__ int basis10(int lane)
     return ai < 0 ? -1 : ai + (H ? 5 : 0);
 }
 
+// The same reduction of 14 values (a wave on the mesh: the ten above and the four
+// depth-density sums), without the two zero values wave_sum16 would carry: 7 + 4 +
+// 2 + 1 exchanges.  Same pairing order, so bit-identical totals.  On return lane l
+// holds the total of value basis14(l) when (l & 3) == 0 and that index is not
+// negative.
+__device__ __forceinline__ float wave_sum14(const float* v, int lane)
+{
+    float a[7], b[4];
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {  // lanes 0-31 keep v[i], lanes 32-63 keep v[7+i]
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[7 + i]), false,
+                                                        false);
+        a[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // even rows keep a[i], odd rows a[4+i] (a[3] alone: odd rows unused)
+        const float hi = i < 3 ? a[4 + i] : a[3];
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[i]), __float_as_uint(hi), false, false);
+        b[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    const bool h3 = lane & 8, h2 = lane & 4;
+    const float c0 = (h3 ? b[2] : b[0]) + dpp<0x128>(h3 ? b[0] : b[2]);
+    const float c1 = (h3 ? b[3] : b[1]) + dpp<0x128>(h3 ? b[1] : b[3]);
+    const float send = h2 ? c0 : c1;
+    float d = (h2 ? c1 : c0) + dpp<0x141>(send);
+    d += dpp<0x4E>(d);
+    d += dpp<0xB1>(d);
+    return d;
+}
+
+// Value index whose total wave_sum14 leaves in lane l (l & 3 == 0), or -1.
+__device__ __forceinline__ int basis14(int lane)
+{
+    const bool H = lane & 32, R = lane & 16;
+    const int j = ((lane & 8) ? 2 : 0) + ((lane & 4) ? 1 : 0);
+    const int ai = j == 3 ? (R ? -1 : 3) : (R ? 4 + j : j);
+    return ai < 0 ? -1 : ai + (H ? 7 : 0);
+}
+
 // AA = true: the reverse mode of the two-layer form.  The back layer sees the
 // upstream gradients scaled by k = T_F (1 - a_m) and, behind it, bg (depth 0) and
 // the alpha term; per entry dL/dalpha = f dL/dalpha_F + (1 - f) dL/dalpha_B and
@@ -894,7 +933,7 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
                         dsF = daF - daB;
                         act = act | actB;
                     }
-                    float gr[16];
+                    float gr[14];
                     gr[0] = wt * GC0;
                     gr[1] = wt * GC1;
                     gr[2] = wt * GC2;
@@ -913,13 +952,11 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
                         gr[11] = ds * dx;
                         gr[12] = ds * dy;
                         gr[13] = ds * sv;
-                        gr[14] = 0.0f;
-                        gr[15] = 0.0f;
                         gD = __builtin_fmaf(g.d.y, ds, gD);
                         if (__ballot(act)) {
-                            const float v = wave_sum16(gr, lane);
-                            const int c = lane >> 2;
-                            if ((lane & 3) == 0 && c < NBASIS && v != 0.0f) atomicAdd(&s_acc[k][c], v);
+                            const float v = wave_sum14(gr, lane);
+                            const int c = basis14(lane);
+                            if ((lane & 3) == 0 && c >= 0 && v != 0.0f) atomicAdd(&s_acc[k][c], v);
                         }
                     } else if (__ballot(act)) {  // off the mesh the density (and so ds) is zero
                         const float v = wave_sum10(gr, lane);
