@@ -503,9 +503,12 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, const float* _
     }
     const bool wave_on = __ballot(on) != 0;
 
-    float T = 1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f, Z = 0.0f;
+    // one layer: a pixel that has stopped (or lies outside the image) carries -T, so
+    // the sign of T is its done flag and the walk needs no separate one (T >= 1e-4
+    // while it runs; the stopping entry is not taken, so |T| is the final value)
+    float T = AA || inside ? 1.0f : -1.0f, C0 = 0.0f, C1 = 0.0f, C2 = 0.0f, Z = 0.0f;
     int last = 0;
-    bool done = !inside;
+    bool done = !inside;  // two layers only
     // back layer (AA only)
     float TB = 1.0f, B0 = 0.0f, B1 = 0.0f, B2 = 0.0f, ZB = 0.0f;
     int lastB = 0;
@@ -516,7 +519,7 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, const float* _
     if ((int)threadIdx.x < CBF && start + (int)threadIdx.x < end)
         load_record(P.rec, P.ids[start + threadIdx.x], ra, rb, rc, rd);
     for (int b0 = start; b0 < end; b0 += CBF) {
-        if (__syncthreads_count(done & doneB) == CT) break;
+        if (__syncthreads_count(AA ? done & doneB : T < 0.0f) == CT) break;
         const int nb = min(CBF, end - b0);
         if constexpr (STATS) nst += nb;
         if ((int)threadIdx.x < CBF)
@@ -524,13 +527,28 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, const float* _
         if ((int)threadIdx.x < CBF && b0 + CBF + (int)threadIdx.x < end)
             load_record(P.rec, P.ids[b0 + CBF + threadIdx.x], ra, rb, rc, rd);
         __syncthreads();
-        bool wdone = __ballot(!(done & doneB)) == 0;
+        bool wdone = __ballot(AA ? !(done & doneB) : T > 0.0f) == 0;
         for (int i = 0; i < CBF / 64 && !wdone; ++i) {
             unsigned long long m = __ballot((s_m[i * 64 + lane] >> wave) & 1);
             // two entries per iteration: their evaluations are independent of the
             // pixel state, the compositing takes them in order
             auto composite_entry = [&](const Staged& g, const Pair& pr, int k) {
                 const float aF = pr.aF;
+                if constexpr (!AA) {
+                    // T < 0 (stopped) makes Tn < 0: low, not included, -|T| kept
+                    const float Tn = T * (1.0f - aF);
+                    const bool low = Tn < STOP_T;
+                    const bool inc = pr.ok & !low;
+                    const float w = inc ? aF * T : 0.0f;
+                    C0 = __builtin_fmaf(w, g.b.z, C0);
+                    C1 = __builtin_fmaf(w, g.b.w, C1);
+                    C2 = __builtin_fmaf(w, g.c.x, C2);
+                    Z = __builtin_fmaf(w, g.c.y, Z);
+                    T = inc ? Tn : (pr.ok & low) ? -fabsf(T) : T;
+                    last = inc ? b0 + k - start + 1 : last;
+                    if constexpr (STATS) ninc += inc ? 1 : 0;
+                    return;
+                }
                 const bool live = !done & pr.ok;
                 const float Tn = T * (1.0f - aF);
                 const bool stop = live & (Tn < STOP_T);
@@ -574,7 +592,7 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, const float* _
                 composite_entry(g, pr, k);
                 if (two) composite_entry(g2, pr2, k2);
                 if constexpr (STATS) nev += two ? 2 : 1;
-                if (__ballot(!(done & doneB)) == 0) {
+                if (__ballot(AA ? !(done & doneB) : T > 0.0f) == 0) {
                     wdone = true;
                     break;
                 }
@@ -591,6 +609,7 @@ k_composite_fwd(CompParams P, const float* __restrict__ state_cm, const float* _
         if (threadIdx.x == 0) atomicAdd(&stats[2], (unsigned long long)nst);
     }
     if (!inside) return;
+    if constexpr (!AA) T = fabsf(T);
     if constexpr (AA) {
         const float ob = 1.0f - ml.am;
         const float Y0 = B0 + TB * P.bg[0], Y1 = B1 + TB * P.bg[1], Y2 = B2 + TB * P.bg[2];
