@@ -127,24 +127,36 @@ k_radix_scatter(const KT* __restrict__ keys_in, const int32_t* __restrict__ vals
     int32_t val[ITEMS];
     int rank[ITEMS];
     const long long wbase = base + (long long)wave * (CHUNK / RS_WAVES);
+    const bool full = base + CHUNK <= n;  // uniform: every block but the last
+    if (full) {
 #pragma unroll
-    for (int r = 0; r < ITEMS; ++r) {
-        const long long e = wbase + r * 64 + lane;
-        const bool act = e < n;
-        key[r] = act ? keys_in[e] : 0u;
-        val[r] = act ? vals_in[e] : 0;
+        for (int r = 0; r < ITEMS; ++r) {
+            key[r] = keys_in[wbase + r * 64 + lane];
+            val[r] = vals_in[wbase + r * 64 + lane];
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < ITEMS; ++r) {
+            const long long e = wbase + r * 64 + lane;
+            const bool act = e < n;
+            key[r] = act ? keys_in[e] : 0u;
+            val[r] = act ? vals_in[e] : 0;
+        }
     }
 #pragma unroll
     for (int r = 0; r < ITEMS; ++r) {
-        const bool act = wbase + r * 64 + lane < n;
+        const bool act = full || wbase + r * 64 + lane < n;
         const int d = (key[r] >> shift) & (R - 1);
-        unsigned long long peers = __ballot(act);
+        // lanes whose digit differs in some bit: for bit b, sgn is all ones where
+        // the lane's bit is set, and ballot ^ sgn marks the lanes that disagree
+        unsigned long long miss = ~__ballot(act);
 #pragma unroll
         for (int b = 0; b < BITS; ++b) {
-            const bool bit = (d >> b) & 1;
-            const unsigned long long bb = __ballot(bit);
-            peers &= bit ? bb : ~bb;
+            const int sgn = (int)((uint32_t)d << (31 - b)) >> 31;
+            const unsigned long long bb = __ballot(sgn != 0);
+            miss |= bb ^ (unsigned long long)(long long)sgn;
         }
+        const unsigned long long peers = ~miss;
         const int before = s_wc[wave][d];
         rank[r] = before + __popcll(peers & lt);
         if (act && (peers >> lane) == 1ull) s_wc[wave][d] = before + __popcll(peers);  // last lane of the group
