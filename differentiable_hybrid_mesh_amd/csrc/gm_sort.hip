@@ -48,15 +48,18 @@ k_radix_hist(const KT* __restrict__ keys, const long long* __restrict__ d_count,
              int64_t scan_words)
 {
     constexpr int R = 1 << BITS;
-    __shared__ int32_t h[RS_WAVES][RS_RADIX];  // one histogram per wave: fewer colliding LDS atomics
+    // four histograms per wave (lanes l and l + 4 share one), a word of padding each so
+    // that equal digits of different copies fall in different banks: fewer colliding
+    // LDS atomics
+    constexpr int HC = RS_WAVES * 4, HS = RS_RADIX + 1;
+    __shared__ int32_t h[HC][HS];
     const long long n = live_count(d_count, n_max);
-    const int wave = threadIdx.x >> 6;
+    const int hc = (threadIdx.x >> 6) * 4 + (threadIdx.x & 3);
     {  // the status words of the single-launch scan that follows
         const int64_t gid = (int64_t)blockIdx.x * RS_THREADS + threadIdx.x;
         if (gid < scan_words) scan_clear[gid] = 0ull;
     }
-#pragma unroll
-    for (int w = 0; w < RS_WAVES; ++w) h[w][threadIdx.x] = 0;
+    for (int i = threadIdx.x; i < HC * HS; i += RS_THREADS) (&h[0][0])[i] = 0;
     __syncthreads();
     // thread t counts the ITEMS consecutive keys from e0, read with 16-byte loads
     // (keys are 256-byte aligned and e0 is a multiple of ITEMS): all of a block's
@@ -77,18 +80,18 @@ k_radix_hist(const KT* __restrict__ keys, const long long* __restrict__ d_count,
 #pragma unroll
             for (int k = 0; k < PER; ++k) {
                 const uint32_t key = sizeof(KT) == 2 ? (w4[k >> 1] >> (16 * (k & 1))) & 0xffffu : w4[k];
-                atomicAdd(&h[wave][(key >> shift) & (R - 1)], 1);
+                atomicAdd(&h[hc][(key >> shift) & (R - 1)], 1);
             }
         }
     } else {
         for (int k = 0; k < ITEMS; ++k)
-            if (e0 + k < n) atomicAdd(&h[wave][((uint32_t)keys[e0 + k] >> shift) & (R - 1)], 1);
+            if (e0 + k < n) atomicAdd(&h[hc][((uint32_t)keys[e0 + k] >> shift) & (R - 1)], 1);
     }
     __syncthreads();
     if (threadIdx.x < R) {
         int c = 0;
 #pragma unroll
-        for (int w = 0; w < RS_WAVES; ++w) c += h[w][threadIdx.x];
+        for (int w = 0; w < HC; ++w) c += h[w][threadIdx.x];
         hist[threadIdx.x * nblocks + blockIdx.x] = c;
     }
 }
@@ -339,9 +342,11 @@ __device__ inline bool culled(const DevCamera& cam, float softness, float dmax, 
     // evaluated whatever dmax is (so its operands load alongside dmax); an uncovered
     // tile (dmax = +inf) keeps the pair
     const bool covered = dmax < INFINITY;
-    const float xa = tx * GM_TILE + 0.5f, ya = ty * GM_TILE + 0.5f;
-    const float xb = (float)min((tx + 1) * GM_TILE, cam.width) - 0.5f;
-    const float yb = (float)min((ty + 1) * GM_TILE, cam.height) - 0.5f;
+    // the tile's first and last pixel centres, in float (exact: integers + 1/2 below
+    // 2^24); the last is clipped to the image's last pixel centre
+    const float xa = (float)(tx * GM_TILE) + 0.5f, ya = (float)(ty * GM_TILE) + 0.5f;
+    const float xb = fminf(xa + (float)(GM_TILE - 1), (float)cam.width - 0.5f);
+    const float yb = fminf(ya + (float)(GM_TILE - 1), (float)cam.height - 0.5f);
     const float ax = g0 * (xa - u), bx = g0 * (xb - u);
     const float ay = g1 * (ya - v), by = g1 * (yb - v);
     const float zmin = zc + (fminf(ax, bx) + fminf(ay, by));
@@ -456,8 +461,8 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
         // row = floor(t / w): the quotient's fraction is at least 1/(2w) away from an
         // integer and t < 2^20, so one reciprocal multiply is exact enough
         const int q = (int)(((float)t + 0.5f) * __builtin_amdgcn_rcpf((float)w));
-        const int ty = y0 + q, tx = x0 + (t - q * w);
-        tile = ty * cam.tx + tx;
+        const int ty = y0 + q, tx = x0 + (t - (int)__umul24(q, w));  // 24-bit products: full rate
+        tile = (int)__umul24(ty, cam.tx) + tx;
         id = gi.w;
         if (!decide || !cp.tile_dmax) return true;
         const float4 ga = s_ga[wave][g], gb = s_gb[wave][g];
