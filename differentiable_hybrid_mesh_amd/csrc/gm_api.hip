@@ -243,8 +243,10 @@ __device__ __forceinline__ void sc_store(unsigned long long* p, unsigned long lo
 // all zero on entry.
 __global__ void __launch_bounds__(SCAN_THREADS) k_scan_lb(const int32_t* __restrict__ in, int64_t n,
                                                           int32_t* __restrict__ out, long long* __restrict__ total,
-                                                          unsigned long long* __restrict__ status)
+                                                          unsigned long long* __restrict__ status,
+                                                          const int32_t* __restrict__ skip)
 {
+    if (skip && *skip) return;  // uniform
     __shared__ long long lds[SCAN_THREADS / 64];
     __shared__ int s_blk;
     __shared__ long long s_pre;
@@ -306,7 +308,7 @@ __global__ void __launch_bounds__(SCAN_THREADS) k_scan_lb(const int32_t* __restr
 int64_t scan_lb_clear_words(int64_t n) { return n <= SCAN1_MAX ? 0 : div_up(n, SCAN_CHUNK) + 1; }
 
 gm_status exclusive_scan_lb(const int32_t* in, int32_t* out, int64_t n, long long* total, void* ws,
-                            hipStream_t stream)
+                            hipStream_t stream, const int32_t* skip)
 {
     if (n <= SCAN1_MAX) {
         k_scan_single<<<1, SCAN1_THREADS, 0, stream>>>(in, n, out, total);
@@ -314,7 +316,7 @@ gm_status exclusive_scan_lb(const int32_t* in, int32_t* out, int64_t n, long lon
         return GM_OK;
     }
     k_scan_lb<<<(unsigned)div_up(n, SCAN_CHUNK), SCAN_THREADS, 0, stream>>>(in, n, out, total,
-                                                                         (unsigned long long*)ws);
+                                                                         (unsigned long long*)ws, skip);
     GM_LAUNCH_CHECK();
     return GM_OK;
 }

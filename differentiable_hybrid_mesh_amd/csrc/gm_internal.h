@@ -82,10 +82,12 @@ gm_status exclusive_scan(const int32_t* in, int32_t* out, int64_t n, long long* 
 // The same scan in one launch for callers whose previous kernel on the stream
 // cleared the first scan_lb_clear_words(n) 64-bit words of ws (the blocks find their
 // offsets by a decoupled look-back over those words; a single block does it all for
-// short inputs).  Workspace: scan_ws_bytes(n).
+// short inputs).  Workspace: scan_ws_bytes(n).  skip (device, may be NULL): when it
+// points to a non-zero word the multi-block launch does nothing (the single-block
+// path ignores it).
 int64_t scan_lb_clear_words(int64_t n);
 gm_status exclusive_scan_lb(const int32_t* in, int32_t* out, int64_t n, long long* total, void* ws,
-                            hipStream_t stream);
+                            hipStream_t stream, const int32_t* skip = nullptr);
 
 // Projection (gm_project.hip): the argument checks of gm_project_gaussians, and its
 // kernel with the depth sort's input written beside the records (keys[i] = the bits

@@ -41,20 +41,85 @@ __device__ inline long long live_count(const long long* __restrict__ d_count, lo
 // ---------------------------------------------------------------------------
 // stable LSD radix sort pass over a digit of BITS <= 8 bits
 // ---------------------------------------------------------------------------
+// The top-byte pass of the 32-bit depth sort is skipped on the device when every
+// listed key (not all ones) has the same top byte and none has all ones in its low 24
+// bits: after the three low-byte passes the order is then already the final one (the
+// unlisted keys, all ones, sort after every listed one on their low 24 bits, in index
+// order).  The first pass's histogram blocks record, per block, the OR and the AND of
+// the listed keys' top bytes, whether a listed key has a low 24 bits of all ones, and
+// the unlisted count; block 0 of the second pass's histogram reduces them to the skip
+// flag and the listed count, which the last pass's kernels read.
+struct TopSkip {
+    int4* stats_out = nullptr;       // first pass: per-block record
+    const int4* stats_in = nullptr;  // second pass: the records ...
+    int32_t* flag_out = nullptr;     // ... reduced by block 0 to {skip, listed count}
+    const int32_t* flag = nullptr;   // last pass: skip when flag[0]; flag[1] = listed count
+    int32_t* count_out = nullptr;    // last pass, skipped: where the listed count is read
+};
+
+__device__ __forceinline__ void block_reduce4(int4& v, int4* s_tmp)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        v.x |= __shfl_xor(v.x, o, 64);
+        v.y &= __shfl_xor(v.y, o, 64);
+        v.z |= __shfl_xor(v.z, o, 64);
+        v.w += __shfl_xor(v.w, o, 64);
+    }
+    if ((threadIdx.x & 63) == 0) s_tmp[threadIdx.x >> 6] = v;
+    __syncthreads();
+    v = make_int4(0, 0xff, 0, 0);
+#pragma unroll
+    for (int w = 0; w < RS_WAVES; ++w) {
+        v.x |= s_tmp[w].x;
+        v.y &= s_tmp[w].y;
+        v.z |= s_tmp[w].z;
+        v.w += s_tmp[w].w;
+    }
+}
+
+__device__ __forceinline__ void top_stats_add(int4& st, uint32_t key)
+{
+    const bool listed = key != 0xffffffffu;
+    const int top = (int)(key >> 24);
+    st.x |= listed ? top : 0;
+    st.y &= listed ? top : 0xff;
+    st.z |= (listed && (key & 0xffffffu) == 0xffffffu) ? 1 : 0;
+    st.w += listed ? 0 : 1;
+}
+
 template <int BITS, typename KT, int ITEMS>
 __global__ void __launch_bounds__(RS_THREADS)
 k_radix_hist(const KT* __restrict__ keys, const long long* __restrict__ d_count, long long n_max,
              int shift, int nblocks, int32_t* __restrict__ hist, unsigned long long* __restrict__ scan_clear,
-             int64_t scan_words)
+             int64_t scan_words, TopSkip ts)
 {
+    if (ts.flag && ts.flag[0]) return;  // uniform: the pass is skipped (so is its scan)
     constexpr int R = 1 << BITS;
     // four histograms per wave (lanes l and l + 4 share one), a word of padding each so
     // that equal digits of different copies fall in different banks: fewer colliding
     // LDS atomics
     constexpr int HC = RS_WAVES * 4, HS = RS_RADIX + 1;
     __shared__ int32_t h[HC][HS];
+    __shared__ int4 s_st[RS_WAVES];
     const long long n = live_count(d_count, n_max);
     const int hc = (threadIdx.x >> 6) * 4 + (threadIdx.x & 3);
+    if (ts.stats_in && blockIdx.x == 0) {  // second pass: the skip decision
+        int4 st = make_int4(0, 0xff, 0, 0);
+        for (int b = threadIdx.x; b < nblocks; b += RS_THREADS) {
+            const int4 r = ts.stats_in[b];
+            st.x |= r.x;
+            st.y &= r.y;
+            st.z |= r.z;
+            st.w += r.w;
+        }
+        block_reduce4(st, s_st);
+        if (threadIdx.x == 0) {
+            ts.flag_out[0] = st.x == st.y && st.z == 0 ? 1 : 0;
+            ts.flag_out[1] = (int32_t)(n - st.w);
+        }
+    }
+    int4 st = make_int4(0, 0xff, 0, 0);  // first pass: this block's record
     {  // the status words of the single-launch scan that follows
         const int64_t gid = (int64_t)blockIdx.x * RS_THREADS + threadIdx.x;
         if (gid < scan_words) scan_clear[gid] = 0ull;
@@ -81,11 +146,21 @@ k_radix_hist(const KT* __restrict__ keys, const long long* __restrict__ d_count,
             for (int k = 0; k < PER; ++k) {
                 const uint32_t key = sizeof(KT) == 2 ? (w4[k >> 1] >> (16 * (k & 1))) & 0xffffu : w4[k];
                 atomicAdd(&h[hc][(key >> shift) & (R - 1)], 1);
+                if (ts.stats_out) top_stats_add(st, key);
             }
         }
     } else {
         for (int k = 0; k < ITEMS; ++k)
-            if (e0 + k < n) atomicAdd(&h[hc][((uint32_t)keys[e0 + k] >> shift) & (R - 1)], 1);
+            if (e0 + k < n) {
+                const uint32_t key = (uint32_t)keys[e0 + k];
+                atomicAdd(&h[hc][(key >> shift) & (R - 1)], 1);
+                if (ts.stats_out) top_stats_add(st, key);
+            }
+    }
+    if (ts.stats_out) {
+        __syncthreads();  // s_st may still be read by the decision above
+        block_reduce4(st, s_st);
+        if (threadIdx.x == 0) ts.stats_out[blockIdx.x] = st;
     }
     __syncthreads();
     if (threadIdx.x < R) {
@@ -108,8 +183,17 @@ template <int BITS, typename KT, int ITEMS>
 __global__ void __launch_bounds__(RS_THREADS)
 k_radix_scatter(const KT* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
                 const long long* __restrict__ d_count, long long n_max, int shift, int nblocks,
-                const int32_t* __restrict__ offs, KT* __restrict__ keys_out, int32_t* __restrict__ vals_out)
+                const int32_t* __restrict__ offs, KT* __restrict__ keys_out, int32_t* __restrict__ vals_out,
+                TopSkip ts)
 {
+    if (ts.flag && ts.flag[0]) {  // uniform: the order is final; move the values to the output
+        const long long n = live_count(d_count, n_max);
+        for (long long i = (long long)blockIdx.x * RS_THREADS + threadIdx.x; i < n;
+             i += (long long)gridDim.x * RS_THREADS)
+            vals_out[i] = vals_in[i];
+        if (blockIdx.x == 0 && threadIdx.x == 0) *ts.count_out = ts.flag[1];
+        return;
+    }
     constexpr int CHUNK = RS_THREADS * ITEMS;
     __shared__ KT s_k[CHUNK];
     __shared__ int32_t s_v[CHUNK];
@@ -217,22 +301,22 @@ size_t radix_ws_bytes(int64_t n, int items)
 {
     const int64_t nb = div_up(n > 0 ? n : 1, (int64_t)RS_THREADS * items);
     return 2 * align_up(sizeof(int32_t) * (size_t)(RS_RADIX * nb + 1), 256) + scan_ws_bytes(RS_RADIX * nb) +
-           align_up(sizeof(long long), 256);
+           align_up(sizeof(long long), 256) + align_up(sizeof(int4) * (size_t)nb + 4 * sizeof(int32_t), 256);
 }
 
 template <int BITS, typename KT, int ITEMS>
 static gm_status radix_pass(const KT* kin, const int32_t* vin, KT* kout, int32_t* vout, int shift,
                             const long long* d_count, int64_t n_max, int nb, int32_t* hist, int32_t* offs,
-                            long long* tot, void* scan_ws, hipStream_t stream)
+                            long long* tot, void* scan_ws, const TopSkip& ts, hipStream_t stream)
 {
     const int64_t nscan = (int64_t)(1 << BITS) * nb;
     k_radix_hist<BITS, KT, ITEMS><<<nb, RS_THREADS, 0, stream>>>(kin, d_count, n_max, shift, nb, hist,
                                                                   (unsigned long long*)scan_ws,
-                                                                  scan_lb_clear_words(nscan));
+                                                                  scan_lb_clear_words(nscan), ts);
     GM_LAUNCH_CHECK();
-    if (gm_status s = exclusive_scan_lb(hist, offs, nscan, tot, scan_ws, stream)) return s;
+    if (gm_status s = exclusive_scan_lb(hist, offs, nscan, tot, scan_ws, stream, ts.flag)) return s;
     k_radix_scatter<BITS, KT, ITEMS><<<nb, RS_THREADS, 0, stream>>>(kin, vin, d_count, n_max, shift, nb, offs, kout,
-                                                                     vout);
+                                                                     vout, ts);
     GM_LAUNCH_CHECK();
     return GM_OK;
 }
@@ -263,24 +347,39 @@ static gm_status radix_sort(KT* ka, int32_t* va, KT* kb, int32_t* vb, int nbits,
     long long* tot = (long long*)w;
     w += align_up(sizeof(long long), 256);
     void* scan_ws = w;
+    w += scan_ws_bytes((int64_t)RS_RADIX * nb);
+    int4* ts_stats = (int4*)w;
+    int32_t* ts_flag = (int32_t*)(ts_stats + nb);
     KT* kin = ka;
     int32_t* vin = va;
     KT* kout = kb;
     int32_t* vout = vb;
     const int npass = radix_passes(nbits);
+    // the skippable top byte: 32-bit keys in four 8-bit passes with the multi-block scan
+    const bool topskip = sizeof(KT) == 4 && nbits == 32 && npass == 4 && scan_lb_clear_words((int64_t)RS_RADIX * nb) > 0;
     int shift = 0;
     for (int p = 0; p < npass; ++p) {
         const int bits = (nbits - shift + (npass - p) - 1) / (npass - p);  // ceil(remaining / passes left)
+        TopSkip ts;
+        if (topskip && p == 0) ts.stats_out = ts_stats;
+        if (topskip && p == 1) {
+            ts.stats_in = ts_stats;
+            ts.flag_out = ts_flag;
+        }
+        if (topskip && p == 3) {
+            ts.flag = ts_flag;
+            ts.count_out = offs + (size_t)(RS_RADIX - 1) * nb;
+        }
         gm_status s = GM_OK;
         switch (bits) {
-        case 1: s = radix_pass<1, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        case 2: s = radix_pass<2, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        case 3: s = radix_pass<3, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        case 4: s = radix_pass<4, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        case 5: s = radix_pass<5, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        case 6: s = radix_pass<6, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        case 7: s = radix_pass<7, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
-        default: s = radix_pass<8, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, stream); break;
+        case 1: s = radix_pass<1, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, ts, stream); break;
+        case 2: s = radix_pass<2, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, ts, stream); break;
+        case 3: s = radix_pass<3, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, ts, stream); break;
+        case 4: s = radix_pass<4, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, ts, stream); break;
+        case 5: s = radix_pass<5, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, ts, stream); break;
+        case 6: s = radix_pass<6, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, ts, stream); break;
+        case 7: s = radix_pass<7, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, ts, stream); break;
+        default: s = radix_pass<8, KT, ITEMS>(kin, vin, kout, vout, shift, d_count, n_max, nb, hist, offs, tot, scan_ws, ts, stream); break;
         }
         if (s) return s;
         shift += bits;
