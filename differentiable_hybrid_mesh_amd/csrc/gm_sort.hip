@@ -798,10 +798,9 @@ static gm_status sort_tiles(const DevCamera& dc, int32_t N, const float* rec, co
         GM_LAUNCH_CHECK();
         return GM_OK;
     }
-    const int32_t* order = w.dva;  // 4 passes (a skipped top-byte pass copies): back in the first buffer pair
+    const int32_t* order = w.dva;  // 4 passes: back in the first buffer pair
     // number of listed Gaussians = offset of top byte 0xff in the depth sort's last
-    // pass, block 0 (written there by a skipped pass too); valid until the tile sort
-    // below reuses the histogram buffers
+    // pass, block 0; valid until the tile sort below reuses the histogram buffers
     const int32_t* d_nvis = radix_last_offsets(w.aux, N, DS_ITEMS) +
                             (size_t)(RS_RADIX - 1) * div_up(N, (int64_t)RS_THREADS * DS_ITEMS);
     const bool lds = tile_dmax && T <= PW_LDS_MAX_TILES;
