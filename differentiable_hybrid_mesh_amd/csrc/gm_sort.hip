@@ -525,7 +525,7 @@ __global__ void __launch_bounds__(64 * PW_WAVES)
 k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nchunks,
         const int32_t* __restrict__ order, const float* __restrict__ rec, int32_t* __restrict__ chunk_cnt,
         const int32_t* __restrict__ chunk_off, unsigned long long* __restrict__ bits,
-        const long long* __restrict__ d_total, long long cap, KT* __restrict__ tkeys,
+        int2* __restrict__ crect, const long long* __restrict__ d_total, long long cap, KT* __restrict__ tkeys,
         int32_t* __restrict__ tvals, int32_t* __restrict__ ranges, int64_t n2)
 {
     if (!EMIT)
@@ -579,14 +579,23 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
         if (chunk >= nchunks) break;
         const int jl = chunk * 64 + lane;
         int nt = 0;
-        if (jl < nvis) {
-            const int id = order[jl];
+        // the counting pass reads the records (the cull needs them) and keeps each
+        // Gaussian's rect in depth order (crect); the emitting pass reads that instead
+        // of gathering 64-byte records again
+        auto stage_cull = [&](int id) {
             const float4* r = reinterpret_cast<const float4*>(rec + (size_t)id * GM_REC);
             const float4 a = r[0], b = r[1], cc = r[2], d = r[3];
-            const int lo = __float_as_int(d.y), hi = __float_as_int(d.z);
-            nt = ((hi & 0xffff) - (lo & 0xffff)) * ((hi >> 16) - (lo >> 16));
             s_ga[wave][lane] = make_float4(a.x, a.y, cc.y, cc.z);
             s_gb[wave][lane] = make_float4(cc.w, d.x * cp.softness, cull_scrit(b.y), 0.0f);
+            return make_int2(__float_as_int(d.y), __float_as_int(d.z));
+        };
+        int id = 0;
+        if (jl < nvis) {
+            id = order[jl];
+            const int2 lh = EMIT ? crect[jl] : stage_cull(id);
+            if (!EMIT) crect[jl] = lh;
+            const int lo = lh.x, hi = lh.y;
+            nt = ((hi & 0xffff) - (lo & 0xffff)) * ((hi >> 16) - (lo >> 16));
             s_gi[wave][lane].y = lo;
             s_gi[wave][lane].z = hi;
             s_gi[wave][lane].w = id;
@@ -601,6 +610,9 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
         c.start = P - nt;
         s_gi[wave][lane].x = c.start;
         c.total = __builtin_amdgcn_readlane(P, 63);
+        // a chunk longer than the stored ballots takes the cull again past them: the
+        // emitting pass then needs the records' cull fields (uniform per chunk)
+        if (EMIT && c.total > PW_WORDS * 64 && jl < nvis) (void)stage_cull(id);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -695,6 +707,7 @@ __global__ void k_tile_ranges(const KT* __restrict__ keys, const long long* __re
 struct SortWs {
     int32_t *cnt, *off;            // per-chunk pair counts and their exclusive prefix
     unsigned long long* bits;      // per-chunk step ballots of the counting pass
+    int2* crect;                   // the listed Gaussians' rects in depth order (counting pass)
     uint32_t *dka, *dkb;
     int32_t *dva, *dvb;
     uint32_t *tka, *tkb;
@@ -718,6 +731,7 @@ static size_t sort_layout(int64_t N, int64_t cap, int64_t T, char* base, SortWs*
     s.cnt = (int32_t*)take(4 * nch);
     s.off = (int32_t*)take(4 * (nch + 1));
     s.bits = (unsigned long long*)take(8 * (size_t)nch * PW_WORDS);
+    s.crect = (int2*)take(8 * (size_t)nch * 64);
     s.dka = (uint32_t*)take(4 * n1);
     s.dkb = (uint32_t*)take(4 * n1);
     s.dva = (int32_t*)take(4 * n1);
@@ -776,7 +790,7 @@ static gm_status emit_and_sort(const DevCamera& dc, const CullParams& cp, const 
     int32_t* va = (npass % 2 == 0) ? sorted_ids : w.tva;
     int32_t* vb = (npass % 2 == 0) ? w.tva : sorted_ids;
     k_pairs<true, false, KT><<<gW, 64 * PW_WAVES, 0, stream>>>(dc, cp, d_nvis, nchunks, order, rec, nullptr, w.off,
-                                                               w.bits, total, kcap, ka, va, nullptr, 0);
+                                                               w.bits, w.crect, total, kcap, ka, va, nullptr, 0);
     GM_LAUNCH_CHECK();
     if (gm_status s = radix_sort<KT, RS_ITEMS>(ka, va, kb, vb, tbits, total, kcap, w.aux, stream)) return s;
     const KT* kfin = (npass % 2 == 0) ? ka : kb;
@@ -798,9 +812,10 @@ static gm_status sort_tiles(const DevCamera& dc, int32_t N, const float* rec, co
         GM_LAUNCH_CHECK();
         return GM_OK;
     }
-    const int32_t* order = w.dva;  // 4 passes: back in the first buffer pair
+    const int32_t* order = w.dva;  // 4 passes (a skipped top-byte pass copies): back in the first buffer pair
     // number of listed Gaussians = offset of top byte 0xff in the depth sort's last
-    // pass, block 0; valid until the tile sort below reuses the histogram buffers
+    // pass, block 0 (written there by a skipped pass too); valid until the tile sort
+    // below reuses the histogram buffers
     const int32_t* d_nvis = radix_last_offsets(w.aux, N, DS_ITEMS) +
                             (size_t)(RS_RADIX - 1) * div_up(N, (int64_t)RS_THREADS * DS_ITEMS);
     const bool lds = tile_dmax && T <= PW_LDS_MAX_TILES;
@@ -810,8 +825,8 @@ static gm_status sort_tiles(const DevCamera& dc, int32_t N, const float* rec, co
     const unsigned gW = (unsigned)std::min<int64_t>(div_up(nchunks, PW_WAVES), PW_COUNT_BLOCKS);
     const unsigned gE = (unsigned)std::min<int64_t>(div_up(nchunks, PW_WAVES), PW_EMIT_BLOCKS);
     auto count = lds ? k_pairs<false, true, uint16_t> : k_pairs<false, false, uint16_t>;  // no keys written
-    count<<<gW, 64 * PW_WAVES, shm, stream>>>(dc, cp, d_nvis, nchunks, order, rec, w.cnt, nullptr, w.bits, nullptr, 0,
-                                              nullptr, nullptr, tile_ranges, 2 * T);  // also clears the ranges
+    count<<<gW, 64 * PW_WAVES, shm, stream>>>(dc, cp, d_nvis, nchunks, order, rec, w.cnt, nullptr, w.bits, w.crect,
+                                              nullptr, 0, nullptr, nullptr, tile_ranges, 2 * T);  // also clears the ranges
     GM_LAUNCH_CHECK();
     if (gm_status s = exclusive_scan(w.cnt, w.off, nchunks, total, w.scan, stream)) return s;
     // 3. emit (tile, id) in depth order; 4. stable sort by tile; 5. tile ranges.
