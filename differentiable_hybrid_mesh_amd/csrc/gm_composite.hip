@@ -920,6 +920,14 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
                     const float dx = pr.dx, dy = pr.dy, oG = pr.oG, al = pr.al, f = pr.f, pdf = pr.pdf, sv = pr.s;
                     const float aF = pr.aF;
                     bool act = (rel < last) & pr.ok;
+                    // whether a lane of the wave takes the entry: the ballot of each
+                    // comparison of act (one layer), so the branch tests a scalar mask
+                    // instead of turning act into a vector value and back
+                    auto any_act = [&]() -> bool {
+                        if constexpr (AA) return __ballot(act) != 0ull;
+                        return (__ballot(rel < last) & __ballot(!(pr.q > g.d.z)) & __ballot(pr.al >= SKIP_ALPHA) &
+                                __ballot(pr.aF >= SKIP_ALPHA)) != 0ull;
+                    };
                     // per-pixel basis sums; the 13 record gradients are linear in them
                     // (formed once per entry at the flush):
                     //  0-2 w GC, 3 w GZ, 4 H, 5 H dx, 6 H dy, 7 H dx^2, 8 H dx dy, 9 H dy^2,
@@ -972,12 +980,12 @@ k_composite_bwd(CompParams P, const float* __restrict__ state_T, const int32_t* 
                         gr[12] = ds * dy;
                         gr[13] = ds * sv;
                         gD = __builtin_fmaf(g.d.y, ds, gD);
-                        if (__ballot(act)) {
+                        if (any_act()) {
                             const float v = wave_sum14(gr, lane);
                             const int c = basis14(lane);
                             if ((lane & 3) == 0 && c >= 0 && v != 0.0f) atomicAdd(&s_acc[k][c], v);
                         }
-                    } else if (__ballot(act)) {  // off the mesh the density (and so ds) is zero
+                    } else if (any_act()) {  // off the mesh the density (and so ds) is zero
                         const float v = wave_sum10(gr, lane);
                         const int c = basis10(lane);
                         if ((lane & 3) == 0 && c >= 0 && v != 0.0f) atomicAdd(&s_acc[k][c], v);
