@@ -311,7 +311,7 @@ __device__ __forceinline__ Pair eval_pair(const Staged& g, float pxc, float pyc,
         const float num = (D - g.c.y) - __builtin_fmaf(g.c.z, p.dx, g.c.w * p.dy);
         if (softness > 0.0f) {
             p.s = on ? num * g.d.y : 0.0f;  // off the mesh D = +inf: keep s finite
-            if (__ballot(on & (fabsf(p.s) <= 6.0f))) {
+            if ((__ballot(on) & __ballot(fabsf(p.s) <= 6.0f)) != 0ull) {  // scalar masks (see the backward's entry skip)
                 float pd, fc;
                 const float fo = normal_cdf_pdf(p.s, pd, fc);
                 p.f = on ? fo : 1.0f;
