@@ -487,7 +487,9 @@ struct ChunkCtx {
 __device__ __forceinline__ int step_owner(const int4 (*s_gi)[64], const ChunkCtx& c, int f0, int& carry)
 {
     const int f = f0 + c.lane;
-    unsigned long long m = __ballot(c.nt > 0 && c.start >= f0 && c.start < f0 + 64);
+    // three comparison masks ANDed (a combined bool would be turned into a vector
+    // value and back)
+    unsigned long long m = __ballot(c.nt > 0) & __ballot(c.start >= f0) & __ballot(c.start < f0 + 64);
     int g = carry;
     if (__popcll(m) <= 6) {
         while (m) {
@@ -512,7 +514,7 @@ __device__ __forceinline__ int step_owner(const int4 (*s_gi)[64], const ChunkCtx
 // the step, else the carried one.
 __device__ __forceinline__ void skip_owner(const ChunkCtx& c, int f0, int& carry)
 {
-    const unsigned long long m = __ballot(c.nt > 0 && c.start >= f0 && c.start < f0 + 64);
+    const unsigned long long m = __ballot(c.nt > 0) & __ballot(c.start >= f0) & __ballot(c.start < f0 + 64);
     if (m) carry = 63 - __builtin_clzll(m);
 }
 
@@ -550,11 +552,13 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
     __syncthreads();
     // tile and id of the pair at flat index f0 + lane (owner g), and its keep
     // decision when `decide` (otherwise it is already known)
+    // Straight-line: a lane past the chunk's pairs takes its owner's first tile and
+    // returns false, so the keep decision stays a comparison mask for the ballot.
     auto keep_of = [&](int f0, int g, int& tile, int& id, bool decide) -> bool {
         const int f = f0 + lane;
-        if (f >= c.total) return false;
+        const bool in = f < c.total;
         const int4 gi = s_gi[wave][g];
-        const int t = f - gi.x;
+        const int t = in ? f - gi.x : 0;
         const int rlo = gi.y, rhi = gi.z;
         const int x0 = rlo & 0xffff, y0 = rlo >> 16, w = (rhi & 0xffff) - x0;
         // row = floor(t / w): the quotient's fraction is at least 1/(2w) away from an
@@ -563,10 +567,10 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
         const int ty = y0 + q, tx = x0 + (t - (int)__umul24(q, w));  // 24-bit products: full rate
         tile = (int)__umul24(ty, cam.tx) + tx;
         id = gi.w;
-        if (!decide || !cp.tile_dmax) return true;
+        if (!decide || !cp.tile_dmax) return in;  // uniform
         const float4 ga = s_ga[wave][g], gb = s_gb[wave][g];
         const float dmax = LDS ? s_dmax[tile] : cp.tile_dmax[tile];
-        return !culled(cam, cp.softness, dmax, tx, ty, ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z);
+        return in & !culled(cam, cp.softness, dmax, tx, ty, ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z);
     };
     // Block b owns chunks b, b + grid, b + 2 grid, ...; its waves take them in turn
     // from an LDS counter.  Chunk pair counts vary with the Gaussians' rects: a fixed
