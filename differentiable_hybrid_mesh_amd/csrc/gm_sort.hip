@@ -552,8 +552,8 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
     __syncthreads();
     // tile and id of the pair at flat index f0 + lane (owner g), and its keep
     // decision when `decide` (otherwise it is already known)
-    // Straight-line: a lane past the chunk's pairs takes its owner's first tile and
-    // returns false, so the keep decision stays a comparison mask for the ballot.
+    // Straight-line: a lane past the chunk's pairs computes with t = 0, reads tile 0
+    // and returns false, so the keep decision stays a comparison mask for the ballot.
     auto keep_of = [&](int f0, int g, int& tile, int& id, bool decide) -> bool {
         const int f = f0 + lane;
         const bool in = f < c.total;
@@ -565,7 +565,10 @@ k_pairs(DevCamera cam, CullParams cp, const int32_t* __restrict__ d_nvis, int nc
         // integer and t < 2^20, so one reciprocal multiply is exact enough
         const int q = (int)(((float)t + 0.5f) * __builtin_amdgcn_rcpf((float)w));
         const int ty = y0 + q, tx = x0 + (t - (int)__umul24(q, w));  // 24-bit products: full rate
-        tile = (int)__umul24(ty, cam.tx) + tx;
+        // a lane past the chunk's pairs may have an owner whose rect this wave never
+        // wrote (a chunk past the listed Gaussians, or a trailing lane found by the
+        // binary search): its tile is then garbage, so it reads tile 0 instead
+        tile = in ? (int)__umul24(ty, cam.tx) + tx : 0;
         id = gi.w;
         if (!decide || !cp.tile_dmax) return in;  // uniform
         const float4 ga = s_ga[wave][g], gb = s_gb[wave][g];
