@@ -44,6 +44,9 @@ struct MeshBwdParams {
     const float* mips;
     int lit;
     double lpos[3], lamb[3], ldif[3], lspec[3], lshin;
+    // the camera widened to fp64 on the host: uniform operands stay in scalar
+    // registers instead of taking vector registers from the per-pixel chain
+    double R[9], t[3], fx, fy, cx, cy, ifx, ify;
 };
 
 __host__ __device__ inline size_t level_offset(int S, int l)
@@ -88,6 +91,20 @@ __device__ inline void bilin(const float* __restrict__ lvl, int s, double u, dou
         b.du[c] = ((t01 - t00) * (1.0 - ay) + (t11 - t10) * ay) * s * su;
         b.dv[c] = (bot - top) * s * sv;
     }
+}
+
+// 1/x in fp64: the hardware's reciprocal estimate refined by two Newton-Raphson
+// steps (r <- r + r (1 - x r)), each of which squares the relative error, so the
+// result is correct to within an ulp or two (the quotients here are values, not
+// decisions); x is a depth, a triangle's doubled area or a sum of perspective
+// weights, never zero, infinite or subnormal at a covered pixel.
+__device__ __forceinline__ double rcp64(double x)
+{
+    double r = __builtin_amdgcn_rcp(x);
+    double e = __builtin_fma(-x, r, 1.0);
+    r = __builtin_fma(r, e, r);
+    e = __builtin_fma(-x, r, 1.0);
+    return __builtin_fma(r, e, r);
 }
 
 __device__ __forceinline__ void addf(float* p, double v)
@@ -197,33 +214,48 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
     int vi[3] = {0, 0, 0}, ti[3] = {0, 0, 0};
     if (f >= 0) {
         const double pu = px + 0.5, pv = py + 0.5;
-        double R[9], t[3];
-#pragma unroll
-        for (int i = 0; i < 9; ++i) R[i] = P.cam.R[i];
-#pragma unroll
-        for (int i = 0; i < 3; ++i) t[i] = P.cam.t[i];
-        const double fx = P.cam.fx, fy = P.cam.fy, cx = P.cam.cx, cy = P.cam.cy;
-        const double rx = (pu - cx) / fx, ry = (pv - cy) / fy;  // the pixel's ray, z = 1
+        const double* R = P.R;
+        const double* t = P.t;
+        const double fx = P.fx, fy = P.fy, cx = P.cx, cy = P.cy;
+        const double rx = (pu - cx) * P.ifx, ry = (pv - cy) * P.ify;  // the pixel's ray, z = 1
         // ---- forward ---------------------------------------------------------------
         // reciprocals taken once (the chain below multiplies by them: these are
         // values, not decisions, so the rounding order is free)
         double xc[3][3], u[3], v[3], z[3], iz[3];
 #pragma unroll
         for (int k = 0; k < 3; ++k) vi[k] = P.faces[k * P.F + f];
+        // everything the corners index goes out in one batch (positions, colours,
+        // normals): one round trip, which the scheduler must not split
+        float vpos[3][3], vcol[3][3] = {}, vnor[3][3] = {};
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+#pragma unroll
+            for (int c = 0; c < 3; ++c) vpos[k][c] = P.verts[c * P.V + vi[k]];
+        if constexpr (LIT)
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+#pragma unroll
+                for (int c = 0; c < 3; ++c) vnor[k][c] = P.vnormal[c * P.V + vi[k]];
+        if (!TEX && P.vcolor)  // the same for every thread
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+#pragma unroll
+                for (int c = 0; c < 3; ++c) vcol[k][c] = P.vcolor[c * P.V + vi[k]];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
-            const double X0 = P.verts[vi[k]], X1 = P.verts[P.V + vi[k]], X2 = P.verts[2 * P.V + vi[k]];
+            const double X0 = vpos[k][0], X1 = vpos[k][1], X2 = vpos[k][2];
 #pragma unroll
             for (int r = 0; r < 3; ++r) xc[k][r] = R[3 * r] * X0 + R[3 * r + 1] * X1 + R[3 * r + 2] * X2 + t[r];
             z[k] = xc[k][2];
-            iz[k] = 1.0 / z[k];
+            iz[k] = rcp64(z[k]);
             u[k] = fx * xc[k][0] * iz[k] + cx;
             v[k] = fy * xc[k][1] * iz[k] + cy;
         }
         const int ea[3] = {1, 2, 0}, eb[3] = {2, 0, 1};  // edge opposite corner k
         double lam[3], w[3], Wsum = 0.0;
         const double A = (u[1] - u[0]) * (v[2] - v[0]) - (v[1] - v[0]) * (u[2] - u[0]);
-        const double iA = 1.0 / A;
+        const double iA = rcp64(A);
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
             const int a = ea[k], b = eb[k];
@@ -232,24 +264,11 @@ k_mesh_bwd(MeshBwdParams P, const int32_t* __restrict__ face_id, const float* __
             w[k] = lam[k] * iz[k];
             Wsum += w[k];
         }
-        const double zz = 1.0 / Wsum;
+        const double zz = rcp64(Wsum);
         double bb[3];
 #pragma unroll
         for (int k = 0; k < 3; ++k) bb[k] = w[k] * zz;
 
-        // the corners' colours and normals, in one batch (one round trip rather than
-        // one per use in the sums below)
-        float vcol[3][3] = {}, vnor[3][3] = {};
-        if (!TEX && P.vcolor)  // the same for every thread
-#pragma unroll
-            for (int k = 0; k < 3; ++k)
-#pragma unroll
-                for (int c = 0; c < 3; ++c) vcol[k][c] = P.vcolor[c * P.V + vi[k]];
-        if constexpr (LIT)
-#pragma unroll
-            for (int k = 0; k < 3; ++k)
-#pragma unroll
-                for (int c = 0; c < 3; ++c) vnor[k][c] = P.vnormal[c * P.V + vi[k]];
         double gc[3], gz = gzf;
 #pragma unroll
         for (int c = 0; c < 3; ++c) gc[c] = gcf[c];
@@ -599,16 +618,28 @@ __global__ void k_pyramid_adjoint(float* __restrict__ fine, const float* __restr
     fine[i] += 0.25f * coarse[((y >> 1) * s + (x >> 1)) * 3 + c];
 }
 
-__global__ void k_zero(float* __restrict__ p, int64_t n)
+// Clears of the gradient outputs, all in one launch: buffer j is zeroed over its n[j]
+// floats (absent buffers have n[j] = 0).
+constexpr int MB_NZERO = 6;
+struct ZeroList {
+    float* p[MB_NZERO];
+    int64_t n[MB_NZERO];
+};
+
+__global__ void k_zero(ZeroList z)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < MB_NZERO; ++j)
+        if (i < z.n[j]) z.p[j][i] = 0.0f;
 }
 
-static gm_status zero(float* p, int64_t n, hipStream_t stream)
+static gm_status zero(const ZeroList& z, hipStream_t stream)
 {
-    if (!p || n <= 0) return GM_OK;
-    k_zero<<<(unsigned)div_up(n, 256), 256, 0, stream>>>(p, n);
+    int64_t n = 0;
+    for (int j = 0; j < MB_NZERO; ++j) n = std::max(n, z.n[j]);
+    if (n <= 0) return GM_OK;
+    k_zero<<<(unsigned)div_up(n, 256), 256, 0, stream>>>(z);
     GM_LAUNCH_CHECK();
     return GM_OK;
 }
@@ -633,6 +664,14 @@ extern "C" gm_status gm_mesh_bwd(const gm_camera* cam, const gm_mesh* mesh, cons
     GM_ARG_CHECK(!(g_uv || g_mips) || mesh->mips, "g_uv / g_mips need a textured mesh");
     MeshBwdParams P{};
     P.cam = dev_camera(*cam);
+    for (int i = 0; i < 9; ++i) P.R[i] = P.cam.R[i];
+    for (int i = 0; i < 3; ++i) P.t[i] = P.cam.t[i];
+    P.fx = P.cam.fx;
+    P.fy = P.cam.fy;
+    P.cx = P.cam.cx;
+    P.cy = P.cam.cy;
+    P.ifx = 1.0 / P.fx;
+    P.ify = 1.0 / P.fy;
     P.V = mesh->V;
     P.F = mesh->F;
     P.verts = mesh->verts;
@@ -661,12 +700,11 @@ extern "C" gm_status gm_mesh_bwd(const gm_camera* cam, const gm_mesh* mesh, cons
         P.lshin = light->shininess;
     }
     const size_t nmips = P.mips ? gm_mipmaps_floats(P.S) : 0;
-    if (gm_status s = zero(g_verts, 3 * (int64_t)P.V, stream)) return s;
-    if (gm_status s = zero(g_vcolor, 3 * (int64_t)P.V, stream)) return s;
-    if (gm_status s = zero(g_vnormal, 3 * (int64_t)P.V, stream)) return s;
-    if (gm_status s = zero(g_uv, 2 * (int64_t)P.Vt, stream)) return s;
-    if (gm_status s = zero(g_mips, (int64_t)nmips, stream)) return s;
-    if (gm_status s = zero(g_light, 13, stream)) return s;
+    ZeroList z{{g_verts, g_vcolor, g_vnormal, g_uv, g_mips, g_light},
+               {3 * (int64_t)P.V, 3 * (int64_t)P.V, 3 * (int64_t)P.V, 2 * (int64_t)P.Vt, (int64_t)nmips, 13}};
+    for (int j = 0; j < MB_NZERO; ++j)
+        if (!z.p[j]) z.n[j] = 0;
+    if (gm_status s = zero(z, stream)) return s;
     if (P.F > 0) {
         const bool tex = P.mips != nullptr, lit = P.lit && P.vnormal;
         auto kern = tex ? (lit ? k_mesh_bwd<true, true> : k_mesh_bwd<true, false>)
