@@ -205,8 +205,9 @@ def test_aa_full(name):
     assert rep["a_frac_pixels"] > 50
 
 
-@pytest.mark.parametrize("view", [0, 5])
+@pytest.mark.parametrize("view", range(16))
 def test_aa_c4_textured_soup(view):
+    """Every one of the 16 views of the textured triangle-soup workload."""
     s = _scene("c4")
     r, gpu, ora, tiles = _run(s, view)
     rep = _check(s, view, gpu, ora, tiles, "c4 aa view %d" % view)

@@ -71,21 +71,31 @@ def test_c2_icosphere():
     assert _run(scenes.make_scene("c2")) > 0
 
 
-@pytest.mark.parametrize("view", [0, 7])
+_SCENES = {}
+
+
+def _scene(name):
+    if name not in _SCENES:
+        _SCENES[name] = scenes.make_scene(name)
+    return _SCENES[name]
+
+
+@pytest.mark.parametrize("view", range(16))
 def test_c4_texture(view):
-    assert _run(scenes.make_scene("c4"), view, seed=view) > 0
+    """Every one of the 16 views of the textured triangle-soup workload."""
+    assert _run(_scene("c4"), view, seed=view) > 0
 
 
 def test_c3_lit():
-    assert _run(scenes.make_scene("c3"), seed=3) > 100000
+    assert _run(_scene("c3"), seed=3) > 100000
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("view", [1, 3])
-def test_c5_lit_rotated_views(view):
-    """The four-sphere workload under its rotated and translated cameras (views 1
-    and 3), Phong lit: the light and normals seen from off the optical axis."""
-    assert _run(scenes.make_scene("c5"), view, seed=50 + view) > 100000
+@pytest.mark.parametrize("view", [0, 1, 2, 3])
+def test_c5_lit_views(view):
+    """Each view of the four-sphere workload (views 1-3 under rotated and translated
+    cameras), Phong lit: the light and normals also seen from off the optical axis."""
+    assert _run(_scene("c5"), view, seed=50 + view) > 100000
 
 
 def test_tiny_lit():

@@ -88,8 +88,9 @@ def test_c2_full():
     assert P.compare_bins(s, 0, gpu) == 0
 
 
-@pytest.mark.parametrize("view", [0, 5, 11])
+@pytest.mark.parametrize("view", range(16))
 def test_c4_views(view):
+    """Every one of the 16 views of the triangle-soup workload on every tile."""
     s = _scene("c4")
     gpu, ora, tiles = _run(s, view, cull=True)
     _check_all(s, view, gpu, ora, tiles, True, "c4 view %d" % view)
