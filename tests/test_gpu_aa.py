@@ -244,6 +244,19 @@ def test_aa_c3_full():
     assert rep["a_frac_pixels"] > 1000 and rep["silhouette_vertices"] > 100
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("view", [0, 1, 2, 3])
+def test_aa_c5_full(view):
+    """Each view of the four-sphere workload antialiased (3M Gaussians, 499,280
+    faces; views 1-3 under rotated and translated cameras), every tile, as for the
+    sphere above."""
+    s = _scene("c5")
+    print("c5 view %d aa full: GPU pass and oracle on all %d tiles" % (view, s.tiles_x * s.tiles_y), flush=True)
+    r, gpu, ora, tiles = _run(s, view)
+    rep = _check(s, view, gpu, ora, tiles, "c5 view %d aa full" % view)
+    assert rep["a_frac_pixels"] > 1000 and rep["silhouette_vertices"] > 100
+
+
 def test_aa_cull_invariance():
     import torch
     from differentiable_hybrid_mesh_amd.pipeline import DeviceScene, Renderer
