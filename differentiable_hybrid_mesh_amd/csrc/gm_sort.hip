@@ -88,6 +88,21 @@ __device__ __forceinline__ void top_stats_add(int4& st, uint32_t key)
     st.w += listed ? 0 : 1;
 }
 
+// Logical index of block b when the first nlive blocks of the grid hold keys.
+// Blocks are dispatched to the eight XCDs in turn (block b on XCD b % 8); among
+// the live blocks XCD x takes the contiguous logical range from x q + min(x, r)
+// (q = nlive / 8, r = nlive % 8), so blocks with consecutive logical indices
+// (adjacent key ranges, histogram columns and digit runs) share one L2 and fill
+// its lines together instead of writing parts of them from several XCDs.  Blocks
+// past the live ones keep their index (their histogram columns are zeros).  A
+// bijection on the grid.
+__device__ __forceinline__ int xcd_block(int b, int nlive)
+{
+    if (b >= nlive) return b;
+    const int q = nlive >> 3, r = nlive & 7, x = b & 7, i = b >> 3;
+    return x * q + min(x, r) + i;
+}
+
 template <int BITS, typename KT, int ITEMS>
 __global__ void __launch_bounds__(RS_THREADS)
 k_radix_hist(const KT* __restrict__ keys, const long long* __restrict__ d_count, long long n_max,
@@ -130,7 +145,8 @@ k_radix_hist(const KT* __restrict__ keys, const long long* __restrict__ d_count,
     // (keys are 256-byte aligned and e0 is a multiple of ITEMS): all of a block's
     // loads are in flight together, where one key per load left it latency-bound
     constexpr int CHUNK = RS_THREADS * ITEMS;
-    const long long e0 = (long long)blockIdx.x * CHUNK + (long long)threadIdx.x * ITEMS;
+    const int lb = xcd_block(blockIdx.x, (int)((n + CHUNK - 1) / CHUNK));
+    const long long e0 = (long long)lb * CHUNK + (long long)threadIdx.x * ITEMS;
     if (e0 + ITEMS <= n) {
         static_assert(ITEMS * sizeof(KT) % 16 == 0, "whole 16-byte loads per thread");
         constexpr int NV = ITEMS * (int)sizeof(KT) / 16;
@@ -160,14 +176,14 @@ k_radix_hist(const KT* __restrict__ keys, const long long* __restrict__ d_count,
     if (ts.stats_out) {
         __syncthreads();  // s_st may still be read by the decision above
         block_reduce4(st, s_st);
-        if (threadIdx.x == 0) ts.stats_out[blockIdx.x] = st;
+        if (threadIdx.x == 0) ts.stats_out[lb] = st;
     }
     __syncthreads();
     if (threadIdx.x < R) {
         int c = 0;
 #pragma unroll
         for (int w = 0; w < HC; ++w) c += h[w][threadIdx.x];
-        hist[threadIdx.x * nblocks + blockIdx.x] = c;
+        hist[threadIdx.x * nblocks + lb] = c;
     }
 }
 
@@ -204,11 +220,12 @@ k_radix_scatter(const KT* __restrict__ keys_in, const int32_t* __restrict__ vals
     const long long n = live_count(d_count, n_max);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const unsigned long long lt = (1ull << lane) - 1ull;
-    const long long base = (long long)blockIdx.x * CHUNK;
+    const int lb = xcd_block(blockIdx.x, (int)((n + CHUNK - 1) / CHUNK));
+    const long long base = (long long)lb * CHUNK;
     if (base >= n) return;
 #pragma unroll
     for (int w = 0; w < RS_WAVES; ++w) s_wc[w][t] = 0;
-    if (t < R) s_goff[t] = offs[t * nblocks + blockIdx.x];
+    if (t < R) s_goff[t] = offs[t * nblocks + lb];
     __syncthreads();
     uint32_t key[ITEMS];  // KT widened
     int32_t val[ITEMS];
